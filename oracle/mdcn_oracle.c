@@ -1,0 +1,175 @@
+/*
+ * mdcn_oracle.c -- reference evaluation of the modulated deformable 2-D
+ * convolution forward pass (DCNv2), in double precision, on the CPU.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, loads or calls it, and the two share no source.
+ *
+ * Source of the definition: the web page "TensorRT 插件解析：
+ * modulatedDeformConvPlugin 可变形卷积插件的原理、参数与使用指南" (trdm.cn),
+ * cited below as [plugin guide §N].  That page describes the operator as
+ *   - layouts and shapes of x, offset, mask, weight, bias, output  [§二]
+ *   - stride / padding / dilation / group / deformable_group       [§三]
+ *   - step 1: per output position and input channel, an anchor
+ *     (output coord * stride - pad), a sample point shifted by the
+ *     kernel tap times dilation plus the learned offset, bilinear
+ *     sampling that yields 0 outside the image, times the mask       [§五 step 1]
+ *   - step 2: a per-group contraction over (C/group)*kh*kw           [§五 step 2]
+ *   - step 3: broadcast add of the optional bias per output channel  [§五 step 3]
+ * The page describes an im2col + GEMM pipeline; this file does NOT follow
+ * that pipeline: it evaluates the definition directly, one output element
+ * at a time, with a single double accumulator.
+ *
+ * Readings of points the page leaves open or that the text extraction
+ * garbled (the extraction dropped '=', '+', '<', '>' and '&'):
+ *   R1 sample point: h = ho*stride_h - pad_h + i*dil_h + dh,
+ *                    w = wo*stride_w - pad_w + j*dil_w + dw.
+ *   R2 a sample with h <= -1, h >= H, w <= -1 or w >= W reads 0; inside
+ *      that window, each of the four bilinear corners that falls off the
+ *      image reads 0.  A non-finite sample coordinate also reads 0.
+ *   R3 floor() (not truncation) splits a coordinate into cell + fraction.
+ *   R4 offset channels: for deformable group q and tap k = i*kw + j,
+ *      channel q*2*K + 2*k holds dh and channel q*2*K + 2*k + 1 holds dw
+ *      (K = kh*kw); mask channel q*K + k holds the modulation scalar.
+ *   R5 deformable group q covers input channels [q*C/dg, (q+1)*C/dg).
+ *   R6 group g covers input channels [g*C/G, (g+1)*C/G) and output
+ *      channels [g*Co/G, (g+1)*Co/G); weight is [Co][C/G][kh][kw].
+ *   R7 the mask multiplies the sampled value as given (no activation).
+ *   R8 Ho, Wo are taken from the offset tensor, not from a formula.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Problem description, passed as an array of 17 int64 values in this order. */
+enum {
+    P_N, P_C, P_H, P_W, P_CO, P_KH, P_KW, P_HO, P_WO,
+    P_SH, P_SW, P_PH, P_PW, P_DH, P_DW, P_GROUP, P_DGROUP, P_COUNT
+};
+
+/* Value of image plane X at integer pixel (y, x); 0 off the image [§五 step 1]. */
+static double pixel_or_zero(const double *X, int64_t H, int64_t W, int64_t y, int64_t x)
+{
+    if (y < 0 || y >= H || x < 0 || x >= W)
+        return 0.0;
+    return X[y * W + x];
+}
+
+/* Bilinear sample of plane X at real point (h, w), zero outside (R2, R3). */
+static double bilinear_zero(const double *X, int64_t H, int64_t W, double h, double w)
+{
+    if (!(h > -1.0 && h < (double)H && w > -1.0 && w < (double)W))
+        return 0.0;
+    double hf = floor(h);
+    double wf = floor(w);
+    int64_t y0 = (int64_t)hf;
+    int64_t x0 = (int64_t)wf;
+    double fy = h - hf; /* weight of the lower row */
+    double fx = w - wf; /* weight of the right column */
+    return (1.0 - fy) * (1.0 - fx) * pixel_or_zero(X, H, W, y0, x0)
+         + (1.0 - fy) * fx         * pixel_or_zero(X, H, W, y0, x0 + 1)
+         + fy         * (1.0 - fx) * pixel_or_zero(X, H, W, y0 + 1, x0)
+         + fy         * fx         * pixel_or_zero(X, H, W, y0 + 1, x0 + 1);
+}
+
+/* One output element out[n][co][ho][wo], straight from the definition. */
+static double output_element(const double *x, const double *offset, const double *mask,
+                             const double *weight, const double *bias, const int64_t *p,
+                             int64_t n, int64_t co, int64_t ho, int64_t wo)
+{
+    const int64_t C = p[P_C], H = p[P_H], W = p[P_W], Co = p[P_CO];
+    const int64_t kh = p[P_KH], kw = p[P_KW], Ho = p[P_HO], Wo = p[P_WO];
+    const int64_t G = p[P_GROUP], DG = p[P_DGROUP];
+    const int64_t K = kh * kw;
+    const int64_t Cg = C / G;        /* input channels per group    (R6) */
+    const int64_t Mg = Co / G;       /* output channels per group   (R6) */
+    const int64_t Cdg = C / DG;      /* input channels per offset group (R5) */
+    const int64_t g = co / Mg;       /* the group this output channel is in */
+    const int64_t HoWo = Ho * Wo;
+    const int64_t pix = ho * Wo + wo;
+
+    double acc = 0.0;
+    for (int64_t cl = 0; cl < Cg; ++cl) {
+        const int64_t c = g * Cg + cl;
+        const int64_t q = c / Cdg;
+        const double *plane = x + (n * C + c) * H * W;
+        for (int64_t i = 0; i < kh; ++i) {
+            for (int64_t j = 0; j < kw; ++j) {
+                const int64_t k = i * kw + j;
+                const int64_t off_h_ch = n * 2 * DG * K + q * 2 * K + 2 * k;   /* R4 */
+                const int64_t off_w_ch = off_h_ch + 1;
+                const int64_t mask_ch = n * DG * K + q * K + k;
+                const double dh = offset[off_h_ch * HoWo + pix];
+                const double dw = offset[off_w_ch * HoWo + pix];
+                const double m = mask[mask_ch * HoWo + pix];
+                const double h = (double)(ho * p[P_SH] - p[P_PH] + i * p[P_DH]) + dh;  /* R1 */
+                const double w = (double)(wo * p[P_SW] - p[P_PW] + j * p[P_DW]) + dw;
+                const double val = bilinear_zero(plane, H, W, h, w) * m;            /* R7 */
+                acc += weight[((co * Cg + cl) * kh + i) * kw + j] * val;
+            }
+        }
+    }
+    if (bias)
+        acc += bias[co];
+    return acc;
+}
+
+/* Threads the OpenMP runtime will use for the calls below. */
+int mdcn_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Full forward: out is [N][Co][Ho][Wo].  bias may be NULL.
+ * Returns 0, or -1 if the description is not one this definition covers. */
+int mdcn_oracle_forward(const double *x, const double *offset, const double *mask,
+                        const double *weight, const double *bias, const int64_t *p,
+                        double *out)
+{
+    const int64_t N = p[P_N], Co = p[P_CO], Ho = p[P_HO], Wo = p[P_WO];
+    if (p[P_GROUP] <= 0 || p[P_DGROUP] <= 0 || p[P_C] % p[P_GROUP] || Co % p[P_GROUP] ||
+        p[P_C] % p[P_DGROUP])
+        return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t co = 0; co < Co; ++co)
+            for (int64_t ho = 0; ho < Ho; ++ho)
+                for (int64_t wo = 0; wo < Wo; ++wo)
+                    out[((n * Co + co) * Ho + ho) * Wo + wo] =
+                        output_element(x, offset, mask, weight, bias, p, n, co, ho, wo);
+    return 0;
+}
+
+/* Selected outputs: idx holds npts flat indices into [N][Co][Ho][Wo];
+ * out[t] receives the element at idx[t]. */
+int mdcn_oracle_points(const double *x, const double *offset, const double *mask,
+                       const double *weight, const double *bias, const int64_t *p,
+                       int64_t npts, const int64_t *idx, double *out)
+{
+    const int64_t N = p[P_N], Co = p[P_CO], Ho = p[P_HO], Wo = p[P_WO];
+    if (p[P_GROUP] <= 0 || p[P_DGROUP] <= 0 || p[P_C] % p[P_GROUP] || Co % p[P_GROUP] ||
+        p[P_C] % p[P_DGROUP])
+        return -1;
+    const int64_t total = N * Co * Ho * Wo;
+    for (int64_t t = 0; t < npts; ++t)
+        if (idx[t] < 0 || idx[t] >= total)
+            return -1;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t t = 0; t < npts; ++t) {
+        int64_t r = idx[t];
+        const int64_t wo = r % Wo; r /= Wo;
+        const int64_t ho = r % Ho; r /= Ho;
+        const int64_t co = r % Co; r /= Co;
+        const int64_t n = r;
+        out[t] = output_element(x, offset, mask, weight, bias, p, n, co, ho, wo);
+    }
+    return 0;
+}
