@@ -1,0 +1,251 @@
+"""Benchmark of the modulated deformable convolution forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype f16]
+
+A step is one mdcn_forward call (every kernel of the path) on one batch of
+seeded synthetic input of the named workload, already resident in device
+memory.  W untimed steps, then K timed steps bracketed by device
+synchronisation; then K more steps with per-kernel HIP events (the library's
+tracing entry point, on the launch stream) for the kernel durations the
+roofline figures use; then the CPU oracle on a bounded sample of the same
+workload.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "modulated deform-conv fwd effective GFLOP/s + HBM GB/s, % roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+ELEM = {"f32": 4, "f16": 2, "bf16": 2}
+DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
+
+
+def kernel_model(pr, dtype, plan_chunk):
+    """Algorithmic bytes and flops of one launch of each kernel, for a launch
+    over `cnt` images.  Bytes count each tensor a kernel must touch once."""
+    e = ELEM[dtype]
+    Ho, Wo = pr.out_hw()
+    P = Ho * Wo
+    K = pr.kh * pr.kw
+    Cg, Mg, G = pr.C // pr.groups, pr.Co // pr.groups, pr.groups
+    Kg = Cg * K
+    Kp = (Kg + 63) // 64 * 64
+    dg = pr.deformable_groups
+    x_img = pr.C * pr.H * pr.W * e
+    off_img = 2 * dg * K * P * e
+    msk_img = dg * K * P * e
+    out_img = pr.Co * P * e
+    w_bytes = pr.Co * Cg * K * e
+    bias_bytes = pr.Co * e if pr.bias else 0
+    col_img = G * P * Kp * e
+
+    def per_launch(name, cnt):
+        if name == "pack_weight":
+            return dict(bytes=w_bytes + pr.Co * Kp * e, flops=0)
+        if name == "to_nhwc":
+            return dict(bytes=2 * cnt * x_img, flops=0)
+        if name == "deform_gather":
+            # x read once, offsets and masks read once, columns written once
+            return dict(bytes=cnt * (x_img + off_img + msk_img + col_img),
+                        flops=0)
+        if name == "gemm_bias":
+            return dict(bytes=cnt * (col_img + out_img) + pr.Co * Kp * e + bias_bytes,
+                        flops=2 * cnt * pr.Co * Kg * P)
+        if name == "depthwise_direct":
+            return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + w_bytes + bias_bytes,
+                        flops=2 * cnt * pr.Co * Kg * P)
+        raise KeyError(name)
+    return per_launch
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--dtype", default=None, help="f32 | f16 | bf16 (default: the workload's "
+                    "lowest-precision dtype)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE %d) is not "
+              "supported. The forward shards by image with no collective; only the one-GPU "
+              "figure is measured." % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from modulated_deformable_convolution_amd import mdcn, workloads
+
+    if not os.path.exists(mdcn.LIBRARY):
+        from modulated_deformable_convolution_amd import build
+        build.build()
+
+    pr, dtypes = workloads.WORKLOADS[args.workload]
+    dtype = args.dtype or ("f16" if "f16" in dtypes else "bf16" if "bf16" in dtypes else dtypes[0])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    inp = workloads.generate(pr, dtype, seed=0)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups)
+    code = mdcn.dtype_code(g["x"].dtype)
+    dims = mdcn.dims_of(g["x"], g["offset"], g["mask"], g["weight"])
+    ws_bytes, _ = mdcn.mdcn_workspace_bytes(op, code, dims)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty(mdcn.mdcn_output_shape(op, dims), dtype=g["x"].dtype, device=dev)
+    plan = mdcn.mdcn_describe_plan(op, code, dims)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(trace=None):
+        mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"], out=out,
+                     workspace=ws, stream=stream.cuda_stream, trace=trace)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Per-kernel device time: HIP events around every launch, on the stream
+    # the kernels run on.
+    trace = mdcn.Trace(capacity=64 * args.steps + 64)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(trace)
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for name, ms in trace.read():
+        d = per_kernel.setdefault(name, [0, 0.0])
+        d[0] += 1
+        d[1] += ms
+    chunk = 1
+    for tok in plan.split():
+        if tok.startswith("chunk="):
+            chunk = int(tok.split("=")[1])
+    model = kernel_model(pr, dtype, chunk)
+    kernels = {}
+    for name, (count, total_ms) in per_kernel.items():
+        avg_ms = total_ms / count
+        launches_per_step = count / args.steps
+        cnt = pr.N if name == "depthwise_direct" else (
+            pr.N / max(1, launches_per_step) if name in ("to_nhwc", "deform_gather", "gemm_bias")
+            else 0)
+        m = model(name, cnt)
+        kernels[name] = dict(launches_per_step=launches_per_step, avg_ms=avg_ms,
+                             ms_per_step=total_ms / args.steps,
+                             algo_bytes_per_launch=m["bytes"],
+                             algo_flops_per_launch=m["flops"],
+                             gbs=m["bytes"] / (avg_ms * 1e-3) / 1e9,
+                             tflops=m["flops"] / (avg_ms * 1e-3) / 1e12)
+    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dominant]
+    peak_tf = MFMA_PEAK_TFLOPS[dtype]
+    t_hbm = dk["algo_bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = dk["algo_flops_per_launch"] / (peak_tf * 1e12)
+    uses_mfma = dominant == "gemm_bias"
+    if uses_mfma and t_mfma > t_hbm:
+        roofline = dict(bound="mfma", achieved=round(dk["tflops"], 2), peak=peak_tf,
+                        unit="TFLOP/s", frac=round(dk["tflops"] / peak_tf, 4), traffic=None)
+    else:
+        roofline = dict(bound="hbm", achieved=round(dk["gbs"], 1), peak=HBM_PEAK_GBS,
+                        unit="GB/s", frac=round(dk["gbs"] / HBM_PEAK_GBS, 4), traffic=None)
+    roofline["kernel"] = dominant
+
+    flops = pr.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e9
+    e = ELEM[dtype]
+    Ho, Wo = pr.out_hw()
+    K = pr.kh * pr.kw
+    min_bytes = e * (pr.N * pr.C * pr.H * pr.W + pr.N * 3 * pr.deformable_groups * K * Ho * Wo
+                     + pr.Co * (pr.C // pr.groups) * K + (pr.Co if pr.bias else 0)
+                     + pr.N * pr.Co * Ho * Wo)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(pr, inp, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; OCDNet-shaped stand-in, no dataset or weights)",
+        "config": {"workload": args.workload, "N": pr.N, "C": pr.C, "Co": pr.Co,
+                   "H": pr.H, "W": pr.W, "kernel": [pr.kh, pr.kw], "stride": list(pr.stride),
+                   "padding": list(pr.padding), "dilation": list(pr.dilation),
+                   "group": pr.groups, "deformable_group": pr.deformable_groups,
+                   "bias": pr.bias, "io_dtype": dtype, "accumulate": "f32",
+                   "parallelism": "single GPU"},
+        "hbm_gbs_effective": round(min_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "plan": plan,
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
+                        for kk, vv in v.items()} for k, v in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+def cpu_baseline(pr, inp, target_s):
+    """The oracle, untouched, on a bounded random sample of the same
+    workload's outputs; scaled to effective GFLOP/s."""
+    import numpy as np
+    from oracle import oracle
+    Ho, Wo = pr.out_hw()
+    total = pr.N * pr.Co * Ho * Wo
+    Kg = (pr.C // pr.groups) * pr.kh * pr.kw
+    rng = np.random.default_rng(0)
+    attrs = pr.attrs()
+    # inputs converted once (not timed)
+    x = inp["x"].double().numpy()
+    off = inp["offset"].double().numpy()
+    msk = inp["mask"].double().numpy()
+    w = inp["weight"].double().numpy()
+    b = inp["bias"].double().numpy() if inp["bias"] is not None else None
+    n = 256
+    elapsed = 0.0
+    while True:
+        idx = rng.choice(total, size=min(n, total), replace=False)
+        t0 = time.perf_counter()
+        oracle.forward_points(x, off, msk, w, b, idx, **attrs)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= target_s or n >= total:
+            break
+        n = min(total, int(n * max(2.0, min(16.0, 1.2 * target_s / max(elapsed, 1e-3)))))
+    flops = 2.0 * len(idx) * Kg
+    return {"value": round(flops / elapsed / 1e9, 3), "unit": "GFLOP/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "%d random output elements of the same workload (seed 0), %.1f s" %
+                      (len(idx), elapsed)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,445 @@
+// api.cpp -- the extern "C" boundary declared in include/mdcn.h: validation,
+// planning, launches on the caller's stream, tracing.  No C++ exception
+// crosses the boundary.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "launch.h"
+#include "mdcn.h"
+#include "plan.h"
+
+struct mdcn_op {
+    mdcn::Attrs attrs;
+};
+
+struct mdcn_trace {
+    int32_t capacity = 0;
+    int32_t count = 0;
+    std::vector<hipEvent_t> start, stop;
+    std::vector<int32_t> kernel;
+};
+
+namespace {
+
+using mdcn::Path;
+using mdcn::Plan;
+using mdcn::Problem;
+
+mdcn_status device_ok()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MDCN_E_DEVICE;
+    static std::mutex mu;
+    static std::map<int, bool> known;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = known.find(dev);
+    if (it == known.end()) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return MDCN_E_DEVICE;
+        const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        it = known.emplace(dev, ok).first;
+    }
+    return it->second ? MDCN_OK : MDCN_E_DEVICE;
+}
+
+struct Range {
+    const char *lo, *hi;
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range range_of(const void *p, size_t bytes)
+{
+    const char *c = static_cast<const char *>(p);
+    return Range{c, c + bytes};
+}
+
+// Records an event pair around each launch while the trace has room.
+struct Recorder {
+    hipStream_t stream;
+    mdcn_trace *trace;
+
+    template <class F>
+    hipError_t run(int32_t kernel, F &&launch)
+    {
+        int32_t slot = -1;
+        if (trace && trace->count < trace->capacity) {
+            slot = trace->count++;
+            trace->kernel[slot] = kernel;
+            hipError_t e = hipEventRecord(trace->start[slot], stream);
+            if (e != hipSuccess)
+                return e;
+        }
+        hipError_t e = launch();
+        if (e != hipSuccess)
+            return e;
+        if (slot >= 0)
+            e = hipEventRecord(trace->stop[slot], stream);
+        return e;
+    }
+};
+
+mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                         const void *x, const void *offset, const void *mask,
+                         const void *weight, const void *bias, int64_t bias_len, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream_ptr,
+                         mdcn_trace *trace)
+{
+    if (!op || !dims)
+        return MDCN_E_NULL;
+    Problem p;
+    mdcn_status st = mdcn::derive_problem(op->attrs, dtype, dims, &p);
+    if (st != MDCN_OK)
+        return st;
+    if (bias && bias_len != p.Co)       // bias_0 == weight_0 [plugin guide §四]
+        return MDCN_E_SHAPE;
+    Plan plan;
+    st = mdcn::make_plan(op->attrs, p, workspace_bytes, true, &plan);
+    if (st != MDCN_OK)
+        return st;
+    if (p.N == 0 || p.P == 0)
+        return MDCN_OK;                 // nothing to compute
+    if (!x || !offset || !mask || !weight || !out)
+        return MDCN_E_NULL;
+    if (plan.path == Path::GatherGemm) {
+        if (!workspace)
+            return MDCN_E_WORKSPACE;
+        st = mdcn::make_plan(op->attrs, p, workspace_bytes, false, &plan);
+        if (st != MDCN_OK)
+            return st;
+    }
+
+    const size_t e = p.elem;
+    const Range inputs[] = {
+        range_of(x, size_t(p.N * p.C * p.H * p.W) * e),
+        range_of(offset, size_t(p.N * 2 * p.DG * p.K * p.P) * e),
+        range_of(mask, size_t(p.N * p.DG * p.K * p.P) * e),
+        range_of(weight, size_t(p.Co * p.Cg * p.K) * e),
+        range_of(bias, bias ? size_t(p.Co) * e : 0),
+    };
+    const Range out_r = range_of(out, size_t(p.N * p.Co * p.P) * e);
+    const Range ws_r = range_of(workspace, plan.path == Path::GatherGemm ? plan.ws_bytes : 0);
+    for (const Range &in : inputs) {
+        if (overlap(out_r, in) || overlap(ws_r, in))
+            return MDCN_E_ALIAS;
+    }
+    if (overlap(out_r, ws_r))
+        return MDCN_E_ALIAS;
+
+    st = device_ok();
+    if (st != MDCN_OK)
+        return st;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    Recorder rec{stream, trace};
+    hipError_t err = hipSuccess;
+
+    if (plan.path == Path::Depthwise) {
+        err = rec.run(mdcn::K_DEPTHWISE, [&] {
+            return mdcn::launch_depthwise(p, x, offset, mask, weight, bias, out, stream);
+        });
+        return err == hipSuccess ? MDCN_OK : MDCN_E_LAUNCH;
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    void *wpack = ws + plan.wpack_off;
+    void *xt = ws + plan.xt_off;
+    void *col = ws + plan.col_off;
+    err = rec.run(mdcn::K_PACK_WEIGHT,
+                  [&] { return mdcn::launch_pack_weight(p, plan, weight, wpack, stream); });
+    if (err != hipSuccess)
+        return MDCN_E_LAUNCH;
+    const size_t x_img = size_t(p.C * p.H * p.W) * e;
+    const size_t off_img = size_t(2 * p.DG * p.K * p.P) * e;
+    const size_t msk_img = size_t(p.DG * p.K * p.P) * e;
+    const size_t out_img = size_t(p.Co * p.P) * e;
+    for (int64_t n0 = 0; n0 < p.N; n0 += plan.chunk) {
+        const int64_t cnt = std::min<int64_t>(plan.chunk, p.N - n0);
+        const char *xc = static_cast<const char *>(x) + size_t(n0) * x_img;
+        const char *oc = static_cast<const char *>(offset) + size_t(n0) * off_img;
+        const char *mc = static_cast<const char *>(mask) + size_t(n0) * msk_img;
+        char *outc = static_cast<char *>(out) + size_t(n0) * out_img;
+        err = rec.run(mdcn::K_TO_NHWC, [&] { return mdcn::launch_to_nhwc(p, cnt, xc, xt, stream); });
+        if (err != hipSuccess)
+            return MDCN_E_LAUNCH;
+        err = rec.run(mdcn::K_GATHER, [&] {
+            return mdcn::launch_gather(p, plan, cnt, xt, oc, mc, col, stream);
+        });
+        if (err != hipSuccess)
+            return MDCN_E_LAUNCH;
+        err = rec.run(mdcn::K_GEMM, [&] {
+            return mdcn::launch_gemm(p, plan, cnt, wpack, col, bias, outc, stream);
+        });
+        if (err != hipSuccess)
+            return MDCN_E_LAUNCH;
+    }
+    return MDCN_OK;
+}
+
+mdcn_status create_impl(const int32_t stride[2], const int32_t padding[2],
+                        const int32_t dilation[2], int32_t group, int32_t dgroup,
+                        mdcn_path path, mdcn_op **out)
+{
+    if (!out)
+        return MDCN_E_NULL;
+    *out = nullptr;
+    mdcn_status st = mdcn::check_attrs(stride, padding, dilation, group, dgroup);
+    if (st != MDCN_OK)
+        return st;
+    if (path != MDCN_PATH_AUTO && path != MDCN_PATH_GATHER_GEMM && path != MDCN_PATH_DEPTHWISE)
+        return MDCN_E_PATH;
+    mdcn_op *op = new (std::nothrow) mdcn_op;
+    if (!op)
+        return MDCN_E_INTERNAL;
+    op->attrs = mdcn::Attrs{stride[0], stride[1], padding[0], padding[1], dilation[0],
+                            dilation[1], group, dgroup, path};
+    *out = op;
+    return MDCN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mdcn_status mdcn_create(const int32_t stride[2], const int32_t padding[2],
+                        const int32_t dilation[2], int32_t group, int32_t deformable_group,
+                        mdcn_op **out)
+{
+    try {
+        return create_impl(stride, padding, dilation, group, deformable_group, MDCN_PATH_AUTO, out);
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+mdcn_status mdcn_create_with_path(const int32_t stride[2], const int32_t padding[2],
+                                  const int32_t dilation[2], int32_t group,
+                                  int32_t deformable_group, mdcn_path path, mdcn_op **out)
+{
+    try {
+        return create_impl(stride, padding, dilation, group, deformable_group, path, out);
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+void mdcn_destroy(mdcn_op *op) { delete op; }
+
+mdcn_status mdcn_output_shape(const mdcn_op *op, const int64_t dims[16], int64_t out_dims[4])
+{
+    try {
+        if (!op || !dims || !out_dims)
+            return MDCN_E_NULL;
+        Problem p;
+        mdcn_status st = mdcn::derive_problem(op->attrs, MDCN_F32, dims, &p);
+        if (st != MDCN_OK)
+            return st;
+        out_dims[0] = p.N;
+        out_dims[1] = p.Co;
+        out_dims[2] = p.Ho;
+        out_dims[3] = p.Wo;
+        return MDCN_OK;
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+mdcn_status mdcn_workspace_bytes(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                                 size_t *bytes, size_t *min_bytes)
+{
+    try {
+        if (!op || !dims || !bytes)
+            return MDCN_E_NULL;
+        Problem p;
+        mdcn_status st = mdcn::derive_problem(op->attrs, dtype, dims, &p);
+        if (st != MDCN_OK)
+            return st;
+        Plan plan;
+        st = mdcn::make_plan(op->attrs, p, 0, true, &plan);
+        if (st != MDCN_OK)
+            return st;
+        const bool none = plan.path == Path::Depthwise || p.N == 0 || p.P == 0;
+        *bytes = none ? 0 : plan.ws_bytes;
+        if (min_bytes)
+            *min_bytes = none ? 0 : mdcn::min_workspace(p, plan);
+        return MDCN_OK;
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+mdcn_status mdcn_forward(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                         const void *x, const void *offset, const void *mask,
+                         const void *weight, const void *bias, int64_t bias_len, void *out,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    try {
+        return forward_impl(op, dtype, dims, x, offset, mask, weight, bias, bias_len, out,
+                            workspace, workspace_bytes, stream, nullptr);
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+mdcn_status mdcn_forward_traced(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                                const void *x, const void *offset, const void *mask,
+                                const void *weight, const void *bias, int64_t bias_len,
+                                void *out, void *workspace, size_t workspace_bytes,
+                                void *stream, mdcn_trace *trace)
+{
+    try {
+        if (!trace)
+            return MDCN_E_NULL;
+        return forward_impl(op, dtype, dims, x, offset, mask, weight, bias, bias_len, out,
+                            workspace, workspace_bytes, stream, trace);
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+mdcn_status mdcn_trace_create(int32_t capacity, mdcn_trace **out)
+{
+    try {
+        if (!out)
+            return MDCN_E_NULL;
+        *out = nullptr;
+        if (capacity <= 0)
+            return MDCN_E_SHAPE;
+        mdcn_trace *t = new (std::nothrow) mdcn_trace;
+        if (!t)
+            return MDCN_E_INTERNAL;
+        t->capacity = capacity;
+        t->start.assign(size_t(capacity), nullptr);
+        t->stop.assign(size_t(capacity), nullptr);
+        t->kernel.assign(size_t(capacity), -1);
+        for (int32_t i = 0; i < capacity; ++i) {
+            if (hipEventCreate(&t->start[i]) != hipSuccess ||
+                hipEventCreate(&t->stop[i]) != hipSuccess) {
+                mdcn_trace_destroy(t);
+                return MDCN_E_LAUNCH;
+            }
+        }
+        *out = t;
+        return MDCN_OK;
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+void mdcn_trace_destroy(mdcn_trace *trace)
+{
+    if (!trace)
+        return;
+    for (hipEvent_t ev : trace->start)
+        if (ev)
+            (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : trace->stop)
+        if (ev)
+            (void)hipEventDestroy(ev);
+    delete trace;
+}
+
+mdcn_status mdcn_trace_reset(mdcn_trace *trace)
+{
+    if (!trace)
+        return MDCN_E_NULL;
+    trace->count = 0;
+    return MDCN_OK;
+}
+
+mdcn_status mdcn_trace_count(const mdcn_trace *trace, int32_t *count)
+{
+    if (!trace || !count)
+        return MDCN_E_NULL;
+    *count = trace->count;
+    return MDCN_OK;
+}
+
+mdcn_status mdcn_trace_read(mdcn_trace *trace, int32_t i, int32_t *kernel_id, float *ms)
+{
+    if (!trace || !kernel_id || !ms)
+        return MDCN_E_NULL;
+    if (i < 0 || i >= trace->count)
+        return MDCN_E_SHAPE;
+    if (hipEventSynchronize(trace->stop[i]) != hipSuccess)
+        return MDCN_E_LAUNCH;
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, trace->start[i], trace->stop[i]) != hipSuccess)
+        return MDCN_E_LAUNCH;
+    *kernel_id = trace->kernel[i];
+    *ms = t;
+    return MDCN_OK;
+}
+
+const char *mdcn_kernel_name(int32_t kernel_id)
+{
+    switch (kernel_id) {
+    case mdcn::K_PACK_WEIGHT: return "pack_weight";
+    case mdcn::K_TO_NHWC: return "to_nhwc";
+    case mdcn::K_GATHER: return "deform_gather";
+    case mdcn::K_GEMM: return "gemm_bias";
+    case mdcn::K_DEPTHWISE: return "depthwise_direct";
+    }
+    return "?";
+}
+
+const char *mdcn_status_string(mdcn_status status)
+{
+    switch (status) {
+    case MDCN_OK: return "ok";
+    case MDCN_E_NULL: return "a required pointer is NULL";
+    case MDCN_E_ATTR: return "invalid attribute (stride/dilation must be > 0, padding >= 0, "
+                             "group and deformable_group > 0)";
+    case MDCN_E_SHAPE: return "tensor dims violate the operator's shape bindings or limits";
+    case MDCN_E_DTYPE: return "unsupported dtype";
+    case MDCN_E_WORKSPACE: return "workspace missing or too small";
+    case MDCN_E_LAUNCH: return "HIP launch or runtime call failed";
+    case MDCN_E_DEVICE: return "the current device is not a gfx950 GPU";
+    case MDCN_E_ALIAS: return "output or workspace overlaps another buffer";
+    case MDCN_E_PATH: return "the requested computation path cannot run this problem";
+    case MDCN_E_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}
+
+int32_t mdcn_abi_version(void) { return MDCN_ABI_VERSION; }
+
+mdcn_status mdcn_describe_plan(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                               size_t workspace_bytes, char *buf, size_t len)
+{
+    try {
+        if (!op || !dims || !buf || len == 0)
+            return MDCN_E_NULL;
+        Problem p;
+        mdcn_status st = mdcn::derive_problem(op->attrs, dtype, dims, &p);
+        if (st != MDCN_OK)
+            return st;
+        Plan plan;
+        st = mdcn::make_plan(op->attrs, p, workspace_bytes, workspace_bytes == 0, &plan);
+        if (st != MDCN_OK)
+            return st;
+        if (plan.path == Path::Depthwise)
+            std::snprintf(buf, len, "path=depthwise_direct N=%lld C=%lld Co=%lld P=%lld ws=0",
+                          (long long)p.N, (long long)p.C, (long long)p.Co, (long long)p.P);
+        else
+            std::snprintf(buf, len,
+                          "path=gather_gemm chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld "
+                          "ws=%zu (wpack=%zu xt/img=%zu col/img=%zu)",
+                          (long long)plan.chunk, (long long)p.Kg, (long long)plan.Kp,
+                          (long long)p.G, (long long)p.Mg, (long long)p.P, plan.ws_bytes,
+                          plan.wpack_bytes, plan.xt_bytes_per_image, plan.col_bytes_per_image);
+        return MDCN_OK;
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+}  // extern "C"

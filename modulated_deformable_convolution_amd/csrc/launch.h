@@ -1,0 +1,44 @@
+// launch.h -- host launchers of the HIP kernels.  Each launcher checks
+// hipGetLastError after its launch and returns it.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "plan.h"
+
+namespace mdcn {
+
+// Kernel ids reported by the tracing API.
+enum KernelId : int32_t {
+    K_PACK_WEIGHT = 0,
+    K_TO_NHWC = 1,
+    K_GATHER = 2,
+    K_GEMM = 3,
+    K_DEPTHWISE = 4,
+    K_COUNT = 5
+};
+
+// weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
+// kk = k*Cg + c' (tap-major), zero for kk >= Kg.
+hipError_t launch_pack_weight(const Problem &p, const Plan &plan, const void *weight,
+                              void *wpack, hipStream_t stream);
+
+// x [cnt][C][H][W] -> xt [cnt][H][W][C] (channels innermost).
+hipError_t launch_to_nhwc(const Problem &p, int64_t cnt, const void *x, void *xt,
+                          hipStream_t stream);
+
+// Deformable im2col of cnt images: col [G][cnt*P][Kp], row (n, pixel),
+// column kk = k*Cg + c', value bilinear0(x[n][g*Cg + c'], sample) * mask.
+hipError_t launch_gather(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
+                         const void *offset, const void *mask, void *col, hipStream_t stream);
+
+// out[n][g*Mg + m][pix] = sum_kk wpack[g][m][kk] * col[g][n*P + pix][kk] (+ bias).
+hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
+                       const void *col, const void *bias, void *out, hipStream_t stream);
+
+// Direct depthwise (C/group == 1) forward of all N images.
+hipError_t launch_depthwise(const Problem &p, const void *x, const void *offset,
+                            const void *mask, const void *weight, const void *bias, void *out,
+                            hipStream_t stream);
+
+}  // namespace mdcn

@@ -1,0 +1,188 @@
+// plan.cpp -- validation and planning (host only).
+#include "plan.h"
+
+#include <algorithm>
+#include <climits>
+
+namespace mdcn {
+
+namespace {
+
+constexpr int64_t kMaxPerImage = (int64_t(1) << 31) - 1;   // elements per image tensor
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Product of non-negative values, saturating at INT64_MAX (dims come from the
+// caller, so their products must not overflow).
+int64_t mul(int64_t a, int64_t b)
+{
+    int64_t r;
+    if (__builtin_mul_overflow(a, b, &r))
+        return INT64_MAX;
+    return r;
+}
+
+int64_t mul(int64_t a, int64_t b, int64_t c) { return mul(mul(a, b), c); }
+
+}  // namespace
+
+size_t dtype_size(mdcn_dtype t)
+{
+    switch (t) {
+    case MDCN_F32: return 4;
+    case MDCN_F16: return 2;
+    case MDCN_BF16: return 2;
+    }
+    return 0;
+}
+
+// [plugin guide §三]: stride and dilation components > 0, padding >= 0,
+// group and deformable_group > 0; all five are required.
+mdcn_status check_attrs(const int32_t stride[2], const int32_t padding[2],
+                        const int32_t dilation[2], int32_t group, int32_t dgroup)
+{
+    if (!stride || !padding || !dilation)
+        return MDCN_E_NULL;
+    for (int i = 0; i < 2; ++i) {
+        if (stride[i] <= 0 || dilation[i] <= 0 || padding[i] < 0)
+            return MDCN_E_ATTR;
+    }
+    if (group <= 0 || dgroup <= 0)
+        return MDCN_E_ATTR;
+    return MDCN_OK;
+}
+
+mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[16],
+                           Problem *out)
+{
+    if (!dims || !out)
+        return MDCN_E_NULL;
+    if (dtype != MDCN_F32 && dtype != MDCN_F16 && dtype != MDCN_BF16)
+        return MDCN_E_DTYPE;
+    for (int i = 0; i < 16; ++i)
+        if (dims[i] < 0)
+            return MDCN_E_SHAPE;
+    const int64_t *x = dims, *off = dims + 4, *msk = dims + 8, *w = dims + 12;
+    Problem p{};
+    p.dtype = dtype;
+    p.elem = dtype_size(dtype);
+    p.N = x[0]; p.C = x[1]; p.H = x[2]; p.W = x[3];
+    p.Co = w[0]; p.kh = w[2]; p.kw = w[3];
+    p.Ho = off[2]; p.Wo = off[3];
+    if (p.N > kMaxPerImage)
+        return MDCN_E_SHAPE;
+    p.G = a.group; p.DG = a.dgroup;
+    p.sh = a.sh; p.sw = a.sw; p.ph = a.ph; p.pw = a.pw; p.dh = a.dh; p.dw = a.dw;
+    if (p.C == 0 || p.H == 0 || p.W == 0 || p.Co == 0 || p.kh == 0 || p.kw == 0)
+        return MDCN_E_SHAPE;
+    // Bindings of [plugin guide §四]: batch of offset and mask equals x's,
+    // mask spatial dims equal offset's, offset has at least 2 channels.
+    if (off[0] != p.N || msk[0] != p.N)
+        return MDCN_E_SHAPE;
+    if (msk[2] != off[2] || msk[3] != off[3])
+        return MDCN_E_SHAPE;
+    if (off[1] < 2)
+        return MDCN_E_SHAPE;
+    // Bindings that keep every read in bounds.
+    if (p.kh > kMaxCoord || p.kw > kMaxCoord || mul(p.kh, p.kw) > kMaxPerImage)
+        return MDCN_E_SHAPE;
+    p.K = p.kh * p.kw;
+    if (p.C % p.G != 0 || p.Co % p.G != 0 || p.C % p.DG != 0)
+        return MDCN_E_SHAPE;
+    if (mul(w[1], p.G) != p.C)
+        return MDCN_E_SHAPE;
+    if (off[1] != mul(2, p.DG, p.K) || msk[1] != mul(p.DG, p.K))
+        return MDCN_E_SHAPE;
+    p.Cg = p.C / p.G;
+    p.Mg = p.Co / p.G;
+    p.Cdg = p.C / p.DG;
+    p.Kg = mul(p.Cg, p.K);
+    if (p.Kg > kMaxPerImage)
+        return MDCN_E_SHAPE;
+    // Size limits of this implementation: 32-bit indexing within an image,
+    // exact float anchors.
+    if (p.H >= kMaxCoord || p.W >= kMaxCoord || p.Ho >= kMaxCoord || p.Wo >= kMaxCoord)
+        return MDCN_E_SHAPE;
+    p.P = p.Ho * p.Wo;
+    const int64_t kp = round_up(p.Kg, 64);
+    if (mul(p.C, p.H, p.W) > kMaxPerImage || mul(p.Co, p.P) > kMaxPerImage ||
+        mul(off[1], p.P) > kMaxPerImage || mul(p.G, p.P, kp) > kMaxPerImage ||
+        mul(p.Co, kp) > kMaxPerImage)
+        return MDCN_E_SHAPE;
+    const int64_t amax_h = mul(std::max<int64_t>(0, p.Ho - 1), p.sh) + mul(p.kh - 1, p.dh);
+    const int64_t amax_w = mul(std::max<int64_t>(0, p.Wo - 1), p.sw) + mul(p.kw - 1, p.dw);
+    if (amax_h < 0 || amax_w < 0 || amax_h >= kMaxCoord || amax_w >= kMaxCoord ||
+        p.ph >= kMaxCoord || p.pw >= kMaxCoord)
+        return MDCN_E_SHAPE;
+    *out = p;
+    return MDCN_OK;
+}
+
+mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
+{
+    switch (a.path) {
+    case MDCN_PATH_AUTO:
+        *out = (p.Cg == 1) ? Path::Depthwise : Path::GatherGemm;
+        return MDCN_OK;
+    case MDCN_PATH_GATHER_GEMM:
+        *out = Path::GatherGemm;
+        return MDCN_OK;
+    case MDCN_PATH_DEPTHWISE:
+        if (p.Cg != 1)
+            return MDCN_E_PATH;
+        *out = Path::Depthwise;
+        return MDCN_OK;
+    }
+    return MDCN_E_PATH;
+}
+
+mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
+                      bool default_sizing, Plan *out)
+{
+    Plan plan{};
+    mdcn_status st = choose_path(a, p, &plan.path);
+    if (st != MDCN_OK)
+        return st;
+    if (plan.path == Path::Depthwise) {
+        plan.chunk = std::max<int64_t>(p.N, 1);
+        *out = plan;
+        return MDCN_OK;
+    }
+    plan.Kp = round_up(p.Kg, 64);
+    plan.wpack_off = 0;
+    plan.wpack_bytes = align_up(size_t(p.G * p.Mg * plan.Kp) * p.elem, kAlign);
+    plan.xt_bytes_per_image = align_up(size_t(p.H * p.W * p.C) * p.elem, kAlign);
+    plan.col_bytes_per_image = align_up(size_t(p.G * p.P * plan.Kp) * p.elem, kAlign);
+    // Default chunk: as many images as fit a 256 MiB column buffer, at least
+    // one; also keep every launch's element count within 32-bit indexing.
+    int64_t by_budget = int64_t(kColumnBudget / std::max<size_t>(plan.col_bytes_per_image, 1));
+    int64_t by_index = kMaxPerImage / std::max<int64_t>(p.G * std::max<int64_t>(p.P, 1) * plan.Kp, 1);
+    int64_t chunk = std::max<int64_t>(1, std::min<int64_t>({std::max<int64_t>(p.N, 1),
+                                                           by_budget, by_index}));
+    const size_t per_image = plan.xt_bytes_per_image + plan.col_bytes_per_image;
+    if (!default_sizing) {
+        if (workspace_bytes < plan.wpack_bytes + per_image)
+            return MDCN_E_WORKSPACE;
+        int64_t fit = int64_t((workspace_bytes - plan.wpack_bytes) / per_image);
+        chunk = std::max<int64_t>(1, std::min(chunk, fit));
+    }
+    plan.chunk = chunk;
+    plan.xt_off = plan.wpack_bytes;
+    plan.col_off = plan.xt_off + size_t(chunk) * plan.xt_bytes_per_image;
+    plan.ws_bytes = plan.col_off + size_t(chunk) * plan.col_bytes_per_image;
+    *out = plan;
+    return MDCN_OK;
+}
+
+size_t min_workspace(const Problem &p, const Plan &plan)
+{
+    (void)p;
+    if (plan.path == Path::Depthwise)
+        return 0;
+    return plan.wpack_bytes + plan.xt_bytes_per_image + plan.col_bytes_per_image;
+}
+
+}  // namespace mdcn

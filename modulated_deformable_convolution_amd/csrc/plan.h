@@ -1,0 +1,66 @@
+// plan.h -- host-side problem derivation, validation and execution planning
+// for the modulated deformable convolution forward.  Pure host C++: nothing
+// here touches the GPU, so every rule can be exercised without one.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "mdcn.h"
+
+namespace mdcn {
+
+// The five attributes of the operator, kept as int64
+// [plugin guide §三: stride, padding, dilation, group, deformable_group].
+struct Attrs {
+    int64_t sh, sw;   // stride
+    int64_t ph, pw;   // padding
+    int64_t dh, dw;   // dilation
+    int64_t group;
+    int64_t dgroup;   // deformable_group
+    mdcn_path path;
+};
+
+// Everything one forward needs to know about its shapes.
+struct Problem {
+    mdcn_dtype dtype;
+    size_t elem;                 // bytes per element
+    int64_t N, C, H, W;          // x
+    int64_t Co, kh, kw;          // weight [Co, C/group, kh, kw]
+    int64_t Ho, Wo;              // from offset dims 2, 3 [plugin guide §二]
+    int64_t G, DG;               // group, deformable_group
+    int64_t Cg, Mg, Cdg;         // C/G, Co/G, C/DG
+    int64_t K, Kg, P;            // kh*kw, Cg*K, Ho*Wo
+    int64_t sh, sw, ph, pw, dh, dw;
+};
+
+enum class Path { GatherGemm, Depthwise };
+
+// Workspace layout of the gather + GEMM path (all offsets 256-byte aligned):
+//   [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
+struct Plan {
+    Path path;
+    int64_t chunk;               // images per pass through gather + GEMM
+    int64_t Kp;                  // contraction length padded to a multiple of 64
+    size_t wpack_off, wpack_bytes;
+    size_t xt_off, xt_bytes_per_image;
+    size_t col_off, col_bytes_per_image;
+    size_t ws_bytes;             // bytes this plan uses
+};
+
+constexpr size_t kColumnBudget = size_t(256) << 20;   // default column-buffer cap
+constexpr int64_t kMaxCoord = int64_t(1) << 24;        // spatial extents and anchors
+
+size_t dtype_size(mdcn_dtype t);
+mdcn_status check_attrs(const int32_t stride[2], const int32_t padding[2],
+                        const int32_t dilation[2], int32_t group, int32_t dgroup);
+mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[16],
+                           Problem *out);
+mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out);
+// Plan for a given workspace size; with default_sizing the plan uses the
+// library's default chunking regardless of workspace_bytes.
+mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
+                      bool default_sizing, Plan *out);
+size_t min_workspace(const Problem &p, const Plan &plan);
+
+}  // namespace mdcn

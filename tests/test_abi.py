@@ -1,0 +1,235 @@
+"""The C ABI library on the host: it loads, exports every declared symbol, and
+its validation, shape, workspace and planning rules behave as include/mdcn.h
+states.  No kernel is launched: every forward here either fails validation
+before touching a device or has nothing to do."""
+import os
+import re
+
+import pytest
+
+from helpers import ensure_built
+
+ensure_built()
+from modulated_deformable_convolution_amd import mdcn  # noqa: E402
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mdcn.h")
+
+# dims of the OCDNet-like stage: x, offset, mask, weight
+DIMS = [4, 256, 160, 160, 4, 18, 160, 160, 4, 9, 160, 160, 256, 256, 3, 3]
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(mdcn_[a-z_]+)\s*\(", text)))
+
+
+def test_abi_version():
+    assert mdcn.mdcn_abi_version() == 1
+
+
+def test_every_declared_symbol_is_exported():
+    lib = mdcn.library()
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(mdcn.EXPORTED) == names
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(stride=(0, 1)), mdcn.MDCN_E_ATTR),
+    (dict(stride=(1, -2)), mdcn.MDCN_E_ATTR),
+    (dict(dilation=(0, 1)), mdcn.MDCN_E_ATTR),
+    (dict(padding=(-1, 0)), mdcn.MDCN_E_ATTR),
+    (dict(group=0), mdcn.MDCN_E_ATTR),
+    (dict(deformable_group=-1), mdcn.MDCN_E_ATTR),
+    (dict(path=7), mdcn.MDCN_E_PATH),
+])
+def test_create_rejects(kw, code):
+    args = dict(stride=1, padding=0, dilation=1, group=1, deformable_group=1)
+    args.update(kw)
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_create(**args)
+    assert e.value.status == code
+
+
+def test_create_null_out():
+    import ctypes
+    lib = mdcn.library()
+    one = (ctypes.c_int32 * 2)(1, 1)
+    assert lib.mdcn_create(one, one, one, 1, 1, None) == mdcn.MDCN_E_NULL
+    assert lib.mdcn_create(None, one, one, 1, 1, ctypes.byref(ctypes.c_void_p())) == \
+        mdcn.MDCN_E_NULL
+
+
+def test_destroy_null_is_safe():
+    mdcn.library().mdcn_destroy(None)
+    mdcn.library().mdcn_trace_destroy(None)
+
+
+def test_output_shape_rule():
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    assert mdcn.mdcn_output_shape(op, DIMS) == (4, 256, 160, 160)
+    # spatial size comes from offset dims 2 and 3, not from a formula
+    d = list(DIMS)
+    d[6:8] = [100, 37]
+    d[10:12] = [100, 37]
+    assert mdcn.mdcn_output_shape(op, d) == (4, 256, 100, 37)
+    op2 = mdcn.mdcn_create(2, 2, 2, 2, 4)
+    d3 = [2, 128, 128, 128, 2, 72, 64, 64, 2, 36, 64, 64, 256, 64, 3, 3]
+    assert mdcn.mdcn_output_shape(op2, d3) == (2, 256, 64, 64)
+
+
+def _bad(i, v, base=DIMS):
+    d = list(base)
+    d[i] = v
+    return d
+
+
+@pytest.mark.parametrize("dims", [
+    _bad(0, -1),                 # negative dim
+    _bad(1, 0),                  # C == 0
+    _bad(2, 0),                  # H == 0
+    _bad(12, 0),                 # Co == 0
+    _bad(14, 0),                 # kh == 0
+    _bad(4, 3),                  # offset.d0 != x.d0
+    _bad(8, 5),                  # mask.d0 != x.d0
+    _bad(10, 159),               # mask.d2 != offset.d2
+    _bad(11, 161),               # mask.d3 != offset.d3
+    _bad(5, 1),                  # offset.d1 < 2
+    _bad(5, 20),                 # offset.d1 != 2*dg*kh*kw
+    _bad(9, 8),                  # mask.d1 != dg*kh*kw
+    _bad(13, 128),               # weight.d1 * group != C
+    _bad(2, 1 << 24),            # spatial extent beyond 2^24
+    _bad(6, 1 << 24),            # output extent beyond 2^24
+])
+def test_shape_bindings(dims):
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_output_shape(op, dims)
+    assert e.value.status == mdcn.MDCN_E_SHAPE
+    st = mdcn.mdcn_forward(op, mdcn.MDCN_F32, dims, 16, 32, 48, 64, 0, 0, 1 << 40,
+                           1 << 41, 1 << 30, 0)
+    assert st == mdcn.MDCN_E_SHAPE
+
+
+def test_group_divisibility():
+    # C = 6 with group 4: not divisible
+    op = mdcn.mdcn_create(1, 1, 1, 4, 1)
+    d = [1, 6, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 8, 1, 3, 3]
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_output_shape(op, d)
+    assert e.value.status == mdcn.MDCN_E_SHAPE
+    # Co % group != 0
+    op = mdcn.mdcn_create(1, 1, 1, 2, 1)
+    d = [1, 6, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 7, 3, 3, 3]
+    with pytest.raises(mdcn.MdcnError):
+        mdcn.mdcn_output_shape(op, d)
+    # C % deformable_group != 0
+    op = mdcn.mdcn_create(1, 1, 1, 1, 4)
+    d = [1, 6, 8, 8, 1, 72, 8, 8, 1, 36, 8, 8, 8, 6, 3, 3]
+    with pytest.raises(mdcn.MdcnError):
+        mdcn.mdcn_output_shape(op, d)
+
+
+def test_forward_validation_codes():
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    F32 = mdcn.MDCN_F32
+    big = 1 << 40
+    # bad dtype
+    assert mdcn.mdcn_forward(op, 9, DIMS, 16, 32, 48, 64, 0, 0, big, big * 2, 1 << 32, 0) == \
+        mdcn.MDCN_E_DTYPE
+    # bias length must equal weight.d0
+    assert mdcn.mdcn_forward(op, F32, DIMS, 16, 32, 48, 64, 80, 255, big, big * 2, 1 << 32,
+                             0) == mdcn.MDCN_E_SHAPE
+    # null input pointer
+    assert mdcn.mdcn_forward(op, F32, DIMS, 0, 32, 48, 64, 0, 0, big, big * 2, 1 << 32, 0) == \
+        mdcn.MDCN_E_NULL
+    # missing or small workspace on the gather + GEMM path
+    assert mdcn.mdcn_forward(op, F32, DIMS, 16, 32, 48, 64, 0, 0, big, 0, 0, 0) == \
+        mdcn.MDCN_E_WORKSPACE
+    _, min_b = mdcn.mdcn_workspace_bytes(op, F32, DIMS)
+    assert mdcn.mdcn_forward(op, F32, DIMS, 16, 32, 48, 64, 0, 0, big, big * 2, min_b - 1,
+                             0) == mdcn.MDCN_E_WORKSPACE
+    # output overlapping an input
+    x_bytes = 4 * 256 * 160 * 160 * 4
+    assert mdcn.mdcn_forward(op, F32, DIMS, big, big * 2, big * 3, big * 4, 0, 0,
+                             big + x_bytes - 4, big * 5, 1 << 32, 0) == mdcn.MDCN_E_ALIAS
+    # workspace overlapping the output
+    assert mdcn.mdcn_forward(op, F32, DIMS, big, big * 2, big * 3, big * 4, 0, 0, big * 5,
+                             big * 5 + 64, 1 << 32, 0) == mdcn.MDCN_E_ALIAS
+    # null op / dims
+    lib = mdcn.library()
+    assert lib.mdcn_forward(None, 0, None, None, None, None, None, None, 0, None, None, 0,
+                            None) == mdcn.MDCN_E_NULL
+
+
+def test_depthwise_path_needs_one_channel_per_group():
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_DEPTHWISE)
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F32, DIMS)
+    assert e.value.status == mdcn.MDCN_E_PATH
+
+
+def test_empty_problems_are_noops():
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    d = list(DIMS)
+    d[0] = d[4] = d[8] = 0          # N == 0
+    assert mdcn.mdcn_forward(op, mdcn.MDCN_F32, d, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) == mdcn.MDCN_OK
+    assert mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F32, d) == (0, 0)
+    d = list(DIMS)
+    d[6] = d[10] = 0                # Ho == 0
+    assert mdcn.mdcn_forward(op, mdcn.MDCN_F32, d, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) == mdcn.MDCN_OK
+
+
+def test_workspace_sizes_and_chunking():
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    # f16: 2 images of 2304 x 25600 halves of columns fit the 256 MiB budget
+    b, mb = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, DIMS)
+    col_img = 2304 * 25600 * 2
+    xt_img = 256 * 160 * 160 * 2
+    wp = 256 * 2304 * 2
+    assert mb == wp + col_img + xt_img
+    assert b == wp + 2 * (col_img + xt_img)
+    assert "chunk=2" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, DIMS)
+    # less workspace: one image per chunk
+    assert "chunk=1" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, DIMS, mb)
+    # f32: one image per chunk (236 MB of columns)
+    assert "chunk=1" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F32, DIMS)
+    # depthwise problem on the automatic path needs no workspace
+    dw = mdcn.mdcn_create(1, 1, 1, 256, 1)
+    d5 = [8, 256, 96, 96, 8, 18, 96, 96, 8, 9, 96, 96, 256, 1, 3, 3]
+    assert mdcn.mdcn_workspace_bytes(dw, mdcn.MDCN_F32, d5) == (0, 0)
+    assert "depthwise" in mdcn.mdcn_describe_plan(dw, mdcn.MDCN_F32, d5)
+    # ... and the gather + GEMM path can be forced for it
+    dwg = mdcn.mdcn_create(1, 1, 1, 256, 1, path=mdcn.MDCN_PATH_GATHER_GEMM)
+    assert mdcn.mdcn_workspace_bytes(dwg, mdcn.MDCN_F32, d5)[0] > 0
+
+
+def test_contraction_padding():
+    # Kg = 4*9 = 36 pads to 64
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    d1 = [1, 4, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 4, 4, 3, 3]
+    assert "Kp=64" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F32, d1)
+
+
+def test_status_strings():
+    for code in range(11):
+        assert mdcn.status_string(code)
+    assert mdcn.status_string(99) == "unknown status"
+    assert mdcn.mdcn_kernel_name(3) == "gemm_bias"
+
+
+def test_forward_without_gpu_reports_device():
+    """With valid arguments and no GPU present, the call fails cleanly with
+    MDCN_E_DEVICE instead of launching.  (Skipped where a GPU exists: the
+    pointers here are not real.)"""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    big = 1 << 40
+    st = mdcn.mdcn_forward(op, mdcn.MDCN_F32, DIMS, big, big * 2, big * 3, big * 4, 0, 0,
+                           big * 5, big * 6, 1 << 32, 0)
+    assert st == mdcn.MDCN_E_DEVICE

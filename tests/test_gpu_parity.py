@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small problems (several tiles, ragged tails in every GEMM dimension, padded
+contraction, scalar and vector gather paths, every dtype and path) are
+compared element by element over the whole output.  The five benchmark
+workloads are run at full size, in the same launch configuration as the
+benchmark, and compared on sampled outputs (seeded random elements plus the
+image borders) that the oracle computes one by one.  Tolerances are those of
+helpers.within_tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import ensure_built, error_report, within_tolerance
+
+ensure_built()
+from modulated_deformable_convolution_amd import mdcn, workloads  # noqa: E402
+from modulated_deformable_convolution_amd.workloads import Problem  # noqa: E402
+from oracle import oracle  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+SMALL = {
+    # Co = 160: one full and one partial 128-row tile; 3 images x 361 pixels:
+    # a ragged column tile; Kg = 288 padded to 320; two offset groups.
+    "multi_tile_dg2": Problem(N=3, C=32, Co=160, H=19, W=19, deformable_groups=2,
+                              offset_dist=("normal", 2.0)),
+    # kh != kw, asymmetric stride/padding/dilation, 3 groups, 6 offset groups.
+    "grouped_strided": Problem(N=2, C=48, Co=96, H=17, W=23, kh=3, kw=2, stride=(2, 1),
+                               padding=(2, 0), dilation=(1, 2), groups=3, deformable_groups=6,
+                               offset_dist=("normal", 1.5)),
+    # channel counts that are not a multiple of the 16-byte vector: scalar gather.
+    "odd_channels": Problem(N=2, C=6, Co=10, H=11, W=9, deformable_groups=2, bias=False,
+                            offset_dist=("normal", 1.0)),
+    # depthwise with a channel multiplier of 2 and 3 offset groups.
+    "depthwise_mult2": Problem(N=2, C=24, Co=48, H=13, W=13, groups=24, deformable_groups=3,
+                               offset_dist=("uniform", 8.0), mask_dist=("uniform_zeros", 0.1)),
+    "kernel_1x1": Problem(N=2, C=16, Co=24, H=9, W=10, kh=1, kw=1, padding=(0, 0),
+                          offset_dist=("normal", 2.0)),
+    "kernel_5x5": Problem(N=1, C=16, Co=16, H=12, W=12, kh=5, kw=5, padding=(2, 2)),
+    # output grid smaller than the conv formula (taken from the offset dims)
+    "smaller_out_grid": Problem(N=2, C=16, Co=32, H=15, W=15, Ho=7, Wo=11),
+    "tiny": workloads.TINY,
+}
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
+
+
+def make_op(pr, path=mdcn.MDCN_PATH_AUTO):
+    return mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups,
+                            pr.deformable_groups, path=path)
+
+
+def run_gpu(pr, inp, path=mdcn.MDCN_PATH_AUTO, workspace_bytes=None, trace=None):
+    g = to_dev(inp)
+    op = make_op(pr, path)
+    ws = None
+    if workspace_bytes is not None:
+        ws = torch.empty(max(workspace_bytes, 1), dtype=torch.uint8, device=DEV)
+    out = mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"],
+                       workspace=ws, trace=trace)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def oracle_full(pr, inp):
+    return oracle.forward(inp["x"], inp["offset"], inp["mask"], inp["weight"], inp["bias"],
+                          **pr.attrs())
+
+
+def paths_for(pr):
+    paths = [mdcn.MDCN_PATH_GATHER_GEMM]
+    if pr.C // pr.groups == 1:
+        paths.append(mdcn.MDCN_PATH_DEPTHWISE)
+    return paths
+
+
+CASES = [(name, dt, path) for name, pr in SMALL.items() for dt in ("f32", "f16", "bf16")
+         for path in paths_for(pr)]
+
+
+@pytest.mark.parametrize("name,dtype,path", CASES)
+def test_small_full_tensor(name, dtype, path):
+    pr = SMALL[name]
+    print("case", name, dtype, "path", path, flush=True)
+    inp = workloads.generate(pr, dtype, seed=1)
+    got = run_gpu(pr, inp, path).double().numpy()
+    ref = oracle_full(pr, inp)
+    assert got.shape == ref.shape
+    ok, err, bound = within_tolerance(got, ref, dtype)
+    assert ok, (name, dtype, error_report(got, ref), float((err / bound).max()))
+
+
+def test_auto_path_matches_forced_paths():
+    pr = SMALL["depthwise_mult2"]
+    inp = workloads.generate(pr, "f32", seed=2)
+    auto = run_gpu(pr, inp, mdcn.MDCN_PATH_AUTO)
+    dw = run_gpu(pr, inp, mdcn.MDCN_PATH_DEPTHWISE)
+    assert torch.equal(auto, dw)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_zero_mask_gives_bias_exactly(dtype):
+    pr = SMALL["multi_tile_dg2"]
+    inp = workloads.generate(pr, dtype, seed=3)
+    inp["mask"] = torch.zeros_like(inp["mask"])
+    got = run_gpu(pr, inp)
+    assert torch.equal(got, inp["bias"][None, :, None, None].expand_as(got))
+
+
+@pytest.mark.parametrize("path", [mdcn.MDCN_PATH_GATHER_GEMM, mdcn.MDCN_PATH_DEPTHWISE])
+def test_off_image_samples_give_bias_exactly(path):
+    pr = SMALL["depthwise_mult2"]
+    inp = workloads.generate(pr, "f32", seed=4)
+    off = inp["offset"]
+    # alternate far below/right, far above/left, and the exact edges h = -1 / w = W
+    far = torch.full_like(off, 1.0e4)
+    far[:, 1::4] = -3.0e7
+    far[:, 2::4] = -1.0e9
+    inp["offset"] = far
+    got = run_gpu(pr, inp, path)
+    assert torch.equal(got, inp["bias"][None, :, None, None].expand_as(got))
+    # exactly on the line h = -1 for every tap (anchor row + offset == -1)
+    Ho, Wo = pr.out_hw()
+    off = torch.zeros_like(inp["offset"])
+    K = pr.kh * pr.kw
+    for q in range(pr.deformable_groups):
+        for k in range(K):
+            i = k // pr.kw
+            anchor = torch.arange(Ho, dtype=torch.float32) * pr.stride[0] - pr.padding[0] \
+                + i * pr.dilation[0]
+            off[:, q * 2 * K + 2 * k] = (-1.0 - anchor)[:, None]
+            off[:, q * 2 * K + 2 * k + 1] = 0.25
+    inp["offset"] = off
+    got = run_gpu(pr, inp, path)
+    assert torch.equal(got, inp["bias"][None, :, None, None].expand_as(got))
+
+
+def test_chunked_workspace_matches_default():
+    pr = SMALL["multi_tile_dg2"]
+    inp = workloads.generate(pr, "f16", seed=5)
+    op = make_op(pr)
+    dims = [pr.N, pr.C, pr.H, pr.W] + list(inp["offset"].shape) + list(inp["mask"].shape) + \
+        list(inp["weight"].shape)
+    full, least = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, dims)
+    assert least < full
+    assert "chunk=1" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, dims, least)
+    a = run_gpu(pr, inp)
+    b = run_gpu(pr, inp, workspace_bytes=least)
+    assert torch.equal(a, b)
+
+
+def test_traced_forward_matches_and_records():
+    pr = SMALL["multi_tile_dg2"]
+    inp = workloads.generate(pr, "bf16", seed=6)
+    tr = mdcn.Trace(64)
+    a = run_gpu(pr, inp, trace=tr)
+    b = run_gpu(pr, inp)
+    assert torch.equal(a, b)
+    names = [n for n, _ in tr.read()]
+    assert names[0] == "pack_weight"
+    assert names.count("gemm_bias") == names.count("deform_gather") >= 1
+    assert all(ms >= 0 for _, ms in tr.read())
+
+
+def test_repeatable():
+    pr = SMALL["grouped_strided"]
+    inp = workloads.generate(pr, "f32", seed=7)
+    assert torch.equal(run_gpu(pr, inp), run_gpu(pr, inp))
+
+
+def test_empty_batch():
+    pr = SMALL["tiny"]
+    inp = workloads.generate(pr, "f32", seed=8)
+    for k in ("x", "offset", "mask"):
+        inp[k] = inp[k][:0].contiguous()
+    got = run_gpu(pr, inp)
+    assert tuple(got.shape) == (0, pr.Co, 8, 8)
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def sample_indices(shape, n_random, seed):
+    """Seeded random flat indices plus every border pixel of two (n, co) planes."""
+    N, Co, Ho, Wo = shape
+    rng = np.random.default_rng(seed)
+    total = N * Co * Ho * Wo
+    idx = set(rng.choice(total, size=min(n_random, total), replace=False).tolist())
+    for n, co in ((0, 0), (N - 1, Co - 1)):
+        base = (n * Co + co) * Ho * Wo
+        for h in range(Ho):
+            for w in (0, Wo - 1):
+                idx.add(base + h * Wo + w)
+        for w in range(Wo):
+            for h in (0, Ho - 1):
+                idx.add(base + h * Wo + w)
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+WORKLOAD_CASES = []
+for _name, (_pr, _dts) in workloads.WORKLOADS.items():
+    for _dt in sorted(set(_dts) | {"f32"}):
+        WORKLOAD_CASES.append((_name, _dt))
+
+
+@pytest.mark.parametrize("name,dtype", WORKLOAD_CASES)
+def test_workload_sampled(name, dtype):
+    """Full-size workload, default plan (as benchmarked), sampled outputs.
+    fp32 runs of the fp16/bf16 workloads check indexing at a tolerance where
+    a single misplaced tap would show."""
+    pr, _ = workloads.WORKLOADS[name]
+    print("workload", name, dtype, flush=True)
+    inp = workloads.generate(pr, dtype, seed=0)
+    got = run_gpu(pr, inp)
+    shape = tuple(got.shape)
+    idx = sample_indices(shape, 4096, seed=11)
+    ref = oracle.forward_points(inp["x"], inp["offset"], inp["mask"], inp["weight"],
+                                inp["bias"], idx, **pr.attrs())
+    g = got.reshape(-1)[torch.from_numpy(idx)].double().numpy()
+    # RMS of the whole output from the GPU result (the fp32 rule's scale floor)
+    rms = float(got.double().pow(2).mean().sqrt())
+    ok, err, bound = within_tolerance(g, ref, dtype, rms=rms)
+    assert ok, (name, dtype, error_report(g, ref), float((err / bound).max()))
+    assert torch.isfinite(got).all()
