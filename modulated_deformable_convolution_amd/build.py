@@ -52,6 +52,10 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    # Every symbol must resolve (a kernel whose host stub went missing shows
+    # up here as an undefined symbol, not later at import).
+    import ctypes
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     os.replace(tmp, LIBRARY)
     if verbose:
         print("built", LIBRARY)

@@ -126,7 +126,13 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         range_of(bias, bias ? size_t(p.Co) * e : 0),
     };
     const Range out_r = range_of(out, size_t(p.N * p.Co * p.P) * e);
-    const Range ws_r = range_of(workspace, plan.path == Path::GatherGemm ? plan.ws_bytes : 0);
+    // the workspace layout starts at the caller's pointer aligned up to kAlign
+    char *ws = nullptr;
+    if (plan.path == Path::GatherGemm) {
+        const uintptr_t raw = reinterpret_cast<uintptr_t>(workspace);
+        ws = reinterpret_cast<char *>((raw + mdcn::kAlign - 1) / mdcn::kAlign * mdcn::kAlign);
+    }
+    const Range ws_r = range_of(ws, plan.path == Path::GatherGemm ? plan.ws_bytes : 0);
     for (const Range &in : inputs) {
         if (overlap(out_r, in) || overlap(ws_r, in))
             return MDCN_E_ALIAS;
@@ -149,7 +155,6 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         return err == hipSuccess ? MDCN_OK : MDCN_E_LAUNCH;
     }
 
-    char *ws = static_cast<char *>(workspace);
     void *wpack = ws + plan.wpack_off;
     void *xt = ws + plan.xt_off;
     void *col = ws + plan.col_off;
@@ -267,7 +272,7 @@ mdcn_status mdcn_workspace_bytes(const mdcn_op *op, mdcn_dtype dtype, const int6
         if (st != MDCN_OK)
             return st;
         const bool none = plan.path == Path::Depthwise || p.N == 0 || p.P == 0;
-        *bytes = none ? 0 : plan.ws_bytes;
+        *bytes = none ? 0 : mdcn::workspace_request(plan);
         if (min_bytes)
             *min_bytes = none ? 0 : mdcn::min_workspace(p, plan);
         return MDCN_OK;

@@ -10,10 +10,16 @@
 //  - the 16-byte vector of channels c'..c'+VEC-1 at one bilinear corner is a
 //    single contiguous load, and consecutive lanes (consecutive channel
 //    vectors, then taps) read and write consecutive memory;
-//  - the geometry (4 corner indices and 4 weights with the mask folded in)
-//    is computed in fp32 per (tap, pixel) and reused for all VEC channels;
 //  - the GEMM reads both of its operands K-contiguous, which is the register
 //    layout of the MFMA A and B fragments.
+//
+// A workgroup owns tp consecutive output pixels of one image and one group,
+// and kc consecutive taps (all of them unless the geometry table would not fit
+// in 64 KB of LDS).  Phase 1 computes, once per (offset group, tap, pixel), the
+// four corner offsets and the four bilinear weights with the mask folded in
+// (fp32) and keeps them in LDS; phase 2 streams the channel vectors.  A corner off the
+// image gets an offset past the end of the image's buffer range, which the
+// buffer load returns as 0, so phase 2 has no branches.
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,80 +27,189 @@ namespace mdcn {
 
 namespace {
 
+constexpr int kMaxTP = 32;       // output pixels per workgroup (at most)
+constexpr int kThreads = 256;
+constexpr size_t kGeoBytes = 64 * 1024;
+constexpr uint32_t kOffImage = 0x80000000u;   // a byte offset no image reaches
+
 struct GatherArgs {
-    uint32_t total;            // work items: G * cnt * P * K * CV
-    uint32_t CV;               // channel vectors per group: Cg / VEC
-    uint32_t K, P, cnt;
-    int Cg, Cdg, C, H, W, HW, Wo, kw;
+    int Cg, Cdg, C, H, W, Wo, kw, K, P;
     int sh, sw, ph, pw, dh, dw;
-    int offC, mskC;            // channels of offset and mask: 2*DG*K, DG*K
-    int Kg, Kp;
+    int offC, mskC;              // channels of offset and mask: 2*DG*K, DG*K
+    int Kg, Kp, cnt;
+    int tp, tiles;               // pixels per workgroup, pixel tiles per image
+    int kc, kchunks;             // taps per workgroup, tap chunks
+    int nq;                      // offset groups one group's channels can span
 };
 
-template <typename T, int VEC>
-__global__ __launch_bounds__(256) void deform_gather_kernel(const T *__restrict__ xt,
-                                                            const T *__restrict__ off,
-                                                            const T *__restrict__ msk,
-                                                            T *__restrict__ col, GatherArgs a)
+struct Geo {
+    uint32_t off[4];             // byte offsets of the corners within the image
+    float wt[4];
+};
+
+template <typename T>
+__device__ __forceinline__ void vec_fma(float *acc, const uint4 &raw, float w)
 {
-    uint32_t t = blockIdx.x * 256u + threadIdx.x;
-    if (t >= a.total)
-        return;
-    const uint32_t cv = t % a.CV;
-    t /= a.CV;
-    const uint32_t k = t % a.K;
-    t /= a.K;
-    const uint32_t pix = t % a.P;
-    t /= a.P;
-    const uint32_t nl = t % a.cnt;
-    const uint32_t g = t / a.cnt;
+    Vec16<T> v;
+    v.raw = raw;
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::N; ++e)
+        acc[e] = fmaf(w, to_f32(v.e[e]), acc[e]);
+}
 
-    const int c = int(g) * a.Cg + int(cv) * VEC;   // first input channel of this vector
-    const int q = c / a.Cdg;                       // its offset group
-    const int ho = int(pix) / a.Wo, wo = int(pix) - (int(pix) / a.Wo) * a.Wo;
-    const int i = int(k) / a.kw, j = int(k) - (int(k) / a.kw) * a.kw;
+// Buffer resource over `bytes` bytes at `base`, built from scalar copies of
+// its inputs so that it provably lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    void *p = reinterpret_cast<void *>((uint64_t(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, int(n), 0x00020000);
+}
 
-    const size_t ob = (size_t(nl) * a.offC + size_t(q) * 2 * a.K + 2 * k) * a.P + pix;
-    const float oh = to_f32(off[ob]);
-    const float ow = to_f32(off[ob + a.P]);
-    const float m = to_f32(msk[(size_t(nl) * a.mskC + size_t(q) * a.K + k) * a.P + pix]);
-    const Taps tp = make_taps(ho * a.sh - a.ph + i * a.dh, wo * a.sw - a.pw + j * a.dw, oh, ow,
-                              m, a.H, a.W);
-
-    const T *img = xt + size_t(nl) * a.HW * a.C + c;
+// One output vector: VEC channels (c'..c'+VEC-1 of group g) at (pixel p0+pl,
+// tap k0+kl), the four corners read with buffer loads (0 off the image).
+template <typename T, bool VECTOR>
+__device__ __forceinline__ void gather_item(const GatherArgs &a, const Geo *geo,
+                                            __amdgpu_buffer_rsrc_t rs, const char *img,
+                                            T *col_g, int g, int q0, int p0, int k0, int pl,
+                                            int kl, int cv)
+{
+    constexpr int VEC = VECTOR ? 16 / int(sizeof(T)) : 1;
+    const int c = g * a.Cg + cv * VEC;
+    const Geo gd = geo[((c / a.Cdg - q0) * a.kc + kl) * a.tp + pl];
+    const uint32_t cb = uint32_t(c) * uint32_t(sizeof(T));
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
         acc[e] = 0.0f;
+    T *dst = col_g + size_t(p0 + pl) * a.Kp + (k0 + kl) * a.Cg + cv * VEC;
+    if constexpr (VECTOR) {
+        uint4 v[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        if (!tp.valid[s])
-            continue;
-        const T *src = img + size_t(tp.idx[s]) * a.C;
-        if constexpr (VEC == 1) {
-            acc[0] = fmaf(tp.wt[s], to_f32(src[0]), acc[0]);
-        } else {
-            const Vec16<T> v = load16(src);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                acc[e] = fmaf(tp.wt[s], to_f32(v.e[e]), acc[e]);
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t o = gd.off[s] == kOffImage ? kOffImage : gd.off[s] + cb;
+            const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
+            __builtin_memcpy(&v[s], &r, 16);
         }
-    }
-    T *row = col + (size_t(g) * a.cnt + nl) * a.P * a.Kp + size_t(pix) * a.Kp;
-    T *dst = row + k * a.Cg + cv * VEC;
-    if constexpr (VEC == 1) {
-        dst[0] = from_f32<T>(acc[0]);
-    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            vec_fma<T>(acc, v[s], gd.wt[s]);
         Vec16<T> o;
 #pragma unroll
         for (int e = 0; e < VEC; ++e)
             o.e[e] = from_f32<T>(acc[e]);
         store16(dst, o);
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            if (gd.off[s] != kOffImage)
+                acc[0] = fmaf(gd.wt[s],
+                              to_f32(*reinterpret_cast<const T *>(img + gd.off[s] + cb)), acc[0]);
+        dst[0] = from_f32<T>(acc[0]);
     }
-    // The last item of each row zeroes the row's padding [Kg, Kp).
-    if (k == a.K - 1 && cv == a.CV - 1) {
-        for (int kk = a.Kg; kk < a.Kp; ++kk)
-            row[kk] = T(0);
+}
+
+template <typename T, bool VECTOR>
+__global__ __launch_bounds__(kThreads) void deform_gather_kernel(const T *__restrict__ xt,
+                                                                 const T *__restrict__ off,
+                                                                 const T *__restrict__ msk,
+                                                                 T *__restrict__ col, GatherArgs a)
+{
+    constexpr int VEC = VECTOR ? 16 / int(sizeof(T)) : 1;
+    extern __shared__ __attribute__((aligned(16))) char geo_raw[];
+    Geo *geo = reinterpret_cast<Geo *>(geo_raw);
+
+    // block coordinates, kept in scalar registers (the buffer resource built
+    // from them must be provably wave-uniform)
+    uint32_t b = blockIdx.x;
+    const int tile = __builtin_amdgcn_readfirstlane(int(b % uint32_t(a.tiles)));
+    b /= uint32_t(a.tiles);
+    const int kch = __builtin_amdgcn_readfirstlane(int(b % uint32_t(a.kchunks)));
+    b /= uint32_t(a.kchunks);
+    const int nl = __builtin_amdgcn_readfirstlane(int(b % uint32_t(a.cnt)));
+    const int g = __builtin_amdgcn_readfirstlane(int(b / uint32_t(a.cnt)));
+    const int p0 = tile * a.tp;
+    const int np = min(a.tp, a.P - p0);
+    const int k0 = kch * a.kc;
+    const int nk = min(a.kc, a.K - k0);
+    const int q0 = (g * a.Cg) / a.Cdg;                   // offset groups of this group:
+    const int q1 = ((g + 1) * a.Cg - 1) / a.Cdg;         // q0 .. q1
+
+    // Phase 1: geometry of (offset group q0+qq, tap k0+kl, pixel p0+pl)
+    // -> geo[(qq*kc + kl)*tp + pl].
+    const int entries = a.nq * a.kc * a.tp;
+    const uint32_t elem_c = uint32_t(a.C) * uint32_t(sizeof(T));   // bytes per NHWC pixel
+    for (int e = int(threadIdx.x); e < entries; e += kThreads) {
+        const int pl = e % a.tp;
+        const int kl = (e / a.tp) % a.kc;
+        const int q = q0 + e / (a.tp * a.kc);
+        Geo gd;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            gd.off[s] = kOffImage;
+            gd.wt[s] = 0.0f;
+        }
+        if (pl < np && kl < nk && q <= q1) {
+            const int pix = p0 + pl;
+            const int k = k0 + kl;
+            const int ho = pix / a.Wo, wo = pix - (pix / a.Wo) * a.Wo;
+            const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+            const size_t ob = (size_t(nl) * a.offC + size_t(q) * 2 * a.K + 2 * k) * a.P + pix;
+            const float oh = to_f32(off[ob]);
+            const float ow = to_f32(off[ob + a.P]);
+            const float m = to_f32(msk[(size_t(nl) * a.mskC + size_t(q) * a.K + k) * a.P + pix]);
+            const Taps tp = make_taps(ho * a.sh - a.ph + i * a.dh, wo * a.sw - a.pw + j * a.dw,
+                                      oh, ow, m, a.H, a.W);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                gd.off[s] = tp.valid[s] ? uint32_t(tp.idx[s]) * elem_c : kOffImage;
+                gd.wt[s] = tp.wt[s];
+            }
+        }
+        geo[e] = gd;
+    }
+    __syncthreads();
+
+    // Phase 2: items (pixel, tap, channel vector), channel vector fastest, so a
+    // wave writes consecutive 16-byte pieces of one column row.
+    const int CV = a.Cg / VEC;
+    const size_t img_bytes = size_t(a.H) * a.W * elem_c;
+    const char *img = reinterpret_cast<const char *>(xt) + size_t(nl) * img_bytes;
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(img, uint32_t(img_bytes));
+    T *col_g = col + (size_t(g) * a.cnt + nl) * size_t(a.P) * a.Kp;
+
+    if (CV <= kThreads && kThreads % CV == 0) {
+        // Each thread keeps one channel vector and walks (pixel, tap) rows.
+        const int cv = int(threadIdx.x) % CV;
+        const int stride = kThreads / CV;
+        int r = int(threadIdx.x) / CV;                   // row = pl*nk + kl
+        int pl = r / nk, kl = r - (r / nk) * nk;
+        while (pl < np) {
+            gather_item<T, VECTOR>(a, geo, rs, img, col_g, g, q0, p0, k0, pl, kl, cv);
+            kl += stride;
+            while (kl >= nk) {
+                kl -= nk;
+                ++pl;
+            }
+        }
+    } else {
+        const int items = np * nk * CV;
+        for (int it = int(threadIdx.x); it < items; it += kThreads) {
+            const int cv = it % CV;
+            const int kl = (it / CV) % nk;
+            gather_item<T, VECTOR>(a, geo, rs, img, col_g, g, q0, p0, k0, it / (CV * nk), kl, cv);
+        }
+    }
+    // Zero each row's padding [Kg, Kp) (once per row: by the first tap chunk).
+    const int pad = a.Kp - a.Kg;
+    if (kch == 0) {
+        for (int it = int(threadIdx.x); it < np * pad; it += kThreads) {
+            const int pl = it / pad;
+            col_g[size_t(p0 + pl) * a.Kp + a.Kg + it % pad] = T(0);
+        }
     }
 }
 
@@ -105,25 +220,38 @@ hipError_t gather_t(const Problem &p, const Plan &plan, int64_t cnt, const void 
     constexpr int V = 16 / sizeof(T);
     const bool vec = (p.Cg % V == 0) && (p.Cdg % V == 0);
     GatherArgs a;
-    a.CV = uint32_t(vec ? p.Cg / V : p.Cg);
-    a.K = uint32_t(p.K);
-    a.P = uint32_t(p.P);
-    a.cnt = uint32_t(cnt);
-    a.total = uint32_t(uint64_t(p.G) * uint64_t(cnt) * uint64_t(p.P) * uint64_t(p.K) * a.CV);
     a.Cg = int(p.Cg); a.Cdg = int(p.Cdg); a.C = int(p.C);
-    a.H = int(p.H); a.W = int(p.W); a.HW = int(p.H * p.W);
-    a.Wo = int(p.Wo); a.kw = int(p.kw);
+    a.H = int(p.H); a.W = int(p.W); a.Wo = int(p.Wo); a.kw = int(p.kw); a.K = int(p.K);
+    a.P = int(p.P);
     a.sh = int(p.sh); a.sw = int(p.sw); a.ph = int(p.ph); a.pw = int(p.pw);
     a.dh = int(p.dh); a.dw = int(p.dw);
     a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
-    a.Kg = int(p.Kg); a.Kp = int(plan.Kp);
-    const dim3 grid((a.total + 255u) / 256u);
+    a.Kg = int(p.Kg); a.Kp = int(plan.Kp); a.cnt = int(cnt);
+    // offset groups one group's channels can touch (a channel range of length
+    // Cg overlaps at most ceil(Cg / Cdg) + 1 blocks), capped by their count
+    a.nq = int(std::min<int64_t>(p.DG, (p.Cg + p.Cdg - 1) / p.Cdg + 1));
+    // pixels and taps per workgroup: shrink until the geometry table fits
+    int tp = kMaxTP, kc = int(p.K);
+    while (size_t(a.nq) * kc * tp * sizeof(Geo) > kGeoBytes) {
+        if (kc > 1)
+            kc = (kc + 1) / 2;
+        else if (tp > 1)
+            tp /= 2;
+        else
+            return hipErrorInvalidValue;   // excluded by validation (offset groups)
+    }
+    a.tp = tp;
+    a.tiles = int((p.P + tp - 1) / tp);
+    a.kc = kc;
+    a.kchunks = int((p.K + kc - 1) / kc);
+    const size_t lds = size_t(a.nq) * kc * tp * sizeof(Geo);
+    const dim3 grid(unsigned(uint64_t(p.G) * cnt * a.kchunks * a.tiles));
     if (vec)
-        hipLaunchKernelGGL((deform_gather_kernel<T, V>), grid, dim3(256), 0, s,
+        hipLaunchKernelGGL((deform_gather_kernel<T, true>), grid, dim3(kThreads), lds, s,
                            static_cast<const T *>(xt), static_cast<const T *>(offset),
                            static_cast<const T *>(mask), static_cast<T *>(col), a);
     else
-        hipLaunchKernelGGL((deform_gather_kernel<T, 1>), grid, dim3(256), 0, s,
+        hipLaunchKernelGGL((deform_gather_kernel<T, false>), grid, dim3(kThreads), lds, s,
                            static_cast<const T *>(xt), static_cast<const T *>(offset),
                            static_cast<const T *>(mask), static_cast<T *>(col), a);
     return hipGetLastError();

@@ -3,13 +3,13 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
 
 namespace mdcn {
 
 namespace {
 
 constexpr int64_t kMaxPerImage = (int64_t(1) << 31) - 1;   // elements per image tensor
-constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -26,6 +26,31 @@ int64_t mul(int64_t a, int64_t b)
 }
 
 int64_t mul(int64_t a, int64_t b, int64_t c) { return mul(mul(a, b), c); }
+
+// GEMM tile: the tallest tile the group's weight rows fill, then the widest
+// column count that still gives about one workgroup per CU or more.
+// MDCN_GEMM_TILE=<0..5> overrides the choice (for tuning).
+GemmTile choose_gemm_tile(const Problem &p, int64_t chunk)
+{
+    if (const char *env = std::getenv("MDCN_GEMM_TILE")) {
+        const int v = std::atoi(env);
+        if (v >= 0 && v < kGemmTileCount)
+            return static_cast<GemmTile>(v);
+    }
+    const int64_t ncols = chunk * p.P;
+    auto tiles = [&](int64_t bm, int64_t bn) {
+        return p.G * ((p.Mg + bm - 1) / bm) * ((ncols + bn - 1) / bn);
+    };
+    constexpr int64_t kFill = 192;   // workgroups that count as filling the GPU
+    if (p.Mg > 128)
+        return tiles(256, 256) >= kFill ? GemmTile::M256_N256_W2x4 : GemmTile::M256_N128_W4x2;
+    if (p.Mg > 64) {
+        if (tiles(128, 256) >= kFill)
+            return GemmTile::M128_N256_W2x4;
+        return tiles(128, 128) >= kFill ? GemmTile::M128_N128_W2x2 : GemmTile::M128_N64_W2x2;
+    }
+    return GemmTile::M64_N128_W2x2;
+}
 
 }  // namespace
 
@@ -108,7 +133,10 @@ mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[
         return MDCN_E_SHAPE;
     p.P = p.Ho * p.Wo;
     const int64_t kp = round_up(p.Kg, 64);
-    if (mul(p.C, p.H, p.W) > kMaxPerImage || mul(p.Co, p.P) > kMaxPerImage ||
+    // image bytes (per-image buffer ranges are 31-bit) and offset groups per
+    // group (the gather's per-workgroup geometry table holds them all)
+    if (mul(mul(p.C, p.H, p.W), int64_t(p.elem)) > kMaxPerImage ||
+        (p.Cg + p.Cdg - 1) / p.Cdg + 1 > 2048 || mul(p.Co, p.P) > kMaxPerImage ||
         mul(off[1], p.P) > kMaxPerImage || mul(p.G, p.P, kp) > kMaxPerImage ||
         mul(p.Co, kp) > kMaxPerImage)
         return MDCN_E_SHAPE;
@@ -159,20 +187,25 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
     // Default chunk: as many images as fit a 256 MiB column buffer, at least
     // one; also keep every launch's element count within 32-bit indexing.
     int64_t by_budget = int64_t(kColumnBudget / std::max<size_t>(plan.col_bytes_per_image, 1));
-    int64_t by_index = kMaxPerImage / std::max<int64_t>(p.G * std::max<int64_t>(p.P, 1) * plan.Kp, 1);
+    // (byte offsets within one launch's columns must fit in 31 bits)
+    int64_t by_index = kMaxPerImage /
+                       std::max<int64_t>(p.G * std::max<int64_t>(p.P, 1) * plan.Kp * int64_t(p.elem), 1);
     int64_t chunk = std::max<int64_t>(1, std::min<int64_t>({std::max<int64_t>(p.N, 1),
                                                            by_budget, by_index}));
     const size_t per_image = plan.xt_bytes_per_image + plan.col_bytes_per_image;
     if (!default_sizing) {
-        if (workspace_bytes < plan.wpack_bytes + per_image)
+        // kAlign bytes may be lost to aligning the caller's pointer
+        if (workspace_bytes < kAlign + plan.wpack_bytes + per_image)
             return MDCN_E_WORKSPACE;
-        int64_t fit = int64_t((workspace_bytes - plan.wpack_bytes) / per_image);
+        int64_t fit = int64_t((workspace_bytes - kAlign - plan.wpack_bytes) / per_image);
         chunk = std::max<int64_t>(1, std::min(chunk, fit));
     }
     plan.chunk = chunk;
+    plan.gemm_tile = choose_gemm_tile(p, chunk);
     plan.xt_off = plan.wpack_bytes;
     plan.col_off = plan.xt_off + size_t(chunk) * plan.xt_bytes_per_image;
     plan.ws_bytes = plan.col_off + size_t(chunk) * plan.col_bytes_per_image;
+    // the caller's pointer is aligned up to kAlign inside the library
     *out = plan;
     return MDCN_OK;
 }
@@ -182,7 +215,14 @@ size_t min_workspace(const Problem &p, const Plan &plan)
     (void)p;
     if (plan.path == Path::Depthwise)
         return 0;
-    return plan.wpack_bytes + plan.xt_bytes_per_image + plan.col_bytes_per_image;
+    return kAlign + plan.wpack_bytes + plan.xt_bytes_per_image + plan.col_bytes_per_image;
+}
+
+size_t workspace_request(const Plan &plan)
+{
+    if (plan.path == Path::Depthwise)
+        return 0;
+    return kAlign + plan.ws_bytes;
 }
 
 }  // namespace mdcn

@@ -36,6 +36,18 @@ struct Problem {
 
 enum class Path { GatherGemm, Depthwise };
 
+// Workgroup tile of the GEMM (rows of the packed weight x columns) and its
+// wave grid; every wave owns a block of 32x32 accumulator tiles.
+enum class GemmTile : int {
+    M256_N256_W2x4 = 0,
+    M256_N128_W4x2 = 1,
+    M128_N256_W2x4 = 2,
+    M128_N128_W2x2 = 3,
+    M128_N64_W2x2 = 4,
+    M64_N128_W2x2 = 5,
+};
+constexpr int kGemmTileCount = 6;
+
 // Workspace layout of the gather + GEMM path (all offsets 256-byte aligned):
 //   [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
 struct Plan {
@@ -46,9 +58,11 @@ struct Plan {
     size_t xt_off, xt_bytes_per_image;
     size_t col_off, col_bytes_per_image;
     size_t ws_bytes;             // bytes this plan uses
+    GemmTile gemm_tile;
 };
 
 constexpr size_t kColumnBudget = size_t(256) << 20;   // default column-buffer cap
+constexpr size_t kAlign = 256;                         // workspace sub-buffer alignment
 constexpr int64_t kMaxCoord = int64_t(1) << 24;        // spatial extents and anchors
 
 size_t dtype_size(mdcn_dtype t);
@@ -62,5 +76,7 @@ mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out);
 mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
                       bool default_sizing, Plan *out);
 size_t min_workspace(const Problem &p, const Plan &plan);
+// Bytes to ask the caller for: the plan's layout plus alignment slack.
+size_t workspace_request(const Plan &plan);
 
 }  // namespace mdcn

@@ -35,6 +35,46 @@ __global__ __launch_bounds__(256) void to_nhwc_kernel(const T *__restrict__ x, T
     }
 }
 
+// The same transpose with 16-byte global accesses on both sides (pixels
+// along the load, channels along the store); requires C and H*W to be
+// multiples of the vector width.
+template <typename T>
+__global__ __launch_bounds__(256) void to_nhwc_vec_kernel(const T *__restrict__ x,
+                                                          T *__restrict__ xt, int C, int HW)
+{
+    constexpr int V = 16 / sizeof(T);
+    constexpr int NV = kTile / V;                      // vectors per tile row
+    __shared__ T tile[kTile][kTile + 1];
+    const int p0 = blockIdx.x * kTile;
+    const int c0 = blockIdx.y * kTile;
+    const size_t img = size_t(blockIdx.z) * size_t(C) * size_t(HW);
+    const T *src = x + img;
+    T *dst = xt + img;
+    for (int v = threadIdx.x; v < kTile * NV; v += 256) {
+        const int r = v / NV, pv = (v % NV) * V;
+        const int c = c0 + r, p = p0 + pv;
+        Vec16<T> val;
+        val.raw = make_uint4(0u, 0u, 0u, 0u);
+        if (c < C && p < HW)
+            val = load16(src + size_t(c) * HW + p);
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            tile[r][pv + e] = val.e[e];
+    }
+    __syncthreads();
+    for (int v = threadIdx.x; v < kTile * NV; v += 256) {
+        const int r = v / NV, cv = (v % NV) * V;
+        const int p = p0 + r, c = c0 + cv;
+        if (p < HW && c < C) {
+            Vec16<T> val;
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                val.e[e] = tile[cv + e][r];
+            store16(dst + size_t(p) * C + c, val);
+        }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void pack_weight_kernel(const T *__restrict__ w,
                                                           T *__restrict__ wp, int total, int Kp,
@@ -63,9 +103,16 @@ hipError_t to_nhwc_t(const Problem &p, int64_t cnt, const void *x, void *xt, hip
     for (int64_t n0 = 0; n0 < cnt; n0 += 65535) {
         grid.z = unsigned(std::min<int64_t>(65535, cnt - n0));
         const size_t off = size_t(n0) * size_t(p.C) * size_t(HW);
-        hipLaunchKernelGGL(to_nhwc_kernel<T>, grid, dim3(256), 0, s,
-                           static_cast<const T *>(x) + off, static_cast<T *>(xt) + off,
-                           int(p.C), HW);
+        constexpr int V = 16 / sizeof(T);
+        if (p.C % V == 0 && HW % V == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+            reinterpret_cast<uintptr_t>(xt) % 16 == 0)
+            hipLaunchKernelGGL(to_nhwc_vec_kernel<T>, grid, dim3(256), 0, s,
+                               static_cast<const T *>(x) + off, static_cast<T *>(xt) + off,
+                               int(p.C), HW);
+        else
+            hipLaunchKernelGGL(to_nhwc_kernel<T>, grid, dim3(256), 0, s,
+                               static_cast<const T *>(x) + off, static_cast<T *>(xt) + off,
+                               int(p.C), HW);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

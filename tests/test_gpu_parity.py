@@ -38,6 +38,13 @@ SMALL = {
     # depthwise with a channel multiplier of 2 and 3 offset groups.
     "depthwise_mult2": Problem(N=2, C=24, Co=48, H=13, W=13, groups=24, deformable_groups=3,
                                offset_dist=("uniform", 8.0), mask_dist=("uniform_zeros", 0.1)),
+    # depthwise: odd offset-group width (one staged plane per workgroup) and a
+    # channel multiplier of 6 (two passes of at most 4 outputs per plane)
+    "depthwise_mult6_odd": Problem(N=2, C=9, Co=54, H=11, W=7, groups=9, deformable_groups=3,
+                                   offset_dist=("uniform", 5.0), mask_dist=("uniform_zeros", 0.1)),
+    # depthwise plane too large for LDS: the plain kernel
+    "depthwise_large_plane": Problem(N=1, C=4, Co=4, H=150, W=150, groups=4,
+                                     offset_dist=("uniform", 20.0)),
     "kernel_1x1": Problem(N=2, C=16, Co=24, H=9, W=10, kh=1, kw=1, padding=(0, 0),
                           offset_dist=("normal", 2.0)),
     "kernel_5x5": Problem(N=1, C=16, Co=16, H=12, W=12, kh=5, kw=5, padding=(2, 2)),
@@ -168,6 +175,32 @@ def test_traced_forward_matches_and_records():
     assert all(ms >= 0 for _, ms in tr.read())
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_unaligned_buffers(dtype):
+    """x, out and the workspace at addresses that are not 16-byte aligned."""
+    pr = SMALL["multi_tile_dg2"]
+    inp = workloads.generate(pr, dtype, seed=13)
+    g = to_dev(inp)
+    op = make_op(pr)
+    shift = 1                                  # one element
+    xs = torch.empty(inp["x"].numel() + shift, dtype=g["x"].dtype, device=DEV)
+    x = xs[shift:].view(inp["x"].shape)
+    x.copy_(g["x"])
+    code = mdcn.dtype_code(x.dtype)
+    dims = mdcn.dims_of(x, g["offset"], g["mask"], g["weight"])
+    shape = mdcn.mdcn_output_shape(op, dims)
+    n_out = int(np.prod(shape))
+    outs = torch.empty(n_out + shift, dtype=x.dtype, device=DEV)
+    out = outs[shift:].view(shape)
+    nbytes, _ = mdcn.mdcn_workspace_bytes(op, code, dims)
+    ws = torch.empty(nbytes + 8, dtype=torch.uint8, device=DEV)[3:]
+    mdcn.forward(op, x, g["offset"], g["mask"], g["weight"], g["bias"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle_full(pr, inp)
+    ok, err, bound = within_tolerance(out.cpu().double().numpy(), ref, dtype)
+    assert ok, error_report(out.cpu().double().numpy(), ref)
+
+
 def test_repeatable():
     pr = SMALL["grouped_strided"]
     inp = workloads.generate(pr, "f32", seed=7)
@@ -227,3 +260,22 @@ def test_workload_sampled(name, dtype):
     ok, err, bound = within_tolerance(g, ref, dtype, rms=rms)
     assert ok, (name, dtype, error_report(g, ref), float((err / bound).max()))
     assert torch.isfinite(got).all()
+
+
+# ---------------------------------------------------------------- every GEMM tile shape
+
+GEMM_TILES = range(6)
+
+
+@pytest.mark.parametrize("tile", GEMM_TILES)
+@pytest.mark.parametrize("name,dtype", [("multi_tile_dg2", "f16"), ("multi_tile_dg2", "f32"),
+                                        ("grouped_strided", "bf16"), ("odd_channels", "f16")])
+def test_every_gemm_tile(tile, name, dtype, monkeypatch):
+    """The planner's tile override (MDCN_GEMM_TILE) forces each GEMM tile shape."""
+    monkeypatch.setenv("MDCN_GEMM_TILE", str(tile))
+    pr = SMALL[name]
+    inp = workloads.generate(pr, dtype, seed=12)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_GATHER_GEMM).double().numpy()
+    ref = oracle_full(pr, inp)
+    ok, err, bound = within_tolerance(got, ref, dtype)
+    assert ok, (tile, name, dtype, error_report(got, ref))
