@@ -29,6 +29,27 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
 
+# HBM traffic per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (scaled by 2.0 / 1.0, the factors a plain copy of known size gives; see
+# profiles/*memory_counters.md), valid only for the kernel sources they were
+# taken on (sha256 of the listed files, first 16 hex digits).
+MEASURED_TRAFFIC = {
+    ("gemm_bias", "ocdnet_n4_c256_160x160", "f16"): {
+        "bytes": (119907 * 2 + 25600) * 1024,
+        "sources": ("gemm.hip", "device_common.h", "plan.cpp"),
+        "sha": "2035032fa30fa41e",
+    },
+}
+
+
+def sources_sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "modulated_deformable_convolution_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def kernel_model(pr, dtype, plan_chunk):
     """Algorithmic bytes and flops of one launch of each kernel, for a launch
@@ -79,6 +100,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-mebibyte device buffer --steps times (a plain copy "
+                         "of known size, to scale memory-traffic counters) and exit")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -91,6 +115,20 @@ def main(argv=None) -> int:
     import numpy as np
     import torch
     from modulated_deformable_convolution_amd import mdcn, workloads
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes": n, "steps": args.steps, "ms": dt * 1e3,
+                          "gbs_read_plus_write": 2 * n / dt / 1e9}))
+        return 0
 
     if not os.path.exists(mdcn.LIBRARY):
         from modulated_deformable_convolution_amd import build
@@ -170,6 +208,9 @@ def main(argv=None) -> int:
         roofline = dict(bound="hbm", achieved=round(dk["gbs"], 1), peak=HBM_PEAK_GBS,
                         unit="GB/s", frac=round(dk["gbs"] / HBM_PEAK_GBS, 4), traffic=None)
     roofline["kernel"] = dominant
+    meas = MEASURED_TRAFFIC.get((dominant, args.workload, dtype))
+    if meas and sources_sha(meas["sources"]) == meas["sha"]:
+        roofline["traffic"] = meas["bytes"]
 
     flops = pr.flops()
     value = flops / (ms_per_step * 1e-3) / 1e9

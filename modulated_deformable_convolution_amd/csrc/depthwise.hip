@@ -18,10 +18,16 @@
 // -1 <= h0 <= H-1 and -1 <= w0 <= W-1 reads inside the staged plane; any other
 // sample is entirely off the image and contributes 0.
 //
+// Taps are branch-free: a sample entirely off the image reads a safe address
+// with factor 0.  With one output channel per input channel and 3x3 taps
+// (the common case) the nine weights are loaded once per workgroup.
+//
 // Workgroups are ordered so that those of one image run on one XCD: the
 // image's offsets and masks, read by every channel block, stay in that L2.
 // When a plane does not fit in LDS, a plain kernel reading x from global
 // memory is used instead.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -42,7 +48,7 @@ constexpr int kStagedThreads = 512;
 constexpr int kMaxMg = 4;                    // output channels per input channel per pass
 constexpr size_t kLdsBytes = 160 * 1024;
 
-template <typename T, int CB>
+template <typename T, int CB, int KT, int UP, bool MG1>
 __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
     const T *__restrict__ x, const T *__restrict__ off, const T *__restrict__ msk,
     const T *__restrict__ w, const T *__restrict__ bias, T *__restrict__ out, DwArgs a)
@@ -70,67 +76,133 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
     }
     __syncthreads();
 
-    // Weights and bias of the workgroup's output channels (uniform).
     const int q = c0 / a.Cdg;                        // every staged channel is in block q
-    for (int m0 = 0; m0 < a.Mg; m0 += kMaxMg) {
-        const int nm = min(kMaxMg, a.Mg - m0);
-        for (int pix = int(threadIdx.x); pix < a.P; pix += kStagedThreads) {
-            const int ho = pix / a.Wo, wo = pix - (pix / a.Wo) * a.Wo;
-            const T *offp = off + (size_t(n) * a.offC + size_t(q) * 2 * a.K) * a.P + pix;
-            const T *mskp = msk + (size_t(n) * a.mskC + size_t(q) * a.K) * a.P + pix;
-            float acc[CB][kMaxMg];
+    // Weights of the workgroup's output channels, when known to be few.
+    float wreg[CB][KT > 0 ? KT : 1];
+    if constexpr (MG1 && KT > 0) {
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int mm = 0; mm < kMaxMg; ++mm)
-                    acc[cb][mm] = 0.0f;
-            for (int k = 0; k < a.K; ++k) {
-                const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
-                const float oh = to_f32(offp[size_t(2 * k) * a.P]);
-                const float ow = to_f32(offp[size_t(2 * k + 1) * a.P]);
-                const float m = to_f32(mskp[size_t(k) * a.P]);
+            for (int k = 0; k < KT; ++k)
+                wreg[cb][k] = to_f32(w[size_t(min(c0 + cb, a.C - 1)) * KT + k]);
+    }
+    const int mg_pass = MG1 ? 1 : kMaxMg;
+    for (int m0 = 0; m0 < a.Mg; m0 += mg_pass) {
+        const int nm = MG1 ? 1 : min(kMaxMg, a.Mg - m0);
+        // Each thread takes UP pixels at a time (kStagedThreads apart), so that
+        // the offsets and masks of all of them are in flight together.
+        for (int pbase = int(threadIdx.x); pbase < a.P; pbase += UP * kStagedThreads) {
+            float acc[UP][CB][kMaxMg];
+#pragma unroll
+            for (int u = 0; u < UP; ++u)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int mm = 0; mm < kMaxMg; ++mm)
+                        acc[u][cb][mm] = 0.0f;
+            // Per pixel slot: the anchor (top-left tap position without offset),
+            // one division per pixel.  A slot past the end works on pixel 0 and
+            // stores nothing.
+            int pix_u[UP], ah[UP], aw[UP];
+#pragma unroll
+            for (int u = 0; u < UP; ++u) {
+                const int pix = pbase + u * kStagedThreads < a.P ? pbase + u * kStagedThreads : 0;
+                const int ho = pix / a.Wo;
+                pix_u[u] = pix;
+                ah[u] = ho * a.sh - a.ph;
+                aw[u] = (pix - ho * a.Wo) * a.sw - a.pw;
+            }
+            // One tap: sample the staged planes at anchor + tap offset + the
+            // learned offset, and accumulate into slot u.  Branch-free: a sample
+            // entirely off the image reads staged entry 0 with factor 0.
+            auto tap = [&](int u, int k, int th, int tw, float oh, float ow, float m) {
                 const float lim = 33554432.0f;       // 2^25: farther is off any image
-                if (!(fabsf(oh) <= lim && fabsf(ow) <= lim))
-                    continue;
-                const float fh = floorf(oh), fw = floorf(ow);
-                const int h0 = ho * a.sh - a.ph + i * a.dh + int(fh);
-                const int w0 = wo * a.sw - a.pw + j * a.dw + int(fw);
-                if (h0 < -1 || h0 >= a.H || w0 < -1 || w0 >= a.W)
-                    continue;                         // all four corners off the image
-                const float ly = oh - fh, lx = ow - fw;
+                const bool fin = fabsf(oh) <= lim && fabsf(ow) <= lim;
+                const float fh = fin ? floorf(oh) : 0.0f, fw = fin ? floorf(ow) : 0.0f;
+                const int h0 = ah[u] + th + int(fh);
+                const int w0 = aw[u] + tw + int(fw);
+                const bool ok = fin && h0 >= -1 && h0 < a.H && w0 >= -1 && w0 < a.W;
+                // fractions in [0, 1) (0 for a non-finite or huge offset, so
+                // that every weight stays finite and the factor 0 gives 0)
+                const float ly = fin ? oh - fh : 0.0f, lx = fin ? ow - fw : 0.0f;
                 const float hy = 1.0f - ly, hx = 1.0f - lx;
+                const float fac = ok ? m : 0.0f;
                 const float w00 = hy * hx, w10 = ly * hx, w01 = hy * lx, w11 = ly * lx;
-                const int idx = (h0 + 1) * PW + (w0 + 1);
+                const int idx = ok ? (h0 + 1) * PW + (w0 + 1) : 0;
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
-                    if (cb >= ncb)
-                        break;
                     const float2 left = planes[cb * PL + idx];       // (X[h0][w0], X[h0+1][w0])
                     const float2 right = planes[cb * PL + idx + 1];  // (.., w0+1)
                     float v = w00 * left.x;
                     v = fmaf(w10, left.y, v);
                     v = fmaf(w01, right.x, v);
                     v = fmaf(w11, right.y, v);
-                    v *= m;
-                    const int co = (c0 + cb) * a.Mg + m0;
+                    v *= fac;
+                    if constexpr (MG1 && KT > 0) {
+                        acc[u][cb][0] = fmaf(wreg[cb][k], v, acc[u][cb][0]);
+                    } else {
+                        const int co = min(c0 + cb, a.C - 1) * a.Mg + m0;
 #pragma unroll
-                    for (int mm = 0; mm < kMaxMg; ++mm)
-                        if (mm < nm)
-                            acc[cb][mm] = fmaf(to_f32(w[size_t(co + mm) * a.K + k]), v,
-                                               acc[cb][mm]);
+                        for (int mm = 0; mm < kMaxMg; ++mm)
+                            if (mm < nm)
+                                acc[u][cb][mm] = fmaf(to_f32(w[size_t(co + mm) * a.K + k]), v,
+                                                      acc[u][cb][mm]);
+                    }
+                }
+            };
+            if constexpr (KT > 0) {
+                // 3x3 taps: tap rows/columns are compile-time, all of the
+                // pixels' offsets and masks are in flight at once
+                float oh[UP][KT], ow[UP][KT], mk[UP][KT];
+#pragma unroll
+                for (int u = 0; u < UP; ++u) {
+                    const T *offp = off + (size_t(n) * a.offC + size_t(q) * 2 * KT) * a.P + pix_u[u];
+                    const T *mskp = msk + (size_t(n) * a.mskC + size_t(q) * KT) * a.P + pix_u[u];
+#pragma unroll
+                    for (int k = 0; k < KT; ++k) {
+                        oh[u][k] = to_f32(offp[size_t(2 * k) * a.P]);
+                        ow[u][k] = to_f32(offp[size_t(2 * k + 1) * a.P]);
+                        mk[u][k] = to_f32(mskp[size_t(k) * a.P]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < UP; ++u)
+#pragma unroll
+                    for (int k = 0; k < KT; ++k)
+                        tap(u, k, (k / 3) * a.dh, (k % 3) * a.dw, oh[u][k], ow[u][k], mk[u][k]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < UP; ++u) {
+                    const T *offp = off + (size_t(n) * a.offC + size_t(q) * 2 * a.K) * a.P + pix_u[u];
+                    const T *mskp = msk + (size_t(n) * a.mskC + size_t(q) * a.K) * a.P + pix_u[u];
+                    int i = 0, j = 0;
+                    for (int k = 0; k < a.K; ++k) {
+                        tap(u, k, i * a.dh, j * a.dw, to_f32(offp[size_t(2 * k) * a.P]),
+                            to_f32(offp[size_t(2 * k + 1) * a.P]), to_f32(mskp[size_t(k) * a.P]));
+                        if (++j == a.kw) {
+                            j = 0;
+                            ++i;
+                        }
+                    }
                 }
             }
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                if (cb >= ncb)
+            for (int u = 0; u < UP; ++u) {
+                const int pix = pbase + u * kStagedThreads;
+                if (pix >= a.P)
                     break;
 #pragma unroll
-                for (int mm = 0; mm < kMaxMg; ++mm) {
-                    if (mm >= nm)
+                for (int cb = 0; cb < CB; ++cb) {
+                    if (cb >= ncb)
                         break;
-                    const int co = (c0 + cb) * a.Mg + m0 + mm;
-                    const float b = a.has_bias ? to_f32(bias[co]) : 0.0f;
-                    out[(size_t(n) * a.Co + co) * a.P + pix] = from_f32<T>(acc[cb][mm] + b);
+#pragma unroll
+                    for (int mm = 0; mm < kMaxMg; ++mm) {
+                        if (mm >= nm)
+                            break;
+                        const int co = (c0 + cb) * a.Mg + m0 + mm;
+                        const float b = a.has_bias ? to_f32(bias[co]) : 0.0f;
+                        out[(size_t(n) * a.Co + co) * a.P + pix] = from_f32<T>(acc[u][cb][mm] + b);
+                    }
                 }
             }
         }
@@ -179,6 +251,26 @@ __global__ __launch_bounds__(256) void depthwise_kernel(const T *__restrict__ x,
 }
 
 template <typename T>
+using DwKernel = void (*)(const T *, const T *, const T *, const T *, const T *, T *, DwArgs);
+
+// The staged kernel instance for (planes, compile-time taps, pixels per
+// thread, exactly one output per input channel).
+template <typename T>
+DwKernel<T> staged_fn(int cb, int kt, int up, bool mg1)
+{
+#define MDCN_DW_PICK(CB_, KT_, UP_)                                                            \
+    if (cb == CB_ && kt == KT_ && up == UP_)                                                   \
+        return mg1 ? &depthwise_staged_kernel<T, CB_, KT_, UP_, true>                          \
+                   : &depthwise_staged_kernel<T, CB_, KT_, UP_, false>;
+    MDCN_DW_PICK(1, 9, 1) MDCN_DW_PICK(1, 9, 2) MDCN_DW_PICK(1, 9, 4)
+    MDCN_DW_PICK(1, 0, 1) MDCN_DW_PICK(1, 0, 2) MDCN_DW_PICK(1, 0, 4)
+    MDCN_DW_PICK(2, 9, 1) MDCN_DW_PICK(2, 9, 2) MDCN_DW_PICK(2, 9, 4)
+    MDCN_DW_PICK(2, 0, 1) MDCN_DW_PICK(2, 0, 2) MDCN_DW_PICK(2, 0, 4)
+#undef MDCN_DW_PICK
+    return nullptr;
+}
+
+template <typename T>
 hipError_t depthwise_t(const Problem &p, const void *x, const void *offset, const void *mask,
                        const void *weight, const void *bias, void *out, hipStream_t s)
 {
@@ -192,29 +284,37 @@ hipError_t depthwise_t(const Problem &p, const void *x, const void *offset, cons
     a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
     a.has_bias = bias != nullptr;
     const size_t plane_bytes = size_t(p.H + 1) * size_t(p.W + 2) * sizeof(float2);
-    // Two planes per workgroup when they fit and share an offset group.
-    const int cb = (2 * plane_bytes <= kLdsBytes && p.Cdg % 2 == 0) ? 2 : 1;
+    // Two planes per workgroup when they fit and share an offset group (each
+    // workgroup reads all of its image's offsets and masks, so sharing them
+    // between planes halves that traffic), two pixels per thread in flight.
+    // MDCN_DW_PLANES=1|2 and MDCN_DW_PIXELS=1|2|4 override (for tuning).
+    int cb = (p.Cdg % 2 == 0 && 2 * plane_bytes <= kLdsBytes) ? 2 : 1, up = 2;
+    if (const char *env = std::getenv("MDCN_DW_PLANES")) {
+        const int v = std::atoi(env);
+        if (v == 1)
+            cb = 1;
+        else if (v == 2 && p.Cdg % 2 == 0 && 2 * plane_bytes <= kLdsBytes)
+            cb = 2;
+    }
+    if (const char *env = std::getenv("MDCN_DW_PIXELS")) {
+        const int v = std::atoi(env);
+        if (v == 1 || v == 2 || v == 4)
+            up = v;
+    }
     if (cb * plane_bytes <= kLdsBytes) {
         a.cblocks = int((p.C + cb - 1) / cb);
         const dim3 grid(unsigned(uint64_t(p.N) * a.cblocks));
         const size_t lds = cb * plane_bytes;
-        const void *fn = cb == 2
-                             ? reinterpret_cast<const void *>(&depthwise_staged_kernel<T, 2>)
-                             : reinterpret_cast<const void *>(&depthwise_staged_kernel<T, 1>);
-        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) !=
-            hipSuccess) {
+        const int kt = (p.kh == 3 && p.kw == 3) ? 9 : 0;   // compile-time 3x3 taps
+        const DwKernel<T> fn = staged_fn<T>(cb, kt, up, p.Mg == 1);
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess) {
             (void)hipGetLastError();       // clear it; use the plain kernel below
-        } else if (cb == 2) {
-            hipLaunchKernelGGL((depthwise_staged_kernel<T, 2>), grid, dim3(kStagedThreads), lds,
-                               s, static_cast<const T *>(x), static_cast<const T *>(offset),
-                               static_cast<const T *>(mask), static_cast<const T *>(weight),
-                               static_cast<const T *>(bias), static_cast<T *>(out), a);
-            return hipGetLastError();
         } else {
-            hipLaunchKernelGGL((depthwise_staged_kernel<T, 1>), grid, dim3(kStagedThreads), lds,
-                               s, static_cast<const T *>(x), static_cast<const T *>(offset),
-                               static_cast<const T *>(mask), static_cast<const T *>(weight),
-                               static_cast<const T *>(bias), static_cast<T *>(out), a);
+            hipLaunchKernelGGL(fn, grid, dim3(kStagedThreads), lds, s, static_cast<const T *>(x),
+                               static_cast<const T *>(offset), static_cast<const T *>(mask),
+                               static_cast<const T *>(weight), static_cast<const T *>(bias),
+                               static_cast<T *>(out), a);
             return hipGetLastError();
         }
     }

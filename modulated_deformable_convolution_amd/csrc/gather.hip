@@ -13,6 +13,10 @@
 //  - the GEMM reads both of its operands K-contiguous, which is the register
 //    layout of the MFMA A and B fragments.
 //
+// Workgroups are numbered so that consecutive pixel tiles of one image run
+// on the same XCD: the corner reads of a band of output rows then hit a band
+// of input rows in that XCD's L2.
+//
 // A workgroup owns tp consecutive output pixels of one image and one group,
 // and kc consecutive taps (all of them unless the geometry table would not fit
 // in 64 KB of LDS).  Phase 1 computes, once per (offset group, tap, pixel), the
@@ -122,9 +126,11 @@ __global__ __launch_bounds__(kThreads) void deform_gather_kernel(const T *__rest
     extern __shared__ __attribute__((aligned(16))) char geo_raw[];
     Geo *geo = reinterpret_cast<Geo *>(geo_raw);
 
-    // block coordinates, kept in scalar registers (the buffer resource built
-    // from them must be provably wave-uniform)
-    uint32_t b = blockIdx.x;
+    // Block coordinates, kept in scalar registers (the buffer resource built
+    // from them must be provably wave-uniform).  Consecutive logical blocks
+    // (consecutive pixel tiles of one image) run on one XCD, so each XCD's L2
+    // holds a band of rows of the image instead of all of it.
+    uint32_t b = xcd_swizzle(blockIdx.x, gridDim.x);
     const int tile = __builtin_amdgcn_readfirstlane(int(b % uint32_t(a.tiles)));
     b /= uint32_t(a.tiles);
     const int kch = __builtin_amdgcn_readfirstlane(int(b % uint32_t(a.kchunks)));

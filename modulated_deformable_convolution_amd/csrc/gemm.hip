@@ -16,9 +16,10 @@
 // buffer_load_dwordx4 ... lds (no register staging).  Such a wave instruction
 // writes 1 KB of LDS contiguously (lane i at +16*i) and here fetches 8 whole
 // rows: 8 lanes per row, so every request is a full, coalesced line.  In LDS
-// a row is 128 bytes with its 16-byte chunk index XORed with (row % 8); the
-// MFMA fragment read of 32 consecutive rows at one chunk then spreads each
-// group of 8 lanes over 8 distinct bank quads (no conflicts).  Rows past the
+// a row is 128 bytes with its 16-byte chunk index XORed with (row / 2) % 8;
+// the MFMA fragment read of 32 consecutive rows at one chunk then spreads
+// each group of 16 lanes over 16 distinct 16-byte bank groups of a 256-byte
+// LDS line.  Rows past the
 // matrix edge are clamped to a valid row; they only feed accumulator rows or
 // columns that the epilogue never stores.  Two LDS stages: the loads of step
 // s+1 are in flight while the MFMAs of step s run (more stages cost
@@ -84,7 +85,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 // One pipeline step's operand loads of one wave: IPW instructions of 8 tile
 // rows each (A rows first, then B rows).  Lane i of an instruction fetches
-// chunk (i%8) ^ (row%8) of row r0 + i/8, which lands in LDS slot r0*8 + i.
+// chunk (i%8) ^ ((row/2)%8) of row r0 + i/8, which lands in LDS slot r0*8 + i.
 template <int BM, int BN, int NW, int STEP>
 __device__ __forceinline__ void issue_step(char *stage_base, __amdgpu_buffer_rsrc_t ra,
                                            __amdgpu_buffer_rsrc_t rb, const uint32_t *voff,
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
 #pragma unroll
     for (int t = 0; t < IPW; ++t) {
         const int row = (wave * IPW + t) * 8 + (lane >> 3);     // tile row (A rows first)
-        const int chunk = (lane & 7) ^ (row & 7);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
         if (row < BM)
             voff[t] = uint32_t(min(m0 + row, a.Mg - 1)) * row_bytes + chunk * 16;
         else
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
                                          st + 1);
         const char *sA = smem + stage * STAGE_BYTES + (wm * WTM + (lane & 31)) * STEP;
         const char *sB = smem + stage * STAGE_BYTES + (BM + wn * WTN + (lane & 31)) * STEP;
-        const int sw = lane & 7;          // row % 8 of every fragment row of this lane
+        const int sw = (lane >> 1) & 7;   // (row / 2) % 8 of every fragment row of this lane
         const int half = lane >> 5;
 #pragma unroll
         for (int kg = 0; kg < NCH / 2; ++kg) {

@@ -42,6 +42,9 @@ SMALL = {
     # channel multiplier of 6 (two passes of at most 4 outputs per plane)
     "depthwise_mult6_odd": Problem(N=2, C=9, Co=54, H=11, W=7, groups=9, deformable_groups=3,
                                    offset_dist=("uniform", 5.0), mask_dist=("uniform_zeros", 0.1)),
+    # depthwise with a 5x3 kernel (runtime tap count)
+    "depthwise_5x3": Problem(N=2, C=8, Co=8, H=12, W=10, kh=5, kw=3, padding=(2, 1), groups=8,
+                             deformable_groups=2, offset_dist=("normal", 2.0)),
     # depthwise plane too large for LDS: the plain kernel
     "depthwise_large_plane": Problem(N=1, C=4, Co=4, H=150, W=150, groups=4,
                                      offset_dist=("uniform", 20.0)),
@@ -279,3 +282,20 @@ def test_every_gemm_tile(tile, name, dtype, monkeypatch):
     ref = oracle_full(pr, inp)
     ok, err, bound = within_tolerance(got, ref, dtype)
     assert ok, (tile, name, dtype, error_report(got, ref))
+
+
+# ---------------------------------------------------------------- depthwise kernel variants
+
+@pytest.mark.parametrize("planes,pixels", [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4)])
+@pytest.mark.parametrize("name", ["depthwise_mult2", "depthwise_5x3"])
+def test_depthwise_variants(planes, pixels, name, monkeypatch):
+    """The staged depthwise kernel with each planes-per-workgroup and
+    pixels-per-thread setting (MDCN_DW_PLANES / MDCN_DW_PIXELS)."""
+    monkeypatch.setenv("MDCN_DW_PLANES", str(planes))
+    monkeypatch.setenv("MDCN_DW_PIXELS", str(pixels))
+    pr = SMALL[name]
+    inp = workloads.generate(pr, "f32", seed=14)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_DEPTHWISE).double().numpy()
+    ref = oracle_full(pr, inp)
+    ok, err, bound = within_tolerance(got, ref, "f32")
+    assert ok, (planes, pixels, name, error_report(got, ref))
