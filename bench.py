@@ -82,6 +82,10 @@ def kernel_model(pr, dtype, plan_chunk):
         if name == "gemm_bias":
             return dict(bytes=cnt * (col_img + out_img) + pr.Co * Kp * e + bias_bytes,
                         flops=2 * cnt * pr.Co * Kg * P)
+        if name == "fused_gather_gemm":
+            # x (NHWC copy), offsets and masks read once, output written once
+            return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + pr.Co * Kp * e
+                        + bias_bytes, flops=2 * cnt * pr.Co * Kg * P)
         if name == "depthwise_direct":
             return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + w_bytes + bias_bytes,
                         flops=2 * cnt * pr.Co * Kg * P)
@@ -100,6 +104,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", default="auto", choices=["auto", "gather_gemm", "fused",
+                                                       "depthwise"],
+                    help="computation path (default: the library's choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte device buffer --steps times (a plain copy "
                          "of known size, to scale memory-traffic counters) and exit")
@@ -141,7 +148,10 @@ def main(argv=None) -> int:
 
     inp = workloads.generate(pr, dtype, seed=0)
     g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
-    op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups)
+    path = {"auto": mdcn.MDCN_PATH_AUTO, "gather_gemm": mdcn.MDCN_PATH_GATHER_GEMM,
+            "fused": mdcn.MDCN_PATH_FUSED, "depthwise": mdcn.MDCN_PATH_DEPTHWISE}[args.path]
+    op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups,
+                          path=path)
     code = mdcn.dtype_code(g["x"].dtype)
     dims = mdcn.dims_of(g["x"], g["offset"], g["mask"], g["weight"])
     ws_bytes, _ = mdcn.mdcn_workspace_bytes(op, code, dims)
@@ -186,8 +196,8 @@ def main(argv=None) -> int:
         avg_ms = total_ms / count
         launches_per_step = count / args.steps
         cnt = pr.N if name == "depthwise_direct" else (
-            pr.N / max(1, launches_per_step) if name in ("to_nhwc", "deform_gather", "gemm_bias")
-            else 0)
+            pr.N / max(1, launches_per_step)
+            if name in ("to_nhwc", "deform_gather", "gemm_bias", "fused_gather_gemm") else 0)
         m = model(name, cnt)
         kernels[name] = dict(launches_per_step=launches_per_step, avg_ms=avg_ms,
                              ms_per_step=total_ms / args.steps,
@@ -200,7 +210,7 @@ def main(argv=None) -> int:
     peak_tf = MFMA_PEAK_TFLOPS[dtype]
     t_hbm = dk["algo_bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = dk["algo_flops_per_launch"] / (peak_tf * 1e12)
-    uses_mfma = dominant == "gemm_bias"
+    uses_mfma = dominant in ("gemm_bias", "fused_gather_gemm")
     if uses_mfma and t_mfma > t_hbm:
         roofline = dict(bound="mfma", achieved=round(dk["tflops"], 2), peak=peak_tf,
                         unit="TFLOP/s", frac=round(dk["tflops"] / peak_tf, 4), traffic=None)

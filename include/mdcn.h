@@ -84,9 +84,14 @@ typedef enum mdcn_path {
     MDCN_PATH_GATHER_GEMM = 1, /* deformable im2col into the workspace, then a grouped
                                   MFMA GEMM with the bias fused in its epilogue
                                   [plugin guide §五 steps 1-3]                             */
-    MDCN_PATH_DEPTHWISE = 2    /* one direct gather-and-multiply-add kernel; requires
+    MDCN_PATH_DEPTHWISE = 2,   /* one direct gather-and-multiply-add kernel; requires
                                   C/group == 1 [plugin guide §三: group == #outputs is the
                                   depthwise case]                                         */
+    MDCN_PATH_FUSED = 3        /* the gather fused into the MFMA GEMM: the GEMM's B tiles
+                                  are made in LDS from the bilinear samples, with no column
+                                  buffer [plugin guide §五 steps 1-3 without the columns];
+                                  requires C/group to be a multiple of 64 (fp16/bf16) or 32
+                                  (fp32) and C/deformable_group of 32 or 16               */
 } mdcn_path;
 
 typedef struct mdcn_op mdcn_op;
@@ -173,7 +178,8 @@ mdcn_status mdcn_trace_count(const mdcn_trace *trace, int32_t *count);
  * MDCN_E_LAUNCH. */
 mdcn_status mdcn_trace_read(mdcn_trace *trace, int32_t i, int32_t *kernel_id, float *ms);
 
-/* Name of a kernel id ("deform_gather", "gemm_bias", ...); "?" if unknown. */
+/* Name of a kernel id ("deform_gather", "gemm_bias", "fused_gather_gemm", ...);
+ * "?" if unknown. */
 const char *mdcn_kernel_name(int32_t kernel_id);
 
 /* ---- misc ---------------------------------------------------------------- */

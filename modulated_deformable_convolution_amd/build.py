@@ -20,8 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libmdcn.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "prep.hip", "gather.hip", "gemm.hip", "depthwise.hip"]
-HEADERS = ["plan.h", "launch.h", "device_common.h"]
+SOURCES = ["plan.cpp", "api.cpp", "prep.hip", "gather.hip", "gemm.hip", "depthwise.hip",
+           "fused.hip"]
+HEADERS = ["plan.h", "launch.h", "device_common.h", "mfma_common.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

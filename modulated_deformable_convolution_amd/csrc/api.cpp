@@ -109,7 +109,7 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         return MDCN_OK;                 // nothing to compute
     if (!x || !offset || !mask || !weight || !out)
         return MDCN_E_NULL;
-    if (plan.path == Path::GatherGemm) {
+    if (plan.path != Path::Depthwise) {
         if (!workspace)
             return MDCN_E_WORKSPACE;
         st = mdcn::make_plan(op->attrs, p, workspace_bytes, false, &plan);
@@ -128,11 +128,11 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     const Range out_r = range_of(out, size_t(p.N * p.Co * p.P) * e);
     // the workspace layout starts at the caller's pointer aligned up to kAlign
     char *ws = nullptr;
-    if (plan.path == Path::GatherGemm) {
+    if (plan.path != Path::Depthwise) {
         const uintptr_t raw = reinterpret_cast<uintptr_t>(workspace);
         ws = reinterpret_cast<char *>((raw + mdcn::kAlign - 1) / mdcn::kAlign * mdcn::kAlign);
     }
-    const Range ws_r = range_of(ws, plan.path == Path::GatherGemm ? plan.ws_bytes : 0);
+    const Range ws_r = range_of(ws, plan.path != Path::Depthwise ? plan.ws_bytes : 0);
     for (const Range &in : inputs) {
         if (overlap(out_r, in) || overlap(ws_r, in))
             return MDCN_E_ALIAS;
@@ -175,6 +175,14 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         err = rec.run(mdcn::K_TO_NHWC, [&] { return mdcn::launch_to_nhwc(p, cnt, xc, xt, stream); });
         if (err != hipSuccess)
             return MDCN_E_LAUNCH;
+        if (plan.path == Path::Fused) {
+            err = rec.run(mdcn::K_FUSED, [&] {
+                return mdcn::launch_fused(p, plan, cnt, wpack, xt, oc, mc, bias, outc, stream);
+            });
+            if (err != hipSuccess)
+                return MDCN_E_LAUNCH;
+            continue;
+        }
         err = rec.run(mdcn::K_GATHER, [&] {
             return mdcn::launch_gather(p, plan, cnt, xt, oc, mc, col, stream);
         });
@@ -199,7 +207,8 @@ mdcn_status create_impl(const int32_t stride[2], const int32_t padding[2],
     mdcn_status st = mdcn::check_attrs(stride, padding, dilation, group, dgroup);
     if (st != MDCN_OK)
         return st;
-    if (path != MDCN_PATH_AUTO && path != MDCN_PATH_GATHER_GEMM && path != MDCN_PATH_DEPTHWISE)
+    if (path != MDCN_PATH_AUTO && path != MDCN_PATH_GATHER_GEMM &&
+        path != MDCN_PATH_DEPTHWISE && path != MDCN_PATH_FUSED)
         return MDCN_E_PATH;
     mdcn_op *op = new (std::nothrow) mdcn_op;
     if (!op)
@@ -392,6 +401,7 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_GATHER: return "deform_gather";
     case mdcn::K_GEMM: return "gemm_bias";
     case mdcn::K_DEPTHWISE: return "depthwise_direct";
+    case mdcn::K_FUSED: return "fused_gather_gemm";
     }
     return "?";
 }
@@ -434,6 +444,14 @@ mdcn_status mdcn_describe_plan(const mdcn_op *op, mdcn_dtype dtype, const int64_
         if (plan.path == Path::Depthwise)
             std::snprintf(buf, len, "path=depthwise_direct N=%lld C=%lld Co=%lld P=%lld ws=0",
                           (long long)p.N, (long long)p.C, (long long)p.Co, (long long)p.P);
+        else if (plan.path == Path::Fused)
+            std::snprintf(buf, len,
+                          "path=fused chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld tile=%d "
+                          "ws=%zu (wpack=%zu xt/img=%zu)",
+                          (long long)plan.chunk, (long long)p.Kg, (long long)plan.Kp,
+                          (long long)p.G, (long long)p.Mg, (long long)p.P,
+                          int(plan.fused_tile), plan.ws_bytes, plan.wpack_bytes,
+                          plan.xt_bytes_per_image);
         else
             std::snprintf(buf, len,
                           "path=gather_gemm chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld "

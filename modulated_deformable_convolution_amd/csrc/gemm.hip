@@ -23,12 +23,14 @@
 // matrix edge are clamped to a valid row; they only feed accumulator rows or
 // columns that the epilogue never stores.  Two LDS stages: the loads of step
 // s+1 are in flight while the MFMAs of step s run (more stages cost
-// occupancy, which matters more here).
+// occupancy, which matters more here).  Each step's fragments are read into
+// registers before the next step's DMA is issued, so the DMA overlaps the
+// MFMAs instead of delaying the reads.
 //
 //   f16 / bf16: one v_mfma_f32_32x32x16_{f16,bf16} per 16-byte fragment pair;
 //   f32:        four v_mfma_f32_32x32x2_f32 per 16-byte fragment pair.
-#include "device_common.h"
 #include "launch.h"
+#include "mfma_common.h"
 
 namespace mdcn {
 
@@ -40,48 +42,6 @@ struct GemmArgs {
     int has_bias;
     int vec_out;        // 16-byte output stores allowed (P and `out` aligned to them)
 };
-
-template <typename T> struct Mma;
-
-template <> struct Mma<half_t> {
-    static __device__ __forceinline__ float16v step(const uint4 &a, const uint4 &b, float16v c)
-    {
-        half8 av, bv;
-        __builtin_memcpy(&av, &a, 16);
-        __builtin_memcpy(&bv, &b, 16);
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, c, 0, 0, 0);
-    }
-};
-
-template <> struct Mma<bf16_t> {
-    static __device__ __forceinline__ float16v step(const uint4 &a, const uint4 &b, float16v c)
-    {
-        bf16x8 av, bv;
-        __builtin_memcpy(&av, &a, 16);
-        __builtin_memcpy(&bv, &b, 16);
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
-    }
-};
-
-template <> struct Mma<float> {
-    static __device__ __forceinline__ float16v step(const uint4 &a, const uint4 &b, float16v c)
-    {
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
-        return c;
-    }
-};
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Raw buffer resource over `bytes` bytes at `base` (loads past the end read 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes),
-                                             0x00020000);
-}
 
 // One pipeline step's operand loads of one wave: IPW instructions of 8 tile
 // rows each (A rows first, then B rows).  Lane i of an instruction fetches
@@ -167,90 +127,20 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
         const int stage = st & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of step st have landed
         __syncthreads();                 // ... and everyone's; stage^1 is free again
+        StepFrags<FM, FN> f;             // all of step st's fragments, before the DMA
+        load_step_frags<FM, FN>(f, smem + stage * STAGE_BYTES + wm * WTM * STEP,
+                                smem + stage * STAGE_BYTES + (BM + wn * WTN) * STEP, lane);
         if (st + 1 < steps)
             issue_step<BM, BN, NW, STEP>(smem + (stage ^ 1) * STAGE_BYTES, ra, rb, voff, wave,
                                          st + 1);
-        const char *sA = smem + stage * STAGE_BYTES + (wm * WTM + (lane & 31)) * STEP;
-        const char *sB = smem + stage * STAGE_BYTES + (BM + wn * WTN + (lane & 31)) * STEP;
-        const int sw = (lane >> 1) & 7;   // (row / 2) % 8 of every fragment row of this lane
-        const int half = lane >> 5;
-#pragma unroll
-        for (int kg = 0; kg < NCH / 2; ++kg) {
-            const int q = kg * 2 + half;
-            uint4 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const uint4 *>(sA + i * 32 * STEP + (q ^ sw) * 16);
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bf[j] = *reinterpret_cast<const uint4 *>(sB + j * 32 * STEP + (q ^ sw) * 16);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = Mma<T>::step(af[i], bf[j], acc[i][j]);
-        }
+        mfma_step_frags<T, FM, FN>(acc, f);
     }
 
-    // Epilogue, through LDS so that each lane stores 16 contiguous bytes of
-    // an output row.  Per 32-row block of the wave's tile: the fp32
-    // accumulators go to the wave's own LDS slice (row-major), then come back
-    // as vectors along the pixel axis; bias is added in fp32 and the sum
-    // rounded once.  Accumulator register r of lane l in a 32x32 tile holds
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-    constexpr int EV = 16 / sizeof(T);                 // output elements per store
-    constexpr int SROW = WTN + 4;                      // slice row, floats (padded)
-    static_assert(NW * 32 * SROW * 4 <= 2 * STAGE_BYTES, "epilogue slices must fit in LDS");
+    // Epilogue through LDS: bias in fp32, one rounding, 16-byte stores.
+    static_assert(NW * 32 * (WTN + 4) * 4 <= 2 * STAGE_BYTES, "epilogue slices must fit in LDS");
     __syncthreads();                                   // operand stages no longer needed
-    float *slice = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
-    const bool vec_out = a.vec_out != 0;               // vectors never straddle two images
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                slice[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SROW + j * 32 + (lane & 31)] =
-                    acc[i][j][r];
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-        const int mb = m0 + wm * WTM + i * 32;         // first output row of the block
-        const int nb = n0 + wn * WTN;                  // first column of the wave's tile
-        if (vec_out) {
-#pragma unroll
-            for (int it = 0; it < 32 * WTN / EV / 64; ++it) {
-                const int e = it * 64 + lane;
-                const int rl = e / (WTN / EV);
-                const int cl = (e % (WTN / EV)) * EV;
-                const int m = mb + rl, n = nb + cl;
-                if (m < a.Mg && n < a.Ncols) {
-                    const float bv = a.has_bias ? to_f32(bias[size_t(g) * a.Mg + m]) : 0.0f;
-                    const int img = n / a.P;
-                    const int pix = n - img * a.P;
-                    const float *sp = slice + rl * SROW + cl;
-                    Vec16<T> o;
-#pragma unroll
-                    for (int t = 0; t < EV; ++t)
-                        o.e[t] = from_f32<T>(sp[t] + bv);
-                    store16(out + (size_t(img) * a.Co + size_t(g) * a.Mg + m) * a.P + pix, o);
-                }
-            }
-        } else {
-            for (int e = lane; e < 32 * WTN; e += 64) {
-                const int rl = e / WTN, cl = e % WTN;
-                const int m = mb + rl, n = nb + cl;
-                if (m < a.Mg && n < a.Ncols) {
-                    const float bv = a.has_bias ? to_f32(bias[size_t(g) * a.Mg + m]) : 0.0f;
-                    const int img = n / a.P;
-                    const int pix = n - img * a.P;
-                    out[(size_t(img) * a.Co + size_t(g) * a.Mg + m) * a.P + pix] =
-                        from_f32<T>(slice[rl * SROW + cl] + bv);
-                }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-    }
+    const EpilogueArgs e{g, m0, n0, a.Mg, a.Ncols, a.P, a.Co, a.has_bias, a.vec_out};
+    epilogue_store<T, WTM, WTN>(acc, smem, bias, out, e, wm, wn, wave, lane);
 }
 
 template <typename T, int BM, int BN, int WM, int WN>

@@ -15,7 +15,8 @@ enum KernelId : int32_t {
     K_GATHER = 2,
     K_GEMM = 3,
     K_DEPTHWISE = 4,
-    K_COUNT = 5
+    K_FUSED = 5,
+    K_COUNT = 6
 };
 
 // weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
@@ -35,6 +36,12 @@ hipError_t launch_gather(const Problem &p, const Plan &plan, int64_t cnt, const 
 // out[n][g*Mg + m][pix] = sum_kk wpack[g][m][kk] * col[g][n*P + pix][kk] (+ bias).
 hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                        const void *col, const void *bias, void *out, hipStream_t stream);
+
+// Fused deformable gather + grouped GEMM + bias of cnt images:
+// out[n][g*Mg + m][pix] from the packed weight, NHWC x, offset and mask.
+hipError_t launch_fused(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
+                        const void *xt, const void *offset, const void *mask, const void *bias,
+                        void *out, hipStream_t stream);
 
 // Direct depthwise (C/group == 1) forward of all N images.
 hipError_t launch_depthwise(const Problem &p, const void *x, const void *offset,

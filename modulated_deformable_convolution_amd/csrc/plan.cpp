@@ -52,6 +52,26 @@ GemmTile choose_gemm_tile(const Problem &p, int64_t chunk)
     return GemmTile::M64_N128_W2x2;
 }
 
+// Fused tile: as for the GEMM, the tallest tile the group fills, then the
+// widest that still gives about one workgroup per CU.
+// MDCN_FUSED_TILE=<0..3> overrides the choice (for tuning).
+FusedTile choose_fused_tile(const Problem &p, int64_t chunk)
+{
+    if (const char *env = std::getenv("MDCN_FUSED_TILE")) {
+        const int v = std::atoi(env);
+        if (v >= 0 && v < kFusedTileCount)
+            return static_cast<FusedTile>(v);
+    }
+    const int64_t ncols = chunk * p.P;
+    auto tiles = [&](int64_t bm, int64_t bn) {
+        return p.G * ((p.Mg + bm - 1) / bm) * ((ncols + bn - 1) / bn);
+    };
+    constexpr int64_t kFill = 192;
+    if (p.Mg > 128)
+        return tiles(256, 128) >= kFill ? FusedTile::M256_N128 : FusedTile::M256_N64;
+    return tiles(128, 128) >= kFill ? FusedTile::M128_N128 : FusedTile::M128_N64;
+}
+
 }  // namespace
 
 size_t dtype_size(mdcn_dtype t)
@@ -149,11 +169,25 @@ mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[
     return MDCN_OK;
 }
 
+bool fused_eligible(const Problem &p)
+{
+    const int64_t se = 128 / int64_t(p.elem);      // K elements per 128-byte step
+    const int64_t ev = 16 / int64_t(p.elem);       // elements per 16-byte chunk
+    const int64_t img_bytes = p.C * p.H * p.W * int64_t(p.elem);
+    return p.Cg % se == 0 && p.Cdg % (4 * ev) == 0 && img_bytes <= kMaxPerImage;
+}
+
 mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
 {
     switch (a.path) {
     case MDCN_PATH_AUTO:
-        *out = (p.Cg == 1) ? Path::Depthwise : Path::GatherGemm;
+        *out = (p.Cg == 1) ? Path::Depthwise
+                           : (fused_eligible(p) ? Path::Fused : Path::GatherGemm);
+        return MDCN_OK;
+    case MDCN_PATH_FUSED:
+        if (!fused_eligible(p))
+            return MDCN_E_PATH;
+        *out = Path::Fused;
         return MDCN_OK;
     case MDCN_PATH_GATHER_GEMM:
         *out = Path::GatherGemm;
@@ -181,6 +215,30 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
     }
     plan.Kp = round_up(p.Kg, 64);
     plan.wpack_off = 0;
+    if (plan.path == Path::Fused) {
+        // Workspace: packed weight + the chunk's images in NHWC.  A chunk's
+        // NHWC bytes stay below 2^31 (one buffer range) and within 512 MiB.
+        plan.wpack_bytes = align_up(size_t(p.G * p.Mg * plan.Kp) * p.elem, kAlign);
+        plan.xt_bytes_per_image = align_up(size_t(p.H * p.W * p.C) * p.elem, kAlign);
+        plan.col_bytes_per_image = 0;
+        const int64_t img = int64_t(plan.xt_bytes_per_image);
+        int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(
+            {std::max<int64_t>(p.N, 1), kMaxPerImage / img, int64_t(kFusedBudget) / img}));
+        if (!default_sizing) {
+            if (workspace_bytes < kAlign + plan.wpack_bytes + size_t(img))
+                return MDCN_E_WORKSPACE;
+            const int64_t fit =
+                int64_t((workspace_bytes - kAlign - plan.wpack_bytes) / size_t(img));
+            chunk = std::max<int64_t>(1, std::min(chunk, fit));
+        }
+        plan.chunk = chunk;
+        plan.fused_tile = choose_fused_tile(p, chunk);
+        plan.xt_off = plan.wpack_bytes;
+        plan.col_off = plan.xt_off + size_t(chunk) * plan.xt_bytes_per_image;
+        plan.ws_bytes = plan.col_off;
+        *out = plan;
+        return MDCN_OK;
+    }
     plan.wpack_bytes = align_up(size_t(p.G * p.Mg * plan.Kp) * p.elem, kAlign);
     plan.xt_bytes_per_image = align_up(size_t(p.H * p.W * p.C) * p.elem, kAlign);
     plan.col_bytes_per_image = align_up(size_t(p.G * p.P * plan.Kp) * p.elem, kAlign);
@@ -217,6 +275,7 @@ size_t min_workspace(const Problem &p, const Plan &plan)
         return 0;
     return kAlign + plan.wpack_bytes + plan.xt_bytes_per_image + plan.col_bytes_per_image;
 }
+
 
 size_t workspace_request(const Plan &plan)
 {

@@ -34,7 +34,7 @@ struct Problem {
     int64_t sh, sw, ph, pw, dh, dw;
 };
 
-enum class Path { GatherGemm, Depthwise };
+enum class Path { GatherGemm, Depthwise, Fused };
 
 // Workgroup tile of the GEMM (rows of the packed weight x columns) and its
 // wave grid; every wave owns a block of 32x32 accumulator tiles.
@@ -48,8 +48,19 @@ enum class GemmTile : int {
 };
 constexpr int kGemmTileCount = 6;
 
-// Workspace layout of the gather + GEMM path (all offsets 256-byte aligned):
-//   [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
+// Workgroup tile of the fused gather-GEMM.
+// (2 x 2 consumer waves plus producer waves.)
+enum class FusedTile : int {
+    M256_N128 = 0,
+    M128_N128 = 1,
+    M256_N64 = 2,
+    M128_N64 = 3,
+};
+constexpr int kFusedTileCount = 4;
+
+// Workspace layout (all offsets 256-byte aligned):
+//   gather + GEMM: [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
+//   fused:         [packed weight: G x Mg x Kp] [x in NHWC: chunk images]
 struct Plan {
     Path path;
     int64_t chunk;               // images per pass through gather + GEMM
@@ -59,13 +70,18 @@ struct Plan {
     size_t col_off, col_bytes_per_image;
     size_t ws_bytes;             // bytes this plan uses
     GemmTile gemm_tile;
+    FusedTile fused_tile;
 };
 
 constexpr size_t kColumnBudget = size_t(256) << 20;   // default column-buffer cap
 constexpr size_t kAlign = 256;                         // workspace sub-buffer alignment
+constexpr size_t kFusedBudget = size_t(512) << 20;    // default NHWC chunk cap (fused)
 constexpr int64_t kMaxCoord = int64_t(1) << 24;        // spatial extents and anchors
 
 size_t dtype_size(mdcn_dtype t);
+// Whether the fused gather-GEMM can run this problem (channel blocks that
+// align with its 128-byte K steps and 16-byte chunks).
+bool fused_eligible(const Problem &p);
 mdcn_status check_attrs(const int32_t stride[2], const int32_t padding[2],
                         const int32_t dilation[2], int32_t group, int32_t dgroup);
 mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[16],

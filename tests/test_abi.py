@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
     (dict(padding=(-1, 0)), mdcn.MDCN_E_ATTR),
     (dict(group=0), mdcn.MDCN_E_ATTR),
     (dict(deformable_group=-1), mdcn.MDCN_E_ATTR),
-    (dict(path=7), mdcn.MDCN_E_PATH),
+    (dict(path=9), mdcn.MDCN_E_PATH),
 ])
 def test_create_rejects(kw, code):
     args = dict(stride=1, padding=0, dilation=1, group=1, deformable_group=1)
@@ -185,6 +185,7 @@ def test_empty_problems_are_noops():
 
 def test_workspace_sizes_and_chunking():
     op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_GATHER_GEMM)
     # f16: 2 images of 2304 x 25600 halves of columns fit the 256 MiB budget
     b, mb = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, DIMS)
     col_img = 2304 * 25600 * 2
@@ -205,6 +206,23 @@ def test_workspace_sizes_and_chunking():
     # ... and the gather + GEMM path can be forced for it
     dwg = mdcn.mdcn_create(1, 1, 1, 256, 1, path=mdcn.MDCN_PATH_GATHER_GEMM)
     assert mdcn.mdcn_workspace_bytes(dwg, mdcn.MDCN_F32, d5)[0] > 0
+
+
+def test_fused_path_plan():
+    # automatic choice for the OCDNet-like stage: fused, all 4 images, NHWC x only
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    desc = mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, DIMS)
+    assert desc.startswith("path=fused") and "chunk=4" in desc
+    b, mb = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, DIMS)
+    assert b == 256 + 256 * 2304 * 2 + 4 * 256 * 160 * 160 * 2
+    assert mb == 256 + 256 * 2304 * 2 + 256 * 160 * 160 * 2
+    # not eligible: C/group = 36 is not a multiple of 64 -> gather + GEMM
+    opg = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_FUSED)
+    d = [1, 36, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 8, 36, 3, 3]
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_workspace_bytes(opg, mdcn.MDCN_F16, d)
+    assert e.value.status == mdcn.MDCN_E_PATH
+    assert mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, d).startswith("path=gather_gemm")
 
 
 def test_contraction_padding():

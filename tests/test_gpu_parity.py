@@ -54,7 +54,21 @@ SMALL = {
     # output grid smaller than the conv formula (taken from the offset dims)
     "smaller_out_grid": Problem(N=2, C=16, Co=32, H=15, W=15, Ho=7, Wo=11),
     "tiny": workloads.TINY,
+    # eligible for the fused gather-GEMM (C/group a multiple of 64, C/dg of 32):
+    # Co = 160 (a partial weight-row tile), 3 x 169 pixels (ragged columns)
+    "fused_multi_tile": Problem(N=3, C=64, Co=160, H=13, W=13, deformable_groups=2,
+                                offset_dist=("normal", 2.0)),
+    # grouped, strided, dilated, 3x2 kernel, 4 offset groups, Mg = 48
+    "fused_grouped": Problem(N=2, C=128, Co=96, H=17, W=15, kh=3, kw=2, stride=(2, 1),
+                             padding=(2, 1), dilation=(2, 1), groups=2, deformable_groups=4,
+                             offset_dist=("normal", 1.5)),
 }
+
+
+def fused_ok(pr, dtype):
+    e = 4 if dtype == "f32" else 2
+    cg, cdg = pr.C // pr.groups, pr.C // pr.deformable_groups
+    return cg % (128 // e) == 0 and cdg % (4 * (16 // e)) == 0
 
 
 def to_dev(inp):
@@ -83,15 +97,17 @@ def oracle_full(pr, inp):
                           **pr.attrs())
 
 
-def paths_for(pr):
+def paths_for(pr, dtype):
     paths = [mdcn.MDCN_PATH_GATHER_GEMM]
     if pr.C // pr.groups == 1:
         paths.append(mdcn.MDCN_PATH_DEPTHWISE)
+    if fused_ok(pr, dtype):
+        paths.append(mdcn.MDCN_PATH_FUSED)
     return paths
 
 
 CASES = [(name, dt, path) for name, pr in SMALL.items() for dt in ("f32", "f16", "bf16")
-         for path in paths_for(pr)]
+         for path in paths_for(pr, dt)]
 
 
 @pytest.mark.parametrize("name,dtype,path", CASES)
@@ -299,3 +315,30 @@ def test_depthwise_variants(planes, pixels, name, monkeypatch):
     ref = oracle_full(pr, inp)
     ok, err, bound = within_tolerance(got, ref, "f32")
     assert ok, (planes, pixels, name, error_report(got, ref))
+
+
+# ---------------------------------------------------------------- fused gather-GEMM tiles
+
+@pytest.mark.parametrize("tile", range(4))
+@pytest.mark.parametrize("name,dtype", [("fused_multi_tile", "f16"), ("fused_multi_tile", "f32"),
+                                        ("fused_grouped", "bf16")])
+def test_every_fused_tile(tile, name, dtype, monkeypatch):
+    """The planner's fused-tile override (MDCN_FUSED_TILE) forces each tile."""
+    monkeypatch.setenv("MDCN_FUSED_TILE", str(tile))
+    pr = SMALL[name]
+    inp = workloads.generate(pr, dtype, seed=15)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_FUSED).double().numpy()
+    ref = oracle_full(pr, inp)
+    ok, err, bound = within_tolerance(got, ref, dtype)
+    assert ok, (tile, name, dtype, error_report(got, ref))
+
+
+def test_fused_matches_gather_gemm_closely():
+    """Both paths round the same fp32 sums once; they agree far inside the
+    tolerance (the column buffer rounds each sample to the storage dtype, the
+    fused path rounds the same samples to the same dtype in LDS)."""
+    pr = SMALL["fused_multi_tile"]
+    inp = workloads.generate(pr, "f16", seed=16)
+    a = run_gpu(pr, inp, mdcn.MDCN_PATH_FUSED).double()
+    b = run_gpu(pr, inp, mdcn.MDCN_PATH_GATHER_GEMM).double()
+    assert float((a - b).abs().max()) <= 2e-3
