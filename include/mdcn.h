@@ -91,7 +91,10 @@ typedef enum mdcn_path {
                                   are made in LDS from the bilinear samples, with no column
                                   buffer [plugin guide §五 steps 1-3 without the columns];
                                   requires C/group to be a multiple of 64 (fp16/bf16) or 32
-                                  (fp32) and C/deformable_group of 32 or 16               */
+                                  (fp32), C/deformable_group of 8 or 4, and a per-tile
+                                  geometry table (32 bytes per offset group, tap and output
+                                  column; 64 or 128 columns) that fits in LDS beside the
+                                  operand stages                                          */
 } mdcn_path;
 
 typedef struct mdcn_op mdcn_op;

@@ -9,23 +9,29 @@
 // Tiling and A (packed weight) movement are those of gemm.hip: BM x BN tile,
 // 128-byte K steps (64 f16/bf16 or 32 f32 channels of one tap, which requires
 // C/group to be a multiple of that), two LDS stages, swizzled 128-byte rows.
+// A 16-byte chunk must lie in one offset group (C/deformable_group a multiple
+// of 8 f16/bf16 or 4 f32 channels).
 // B rows are output pixels (columns n*P + pix of the chunk).
 //
-// The workgroup's waves specialise.  Consumer waves move A by DMA and run the
-// MFMAs: at each step they read the staged fragments into registers, issue
-// the DMA of the next step's A rows into the other stage, then multiply, so
-// the DMA flies under the MFMAs.  Producer waves make the B rows: each
-// producer thread owns one B row and CPT of its eight 16-byte chunks, keeps
-// that pixel's bilinear geometry for the current (tap, offset group) in
-// registers -- four corner byte offsets into the NHWC chunk and four fp32
-// weights with the mask folded in -- and recomputes it only when the tap or
-// offset group changes, from offset and mask values it loaded one step
-// earlier.  Its corner loads (buffer loads; a corner off the image gets an
-// out-of-range offset and reads 0) are issued three steps ahead of the
-// consumers, between the chunks of the blend, conversion and LDS write of the
-// step one ahead, so each load has two steps to land.  One consumer and one producer
-// wave share each SIMD, so MFMA and VALU work overlap; one barrier per step
-// separates the two LDS stages.
+// The workgroup's waves specialise.  Consumer waves only read the staged
+// fragments and run the MFMAs (an in-order wave that issues memory operations
+// stalls whenever the texture unit's queue is full, which would stop its
+// MFMAs).  Producer waves move A by DMA and make the B rows.
+//
+// Gather cost is set by how many cache lines one load instruction touches,
+// not by its bytes, so a producer load reads whole lines: eight lanes read
+// the 128 bytes (the step's channels) of one pixel's corner, and a thread
+// handles CPT rows (pixels) for one 16-byte chunk.  The bilinear geometry of
+// every (offset group, tap, row) of the tile -- four corner byte offsets into
+// the NHWC chunk and four fp32 weights with the mask folded in -- is built
+// once per tile into an LDS table by the whole workgroup; a producer re-reads
+// its rows' entries when the tap or offset group changes.  Corner loads
+// (buffer loads; a corner off the image gets an out-of-range offset and
+// reads 0) are issued three steps ahead of the consumers, between the rounds
+// of the blend, conversion and LDS write of the step one ahead, so each load
+// has two steps to land.  One consumer and one producer wave share each SIMD,
+// so MFMA and VALU work overlap; one barrier per step separates the two LDS
+// stages.
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -42,6 +48,8 @@ struct FusedArgs {
     int Cg, Cdg, C, H, W, Wo, kw, K;
     int sh, sw, ph, pw, dh, dw;
     int offC, mskC;
+    int DG;                      // deformable groups
+    int nq;                      // offset groups of the geometry table (per group)
     uint32_t img_bytes;          // bytes of one NHWC image
     uint32_t chunk_bytes;        // bytes of the chunk's NHWC images (< 2^31)
     int steps;                   // K steps: Kg / (128 / sizeof(T))
@@ -71,13 +79,29 @@ __device__ __forceinline__ void issue_a_rows(char *stage_base, __amdgpu_buffer_r
             step * 128, 0, 0);
 }
 
-// Instruction t of issue_a_rows alone.
-__device__ __forceinline__ void issue_a_row(char *stage_base, __amdgpu_buffer_rsrc_t ra,
-                                            const uint32_t *voff_a, int wave, int step, int ipwa,
-                                            int t)
+// A 16-byte LDS store the compiler does not track.  The compiler orders
+// every LDS access after an LDS-writing DMA behind that DMA's completion;
+// the producer's B stores never overlap the A rows its DMA fills, so they
+// are written here, and the explicit lgkmcnt(0) before each barrier covers
+// them.  (An untracked LDS operation can only make the compiler's own
+// lgkmcnt waits wait longer, never shorter: LDS operations complete in order.)
+__device__ __forceinline__ void lds_store16(char *p, uint4 v)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(stage_base + (wave * ipwa + t) * 8 * 128),
-                                             16, voff_a[t], step * 128, 0, 0);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const uint32_t addr = uint32_t(reinterpret_cast<uintptr_t>((lds_void *)p));
+    const u32x4 d = {v.x, v.y, v.z, v.w};
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(d) : "memory");
+}
+
+// x / d for 0 <= x, d < 2^16 through the fp32 reciprocal rd ~ 1/d: the
+// product is within one of the quotient, and one correction each way makes
+// it exact.
+__device__ __forceinline__ int div_small(int x, int d, float rd)
+{
+    int q = int(float(x) * rd);
+    q -= int(q * d > x);
+    q += int((q + 1) * d <= x);
+    return q;
 }
 
 template <typename T>
@@ -90,6 +114,47 @@ __device__ __forceinline__ void fma_chunk(float *acc, const uint4 &raw, float w)
         acc[e] = fmaf(w, to_f32(v.e[e]), acc[e]);
 }
 
+// The tile's geometry table: for every (offset group qf+qq, tap k, B row r)
+// entry e = (qq*K + k)*BN + r, 32 bytes: the byte offsets into the NHWC chunk
+// of the four bilinear corners of row r's sample (kOffImage for a corner off
+// the image) and their weights with the mask folded in.  Built once per
+// tile by the whole workgroup; rows past the last column repeat a valid one.
+template <typename T, int BN, int NT>
+__device__ __forceinline__ void build_geo_table(char *tab, const FusedArgs &a,
+                                                const T *__restrict__ off,
+                                                const T *__restrict__ msk, int qf, int n0,
+                                                int tid)
+{
+    const int E = a.nq * a.K * BN;
+    const uint32_t elem_c = uint32_t(a.C) * uint32_t(sizeof(T));
+#pragma unroll 2
+    for (int e = tid; e < E; e += NT) {
+        const int r = e % BN;
+        const int kq = e / BN;
+        const int k = kq % a.K;
+        const int q = min(qf + kq / a.K, a.DG - 1);
+        const int ncol = min(n0 + r, a.Ncols - 1);
+        const int img = ncol / a.P;
+        const int pix = ncol - img * a.P;
+        const int ho = pix / a.Wo, wo = pix - ho * a.Wo;
+        const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+        const size_t ob = (size_t(img) * a.offC + size_t(q) * 2 * a.K + 2 * k) * a.P + pix;
+        const float oh = to_f32(off[ob]);
+        const float ow = to_f32(off[ob + a.P]);
+        const float m = to_f32(msk[(size_t(img) * a.mskC + size_t(q) * a.K + k) * a.P + pix]);
+        const Taps tp = make_taps(ho * a.sh - a.ph + i * a.dh, wo * a.sw - a.pw + j * a.dw, oh,
+                                  ow, m, a.H, a.W);
+        const uint32_t base = uint32_t(img) * a.img_bytes;
+        uint32_t o[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            o[s] = tp.valid[s] ? base + uint32_t(tp.idx[s]) * elem_c : kOffImage;
+        *reinterpret_cast<uint4 *>(tab + size_t(e) * 32) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4 *>(tab + size_t(e) * 32 + 16) =
+            make_float4(tp.wt[0], tp.wt[1], tp.wt[2], tp.wt[3]);
+    }
+}
+
 template <typename T, int BM, int BN, int CWM, int CWN, int PW>
 __global__ __launch_bounds__((CWM * CWN + PW) * 64) void fused_kernel(
     const T *__restrict__ A, const T *__restrict__ xt, const T *__restrict__ off,
@@ -98,20 +163,22 @@ __global__ __launch_bounds__((CWM * CWN + PW) * 64) void fused_kernel(
     constexpr int STEP = 128;
     constexpr int NC = CWM * CWN;                // consumer (MFMA) waves
     constexpr int NP = PW * 64;                  // producer threads
+    constexpr int NT = NC * 64 + NP;
     constexpr int WTM = BM / CWM, WTN = BN / CWN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int STAGE_BYTES = (BM + BN) * STEP;
     constexpr int EV = 16 / int(sizeof(T));      // elements per 16-byte chunk
     constexpr int SE = STEP / int(sizeof(T));    // K elements per step
-    constexpr int IPWA = BM / 8 / NC;            // A load instructions per consumer wave
-    constexpr int CPT = BN * 8 / NP;             // B chunks per producer thread per step
-    constexpr int TPR = 8 / CPT;                 // producer threads per B row
-    static_assert(BM % 32 == 0 && BN % 32 == 0 && (BM / 8) % NC == 0,
-                  "A rows must split evenly into 8-row load instructions per consumer wave");
-    static_assert((BN * 8) % NP == 0 && CPT >= 1 && CPT <= 8 && 8 % CPT == 0,
-                  "B chunks must split evenly over the producer threads");
+    constexpr int IPWA = BM / 8 / PW;            // A load instructions per producer wave
+    constexpr int ROWS = NP / 8;                 // B rows per producer round
+    constexpr int CPT = BN / ROWS;               // rounds: B rows per producer thread
+    static_assert(BM % 32 == 0 && BN % 32 == 0 && (BM / 8) % PW == 0,
+                  "A rows must split evenly into 8-row load instructions per producer wave");
+    static_assert(NP % 8 == 0 && BN % ROWS == 0 && CPT >= 1 && CPT <= 8,
+                  "B rows must split evenly over the producer rounds");
     static_assert(NC * 32 * (WTN + 4) * 4 <= 2 * STAGE_BYTES, "epilogue slices must fit in LDS");
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    extern __shared__ __attribute__((aligned(16))) char tab[];   // geometry table
 
     uint32_t bid = xcd_swizzle(blockIdx.x, gridDim.x);
     const int mt = int(bid % uint32_t(a.tiles_m));
@@ -119,23 +186,17 @@ __global__ __launch_bounds__((CWM * CWN + PW) * 64) void fused_kernel(
     const int nt = int(bid % uint32_t(a.tiles_n));
     const int g = __builtin_amdgcn_readfirstlane(int(bid / uint32_t(a.tiles_n)));
     const int m0 = mt * BM, n0 = nt * BN;
+    const int qf = (g * a.Cg) / a.Cdg;           // first offset group of group g
 
     const int tid = int(threadIdx.x);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+    build_geo_table<T, BN, NT>(tab, a, off, msk, qf, n0, tid);
+    __syncthreads();
+
     if (wave < NC) {
-        // ---------------- consumer: A by DMA, MFMAs over the staged tiles
-        const uint32_t row_bytes = uint32_t(a.Kp) * uint32_t(sizeof(T));
-        const char *Ag = reinterpret_cast<const char *>(A) + size_t(g) * a.Mg * row_bytes;
-        const __amdgpu_buffer_rsrc_t ra = scalar_rsrc(Ag, uint32_t(a.Mg) * row_bytes);
-        uint32_t voff_a[IPWA];
-#pragma unroll
-        for (int t = 0; t < IPWA; ++t) {
-            const int row = (wave * IPWA + t) * 8 + (lane >> 3);
-            voff_a[t] = uint32_t(min(m0 + row, a.Mg - 1)) * row_bytes +
-                        swz_chunk(row, lane & 7) * 16;
-        }
+        // ---------------- consumer: MFMAs over the staged tiles
         const int wm = wave % CWM, wn = wave / CWM;
         float16v acc[FM][FN];
 #pragma unroll
@@ -145,25 +206,20 @@ __global__ __launch_bounds__((CWM * CWN + PW) * 64) void fused_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.0f;
-        issue_a_rows<IPWA>(smem, ra, voff_a, wave, 0);
         for (int st = 0; st < a.steps; ++st) {
             const int stage = st & 1;
-            __builtin_amdgcn_s_waitcnt(0);   // this wave's A rows of step st have landed
-            lds_barrier();                   // ... and all of step st's A and B
-            StepFrags<FM, FN> f;             // read before the DMA into the other stage
-            load_step_frags<FM, FN>(f, smem + stage * STAGE_BYTES + wm * WTM * STEP,
-                                    smem + stage * STAGE_BYTES + (BM + wn * WTN) * STEP, lane);
-            // The next step's A DMA is spread over the four k-groups of MFMAs
-            // so that a busy texture unit never holds up the whole step.
-            const bool more = st + 1 < a.steps;
+            lds_barrier();                   // step st's A and B are in LDS
+            const char *sA = smem + stage * STAGE_BYTES + wm * WTM * STEP;
+            const char *sB = smem + stage * STAGE_BYTES + (BM + wn * WTN) * STEP;
+            // fragments one k-group ahead of the MFMAs (two register sets)
+            uint4 fa[2][FM], fb[2][FN];
+            load_kgroup_frags<FM, FN>(fa[0], fb[0], sA, sB, lane, 0);
 #pragma unroll
             for (int kg = 0; kg < 4; ++kg) {
-                mfma_kgroup<T, FM, FN>(acc, f, kg);
-#pragma unroll
-                for (int t = 0; t < IPWA; ++t)
-                    if (more && (t * 4) / IPWA == kg)
-                        issue_a_row(smem + (stage ^ 1) * STAGE_BYTES, ra, voff_a, wave, st + 1,
-                                    IPWA, t);
+                if (kg < 3)
+                    load_kgroup_frags<FM, FN>(fa[(kg + 1) & 1], fb[(kg + 1) & 1], sA, sB, lane,
+                                              kg + 1);
+                mfma_frags<T, FM, FN>(acc, fa[kg & 1], fb[kg & 1]);
             }
         }
         __syncthreads();                     // operand stages no longer needed
@@ -173,182 +229,179 @@ __global__ __launch_bounds__((CWM * CWN + PW) * 64) void fused_kernel(
     }
 
     // ---------------- producer: B from the bilinear gather
+    // Lane c of each group of eight owns 16-byte chunk c of every B row the
+    // group handles, rows r0 + ROWS*i for i < CPT: the eight lanes of a
+    // corner load read one whole 128-byte line (the step's channels of one
+    // pixel), so each load instruction touches eight lines.
     const int ptid = tid - NC * 64;
-    // This thread's B row (output column) and chunk range.
-    const int brow = ptid / TPR;
-    const int bh = ptid % TPR;
-    const int ncol = min(n0 + brow, a.Ncols - 1);        // rows past the edge: any valid column
-    const int img = ncol / a.P;
-    const int pix = ncol - img * a.P;
-    const int ho = pix / a.Wo;
-    const int anc_h = ho * a.sh - a.ph, anc_w = (pix - ho * a.Wo) * a.sw - a.pw;
-    const uint32_t elem_c = uint32_t(a.C) * uint32_t(sizeof(T));
-    // Per corner: byte offset of this thread's first chunk at that corner
-    // (image base + pixel + the thread's channel slot), or kOffImage for a
-    // corner off the image; the step's channel base is added as the uniform
-    // buffer offset, the chunk index as the immediate offset.  kOffImage plus
-    // either stays past the end of the range, so such a load reads 0.
-    const uint32_t lane_base = uint32_t(img) * a.img_bytes + uint32_t(bh * CPT * 16);
+    const int pw = wave - NC;
+    const int c = ptid & 7;
+    const int r0 = ptid >> 3;
+    // The packed weight's rows of the tile (A), moved by DMA: IPWA
+    // instructions of 8 rows per producer wave and step.
+    const uint32_t row_bytes = uint32_t(a.Kp) * uint32_t(sizeof(T));
+    const char *Ag = reinterpret_cast<const char *>(A) + size_t(g) * a.Mg * row_bytes;
+    const __amdgpu_buffer_rsrc_t ra = scalar_rsrc(Ag, uint32_t(a.Mg) * row_bytes);
+    uint32_t voff_a[IPWA];
+#pragma unroll
+    for (int t = 0; t < IPWA; ++t) {
+        const int row = (pw * IPWA + t) * 8 + (lane >> 3);
+        voff_a[t] = uint32_t(min(m0 + row, a.Mg - 1)) * row_bytes + swz_chunk(row, lane & 7) * 16;
+    }
     const __amdgpu_buffer_rsrc_t rx = scalar_rsrc(xt, a.chunk_bytes);
-    char *b_lds = smem + BM * STEP + brow * STEP;
+    char *b_lds = smem + BM * STEP;
 
-    uint32_t goff[4];
-    float gwt[4];
-    int gk = -1, gq = -1;                 // (tap, offset group) of goff/gwt
-    T pf_oh, pf_ow, pf_m;                 // offset and mask of the next geo_for's step
+    // Geometry of the (tap, offset group) last read from the table, the
+    // lane's chunk offset included.  kOffImage plus the chunk and channel
+    // offsets stays past the end of the range, so such a load reads 0.
+    uint32_t goff[CPT][4];
+    float gwt[CPT][4];
+    int gk = -1, gq = -1;
 
-    // (tap, offset group) of this thread's chunks at K step `step`: the step
+    // (tap, offset group) of this lane's chunk at K step `step`: the step
     // covers channels cbase .. cbase+SE-1 of tap k (SE divides C/group).
+    const int spt = a.Cg / SE;                   // steps per tap
+    const float r_spt = 1.0f / float(spt), r_cdg = 1.0f / float(a.Cdg);
     auto step_tap = [&](int step, int &k, int &q, int &cbase) {
-        const int kk0 = step * SE;
-        k = kk0 / a.Cg;
-        cbase = g * a.Cg + (kk0 - k * a.Cg);                     // uniform first channel
-        q = (cbase + bh * CPT * EV) / a.Cdg;
+        k = div_small(step, spt, r_spt);
+        cbase = g * a.Cg + (step - k * spt) * SE;               // uniform first channel
+        q = div_small(cbase + c * EV, a.Cdg, r_cdg);
     };
-    auto fetch_geo = [&](int k, int q) {
-        const size_t ob = (size_t(img) * a.offC + size_t(q) * 2 * a.K + 2 * k) * a.P + pix;
-        pf_oh = off[ob];
-        pf_ow = off[ob + a.P];
-        pf_m = msk[(size_t(img) * a.mskC + size_t(q) * a.K + k) * a.P + pix];
-    };
-    // A register set: the corner chunks of one step and the four bilinear
-    // weights they are blended with (the weights of later steps may differ).
-    struct BSet {
-        uint4 v[CPT][4];
-        float w[4];
-    };
-    // Geometry of step `step`: recomputes the corner offsets and weights
-    // (goff, gwt) if the (tap, offset group) changed, and starts loading the
-    // offset and mask of the step after (the last step reloads its own; a
-    // load behind no branch lets the compiler's later wait for it count
-    // exactly, leaving the corner loads in flight).  Returns the step's
-    // uniform channel byte offset.
+    // Geometry of step `step` (from the table when the tap or offset group
+    // changed); returns the step's uniform channel byte offset.
     auto geo_for = [&](int step) -> int {
         int k, q, cbase;
         step_tap(step, k, q, cbase);
-        // pf_* hold this step's offset and mask.  They are converted and
-        // pinned here, outside the branch: with their only use inside it the
-        // compiler moves the loads into the branch, right in front of the
-        // use, where waiting for them also waits for every corner load.
-        float oh = to_f32(pf_oh), ow = to_f32(pf_ow), m = to_f32(pf_m);
-        asm volatile("" : "+v"(oh), "+v"(ow), "+v"(m));
         if (k != gk || q != gq) {
-            const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
-            const Taps tp = make_taps(anc_h + i * a.dh, anc_w + j * a.dw, oh, ow, m, a.H, a.W);
+            const char *ent = tab + (size_t((q - qf) * a.K + k) * BN + r0) * 32;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                goff[s] = tp.valid[s] ? lane_base + uint32_t(tp.idx[s]) * elem_c : kOffImage;
-                gwt[s] = tp.wt[s];
+            for (int i = 0; i < CPT; ++i) {
+                const uint4 o = *reinterpret_cast<const uint4 *>(ent + i * ROWS * 32);
+                const float4 w = *reinterpret_cast<const float4 *>(ent + i * ROWS * 32 + 16);
+                goff[i][0] = o.x + uint32_t(c * 16);
+                goff[i][1] = o.y + uint32_t(c * 16);
+                goff[i][2] = o.z + uint32_t(c * 16);
+                goff[i][3] = o.w + uint32_t(c * 16);
+                gwt[i][0] = w.x;
+                gwt[i][1] = w.y;
+                gwt[i][2] = w.z;
+                gwt[i][3] = w.w;
             }
             gk = k;
             gq = q;
         }
-        int k1, q1, c1;
-        step_tap(min(step + 1, a.steps - 1), k1, q1, c1);
-        fetch_geo(k1, q1);
         return __builtin_amdgcn_readfirstlane(cbase * int(sizeof(T)));
     };
-    // The four corner loads of chunk jc (geometry from the last geo_for).
-    auto issue_chunk = [&](int jc, int soff, BSet &b) {
+    // A register set: the corner chunks of one step and the weights they are
+    // blended with (the weights of later steps may differ).
+    struct BSet {
+        uint4 v[CPT][4];
+        float w[CPT][4];
+    };
+    // Round i: record the current weights in b, issue the four corner loads.
+    auto refill_round = [&](int i, int soff, BSet &b) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const auto r = __builtin_amdgcn_raw_buffer_load_b128(rx, goff[s] + jc * 16, soff, 0);
-            __builtin_memcpy(&b.v[jc][s], &r, 16);
+            b.w[i][s] = gwt[i][s];
+            const auto r = __builtin_amdgcn_raw_buffer_load_b128(rx, goff[i][s], soff, 0);
+            __builtin_memcpy(&b.v[i][s], &r, 16);
         }
     };
-    auto keep_weights = [&](BSet &b) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            b.w[s] = gwt[s];
-    };
-    // Blend, convert and store chunk jc of a step into LDS stage `stage`.
-    auto blend_chunk = [&](int jc, const BSet &b, int stage) {
+    // Round i: blend, convert and store the lane's chunk of row r0 + ROWS*i.
+    auto blend_round = [&](int i, const BSet &b, int stage) {
         float accv[EV];
 #pragma unroll
         for (int e = 0; e < EV; ++e)
             accv[e] = 0.0f;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            fma_chunk<T>(accv, b.v[jc][s], b.w[s]);
+            fma_chunk<T>(accv, b.v[i][s], b.w[i][s]);
         Vec16<T> o;
 #pragma unroll
         for (int e = 0; e < EV; ++e)
             o.e[e] = from_f32<T>(accv[e]);
-        *reinterpret_cast<uint4 *>(b_lds + stage * STAGE_BYTES +
-                                   swz_chunk(brow, bh * CPT + jc) * 16) = o.raw;
+        const int row = r0 + ROWS * i;
+        lds_store16(b_lds + stage * STAGE_BYTES + row * STEP + swz_chunk(row, c) * 16, o.raw);
     };
-    // Blend one step from set b into `stage` and, chunk by chunk, refill b
-    // with the corners of step `next` (when `more`): the loads go out between
-    // the chunks of the blend, so the texture unit is fed while the VALU
-    // works, and each load has two steps to land.
-    auto blend_and_refill = [&](BSet &b, int stage, int next, bool more) {
-        const int soff = more ? geo_for(next) : 0;
+    auto load_b = [&](int step, BSet &b) {
+        const int soff = geo_for(step);
 #pragma unroll
-        for (int jc = 0; jc < CPT; ++jc) {
-            blend_chunk(jc, b, stage);
+        for (int i = 0; i < CPT; ++i)
+            refill_round(i, soff, b);
+    };
+    // Blend one step from set b into `stage` and, round by round, refill b
+    // with the corners of the step geo_for last set up (when `more`; soff is
+    // its channel offset): the loads go out between
+    // the rounds of the blend, so the texture unit is fed while the VALU
+    // works, and each load has two steps to land.
+    auto blend_and_refill = [&](BSet &b, int stage, int soff, bool more) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            blend_round(i, b, stage);
             if (more)
-                issue_chunk(jc, soff, b);
-            __builtin_amdgcn_sched_barrier(0);   // keep the chunks interleaved
+                refill_round(i, soff, b);
+            __builtin_amdgcn_sched_barrier(0);   // keep the rounds interleaved
         }
-        if (more)
-            keep_weights(b);
     };
 
     // Two register sets: s0 holds the even steps, s1 the odd ones.  Step
     // st+1's B is finished while the consumers run step st, and its set is
-    // refilled with step st+3.  Only this wave's LDS writes must be complete
-    // at the barrier; the loads of later steps stay in flight, so the wait is
-    // explicit (a fence here would wait for every load): s_waitcnt
-    // lgkmcnt(0), in the gfx9 encoding (vmcnt in bits 3:0 and 15:14 at its
-    // maximum, expcnt 6:4 at its maximum, lgkmcnt 11:8 zero).
-    constexpr int WAIT_LDS = 0xC07F;
+    // refilled with step st+3.  At a barrier the wave's LDS writes and A DMA
+    // must be complete but the corner loads behind them stay in flight, so the
+    // wait is explicit (a fence would wait for every load): s_waitcnt
+    // vmcnt(4*CPT) lgkmcnt(0), in the gfx9 encoding (vmcnt in bits 3:0 and
+    // 15:14, expcnt 6:4 at its maximum, lgkmcnt 11:8).
+    constexpr int WAIT_A = ((4 * CPT) & 15) | ((((4 * CPT) >> 4) & 3) << 14) | 0x70;
     BSet s0, s1;
-    {
-        int k0, q0, c0;
-        step_tap(0, k0, q0, c0);
-        fetch_geo(k0, q0);
-    }
-    auto load_b = [&](int step, BSet &b) {
-        const int soff = geo_for(step);
-        keep_weights(b);
-#pragma unroll
-        for (int jc = 0; jc < CPT; ++jc)
-            issue_chunk(jc, soff, b);
-    };
-    // Steps 0, 1 and 2 (the last step again when there are fewer: no load
-    // behind a branch here either).
+    // A of step 0, then B of steps 0, 1 and 2 (the last step again when there
+    // are fewer, so that no load sits behind a branch and the compiler's
+    // waits count exactly).
+    issue_a_rows<IPWA>(smem, ra, voff_a, pw, 0);
     load_b(0, s0);
     load_b(min(1, a.steps - 1), s1);
-    blend_and_refill(s0, 0, min(2, a.steps - 1), true);
-    auto body = [&](int st, BSet &b, bool more) {
+    blend_and_refill(s0, 0, geo_for(min(2, a.steps - 1)), true);
+    // Body of step st: after the barrier, the DMA of step st+1's A rows,
+    // then step st+1's B.  The previous body issued its A DMA before its
+    // 4*CPT corner loads (when it had any), so at this barrier everything but
+    // those loads must have landed.
+    auto body = [&](int st, BSet &b, bool more, bool prev_loaded) {
         const int stage = st & 1;
         // The compiler barrier and scheduling fences keep the B stores before
         // the barrier and step st+1's B arithmetic after it, so the consumers
         // are released as soon as step st's operands are in LDS.
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(WAIT_LDS);
+        if (prev_loaded)
+            __builtin_amdgcn_s_waitcnt(WAIT_A);
+        else
+            __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();    // step st's A and B are in LDS
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        if (st + 1 < a.steps)
-            blend_and_refill(b, stage ^ 1, st + 3, more);
+        if (st + 1 < a.steps) {
+            // table reads first: an LDS access after an LDS-writing DMA is
+            // made to wait for the DMA (and so for every older load)
+            const int soff = more ? geo_for(st + 3) : 0;
+            issue_a_rows<IPWA>(smem + (stage ^ 1) * STAGE_BYTES, ra, voff_a, pw, st + 1);
+            blend_and_refill(b, stage ^ 1, soff, more);
+        }
     };
     // Main loop: every body loads (st + 4 < steps); then at most four steps,
     // loading while st + 3 < steps.
     int st = 0;
     for (; st + 4 < a.steps; st += 2) {
-        body(st, s1, true);
-        body(st + 1, s0, true);
+        body(st, s1, true, true);
+        body(st + 1, s0, true, true);
     }
+    // body(t) loads when t + 3 < steps; the prologue loaded before body(0)
     if (st < a.steps)
-        body(st, s1, st + 3 < a.steps);
+        body(st, s1, st + 3 < a.steps, st == 0 || st + 2 < a.steps);
     if (st + 1 < a.steps)
-        body(st + 1, s0, st + 4 < a.steps);
+        body(st + 1, s0, st + 4 < a.steps, st + 3 < a.steps);
     if (st + 2 < a.steps)
-        body(st + 2, s1, false);
+        body(st + 2, s1, false, st + 4 < a.steps);
     if (st + 3 < a.steps)
-        body(st + 3, s0, false);
+        body(st + 3, s0, false, false);
     __syncthreads();                     // matches the consumers' barrier before the epilogue
 }
 
@@ -372,12 +425,26 @@ hipError_t fused_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void
     a.sh = int(p.sh); a.sw = int(p.sw); a.ph = int(p.ph); a.pw = int(p.pw);
     a.dh = int(p.dh); a.dw = int(p.dw);
     a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
+    a.DG = int(p.DG);
+    a.nq = int(fused_offset_groups(p));
     a.img_bytes = uint32_t(size_t(p.H) * p.W * p.C * sizeof(T));
     a.chunk_bytes = uint32_t(size_t(cnt) * a.img_bytes);
     a.steps = int(p.Kg * int64_t(sizeof(T)) / 128);
     const uint64_t blocks = uint64_t(p.G) * a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((fused_kernel<T, BM, BN, CWM, CWN, PW>), dim3(uint32_t(blocks)),
-                       dim3((CWM * CWN + PW) * 64), 0, s, static_cast<const T *>(wpack),
+    // The geometry table is the dynamic part of the LDS; the plan only picks
+    // tiles whose stages and table fit.
+    const size_t table = fused_table_bytes(p, BN);
+    const size_t stages = size_t(2) * (BM + BN) * 128;
+    if (stages + table > kLdsBytes)
+        return hipErrorInvalidValue;
+    auto kern = fused_kernel<T, BM, BN, CWM, CWN, PW>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+        int(kLdsBytes - stages));
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL(kern, dim3(uint32_t(blocks)), dim3((CWM * CWN + PW) * 64), table, s,
+                       static_cast<const T *>(wpack),
                        static_cast<const T *>(xt), static_cast<const T *>(offset),
                        static_cast<const T *>(mask), static_cast<const T *>(bias),
                        static_cast<T *>(out), a);
@@ -390,14 +457,17 @@ hipError_t fused_t(const Problem &p, const Plan &plan, int64_t cnt, const void *
                    void *out, hipStream_t s)
 {
     switch (plan.fused_tile) {
+    // <BM, BN, consumer wave grid CWM x CWN, producer waves>: 16, 16, 12 and
+    // 8 waves, i.e. 4, 4, 3 and 2 waves per SIMD (at most 128, 128, 168 and
+    // 256 registers each), half of them producers or close to it.
     case FusedTile::M256_N128:
-        return fused_cfg<T, 256, 128, 2, 2, 4>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return fused_cfg<T, 256, 128, 4, 2, 8>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
     case FusedTile::M128_N128:
-        return fused_cfg<T, 128, 128, 2, 2, 4>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return fused_cfg<T, 128, 128, 2, 4, 8>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
     case FusedTile::M256_N64:
-        return fused_cfg<T, 256, 64, 2, 2, 2>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return fused_cfg<T, 256, 64, 4, 2, 4>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
     case FusedTile::M128_N64:
-        return fused_cfg<T, 128, 64, 2, 2, 2>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return fused_cfg<T, 128, 64, 2, 2, 4>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
     }
     return hipErrorInvalidValue;
 }

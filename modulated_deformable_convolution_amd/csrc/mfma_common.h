@@ -105,6 +105,35 @@ __device__ __forceinline__ void load_step_frags(StepFrags<FM, FN> &f, const char
     }
 }
 
+// The A and B fragments of k-group kg alone (see load_step_frags).
+template <int FM, int FN>
+__device__ __forceinline__ void load_kgroup_frags(uint4 (&fa)[FM], uint4 (&fb)[FN], const char *sA,
+                                                  const char *sB, int lane, int kg)
+{
+    const char *pa = sA + (lane & 31) * 128;
+    const char *pb = sB + (lane & 31) * 128;
+    const int q = kg * 2 + (lane >> 5);
+    const int sw = (lane >> 1) & 7;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        fa[i] = *reinterpret_cast<const uint4 *>(pa + i * 32 * 128 + (q ^ sw) * 16);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        fb[j] = *reinterpret_cast<const uint4 *>(pb + j * 32 * 128 + (q ^ sw) * 16);
+}
+
+// The MFMAs of one k-group from its fragments.
+template <typename T, int FM, int FN>
+__device__ __forceinline__ void mfma_frags(float16v (&acc)[FM][FN], const uint4 (&fa)[FM],
+                                           const uint4 (&fb)[FN])
+{
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = Mma<T>::step(fa[i], fb[j], acc[i][j]);
+}
+
 // The MFMAs of k-group kg of a step.
 template <typename T, int FM, int FN>
 __device__ __forceinline__ void mfma_kgroup(float16v (&acc)[FM][FN], const StepFrags<FM, FN> &f,

@@ -53,23 +53,37 @@ GemmTile choose_gemm_tile(const Problem &p, int64_t chunk)
 }
 
 // Fused tile: as for the GEMM, the tallest tile the group fills, then the
-// widest that still gives about one workgroup per CU.
-// MDCN_FUSED_TILE=<0..3> overrides the choice (for tuning).
-FusedTile choose_fused_tile(const Problem &p, int64_t chunk)
+// widest that still gives about one workgroup per CU; among tiles whose LDS
+// fits.  MDCN_FUSED_TILE=<0..3> overrides the choice (for tuning) when that
+// tile fits.  Returns false when no tile fits.
+bool choose_fused_tile(const Problem &p, int64_t chunk, FusedTile *out)
 {
+    auto fits = [&](FusedTile t) { return fused_lds_bytes(p, t) <= kLdsBytes; };
     if (const char *env = std::getenv("MDCN_FUSED_TILE")) {
         const int v = std::atoi(env);
-        if (v >= 0 && v < kFusedTileCount)
-            return static_cast<FusedTile>(v);
+        if (v >= 0 && v < kFusedTileCount && fits(static_cast<FusedTile>(v))) {
+            *out = static_cast<FusedTile>(v);
+            return true;
+        }
     }
     const int64_t ncols = chunk * p.P;
     auto tiles = [&](int64_t bm, int64_t bn) {
         return p.G * ((p.Mg + bm - 1) / bm) * ((ncols + bn - 1) / bn);
     };
     constexpr int64_t kFill = 192;
+    FusedTile pref;
     if (p.Mg > 128)
-        return tiles(256, 128) >= kFill ? FusedTile::M256_N128 : FusedTile::M256_N64;
-    return tiles(128, 128) >= kFill ? FusedTile::M128_N128 : FusedTile::M128_N64;
+        pref = tiles(256, 128) >= kFill ? FusedTile::M256_N128 : FusedTile::M256_N64;
+    else
+        pref = tiles(128, 128) >= kFill ? FusedTile::M128_N128 : FusedTile::M128_N64;
+    const FusedTile order[] = {pref, p.Mg > 128 ? FusedTile::M256_N64 : FusedTile::M128_N64,
+                               FusedTile::M128_N128, FusedTile::M128_N64};
+    for (FusedTile t : order)
+        if (fits(t)) {
+            *out = t;
+            return true;
+        }
+    return false;
 }
 
 }  // namespace
@@ -169,12 +183,42 @@ mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[
     return MDCN_OK;
 }
 
+int64_t fused_offset_groups(const Problem &p)
+{
+    if (p.Cdg % p.Cg == 0)
+        return 1;                                   // a group lies inside one offset group
+    if (p.Cg % p.Cdg == 0)
+        return p.Cg / p.Cdg;                        // offset groups tile the group
+    return (p.Cg + p.Cdg - 1) / p.Cdg + 1;          // bound for a misaligned start
+}
+
+size_t fused_table_bytes(const Problem &p, int64_t bn)
+{
+    return size_t(fused_offset_groups(p)) * size_t(p.K) * size_t(bn) * 32;
+}
+
+size_t fused_lds_bytes(const Problem &p, FusedTile t)
+{
+    int64_t bm = 128, bn = 64;
+    switch (t) {
+    case FusedTile::M256_N128: bm = 256; bn = 128; break;
+    case FusedTile::M128_N128: bm = 128; bn = 128; break;
+    case FusedTile::M256_N64: bm = 256; bn = 64; break;
+    case FusedTile::M128_N64: bm = 128; bn = 64; break;
+    }
+    return size_t(2 * (bm + bn) * 128) + fused_table_bytes(p, bn);
+}
+
 bool fused_eligible(const Problem &p)
 {
     const int64_t se = 128 / int64_t(p.elem);      // K elements per 128-byte step
     const int64_t ev = 16 / int64_t(p.elem);       // elements per 16-byte chunk
     const int64_t img_bytes = p.C * p.H * p.W * int64_t(p.elem);
-    return p.Cg % se == 0 && p.Cdg % (4 * ev) == 0 && img_bytes <= kMaxPerImage;
+    FusedTile t;
+    // (channel and step indices below 2^16 keep the kernel's division by
+    // fp32 reciprocal exact)
+    return p.Cg % se == 0 && p.Cdg % ev == 0 && img_bytes <= kMaxPerImage &&
+           p.C < 65536 && p.Kg < 65536 && choose_fused_tile(p, 1, &t);
 }
 
 mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
@@ -232,7 +276,9 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
             chunk = std::max<int64_t>(1, std::min(chunk, fit));
         }
         plan.chunk = chunk;
-        plan.fused_tile = choose_fused_tile(p, chunk);
+        if (!choose_fused_tile(p, chunk, &plan.fused_tile))
+            return MDCN_E_PATH;                 // fused_eligible said some tile fits
+
         plan.xt_off = plan.wpack_bytes;
         plan.col_off = plan.xt_off + size_t(chunk) * plan.xt_bytes_per_image;
         plan.ws_bytes = plan.col_off;

@@ -77,11 +77,21 @@ constexpr size_t kColumnBudget = size_t(256) << 20;   // default column-buffer c
 constexpr size_t kAlign = 256;                         // workspace sub-buffer alignment
 constexpr size_t kFusedBudget = size_t(512) << 20;    // default NHWC chunk cap (fused)
 constexpr int64_t kMaxCoord = int64_t(1) << 24;        // spatial extents and anchors
+constexpr size_t kLdsBytes = size_t(160) << 10;        // LDS of one gfx950 workgroup
 
 size_t dtype_size(mdcn_dtype t);
-// Whether the fused gather-GEMM can run this problem (channel blocks that
-// align with its 128-byte K steps and 16-byte chunks).
+// Whether the fused gather-GEMM can run this problem: channel blocks that
+// align with its 128-byte K steps and 16-byte chunks, and some tile whose LDS
+// (operand stages plus geometry table) fits.
 bool fused_eligible(const Problem &p);
+// Offset groups that one group's channels can span (an upper bound where the
+// group and offset-group sizes divide neither way).
+int64_t fused_offset_groups(const Problem &p);
+// Bytes of the fused kernel's per-tile geometry table for a BN-column tile:
+// 32 bytes per (offset group, tap, column).
+size_t fused_table_bytes(const Problem &p, int64_t bn);
+// Operand stages plus geometry table of a fused tile.
+size_t fused_lds_bytes(const Problem &p, FusedTile t);
 mdcn_status check_attrs(const int32_t stride[2], const int32_t padding[2],
                         const int32_t dilation[2], int32_t group, int32_t dgroup);
 mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[16],

@@ -225,6 +225,57 @@ def test_fused_path_plan():
     assert mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, d).startswith("path=gather_gemm")
 
 
+def _fused_dims(n, c, h, w, co, k, dg, g):
+    """dims[16] of a stride-1, pad-(k//2) problem with a k x k kernel."""
+    kk = k * k
+    return [n, c, h, w, n, 2 * dg * kk, h, w, n, dg * kk, h, w, co, c // g, k, k]
+
+
+def _tile_of(desc):
+    return int(desc.split("tile=")[1].split()[0])
+
+
+def test_fused_tile_fits_lds():
+    """The fused kernel keeps a per-tile geometry table in LDS (32 bytes per
+    offset group, tap and output column) beside two operand stages of
+    2 * (BM + BN) * 128 bytes; only tiles that fit in 160 KiB are chosen."""
+    f16 = mdcn.MDCN_F16
+    # C = 256, dg = 1, 3x3: 9 * 128 * 32 = 36 KiB + 96 KiB -> the 256 x 128 tile
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_FUSED)
+    assert _tile_of(mdcn.mdcn_describe_plan(op, f16, DIMS)) == 0
+    # C/dg = 32 with C/group = 64: two offset groups per group, 72 KiB of table:
+    # 256 x 128 (168 KiB) does not fit, 256 x 64 (80 + 36 KiB) does
+    op2 = mdcn.mdcn_create(1, 1, 1, 1, 2, path=mdcn.MDCN_PATH_FUSED)
+    d = _fused_dims(4, 64, 64, 64, 256, 3, 2, 1)
+    assert _tile_of(mdcn.mdcn_describe_plan(op2, f16, d)) == 2
+    # 5x5 kernel, Co = 64: 25 * 128 * 32 = 100 KiB + 64 KiB does not fit at
+    # 128 columns; 128 x 64 (48 + 50 KiB) does
+    op5 = mdcn.mdcn_create(1, 2, 1, 1, 1, path=mdcn.MDCN_PATH_FUSED)
+    d5 = _fused_dims(4, 64, 64, 64, 64, 5, 1, 1)
+    assert _tile_of(mdcn.mdcn_describe_plan(op5, f16, d5)) == 3
+    # C/dg = 8 with C/group = 64: eight offset groups, 144 KiB of table even
+    # at 64 columns: not eligible
+    op8 = mdcn.mdcn_create(1, 1, 1, 1, 8, path=mdcn.MDCN_PATH_FUSED)
+    d8 = _fused_dims(2, 64, 16, 16, 64, 3, 8, 1)
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_workspace_bytes(op8, f16, d8)
+    assert e.value.status == mdcn.MDCN_E_PATH
+    # C/dg = 4 halves: a 16-byte chunk would straddle offset groups
+    op16 = mdcn.mdcn_create(1, 1, 1, 1, 16, path=mdcn.MDCN_PATH_FUSED)
+    d16 = _fused_dims(2, 64, 16, 16, 64, 3, 16, 1)
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_workspace_bytes(op16, f16, d16)
+    assert e.value.status == mdcn.MDCN_E_PATH
+    # ... but 4 fp32 channels are one chunk; 16 offset groups of 4 over
+    # C/group = 64 f32 is 16 * 9 * 64 * 32 = 288 KiB of table: not eligible either
+    with pytest.raises(mdcn.MdcnError):
+        mdcn.mdcn_workspace_bytes(op16, mdcn.MDCN_F32, d16)
+    # a misaligned group (C/group = 64, C/dg = 96) spans up to two offset groups
+    opm = mdcn.mdcn_create(1, 1, 1, 3, 2, path=mdcn.MDCN_PATH_FUSED)
+    dm = _fused_dims(2, 192, 16, 16, 96, 3, 2, 3)
+    assert mdcn.mdcn_describe_plan(opm, f16, dm).startswith("path=fused")
+
+
 def test_contraction_padding():
     # Kg = 4*9 = 36 pads to 64
     op = mdcn.mdcn_create(1, 1, 1, 1, 1)

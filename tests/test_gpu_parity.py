@@ -62,13 +62,31 @@ SMALL = {
     "fused_grouped": Problem(N=2, C=128, Co=96, H=17, W=15, kh=3, kw=2, stride=(2, 1),
                              padding=(2, 1), dilation=(2, 1), groups=2, deformable_groups=4,
                              offset_dist=("normal", 1.5)),
+    # C/dg = 16: the lanes of one output column read different offset groups
+    # (f16/bf16: two 16-byte chunks per offset group; f32: four)
+    "fused_narrow_dg": Problem(N=2, C=64, Co=64, H=11, W=13, deformable_groups=4,
+                               offset_dist=("normal", 2.0)),
+    # C/group = 64 and C/dg = 96: group 1 spans offset groups 0 and 1
+    "fused_misaligned_groups": Problem(N=2, C=192, Co=96, H=9, W=11, groups=3,
+                                       deformable_groups=2, offset_dist=("normal", 2.0)),
+    # 5x5 taps: the geometry table only fits beside a 64-column tile
+    "fused_5x5": Problem(N=2, C=64, Co=64, H=11, W=10, kh=5, kw=5, padding=(2, 2),
+                         offset_dist=("normal", 2.0)),
 }
 
 
 def fused_ok(pr, dtype):
-    e = 4 if dtype == "f32" else 2
-    cg, cdg = pr.C // pr.groups, pr.C // pr.deformable_groups
-    return cg % (128 // e) == 0 and cdg % (4 * (16 // e)) == 0
+    """Whether the library accepts the fused path for this problem (a host
+    query: an op created for the fused path reports MDCN_E_PATH otherwise)."""
+    op = make_op(pr, mdcn.MDCN_PATH_FUSED)
+    shapes = pr.shapes()
+    dims = [int(v) for k in ("x", "offset", "mask", "weight") for v in shapes[k]]
+    try:
+        mdcn.mdcn_workspace_bytes(op, mdcn.dtype_code(workloads.DTYPES[dtype]), dims)
+    except mdcn.MdcnError as e:
+        assert e.status == mdcn.MDCN_E_PATH
+        return False
+    return True
 
 
 def to_dev(inp):
@@ -321,7 +339,7 @@ def test_depthwise_variants(planes, pixels, name, monkeypatch):
 
 @pytest.mark.parametrize("tile", range(4))
 @pytest.mark.parametrize("name,dtype", [("fused_multi_tile", "f16"), ("fused_multi_tile", "f32"),
-                                        ("fused_grouped", "bf16")])
+                                        ("fused_grouped", "bf16"), ("fused_narrow_dg", "f16")])
 def test_every_fused_tile(tile, name, dtype, monkeypatch):
     """The planner's fused-tile override (MDCN_FUSED_TILE) forces each tile."""
     monkeypatch.setenv("MDCN_FUSED_TILE", str(tile))
