@@ -34,10 +34,25 @@ DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
 # profiles/*memory_counters.md), valid only for the kernel sources they were
 # taken on (sha256 of the listed files, first 16 hex digits).
 MEASURED_TRAFFIC = {
+    ("fused_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
+        "bytes": (53987 * 2 + 51200) * 1024,
+        "sources": ('fused.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
+        "sha": "5c486bcb79f0f555",
+    },
     ("gemm_bias", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (119907 * 2 + 25600) * 1024,
-        "sources": ("gemm.hip", "device_common.h", "plan.cpp"),
-        "sha": "2035032fa30fa41e",
+        "bytes": (119917 * 2 + 25600) * 1024,
+        "sources": ('gemm.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp'),
+        "sha": "d279360328852a4b",
+    },
+    ("deform_gather", "ocdnet_n4_c256_160x160", "f16"): {
+        "bytes": (23296 * 2 + 230400) * 1024,
+        "sources": ('gather.hip', 'device_common.h', 'plan.cpp'),
+        "sha": "eaff17c485000b0c",
+    },
+    ("depthwise_direct", "depthwise_n8_c256_96x96", "f32"): {
+        "bytes": (52535 * 2 + 73728) * 1024,
+        "sources": ('depthwise.hip', 'device_common.h'),
+        "sha": "ecc5f5105b98c6ec",
     },
 }
 

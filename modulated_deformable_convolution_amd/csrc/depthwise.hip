@@ -8,24 +8,27 @@
 //
 // The samples land anywhere on the plane (offsets are unbounded), so each
 // output needs kh*kw*4 effectively random reads of its input plane.  The
-// fastest memory for random reads is LDS: a workgroup stages CB whole input
-// planes there, in a layout where one 16-byte read returns all four bilinear
-// corners.  The plane is padded by one zero row/column on every side (the
-// zero that bilinear interpolation reads off the image), and entry [r][c] of
-// the staged plane holds the vertical pair (X[r][c], X[r+1][c]) of the padded
-// plane X.  Corners (h0, w0) .. (h0+1, w0+1) are then pairs [h0+1][w0+1] and
-// [h0+1][w0+2]: adjacent 8-byte entries, one ds_read2_b64.  Any sample with
-// -1 <= h0 <= H-1 and -1 <= w0 <= W-1 reads inside the staged plane; any other
-// sample is entirely off the image and contributes 0.
+// fastest memory for random reads is LDS, and on gfx950 a random LDS read
+// costs about the same per lane up to 8 bytes and less than twice that for
+// 16: wider entries are nearly free.  A workgroup therefore stages CH
+// channels of one image interleaved, one ENT-byte entry (4 fp32 or 8 fp16
+// channels for ENT = 16) per plane position.  Channels that share an offset
+// group share every sample position, so one sampling geometry (corner
+// address and four weights with the mask folded in) serves all CH channels,
+// and the four corners of a sample are four aligned entry reads.
 //
-// Taps are branch-free: a sample entirely off the image reads a safe address
-// with factor 0.  With one output channel per input channel and 3x3 taps
-// (the common case) the nine weights are loaded once per workgroup.
+// The staged plane has a zero ring two entries wide.  A sample's top-left
+// corner (h0, w0) is clamped to [-2, H] x [-2, W]: a sample with -1 <= h0 <=
+// H-1 and -1 <= w0 <= W-1 is unchanged (its off-image corners read the ring's
+// zeros, the zero that bilinear interpolation reads off the image), and any
+// other sample lies entirely off the image and lands on a window of ring
+// zeros, so it contributes 0 whatever its weights.  Taps need no validity
+// test, and no input value can leak into an off-image sample.
 //
 // Workgroups are ordered so that those of one image run on one XCD: the
 // image's offsets and masks, read by every channel block, stay in that L2.
-// When a plane does not fit in LDS, a plain kernel reading x from global
-// memory is used instead.
+// When not even a one-channel plane fits in LDS, a plain kernel reading x
+// from global memory is used instead.
 #include <cstdlib>
 
 #include "device_common.h"
@@ -48,162 +51,298 @@ constexpr int kStagedThreads = 512;
 constexpr int kMaxMg = 4;                    // output channels per input channel per pass
 constexpr size_t kLdsBytes = 160 * 1024;
 
-template <typename T, int CB, int KT, int UP, bool MG1>
+template <int ENT> struct EntryType;
+template <> struct EntryType<16> { typedef uint4 type; };
+template <> struct EntryType<8> { typedef uint2 type; };
+template <> struct EntryType<4> { typedef uint32_t type; };
+template <> struct EntryType<2> { typedef uint16_t type; };
+
+// Channel ch of a staged entry, as fp32.
+template <typename T, int ENT>
+__device__ __forceinline__ float entry_at(const typename EntryType<ENT>::type &e, int ch)
+{
+    T v[ENT / sizeof(T)];
+    __builtin_memcpy(v, &e, ENT);
+    return to_f32(v[ch]);
+}
+
+// Buffer resource over `bytes` bytes at a uniform `base` (scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dw_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    void *p = reinterpret_cast<void *>((uint64_t(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, int(__builtin_amdgcn_readfirstlane(bytes)),
+                                             0x00020000);
+}
+
+// One element at byte offset vo + so of a buffer.
+template <typename T>
+__device__ __forceinline__ T dw_load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so)
+{
+    T v;
+    if constexpr (sizeof(T) == 4) {
+        const uint32_t b = __builtin_amdgcn_raw_buffer_load_b32(r, vo, int(so), 0);
+        __builtin_memcpy(&v, &b, 4);
+    } else {
+        const uint16_t b = __builtin_amdgcn_raw_buffer_load_b16(r, vo, int(so), 0);
+        __builtin_memcpy(&v, &b, 2);
+    }
+    return v;
+}
+
+template <typename T, int ENT, int UP, bool KT9, bool MG1>
 __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
     const T *__restrict__ x, const T *__restrict__ off, const T *__restrict__ msk,
     const T *__restrict__ w, const T *__restrict__ bias, T *__restrict__ out, DwArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) float2 planes[];
-    const int PW = a.W + 2;                          // staged row length (pairs)
-    const int PL = (a.H + 1) * PW;                   // staged plane length (pairs)
+    constexpr int CH = ENT / int(sizeof(T));        // channels per entry
+    using Ent = typename EntryType<ENT>::type;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int PW = a.W + 4, PH = a.H + 4;            // staged plane, entries
+    const int tid = int(threadIdx.x);
 
     const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
     const int n = __builtin_amdgcn_readfirstlane(int(lid / uint32_t(a.cblocks)));
-    const int c0 = __builtin_amdgcn_readfirstlane(int(lid % uint32_t(a.cblocks)) * CB);
-    const int ncb = min(CB, a.C - c0);
+    const int c0 = __builtin_amdgcn_readfirstlane(int(lid % uint32_t(a.cblocks)) * CH);
+    const int ncb = min(CH, a.C - c0);
 
-    // Stage: pair [r][c] = (X[r][c], X[r+1][c]), X[r][c] = x[r-1][c-1] or 0.
-    for (int cb = 0; cb < CB; ++cb) {
-        const T *plane = x + (size_t(n) * a.C + min(c0 + cb, a.C - 1)) * a.HW;
-        for (int e = int(threadIdx.x); e < PL; e += kStagedThreads) {
-            const int r = e / PW, c = e - (e / PW) * PW;
-            const int xr = r - 1, xc = c - 1;
-            const bool cin = xc >= 0 && xc < a.W;
-            const float v0 = (cin && xr >= 0) ? to_f32(plane[xr * a.W + xc]) : 0.0f;
-            const float v1 = (cin && xr + 1 < a.H) ? to_f32(plane[(xr + 1) * a.W + xc]) : 0.0f;
-            planes[cb * PL + e] = make_float2(v0, v1);
+    // Stage: entry [r][cc] = channels c0 .. c0+CH-1 of x[r-2][cc-2], or 0 in
+    // the ring (r < 2 or r >= H+2, cc < 2 or cc >= W+2) and past the last
+    // channel.
+    // Each thread takes SU entries kStagedThreads apart at a time and issues
+    // all of their loads before writing any, so a whole batch of HBM reads is
+    // in flight (one entry at a time would pay the full latency each time).
+    {
+        constexpr int SU = 8;
+        const int NE = PH * PW;
+        for (int e0 = tid; e0 < NE; e0 += SU * kStagedThreads) {
+            T v[SU][CH];
+#pragma unroll
+            for (int su = 0; su < SU; ++su) {
+                const int e = e0 + su * kStagedThreads;
+                const int r = e / PW, cc = e - (e / PW) * PW;
+                const int xr = r - 2, xc = cc - 2;
+                const bool in = (e < NE) & (xr >= 0) & (xr < a.H) & (xc >= 0) & (xc < a.W);
+#pragma unroll
+                for (int ch = 0; ch < CH; ++ch)
+                    v[su][ch] = (in && ch < ncb)
+                                    ? x[(size_t(n) * a.C + c0 + ch) * a.HW + size_t(xr) * a.W + xc]
+                                    : from_f32<T>(0.0f);
+            }
+#pragma unroll
+            for (int su = 0; su < SU; ++su) {
+                const int e = e0 + su * kStagedThreads;
+                if (e < NE) {
+                    Ent en;
+                    __builtin_memcpy(&en, v[su], ENT);
+                    *reinterpret_cast<Ent *>(lds + size_t(e) * ENT) = en;
+                }
+            }
+        }
+    }
+    // With one output per channel and 3x3 taps, the workgroup's weights go
+    // to LDS too, as fp32 [tap][channel], after the plane: one uniform read
+    // per tap (in scalar registers, 9*CH of them would crowd out the rest).
+    float *wtab = reinterpret_cast<float *>(lds + size_t(PH) * PW * ENT);
+    if constexpr (MG1 && KT9) {
+        for (int e = tid; e < 9 * CH; e += kStagedThreads) {
+            const int k = e / CH, ch = e - (e / CH) * CH;
+            wtab[e] = to_f32(w[size_t(min(c0 + ch, a.C - 1)) * 9 + k]);
         }
     }
     __syncthreads();
 
     const int q = c0 / a.Cdg;                        // every staged channel is in block q
-    // Weights of the workgroup's output channels, when known to be few.
-    float wreg[CB][KT > 0 ? KT : 1];
-    if constexpr (MG1 && KT > 0) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int k = 0; k < KT; ++k)
-                wreg[cb][k] = to_f32(w[size_t(min(c0 + cb, a.C - 1)) * KT + k]);
-    }
     const int mg_pass = MG1 ? 1 : kMaxMg;
     for (int m0 = 0; m0 < a.Mg; m0 += mg_pass) {
         const int nm = MG1 ? 1 : min(kMaxMg, a.Mg - m0);
-        // Each thread takes UP pixels at a time (kStagedThreads apart), so that
-        // the offsets and masks of all of them are in flight together.
-        for (int pbase = int(threadIdx.x); pbase < a.P; pbase += UP * kStagedThreads) {
-            float acc[UP][CB][kMaxMg];
+        // One tap of one pixel for all CH channels: sample at anchor + tap
+        // offset + the learned offset.  Branch-free: a sample entirely off the
+        // image reads the all-zero window with weight 0.
+        // One sample of one pixel for all CH channels: its four corner
+        // entries and weights.  sample() does the geometry and issues the
+        // reads; blend() accumulates.  Branch-free: a sample entirely off the
+        // image lands on ring zeros.
+        struct Smp {
+            Ent e00, e01, e10, e11;
+            float w00, w01, w10, w11;
+            float wk[CH];                            // tap weights (staged weights only)
+        };
+        auto sample = [&](Smp &sm, int k, int ah, int aw, float oh, float ow, float m) {
+            // Offsets clamped to +-2^24 (a NaN becomes -2^24): farther is off
+            // any image, and the integer parts stay exact.
+            const float lim = 16777216.0f;
+            oh = fminf(fmaxf(oh, -lim), lim);
+            ow = fminf(fmaxf(ow, -lim), lim);
+            const float fh = floorf(oh), fw = floorf(ow);
+            // (integers below 2^25 add exactly in fp32; one med3 clamps each)
+            const int h0 = int(__builtin_amdgcn_fmed3f(float(ah) + fh, -2.0f, float(a.H)));
+            const int w0 = int(__builtin_amdgcn_fmed3f(float(aw) + fw, -2.0f, float(a.W)));
+            const float ly = oh - fh, lx = ow - fw;
+            const float hxm = (1.0f - lx) * m, lxm = lx * m, hy = 1.0f - ly;
+            sm.w00 = hy * hxm;
+            sm.w01 = hy * lxm;
+            sm.w10 = ly * hxm;
+            sm.w11 = ly * lxm;
+            const char *pe = lds + uint32_t((h0 + 2) * PW + (w0 + 2)) * uint32_t(ENT);
+            sm.e00 = *reinterpret_cast<const Ent *>(pe);
+            sm.e01 = *reinterpret_cast<const Ent *>(pe + ENT);
+            sm.e10 = *reinterpret_cast<const Ent *>(pe + size_t(PW) * ENT);
+            sm.e11 = *reinterpret_cast<const Ent *>(pe + size_t(PW + 1) * ENT);
+            if constexpr (MG1 && KT9)
+                __builtin_memcpy(sm.wk, wtab + k * CH, sizeof(sm.wk));
+        };
+        auto blend = [&](float (&acc)[CH][kMaxMg], const Smp &sm, int k) {
 #pragma unroll
-            for (int u = 0; u < UP; ++u)
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
+            for (int ch = 0; ch < CH; ++ch) {
+                float v = sm.w00 * entry_at<T, ENT>(sm.e00, ch);
+                v = fmaf(sm.w01, entry_at<T, ENT>(sm.e01, ch), v);
+                v = fmaf(sm.w10, entry_at<T, ENT>(sm.e10, ch), v);
+                v = fmaf(sm.w11, entry_at<T, ENT>(sm.e11, ch), v);
+                if constexpr (MG1 && KT9) {
+                    acc[ch][0] = fmaf(sm.wk[ch], v, acc[ch][0]);
+                } else {
+                    const int co = min(c0 + ch, a.C - 1) * a.Mg + m0;
 #pragma unroll
                     for (int mm = 0; mm < kMaxMg; ++mm)
-                        acc[u][cb][mm] = 0.0f;
-            // Per pixel slot: the anchor (top-left tap position without offset),
-            // one division per pixel.  A slot past the end works on pixel 0 and
-            // stores nothing.
-            int pix_u[UP], ah[UP], aw[UP];
-#pragma unroll
-            for (int u = 0; u < UP; ++u) {
-                const int pix = pbase + u * kStagedThreads < a.P ? pbase + u * kStagedThreads : 0;
-                const int ho = pix / a.Wo;
-                pix_u[u] = pix;
-                ah[u] = ho * a.sh - a.ph;
-                aw[u] = (pix - ho * a.Wo) * a.sw - a.pw;
+                        if (mm < nm)
+                            acc[ch][mm] = fmaf(to_f32(w[size_t(co + mm) * a.K + k]), v,
+                                               acc[ch][mm]);
+                }
             }
-            // One tap: sample the staged planes at anchor + tap offset + the
-            // learned offset, and accumulate into slot u.  Branch-free: a sample
-            // entirely off the image reads staged entry 0 with factor 0.
-            auto tap = [&](int u, int k, int th, int tw, float oh, float ow, float m) {
-                const float lim = 33554432.0f;       // 2^25: farther is off any image
-                const bool fin = fabsf(oh) <= lim && fabsf(ow) <= lim;
-                const float fh = fin ? floorf(oh) : 0.0f, fw = fin ? floorf(ow) : 0.0f;
-                const int h0 = ah[u] + th + int(fh);
-                const int w0 = aw[u] + tw + int(fw);
-                const bool ok = fin && h0 >= -1 && h0 < a.H && w0 >= -1 && w0 < a.W;
-                // fractions in [0, 1) (0 for a non-finite or huge offset, so
-                // that every weight stays finite and the factor 0 gives 0)
-                const float ly = fin ? oh - fh : 0.0f, lx = fin ? ow - fw : 0.0f;
-                const float hy = 1.0f - ly, hx = 1.0f - lx;
-                const float fac = ok ? m : 0.0f;
-                const float w00 = hy * hx, w10 = ly * hx, w01 = hy * lx, w11 = ly * lx;
-                const int idx = ok ? (h0 + 1) * PW + (w0 + 1) : 0;
+        };
+        auto tap = [&](float (&acc)[CH][kMaxMg], int k, int ah, int aw, float oh, float ow,
+                       float m) {
+            Smp sm;
+            sample(sm, k, ah, aw, oh, ow, m);
+            blend(acc, sm, k);
+        };
+        auto store = [&](const float (&acc)[CH][kMaxMg], int pix) {
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const float2 left = planes[cb * PL + idx];       // (X[h0][w0], X[h0+1][w0])
-                    const float2 right = planes[cb * PL + idx + 1];  // (.., w0+1)
-                    float v = w00 * left.x;
-                    v = fmaf(w10, left.y, v);
-                    v = fmaf(w01, right.x, v);
-                    v = fmaf(w11, right.y, v);
-                    v *= fac;
-                    if constexpr (MG1 && KT > 0) {
-                        acc[u][cb][0] = fmaf(wreg[cb][k], v, acc[u][cb][0]);
-                    } else {
-                        const int co = min(c0 + cb, a.C - 1) * a.Mg + m0;
+            for (int ch = 0; ch < CH; ++ch) {
+                if (ch >= ncb)
+                    break;
 #pragma unroll
-                        for (int mm = 0; mm < kMaxMg; ++mm)
-                            if (mm < nm)
-                                acc[u][cb][mm] = fmaf(to_f32(w[size_t(co + mm) * a.K + k]), v,
-                                                      acc[u][cb][mm]);
+                for (int mm = 0; mm < kMaxMg; ++mm) {
+                    if (mm >= nm)
+                        break;
+                    const int co = (c0 + ch) * a.Mg + m0 + mm;
+                    const float b = a.has_bias ? to_f32(bias[co]) : 0.0f;
+                    out[(size_t(n) * a.Co + co) * a.P + pix] = from_f32<T>(acc[ch][mm] + b);
+                }
+            }
+        };
+        if constexpr (KT9) {
+            // 3x3 taps: the offsets and masks of UP pixels are loaded one
+            // group ahead of their taps (two register sets).
+            struct Geo {
+                T oh[UP][9], ow[UP][9], mk[UP][9];
+            };
+            // Buffer loads from the offset group's rows of this image: the
+            // pixel is the vector offset, the row the scalar one (a plain
+            // pointer per row would hold 27 64-bit addresses in scalar
+            // registers).
+            const uint32_t rowb = uint32_t(a.P) * uint32_t(sizeof(T));
+            const __amdgpu_buffer_rsrc_t roff = dw_rsrc(
+                off + (size_t(n) * a.offC + size_t(q) * 18) * a.P, 18 * rowb);
+            const __amdgpu_buffer_rsrc_t rmsk = dw_rsrc(
+                msk + (size_t(n) * a.mskC + size_t(q) * 9) * a.P, 9 * rowb);
+            auto load_geo = [&](Geo &gs, int pbase) {
+#pragma unroll
+                for (int u = 0; u < UP; ++u) {
+                    // row offsets built up in vector registers: uniform per-row
+                    // offsets would each hold a scalar register for the loop
+                    uint32_t vh = uint32_t(min(pbase + u * kStagedThreads, a.P - 1)) *
+                                  uint32_t(sizeof(T));
+                    uint32_t vm = vh;
+#pragma unroll
+                    for (int k = 0; k < 9; ++k) {
+                        gs.oh[u][k] = dw_load<T>(roff, vh, 0);
+                        gs.ow[u][k] = dw_load<T>(roff, vh + rowb, 0);
+                        gs.mk[u][k] = dw_load<T>(rmsk, vm, 0);
+                        vh += 2 * rowb;
+                        vm += rowb;
                     }
                 }
             };
-            if constexpr (KT > 0) {
-                // 3x3 taps: tap rows/columns are compile-time, all of the
-                // pixels' offsets and masks are in flight at once
-                float oh[UP][KT], ow[UP][KT], mk[UP][KT];
+            auto group = [&](const Geo &gs, int pbase) {
 #pragma unroll
                 for (int u = 0; u < UP; ++u) {
-                    const T *offp = off + (size_t(n) * a.offC + size_t(q) * 2 * KT) * a.P + pix_u[u];
-                    const T *mskp = msk + (size_t(n) * a.mskC + size_t(q) * KT) * a.P + pix_u[u];
+                    const int pix = min(pbase + u * kStagedThreads, a.P - 1);
+                    const int ho = pix / a.Wo;
+                    const int ah = ho * a.sh - a.ph, aw = (pix - ho * a.Wo) * a.sw - a.pw;
+                    float acc[CH][kMaxMg];
 #pragma unroll
-                    for (int k = 0; k < KT; ++k) {
-                        oh[u][k] = to_f32(offp[size_t(2 * k) * a.P]);
-                        ow[u][k] = to_f32(offp[size_t(2 * k + 1) * a.P]);
-                        mk[u][k] = to_f32(mskp[size_t(k) * a.P]);
+                    for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+                        for (int mm = 0; mm < kMaxMg; ++mm)
+                            acc[ch][mm] = 0.0f;
+                    // Taps software-pipelined: tap k+1's geometry and corner
+                    // reads are issued before tap k's blend, so the LDS
+                    // latency overlaps arithmetic.  The accumulators are
+                    // pinned after every blend (an empty asm that claims to
+                    // change them): their only use, the store, is
+                    // conditional, and the compiler would otherwise sink every
+                    // blend into it, keeping all nine taps' corners live.
+                    Smp sp[2];
+                    sample(sp[0], 0, ah, aw, to_f32(gs.oh[u][0]), to_f32(gs.ow[u][0]),
+                           to_f32(gs.mk[u][0]));
+#pragma unroll
+                    for (int k = 0; k < 9; ++k) {
+                        if (k < 8)
+                            sample(sp[(k + 1) & 1], k + 1, ah + ((k + 1) / 3) * a.dh,
+                                   aw + ((k + 1) % 3) * a.dw, to_f32(gs.oh[u][k + 1]),
+                                   to_f32(gs.ow[u][k + 1]), to_f32(gs.mk[u][k + 1]));
+                        blend(acc, sp[k & 1], k);
+#pragma unroll
+                        for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+                            for (int mm = 0; mm < (MG1 ? 1 : kMaxMg); ++mm)
+                                asm volatile("" : "+v"(acc[ch][mm]));
+                        __builtin_amdgcn_sched_barrier(0);
                     }
+                    if (pbase + u * kStagedThreads < a.P)
+                        store(acc, pbase + u * kStagedThreads);
                 }
-#pragma unroll
-                for (int u = 0; u < UP; ++u)
-#pragma unroll
-                    for (int k = 0; k < KT; ++k)
-                        tap(u, k, (k / 3) * a.dh, (k % 3) * a.dw, oh[u][k], ow[u][k], mk[u][k]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < UP; ++u) {
-                    const T *offp = off + (size_t(n) * a.offC + size_t(q) * 2 * a.K) * a.P + pix_u[u];
-                    const T *mskp = msk + (size_t(n) * a.mskC + size_t(q) * a.K) * a.P + pix_u[u];
-                    int i = 0, j = 0;
-                    for (int k = 0; k < a.K; ++k) {
-                        tap(u, k, i * a.dh, j * a.dw, to_f32(offp[size_t(2 * k) * a.P]),
-                            to_f32(offp[size_t(2 * k + 1) * a.P]), to_f32(mskp[size_t(k) * a.P]));
-                        if (++j == a.kw) {
-                            j = 0;
-                            ++i;
-                        }
-                    }
-                }
+            };
+            constexpr int STRIDE = UP * kStagedThreads;
+            Geo g0, g1;
+            int pb = tid;
+            load_geo(g0, pb);
+            // two groups per trip, so that the register sets keep their names
+            for (; pb + STRIDE < a.P; pb += 2 * STRIDE) {
+                load_geo(g1, pb + STRIDE);
+                group(g0, pb);
+                if (pb + 2 * STRIDE < a.P)
+                    load_geo(g0, pb + 2 * STRIDE);
+                group(g1, pb + STRIDE);
             }
+            if (pb < a.P)
+                group(g0, pb);
+        } else {
+            for (int pix = tid; pix < a.P; pix += kStagedThreads) {
+                const int ho = pix / a.Wo;
+                const int ah = ho * a.sh - a.ph, aw = (pix - ho * a.Wo) * a.sw - a.pw;
+                const T *offp = off + (size_t(n) * a.offC + size_t(q) * 2 * a.K) * a.P + pix;
+                const T *mskp = msk + (size_t(n) * a.mskC + size_t(q) * a.K) * a.P + pix;
+                float acc[CH][kMaxMg];
 #pragma unroll
-            for (int u = 0; u < UP; ++u) {
-                const int pix = pbase + u * kStagedThreads;
-                if (pix >= a.P)
-                    break;
+                for (int ch = 0; ch < CH; ++ch)
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    if (cb >= ncb)
-                        break;
-#pragma unroll
-                    for (int mm = 0; mm < kMaxMg; ++mm) {
-                        if (mm >= nm)
-                            break;
-                        const int co = (c0 + cb) * a.Mg + m0 + mm;
-                        const float b = a.has_bias ? to_f32(bias[co]) : 0.0f;
-                        out[(size_t(n) * a.Co + co) * a.P + pix] = from_f32<T>(acc[u][cb][mm] + b);
+                    for (int mm = 0; mm < kMaxMg; ++mm)
+                        acc[ch][mm] = 0.0f;
+                int i = 0, j = 0;
+                for (int k = 0; k < a.K; ++k) {
+                    tap(acc, k, ah + i * a.dh, aw + j * a.dw, to_f32(offp[size_t(2 * k) * a.P]),
+                        to_f32(offp[size_t(2 * k + 1) * a.P]), to_f32(mskp[size_t(k) * a.P]));
+                    if (++j == a.kw) {
+                        j = 0;
+                        ++i;
                     }
                 }
+                store(acc, pix);
             }
         }
     }
@@ -253,19 +392,24 @@ __global__ __launch_bounds__(256) void depthwise_kernel(const T *__restrict__ x,
 template <typename T>
 using DwKernel = void (*)(const T *, const T *, const T *, const T *, const T *, T *, DwArgs);
 
-// The staged kernel instance for (planes, compile-time taps, pixels per
-// thread, exactly one output per input channel).
+// The staged kernel instance for (entry bytes, pixels per thread, 3x3 taps,
+// exactly one output per input channel).
 template <typename T>
-DwKernel<T> staged_fn(int cb, int kt, int up, bool mg1)
+DwKernel<T> staged_fn(int ent, int up, bool kt9, bool mg1)
 {
-#define MDCN_DW_PICK(CB_, KT_, UP_)                                                            \
-    if (cb == CB_ && kt == KT_ && up == UP_)                                                   \
-        return mg1 ? &depthwise_staged_kernel<T, CB_, KT_, UP_, true>                          \
-                   : &depthwise_staged_kernel<T, CB_, KT_, UP_, false>;
-    MDCN_DW_PICK(1, 9, 1) MDCN_DW_PICK(1, 9, 2) MDCN_DW_PICK(1, 9, 4)
-    MDCN_DW_PICK(1, 0, 1) MDCN_DW_PICK(1, 0, 2) MDCN_DW_PICK(1, 0, 4)
-    MDCN_DW_PICK(2, 9, 1) MDCN_DW_PICK(2, 9, 2) MDCN_DW_PICK(2, 9, 4)
-    MDCN_DW_PICK(2, 0, 1) MDCN_DW_PICK(2, 0, 2) MDCN_DW_PICK(2, 0, 4)
+#define MDCN_DW_PICK(ENT_, UP_)                                                                \
+    if (ent == ENT_ && up == UP_) {                                                            \
+        if (kt9)                                                                               \
+            return mg1 ? &depthwise_staged_kernel<T, ENT_, UP_, true, true>                    \
+                       : &depthwise_staged_kernel<T, ENT_, UP_, true, false>;                  \
+        return mg1 ? &depthwise_staged_kernel<T, ENT_, UP_, false, true>                       \
+                   : &depthwise_staged_kernel<T, ENT_, UP_, false, false>;                     \
+    }
+    MDCN_DW_PICK(16, 1) MDCN_DW_PICK(16, 2) MDCN_DW_PICK(8, 1) MDCN_DW_PICK(8, 2)
+    MDCN_DW_PICK(4, 1) MDCN_DW_PICK(4, 2)
+    if constexpr (sizeof(T) == 2) {
+        MDCN_DW_PICK(2, 1) MDCN_DW_PICK(2, 2)
+    }
 #undef MDCN_DW_PICK
     return nullptr;
 }
@@ -283,40 +427,48 @@ hipError_t depthwise_t(const Problem &p, const void *x, const void *offset, cons
     a.dh = int(p.dh); a.dw = int(p.dw);
     a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
     a.has_bias = bias != nullptr;
-    const size_t plane_bytes = size_t(p.H + 1) * size_t(p.W + 2) * sizeof(float2);
-    // Two planes per workgroup when they fit and share an offset group (each
-    // workgroup reads all of its image's offsets and masks, so sharing them
-    // between planes halves that traffic), two pixels per thread in flight.
-    // MDCN_DW_PLANES=1|2 and MDCN_DW_PIXELS=1|2|4 override (for tuning).
-    int cb = (p.Cdg % 2 == 0 && 2 * plane_bytes <= kLdsBytes) ? 2 : 1, up = 2;
-    if (const char *env = std::getenv("MDCN_DW_PLANES")) {
+    const size_t positions = size_t(p.H + 4) * size_t(p.W + 4);
+    // The widest entry whose channels share an offset group and whose plane
+    // fits in LDS; one pixel per thread at a time, the next one's offsets and
+    // masks in flight.  MDCN_DW_ENTRY=<bytes>
+    // and MDCN_DW_PIXELS=1|2 override (for tuning), where allowed.
+    auto allowed = [&](int ent) {
+        const int ch = ent / int(sizeof(T));
+        return ch >= 1 && p.Cdg % ch == 0 &&
+               positions * size_t(ent) + 9 * size_t(ch) * sizeof(float) <= kLdsBytes;
+    };
+    int ent = 0, up = 1;
+    for (int e : {16, 8, 4, 2})
+        if (e >= int(sizeof(T)) && allowed(e)) {
+            ent = e;
+            break;
+        }
+    if (const char *env = std::getenv("MDCN_DW_ENTRY")) {
         const int v = std::atoi(env);
-        if (v == 1)
-            cb = 1;
-        else if (v == 2 && p.Cdg % 2 == 0 && 2 * plane_bytes <= kLdsBytes)
-            cb = 2;
+        if ((v == 16 || v == 8 || v == 4 || v == 2) && v >= int(sizeof(T)) && allowed(v))
+            ent = v;
     }
     if (const char *env = std::getenv("MDCN_DW_PIXELS")) {
         const int v = std::atoi(env);
-        if (v == 1 || v == 2 || v == 4)
+        if (v == 1 || v == 2)
             up = v;
     }
-    if (cb * plane_bytes <= kLdsBytes) {
-        a.cblocks = int((p.C + cb - 1) / cb);
+    if (ent > 0) {
+        const int ch = ent / int(sizeof(T));
+        a.cblocks = int((p.C + ch - 1) / ch);
         const dim3 grid(unsigned(uint64_t(p.N) * a.cblocks));
-        const size_t lds = cb * plane_bytes;
-        const int kt = (p.kh == 3 && p.kw == 3) ? 9 : 0;   // compile-time 3x3 taps
-        const DwKernel<T> fn = staged_fn<T>(cb, kt, up, p.Mg == 1);
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess) {
-            (void)hipGetLastError();       // clear it; use the plain kernel below
-        } else {
+        const size_t lds = positions * size_t(ent) + 9 * size_t(ch) * sizeof(float);
+        const DwKernel<T> fn = staged_fn<T>(ent, up, p.kh == 3 && p.kw == 3, p.Mg == 1);
+        if (fn != nullptr &&
+            hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess) {
             hipLaunchKernelGGL(fn, grid, dim3(kStagedThreads), lds, s, static_cast<const T *>(x),
                                static_cast<const T *>(offset), static_cast<const T *>(mask),
                                static_cast<const T *>(weight), static_cast<const T *>(bias),
                                static_cast<T *>(out), a);
             return hipGetLastError();
         }
+        (void)hipGetLastError();           // clear it; use the plain kernel below
     }
     const dim3 grid((a.total + 255u) / 256u, unsigned(std::min<int64_t>(p.N, 65535)));
     hipLaunchKernelGGL(depthwise_kernel<T>, grid, dim3(256), 0, s, static_cast<const T *>(x),

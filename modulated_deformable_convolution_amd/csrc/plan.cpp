@@ -72,7 +72,10 @@ bool choose_fused_tile(const Problem &p, int64_t chunk, FusedTile *out)
     };
     constexpr int64_t kFill = 192;
     FusedTile pref;
-    if (p.Mg > 128)
+    if (p.elem == 4)
+        pref = FusedTile::M128_N64;     // fp32: half the channels per step; the
+                                        // 8-wave tile with 256 registers a wave wins
+    else if (p.Mg > 128)
         pref = tiles(256, 128) >= kFill ? FusedTile::M256_N128 : FusedTile::M256_N64;
     else
         pref = tiles(128, 128) >= kFill ? FusedTile::M128_N128 : FusedTile::M128_N64;

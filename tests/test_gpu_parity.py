@@ -320,19 +320,50 @@ def test_every_gemm_tile(tile, name, dtype, monkeypatch):
 
 # ---------------------------------------------------------------- depthwise kernel variants
 
-@pytest.mark.parametrize("planes,pixels", [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4)])
-@pytest.mark.parametrize("name", ["depthwise_mult2", "depthwise_5x3"])
-def test_depthwise_variants(planes, pixels, name, monkeypatch):
-    """The staged depthwise kernel with each planes-per-workgroup and
-    pixels-per-thread setting (MDCN_DW_PLANES / MDCN_DW_PIXELS)."""
-    monkeypatch.setenv("MDCN_DW_PLANES", str(planes))
+@pytest.mark.parametrize("entry,pixels", [(16, 1), (16, 2), (8, 1), (8, 2), (4, 1), (4, 2),
+                                          (2, 1)])
+@pytest.mark.parametrize("name,dtype", [("depthwise_mult2", "f32"), ("depthwise_5x3", "f32"),
+                                        ("depthwise_mult2", "f16"), ("depthwise_5x3", "bf16"),
+                                        ("depthwise_mult6_odd", "f32")])
+def test_depthwise_variants(entry, pixels, name, dtype, monkeypatch):
+    """The staged depthwise kernel with each LDS entry width (channels staged
+    interleaved per plane position) and pixels-per-thread setting
+    (MDCN_DW_ENTRY / MDCN_DW_PIXELS; widths a problem cannot use fall back to
+    the default)."""
+    monkeypatch.setenv("MDCN_DW_ENTRY", str(entry))
     monkeypatch.setenv("MDCN_DW_PIXELS", str(pixels))
     pr = SMALL[name]
-    inp = workloads.generate(pr, "f32", seed=14)
+    inp = workloads.generate(pr, dtype, seed=14)
     got = run_gpu(pr, inp, mdcn.MDCN_PATH_DEPTHWISE).double().numpy()
     ref = oracle_full(pr, inp)
-    ok, err, bound = within_tolerance(got, ref, "f32")
-    assert ok, (planes, pixels, name, error_report(got, ref))
+    ok, err, bound = within_tolerance(got, ref, dtype)
+    assert ok, (entry, pixels, name, dtype, error_report(got, ref))
+
+
+@pytest.mark.parametrize("name,dtype,path", [
+    ("multi_tile_dg2", "f32", mdcn.MDCN_PATH_GATHER_GEMM),
+    ("fused_multi_tile", "f16", mdcn.MDCN_PATH_FUSED),
+    ("fused_multi_tile", "f32", mdcn.MDCN_PATH_FUSED),
+    ("depthwise_mult2", "f32", mdcn.MDCN_PATH_DEPTHWISE),
+    ("depthwise_5x3", "bf16", mdcn.MDCN_PATH_DEPTHWISE)])
+def test_nonfinite_and_huge_offsets(name, dtype, path):
+    """A NaN, infinite or far-off-image offset puts its sample off the image:
+    it contributes 0, as in the oracle's zero-padded bilinear read (where any
+    comparison with NaN fails).  One offset in ten is replaced."""
+    pr = SMALL[name]
+    inp = workloads.generate(pr, dtype, seed=21)
+    flat = inp["offset"].clone().view(-1)
+    g = torch.Generator().manual_seed(21)
+    idx = torch.randperm(flat.numel(), generator=g)[: flat.numel() // 10]
+    big = 1e30 if dtype == "f32" else 6e4
+    vals = torch.tensor([float("nan"), float("inf"), float("-inf"), big, -big, 3e3])
+    flat[idx] = vals[torch.arange(idx.numel()) % vals.numel()].to(flat.dtype)
+    inp["offset"] = flat.view(inp["offset"].shape)
+    got = run_gpu(pr, inp, path).double().numpy()
+    ref = oracle_full(pr, inp)
+    assert np.isfinite(ref).all()
+    ok, err, bound = within_tolerance(got, ref, dtype)
+    assert ok, (name, dtype, path, error_report(got, ref))
 
 
 # ---------------------------------------------------------------- fused gather-GEMM tiles
