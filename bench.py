@@ -66,7 +66,7 @@ def sources_sha(files):
     return h.hexdigest()[:16]
 
 
-def kernel_model(pr, dtype, plan_chunk):
+def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
     """Algorithmic bytes and flops of one launch of each kernel, for a launch
     over `cnt` images.  Bytes count each tensor a kernel must touch once."""
     e = ELEM[dtype]
@@ -101,8 +101,16 @@ def kernel_model(pr, dtype, plan_chunk):
             # x (NHWC copy), offsets and masks read once, output written once
             return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + pr.Co * Kp * e
                         + bias_bytes, flops=2 * cnt * pr.Co * Kg * P)
+        if name == "depthwise_geometry":
+            # offsets and masks read once, a 16-byte record per offset group, tap
+            # and pixel written once
+            return dict(bytes=cnt * (off_img + msk_img + 16 * dg * K * P), flops=0)
         if name == "depthwise_direct":
-            return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + w_bytes + bias_bytes,
+            # with the geometry (staged kernel): x and the geometry read
+            # once, output written once; without it (plain kernel): x,
+            # offsets and masks
+            geo_in = 16 * dg * K * P if plan_geo else off_img + msk_img
+            return dict(bytes=cnt * (x_img + geo_in + out_img) + w_bytes + bias_bytes,
                         flops=2 * cnt * pr.Co * Kg * P)
         raise KeyError(name)
     return per_launch
@@ -205,14 +213,14 @@ def main(argv=None) -> int:
     for tok in plan.split():
         if tok.startswith("chunk="):
             chunk = int(tok.split("=")[1])
-    model = kernel_model(pr, dtype, chunk)
+    model = kernel_model(pr, dtype, chunk, plan_geo="depthwise_geometry" in per_kernel)
     kernels = {}
     for name, (count, total_ms) in per_kernel.items():
         avg_ms = total_ms / count
         launches_per_step = count / args.steps
-        cnt = pr.N if name == "depthwise_direct" else (
-            pr.N / max(1, launches_per_step)
-            if name in ("to_nhwc", "deform_gather", "gemm_bias", "fused_gather_gemm") else 0)
+        cnt = (pr.N / max(1, launches_per_step)
+               if name in ("to_nhwc", "deform_gather", "gemm_bias", "fused_gather_gemm",
+                           "depthwise_geometry", "depthwise_direct") else 0)
         m = model(name, cnt)
         kernels[name] = dict(launches_per_step=launches_per_step, avg_ms=avg_ms,
                              ms_per_step=total_ms / args.steps,

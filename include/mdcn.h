@@ -84,9 +84,12 @@ typedef enum mdcn_path {
     MDCN_PATH_GATHER_GEMM = 1, /* deformable im2col into the workspace, then a grouped
                                   MFMA GEMM with the bias fused in its epilogue
                                   [plugin guide §五 steps 1-3]                             */
-    MDCN_PATH_DEPTHWISE = 2,   /* one direct gather-and-multiply-add kernel; requires
+    MDCN_PATH_DEPTHWISE = 2,   /* a direct gather-and-multiply-add kernel; requires
                                   C/group == 1 [plugin guide §三: group == #outputs is the
-                                  depthwise case]                                         */
+                                  depthwise case].  Where a plane of the input fits in LDS
+                                  the sampling geometry (16 bytes per offset group, tap and
+                                  output pixel) is first written to the workspace by a
+                                  small kernel; otherwise no workspace is used            */
     MDCN_PATH_FUSED = 3        /* the gather fused into the MFMA GEMM: the GEMM's B tiles
                                   are made in LDS from the bilinear samples, with no column
                                   buffer [plugin guide §五 steps 1-3 without the columns];
@@ -181,7 +184,8 @@ mdcn_status mdcn_trace_count(const mdcn_trace *trace, int32_t *count);
  * MDCN_E_LAUNCH. */
 mdcn_status mdcn_trace_read(mdcn_trace *trace, int32_t i, int32_t *kernel_id, float *ms);
 
-/* Name of a kernel id ("deform_gather", "gemm_bias", "fused_gather_gemm", ...);
+/* Name of a kernel id ("pack_weight", "to_nhwc", "deform_gather",
+ * "gemm_bias", "depthwise_direct", "fused_gather_gemm", "depthwise_geometry");
  * "?" if unknown. */
 const char *mdcn_kernel_name(int32_t kernel_id);
 

@@ -109,7 +109,7 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         return MDCN_OK;                 // nothing to compute
     if (!x || !offset || !mask || !weight || !out)
         return MDCN_E_NULL;
-    if (plan.path != Path::Depthwise) {
+    if (plan.ws_bytes > 0) {
         if (!workspace)
             return MDCN_E_WORKSPACE;
         st = mdcn::make_plan(op->attrs, p, workspace_bytes, false, &plan);
@@ -128,11 +128,11 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     const Range out_r = range_of(out, size_t(p.N * p.Co * p.P) * e);
     // the workspace layout starts at the caller's pointer aligned up to kAlign
     char *ws = nullptr;
-    if (plan.path != Path::Depthwise) {
+    if (plan.ws_bytes > 0) {
         const uintptr_t raw = reinterpret_cast<uintptr_t>(workspace);
         ws = reinterpret_cast<char *>((raw + mdcn::kAlign - 1) / mdcn::kAlign * mdcn::kAlign);
     }
-    const Range ws_r = range_of(ws, plan.path != Path::Depthwise ? plan.ws_bytes : 0);
+    const Range ws_r = range_of(ws, plan.ws_bytes);
     for (const Range &in : inputs) {
         if (overlap(out_r, in) || overlap(ws_r, in))
             return MDCN_E_ALIAS;
@@ -148,11 +148,32 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     Recorder rec{stream, trace};
     hipError_t err = hipSuccess;
 
+    const size_t x_img = size_t(p.C * p.H * p.W) * e;
+    const size_t off_img = size_t(2 * p.DG * p.K * p.P) * e;
+    const size_t msk_img = size_t(p.DG * p.K * p.P) * e;
+    const size_t out_img = size_t(p.Co * p.P) * e;
     if (plan.path == Path::Depthwise) {
-        err = rec.run(mdcn::K_DEPTHWISE, [&] {
-            return mdcn::launch_depthwise(p, x, offset, mask, weight, bias, out, stream);
-        });
-        return err == hipSuccess ? MDCN_OK : MDCN_E_LAUNCH;
+        for (int64_t n0 = 0; n0 < p.N; n0 += plan.chunk) {
+            const int64_t cnt = std::min<int64_t>(plan.chunk, p.N - n0);
+            const char *xc = static_cast<const char *>(x) + size_t(n0) * x_img;
+            const char *oc = static_cast<const char *>(offset) + size_t(n0) * off_img;
+            const char *mc = static_cast<const char *>(mask) + size_t(n0) * msk_img;
+            char *outc = static_cast<char *>(out) + size_t(n0) * out_img;
+            if (plan.ws_bytes > 0) {
+                err = rec.run(mdcn::K_DW_GEOMETRY, [&] {
+                    return mdcn::launch_dw_geometry(p, cnt, oc, mc, ws, stream);
+                });
+                if (err != hipSuccess)
+                    return MDCN_E_LAUNCH;
+            }
+            err = rec.run(mdcn::K_DEPTHWISE, [&] {
+                return mdcn::launch_depthwise(p, cnt, xc, plan.ws_bytes > 0 ? ws : nullptr, oc,
+                                              mc, weight, bias, outc, stream);
+            });
+            if (err != hipSuccess)
+                return MDCN_E_LAUNCH;
+        }
+        return MDCN_OK;
     }
 
     void *wpack = ws + plan.wpack_off;
@@ -162,10 +183,6 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
                   [&] { return mdcn::launch_pack_weight(p, plan, weight, wpack, stream); });
     if (err != hipSuccess)
         return MDCN_E_LAUNCH;
-    const size_t x_img = size_t(p.C * p.H * p.W) * e;
-    const size_t off_img = size_t(2 * p.DG * p.K * p.P) * e;
-    const size_t msk_img = size_t(p.DG * p.K * p.P) * e;
-    const size_t out_img = size_t(p.Co * p.P) * e;
     for (int64_t n0 = 0; n0 < p.N; n0 += plan.chunk) {
         const int64_t cnt = std::min<int64_t>(plan.chunk, p.N - n0);
         const char *xc = static_cast<const char *>(x) + size_t(n0) * x_img;
@@ -280,7 +297,7 @@ mdcn_status mdcn_workspace_bytes(const mdcn_op *op, mdcn_dtype dtype, const int6
         st = mdcn::make_plan(op->attrs, p, 0, true, &plan);
         if (st != MDCN_OK)
             return st;
-        const bool none = plan.path == Path::Depthwise || p.N == 0 || p.P == 0;
+        const bool none = plan.ws_bytes == 0 || p.N == 0 || p.P == 0;
         *bytes = none ? 0 : mdcn::workspace_request(plan);
         if (min_bytes)
             *min_bytes = none ? 0 : mdcn::min_workspace(p, plan);
@@ -402,6 +419,7 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_GEMM: return "gemm_bias";
     case mdcn::K_DEPTHWISE: return "depthwise_direct";
     case mdcn::K_FUSED: return "fused_gather_gemm";
+    case mdcn::K_DW_GEOMETRY: return "depthwise_geometry";
     }
     return "?";
 }
@@ -442,8 +460,12 @@ mdcn_status mdcn_describe_plan(const mdcn_op *op, mdcn_dtype dtype, const int64_
         if (st != MDCN_OK)
             return st;
         if (plan.path == Path::Depthwise)
-            std::snprintf(buf, len, "path=depthwise_direct N=%lld C=%lld Co=%lld P=%lld ws=0",
-                          (long long)p.N, (long long)p.C, (long long)p.Co, (long long)p.P);
+            std::snprintf(buf, len,
+                          "path=depthwise_direct N=%lld C=%lld Co=%lld P=%lld chunk=%lld entry=%d "
+                          "ws=%zu (geometry/img=%zu)",
+                          (long long)p.N, (long long)p.C, (long long)p.Co, (long long)p.P,
+                          (long long)plan.chunk, mdcn::dw_default_entry(p), plan.ws_bytes,
+                          plan.geo_bytes_per_image);
         else if (plan.path == Path::Fused)
             std::snprintf(buf, len,
                           "path=fused chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld tile=%d "

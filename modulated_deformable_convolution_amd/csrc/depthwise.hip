@@ -25,10 +25,18 @@
 // zeros, so it contributes 0 whatever its weights.  Taps need no validity
 // test, and no input value can leak into an off-image sample.
 //
+// The geometry of a sample depends on the image, offset group, tap and
+// pixel, not on the channel, so a small kernel computes it once per image
+// (dw_geometry_kernel, one 16-byte record per sample) and every channel
+// block of the image reads it back instead of recomputing it from offsets
+// and masks.  A sample entirely off the image gets the record of one fixed
+// window of ring zeros: the lanes holding such samples then read the same
+// LDS addresses, which costs no bank conflicts (random samples spread over
+// the plane are what bounds this kernel).
 // Workgroups are ordered so that those of one image run on one XCD: the
-// image's offsets and masks, read by every channel block, stay in that L2.
-// When not even a one-channel plane fits in LDS, a plain kernel reading x
-// from global memory is used instead.
+// image's geometry, read by every channel block, stays in that L2.
+// When not even a one-channel plane fits in LDS, a plain kernel reading x,
+// offsets and masks from global memory is used instead (no workspace).
 #include <cstdlib>
 
 #include "device_common.h"
@@ -45,11 +53,87 @@ struct DwArgs {
     int offC, mskC;
     int has_bias;
     int cblocks;             // channel blocks per image (staged kernel)
+    int DG;
 };
+
+// Sampling geometry: rows r = (img*DG + q)*K + k of P records, one per
+// (image, offset group, tap, pixel).  A record holds the index of the
+// sample's top-left corner in the zero-ringed (H+4) x (W+4) plane, the
+// fractional row part ly, and the two column weights with the mask folded in,
+// lx*m and (1-lx)*m; the four bilinear weights are their products with ly
+// and 1-ly.
+struct DwGeoArgs {
+    uint32_t groups;         // cnt * DG
+    int P, Wo, K, kw, DG, H, W, PW;
+    int sh, sw, ph, pw, dh, dw;
+    int offC, mskC;
+};
+
+constexpr int kGeoThreads = 128;
+constexpr int kGeoTaps = 9;                  // taps whose inputs are loaded at once
+
+// One thread per (image, offset group, pixel), all taps: the loads of up to
+// kGeoTaps taps are issued together (a thread per record would have one load
+// in flight and retire after one round trip).
+template <typename T>
+__global__ __launch_bounds__(kGeoThreads) void dw_geometry_kernel(const T *__restrict__ off,
+                                                                  const T *__restrict__ msk,
+                                                                  uint4 *__restrict__ geo,
+                                                                  DwGeoArgs a)
+{
+    const int pix = int(blockIdx.x) * kGeoThreads + int(threadIdx.x);
+    if (pix >= a.P)
+        return;
+    const int ho = pix / a.Wo, wo = pix - (pix / a.Wo) * a.Wo;
+    const int bh = ho * a.sh - a.ph, bw = wo * a.sw - a.pw;
+    // grid y over (image, offset group), strided when there are more
+    for (uint32_t g = blockIdx.y; g < a.groups; g += gridDim.y) {
+        const int q = int(g % uint32_t(a.DG));
+        const int img = int(g / uint32_t(a.DG));
+        const T *ob = off + (size_t(img) * a.offC + size_t(q) * 2 * a.K) * a.P + pix;
+        const T *mb = msk + (size_t(img) * a.mskC + size_t(q) * a.K) * a.P + pix;
+        uint4 *gb = geo + size_t(g) * a.K * a.P + pix;
+        for (int k0 = 0; k0 < a.K; k0 += kGeoTaps) {
+            float oh[kGeoTaps], ow[kGeoTaps], m[kGeoTaps];
+#pragma unroll
+            for (int t = 0; t < kGeoTaps; ++t) {
+                const int k = min(k0 + t, a.K - 1);
+                oh[t] = to_f32(ob[size_t(2 * k) * a.P]);
+                ow[t] = to_f32(ob[size_t(2 * k + 1) * a.P]);
+                m[t] = to_f32(mb[size_t(k) * a.P]);
+            }
+#pragma unroll
+            for (int t = 0; t < kGeoTaps; ++t) {
+                const int k = k0 + t;
+                if (k >= a.K)
+                    break;
+                const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+                const int ah = bh + i * a.dh, aw = bw + j * a.dw;
+                // Offsets clamped to +-2^24 (a NaN becomes -2^24): farther is
+                // off any image, and the integer parts stay exact.  A sample
+                // whose top-left corner (h0, w0) lies outside [-1, H-1] x
+                // [-1, W-1] has no corner on the image; it gets entry 0, whose
+                // 2 x 2 window (ring rows and columns 0 and 1) is all zeros,
+                // so it contributes 0 whatever its weights.
+                const float lim = 16777216.0f;
+                const float vh = fminf(fmaxf(oh[t], -lim), lim);
+                const float vw = fminf(fmaxf(ow[t], -lim), lim);
+                const float fh = floorf(vh), fw = floorf(vw);
+                const float h0 = float(ah) + fh, w0 = float(aw) + fw;
+                const bool on = (h0 >= -1.0f) & (h0 <= float(a.H - 1)) & (w0 >= -1.0f) &
+                                (w0 <= float(a.W - 1));
+                const uint32_t e = on ? uint32_t((int(h0) + 2) * a.PW + (int(w0) + 2)) : 0u;
+                const float ly = vh - fh, lx = vw - fw;
+                gb[size_t(k) * a.P] = make_uint4(e, __builtin_bit_cast(uint32_t, ly),
+                                                 __builtin_bit_cast(uint32_t, lx * m[t]),
+                                                 __builtin_bit_cast(uint32_t, (1.0f - lx) * m[t]));
+            }
+        }
+    }
+}
 
 constexpr int kStagedThreads = 512;
 constexpr int kMaxMg = 4;                    // output channels per input channel per pass
-constexpr size_t kLdsBytes = 160 * 1024;
 
 template <int ENT> struct EntryType;
 template <> struct EntryType<16> { typedef uint4 type; };
@@ -94,8 +178,8 @@ __device__ __forceinline__ T dw_load(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint
 
 template <typename T, int ENT, int UP, bool KT9, bool MG1>
 __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
-    const T *__restrict__ x, const T *__restrict__ off, const T *__restrict__ msk,
-    const T *__restrict__ w, const T *__restrict__ bias, T *__restrict__ out, DwArgs a)
+    const T *__restrict__ x, const uint4 *__restrict__ geo, const T *__restrict__ w,
+    const T *__restrict__ bias, T *__restrict__ out, DwArgs a)
 {
     constexpr int CH = ENT / int(sizeof(T));        // channels per entry
     using Ent = typename EntryType<ENT>::type;
@@ -155,38 +239,29 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
     __syncthreads();
 
     const int q = c0 / a.Cdg;                        // every staged channel is in block q
+    // This image's geometry of offset group q: per tap a row of P records.
+    const uint32_t rowb = uint32_t(a.P) * 16u;
+    const __amdgpu_buffer_rsrc_t rgeo =
+        dw_rsrc(geo + (size_t(n) * a.DG + q) * size_t(a.K) * size_t(a.P), uint32_t(a.K) * rowb);
     const int mg_pass = MG1 ? 1 : kMaxMg;
     for (int m0 = 0; m0 < a.Mg; m0 += mg_pass) {
         const int nm = MG1 ? 1 : min(kMaxMg, a.Mg - m0);
-        // One tap of one pixel for all CH channels: sample at anchor + tap
-        // offset + the learned offset.  Branch-free: a sample entirely off the
-        // image reads the all-zero window with weight 0.
         // One sample of one pixel for all CH channels: its four corner
-        // entries and weights.  sample() does the geometry and issues the
-        // reads; blend() accumulates.  Branch-free: a sample entirely off the
-        // image lands on ring zeros.
+        // entries and weights.  sample() issues the reads, blend()
+        // accumulates.  A sample entirely off the image lands on ring zeros.
         struct Smp {
             Ent e00, e01, e10, e11;
-            float w00, w01, w10, w11;
+            float w[4];
             float wk[CH];                            // tap weights (staged weights only)
         };
-        auto sample = [&](Smp &sm, int k, int ah, int aw, float oh, float ow, float m) {
-            // Offsets clamped to +-2^24 (a NaN becomes -2^24): farther is off
-            // any image, and the integer parts stay exact.
-            const float lim = 16777216.0f;
-            oh = fminf(fmaxf(oh, -lim), lim);
-            ow = fminf(fmaxf(ow, -lim), lim);
-            const float fh = floorf(oh), fw = floorf(ow);
-            // (integers below 2^25 add exactly in fp32; one med3 clamps each)
-            const int h0 = int(__builtin_amdgcn_fmed3f(float(ah) + fh, -2.0f, float(a.H)));
-            const int w0 = int(__builtin_amdgcn_fmed3f(float(aw) + fw, -2.0f, float(a.W)));
-            const float ly = oh - fh, lx = ow - fw;
-            const float hxm = (1.0f - lx) * m, lxm = lx * m, hy = 1.0f - ly;
-            sm.w00 = hy * hxm;
-            sm.w01 = hy * lxm;
-            sm.w10 = ly * hxm;
-            sm.w11 = ly * lxm;
-            const char *pe = lds + uint32_t((h0 + 2) * PW + (w0 + 2)) * uint32_t(ENT);
+        auto sample = [&](Smp &sm, int k, const uint4 &g) {
+            const float ly = __builtin_bit_cast(float, g.y);
+            const float lxm = __builtin_bit_cast(float, g.z), hxm = __builtin_bit_cast(float, g.w);
+            sm.w[0] = fmaf(-ly, hxm, hxm);
+            sm.w[1] = fmaf(-ly, lxm, lxm);
+            sm.w[2] = ly * hxm;
+            sm.w[3] = ly * lxm;
+            const char *pe = lds + g.x * uint32_t(ENT);
             sm.e00 = *reinterpret_cast<const Ent *>(pe);
             sm.e01 = *reinterpret_cast<const Ent *>(pe + ENT);
             sm.e10 = *reinterpret_cast<const Ent *>(pe + size_t(PW) * ENT);
@@ -197,10 +272,10 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
         auto blend = [&](float (&acc)[CH][kMaxMg], const Smp &sm, int k) {
 #pragma unroll
             for (int ch = 0; ch < CH; ++ch) {
-                float v = sm.w00 * entry_at<T, ENT>(sm.e00, ch);
-                v = fmaf(sm.w01, entry_at<T, ENT>(sm.e01, ch), v);
-                v = fmaf(sm.w10, entry_at<T, ENT>(sm.e10, ch), v);
-                v = fmaf(sm.w11, entry_at<T, ENT>(sm.e11, ch), v);
+                float v = sm.w[0] * entry_at<T, ENT>(sm.e00, ch);
+                v = fmaf(sm.w[1], entry_at<T, ENT>(sm.e01, ch), v);
+                v = fmaf(sm.w[2], entry_at<T, ENT>(sm.e10, ch), v);
+                v = fmaf(sm.w[3], entry_at<T, ENT>(sm.e11, ch), v);
                 if constexpr (MG1 && KT9) {
                     acc[ch][0] = fmaf(sm.wk[ch], v, acc[ch][0]);
                 } else {
@@ -213,11 +288,16 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
                 }
             }
         };
-        auto tap = [&](float (&acc)[CH][kMaxMg], int k, int ah, int aw, float oh, float ow,
-                       float m) {
-            Smp sm;
-            sample(sm, k, ah, aw, oh, ow, m);
-            blend(acc, sm, k);
+        // The accumulators are pinned after every blend (an empty asm that
+        // claims to change them): their only use, the store, is conditional,
+        // and the compiler would otherwise sink every blend into it, keeping
+        // all the taps' corners live.
+        auto pin = [&](float (&acc)[CH][kMaxMg]) {
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch)
+#pragma unroll
+                for (int mm = 0; mm < (MG1 ? 1 : kMaxMg); ++mm)
+                    asm volatile("" : "+v"(acc[ch][mm]));
         };
         auto store = [&](const float (&acc)[CH][kMaxMg], int pix) {
 #pragma unroll
@@ -234,73 +314,50 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
                 }
             }
         };
+        // One tap's geometry record (vector offset vo = the pixel's record).
+        auto load_tap = [&](uint4 &g, uint32_t vo) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rgeo, vo, 0, 0);
+            g = make_uint4(v[0], v[1], v[2], v[3]);
+        };
         if constexpr (KT9) {
-            // 3x3 taps: the offsets and masks of UP pixels are loaded one
-            // group ahead of their taps (two register sets).
+            // 3x3 taps: the geometry of UP pixels is loaded one group ahead
+            // of their taps (two register sets).
             struct Geo {
-                T oh[UP][9], ow[UP][9], mk[UP][9];
+                uint4 g[UP][9];
             };
-            // Buffer loads from the offset group's rows of this image: the
-            // pixel is the vector offset, the row the scalar one (a plain
-            // pointer per row would hold 27 64-bit addresses in scalar
-            // registers).
-            const uint32_t rowb = uint32_t(a.P) * uint32_t(sizeof(T));
-            const __amdgpu_buffer_rsrc_t roff = dw_rsrc(
-                off + (size_t(n) * a.offC + size_t(q) * 18) * a.P, 18 * rowb);
-            const __amdgpu_buffer_rsrc_t rmsk = dw_rsrc(
-                msk + (size_t(n) * a.mskC + size_t(q) * 9) * a.P, 9 * rowb);
             auto load_geo = [&](Geo &gs, int pbase) {
 #pragma unroll
                 for (int u = 0; u < UP; ++u) {
                     // row offsets built up in vector registers: uniform per-row
                     // offsets would each hold a scalar register for the loop
-                    uint32_t vh = uint32_t(min(pbase + u * kStagedThreads, a.P - 1)) *
-                                  uint32_t(sizeof(T));
-                    uint32_t vm = vh;
+                    uint32_t vo = uint32_t(min(pbase + u * kStagedThreads, a.P - 1)) * 16u;
 #pragma unroll
                     for (int k = 0; k < 9; ++k) {
-                        gs.oh[u][k] = dw_load<T>(roff, vh, 0);
-                        gs.ow[u][k] = dw_load<T>(roff, vh + rowb, 0);
-                        gs.mk[u][k] = dw_load<T>(rmsk, vm, 0);
-                        vh += 2 * rowb;
-                        vm += rowb;
+                        load_tap(gs.g[u][k], vo);
+                        vo += rowb;
                     }
                 }
             };
             auto group = [&](const Geo &gs, int pbase) {
 #pragma unroll
                 for (int u = 0; u < UP; ++u) {
-                    const int pix = min(pbase + u * kStagedThreads, a.P - 1);
-                    const int ho = pix / a.Wo;
-                    const int ah = ho * a.sh - a.ph, aw = (pix - ho * a.Wo) * a.sw - a.pw;
                     float acc[CH][kMaxMg];
 #pragma unroll
                     for (int ch = 0; ch < CH; ++ch)
 #pragma unroll
                         for (int mm = 0; mm < kMaxMg; ++mm)
                             acc[ch][mm] = 0.0f;
-                    // Taps software-pipelined: tap k+1's geometry and corner
-                    // reads are issued before tap k's blend, so the LDS
-                    // latency overlaps arithmetic.  The accumulators are
-                    // pinned after every blend (an empty asm that claims to
-                    // change them): their only use, the store, is
-                    // conditional, and the compiler would otherwise sink every
-                    // blend into it, keeping all nine taps' corners live.
+                    // Taps software-pipelined: tap k+1's corner reads are
+                    // issued before tap k's blend, so the LDS latency overlaps
+                    // arithmetic.
                     Smp sp[2];
-                    sample(sp[0], 0, ah, aw, to_f32(gs.oh[u][0]), to_f32(gs.ow[u][0]),
-                           to_f32(gs.mk[u][0]));
+                    sample(sp[0], 0, gs.g[u][0]);
 #pragma unroll
                     for (int k = 0; k < 9; ++k) {
                         if (k < 8)
-                            sample(sp[(k + 1) & 1], k + 1, ah + ((k + 1) / 3) * a.dh,
-                                   aw + ((k + 1) % 3) * a.dw, to_f32(gs.oh[u][k + 1]),
-                                   to_f32(gs.ow[u][k + 1]), to_f32(gs.mk[u][k + 1]));
+                            sample(sp[(k + 1) & 1], k + 1, gs.g[u][k + 1]);
                         blend(acc, sp[k & 1], k);
-#pragma unroll
-                        for (int ch = 0; ch < CH; ++ch)
-#pragma unroll
-                            for (int mm = 0; mm < (MG1 ? 1 : kMaxMg); ++mm)
-                                asm volatile("" : "+v"(acc[ch][mm]));
+                        pin(acc);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     if (pbase + u * kStagedThreads < a.P)
@@ -323,24 +380,21 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
                 group(g0, pb);
         } else {
             for (int pix = tid; pix < a.P; pix += kStagedThreads) {
-                const int ho = pix / a.Wo;
-                const int ah = ho * a.sh - a.ph, aw = (pix - ho * a.Wo) * a.sw - a.pw;
-                const T *offp = off + (size_t(n) * a.offC + size_t(q) * 2 * a.K) * a.P + pix;
-                const T *mskp = msk + (size_t(n) * a.mskC + size_t(q) * a.K) * a.P + pix;
                 float acc[CH][kMaxMg];
 #pragma unroll
                 for (int ch = 0; ch < CH; ++ch)
 #pragma unroll
                     for (int mm = 0; mm < kMaxMg; ++mm)
                         acc[ch][mm] = 0.0f;
-                int i = 0, j = 0;
+                uint32_t vo = uint32_t(pix) * 16u;
                 for (int k = 0; k < a.K; ++k) {
-                    tap(acc, k, ah + i * a.dh, aw + j * a.dw, to_f32(offp[size_t(2 * k) * a.P]),
-                        to_f32(offp[size_t(2 * k + 1) * a.P]), to_f32(mskp[size_t(k) * a.P]));
-                    if (++j == a.kw) {
-                        j = 0;
-                        ++i;
-                    }
+                    uint4 g;
+                    load_tap(g, vo);
+                    vo += rowb;
+                    Smp sm;
+                    sample(sm, k, g);
+                    blend(acc, sm, k);
+                    pin(acc);
                 }
                 store(acc, pix);
             }
@@ -390,7 +444,7 @@ __global__ __launch_bounds__(256) void depthwise_kernel(const T *__restrict__ x,
 }
 
 template <typename T>
-using DwKernel = void (*)(const T *, const T *, const T *, const T *, const T *, T *, DwArgs);
+using DwKernel = void (*)(const T *, const uint4 *, const T *, const T *, T *, DwArgs);
 
 // The staged kernel instance for (entry bytes, pixels per thread, 3x3 taps,
 // exactly one output per input channel).
@@ -415,37 +469,27 @@ DwKernel<T> staged_fn(int ent, int up, bool kt9, bool mg1)
 }
 
 template <typename T>
-hipError_t depthwise_t(const Problem &p, const void *x, const void *offset, const void *mask,
-                       const void *weight, const void *bias, void *out, hipStream_t s)
+hipError_t depthwise_t(const Problem &p, int64_t cnt, const void *x, const void *geo,
+                       const void *offset, const void *mask, const void *weight, const void *bias,
+                       void *out, hipStream_t s)
 {
     DwArgs a;
     a.total = uint32_t(p.Co * p.P);
-    a.N = int(p.N); a.C = int(p.C); a.H = int(p.H); a.W = int(p.W); a.HW = int(p.H * p.W);
+    a.N = int(cnt); a.C = int(p.C); a.H = int(p.H); a.W = int(p.W); a.HW = int(p.H * p.W);
     a.Co = int(p.Co); a.Mg = int(p.Mg); a.Cdg = int(p.Cdg); a.K = int(p.K); a.P = int(p.P);
     a.Wo = int(p.Wo); a.kw = int(p.kw);
     a.sh = int(p.sh); a.sw = int(p.sw); a.ph = int(p.ph); a.pw = int(p.pw);
     a.dh = int(p.dh); a.dw = int(p.dw);
     a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
     a.has_bias = bias != nullptr;
-    const size_t positions = size_t(p.H + 4) * size_t(p.W + 4);
-    // The widest entry whose channels share an offset group and whose plane
-    // fits in LDS; one pixel per thread at a time, the next one's offsets and
-    // masks in flight.  MDCN_DW_ENTRY=<bytes>
-    // and MDCN_DW_PIXELS=1|2 override (for tuning), where allowed.
-    auto allowed = [&](int ent) {
-        const int ch = ent / int(sizeof(T));
-        return ch >= 1 && p.Cdg % ch == 0 &&
-               positions * size_t(ent) + 9 * size_t(ch) * sizeof(float) <= kLdsBytes;
-    };
-    int ent = 0, up = 1;
-    for (int e : {16, 8, 4, 2})
-        if (e >= int(sizeof(T)) && allowed(e)) {
-            ent = e;
-            break;
-        }
+    a.DG = int(p.DG);
+    // The widest allowed entry, one pixel per thread at a time with the next
+    // one's geometry in flight.  MDCN_DW_ENTRY=<bytes> and MDCN_DW_PIXELS=1|2
+    // override (for tuning), where allowed.
+    int ent = dw_default_entry(p), up = 1;
     if (const char *env = std::getenv("MDCN_DW_ENTRY")) {
         const int v = std::atoi(env);
-        if ((v == 16 || v == 8 || v == 4 || v == 2) && v >= int(sizeof(T)) && allowed(v))
+        if ((v == 16 || v == 8 || v == 4 || v == 2) && dw_entry_allowed(p, v))
             ent = v;
     }
     if (const char *env = std::getenv("MDCN_DW_PIXELS")) {
@@ -453,24 +497,25 @@ hipError_t depthwise_t(const Problem &p, const void *x, const void *offset, cons
         if (v == 1 || v == 2)
             up = v;
     }
-    if (ent > 0) {
+    if (ent > 0 && geo != nullptr) {
         const int ch = ent / int(sizeof(T));
         a.cblocks = int((p.C + ch - 1) / ch);
-        const dim3 grid(unsigned(uint64_t(p.N) * a.cblocks));
-        const size_t lds = positions * size_t(ent) + 9 * size_t(ch) * sizeof(float);
+        const dim3 grid(unsigned(uint64_t(cnt) * a.cblocks));
+        const size_t lds = size_t(p.H + 4) * size_t(p.W + 4) * size_t(ent) +
+                           9 * size_t(ch) * sizeof(float);
         const DwKernel<T> fn = staged_fn<T>(ent, up, p.kh == 3 && p.kw == 3, p.Mg == 1);
         if (fn != nullptr &&
             hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess) {
             hipLaunchKernelGGL(fn, grid, dim3(kStagedThreads), lds, s, static_cast<const T *>(x),
-                               static_cast<const T *>(offset), static_cast<const T *>(mask),
+                               static_cast<const uint4 *>(geo),
                                static_cast<const T *>(weight), static_cast<const T *>(bias),
                                static_cast<T *>(out), a);
             return hipGetLastError();
         }
         (void)hipGetLastError();           // clear it; use the plain kernel below
     }
-    const dim3 grid((a.total + 255u) / 256u, unsigned(std::min<int64_t>(p.N, 65535)));
+    const dim3 grid((a.total + 255u) / 256u, unsigned(std::min<int64_t>(cnt, 65535)));
     hipLaunchKernelGGL(depthwise_kernel<T>, grid, dim3(256), 0, s, static_cast<const T *>(x),
                        static_cast<const T *>(offset), static_cast<const T *>(mask),
                        static_cast<const T *>(weight), static_cast<const T *>(bias),
@@ -478,16 +523,49 @@ hipError_t depthwise_t(const Problem &p, const void *x, const void *offset, cons
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t dw_geometry_t(const Problem &p, int64_t cnt, const void *offset, const void *mask,
+                         void *geo, hipStream_t s)
+{
+    DwGeoArgs a;
+    a.groups = uint32_t(cnt * p.DG);
+    a.P = int(p.P); a.Wo = int(p.Wo); a.K = int(p.K); a.kw = int(p.kw); a.DG = int(p.DG);
+    a.H = int(p.H); a.W = int(p.W); a.PW = int(p.W + 4);
+    a.sh = int(p.sh); a.sw = int(p.sw); a.ph = int(p.ph); a.pw = int(p.pw);
+    a.dh = int(p.dh); a.dw = int(p.dw);
+    a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
+    const dim3 grid(unsigned((p.P + kGeoThreads - 1) / kGeoThreads),
+                    std::min<unsigned>(a.groups, 65535u));
+    hipLaunchKernelGGL(dw_geometry_kernel<T>, grid, dim3(kGeoThreads), 0, s,
+                       static_cast<const T *>(offset), static_cast<const T *>(mask),
+                       static_cast<uint4 *>(geo), a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_depthwise(const Problem &p, const void *x, const void *offset,
-                            const void *mask, const void *weight, const void *bias, void *out,
-                            hipStream_t stream)
+hipError_t launch_depthwise(const Problem &p, int64_t cnt, const void *x, const void *geo,
+                            const void *offset, const void *mask, const void *weight,
+                            const void *bias, void *out, hipStream_t stream)
 {
     switch (p.dtype) {
-    case MDCN_F32: return depthwise_t<float>(p, x, offset, mask, weight, bias, out, stream);
-    case MDCN_F16: return depthwise_t<half_t>(p, x, offset, mask, weight, bias, out, stream);
-    case MDCN_BF16: return depthwise_t<bf16_t>(p, x, offset, mask, weight, bias, out, stream);
+    case MDCN_F32:
+        return depthwise_t<float>(p, cnt, x, geo, offset, mask, weight, bias, out, stream);
+    case MDCN_F16:
+        return depthwise_t<half_t>(p, cnt, x, geo, offset, mask, weight, bias, out, stream);
+    case MDCN_BF16:
+        return depthwise_t<bf16_t>(p, cnt, x, geo, offset, mask, weight, bias, out, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_dw_geometry(const Problem &p, int64_t cnt, const void *offset,
+                              const void *mask, void *geo, hipStream_t stream)
+{
+    switch (p.dtype) {
+    case MDCN_F32: return dw_geometry_t<float>(p, cnt, offset, mask, geo, stream);
+    case MDCN_F16: return dw_geometry_t<half_t>(p, cnt, offset, mask, geo, stream);
+    case MDCN_BF16: return dw_geometry_t<bf16_t>(p, cnt, offset, mask, geo, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -16,7 +16,8 @@ enum KernelId : int32_t {
     K_GEMM = 3,
     K_DEPTHWISE = 4,
     K_FUSED = 5,
-    K_COUNT = 6
+    K_DW_GEOMETRY = 6,
+    K_COUNT = 7
 };
 
 // weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
@@ -43,9 +44,17 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, int64_t cnt, const v
                         const void *xt, const void *offset, const void *mask, const void *bias,
                         void *out, hipStream_t stream);
 
-// Direct depthwise (C/group == 1) forward of all N images.
-hipError_t launch_depthwise(const Problem &p, const void *x, const void *offset,
-                            const void *mask, const void *weight, const void *bias, void *out,
-                            hipStream_t stream);
+// Depthwise sampling geometry of cnt images: for each (image, offset group,
+// tap, pixel) a 16-byte record geo[((img*DG + q)*K + k)*P + pix] = {staged
+// plane entry of the sample's top-left corner (0 for a sample with no corner
+// on the image), ly, lx*m, (1-lx)*m}.
+hipError_t launch_dw_geometry(const Problem &p, int64_t cnt, const void *offset,
+                              const void *mask, void *geo, hipStream_t stream);
+
+// Direct depthwise (C/group == 1) forward of cnt images (geo from
+// launch_dw_geometry; null when the plan uses the plain kernel).
+hipError_t launch_depthwise(const Problem &p, int64_t cnt, const void *x, const void *geo,
+                            const void *offset, const void *mask, const void *weight,
+                            const void *bias, void *out, hipStream_t stream);
 
 }  // namespace mdcn

@@ -256,7 +256,27 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
     if (st != MDCN_OK)
         return st;
     if (plan.path == Path::Depthwise) {
+        // The staged kernel reads each (offset group, tap, pixel)'s sampling
+        // record (corner entry and weight factors), computed once per image
+        // by a geometry kernel: 16 bytes each.  Chunks of images within a
+        // 256 MiB budget.
         plan.chunk = std::max<int64_t>(p.N, 1);
+        if (dw_default_entry(p) == 0) {
+            *out = plan;                        // plain kernel: no workspace
+            return MDCN_OK;
+        }
+        plan.geo_bytes_per_image = align_up(size_t(p.DG * p.K * p.P) * 16, kAlign);
+        const int64_t img = int64_t(std::max<size_t>(plan.geo_bytes_per_image, 1));
+        int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(
+            {std::max<int64_t>(p.N, 1), int64_t(kColumnBudget) / img, kMaxPerImage / img}));
+        if (!default_sizing) {
+            if (workspace_bytes < kAlign + size_t(img))
+                return MDCN_E_WORKSPACE;
+            chunk = std::max<int64_t>(1, std::min<int64_t>(
+                chunk, int64_t((workspace_bytes - kAlign) / size_t(img))));
+        }
+        plan.chunk = chunk;
+        plan.ws_bytes = size_t(chunk) * plan.geo_bytes_per_image;
         *out = plan;
         return MDCN_OK;
     }
@@ -321,16 +341,35 @@ size_t min_workspace(const Problem &p, const Plan &plan)
 {
     (void)p;
     if (plan.path == Path::Depthwise)
-        return 0;
+        return plan.geo_bytes_per_image ? kAlign + plan.geo_bytes_per_image : 0;
     return kAlign + plan.wpack_bytes + plan.xt_bytes_per_image + plan.col_bytes_per_image;
 }
 
 
 size_t workspace_request(const Plan &plan)
 {
-    if (plan.path == Path::Depthwise)
+    if (plan.ws_bytes == 0)
         return 0;
     return kAlign + plan.ws_bytes;
+}
+
+bool dw_entry_allowed(const Problem &p, int ent)
+{
+    const int ch = ent / int(p.elem);
+    const size_t positions = size_t(p.H + 4) * size_t(p.W + 4);
+    // one image's geometry (16 bytes per offset group, tap and pixel) is one
+    // buffer range
+    const double geo = double(p.DG) * double(p.K) * double(p.P) * 16.0;
+    return ent >= int(p.elem) && ch >= 1 && p.Cdg % ch == 0 && geo <= double(kMaxPerImage) &&
+           positions * size_t(ent) + 9 * size_t(ch) * sizeof(float) <= kLdsBytes;
+}
+
+int dw_default_entry(const Problem &p)
+{
+    for (int e : {16, 8, 4, 2})
+        if (dw_entry_allowed(p, e))
+            return e;
+    return 0;
 }
 
 }  // namespace mdcn

@@ -61,6 +61,7 @@ constexpr int kFusedTileCount = 4;
 // Workspace layout (all offsets 256-byte aligned):
 //   gather + GEMM: [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
 //   fused:         [packed weight: G x Mg x Kp] [x in NHWC: chunk images]
+//   depthwise:     [sampling geometry: chunk images x DG x K x 5 x P words]
 struct Plan {
     Path path;
     int64_t chunk;               // images per pass through gather + GEMM
@@ -68,6 +69,7 @@ struct Plan {
     size_t wpack_off, wpack_bytes;
     size_t xt_off, xt_bytes_per_image;
     size_t col_off, col_bytes_per_image;
+    size_t geo_bytes_per_image;  // depthwise: sampling geometry of one image (0: none)
     size_t ws_bytes;             // bytes this plan uses
     GemmTile gemm_tile;
     FusedTile fused_tile;
@@ -80,6 +82,12 @@ constexpr int64_t kMaxCoord = int64_t(1) << 24;        // spatial extents and an
 constexpr size_t kLdsBytes = size_t(160) << 10;        // LDS of one gfx950 workgroup
 
 size_t dtype_size(mdcn_dtype t);
+// Depthwise: the widest LDS entry (bytes of channels per plane position) the
+// staged kernel can use for this problem -- its channels share an offset
+// group and the zero-ringed plane fits in LDS -- or 0 when none can.
+int dw_default_entry(const Problem &p);
+// Whether entry width `ent` is usable for this problem.
+bool dw_entry_allowed(const Problem &p, int ent);
 // Whether the fused gather-GEMM can run this problem: channel blocks that
 // align with its 128-byte K steps and 16-byte chunks, and some tile whose LDS
 // (operand stages plus geometry table) fits.

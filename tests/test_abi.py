@@ -198,11 +198,24 @@ def test_workspace_sizes_and_chunking():
     assert "chunk=1" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, DIMS, mb)
     # f32: one image per chunk (236 MB of columns)
     assert "chunk=1" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F32, DIMS)
-    # depthwise problem on the automatic path needs no workspace
+    # depthwise problem on the automatic path: the sampling geometry of each
+    # image (a 16-byte record per tap and pixel), all 8 images at once
     dw = mdcn.mdcn_create(1, 1, 1, 256, 1)
     d5 = [8, 256, 96, 96, 8, 18, 96, 96, 8, 9, 96, 96, 256, 1, 3, 3]
-    assert mdcn.mdcn_workspace_bytes(dw, mdcn.MDCN_F32, d5) == (0, 0)
-    assert "depthwise" in mdcn.mdcn_describe_plan(dw, mdcn.MDCN_F32, d5)
+    geo_img = 9 * 96 * 96 * 16
+    assert mdcn.mdcn_workspace_bytes(dw, mdcn.MDCN_F32, d5) == (256 + 8 * geo_img,
+                                                                256 + geo_img)
+    plan = mdcn.mdcn_describe_plan(dw, mdcn.MDCN_F32, d5)
+    assert "depthwise" in plan and "chunk=8" in plan
+    assert "chunk=3" in mdcn.mdcn_describe_plan(dw, mdcn.MDCN_F32, d5, 256 + 3 * geo_img + 5)
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_describe_plan(dw, mdcn.MDCN_F32, d5, geo_img)
+    assert e.value.status == mdcn.MDCN_E_WORKSPACE
+    # a plane too large for LDS (304 x 304 entries of 4 bytes with the ring):
+    # the plain kernel, no workspace
+    big = [1, 16, 300, 300, 1, 18, 300, 300, 1, 9, 300, 300, 16, 1, 3, 3]
+    dwb = mdcn.mdcn_create(1, 1, 1, 16, 1)
+    assert mdcn.mdcn_workspace_bytes(dwb, mdcn.MDCN_F32, big) == (0, 0)
     # ... and the gather + GEMM path can be forced for it
     dwg = mdcn.mdcn_create(1, 1, 1, 256, 1, path=mdcn.MDCN_PATH_GATHER_GEMM)
     assert mdcn.mdcn_workspace_bytes(dwg, mdcn.MDCN_F32, d5)[0] > 0
