@@ -88,7 +88,9 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
     def per_launch(name, cnt):
         if name == "pack_weight":
             return dict(bytes=w_bytes + pr.Co * Kp * e, flops=0)
-        if name == "to_nhwc":
+        if name == "pack_weight_steps":
+            return dict(bytes=2 * w_bytes, flops=0)
+        if name in ("to_nhwc", "to_channel_blocks"):
             return dict(bytes=2 * cnt * x_img, flops=0)
         if name == "deform_gather":
             # x read once, offsets and masks read once, columns written once
@@ -97,7 +99,7 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
         if name == "gemm_bias":
             return dict(bytes=cnt * (col_img + out_img) + pr.Co * Kp * e + bias_bytes,
                         flops=2 * cnt * pr.Co * Kg * P)
-        if name == "fused_gather_gemm":
+        if name in ("fused_gather_gemm", "window_gather_gemm"):
             # x (NHWC copy), offsets and masks read once, output written once
             return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + pr.Co * Kp * e
                         + bias_bytes, flops=2 * cnt * pr.Co * Kg * P)
@@ -128,7 +130,7 @@ def main(argv=None) -> int:
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "gather_gemm", "fused",
-                                                       "depthwise"],
+                                                       "window", "depthwise"],
                     help="computation path (default: the library's choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte device buffer --steps times (a plain copy "
@@ -172,7 +174,8 @@ def main(argv=None) -> int:
     inp = workloads.generate(pr, dtype, seed=0)
     g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
     path = {"auto": mdcn.MDCN_PATH_AUTO, "gather_gemm": mdcn.MDCN_PATH_GATHER_GEMM,
-            "fused": mdcn.MDCN_PATH_FUSED, "depthwise": mdcn.MDCN_PATH_DEPTHWISE}[args.path]
+            "fused": mdcn.MDCN_PATH_FUSED, "window": mdcn.MDCN_PATH_WINDOW,
+            "depthwise": mdcn.MDCN_PATH_DEPTHWISE}[args.path]
     op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups,
                           path=path)
     code = mdcn.dtype_code(g["x"].dtype)
@@ -219,8 +222,10 @@ def main(argv=None) -> int:
         avg_ms = total_ms / count
         launches_per_step = count / args.steps
         cnt = (pr.N / max(1, launches_per_step)
-               if name in ("to_nhwc", "deform_gather", "gemm_bias", "fused_gather_gemm",
-                           "depthwise_geometry", "depthwise_direct") else 0)
+               if name in ("to_nhwc", "to_channel_blocks", "deform_gather", "gemm_bias",
+                           "fused_gather_gemm", "window_gather_gemm", "depthwise_geometry",
+                           "depthwise_direct")
+               else 0)
         m = model(name, cnt)
         kernels[name] = dict(launches_per_step=launches_per_step, avg_ms=avg_ms,
                              ms_per_step=total_ms / args.steps,
@@ -233,7 +238,7 @@ def main(argv=None) -> int:
     peak_tf = MFMA_PEAK_TFLOPS[dtype]
     t_hbm = dk["algo_bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = dk["algo_flops_per_launch"] / (peak_tf * 1e12)
-    uses_mfma = dominant in ("gemm_bias", "fused_gather_gemm")
+    uses_mfma = dominant in ("gemm_bias", "fused_gather_gemm", "window_gather_gemm")
     if uses_mfma and t_mfma > t_hbm:
         roofline = dict(bound="mfma", achieved=round(dk["tflops"], 2), peak=peak_tf,
                         unit="TFLOP/s", frac=round(dk["tflops"] / peak_tf, 4), traffic=None)

@@ -90,7 +90,7 @@ typedef enum mdcn_path {
                                   the sampling geometry (16 bytes per offset group, tap and
                                   output pixel) is first written to the workspace by a
                                   small kernel; otherwise no workspace is used            */
-    MDCN_PATH_FUSED = 3        /* the gather fused into the MFMA GEMM: the GEMM's B tiles
+    MDCN_PATH_FUSED = 3,       /* the gather fused into the MFMA GEMM: the GEMM's B tiles
                                   are made in LDS from the bilinear samples, with no column
                                   buffer [plugin guide §五 steps 1-3 without the columns];
                                   requires C/group to be a multiple of 64 (fp16/bf16) or 32
@@ -98,6 +98,16 @@ typedef enum mdcn_path {
                                   geometry table (32 bytes per offset group, tap and output
                                   column; 64 or 128 columns) that fits in LDS beside the
                                   operand stages                                          */
+    MDCN_PATH_WINDOW = 4       /* the gather fused into the MFMA GEMM with each output
+                                  tile's input window staged in LDS: a workgroup computes
+                                  256 output channels x 256 output pixels; per chunk of 16
+                                  input channels the input rectangle its samples can reach
+                                  (anchors plus an offset margin) is copied to LDS once and
+                                  the 9 taps read their bilinear corners from it; a sample
+                                  with a corner on the image outside the rectangle is read
+                                  from global memory.  Requires fp16/bf16, a 3x3 kernel,
+                                  C/group a multiple of 16 and each group inside one
+                                  deformable group [plugin guide §五 steps 1-3]           */
 } mdcn_path;
 
 typedef struct mdcn_op mdcn_op;

@@ -179,8 +179,12 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     void *wpack = ws + plan.wpack_off;
     void *xt = ws + plan.xt_off;
     void *col = ws + plan.col_off;
-    err = rec.run(mdcn::K_PACK_WEIGHT,
-                  [&] { return mdcn::launch_pack_weight(p, plan, weight, wpack, stream); });
+    if (plan.path == Path::Window)
+        err = rec.run(mdcn::K_PACK_WEIGHT_STEPS,
+                      [&] { return mdcn::launch_pack_weight_steps(p, weight, wpack, stream); });
+    else
+        err = rec.run(mdcn::K_PACK_WEIGHT,
+                      [&] { return mdcn::launch_pack_weight(p, plan, weight, wpack, stream); });
     if (err != hipSuccess)
         return MDCN_E_LAUNCH;
     for (int64_t n0 = 0; n0 < p.N; n0 += plan.chunk) {
@@ -189,12 +193,25 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         const char *oc = static_cast<const char *>(offset) + size_t(n0) * off_img;
         const char *mc = static_cast<const char *>(mask) + size_t(n0) * msk_img;
         char *outc = static_cast<char *>(out) + size_t(n0) * out_img;
-        err = rec.run(mdcn::K_TO_NHWC, [&] { return mdcn::launch_to_nhwc(p, cnt, xc, xt, stream); });
+        if (plan.path == Path::Window)
+            err = rec.run(mdcn::K_TO_BLOCKS,
+                          [&] { return mdcn::launch_to_channel_blocks(p, cnt, xc, xt, stream); });
+        else
+            err = rec.run(mdcn::K_TO_NHWC,
+                          [&] { return mdcn::launch_to_nhwc(p, cnt, xc, xt, stream); });
         if (err != hipSuccess)
             return MDCN_E_LAUNCH;
         if (plan.path == Path::Fused) {
             err = rec.run(mdcn::K_FUSED, [&] {
                 return mdcn::launch_fused(p, plan, cnt, wpack, xt, oc, mc, bias, outc, stream);
+            });
+            if (err != hipSuccess)
+                return MDCN_E_LAUNCH;
+            continue;
+        }
+        if (plan.path == Path::Window) {
+            err = rec.run(mdcn::K_WINDOW, [&] {
+                return mdcn::launch_window(p, plan, cnt, wpack, xt, oc, mc, bias, outc, stream);
             });
             if (err != hipSuccess)
                 return MDCN_E_LAUNCH;
@@ -225,7 +242,7 @@ mdcn_status create_impl(const int32_t stride[2], const int32_t padding[2],
     if (st != MDCN_OK)
         return st;
     if (path != MDCN_PATH_AUTO && path != MDCN_PATH_GATHER_GEMM &&
-        path != MDCN_PATH_DEPTHWISE && path != MDCN_PATH_FUSED)
+        path != MDCN_PATH_DEPTHWISE && path != MDCN_PATH_FUSED && path != MDCN_PATH_WINDOW)
         return MDCN_E_PATH;
     mdcn_op *op = new (std::nothrow) mdcn_op;
     if (!op)
@@ -420,6 +437,9 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_DEPTHWISE: return "depthwise_direct";
     case mdcn::K_FUSED: return "fused_gather_gemm";
     case mdcn::K_DW_GEOMETRY: return "depthwise_geometry";
+    case mdcn::K_WINDOW: return "window_gather_gemm";
+    case mdcn::K_PACK_WEIGHT_STEPS: return "pack_weight_steps";
+    case mdcn::K_TO_BLOCKS: return "to_channel_blocks";
     }
     return "?";
 }
@@ -473,6 +493,14 @@ mdcn_status mdcn_describe_plan(const mdcn_op *op, mdcn_dtype dtype, const int64_
                           (long long)plan.chunk, (long long)p.Kg, (long long)plan.Kp,
                           (long long)p.G, (long long)p.Mg, (long long)p.P,
                           int(plan.fused_tile), plan.ws_bytes, plan.wpack_bytes,
+                          plan.xt_bytes_per_image);
+        else if (plan.path == Path::Window)
+            std::snprintf(buf, len,
+                          "path=window chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld tile=%d "
+                          "margin=%lld ws=%zu (wpack=%zu xt/img=%zu)",
+                          (long long)plan.chunk, (long long)p.Kg, (long long)plan.Kp,
+                          (long long)p.G, (long long)p.Mg, (long long)p.P, int(plan.win_tile),
+                          (long long)plan.win_margin, plan.ws_bytes, plan.wpack_bytes,
                           plan.xt_bytes_per_image);
         else
             std::snprintf(buf, len,

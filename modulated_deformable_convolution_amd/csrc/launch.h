@@ -17,13 +17,26 @@ enum KernelId : int32_t {
     K_DEPTHWISE = 4,
     K_FUSED = 5,
     K_DW_GEOMETRY = 6,
-    K_COUNT = 7
+    K_WINDOW = 7,
+    K_PACK_WEIGHT_STEPS = 8,
+    K_TO_BLOCKS = 9,
+    K_COUNT = 10
 };
 
 // weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
 // kk = k*Cg + c' (tap-major), zero for kk >= Kg.
 hipError_t launch_pack_weight(const Problem &p, const Plan &plan, const void *weight,
                               void *wpack, hipStream_t stream);
+
+// weight [Co][Cg][kh][kw] -> the window path's step-major planes:
+// [G][S][2][Mg][8], S = (Cg/16)*K steps (chunk of 16 channels, tap), half h
+// of the chunk's channels; requires Cg % 16 == 0.
+hipError_t launch_pack_weight_steps(const Problem &p, const void *weight, void *wpack,
+                                    hipStream_t stream);
+
+// x [cnt][C][H][W] -> xb [cnt][C/8][H][W][8] (8-channel blocks; C % 8 == 0).
+hipError_t launch_to_channel_blocks(const Problem &p, int64_t cnt, const void *x, void *xb,
+                                    hipStream_t stream);
 
 // x [cnt][C][H][W] -> xt [cnt][H][W][C] (channels innermost).
 hipError_t launch_to_nhwc(const Problem &p, int64_t cnt, const void *x, void *xt,
@@ -43,6 +56,14 @@ hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const vo
 hipError_t launch_fused(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                         const void *xt, const void *offset, const void *mask, const void *bias,
                         void *out, hipStream_t stream);
+
+// The same, with each output tile's input window staged in LDS (fp16/bf16,
+// 3x3 kernels; plan.win_tile, win_margin, win_lead), from the step-major
+// weight (launch_pack_weight_steps) and x in 8-channel blocks
+// (launch_to_channel_blocks).
+hipError_t launch_window(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
+                         const void *xt, const void *offset, const void *mask, const void *bias,
+                         void *out, hipStream_t stream);
 
 // Depthwise sampling geometry of cnt images: for each (image, offset group,
 // tap, pixel) a 16-byte record geo[((img*DG + q)*K + k)*P + pix] = {staged

@@ -224,12 +224,104 @@ bool fused_eligible(const Problem &p)
            p.C < 65536 && p.Kg < 65536 && choose_fused_tile(p, 1, &t);
 }
 
+int64_t window_extent(int64_t tile, int64_t stride, int64_t k, int64_t dil, int64_t margin)
+{
+    return (tile - 1) * stride + (k - 1) * dil + 2 + 2 * margin;
+}
+
+namespace {
+
+void window_tile_dims(WindowTile t, int64_t *th, int64_t *tw)
+{
+    switch (t) {
+    case WindowTile::H16_W16: *th = 16; *tw = 16; return;
+    case WindowTile::H8_W32: *th = 8; *tw = 32; return;
+    case WindowTile::H32_W8: *th = 32; *tw = 8; return;
+    }
+    *th = 16;
+    *tw = 16;
+}
+
+// Largest margin <= cap whose window fits (-1 when not even 0 fits).
+int64_t window_margin_fit(const Problem &p, WindowTile t, int64_t cap)
+{
+    int64_t th, tw;
+    window_tile_dims(t, &th, &tw);
+    for (int64_t m = cap; m >= 0; --m) {
+        const int64_t wr = window_extent(th, p.sh, p.kh, p.dh, m);
+        const int64_t wc = window_extent(tw, p.sw, p.kw, p.dw, m);
+        if (wr * wc <= kWindowPixels && wc * 16 + 32 <= kWindowZeroBytes)
+            return m;
+    }
+    return -1;
+}
+
+}  // namespace
+
+// Tile: the fewest padded output pixels (ragged edges), then the widest
+// margin, among tiles whose window fits with a margin >= 2.
+// MDCN_WIN_TILE=<0..2> and MDCN_WIN_MARGIN=<m> override (for tuning).
+bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin)
+{
+    int64_t cap = kWindowMaxMargin;
+    if (const char *env = std::getenv("MDCN_WIN_MARGIN")) {
+        const int v = std::atoi(env);
+        if (v >= 0 && v <= 64)
+            cap = v;
+    }
+    const int64_t min_margin = std::min<int64_t>(2, cap);
+    if (const char *env = std::getenv("MDCN_WIN_TILE")) {
+        const int v = std::atoi(env);
+        if (v >= 0 && v < kWindowTileCount) {
+            const int64_t m = window_margin_fit(p, static_cast<WindowTile>(v), cap);
+            if (m >= min_margin) {
+                *tile = static_cast<WindowTile>(v);
+                *margin = m;
+                return true;
+            }
+        }
+    }
+    bool found = false;
+    int64_t best_pad = 0, best_m = 0;
+    for (int i = 0; i < kWindowTileCount; ++i) {
+        const WindowTile t = static_cast<WindowTile>(i);
+        const int64_t m = window_margin_fit(p, t, cap);
+        if (m < min_margin)
+            continue;
+        int64_t th, tw;
+        window_tile_dims(t, &th, &tw);
+        const int64_t pad = ((p.Ho + th - 1) / th) * th * ((p.Wo + tw - 1) / tw) * tw;
+        if (!found || pad < best_pad || (pad == best_pad && m > best_m)) {
+            found = true;
+            best_pad = pad;
+            best_m = m;
+            *tile = t;
+            *margin = m;
+        }
+    }
+    return found;
+}
+
+bool window_eligible(const Problem &p)
+{
+    const int64_t img_bytes = p.C * p.H * p.W * int64_t(p.elem);
+    WindowTile t;
+    int64_t m;
+    return p.elem == 2 && p.kh == 3 && p.kw == 3 && p.Cg % 16 == 0 && p.Cdg % p.Cg == 0 &&
+           img_bytes <= kMaxPerImage && choose_window(p, &t, &m);
+}
+
 mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
 {
     switch (a.path) {
     case MDCN_PATH_AUTO:
         *out = (p.Cg == 1) ? Path::Depthwise
                            : (fused_eligible(p) ? Path::Fused : Path::GatherGemm);
+        return MDCN_OK;
+    case MDCN_PATH_WINDOW:
+        if (!window_eligible(p))
+            return MDCN_E_PATH;
+        *out = Path::Window;
         return MDCN_OK;
     case MDCN_PATH_FUSED:
         if (!fused_eligible(p))
@@ -282,7 +374,7 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
     }
     plan.Kp = round_up(p.Kg, 64);
     plan.wpack_off = 0;
-    if (plan.path == Path::Fused) {
+    if (plan.path == Path::Fused || plan.path == Path::Window) {
         // Workspace: packed weight + the chunk's images in NHWC.  A chunk's
         // NHWC bytes stay below 2^31 (one buffer range) and within 512 MiB.
         plan.wpack_bytes = align_up(size_t(p.G * p.Mg * plan.Kp) * p.elem, kAlign);
@@ -299,8 +391,19 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
             chunk = std::max<int64_t>(1, std::min(chunk, fit));
         }
         plan.chunk = chunk;
-        if (!choose_fused_tile(p, chunk, &plan.fused_tile))
+        if (plan.path == Path::Fused && !choose_fused_tile(p, chunk, &plan.fused_tile))
             return MDCN_E_PATH;                 // fused_eligible said some tile fits
+        if (plan.path == Path::Window) {
+            if (!choose_window(p, &plan.win_tile, &plan.win_margin))
+                return MDCN_E_PATH;
+            // MDCN_WIN_LEAD=3|5|7 overrides (for tuning)
+            plan.win_lead = kWindowMaxLead;
+            if (const char *env = std::getenv("MDCN_WIN_LEAD")) {
+                const int v = std::atoi(env);
+                if (v == 3 || v == 5 || v == 7)
+                    plan.win_lead = v;
+            }
+        }
 
         plan.xt_off = plan.wpack_bytes;
         plan.col_off = plan.xt_off + size_t(chunk) * plan.xt_bytes_per_image;

@@ -34,7 +34,7 @@ struct Problem {
     int64_t sh, sw, ph, pw, dh, dw;
 };
 
-enum class Path { GatherGemm, Depthwise, Fused };
+enum class Path { GatherGemm, Depthwise, Fused, Window };
 
 // Workgroup tile of the GEMM (rows of the packed weight x columns) and its
 // wave grid; every wave owns a block of 32x32 accumulator tiles.
@@ -58,6 +58,19 @@ enum class FusedTile : int {
 };
 constexpr int kFusedTileCount = 4;
 
+// Output-pixel tile (rows x columns, 256 pixels) of the windowed fused
+// kernel.
+enum class WindowTile : int {
+    H16_W16 = 0,
+    H8_W32 = 1,
+    H32_W8 = 2,
+};
+constexpr int kWindowTileCount = 3;
+constexpr int kWindowPixels = 1280;      // input positions one LDS window can hold
+constexpr int kWindowZeroBytes = 1024;   // zeroed LDS after each window (>= 16*columns + 32)
+constexpr int64_t kWindowMaxMargin = 8;  // default offset margin around the anchors
+constexpr int kWindowMaxLead = 7;        // weight copies issued this many K steps ahead
+
 // Workspace layout (all offsets 256-byte aligned):
 //   gather + GEMM: [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
 //   fused:         [packed weight: G x Mg x Kp] [x in NHWC: chunk images]
@@ -73,6 +86,9 @@ struct Plan {
     size_t ws_bytes;             // bytes this plan uses
     GemmTile gemm_tile;
     FusedTile fused_tile;
+    WindowTile win_tile;
+    int64_t win_margin;          // window: pixels of margin around the tile's anchors
+    int win_lead;                // window: K steps the weight copies run ahead (3, 5, 7)
 };
 
 constexpr size_t kColumnBudget = size_t(256) << 20;   // default column-buffer cap
@@ -100,6 +116,16 @@ int64_t fused_offset_groups(const Problem &p);
 size_t fused_table_bytes(const Problem &p, int64_t bn);
 // Operand stages plus geometry table of a fused tile.
 size_t fused_lds_bytes(const Problem &p, FusedTile t);
+// Window rows (or columns) that a tile of `tile` output rows (columns) needs:
+// its anchors for every tap, both bilinear corners, and `margin` pixels on
+// each side.
+int64_t window_extent(int64_t tile, int64_t stride, int64_t k, int64_t dil, int64_t margin);
+// Whether the windowed fused kernel can run this problem: fp16/bf16, 3x3
+// kernels, C/group a multiple of 16 inside one offset group, and some tile
+// whose window (with a margin of at least 2) fits in LDS.
+bool window_eligible(const Problem &p);
+// Tile and margin for the windowed kernel (false when none fits).
+bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin);
 mdcn_status check_attrs(const int32_t stride[2], const int32_t padding[2],
                         const int32_t dilation[2], int32_t group, int32_t dgroup);
 mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[16],

@@ -1,6 +1,6 @@
-// prep.hip -- layout kernels of the gather + GEMM path: x to channels-last,
-// and the weight repacked in the tap-major contraction order the gather
-// writes.  Both only move data.
+// prep.hip -- layout kernels: x to channels-last (NHWC) or to 8-channel
+// blocks ([C/8][H][W][8] per image), and the weight repacked in the order a
+// path's contraction walks it.  All of them only move data.
 #include "device_common.h"
 #include "launch.h"
 
@@ -10,8 +10,16 @@ namespace {
 
 constexpr int kTile = 64;
 
+// Destination of (channel c, pixel p) of one image: NHWC, or 8-channel
+// blocks (block c/8 is a plane of HW x 8 channels).
+template <bool BLK>
+__device__ __forceinline__ size_t dst_index(int c, int p, int C, int HW)
+{
+    return BLK ? (size_t(c >> 3) * HW + p) * 8 + (c & 7) : size_t(p) * C + c;
+}
+
 // One 64 (channels) x 64 (pixels) tile through LDS per workgroup.
-template <typename T>
+template <typename T, bool BLK>
 __global__ __launch_bounds__(256) void to_nhwc_kernel(const T *__restrict__ x, T *__restrict__ xt,
                                                       int C, int HW)
 {
@@ -31,14 +39,14 @@ __global__ __launch_bounds__(256) void to_nhwc_kernel(const T *__restrict__ x, T
     for (int r = ty; r < kTile; r += 256 / kTile) {
         const int p = p0 + r, c = c0 + tx;
         if (p < HW && c < C)
-            dst[size_t(p) * C + c] = tile[tx][r];
+            dst[dst_index<BLK>(c, p, C, HW)] = tile[tx][r];
     }
 }
 
 // The same transpose with 16-byte global accesses on both sides (pixels
 // along the load, channels along the store); requires C and H*W to be
-// multiples of the vector width.
-template <typename T>
+// multiples of the vector width (and, for blocks, 8 channels per vector).
+template <typename T, bool BLK>
 __global__ __launch_bounds__(256) void to_nhwc_vec_kernel(const T *__restrict__ x,
                                                           T *__restrict__ xt, int C, int HW)
 {
@@ -70,7 +78,7 @@ __global__ __launch_bounds__(256) void to_nhwc_vec_kernel(const T *__restrict__ 
 #pragma unroll
             for (int e = 0; e < V; ++e)
                 val.e[e] = tile[cv + e][r];
-            store16(dst + size_t(p) * C + c, val);
+            store16(dst + dst_index<BLK>(c, p, C, HW), val);
         }
     }
 }
@@ -94,7 +102,32 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const T *__restrict__ 
     wp[t] = v;
 }
 
+// The window path's weight: for each group g, K step st = chunk*K + k
+// (chunk of 16 channels, tap k) and half h, the plane of Mg rows of 8
+// channels: wp[(((g*S + st)*2 + h)*Mg + m)*8 + e] =
+// weight[g*Mg + m][16*chunk + 8*h + e][k], S = (Cg/16)*K.
 template <typename T>
+__global__ __launch_bounds__(256) void pack_weight_steps_kernel(const T *__restrict__ w,
+                                                                T *__restrict__ wp, int total,
+                                                                int Mg, int Cg, int K, int S)
+{
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= total)
+        return;
+    const int e = t & 7;
+    int r = t >> 3;
+    const int m = r % Mg;
+    r /= Mg;
+    const int h = r & 1;
+    r >>= 1;
+    const int st = r % S;
+    const int g = r / S;
+    const int chunk = st / K, k = st - chunk * K;
+    const int cl = chunk * 16 + h * 8 + e;
+    wp[t] = w[(size_t(g * Mg + m) * Cg + cl) * K + k];
+}
+
+template <typename T, bool BLK>
 hipError_t to_nhwc_t(const Problem &p, int64_t cnt, const void *x, void *xt, hipStream_t s)
 {
     const int HW = int(p.H * p.W);
@@ -104,13 +137,13 @@ hipError_t to_nhwc_t(const Problem &p, int64_t cnt, const void *x, void *xt, hip
         grid.z = unsigned(std::min<int64_t>(65535, cnt - n0));
         const size_t off = size_t(n0) * size_t(p.C) * size_t(HW);
         constexpr int V = 16 / sizeof(T);
-        if (p.C % V == 0 && HW % V == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
-            reinterpret_cast<uintptr_t>(xt) % 16 == 0)
-            hipLaunchKernelGGL(to_nhwc_vec_kernel<T>, grid, dim3(256), 0, s,
+        if (p.C % V == 0 && HW % V == 0 && (!BLK || V == 8) &&
+            reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(xt) % 16 == 0)
+            hipLaunchKernelGGL((to_nhwc_vec_kernel<T, BLK>), grid, dim3(256), 0, s,
                                static_cast<const T *>(x) + off, static_cast<T *>(xt) + off,
                                int(p.C), HW);
         else
-            hipLaunchKernelGGL(to_nhwc_kernel<T>, grid, dim3(256), 0, s,
+            hipLaunchKernelGGL((to_nhwc_kernel<T, BLK>), grid, dim3(256), 0, s,
                                static_cast<const T *>(x) + off, static_cast<T *>(xt) + off,
                                int(p.C), HW);
         hipError_t e = hipGetLastError();
@@ -137,9 +170,46 @@ hipError_t launch_to_nhwc(const Problem &p, int64_t cnt, const void *x, void *xt
                           hipStream_t stream)
 {
     switch (p.dtype) {
-    case MDCN_F32: return to_nhwc_t<float>(p, cnt, x, xt, stream);
-    case MDCN_F16: return to_nhwc_t<half_t>(p, cnt, x, xt, stream);
-    case MDCN_BF16: return to_nhwc_t<bf16_t>(p, cnt, x, xt, stream);
+    case MDCN_F32: return to_nhwc_t<float, false>(p, cnt, x, xt, stream);
+    case MDCN_F16: return to_nhwc_t<half_t, false>(p, cnt, x, xt, stream);
+    case MDCN_BF16: return to_nhwc_t<bf16_t, false>(p, cnt, x, xt, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_to_channel_blocks(const Problem &p, int64_t cnt, const void *x, void *xb,
+                                    hipStream_t stream)
+{
+    if (p.C % 8 != 0)
+        return hipErrorInvalidValue;
+    switch (p.dtype) {
+    case MDCN_F32: return to_nhwc_t<float, true>(p, cnt, x, xb, stream);
+    case MDCN_F16: return to_nhwc_t<half_t, true>(p, cnt, x, xb, stream);
+    case MDCN_BF16: return to_nhwc_t<bf16_t, true>(p, cnt, x, xb, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t pack_weight_steps_t(const Problem &p, const void *w, void *wp, hipStream_t s)
+{
+    const int S = int(p.Cg / 16 * p.K);
+    const int total = int(p.G * S * 2 * p.Mg * 8);
+    hipLaunchKernelGGL(pack_weight_steps_kernel<T>, dim3((total + 255) / 256), dim3(256), 0, s,
+                       static_cast<const T *>(w), static_cast<T *>(wp), total, int(p.Mg),
+                       int(p.Cg), int(p.K), S);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_weight_steps(const Problem &p, const void *weight, void *wpack,
+                                    hipStream_t stream)
+{
+    if (p.Cg % 16 != 0)
+        return hipErrorInvalidValue;
+    switch (p.dtype) {
+    case MDCN_F32: return pack_weight_steps_t<float>(p, weight, wpack, stream);
+    case MDCN_F16: return pack_weight_steps_t<half_t>(p, weight, wpack, stream);
+    case MDCN_BF16: return pack_weight_steps_t<bf16_t>(p, weight, wpack, stream);
     }
     return hipErrorInvalidValue;
 }

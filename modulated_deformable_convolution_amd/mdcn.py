@@ -38,6 +38,7 @@ MDCN_PATH_AUTO = 0
 MDCN_PATH_GATHER_GEMM = 1
 MDCN_PATH_DEPTHWISE = 2
 MDCN_PATH_FUSED = 3
+MDCN_PATH_WINDOW = 4
 
 EXPORTED = [
     "mdcn_create", "mdcn_create_with_path", "mdcn_destroy", "mdcn_output_shape",

@@ -222,13 +222,17 @@ def test_workspace_sizes_and_chunking():
 
 
 def test_fused_path_plan():
-    # automatic choice for the OCDNet-like stage: fused, all 4 images, NHWC x only
+    # automatic choice for the OCDNet-like stage: fused, all 4 images, packed
+    # weight + NHWC x only; the windowed kernel uses the same workspace
     op = mdcn.mdcn_create(1, 1, 1, 1, 1)
     desc = mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, DIMS)
     assert desc.startswith("path=fused") and "chunk=4" in desc
+    opw = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_WINDOW)
+    assert mdcn.mdcn_describe_plan(opw, mdcn.MDCN_F16, DIMS).startswith("path=window")
     b, mb = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, DIMS)
     assert b == 256 + 256 * 2304 * 2 + 4 * 256 * 160 * 160 * 2
     assert mb == 256 + 256 * 2304 * 2 + 256 * 160 * 160 * 2
+    assert mdcn.mdcn_workspace_bytes(opw, mdcn.MDCN_F16, DIMS) == (b, mb)
     # not eligible: C/group = 36 is not a multiple of 64 -> gather + GEMM
     opg = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_FUSED)
     d = [1, 36, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 8, 36, 3, 3]
@@ -315,3 +319,61 @@ def test_forward_without_gpu_reports_device():
     st = mdcn.mdcn_forward(op, mdcn.MDCN_F32, DIMS, big, big * 2, big * 3, big * 4, 0, 0,
                            big * 5, big * 6, 1 << 32, 0)
     assert st == mdcn.MDCN_E_DEVICE
+
+
+def _win_desc(op, dtype, dims):
+    d = mdcn.mdcn_describe_plan(op, dtype, dims)
+    return d, int(d.split("tile=")[1].split()[0]), int(d.split("margin=")[1].split()[0])
+
+
+def test_window_path_plan():
+    """The windowed fused kernel: fp16/bf16, 3x3, C/group a multiple of 16
+    inside one offset group; the tile with the fewest padded output pixels,
+    the widest margin (at most 8) whose window (at most 1280 input positions)
+    fits its LDS buffer."""
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_WINDOW)
+    # OCDNet-like stage: 16 x 16 tiles, window 35 x 35 (margin 8)
+    d, tile, margin = _win_desc(op, mdcn.MDCN_F16, DIMS)
+    assert d.startswith("path=window") and tile == 0 and margin == 8
+    # a wide, short output (8 x 64): 8 x 32 tiles pad least
+    d, tile, margin = _win_desc(op, mdcn.MDCN_BF16, _fused_dims(1, 32, 8, 64, 64, 3, 1, 1))
+    assert tile == 1 and margin >= 2
+    # tall and narrow (64 x 8): 32 x 8 tiles
+    d, tile, margin = _win_desc(op, mdcn.MDCN_BF16, _fused_dims(1, 32, 64, 8, 64, 3, 1, 1))
+    assert tile == 2 and margin >= 2
+    # 9 x 70: 16 x 16 tiles (16 x 80 padded pixels) pad least
+    assert _win_desc(op, mdcn.MDCN_BF16, _fused_dims(1, 32, 9, 70, 64, 3, 1, 1))[1] == 0
+    # stride (2, 1): a 16 x 16 tile's window spans 30 + 2 + 2 + 2m rows and
+    # 15 + 2 + 2 + 2m columns, at most 1280 positions: margin 5; with stride
+    # and dilation 2 no tile fits
+    ops = mdcn.mdcn_create((2, 1), 1, 1, 2, 1, path=mdcn.MDCN_PATH_WINDOW)
+    ds = [2, 64, 64, 64, 2, 18, 32, 64, 2, 9, 32, 64, 64, 32, 3, 3]
+    d, tile, margin = _win_desc(ops, mdcn.MDCN_F16, ds)
+    assert tile == 0 and margin == 5
+    opd = mdcn.mdcn_create(2, 2, 2, 2, 1, path=mdcn.MDCN_PATH_WINDOW)
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_workspace_bytes(opd, mdcn.MDCN_F16, ds)
+    assert e.value.status == mdcn.MDCN_E_PATH
+    # not eligible: fp32, a 5x5 kernel, C/group = 8, a group spanning two
+    # offset groups
+    for dtype, g, dg, dims in [(mdcn.MDCN_F32, 1, 1, DIMS),
+                               (mdcn.MDCN_F16, 1, 1, _fused_dims(1, 32, 12, 12, 32, 5, 1, 1)),
+                               (mdcn.MDCN_F16, 2, 1, _fused_dims(1, 16, 12, 12, 32, 3, 1, 2)),
+                               (mdcn.MDCN_F16, 2, 4, _fused_dims(1, 64, 12, 12, 32, 3, 4, 2))]:
+        opx = mdcn.mdcn_create(1, 1, 1, g, dg, path=mdcn.MDCN_PATH_WINDOW)
+        with pytest.raises(mdcn.MdcnError) as e:
+            mdcn.mdcn_workspace_bytes(opx, dtype, dims)
+        assert e.value.status == mdcn.MDCN_E_PATH
+    # a group inside one offset group (C/group = 32, C/dg = 64) is eligible
+    opx = mdcn.mdcn_create(1, 1, 1, 4, 2, path=mdcn.MDCN_PATH_WINDOW)
+    assert _win_desc(opx, mdcn.MDCN_F16, _fused_dims(1, 128, 12, 12, 64, 3, 2, 4))[0].startswith(
+        "path=window")
+    # margin and tile overrides (tuning)
+    import os
+    os.environ["MDCN_WIN_MARGIN"] = "3"
+    os.environ["MDCN_WIN_TILE"] = "1"
+    try:
+        _, tile, margin = _win_desc(op, mdcn.MDCN_F16, DIMS)
+        assert tile == 1 and margin == 3
+    finally:
+        del os.environ["MDCN_WIN_MARGIN"], os.environ["MDCN_WIN_TILE"]

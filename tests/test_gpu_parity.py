@@ -72,13 +72,28 @@ SMALL = {
     # 5x5 taps: the geometry table only fits beside a 64-column tile
     "fused_5x5": Problem(N=2, C=64, Co=64, H=11, W=10, kh=5, kw=5, padding=(2, 2),
                          offset_dist=("normal", 2.0)),
+    # eligible for the windowed kernel (fp16/bf16): Co = 288 (a full and a
+    # partial 256-row tile), 37 x 37 (ragged 16 x 16 tiles), offsets wide
+    # enough that some samples leave the window (the fallback)
+    "window_multi_tile": Problem(N=2, C=32, Co=288, H=37, W=37,
+                                 offset_dist=("normal", 3.0)),
+    # stride (2, 1), dilation (1, 2), 2 groups inside 2 offset groups, Mg = 48
+    "window_grouped": Problem(N=2, C=64, Co=96, H=23, W=19, stride=(2, 1), padding=(1, 2),
+                              dilation=(1, 2), groups=2, deformable_groups=2,
+                              offset_dist=("normal", 2.0)),
+    # offsets up to 20 px: many samples off the image or outside the window
+    "window_far_offsets": Problem(N=1, C=16, Co=32, H=30, W=30,
+                                  offset_dist=("uniform", 20.0),
+                                  mask_dist=("uniform_zeros", 0.1)),
+    # also eligible for the fused kernel (C/group = 64)
+    "window_fused_cmp": Problem(N=2, C=64, Co=128, H=21, W=21, offset_dist=("normal", 2.0)),
 }
 
 
-def fused_ok(pr, dtype):
-    """Whether the library accepts the fused path for this problem (a host
-    query: an op created for the fused path reports MDCN_E_PATH otherwise)."""
-    op = make_op(pr, mdcn.MDCN_PATH_FUSED)
+def path_ok(pr, dtype, path):
+    """Whether the library accepts `path` for this problem (a host query: an
+    op created for that path reports MDCN_E_PATH otherwise)."""
+    op = make_op(pr, path)
     shapes = pr.shapes()
     dims = [int(v) for k in ("x", "offset", "mask", "weight") for v in shapes[k]]
     try:
@@ -119,8 +134,10 @@ def paths_for(pr, dtype):
     paths = [mdcn.MDCN_PATH_GATHER_GEMM]
     if pr.C // pr.groups == 1:
         paths.append(mdcn.MDCN_PATH_DEPTHWISE)
-    if fused_ok(pr, dtype):
+    if path_ok(pr, dtype, mdcn.MDCN_PATH_FUSED):
         paths.append(mdcn.MDCN_PATH_FUSED)
+    if path_ok(pr, dtype, mdcn.MDCN_PATH_WINDOW):
+        paths.append(mdcn.MDCN_PATH_WINDOW)
     return paths
 
 
@@ -344,6 +361,8 @@ def test_depthwise_variants(entry, pixels, name, dtype, monkeypatch):
     ("multi_tile_dg2", "f32", mdcn.MDCN_PATH_GATHER_GEMM),
     ("fused_multi_tile", "f16", mdcn.MDCN_PATH_FUSED),
     ("fused_multi_tile", "f32", mdcn.MDCN_PATH_FUSED),
+    ("window_multi_tile", "f16", mdcn.MDCN_PATH_WINDOW),
+    ("window_grouped", "bf16", mdcn.MDCN_PATH_WINDOW),
     ("depthwise_mult2", "f32", mdcn.MDCN_PATH_DEPTHWISE),
     ("depthwise_5x3", "bf16", mdcn.MDCN_PATH_DEPTHWISE)])
 def test_nonfinite_and_huge_offsets(name, dtype, path):
@@ -391,3 +410,63 @@ def test_fused_matches_gather_gemm_closely():
     a = run_gpu(pr, inp, mdcn.MDCN_PATH_FUSED).double()
     b = run_gpu(pr, inp, mdcn.MDCN_PATH_GATHER_GEMM).double()
     assert float((a - b).abs().max()) <= 2e-3
+
+
+# ---------------------------------------------------------------- windowed fused kernel
+
+@pytest.mark.parametrize("tile", range(3))
+@pytest.mark.parametrize("margin", [2, 8])
+@pytest.mark.parametrize("name,dtype", [("window_multi_tile", "f16"), ("window_grouped", "bf16"),
+                                        ("window_far_offsets", "f16")])
+def test_every_window_tile(tile, margin, name, dtype, monkeypatch):
+    """Each tile shape (MDCN_WIN_TILE) with a narrow (many samples through
+    the fallback) and the default margin (MDCN_WIN_MARGIN); a tile whose
+    window does not fit falls back to the planner's choice."""
+    monkeypatch.setenv("MDCN_WIN_TILE", str(tile))
+    monkeypatch.setenv("MDCN_WIN_MARGIN", str(margin))
+    pr = SMALL[name]
+    print("window", name, dtype, tile, margin, flush=True)
+    inp = workloads.generate(pr, dtype, seed=17)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW).double().numpy()
+    ref = oracle_full(pr, inp)
+    ok, err, bound = within_tolerance(got, ref, dtype)
+    assert ok, (tile, margin, name, dtype, error_report(got, ref))
+
+
+def test_window_matches_fused_closely():
+    """The windowed and the fused kernel round the same fp32 bilinear sums
+    once to fp16 and accumulate in fp32 in different orders: they agree far
+    inside the tolerance."""
+    pr = SMALL["window_fused_cmp"]
+    inp = workloads.generate(pr, "f16", seed=18)
+    a = run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW).double()
+    b = run_gpu(pr, inp, mdcn.MDCN_PATH_FUSED).double()
+    assert float((a - b).abs().max()) <= 2e-3
+
+
+@pytest.mark.parametrize("margin", [2, 8])
+def test_window_exact_cases(margin, monkeypatch):
+    """Exact results on the windowed kernel: a zero mask gives the bias, and
+    samples off the image (far away, or exactly on h = -1) give the bias."""
+    monkeypatch.setenv("MDCN_WIN_MARGIN", str(margin))
+    pr = SMALL["window_multi_tile"]
+    inp = workloads.generate(pr, "f16", seed=19)
+    bias = inp["bias"][None, :, None, None]
+    z = dict(inp, mask=torch.zeros_like(inp["mask"]))
+    got = run_gpu(pr, z, mdcn.MDCN_PATH_WINDOW)
+    assert torch.equal(got, bias.expand_as(got))
+    far = torch.full_like(inp["offset"], 3.0e4)
+    far[:, 1::4] = -3.0e4
+    got = run_gpu(pr, dict(inp, offset=far), mdcn.MDCN_PATH_WINDOW)
+    assert torch.equal(got, bias.expand_as(got))
+    Ho, Wo = pr.out_hw()
+    off = torch.zeros_like(inp["offset"])
+    K = pr.kh * pr.kw
+    for k in range(K):
+        i = k // pr.kw
+        anchor = torch.arange(Ho, dtype=torch.float32) * pr.stride[0] - pr.padding[0] \
+            + i * pr.dilation[0]
+        off[:, 2 * k] = (-1.0 - anchor)[:, None].to(off.dtype)
+        off[:, 2 * k + 1] = 0.25
+    got = run_gpu(pr, dict(inp, offset=off), mdcn.MDCN_PATH_WINDOW)
+    assert torch.equal(got, bias.expand_as(got))
