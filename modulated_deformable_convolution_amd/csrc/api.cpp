@@ -179,9 +179,12 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     void *wpack = ws + plan.wpack_off;
     void *xt = ws + plan.xt_off;
     void *col = ws + plan.col_off;
+    uint32_t *win_flags = reinterpret_cast<uint32_t *>(ws + plan.flag_off);
     if (plan.path == Path::Window)
-        err = rec.run(mdcn::K_PACK_WEIGHT_STEPS,
-                      [&] { return mdcn::launch_pack_weight_steps(p, weight, wpack, stream); });
+        err = rec.run(mdcn::K_PACK_WEIGHT_STEPS, [&] {
+            return mdcn::launch_pack_weight_steps(p, weight, wpack, win_flags,
+                                                  int(plan.win_slots), stream);
+        });
     else
         err = rec.run(mdcn::K_PACK_WEIGHT,
                       [&] { return mdcn::launch_pack_weight(p, plan, weight, wpack, stream); });
@@ -210,8 +213,14 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
             continue;
         }
         if (plan.path == Path::Window) {
+            // every launch of this forward publishes partial sums with its own
+            // flag value (the flags were zeroed with the weight packing)
+            const mdcn::WindowScratch scratch{reinterpret_cast<float *>(ws + plan.part_off),
+                                              win_flags, int(plan.win_slots),
+                                              int(n0 / plan.chunk) + 1};
             err = rec.run(mdcn::K_WINDOW, [&] {
-                return mdcn::launch_window(p, plan, cnt, wpack, xt, oc, mc, bias, outc, stream);
+                return mdcn::launch_window(p, plan, cnt, wpack, xt, oc, mc, bias, outc, scratch,
+                                           stream);
             });
             if (err != hipSuccess)
                 return MDCN_E_LAUNCH;
@@ -497,11 +506,11 @@ mdcn_status mdcn_describe_plan(const mdcn_op *op, mdcn_dtype dtype, const int64_
         else if (plan.path == Path::Window)
             std::snprintf(buf, len,
                           "path=window chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld tile=%d "
-                          "margin=%lld ws=%zu (wpack=%zu xt/img=%zu)",
+                          "margin=%lld slots=%lld ws=%zu (wpack=%zu xt/img=%zu)",
                           (long long)plan.chunk, (long long)p.Kg, (long long)plan.Kp,
                           (long long)p.G, (long long)p.Mg, (long long)p.P, int(plan.win_tile),
-                          (long long)plan.win_margin, plan.ws_bytes, plan.wpack_bytes,
-                          plan.xt_bytes_per_image);
+                          (long long)plan.win_margin, (long long)plan.win_slots, plan.ws_bytes,
+                          plan.wpack_bytes, plan.xt_bytes_per_image);
         else
             std::snprintf(buf, len,
                           "path=gather_gemm chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld "

@@ -31,8 +31,9 @@ hipError_t launch_pack_weight(const Problem &p, const Plan &plan, const void *we
 // weight [Co][Cg][kh][kw] -> the window path's step-major planes:
 // [G][S][2][Mg][8], S = (Cg/16)*K steps (chunk of 16 channels, tap), half h
 // of the chunk's channels; requires Cg % 16 == 0.
+// Also zeroes nflags flags at `flags` (the windowed kernel's; may be null).
 hipError_t launch_pack_weight_steps(const Problem &p, const void *weight, void *wpack,
-                                    hipStream_t stream);
+                                    uint32_t *flags, int nflags, hipStream_t stream);
 
 // x [cnt][C][H][W] -> xb [cnt][C/8][H][W][8] (8-channel blocks; C % 8 == 0).
 hipError_t launch_to_channel_blocks(const Problem &p, int64_t cnt, const void *x, void *xb,
@@ -61,9 +62,21 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, int64_t cnt, const v
 // 3x3 kernels; plan.win_tile, win_margin, win_lead), from the step-major
 // weight (launch_pack_weight_steps) and x in 8-channel blocks
 // (launch_to_channel_blocks).
+// Scratch of the windowed kernel: `slots` partial-sum slots of 256 KiB (one
+// per workgroup; a tile split between two workgroups passes its first
+// chunks' sums through the first one's slot) and one flag per slot, zeroed
+// before the forward (launch_pack_weight_steps); `epoch` (> 0) is the value
+// a launch publishes its flags with, distinct for every launch of one
+// forward.
+struct WindowScratch {
+    float *partial;
+    uint32_t *flags;
+    int slots;
+    int epoch;
+};
 hipError_t launch_window(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                          const void *xt, const void *offset, const void *mask, const void *bias,
-                         void *out, hipStream_t stream);
+                         void *out, const WindowScratch &ws, hipStream_t stream);
 
 // Depthwise sampling geometry of cnt images: for each (image, offset group,
 // tap, pixel) a 16-byte record geo[((img*DG + q)*K + k)*P + pix] = {staged

@@ -302,6 +302,13 @@ bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin)
     return found;
 }
 
+int64_t window_tiles_per_image(const Problem &p, WindowTile t)
+{
+    int64_t th, tw;
+    window_tile_dims(t, &th, &tw);
+    return p.G * ((p.Ho + th - 1) / th) * ((p.Wo + tw - 1) / tw) * ((p.Mg + 255) / 256);
+}
+
 bool window_eligible(const Problem &p)
 {
     const int64_t img_bytes = p.C * p.H * p.W * int64_t(p.elem);
@@ -390,22 +397,56 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
                 int64_t((workspace_bytes - kAlign - plan.wpack_bytes) / size_t(img));
             chunk = std::max<int64_t>(1, std::min(chunk, fit));
         }
-        plan.chunk = chunk;
         if (plan.path == Path::Fused && !choose_fused_tile(p, chunk, &plan.fused_tile))
             return MDCN_E_PATH;                 // fused_eligible said some tile fits
+        plan.xt_off = plan.wpack_bytes;
         if (plan.path == Path::Window) {
             if (!choose_window(p, &plan.win_tile, &plan.win_margin))
                 return MDCN_E_PATH;
-            // MDCN_WIN_LEAD=3|5|7 overrides (for tuning)
+            // MDCN_WIN_LEAD=3|5|7 overrides (for tuning); MDCN_WIN_CTAS=<n>
+            // caps the workgroups (more tiles split between two of them)
             plan.win_lead = kWindowMaxLead;
             if (const char *env = std::getenv("MDCN_WIN_LEAD")) {
                 const int v = std::atoi(env);
                 if (v == 3 || v == 5 || v == 7)
                     plan.win_lead = v;
             }
+            plan.win_max_ctas = 0;
+            if (const char *env = std::getenv("MDCN_WIN_CTAS")) {
+                const int v = std::atoi(env);
+                if (v > 0)
+                    plan.win_max_ctas = v;
+            }
+            // Partial-sum slots and flags for the chunk's tiles (one slot per
+            // workgroup, at most kWindowSlots); with a given workspace, the
+            // largest chunk whose layout fits.
+            plan.win_tiles_per_image = window_tiles_per_image(p, plan.win_tile);
+            auto layout = [&](int64_t c, Plan *pl) {
+                pl->win_slots = std::min<int64_t>(kWindowSlots, c * pl->win_tiles_per_image);
+                pl->part_off = align_up(pl->xt_off + size_t(c) * pl->xt_bytes_per_image, kAlign);
+                pl->flag_off = pl->part_off + size_t(pl->win_slots) * kWindowSlotBytes;
+                return pl->flag_off + align_up(size_t(pl->win_slots) * 4, kAlign);
+            };
+            if (!default_sizing) {
+                if (workspace_bytes < kAlign + layout(1, &plan))
+                    return MDCN_E_WORKSPACE;
+                int64_t lo = 1, hi = chunk;             // largest fitting chunk in [1, chunk]
+                while (lo < hi) {
+                    const int64_t mid = lo + (hi - lo + 1) / 2;
+                    if (kAlign + layout(mid, &plan) <= workspace_bytes)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                chunk = lo;
+            }
+            plan.chunk = chunk;
+            plan.ws_bytes = layout(chunk, &plan);
+            plan.col_off = plan.ws_bytes;
+            *out = plan;
+            return MDCN_OK;
         }
-
-        plan.xt_off = plan.wpack_bytes;
+        plan.chunk = chunk;
         plan.col_off = plan.xt_off + size_t(chunk) * plan.xt_bytes_per_image;
         plan.ws_bytes = plan.col_off;
         *out = plan;
@@ -445,6 +486,11 @@ size_t min_workspace(const Problem &p, const Plan &plan)
     (void)p;
     if (plan.path == Path::Depthwise)
         return plan.geo_bytes_per_image ? kAlign + plan.geo_bytes_per_image : 0;
+    if (plan.path == Path::Window) {
+        const int64_t slots = std::min<int64_t>(kWindowSlots, plan.win_tiles_per_image);
+        return kAlign + align_up(plan.wpack_bytes + plan.xt_bytes_per_image, kAlign) +
+               size_t(slots) * kWindowSlotBytes + align_up(size_t(slots) * 4, kAlign);
+    }
     return kAlign + plan.wpack_bytes + plan.xt_bytes_per_image + plan.col_bytes_per_image;
 }
 

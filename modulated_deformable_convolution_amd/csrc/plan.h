@@ -70,10 +70,14 @@ constexpr int kWindowPixels = 1280;      // input positions one LDS window can h
 constexpr int kWindowZeroBytes = 1024;   // zeroed LDS after each window (>= 16*columns + 32)
 constexpr int64_t kWindowMaxMargin = 8;  // default offset margin around the anchors
 constexpr int kWindowMaxLead = 7;        // weight copies issued this many K steps ahead
+constexpr int64_t kWindowSlots = 256;    // partial-sum slots at most (one per workgroup)
+constexpr size_t kWindowSlotBytes = size_t(256) * 256 * 4;   // fp32 256 x 256 tile
 
 // Workspace layout (all offsets 256-byte aligned):
 //   gather + GEMM: [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
 //   fused:         [packed weight: G x Mg x Kp] [x in NHWC: chunk images]
+//   window:        [packed weight] [x in 8-channel blocks: chunk images]
+//                  [partial sums: slots x 256 KiB] [flags: slots x 4 bytes]
 //   depthwise:     [sampling geometry: chunk images x DG x K x 5 x P words]
 struct Plan {
     Path path;
@@ -89,6 +93,10 @@ struct Plan {
     WindowTile win_tile;
     int64_t win_margin;          // window: pixels of margin around the tile's anchors
     int win_lead;                // window: K steps the weight copies run ahead (3, 5, 7)
+    int64_t win_tiles_per_image; // window: output tiles (256 x 256) of one image, all groups
+    int64_t win_slots;           // window: partial-sum slots
+    int64_t win_max_ctas;        // window: cap on the workgroups (0: none; tuning and tests)
+    size_t part_off, flag_off;   // window: offsets of the partial sums and the flags
 };
 
 constexpr size_t kColumnBudget = size_t(256) << 20;   // default column-buffer cap
@@ -126,6 +134,8 @@ int64_t window_extent(int64_t tile, int64_t stride, int64_t k, int64_t dil, int6
 bool window_eligible(const Problem &p);
 // Tile and margin for the windowed kernel (false when none fits).
 bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin);
+// Output tiles of one image (all groups) for a window tile shape.
+int64_t window_tiles_per_image(const Problem &p, WindowTile t);
 mdcn_status check_attrs(const int32_t stride[2], const int32_t padding[2],
                         const int32_t dilation[2], int32_t group, int32_t dgroup);
 mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[16],

@@ -1,6 +1,8 @@
 // prep.hip -- layout kernels: x to channels-last (NHWC) or to 8-channel
 // blocks ([C/8][H][W][8] per image), and the weight repacked in the order a
 // path's contraction walks it.  All of them only move data.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -109,9 +111,13 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const T *__restrict__ 
 template <typename T>
 __global__ __launch_bounds__(256) void pack_weight_steps_kernel(const T *__restrict__ w,
                                                                 T *__restrict__ wp, int total,
-                                                                int Mg, int Cg, int K, int S)
+                                                                int Mg, int Cg, int K, int S,
+                                                                uint32_t *__restrict__ flags,
+                                                                int nflags)
 {
     const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t < nflags)
+        flags[t] = 0u;
     if (t >= total)
         return;
     const int e = t & 7;
@@ -191,25 +197,27 @@ hipError_t launch_to_channel_blocks(const Problem &p, int64_t cnt, const void *x
 }
 
 template <typename T>
-hipError_t pack_weight_steps_t(const Problem &p, const void *w, void *wp, hipStream_t s)
+hipError_t pack_weight_steps_t(const Problem &p, const void *w, void *wp, uint32_t *flags,
+                               int nflags, hipStream_t s)
 {
     const int S = int(p.Cg / 16 * p.K);
     const int total = int(p.G * S * 2 * p.Mg * 8);
-    hipLaunchKernelGGL(pack_weight_steps_kernel<T>, dim3((total + 255) / 256), dim3(256), 0, s,
+    const int n = std::max(total, flags ? nflags : 0);
+    hipLaunchKernelGGL(pack_weight_steps_kernel<T>, dim3((n + 255) / 256), dim3(256), 0, s,
                        static_cast<const T *>(w), static_cast<T *>(wp), total, int(p.Mg),
-                       int(p.Cg), int(p.K), S);
+                       int(p.Cg), int(p.K), S, flags, flags ? nflags : 0);
     return hipGetLastError();
 }
 
 hipError_t launch_pack_weight_steps(const Problem &p, const void *weight, void *wpack,
-                                    hipStream_t stream)
+                                    uint32_t *flags, int nflags, hipStream_t stream)
 {
     if (p.Cg % 16 != 0)
         return hipErrorInvalidValue;
     switch (p.dtype) {
-    case MDCN_F32: return pack_weight_steps_t<float>(p, weight, wpack, stream);
-    case MDCN_F16: return pack_weight_steps_t<half_t>(p, weight, wpack, stream);
-    case MDCN_BF16: return pack_weight_steps_t<bf16_t>(p, weight, wpack, stream);
+    case MDCN_F32: return pack_weight_steps_t<float>(p, weight, wpack, flags, nflags, stream);
+    case MDCN_F16: return pack_weight_steps_t<half_t>(p, weight, wpack, flags, nflags, stream);
+    case MDCN_BF16: return pack_weight_steps_t<bf16_t>(p, weight, wpack, flags, nflags, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -36,6 +36,9 @@
 // The LDS copies are issued as inline-assembly DMA (buffer_load ... lds): the
 // waits for them are explicit (s_waitcnt vmcnt + barrier), so the compiler,
 // which does not see them, cannot make LDS reads wait for unrelated copies.
+#include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 #include "launch.h"
@@ -52,37 +55,67 @@ constexpr int kTaps = 9;                      // 3x3 kernels
 constexpr uint32_t kOOB = 0x80000000u;        // a byte offset past every buffer range
 
 // LDS layout (bytes):
-//   window buffer b (b = 0, 1): [plane 0: kWinPx x 16][plane 1: kWinPx x 16][zeros: kWinZero]
+//   window buffer b (b = 0, 1): [plane 0: kWinPx x 16][gap][plane 1: kWinPx x 16][zeros]
 //   window copy table:          [instruction t][thread]: source byte offset of the
 //                               thread's 16 bytes of window copy instruction t
+//   parked tile index:          one word per wave (256 bytes reserved)
 //   A stage s (s = 0..LEAD):    [plane 0: 256 rows x 16][plane 1: 256 rows x 16]
 // Plane p of an entry holds channels 8p..8p+7 of the chunk.
 constexpr int kWinPlane = kWindowPixels * 16;
+// Plane 1 starts this many bytes past the end of plane 0, so that lanes
+// reading the two planes at the same position use different LDS banks.
+constexpr int kPlaneGap = 128;
+constexpr int kPlane1 = kWinPlane + kPlaneGap;          // start of plane 1
+constexpr int kWinZeroOff = kPlane1 + kWinPlane;        // start of the zero area
 constexpr int kWinZero = kWindowZeroBytes;
-constexpr int kWinBuf = 2 * kWinPlane + kWinZero;
+constexpr int kWinBuf = kWinZeroOff + kWinZero;
 constexpr int kAStage = 256 * 2 * 16;
 constexpr int kWinInstr = 2 * kWindowPixels / 64 / 4;   // window DMA instructions per wave
 constexpr int kWoffOff = 2 * kWinBuf;
-constexpr int kAOff = kWoffOff + kWinInstr * 256 * 4;
+constexpr int kParkOff = kWoffOff + kWinInstr * 256 * 4;  // 4 words: a tile index per wave
+constexpr int kAOff = kParkOff + 256;
 // A stages: the copy of step s+LEAD is issued in step s, into one of LEAD+1
 // stages.
 constexpr int lds_total(int lead) { return kAOff + (lead + 1) * kAStage; }
 constexpr int kAInstr = kAStage / 1024 / 4;             // A DMA instructions per wave
 constexpr int kEpRow = 256 + 4;                          // epilogue slice row, floats
+// Cache-policy operand of a buffer access with device scope (the SC1 bit on
+// gfx950): a store is written through to where every XCD sees it and a load
+// is served from there.  The partial sums passed between workgroups use it,
+// so no whole-L2 writeback or invalidate is needed on either side.
+constexpr int kDevScope = 16;
 static_assert(lds_total(kWindowMaxLead) <= int(kLdsBytes), "LDS budget");
 static_assert(32 * kEpRow * 4 <= lds_total(2), "epilogue slice must fit");
-static_assert((2 * kWindowPixels) % 256 == 0, "window DMA covers whole wave instructions");
+static_assert(kWindowPixels % 128 == 0,
+              "window DMA covers whole wave instructions, none straddling the two planes");
 
 struct WinArgs {
+    const void *A, *xt, *off, *msk, *bias;   // step-major weight, x blocks, offset, mask, bias|null
+    void *out;
+    float *partial;                          // partial-sum slots
+    uint32_t *flags;                         // one flag per slot
     int Mg, Kp, Co, P, Ho, Wo;
     int C, H, W, Cg, nch;          // nch: chunks of 16 channels per group
     int sh, sw, ph, pw, dh, dw;
     int margin, WR, WC;            // window rows / columns
-    int tiles_x, tiles_y, tiles_m, cnt;
+    int tiles_x, tiles_y, tiles_m, cnt, tiles;
+    int epoch;                     // value that marks partial sums published by this launch
     int offC, mskC, Cdg;           // offset / mask channels per image; C / deformable_group
     int has_bias, vec_out;
     uint32_t img_bytes, chunk_bytes, a_bytes;
 };
+
+// The kernel's only argument, read through a pointer into the kernarg
+// segment that the compiler cannot see through at each use site: every
+// region (set-up, tile prologue, fallback, epilogue) loads the fields it needs
+// with scalar loads instead of keeping them in registers across the main
+// loop, where scalar registers are scarce.
+typedef const WinArgs __attribute__((address_space(4))) *KArgs;
+__device__ __forceinline__ KArgs fresh_args(KArgs p)
+{
+    asm volatile("" : "+s"(p));
+    return p;
+}
 
 // Buffer resource (4 scalar registers) over `bytes` bytes at `base`.
 __device__ __forceinline__ v4i srd(const void *base, uint32_t bytes)
@@ -95,6 +128,20 @@ __device__ __forceinline__ v4i srd(const void *base, uint32_t bytes)
     r.w = 0x00020000;
     return r;
 }
+
+// The same as a buffer resource value for the buffer load/store builtins.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t srd_b(const void *base, uint32_t bytes)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    void *p = reinterpret_cast<void *>((uint64_t(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0,
+                                             int(__builtin_amdgcn_readfirstlane(bytes)),
+                                             0x00020000);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16*lane.
 // The compiler does not see this write to LDS; callers wait with vmcnt and
@@ -176,366 +223,589 @@ __device__ __forceinline__ uint4 blend(const uint4 &c0, const uint4 &c1, const u
 
 template <typename T, int TH, int TW, int LEAD>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void window_kernel(const T *__restrict__ A, const T *__restrict__ xt, const T *__restrict__ off,
-                   const T *__restrict__ msk, const T *__restrict__ bias, T *__restrict__ out,
-                   WinArgs a)
+void window_kernel(WinArgs args)
 {
+    (void)args;
+    const KArgs pa = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
+    KArgs a = fresh_args(pa);
     static_assert(TH * TW == 256 && TW % 8 == 0, "a tile is 256 pixels, rows of 8-pixel vectors");
     static_assert(LEAD >= 2 && LEAD + 1 <= 9, "copies lead by 2..8 steps");
     constexpr int kAStages = LEAD + 1;
-    constexpr int E = int(sizeof(T));
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-    // ---- workgroup -> (group, image, tile row, tile column, channel tile)
-    uint32_t bid = xcd_swizzle(blockIdx.x, gridDim.x);
-    const int mt = int(bid % uint32_t(a.tiles_m));
-    bid /= uint32_t(a.tiles_m);
-    const int tx = int(bid % uint32_t(a.tiles_x));
-    bid /= uint32_t(a.tiles_x);
-    const int ty = int(bid % uint32_t(a.tiles_y));
-    bid /= uint32_t(a.tiles_y);
-    const int img = int(bid % uint32_t(a.cnt));
-    const int g = __builtin_amdgcn_readfirstlane(int(bid / uint32_t(a.cnt)));
-    const int m0 = mt * 256;
-    const int ho0 = ty * TH, wo0 = tx * TW;
-    const int r0 = ho0 * a.sh - a.ph - a.margin;     // window origin (input coordinates)
-    const int c0 = wo0 * a.sw - a.pw - a.margin;
-    const int q = (g * a.Cg) / a.Cdg;                // the group's offset group
-
-    const int tid = int(threadIdx.x);
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = lane >> 5;                      // plane: channels 8*half..+8 of a chunk
-
     const uint32_t lds0 = lds_addr(smem);
-    const v4i rx = srd(xt, a.chunk_bytes);
-    const v4i ra = srd(reinterpret_cast<const char *>(A) + size_t(g) * a.a_bytes, a.a_bytes);
-    const uint32_t hw16 = uint32_t(a.H * a.W) * 16;   // bytes of one 8-channel block plane
-
-    // ---- per-lane DMA source offsets of the window (per tile, kept in LDS)
-    // and of the A rows
     uint32_t *woff_tab = reinterpret_cast<uint32_t *>(smem + kWoffOff);
-#pragma unroll
-    for (int t = 0; t < kWinInstr; ++t) {
-        const int S = (t * 4 + wave) * 64 + lane;          // 16-byte slot of the buffer
-        const int pl = S / kWindowPixels;
-        const int px = S - pl * kWindowPixels;
-        const int r = px / a.WC, c = px - (px / a.WC) * a.WC;
-        const int gr = r0 + r, gc = c0 + c;
-        const bool ok = px < a.WR * a.WC && (unsigned)gr < (unsigned)a.H &&
-                        (unsigned)gc < (unsigned)a.W;
-        const uint32_t o = ok ? uint32_t(img) * a.img_bytes + uint32_t(pl) * hw16 +
-                                    uint32_t(gr * a.W + gc) * 16
-                              : kOOB;
-        woff_tab[t * 256 + tid] = o;
-    }
-    uint32_t aoff[kAInstr];
-#pragma unroll
-    for (int t = 0; t < kAInstr; ++t) {
-        const int S = (t * 4 + wave) * 64 + lane;
-        const int pl = S >> 8, row = S & 255;
-        aoff[t] = (m0 + row < a.Mg) ? uint32_t(pl * a.Mg + m0 + row) * 16 : kOOB;
-    }
-    // the group's first 8-channel block plane, bytes
-    const uint32_t ch_base = uint32_t(g * a.Cg / 8) * hw16;
-    // (the table is read back only after the barrier that follows its writes)
-    auto issue_window = [&](int chunk, int buf) {
-        const uint32_t soff = __builtin_amdgcn_readfirstlane(ch_base + uint32_t(chunk * 2) * hw16);
-        uint32_t wo[kWinInstr];                 // all table reads first: one LDS wait
-#pragma unroll
-        for (int t = 0; t < kWinInstr; ++t)
-            wo[t] = woff_tab[t * 256 + tid];
-#pragma unroll
-        for (int t = 0; t < kWinInstr; ++t)
-            dma16(lds0 + buf * kWinBuf + (t * 4 + wave) * 1024, rx, wo[t], soff);
-    };
-    const int steps = a.nch * kTaps;
-    auto issue_a = [&](int step) {
-        const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(step * 2 * a.Mg) * 16);
-#pragma unroll
-        for (int t = 0; t < kAInstr; ++t)
-            dma16(lds0 + kAOff + (step % kAStages) * kAStage + (t * 4 + wave) * 1024, ra, aoff[t],
-                  soff);
-    };
-
-    // ---- prologue copies: window of chunk 0, A of steps 0 .. LEAD-1
-    issue_window(0, 0);
-#pragma unroll
-    for (int s = 0; s < LEAD; ++s)
-        if (s < steps)
-            issue_a(s);
-
-    // ---- sampling geometry of the lane's two pixels, all taps
-    uint32_t gaddr[2][kTaps];
-    float gw[2][kTaps][4];
-    uint32_t fbl = 0;                                // lane: (slab, tap) needs the fallback
-    {
-        const int P = a.P;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int n = (wave * 2 + s) * 32 + (lane & 31);
-            const int ho = ho0 + n / TW, wo = wo0 + n % TW;
-            const bool pv = ho < a.Ho && wo < a.Wo;
-            const int pix = pv ? ho * a.Wo + wo : 0;
-            const size_t ob = (size_t(img) * a.offC + size_t(q) * 2 * kTaps) * P + pix;
-            const size_t mb = (size_t(img) * a.mskC + size_t(q) * kTaps) * P + pix;
-            float oh[kTaps], ow[kTaps], mm[kTaps];
-#pragma unroll
-            for (int k = 0; k < kTaps; ++k) {
-                oh[k] = to_f32(off[ob + size_t(2 * k) * P]);
-                ow[k] = to_f32(off[ob + size_t(2 * k + 1) * P]);
-                mm[k] = to_f32(msk[mb + size_t(k) * P]);
-            }
-#pragma unroll
-            for (int k = 0; k < kTaps; ++k) {
-                const int i = k / 3, j = k % 3;
-                const int ah = ho * a.sh - a.ph + i * a.dh;
-                const int aw = wo * a.sw - a.pw + j * a.dw;
-                const float lim = 33554432.0f;
-                const bool fin = fabsf(oh[k]) <= lim && fabsf(ow[k]) <= lim;
-                const float fh = fin ? floorf(oh[k]) : 0.0f;
-                const float fw = fin ? floorf(ow[k]) : 0.0f;
-                const float ly = fin ? oh[k] - fh : 0.0f;
-                const float lx = fin ? ow[k] - fw : 0.0f;
-                const int h0 = ah + int(fh), w0 = aw + int(fw);
-                const bool any = pv && fin && h0 >= -1 && h0 < a.H && w0 >= -1 && w0 < a.W;
-                const int lr = h0 - r0, lc = w0 - c0;
-                const bool inw = (unsigned)lr <= unsigned(a.WR - 2) &&
-                                 (unsigned)lc <= unsigned(a.WC - 2);
-                const bool use = any && inw;
-                const float hy = 1.0f - ly, hx = 1.0f - lx, m = mm[k];
-                gw[s][k][0] = use ? hy * hx * m : 0.0f;
-                gw[s][k][1] = use ? hy * lx * m : 0.0f;
-                gw[s][k][2] = use ? ly * hx * m : 0.0f;
-                gw[s][k][3] = use ? ly * lx * m : 0.0f;
-                gaddr[s][k] = use ? uint32_t(half * kWinPlane + (lr * a.WC + lc) * 16)
-                                  : uint32_t(2 * kWinPlane);
-                fbl |= uint32_t(any && !inw) << (s * kTaps + k);
-            }
-        }
-    }
-    // wave-level: which (slab, tap) has a lane that needs the fallback
-    uint32_t fbw = 0;
-#pragma unroll
-    for (int b = 0; b < 2 * kTaps; ++b)
-        fbw |= uint32_t(__builtin_amdgcn_ballot_w64(((fbl >> b) & 1u) != 0u) != 0) << b;
-    fbw = __builtin_amdgcn_readfirstlane(fbw);
-
-    // Fallback: the lane's 8 channels of sample (slab s, tap k) in chunk
-    // `chunk`, from global memory (rare).
-    auto fallback = [&](int s, int k, int chunk, uint4 &bv) {
-        if ((fbl >> (s * kTaps + k)) & 1u) {
-            const int n = (wave * 2 + s) * 32 + (lane & 31);
-            const int ho = ho0 + n / TW, wo = wo0 + n % TW;
-            const int pix = ho * a.Wo + wo;
-            const size_t ob = (size_t(img) * a.offC + size_t(q) * 2 * kTaps + 2 * k) * a.P + pix;
-            const float oh = to_f32(off[ob]), ow = to_f32(off[ob + a.P]);
-            const float m = to_f32(msk[(size_t(img) * a.mskC + size_t(q) * kTaps + k) * a.P + pix]);
-            const int i = k / 3, j = k % 3;
-            const Taps tp = make_taps(ho * a.sh - a.ph + i * a.dh, wo * a.sw - a.pw + j * a.dw,
-                                      oh, ow, m, a.H, a.W);
-            const uint32_t cb = ch_base + uint32_t(chunk * 2 + half) * hw16;
-            uint4 cv[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t o = tp.valid[t]
-                                       ? uint32_t(img) * a.img_bytes + uint32_t(tp.idx[t]) * 16 +
-                                             cb
-                                       : kOOB;
-                const auto r = __builtin_amdgcn_raw_buffer_load_b128(
-                    __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(xt), (short)0,
-                                                      int(a.chunk_bytes), 0x00020000),
-                    o, 0, 0);
-                __builtin_memcpy(&cv[t], &r, 16);
-            }
-            const float w4[4] = {tp.wt[0], tp.wt[1], tp.wt[2], tp.wt[3]};
-            bv = blend<T>(cv[0], cv[1], cv[2], cv[3], w4, 0.0f);
-        }
-    };
 
     // zero areas of both window buffers (read by lanes whose sample is not
-    // in the window)
-    for (int i = tid; i < 2 * kWinZero / 8; i += 256) {
+    // in the window); no copy ever writes them
+    for (int i = int(threadIdx.x); i < 2 * kWinZero / 8; i += 256) {
         const int b = i / (kWinZero / 8), o = i - b * (kWinZero / 8);
-        *reinterpret_cast<uint2 *>(smem + b * kWinBuf + 2 * kWinPlane + o * 8) = make_uint2(0u, 0u);
+        *reinterpret_cast<uint2 *>(smem + b * kWinBuf + kWinZeroOff + o * 8) = make_uint2(0u, 0u);
     }
 
-    float16v acc[8][2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[i][s][r] = 0.0f;
-
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // A fragment of block i of step `step` (plane = half, row = 32i + lane%32)
-    const uint32_t a_lane = uint32_t(half * (kAStage / 2) + (lane & 31) * 16);
-    auto read_a = [&](uint4 (&fa)[8], int step) {
-        const uint32_t so = __builtin_amdgcn_readfirstlane(
-            uint32_t(kAOff + (step % kAStages) * kAStage));
-        const char *st = smem + (a_lane + so);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
+    // This workgroup's share of the (tile, chunk) units: [u0, u1), split
+    // evenly.  A tile shared with the previous workgroup (its first chunks
+    // are there) comes first in the range, a tile shared with the next one
+    // last.  Tiles are processed from the last to the first:
+    // the partial sums of the last tile are published at once, and the first
+    // tile is finished with the previous workgroup's partial sums at the
+    // very end, so a workgroup only ever waits for a lower-numbered one
+    // (dispatched earlier, and publishing first).
+    //
+    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2),
+    // so with a grid that is a multiple of 8 the tiles are first split into
+    // 8 contiguous runs of whole tiles, one per XCD (neighbouring tiles share
+    // window rows, which then stay in one L2), and each run is split evenly
+    // over that XCD's workgroups cta = x, x+8, x+16, ...: the previous
+    // workgroup of a run is cta-8.
+    const uint32_t cta = blockIdx.x;
+    // [u0, u1) and the run's previous workgroup, from the arguments
+    // (recomputed where needed rather than kept in scalar registers)
+    struct Range {
+        uint32_t u0, u1, prev;
     };
-    const uint32_t wrow = uint32_t(a.WC * 16);
-    // corners of (slab s, tap k) from window buffer `buf`
-    auto read_corners = [&](uint4 (&cr)[4], int s, int k, int buf) {
-        const uint32_t bo = __builtin_amdgcn_readfirstlane(uint32_t(buf ? kWinBuf : 0));
-        const char *p = smem + (gaddr[s][k] + bo);
-        const char *p2 = p + wrow;
-        cr[0] = *reinterpret_cast<const uint4 *>(p);
-        cr[1] = *reinterpret_cast<const uint4 *>(p + 16);
-        cr[2] = *reinterpret_cast<const uint4 *>(p2);
-        cr[3] = *reinterpret_cast<const uint4 *>(p2 + 16);
+    auto range_of = [&](KArgs a) {
+        const uint32_t ncta = gridDim.x, nch = uint32_t(a->nch), tiles = uint32_t(a->tiles);
+        const uint32_t ngrp = (ncta % 8u == 0u && tiles >= ncta) ? 8u : 1u;
+        const uint32_t grp = cta % ngrp, per = ncta / ngrp, idx = cta / ngrp;
+        const uint32_t tg0 = uint32_t((uint64_t(grp) * tiles) / ngrp);
+        const uint32_t tg1 = uint32_t((uint64_t(grp + 1) * tiles) / ngrp);
+        const uint32_t U = (tg1 - tg0) * nch;
+        Range r;
+        r.u0 = tg0 * nch + uint32_t((uint64_t(idx) * U) / per);
+        r.u1 = tg0 * nch + uint32_t((uint64_t(idx + 1) * U) / per);
+        r.prev = cta - ngrp;
+        return r;
     };
-
-    float zero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-    uint4 fa[8];
-    uint4 cr[2][4];
-    uint4 b[2];
-    // step 0's operands
-    read_a(fa, 0);
-    read_corners(cr[0], 0, 0, 0);
-    read_corners(cr[1], 1, 0, 0);
-    b[0] = blend<T>(cr[0][0], cr[0][1], cr[0][2], cr[0][3], gw[0][0], zero);
-    b[1] = blend<T>(cr[1][0], cr[1][1], cr[1][2], cr[1][3], gw[1][0], zero);
-    if (fbw & (1u | (1u << kTaps))) {
-        fallback(0, 0, 0, b[0]);
-        fallback(1, 0, 0, b[1]);
-    }
-    if (steps > 1) {
-        read_corners(cr[0], 0, 1 % kTaps, 0);
-        read_corners(cr[1], 1, 1 % kTaps, 0);
-    }
-
-    // One step: s = chunk*9 + k.  K (tap) is a compile-time index so the
-    // geometry stays in registers.
-    auto step_body = [&](int chunk, auto kc) {
-        constexpr int k = decltype(kc)::value;
-        const int s = chunk * kTaps + k;
-        const bool last_chunk = chunk + 1 >= a.nch;
-        // A of step s+1 (and, with it, every older copy) has landed; the
-        // previous step's LDS reads are complete.  A(s+1) was issued in step
-        // s+1-LEAD; issued after it, and allowed to be in flight: the A
-        // copies of the LEAD-2 steps between, and the window copy of the
-        // next chunk when a step k == 0 lies in [s+1-LEAD, s-1].  In the last
-        // chunk no window is issued and the A copies stop at the last step.
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        if (last_chunk) {
-            constexpr int NA = kAInstr * ((LEAD - 2) < (7 - k) ? (LEAD - 2) : (7 - k > 0 ? 7 - k : 0));
-            __builtin_amdgcn_s_waitcnt((NA & 15) | ((NA >> 4) << 14) | 0x70);
-        } else if (k >= 1 && k <= LEAD - 1) {
-            constexpr int N = kAInstr * (LEAD - 2) + kWinInstr;
-            __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
-        } else {
-            constexpr int N = kAInstr * (LEAD - 2);
-            __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
-        }
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::: "memory");
-        if (s + LEAD < steps)
-            issue_a(s + LEAD);
-        if (k == 0 && !last_chunk)
-            issue_window(chunk + 1, (chunk + 1) & 1);
-
-        // MFMAs of step s, interleaved group by group (the wave issues in
-        // order and is the only one on its SIMD) with the reads of step
-        // s+1's A fragments (block i as soon as its two MFMAs have issued),
-        // the blend of step s+1's B (one element pair per group) and the
-        // corner reads of step s+2 (a slab's, once its blend is done).
-        // Reads past the last step hit valid (stale) LDS and are never used.
-        constexpr int k1 = (k + 1) % kTaps, k2 = (k + 2) % kTaps;
-        const int ch1 = (k + 1 >= kTaps) ? chunk + 1 : chunk;
-        const int ch2 = (k + 2 >= kTaps) ? chunk + 1 : chunk;
-        const uint32_t so = __builtin_amdgcn_readfirstlane(
-            uint32_t(kAOff + ((s + 1) % kAStages) * kAStage));
-        const char *st = smem + (a_lane + so);
-        uint32_t bn[2][4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            acc[i][0] = Mma<T>::step(fa[i], b[0], acc[i][0]);
-            acc[i][1] = Mma<T>::step(fa[i], b[1], acc[i][1]);
-            fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
-            const int sl = i >> 2, pr = i & 3;
-            bn[sl][pr] = blend_pair<T>(cr[sl], gw[sl][k1], zero, pr);
-            if (pr == 3)
-                read_corners(cr[sl], sl, k2, ch2 & 1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        b[0] = make_uint4(bn[0][0], bn[0][1], bn[0][2], bn[0][3]);
-        b[1] = make_uint4(bn[1][0], bn[1][1], bn[1][2], bn[1][3]);
-        if (s + 1 < steps && (fbw & ((1u << k1) | (1u << (kTaps + k1))))) {
-            fallback(0, k1, ch1, b[0]);
-            fallback(1, k1, ch1, b[1]);
-        }
+    // a tile's chunk segment [c_lo, c_hi) in this workgroup and its position
+    struct TileInfo {
+        int c_lo, c_hi, m0, ho0, wo0, img, g;
     };
-
-    for (int chunk = 0; chunk < a.nch; ++chunk) {
-        step_body(chunk, std::integral_constant<int, 0>{});
-        step_body(chunk, std::integral_constant<int, 1>{});
-        step_body(chunk, std::integral_constant<int, 2>{});
-        step_body(chunk, std::integral_constant<int, 3>{});
-        step_body(chunk, std::integral_constant<int, 4>{});
-        step_body(chunk, std::integral_constant<int, 5>{});
-        step_body(chunk, std::integral_constant<int, 6>{});
-        step_body(chunk, std::integral_constant<int, 7>{});
-        step_body(chunk, std::integral_constant<int, 8>{});
+    auto tile_info = [&](KArgs a, const Range &r, int tile) {
+        const uint32_t nch = uint32_t(a->nch);
+        TileInfo ti;
+        ti.c_lo = int(max(r.u0, uint32_t(tile) * nch) - uint32_t(tile) * nch);
+        ti.c_hi = int(min(r.u1, uint32_t(tile + 1) * nch) - uint32_t(tile) * nch);
+        uint32_t bid = uint32_t(tile);
+        ti.m0 = int(bid % uint32_t(a->tiles_m)) * 256;
+        bid /= uint32_t(a->tiles_m);
+        ti.wo0 = int(bid % uint32_t(a->tiles_x)) * TW;
+        bid /= uint32_t(a->tiles_x);
+        ti.ho0 = int(bid % uint32_t(a->tiles_y)) * TH;
+        bid /= uint32_t(a->tiles_y);
+        ti.img = int(bid % uint32_t(a->cnt));
+        ti.g = int(bid / uint32_t(a->cnt));
+        return ti;
+    };
+    int tile;
+    {
+        const Range r = range_of(a);
+        if (r.u0 >= r.u1)
+            return;
+        tile = int((r.u1 - 1) / uint32_t(a->nch));   // the range's last tile comes first
     }
+    // per-wave LDS word that holds the tile index across the main loop
+    int *tile_park = reinterpret_cast<int *>(smem + kParkOff) +
+                     __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
 
-    // ---- epilogue: per block of 32 output channels, through LDS, + bias,
-    // one rounding, 16-byte stores of 8 pixels along a tile row.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    float *slice = reinterpret_cast<float *>(smem);
-    const bool vec = a.vec_out != 0;
+    for (;;) {
+        // Every lane- and argument-derived value is derived afresh per tile
+        // (the thread index passes through an empty asm): a value hoisted out
+        // of the tile loop would be live across the main loop, where no
+        // register is free, and its spill reloads would wait for every store
+        // in flight.
+        int tid = int(threadIdx.x);
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int half = lane >> 5;                  // plane: channels 8*half..+8 of a chunk
+        KArgs a = fresh_args(pa);
+        const v4i rx = srd(a->xt, a->chunk_bytes);
+        const uint32_t hw16 = uint32_t(a->H * a->W) * 16;   // bytes of one 8-channel block plane
+        const uint32_t wrow = uint32_t(a->WC * 16);
+        const uint32_t a_lane = uint32_t(half * (kAStage / 2) + (lane & 31) * 16);
+        float zero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+        const int nch = a->nch;
+        const TileInfo ti = tile_info(a, range_of(a), tile);
+        const int c_lo = ti.c_lo, c_hi = ti.c_hi;
+        const int m0 = ti.m0, ho0 = ti.ho0, wo0 = ti.wo0, img = ti.img;
+        const int g = __builtin_amdgcn_readfirstlane(ti.g);
+        const int r0 = ho0 * a->sh - a->ph - a->margin;  // window origin (input coordinates)
+        const int c0 = wo0 * a->sw - a->pw - a->margin;
+        const int q = (g * a->Cg) / a->Cdg;              // the group's offset group
+        const v4i ra =
+            srd(static_cast<const char *>(a->A) + size_t(g) * a->a_bytes, a->a_bytes);
+        if (lane == 0)
+            *tile_park = tile;
+
+        // ---- per-lane DMA source offsets of the window (kept in LDS; each
+        // thread reads back only its own entries) and of the A rows
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+        for (int t = 0; t < kWinInstr; ++t) {
+            const int S = (t * 4 + wave) * 64 + lane;          // 16-byte slot of the buffer
+            const int pl = S / kWindowPixels;
+            const int px = S - pl * kWindowPixels;
+            const int r = px / a->WC, c = px - (px / a->WC) * a->WC;
+            const int gr = r0 + r, gc = c0 + c;
+            const bool ok = px < a->WR * a->WC && (unsigned)gr < (unsigned)a->H &&
+                            (unsigned)gc < (unsigned)a->W;
+            woff_tab[t * 256 + tid] = ok ? uint32_t(img) * a->img_bytes + uint32_t(pl) * hw16 +
+                                               uint32_t(gr * a->W + gc) * 16
+                                         : kOOB;
+        }
+        uint32_t aoff[kAInstr];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int t = 0; t < kAInstr; ++t) {
+            const int S = (t * 4 + wave) * 64 + lane;
+            const int pl = S >> 8, row = S & 255;
+            aoff[t] = (m0 + row < a->Mg) ? uint32_t(pl * a->Mg + m0 + row) * 16 : kOOB;
+        }
+        // the group's first 8-channel block plane, bytes
+        const uint32_t ch_base = uint32_t(g * a->Cg / 8) * hw16;
+        auto issue_window = [&](int chunk, int buf) {
+            const uint32_t soff =
+                __builtin_amdgcn_readfirstlane(ch_base + uint32_t(chunk * 2) * hw16);
+            uint32_t wo[kWinInstr];                 // all table reads first: one LDS wait
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                slice[(8 * (r >> 2) + 4 * half + (r & 3)) * kEpRow + (wave * 2 + s) * 32 +
-                      (lane & 31)] = acc[i][s][r];
-        __syncthreads();
+            for (int t = 0; t < kWinInstr; ++t)
+                wo[t] = woff_tab[t * 256 + tid];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int v = tid + 256 * j;
-            const int row = v >> 5, n = (v & 31) * 8;
-            const int m = m0 + i * 32 + row;
-            const int ho = ho0 + n / TW, wo = wo0 + n % TW;
-            if (m < a.Mg && ho < a.Ho) {
-                const float bv = a.has_bias ? to_f32(bias[size_t(g) * a.Mg + m]) : 0.0f;
-                T *dst = out + (size_t(img) * a.Co + size_t(g) * a.Mg + m) * a.P +
-                         size_t(ho) * a.Wo + wo;
-                const float *sp = slice + row * kEpRow + n;
-                if (vec && wo + 8 <= a.Wo) {
-                    Vec16<T> o;
+            for (int t = 0; t < kWinInstr; ++t)
+                dma16(lds0 + buf * kWinBuf + (t * 4 + wave) * 1024 +
+                          ((t * 4 + wave) * 64 >= kWindowPixels ? kPlaneGap : 0),
+                      rx, wo[t], soff);
+        };
+        // K steps of the segment: step s (relative to its first chunk c_lo)
+        // is tap s % 9 of chunk c_lo + s / 9; its A tile is step
+        // 9*c_lo + s of the group's step-major weight.
+        const int steps = (c_hi - c_lo) * kTaps;
+        const int s_base = c_lo * kTaps;
+        // (bytes per step of the step-major weight, held in a register: the
+        // compiler would otherwise reload the argument inside the main loop)
+        uint32_t a_step = uint32_t(a->Mg) * 32;
+        asm volatile("" : "+s"(a_step));
+        auto issue_a = [&](int step) {
+            const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(s_base + step) * a_step);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        o.e[e] = from_f32<T>(sp[e] + bv);
-                    store16(dst, o);
-                } else {
-                    for (int e = 0; e < 8 && wo + e < a.Wo; ++e)
-                        dst[e] = from_f32<T>(sp[e] + bv);
+            for (int t = 0; t < kAInstr; ++t)
+                dma16(lds0 + kAOff + (step % kAStages) * kAStage + (t * 4 + wave) * 1024, ra,
+                      aoff[t], soff);
+        };
+
+        // ---- prologue copies: window of the first chunk, A of steps 0 .. LEAD-1
+        issue_window(c_lo, 0);
+#pragma unroll
+        for (int s = 0; s < LEAD; ++s)
+            if (s < steps)
+                issue_a(s);
+
+        // ---- sampling geometry of the lane's two pixels, all taps
+        uint32_t gaddr[2][kTaps];
+        float gw[2][kTaps][4];
+        uint32_t fbl = 0;                            // lane: (slab, tap) needs the fallback
+        {
+            const int P = a->P;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int n = (wave * 2 + s) * 32 + (lane & 31);
+                const int ho = ho0 + n / TW, wo = wo0 + n % TW;
+                const bool pv = ho < a->Ho && wo < a->Wo;
+                const int pix = pv ? ho * a->Wo + wo : 0;
+                const size_t ob = (size_t(img) * a->offC + size_t(q) * 2 * kTaps) * P + pix;
+                const size_t mb = (size_t(img) * a->mskC + size_t(q) * kTaps) * P + pix;
+                const T *off = static_cast<const T *>(a->off);
+                const T *msk = static_cast<const T *>(a->msk);
+                float oh[kTaps], ow[kTaps], mm[kTaps];
+#pragma unroll
+                for (int k = 0; k < kTaps; ++k) {
+                    oh[k] = to_f32(off[ob + size_t(2 * k) * P]);
+                    ow[k] = to_f32(off[ob + size_t(2 * k + 1) * P]);
+                    mm[k] = to_f32(msk[mb + size_t(k) * P]);
                 }
+#pragma unroll
+                for (int k = 0; k < kTaps; ++k) {
+                    const int i = k / 3, j = k % 3;
+                    const int ah = ho * a->sh - a->ph + i * a->dh;
+                    const int aw = wo * a->sw - a->pw + j * a->dw;
+                    const float lim = 33554432.0f;
+                    const bool fin = fabsf(oh[k]) <= lim && fabsf(ow[k]) <= lim;
+                    const float fh = fin ? floorf(oh[k]) : 0.0f;
+                    const float fw = fin ? floorf(ow[k]) : 0.0f;
+                    const float ly = fin ? oh[k] - fh : 0.0f;
+                    const float lx = fin ? ow[k] - fw : 0.0f;
+                    const int h0 = ah + int(fh), w0 = aw + int(fw);
+                    const bool any = pv && fin && h0 >= -1 && h0 < a->H && w0 >= -1 && w0 < a->W;
+                    const int lr = h0 - r0, lc = w0 - c0;
+                    const bool inw = (unsigned)lr <= unsigned(a->WR - 2) &&
+                                     (unsigned)lc <= unsigned(a->WC - 2);
+                    const bool use = any && inw;
+                    const float hy = 1.0f - ly, hx = 1.0f - lx, m = mm[k];
+                    gw[s][k][0] = use ? hy * hx * m : 0.0f;
+                    gw[s][k][1] = use ? hy * lx * m : 0.0f;
+                    gw[s][k][2] = use ? ly * hx * m : 0.0f;
+                    gw[s][k][3] = use ? ly * lx * m : 0.0f;
+                    gaddr[s][k] = use ? uint32_t(half * kPlane1 + (lr * a->WC + lc) * 16)
+                                      : uint32_t(kWinZeroOff);
+                    fbl |= uint32_t(any && !inw) << (s * kTaps + k);
+                }
+                __builtin_amdgcn_sched_barrier(0);    // one slab's loads in flight at a time
             }
         }
+        // wave-level: which (slab, tap) has a lane that needs the fallback
+        uint32_t fbw = 0;
+#pragma unroll
+        for (int b = 0; b < 2 * kTaps; ++b)
+            fbw |= uint32_t(__builtin_amdgcn_ballot_w64(((fbl >> b) & 1u) != 0u) != 0) << b;
+        fbw = __builtin_amdgcn_readfirstlane(fbw);
+
+        // Fallback: the lane's 8 channels of sample (slab s, tap k) in chunk
+        // `chunk`, from global memory (rare).
+        auto fallback = [&](int s, int k, int chunk, uint4 &bv) {
+            if ((fbl >> (s * kTaps + k)) & 1u) {
+                KArgs a = fresh_args(pa);
+                const T *offp = static_cast<const T *>(a->off);
+                const T *mskp = static_cast<const T *>(a->msk);
+                const int n = (wave * 2 + s) * 32 + (lane & 31);
+                const int ho = ho0 + n / TW, wo = wo0 + n % TW;
+                const int pix = ho * a->Wo + wo;
+                const size_t ob =
+                    (size_t(img) * a->offC + size_t(q) * 2 * kTaps + 2 * k) * a->P + pix;
+                const float oh = to_f32(offp[ob]), ow = to_f32(offp[ob + a->P]);
+                const float m =
+                    to_f32(mskp[(size_t(img) * a->mskC + size_t(q) * kTaps + k) * a->P + pix]);
+                const int i = k / 3, j = k % 3;
+                const Taps tp = make_taps(ho * a->sh - a->ph + i * a->dh,
+                                          wo * a->sw - a->pw + j * a->dw, oh, ow, m, a->H, a->W);
+                const uint32_t cb = ch_base + uint32_t(chunk * 2 + half) * hw16;
+                uint4 cv[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t o = tp.valid[t] ? uint32_t(img) * a->img_bytes +
+                                                         uint32_t(tp.idx[t]) * 16 + cb
+                                                   : kOOB;
+                    const auto r = __builtin_amdgcn_raw_buffer_load_b128(
+                        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a->xt), (short)0,
+                                                          int(a->chunk_bytes), 0x00020000),
+                        o, 0, 0);
+                    __builtin_memcpy(&cv[t], &r, 16);
+                }
+                const float w4[4] = {tp.wt[0], tp.wt[1], tp.wt[2], tp.wt[3]};
+                bv = blend<T>(cv[0], cv[1], cv[2], cv[3], w4, 0.0f);
+            }
+        };
+
+        // Accumulators: zero, or -- for a tile whose first chunks the
+        // previous workgroup of the run computed -- its partial sums, which
+        // that workgroup published first thing (so the wait is short; the
+        // spin is bounded, so that a broken invariant gives a wrong result,
+        // never a stuck GPU).  The slot holds each lane's accumulator
+        // registers as they are: wave w's 64 KB, 16-byte group j of every
+        // lane at w*64K + j*1K + lane*16.
+        float16v acc[8][2];
+        {
+            const bool resume = c_lo > 0;
+            const uint32_t prev = range_of(a).prev;
+            if (resume && tid == 0) {
+                for (uint32_t it = 0; it < (1u << 26); ++it) {
+                    if (__hip_atomic_load(a->flags + prev, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == uint32_t(a->epoch))
+                        break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __builtin_amdgcn_s_barrier();
+            // (a tile started here reads through an empty buffer: zeros, with
+            // no memory access and no branch)
+            const __amdgpu_buffer_rsrc_t rs =
+                srd_b(a->partial + (resume ? size_t(prev) * 65536 : 0),
+                      resume ? uint32_t(65536 * 4) : 0u);
+            const uint32_t lo = uint32_t(wave * 65536 + lane * 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                            rs, lo + uint32_t(((i * 2 + s) * 4 + q) * 1024), 0, kDevScope);
+                        float4v f;
+                        __builtin_memcpy(&f, &v, 16);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][s][4 * q + e] = f[e];
+                    }
+        }
+
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+
+        // A fragment of block i of step `step` (plane = half, row = 32i + lane%32)
+        auto read_a = [&](uint4 (&fa)[8], int step) {
+            const uint32_t so = __builtin_amdgcn_readfirstlane(
+                uint32_t(kAOff + (step % kAStages) * kAStage));
+            const char *st = smem + (a_lane + so);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
+        };
+        // corners of (slab s, tap k) from window buffer `buf`
+        auto read_corners = [&](uint4 (&cr)[4], int s, int k, int buf) {
+            const uint32_t bo = __builtin_amdgcn_readfirstlane(uint32_t(buf ? kWinBuf : 0));
+            const char *p = smem + (gaddr[s][k] + bo);
+            const char *p2 = p + wrow;
+            cr[0] = *reinterpret_cast<const uint4 *>(p);
+            cr[1] = *reinterpret_cast<const uint4 *>(p + 16);
+            cr[2] = *reinterpret_cast<const uint4 *>(p2);
+            cr[3] = *reinterpret_cast<const uint4 *>(p2 + 16);
+        };
+
+        uint4 fa[8];
+        uint4 cr[2][4];
+        uint4 b[2];
+        // step 0's operands
+        read_a(fa, 0);
+        read_corners(cr[0], 0, 0, 0);
+        read_corners(cr[1], 1, 0, 0);
+        b[0] = blend<T>(cr[0][0], cr[0][1], cr[0][2], cr[0][3], gw[0][0], zero);
+        b[1] = blend<T>(cr[1][0], cr[1][1], cr[1][2], cr[1][3], gw[1][0], zero);
+        if (fbw & (1u | (1u << kTaps))) {
+            fallback(0, 0, c_lo, b[0]);
+            fallback(1, 0, c_lo, b[1]);
+        }
+        read_corners(cr[0], 0, 1, 0);
+        read_corners(cr[1], 1, 1, 0);
+
+        // One step: relative step s = rc*9 + k of chunk c_lo + rc.  The tap
+        // k is a compile-time index so the geometry stays in registers.
+        auto step_body = [&](int rc, auto kc) {
+            constexpr int k = decltype(kc)::value;
+            const int s = rc * kTaps + k;
+            const int chunk = c_lo + rc;
+            const bool last_chunk = chunk + 1 >= c_hi;
+            // A of step s+1 (and, with it, every older copy) has landed.  A(s+1)
+            // was issued in step s+1-LEAD; issued after it, and allowed to be in
+            // flight: the A copies of the LEAD-2 steps between, and the window
+            // copy of the next chunk when a step k == 0 lies in [s+1-LEAD, s-1].
+            // In the last chunk no window is issued and the A copies stop at the
+            // last step.  (No LDS wait: every LDS read of an A stage or window
+            // buffer that a copy issued after this barrier overwrites was
+            // consumed -- so waited for -- in an earlier step.)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int kNoLgkm = 0x70 | 0xF00;         // expcnt and lgkmcnt: no wait
+            if (last_chunk) {
+                constexpr int NA =
+                    kAInstr * ((LEAD - 2) < (7 - k) ? (LEAD - 2) : (7 - k > 0 ? 7 - k : 0));
+                __builtin_amdgcn_s_waitcnt((NA & 15) | ((NA >> 4) << 14) | kNoLgkm);
+            } else if (k >= 1 && k <= LEAD - 1) {
+                constexpr int N = kAInstr * (LEAD - 2) + kWinInstr;
+                __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+            } else {
+                constexpr int N = kAInstr * (LEAD - 2);
+                __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+            }
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+            if (s + LEAD < steps)
+                issue_a(s + LEAD);
+            if (k == 0 && !last_chunk)
+                issue_window(chunk + 1, (rc + 1) & 1);
+
+            // MFMAs of step s, interleaved group by group (the wave issues in
+            // order and is the only one on its SIMD) with the reads of step
+            // s+1's A fragments (block i as soon as its two MFMAs have issued),
+            // the blend of step s+1's B (one element pair per group) and the
+            // corner reads of step s+2 (a slab's, once its blend is done).
+            // Reads past the last step hit valid (stale) LDS and are never used.
+            constexpr int k1 = (k + 1) % kTaps, k2 = (k + 2) % kTaps;
+            const int rc1 = (k + 1 >= kTaps) ? rc + 1 : rc;
+            const int rc2 = (k + 2 >= kTaps) ? rc + 1 : rc;
+            const uint32_t so = __builtin_amdgcn_readfirstlane(
+                uint32_t(kAOff + ((s + 1) % kAStages) * kAStage));
+            const char *st = smem + (a_lane + so);
+            uint32_t bn[2][4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                acc[i][0] = Mma<T>::step(fa[i], b[0], acc[i][0]);
+                acc[i][1] = Mma<T>::step(fa[i], b[1], acc[i][1]);
+                fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
+                const int sl = i >> 2, pr = i & 3;
+                bn[sl][pr] = blend_pair<T>(cr[sl], gw[sl][k1], zero, pr);
+                if (pr == 3)
+                    read_corners(cr[sl], sl, k2, rc2 & 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            b[0] = make_uint4(bn[0][0], bn[0][1], bn[0][2], bn[0][3]);
+            b[1] = make_uint4(bn[1][0], bn[1][1], bn[1][2], bn[1][3]);
+            if (s + 1 < steps && (fbw & ((1u << k1) | (1u << (kTaps + k1))))) {
+                fallback(0, k1, c_lo + rc1, b[0]);
+                fallback(1, k1, c_lo + rc1, b[1]);
+            }
+        };
+
+        for (int rc = 0; rc < c_hi - c_lo; ++rc) {
+            step_body(rc, std::integral_constant<int, 0>{});
+            step_body(rc, std::integral_constant<int, 1>{});
+            step_body(rc, std::integral_constant<int, 2>{});
+            step_body(rc, std::integral_constant<int, 3>{});
+            step_body(rc, std::integral_constant<int, 4>{});
+            step_body(rc, std::integral_constant<int, 5>{});
+            step_body(rc, std::integral_constant<int, 6>{});
+            step_body(rc, std::integral_constant<int, 7>{});
+            step_body(rc, std::integral_constant<int, 8>{});
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+
+        // the main loop is over: the tile's state comes back from LDS and
+        // the arguments rather than from registers held across it
+        asm volatile("" ::: "memory");
+        tile = __builtin_amdgcn_readfirstlane(*tile_park);
+        tid = int(threadIdx.x);
+        asm volatile("" : "+v"(tid));
+        a = fresh_args(pa);
+        const Range rg = range_of(a);
+        const TileInfo te = tile_info(a, rg, tile);
+
+        if (te.c_hi < a->nch) {
+            // ---- the tile's first chunks: publish the accumulators as they
+            // are (the layout the next workgroup of the run loads them in),
+            // then the flag once every store is complete
+            const __amdgpu_buffer_rsrc_t rs =
+                srd_b(a->partial + size_t(cta) * 65536, uint32_t(65536 * 4));
+            const uint32_t lo = uint32_t((tid >> 6) * 65536 + (tid & 63) * 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4v f = {acc[i][s][4 * q], acc[i][s][4 * q + 1],
+                                           acc[i][s][4 * q + 2], acc[i][s][4 * q + 3]};
+                        u32x4 u;
+                        __builtin_memcpy(&u, &f, 16);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u, rs, lo + uint32_t(((i * 2 + s) * 4 + q) * 1024), 0, kDevScope);
+                    }
+            // device-scope stores are complete (acknowledged where every XCD
+            // sees them) once the counter drains; only then the flag
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();
+            if (tid == 0)
+                __hip_atomic_store(a->flags + cta, uint32_t(a->epoch), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            // ---- the tile's last chunks: per block of 32 output channels,
+            // through an LDS slice [row][pixel] of fp32 sums, + bias, one
+            // rounding, 16-byte stores of 8 pixels along a tile row.  No load
+            // is issued between the stores (on this GPU a load's wait also
+            // waits for every older store).
+            float *bias_l = reinterpret_cast<float *>(smem + kWoffOff);   // dead copy table
+            {
+                const T *bias = static_cast<const T *>(a->bias);
+                const int m = te.m0 + tid;
+                bias_l[tid] =
+                    (bias && m < a->Mg) ? to_f32(bias[size_t(te.g) * a->Mg + m]) : 0.0f;
+            }
+            __syncthreads();
+            // output planes of the tile's image and group, as a buffer (a
+            // lane with nothing to store gets an out-of-range offset, so
+            // every block issues the same stores with no branches)
+            const int Mg = a->Mg, P = a->P, Ho = a->Ho, Wo = a->Wo;
+            const __amdgpu_buffer_rsrc_t ro =
+                srd_b(static_cast<const T *>(a->out) +
+                          (size_t(te.img) * a->Co + size_t(te.g) * a->Mg) * a->P,
+                      uint32_t(size_t(Mg) * P * sizeof(T)));
+            const bool vec = a->vec_out != 0;
+            float *slice = reinterpret_cast<float *>(smem);
+            // this thread's 4 x 8 sums of a block: row tid/32 + 8*jj, pixels
+            // 8*(tid%32) ..+8
+            const int row0 = tid >> 5, n = (tid & 31) * 8;
+            const int ho = te.ho0 + n / TW, wo = te.wo0 + n % TW;
+            const uint32_t pix_off = uint32_t(ho * Wo + wo) * sizeof(T);   // bytes in a plane
+            // (with vec, Wo and wo are multiples of 8: wo < Wo keeps all 8 inside)
+            const bool pix_ok = ho < Ho && wo < Wo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        slice[(8 * (r >> 2) + 4 * ((tid >> 5) & 1) + (r & 3)) * kEpRow +
+                              (__builtin_amdgcn_readfirstlane(tid >> 6) * 2 + s) * 32 +
+                              (tid & 31)] = acc[i][s][r];
+                lds_barrier();                       // LDS only: stores stay in flight
+                // per-block bases behind an empty asm, so that the per-(i, jj)
+                // LDS addresses become base + immediate instead of 32 hoisted
+                // (and spilled) registers (integer offsets pass through the
+                // asm: a pointer would lose its LDS address space)
+                uint32_t sl_o = uint32_t(row0 * kEpRow + n), bl_o = uint32_t(i * 32 + row0);
+                asm volatile("" : "+v"(sl_o), "+v"(bl_o));
+                const float *sl_b = slice + sl_o;
+                const float *bl_b = bias_l + bl_o;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int row = row0 + 8 * jj;
+                    const float *sp = sl_b + 8 * jj * kEpRow;
+                    const int m = te.m0 + i * 32 + row;
+                    const bool ok = m < Mg && pix_ok;
+                    const float bv = bl_b[8 * jj];
+                    const uint32_t base =
+                        ok ? uint32_t(m) * uint32_t(P) * sizeof(T) + pix_off : kOOB;
+                    if (vec) {
+                        Vec16<T> o;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            o.e[e] = from_f32<T>(sp[e] + bv);
+                        u32x4 ov;
+                        __builtin_memcpy(&ov, &o.raw, 16);
+                        __builtin_amdgcn_raw_buffer_store_b128(ov, ro, base, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const T h = from_f32<T>(sp[e] + bv);
+                            uint16_t hb;
+                            __builtin_memcpy(&hb, &h, 2);
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                hb, ro, (wo + e < Wo) ? base + uint32_t(e) * sizeof(T) : kOOB,
+                                0, 0);
+                        }
+                    }
+                }
+                lds_barrier();
+            }
+        }
+        if (tile <= int(rg.u0 / uint32_t(a->nch)))
+            break;                                   // that was the range's first tile
+        --tile;
     }
+}
+
+// Compute units of the current device (cached per device).
+int cu_count()
+{
+    static std::mutex mu;
+    static std::map<int, int> known;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 1;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = known.find(dev);
+    if (it == known.end()) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        it = known.emplace(dev, n).first;
+    }
+    return it->second;
 }
 
 template <typename T, int TH, int TW, int LEAD>
 hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                       const void *xt, const void *offset, const void *mask, const void *bias,
-                      void *out, hipStream_t s)
+                      void *out, const WindowScratch &ws, hipStream_t s)
 {
     WinArgs a;
     a.Mg = int(p.Mg); a.Kp = int(plan.Kp); a.Co = int(p.Co); a.P = int(p.P);
@@ -561,10 +831,21 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
     a.a_bytes = uint32_t(size_t(p.Mg) * p.Kg * sizeof(T));     // one group's weight
     if (a.WR * a.WC > kWindowPixels || a.WC * 16 + 32 > kWinZero)
         return hipErrorInvalidValue;
-    const uint64_t blocks = uint64_t(p.G) * cnt * a.tiles_y * a.tiles_x * a.tiles_m;
-    if (blocks == 0)
+    const uint64_t tiles = uint64_t(p.G) * cnt * a.tiles_y * a.tiles_x * a.tiles_m;
+    if (tiles == 0)
         return hipSuccess;
-    if (blocks > 0x7fffffffull)
+    if (tiles * uint64_t(a.nch) > 0xffffffffull)
+        return hipErrorInvalidValue;
+    a.tiles = int(tiles);
+    a.epoch = ws.epoch;
+    // One workgroup per CU (at most one tile's worth of units each fewer:
+    // every tile then spans at most two workgroups), and no more than the
+    // workspace has partial-sum slots for.
+    uint64_t blocks = std::min<uint64_t>(
+        {tiles, uint64_t(std::max(1, cu_count())), uint64_t(std::max(1, ws.slots))});
+    if (plan.win_max_ctas > 0)
+        blocks = std::min<uint64_t>(blocks, uint64_t(plan.win_max_ctas));
+    if (ws.epoch <= 0 || (blocks < tiles && (!ws.partial || !ws.flags)))
         return hipErrorInvalidValue;
     auto kern = window_kernel<T, TH, TW, LEAD>;
     constexpr int lds = lds_total(LEAD);
@@ -572,25 +853,27 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
         reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess)
         return attr;
-    hipLaunchKernelGGL(kern, dim3(uint32_t(blocks)), dim3(256), lds, s,
-                       static_cast<const T *>(wpack), static_cast<const T *>(xt),
-                       static_cast<const T *>(offset), static_cast<const T *>(mask),
-                       static_cast<const T *>(bias), static_cast<T *>(out), a);
+    a.A = wpack; a.xt = xt; a.off = offset; a.msk = mask; a.bias = bias; a.out = out;
+    a.partial = ws.partial; a.flags = ws.flags;
+    hipLaunchKernelGGL(kern, dim3(uint32_t(blocks)), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
 template <typename T, int TH, int TW>
 hipError_t window_lead(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                        const void *xt, const void *offset, const void *mask, const void *bias,
-                       void *out, hipStream_t s)
+                       void *out, const WindowScratch &ws, hipStream_t s)
 {
     switch (plan.win_lead) {
     case 3:
-        return window_cfg<T, TH, TW, 3>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return window_cfg<T, TH, TW, 3>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws,
+                                          s);
     case 5:
-        return window_cfg<T, TH, TW, 5>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return window_cfg<T, TH, TW, 5>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws,
+                                          s);
     case 7:
-        return window_cfg<T, TH, TW, 7>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return window_cfg<T, TH, TW, 7>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws,
+                                          s);
     }
     return hipErrorInvalidValue;
 }
@@ -598,15 +881,15 @@ hipError_t window_lead(const Problem &p, const Plan &plan, int64_t cnt, const vo
 template <typename T>
 hipError_t window_t(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                     const void *xt, const void *offset, const void *mask, const void *bias,
-                    void *out, hipStream_t s)
+                    void *out, const WindowScratch &ws, hipStream_t s)
 {
     switch (plan.win_tile) {
     case WindowTile::H16_W16:
-        return window_lead<T, 16, 16>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return window_lead<T, 16, 16>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
     case WindowTile::H8_W32:
-        return window_lead<T, 8, 32>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return window_lead<T, 8, 32>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
     case WindowTile::H32_W8:
-        return window_lead<T, 32, 8>(p, plan, cnt, wpack, xt, offset, mask, bias, out, s);
+        return window_lead<T, 32, 8>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
     }
     return hipErrorInvalidValue;
 }
@@ -615,13 +898,13 @@ hipError_t window_t(const Problem &p, const Plan &plan, int64_t cnt, const void 
 
 hipError_t launch_window(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                          const void *xt, const void *offset, const void *mask, const void *bias,
-                         void *out, hipStream_t stream)
+                         void *out, const WindowScratch &ws, hipStream_t stream)
 {
     switch (p.dtype) {
     case MDCN_F16:
-        return window_t<half_t>(p, plan, cnt, wpack, xt, offset, mask, bias, out, stream);
+        return window_t<half_t>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, stream);
     case MDCN_BF16:
-        return window_t<bf16_t>(p, plan, cnt, wpack, xt, offset, mask, bias, out, stream);
+        return window_t<bf16_t>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, stream);
     case MDCN_F32:
         break;
     }

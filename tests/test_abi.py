@@ -232,7 +232,12 @@ def test_fused_path_plan():
     b, mb = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, DIMS)
     assert b == 256 + 256 * 2304 * 2 + 4 * 256 * 160 * 160 * 2
     assert mb == 256 + 256 * 2304 * 2 + 256 * 160 * 160 * 2
-    assert mdcn.mdcn_workspace_bytes(opw, mdcn.MDCN_F16, DIMS) == (b, mb)
+    # the windowed kernel: the same packed weight and x (in 8-channel blocks),
+    # plus a 256 KiB partial-sum slot and a flag per workgroup (at most 256;
+    # 100 tiles per image)
+    wp, ximg, slot = 256 * 2304 * 2, 256 * 160 * 160 * 2, 256 * 256 * 4
+    assert mdcn.mdcn_workspace_bytes(opw, mdcn.MDCN_F16, DIMS) == (
+        256 + wp + 4 * ximg + 256 * slot + 1024, 256 + wp + ximg + 100 * slot + 512)
     # not eligible: C/group = 36 is not a multiple of 64 -> gather + GEMM
     opg = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_FUSED)
     d = [1, 36, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 8, 36, 3, 3]

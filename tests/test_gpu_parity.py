@@ -470,3 +470,49 @@ def test_window_exact_cases(margin, monkeypatch):
         off[:, 2 * k + 1] = 0.25
     got = run_gpu(pr, dict(inp, offset=off), mdcn.MDCN_PATH_WINDOW)
     assert torch.equal(got, bias.expand_as(got))
+
+
+@pytest.mark.parametrize("ctas", [1, 5, 7, 13])
+@pytest.mark.parametrize("name,dtype", [("window_multi_tile", "f16"), ("window_grouped", "bf16"),
+                                        ("window_far_offsets", "f16")])
+def test_window_split_tiles(ctas, name, dtype, monkeypatch):
+    """Fewer workgroups than tiles (MDCN_WIN_CTAS): the (tile, chunk) units
+    are split evenly, tiles span two workgroups and are combined through the
+    partial-sum slots."""
+    monkeypatch.setenv("MDCN_WIN_CTAS", str(ctas))
+    pr = SMALL[name]
+    print("window split", name, dtype, ctas, flush=True)
+    inp = workloads.generate(pr, dtype, seed=20)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW).double().numpy()
+    ref = oracle_full(pr, inp)
+    ok, err, bound = within_tolerance(got, ref, dtype)
+    assert ok, (ctas, name, dtype, error_report(got, ref))
+
+
+def test_window_split_matches_unsplit(monkeypatch):
+    """Splitting a tile between workgroups only changes the fp32 summation
+    order: the result stays within a few fp16 ulps of the unsplit one."""
+    pr = SMALL["window_multi_tile"]
+    inp = workloads.generate(pr, "f16", seed=22)
+    a = run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW).double()
+    monkeypatch.setenv("MDCN_WIN_CTAS", "11")
+    b = run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW).double()
+    assert float((a - b).abs().max()) <= 2e-3
+
+
+@pytest.mark.parametrize("name", ["ocdnet_n4_c256_160x160", "deep_n16_c512_40x40"])
+def test_window_workload_sampled(name):
+    """Full-size fp16 workloads on the windowed kernel (one workgroup per CU,
+    tiles split between workgroups), sampled outputs against the oracle."""
+    pr, _ = workloads.WORKLOADS[name]
+    print("window workload", name, flush=True)
+    inp = workloads.generate(pr, "f16", seed=0)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW)
+    idx = sample_indices(tuple(got.shape), 4096, seed=12)
+    ref = oracle.forward_points(inp["x"], inp["offset"], inp["mask"], inp["weight"],
+                                inp["bias"], idx, **pr.attrs())
+    g = got.reshape(-1)[torch.from_numpy(idx)].double().numpy()
+    rms = float(got.double().pow(2).mean().sqrt())
+    ok, err, bound = within_tolerance(g, ref, "f16", rms=rms)
+    assert ok, (name, error_report(g, ref), float((err / bound).max()))
+    assert torch.isfinite(got).all()
