@@ -318,12 +318,31 @@ bool window_eligible(const Problem &p)
            img_bytes <= kMaxPerImage && choose_window(p, &t, &m);
 }
 
+// The windowed kernel is the faster of the two MFMA paths when its tiles are
+// nearly full: at least 90% of the padded output pixels x padded output
+// channels of the chosen tiling are real (a 16x16 tile wastes a third of a
+// 40x40 image; fewer than 256 channels per group waste rows of every tile).
+bool window_preferred(const Problem &p)
+{
+    if (!window_eligible(p))
+        return false;
+    WindowTile t;
+    int64_t m, th, tw;
+    choose_window(p, &t, &m);
+    window_tile_dims(t, &th, &tw);
+    const int64_t pad_px = ((p.Ho + th - 1) / th) * th * ((p.Wo + tw - 1) / tw) * tw;
+    const int64_t pad_m = ((p.Mg + 255) / 256) * 256;
+    return 10 * p.Ho * p.Wo * p.Mg >= 9 * pad_px * pad_m;
+}
+
 mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
 {
     switch (a.path) {
     case MDCN_PATH_AUTO:
-        *out = (p.Cg == 1) ? Path::Depthwise
-                           : (fused_eligible(p) ? Path::Fused : Path::GatherGemm);
+        *out = (p.Cg == 1)              ? Path::Depthwise
+               : window_preferred(p)   ? Path::Window
+               : fused_eligible(p)     ? Path::Fused
+                                       : Path::GatherGemm;
         return MDCN_OK;
     case MDCN_PATH_WINDOW:
         if (!window_eligible(p))

@@ -222,11 +222,16 @@ def test_workspace_sizes_and_chunking():
 
 
 def test_fused_path_plan():
-    # automatic choice for the OCDNet-like stage: fused, all 4 images, packed
-    # weight + NHWC x only; the windowed kernel uses the same workspace
-    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    # automatic choice for the OCDNet-like stage: the windowed kernel (its
+    # 16x16 tiles cover 160x160 exactly and all 256 output channels);
+    # the fused kernel takes all 4 images, packed weight + NHWC x only
+    auto = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, DIMS).startswith("path=window")
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_FUSED)
     desc = mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, DIMS)
     assert desc.startswith("path=fused") and "chunk=4" in desc
+    # f32 is not windowed: the automatic choice is the fused kernel
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F32, DIMS).startswith("path=fused")
     opw = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_WINDOW)
     assert mdcn.mdcn_describe_plan(opw, mdcn.MDCN_F16, DIMS).startswith("path=window")
     b, mb = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, DIMS)
@@ -238,13 +243,22 @@ def test_fused_path_plan():
     wp, ximg, slot = 256 * 2304 * 2, 256 * 160 * 160 * 2, 256 * 256 * 4
     assert mdcn.mdcn_workspace_bytes(opw, mdcn.MDCN_F16, DIMS) == (
         256 + wp + 4 * ximg + 256 * slot + 1024, 256 + wp + ximg + 100 * slot + 512)
+    assert mdcn.mdcn_workspace_bytes(auto, mdcn.MDCN_F16, DIMS) == \
+        mdcn.mdcn_workspace_bytes(opw, mdcn.MDCN_F16, DIMS)
+    # tiles that are not nearly full keep the fused kernel: 40x40 in 16x16
+    # tiles (69% of the pixels), or 128 output channels in 256-row tiles
+    d40 = [16, 512, 40, 40, 16, 18, 40, 40, 16, 9, 40, 40, 512, 512, 3, 3]
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, d40).startswith("path=fused")
+    assert mdcn.mdcn_describe_plan(opw, mdcn.MDCN_F16, d40).startswith("path=window")
+    d128 = [4, 256, 160, 160, 4, 18, 160, 160, 4, 9, 160, 160, 128, 256, 3, 3]
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, d128).startswith("path=fused")
     # not eligible: C/group = 36 is not a multiple of 64 -> gather + GEMM
     opg = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_FUSED)
     d = [1, 36, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 8, 36, 3, 3]
     with pytest.raises(mdcn.MdcnError) as e:
         mdcn.mdcn_workspace_bytes(opg, mdcn.MDCN_F16, d)
     assert e.value.status == mdcn.MDCN_E_PATH
-    assert mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, d).startswith("path=gather_gemm")
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, d).startswith("path=gather_gemm")
 
 
 def _fused_dims(n, c, h, w, co, k, dg, g):
