@@ -744,13 +744,24 @@ void window_kernel(WinArgs args)
                 asm volatile("" : "+v"(sl_o), "+v"(bl_o));
                 const float *sl_b = slice + sl_o;
                 const float *bl_b = bias_l + bl_o;
+                // all of the block's LDS reads first (16-byte reads: a slice
+                // row is 1040 bytes and n a multiple of 8), then one wait
+                float4v sv[4][2];
+                float bvv[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    sv[jj][0] = *reinterpret_cast<const float4v *>(sl_b + 8 * jj * kEpRow);
+                    sv[jj][1] = *reinterpret_cast<const float4v *>(sl_b + 8 * jj * kEpRow + 4);
+                    bvv[jj] = bl_b[8 * jj];
+                }
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int row = row0 + 8 * jj;
-                    const float *sp = sl_b + 8 * jj * kEpRow;
+                    const float sp[8] = {sv[jj][0][0], sv[jj][0][1], sv[jj][0][2], sv[jj][0][3],
+                                         sv[jj][1][0], sv[jj][1][1], sv[jj][1][2], sv[jj][1][3]};
                     const int m = te.m0 + i * 32 + row;
                     const bool ok = m < Mg && pix_ok;
-                    const float bv = bl_b[8 * jj];
+                    const float bv = bvv[jj];
                     const uint32_t base =
                         ok ? uint32_t(m) * uint32_t(P) * sizeof(T) + pix_off : kOOB;
                     if (vec) {
