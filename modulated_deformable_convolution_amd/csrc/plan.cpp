@@ -309,6 +309,60 @@ int64_t window_tiles_per_image(const Problem &p, WindowTile t)
     return p.G * ((p.Ho + th - 1) / th) * ((p.Wo + tw - 1) / tw) * ((p.Mg + 255) / 256);
 }
 
+namespace {
+
+// Greedy fill of one run's units [0, U) (nch per tile) into `per` ranges of
+// cost <= T, cost = 4 x chunks + seg_x4 x tiles touched; returns the number of
+// units placed (U when T is feasible).  ends[k] receives each range's end.
+int64_t split_fill(int64_t U, int64_t nch, int64_t per, int64_t seg_x4, int64_t T,
+                   int64_t *ends)
+{
+    int64_t pos = 0;
+    for (int64_t k = 0; k < per; ++k) {
+        const int64_t start = pos;
+        while (pos < U) {
+            const int64_t touched = pos / nch - start / nch + 1;
+            if (4 * (pos + 1 - start) + seg_x4 * touched > T)
+                break;
+            ++pos;
+        }
+        if (ends)
+            ends[k] = pos;
+    }
+    return pos;
+}
+
+}  // namespace
+
+bool window_split(int64_t tiles, int64_t nch, int64_t ncta, int64_t seg_cost_x4,
+                  uint32_t *bounds)
+{
+    if (tiles <= 0 || nch <= 0 || ncta <= 0 || ncta > kWindowSlots || seg_cost_x4 < 0 ||
+        tiles * nch > int64_t(0xffffffffll))
+        return false;
+    const int64_t ngrp = (ncta % 8 == 0 && tiles >= ncta) ? 8 : 1;
+    const int64_t per = ncta / ngrp;
+    int64_t ends[kWindowSlots];
+    for (int64_t grp = 0; grp < ngrp; ++grp) {
+        const int64_t tg0 = grp * tiles / ngrp, tg1 = (grp + 1) * tiles / ngrp;
+        const int64_t U = (tg1 - tg0) * nch;
+        // smallest feasible bound on the per-range cost
+        int64_t lo = 0, hi = 4 * U + seg_cost_x4 * (tg1 - tg0);
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (split_fill(U, nch, per, seg_cost_x4, mid, nullptr) >= U)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        split_fill(U, nch, per, seg_cost_x4, lo, ends);
+        for (int64_t k = 0; k < per; ++k)
+            bounds[grp * per + k] = uint32_t(tg0 * nch + (k ? ends[k - 1] : 0));
+    }
+    bounds[ncta] = uint32_t(tiles * nch);
+    return true;
+}
+
 bool window_eligible(const Problem &p)
 {
     const int64_t img_bytes = p.C * p.H * p.W * int64_t(p.elem);
@@ -435,6 +489,14 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
                 const int v = std::atoi(env);
                 if (v > 0)
                     plan.win_max_ctas = v;
+            }
+            // a tile a workgroup touches costs about 3 chunks of main loop
+            // (its prologue and epilogue), in quarter chunks
+            plan.win_seg_cost_x4 = 12;
+            if (const char *env = std::getenv("MDCN_WIN_SEG_X4")) {
+                const int v = std::atoi(env);
+                if (v >= 0 && v <= 1024)
+                    plan.win_seg_cost_x4 = v;
             }
             // Partial-sum slots and flags for the chunk's tiles (one slot per
             // workgroup, at most kWindowSlots); with a given workspace, the

@@ -96,6 +96,7 @@ struct Plan {
     int64_t win_tiles_per_image; // window: output tiles (256 x 256) of one image, all groups
     int64_t win_slots;           // window: partial-sum slots
     int64_t win_max_ctas;        // window: cap on the workgroups (0: none; tuning and tests)
+    int64_t win_seg_cost_x4;     // window: cost of one tile segment, quarter chunks
     size_t part_off, flag_off;   // window: offsets of the partial sums and the flags
 };
 
@@ -136,6 +137,17 @@ bool window_eligible(const Problem &p);
 bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin);
 // Output tiles of one image (all groups) for a window tile shape.
 int64_t window_tiles_per_image(const Problem &p, WindowTile t);
+
+// Split the windowed kernel's (tile, chunk) units over `ncta` workgroups
+// (ncta <= kWindowSlots): bounds[j]..bounds[j+1] is the range of workgroup
+// slot j, slots ordered run by run (the tiles are first cut into 8 runs of
+// whole tiles, one per XCD, when ncta is a multiple of 8 and tiles >= ncta).
+// Within a run the ranges are contiguous and chosen to even out
+// chunks + seg_cost x (tiles touched): each tile a workgroup touches costs a
+// prologue and an epilogue.  Empty ranges only come last in a run.  Returns
+// false when the sizes do not fit (more than 2^32 units).
+bool window_split(int64_t tiles, int64_t nch, int64_t ncta, int64_t seg_cost_x4,
+                  uint32_t *bounds);
 mdcn_status check_attrs(const int32_t stride[2], const int32_t padding[2],
                         const int32_t dilation[2], int32_t group, int32_t dgroup);
 mdcn_status derive_problem(const Attrs &a, mdcn_dtype dtype, const int64_t dims[16],

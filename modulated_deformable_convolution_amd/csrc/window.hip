@@ -103,7 +103,10 @@ struct WinArgs {
     int offC, mskC, Cdg;           // offset / mask channels per image; C / deformable_group
     int has_bias, vec_out;
     uint32_t img_bytes, chunk_bytes, a_bytes;
+    // unit range of each workgroup slot (slot j = run * per + index in run)
+    uint32_t bounds[kWindowSlots + 1];
 };
+static_assert(sizeof(WinArgs) <= 4096, "kernel arguments are at most 4 KiB");
 
 // The kernel's only argument, read through a pointer into the kernarg
 // segment that the compiler cannot see through at each use site: every
@@ -265,15 +268,13 @@ void window_kernel(WinArgs args)
         uint32_t u0, u1, prev;
     };
     auto range_of = [&](KArgs a) {
-        const uint32_t ncta = gridDim.x, nch = uint32_t(a->nch), tiles = uint32_t(a->tiles);
+        const uint32_t ncta = gridDim.x, tiles = uint32_t(a->tiles);
         const uint32_t ngrp = (ncta % 8u == 0u && tiles >= ncta) ? 8u : 1u;
         const uint32_t grp = cta % ngrp, per = ncta / ngrp, idx = cta / ngrp;
-        const uint32_t tg0 = uint32_t((uint64_t(grp) * tiles) / ngrp);
-        const uint32_t tg1 = uint32_t((uint64_t(grp + 1) * tiles) / ngrp);
-        const uint32_t U = (tg1 - tg0) * nch;
+        const uint32_t j = grp * per + idx;
         Range r;
-        r.u0 = tg0 * nch + uint32_t((uint64_t(idx) * U) / per);
-        r.u1 = tg0 * nch + uint32_t((uint64_t(idx + 1) * U) / per);
+        r.u0 = a->bounds[j];
+        r.u1 = a->bounds[j + 1];
         r.prev = cta - ngrp;
         return r;
     };
@@ -341,12 +342,16 @@ void window_kernel(WinArgs args)
 
         // ---- per-lane DMA source offsets of the window (kept in LDS; each
         // thread reads back only its own entries) and of the A rows
+        const float inv_wc = 1.0f / float(a->WC);
 #pragma unroll
         for (int t = 0; t < kWinInstr; ++t) {
             const int S = (t * 4 + wave) * 64 + lane;          // 16-byte slot of the buffer
-            const int pl = S / kWindowPixels;
+            const int pl = S >= kWindowPixels ? 1 : 0;       // S < 2 * kWindowPixels
             const int px = S - pl * kWindowPixels;
-            const int r = px / a->WC, c = px - (px / a->WC) * a->WC;
+            // px / WC through a float reciprocal: px < 1280 and WC <= 64, so
+            // px/WC is at least 1/128 away from the next integer, far above
+            // the float error (the plane of slot S is S / 1280 likewise)
+            const int r = int((float(px) + 0.5f) * inv_wc), c = px - r * a->WC;
             const int gr = r0 + r, gc = c0 + c;
             const bool ok = px < a->WR * a->WC && (unsigned)gr < (unsigned)a->H &&
                             (unsigned)gc < (unsigned)a->W;
@@ -449,7 +454,6 @@ void window_kernel(WinArgs args)
                                       : uint32_t(kWinZeroOff);
                     fbl |= uint32_t(any && !inw) << (s * kTaps + k);
                 }
-                __builtin_amdgcn_sched_barrier(0);    // one slab's loads in flight at a time
             }
         }
         // wave-level: which (slab, tap) has a lane that needs the fallback
@@ -793,6 +797,25 @@ void window_kernel(WinArgs args)
     }
 }
 
+// window_split for the last sizes asked (the same for every forward of one
+// problem), behind a lock.
+bool split_cached(int64_t tiles, int64_t nch, int64_t ncta, int64_t seg_x4, uint32_t *bounds)
+{
+    static std::mutex mu;
+    static int64_t key[4] = {-1, -1, -1, -1};
+    static uint32_t cached[kWindowSlots + 1];
+    std::lock_guard<std::mutex> lock(mu);
+    if (key[0] != tiles || key[1] != nch || key[2] != ncta || key[3] != seg_x4) {
+        if (!window_split(tiles, nch, ncta, seg_x4, cached)) {
+            key[0] = -1;
+            return false;
+        }
+        key[0] = tiles; key[1] = nch; key[2] = ncta; key[3] = seg_x4;
+    }
+    std::copy(cached, cached + ncta + 1, bounds);
+    return true;
+}
+
 // Compute units of the current device (cached per device).
 int cu_count()
 {
@@ -857,6 +880,9 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
     if (plan.win_max_ctas > 0)
         blocks = std::min<uint64_t>(blocks, uint64_t(plan.win_max_ctas));
     if (ws.epoch <= 0 || (blocks < tiles && (!ws.partial || !ws.flags)))
+        return hipErrorInvalidValue;
+    if (!split_cached(int64_t(tiles), int64_t(a.nch), int64_t(blocks), plan.win_seg_cost_x4,
+                      a.bounds))
         return hipErrorInvalidValue;
     auto kern = window_kernel<T, TH, TW, LEAD>;
     constexpr int lds = lds_total(LEAD);
