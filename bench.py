@@ -137,6 +137,9 @@ def main(argv=None) -> int:
     ap.add_argument("--path", default="auto", choices=["auto", "gather_gemm", "fused",
                                                        "window", "depthwise"],
                     help="computation path (default: the library's choice)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph that holds one captured forward (the "
+                         "launch mode for small problems) instead of eager forwards")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte device buffer --steps times (a plain copy "
                          "of known size, to scale memory-traffic counters) and exit")
@@ -198,9 +201,23 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    timed = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"],
+                             out=out, workspace=ws)
+        stream.wait_stream(side)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        timed = graph.replay
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        timed()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -286,7 +303,8 @@ def main(argv=None) -> int:
                    "padding": list(pr.padding), "dilation": list(pr.dilation),
                    "group": pr.groups, "deformable_group": pr.deformable_groups,
                    "bias": pr.bias, "io_dtype": dtype, "accumulate": "f32",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "launch": "graph replay" if args.graph else "eager"},
         "hbm_gbs_effective": round(min_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "plan": plan,
         "roofline": roofline,
