@@ -64,8 +64,9 @@ enum class WindowTile : int {
     H16_W16 = 0,
     H8_W32 = 1,
     H32_W8 = 2,
+    FLAT = 3,        // 256 consecutive output pixels in raster order (narrow images)
 };
-constexpr int kWindowTileCount = 3;
+constexpr int kWindowTileCount = 4;
 constexpr int kWindowPixels = 1280;      // input positions one LDS window can hold
 constexpr int kWindowZeroBytes = 1024;   // zeroed LDS after each window (>= 16*columns + 32)
 constexpr int64_t kWindowMaxMargin = 8;  // default offset margin around the anchors
@@ -137,6 +138,8 @@ bool window_eligible(const Problem &p);
 bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin);
 // Output tiles of one image (all groups) for a window tile shape.
 int64_t window_tiles_per_image(const Problem &p, WindowTile t);
+// Output rows a flat tile (256 consecutive pixels of rows Wo wide) can span.
+int64_t window_flat_rows(int64_t Wo);
 
 // Split the windowed kernel's (tile, chunk) units over `ncta` workgroups
 // (ncta <= kWindowSlots): bounds[j]..bounds[j+1] is the range of workgroup

@@ -232,6 +232,20 @@ void window_kernel(WinArgs args)
     const KArgs pa = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
     KArgs a = fresh_args(pa);
     static_assert(TH * TW == 256 && TW % 8 == 0, "a tile is 256 pixels, rows of 8-pixel vectors");
+    // TH = 1: a flat tile, 256 consecutive output pixels in raster order
+    // (ho0 holds its first pixel's index, wo0 is 0)
+    constexpr bool kFlat = TH == 1;
+    // output pixel (ho, wo) of the tile's pixel n
+    auto out_pixel = [](int n, int ho0, int wo0, int Wo, int &ho, int &wo) {
+        if constexpr (kFlat) {
+            const int pp = ho0 + n;
+            ho = pp / Wo;
+            wo = pp - ho * Wo;
+        } else {
+            ho = ho0 + n / TW;
+            wo = wo0 + n % TW;
+        }
+    };
     static_assert(LEAD >= 2 && LEAD + 1 <= 9, "copies lead by 2..8 steps");
     constexpr int kAStages = LEAD + 1;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -292,7 +306,7 @@ void window_kernel(WinArgs args)
         bid /= uint32_t(a->tiles_m);
         ti.wo0 = int(bid % uint32_t(a->tiles_x)) * TW;
         bid /= uint32_t(a->tiles_x);
-        ti.ho0 = int(bid % uint32_t(a->tiles_y)) * TH;
+        ti.ho0 = int(bid % uint32_t(a->tiles_y)) * (kFlat ? 256 : TH);
         bid /= uint32_t(a->tiles_y);
         ti.img = int(bid % uint32_t(a->cnt));
         ti.g = int(bid / uint32_t(a->cnt));
@@ -332,7 +346,8 @@ void window_kernel(WinArgs args)
         const int c_lo = ti.c_lo, c_hi = ti.c_hi;
         const int m0 = ti.m0, ho0 = ti.ho0, wo0 = ti.wo0, img = ti.img;
         const int g = __builtin_amdgcn_readfirstlane(ti.g);
-        const int r0 = ho0 * a->sh - a->ph - a->margin;  // window origin (input coordinates)
+        // window origin (input coordinates)
+        const int r0 = (kFlat ? ho0 / a->Wo : ho0) * a->sh - a->ph - a->margin;
         const int c0 = wo0 * a->sw - a->pw - a->margin;
         const int q = (g * a->Cg) / a->Cdg;              // the group's offset group
         const v4i ra =
@@ -414,7 +429,8 @@ void window_kernel(WinArgs args)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int n = (wave * 2 + s) * 32 + (lane & 31);
-                const int ho = ho0 + n / TW, wo = wo0 + n % TW;
+                int ho, wo;
+                out_pixel(n, ho0, wo0, a->Wo, ho, wo);
                 const bool pv = ho < a->Ho && wo < a->Wo;
                 const int pix = pv ? ho * a->Wo + wo : 0;
                 const size_t ob = (size_t(img) * a->offC + size_t(q) * 2 * kTaps) * P + pix;
@@ -471,7 +487,8 @@ void window_kernel(WinArgs args)
                 const T *offp = static_cast<const T *>(a->off);
                 const T *mskp = static_cast<const T *>(a->msk);
                 const int n = (wave * 2 + s) * 32 + (lane & 31);
-                const int ho = ho0 + n / TW, wo = wo0 + n % TW;
+                int ho, wo;
+                out_pixel(n, ho0, wo0, a->Wo, ho, wo);
                 const int pix = ho * a->Wo + wo;
                 const size_t ob =
                     (size_t(img) * a->offC + size_t(q) * 2 * kTaps + 2 * k) * a->P + pix;
@@ -726,7 +743,8 @@ void window_kernel(WinArgs args)
             // this thread's 4 x 8 sums of a block: row tid/32 + 8*jj, pixels
             // 8*(tid%32) ..+8
             const int row0 = tid >> 5, n = (tid & 31) * 8;
-            const int ho = te.ho0 + n / TW, wo = te.wo0 + n % TW;
+            int ho, wo;
+            out_pixel(n, te.ho0, te.wo0, Wo, ho, wo);
             const uint32_t pix_off = uint32_t(ho * Wo + wo) * sizeof(T);   // bytes in a plane
             // (with vec, Wo and wo are multiples of 8: wo < Wo keeps all 8 inside)
             const bool pix_ok = ho < Ho && wo < Wo;
@@ -783,7 +801,10 @@ void window_kernel(WinArgs args)
                             uint16_t hb;
                             __builtin_memcpy(&hb, &h, 2);
                             __builtin_amdgcn_raw_buffer_store_b16(
-                                hb, ro, (wo + e < Wo) ? base + uint32_t(e) * sizeof(T) : kOOB,
+                                hb, ro,
+                                (kFlat ? ho * Wo + wo + e < Ho * Wo : wo + e < Wo)
+                                    ? base + uint32_t(e) * sizeof(T)
+                                    : kOOB,
                                 0, 0);
                         }
                     }
@@ -849,17 +870,22 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
     a.sh = int(p.sh); a.sw = int(p.sw); a.ph = int(p.ph); a.pw = int(p.pw);
     a.dh = int(p.dh); a.dw = int(p.dw);
     a.margin = int(plan.win_margin);
-    a.WR = int(window_extent(TH, p.sh, p.kh, p.dh, plan.win_margin));
-    a.WC = int(window_extent(TW, p.sw, p.kw, p.dw, plan.win_margin));
-    a.tiles_y = int((p.Ho + TH - 1) / TH);
-    a.tiles_x = int((p.Wo + TW - 1) / TW);
+    constexpr bool flat = TH == 1;
+    a.WR = int(window_extent(flat ? window_flat_rows(p.Wo) : TH, p.sh, p.kh, p.dh,
+                             plan.win_margin));
+    a.WC = int(window_extent(flat ? p.Wo : TW, p.sw, p.kw, p.dw, plan.win_margin));
+    a.tiles_y = int(flat ? (p.P + 255) / 256 : (p.Ho + TH - 1) / TH);
+    a.tiles_x = int(flat ? 1 : (p.Wo + TW - 1) / TW);
     a.tiles_m = int((p.Mg + 255) / 256);
     a.cnt = int(cnt);
     a.offC = int(2 * p.DG * p.K);
     a.mskC = int(p.DG * p.K);
     a.Cdg = int(p.Cdg);
     a.has_bias = bias != nullptr;
-    a.vec_out = (p.Wo % 8 == 0) && reinterpret_cast<uintptr_t>(out) % 16 == 0;
+    // 8-pixel vectors stay inside the image: rows of a multiple of 8 pixels,
+    // or (flat tiles, where a vector may run on into the next row) planes of
+    // a multiple of 8 pixels
+    a.vec_out = ((flat ? p.P : p.Wo) % 8 == 0) && reinterpret_cast<uintptr_t>(out) % 16 == 0;
     a.img_bytes = uint32_t(size_t(p.H) * p.W * p.C * sizeof(T));
     a.chunk_bytes = uint32_t(size_t(cnt) * a.img_bytes);
     a.a_bytes = uint32_t(size_t(p.Mg) * p.Kg * sizeof(T));     // one group's weight
@@ -927,6 +953,8 @@ hipError_t window_t(const Problem &p, const Plan &plan, int64_t cnt, const void 
         return window_lead<T, 8, 32>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
     case WindowTile::H32_W8:
         return window_lead<T, 32, 8>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
+    case WindowTile::FLAT:
+        return window_lead<T, 1, 256>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
     }
     return hipErrorInvalidValue;
 }

@@ -245,11 +245,14 @@ def test_fused_path_plan():
         256 + wp + 4 * ximg + 256 * slot + 1024, 256 + wp + ximg + 100 * slot + 512)
     assert mdcn.mdcn_workspace_bytes(auto, mdcn.MDCN_F16, DIMS) == \
         mdcn.mdcn_workspace_bytes(opw, mdcn.MDCN_F16, DIMS)
-    # tiles that are not nearly full keep the fused kernel: 40x40 in 16x16
-    # tiles (69% of the pixels), or 128 output channels in 256-row tiles
+    # 40x40 in flat tiles: 1600 of 1792 pixels (89%) -> windowed; tiles that
+    # are not nearly full keep the fused kernel: 13x21 (273 of 512 pixels),
+    # or 128 output channels in 256-row tiles
     d40 = [16, 512, 40, 40, 16, 18, 40, 40, 16, 9, 40, 40, 512, 512, 3, 3]
-    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, d40).startswith("path=fused")
-    assert mdcn.mdcn_describe_plan(opw, mdcn.MDCN_F16, d40).startswith("path=window")
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, d40).startswith("path=window")
+    d13 = [2, 256, 13, 21, 2, 18, 13, 21, 2, 9, 13, 21, 256, 256, 3, 3]
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, d13).startswith("path=fused")
+    assert mdcn.mdcn_describe_plan(opw, mdcn.MDCN_F16, d13).startswith("path=window")
     d128 = [4, 256, 160, 160, 4, 18, 160, 160, 4, 9, 160, 160, 128, 256, 3, 3]
     assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, d128).startswith("path=fused")
     # not eligible: C/group = 36 is not a multiple of 64 -> gather + GEMM
@@ -360,8 +363,23 @@ def test_window_path_plan():
     # tall and narrow (64 x 8): 32 x 8 tiles
     d, tile, margin = _win_desc(op, mdcn.MDCN_BF16, _fused_dims(1, 32, 64, 8, 64, 3, 1, 1))
     assert tile == 2 and margin >= 2
-    # 9 x 70: 16 x 16 tiles (16 x 80 padded pixels) pad least
+    # 9 x 70: 16 x 16 tiles (16 x 80 padded pixels) pad least; a flat tile's
+    # window would need 70 + 2 + 2 + 2m columns (at most 62 fit a row of the
+    # zero area)
     assert _win_desc(op, mdcn.MDCN_BF16, _fused_dims(1, 32, 9, 70, 64, 3, 1, 1))[1] == 0
+    # narrow images: flat tiles (256 consecutive pixels in raster order).
+    # 40 x 40: 7 flat tiles pad 1600 to 1792 pixels (16 x 16 tiles: 2304);
+    # a run of 256 pixels spans up to 8 rows, so the window is
+    # (8 - 1 + 2 + 2 + 2m) x (40 - 1 + 2 + 2 + 2m) <= 1280: margin 6
+    d40 = [16, 512, 40, 40, 16, 18, 40, 40, 16, 9, 40, 40, 512, 512, 3, 3]
+    d, tile, margin = _win_desc(op, mdcn.MDCN_F16, d40)
+    assert tile == 3 and margin == 6
+    # 37 x 37: 1369 pixels in 6 flat tiles (1536) against 2304 in 16 x 16 tiles
+    d, tile, margin = _win_desc(op, mdcn.MDCN_F16, _fused_dims(2, 32, 37, 37, 288, 3, 1, 1))
+    assert tile == 3 and margin == 6
+    # 64 x 8: flat tiles pad as little as 32 x 8 ones, with the same margin:
+    # the first listed tile stays
+    assert _win_desc(op, mdcn.MDCN_BF16, _fused_dims(1, 32, 64, 8, 64, 3, 1, 1))[1] == 2
     # stride (2, 1): a 16 x 16 tile's window spans 30 + 2 + 2 + 2m rows and
     # 15 + 2 + 2 + 2m columns, at most 1280 positions: margin 5; with stride
     # and dilation 2 no tile fits

@@ -85,6 +85,10 @@ SMALL = {
     "window_far_offsets": Problem(N=1, C=16, Co=32, H=30, W=30,
                                   offset_dist=("uniform", 20.0),
                                   mask_dist=("uniform_zeros", 0.1)),
+    # 13 x 21 = 273 output pixels: flat tiles (MDCN_WIN_TILE=3) wrap rows,
+    # the last one is ragged, and a plane is not a multiple of 8 pixels
+    # (element stores)
+    "window_flat_ragged": Problem(N=2, C=32, Co=64, H=13, W=21, offset_dist=("normal", 2.0)),
     # also eligible for the fused kernel (C/group = 64)
     "window_fused_cmp": Problem(N=2, C=64, Co=128, H=21, W=21, offset_dist=("normal", 2.0)),
 }
@@ -414,10 +418,11 @@ def test_fused_matches_gather_gemm_closely():
 
 # ---------------------------------------------------------------- windowed fused kernel
 
-@pytest.mark.parametrize("tile", range(3))
+@pytest.mark.parametrize("tile", range(4))
 @pytest.mark.parametrize("margin", [2, 8])
 @pytest.mark.parametrize("name,dtype", [("window_multi_tile", "f16"), ("window_grouped", "bf16"),
-                                        ("window_far_offsets", "f16")])
+                                        ("window_far_offsets", "f16"),
+                                        ("window_flat_ragged", "f16")])
 def test_every_window_tile(tile, margin, name, dtype, monkeypatch):
     """Each tile shape (MDCN_WIN_TILE) with a narrow (many samples through
     the fallback) and the default margin (MDCN_WIN_MARGIN); a tile whose
@@ -477,8 +482,8 @@ def test_window_exact_cases(margin, monkeypatch):
                                         ("window_far_offsets", "f16")])
 def test_window_split_tiles(ctas, name, dtype, monkeypatch):
     """Fewer workgroups than tiles (MDCN_WIN_CTAS): the (tile, chunk) units
-    are split evenly, tiles span two workgroups and are combined through the
-    partial-sum slots."""
+    are split into contiguous ranges, tiles span two workgroups and are
+    combined through the partial-sum slots."""
     monkeypatch.setenv("MDCN_WIN_CTAS", str(ctas))
     pr = SMALL[name]
     print("window split", name, dtype, ctas, flush=True)
