@@ -97,6 +97,11 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
             return dict(bytes=2 * w_bytes, flops=0)
         if name in ("to_nhwc", "to_channel_blocks"):
             return dict(bytes=2 * cnt * x_img, flops=0)
+        if name in ("prep_nhwc", "prep_blocks"):
+            # the weight repacked and the first chunk's x moved, in one launch
+            first = min(plan_chunk, pr.N)
+            wb = w_bytes + pr.Co * Kp * e if name == "prep_nhwc" else 2 * w_bytes
+            return dict(bytes=wb + 2 * first * x_img, flops=0)
         if name == "deform_gather":
             # x read once, offsets and masks read once, columns written once
             return dict(bytes=cnt * (x_img + off_img + msk_img + col_img),

@@ -194,9 +194,13 @@ mdcn_status mdcn_trace_count(const mdcn_trace *trace, int32_t *count);
  * MDCN_E_LAUNCH. */
 mdcn_status mdcn_trace_read(mdcn_trace *trace, int32_t i, int32_t *kernel_id, float *ms);
 
-/* Name of a kernel id ("pack_weight", "to_nhwc", "deform_gather",
- * "gemm_bias", "depthwise_direct", "fused_gather_gemm", "depthwise_geometry");
- * "?" if unknown. */
+/* Name of a kernel id: "prep_nhwc" / "prep_blocks" (the weight repacked and
+ * the first chunk of x to channels-last / 8-channel blocks, in one launch),
+ * "to_nhwc" / "to_channel_blocks" (x of a later chunk), "deform_gather",
+ * "gemm_bias", "fused_gather_gemm", "window_gather_gemm",
+ * "depthwise_geometry", "depthwise_direct"; "pack_weight" and
+ * "pack_weight_steps" (standalone weight repacking) are not launched by the
+ * forward.  "?" if unknown. */
 const char *mdcn_kernel_name(int32_t kernel_id);
 
 /* ---- misc ---------------------------------------------------------------- */

@@ -180,23 +180,21 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     void *xt = ws + plan.xt_off;
     void *col = ws + plan.col_off;
     uint32_t *win_flags = reinterpret_cast<uint32_t *>(ws + plan.flag_off);
-    if (plan.path == Path::Window)
-        err = rec.run(mdcn::K_PACK_WEIGHT_STEPS, [&] {
-            return mdcn::launch_pack_weight_steps(p, weight, wpack, win_flags,
-                                                  int(plan.win_slots), stream);
-        });
-    else
-        err = rec.run(mdcn::K_PACK_WEIGHT,
-                      [&] { return mdcn::launch_pack_weight(p, plan, weight, wpack, stream); });
-    if (err != hipSuccess)
-        return MDCN_E_LAUNCH;
+    // The weight is repacked (and the window path's flags cleared) in the
+    // same launch as the first chunk's x layout change.
     for (int64_t n0 = 0; n0 < p.N; n0 += plan.chunk) {
         const int64_t cnt = std::min<int64_t>(plan.chunk, p.N - n0);
         const char *xc = static_cast<const char *>(x) + size_t(n0) * x_img;
         const char *oc = static_cast<const char *>(offset) + size_t(n0) * off_img;
         const char *mc = static_cast<const char *>(mask) + size_t(n0) * msk_img;
         char *outc = static_cast<char *>(out) + size_t(n0) * out_img;
-        if (plan.path == Path::Window)
+        if (n0 == 0)
+            err = rec.run(plan.path == Path::Window ? mdcn::K_PREP_BLOCKS : mdcn::K_PREP_NHWC,
+                          [&] {
+                              return mdcn::launch_prep(p, plan, cnt, xc, xt, weight, wpack,
+                                                       win_flags, int(plan.win_slots), stream);
+                          });
+        else if (plan.path == Path::Window)
             err = rec.run(mdcn::K_TO_BLOCKS,
                           [&] { return mdcn::launch_to_channel_blocks(p, cnt, xc, xt, stream); });
         else
@@ -449,6 +447,8 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_WINDOW: return "window_gather_gemm";
     case mdcn::K_PACK_WEIGHT_STEPS: return "pack_weight_steps";
     case mdcn::K_TO_BLOCKS: return "to_channel_blocks";
+    case mdcn::K_PREP_NHWC: return "prep_nhwc";
+    case mdcn::K_PREP_BLOCKS: return "prep_blocks";
     }
     return "?";
 }

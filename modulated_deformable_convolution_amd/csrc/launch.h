@@ -20,7 +20,9 @@ enum KernelId : int32_t {
     K_WINDOW = 7,
     K_PACK_WEIGHT_STEPS = 8,
     K_TO_BLOCKS = 9,
-    K_COUNT = 10
+    K_PREP_NHWC = 10,
+    K_PREP_BLOCKS = 11,
+    K_COUNT = 12
 };
 
 // weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
@@ -38,6 +40,13 @@ hipError_t launch_pack_weight_steps(const Problem &p, const void *weight, void *
 // x [cnt][C][H][W] -> xb [cnt][C/8][H][W][8] (8-channel blocks; C % 8 == 0).
 hipError_t launch_to_channel_blocks(const Problem &p, int64_t cnt, const void *x, void *xb,
                                     hipStream_t stream);
+
+// The first chunk's set-up in one launch: x of cnt images to channels-last
+// (window path: to 8-channel blocks) and the weight repacked for the plan's
+// path (window path: step-major, with nflags flags cleared).
+hipError_t launch_prep(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
+                       const void *weight, void *wpack, uint32_t *flags, int nflags,
+                       hipStream_t stream);
 
 // x [cnt][C][H][W] -> xt [cnt][H][W][C] (channels innermost).
 hipError_t launch_to_nhwc(const Problem &p, int64_t cnt, const void *x, void *xt,

@@ -20,15 +20,16 @@ __device__ __forceinline__ size_t dst_index(int c, int p, int C, int HW)
     return BLK ? (size_t(c >> 3) * HW + p) * 8 + (c & 7) : size_t(p) * C + c;
 }
 
-// One 64 (channels) x 64 (pixels) tile through LDS per workgroup.
+// One 64 (channels) x 64 (pixels) tile through LDS per workgroup: tile
+// (bx, by) of image bz.
 template <typename T, bool BLK>
-__global__ __launch_bounds__(256) void to_nhwc_kernel(const T *__restrict__ x, T *__restrict__ xt,
-                                                      int C, int HW)
+__device__ __forceinline__ void transpose_tile(const T *__restrict__ x, T *__restrict__ xt,
+                                               int C, int HW, int bx, int by, int bz,
+                                               T (*tile)[kTile + 1])
 {
-    __shared__ T tile[kTile][kTile + 1];
-    const int p0 = blockIdx.x * kTile;
-    const int c0 = blockIdx.y * kTile;
-    const size_t img = size_t(blockIdx.z) * size_t(C) * size_t(HW);
+    const int p0 = bx * kTile;
+    const int c0 = by * kTile;
+    const size_t img = size_t(bz) * size_t(C) * size_t(HW);
     const int tx = threadIdx.x % kTile;
     const int ty = threadIdx.x / kTile;
     const T *src = x + img;
@@ -45,19 +46,27 @@ __global__ __launch_bounds__(256) void to_nhwc_kernel(const T *__restrict__ x, T
     }
 }
 
+template <typename T, bool BLK>
+__global__ __launch_bounds__(256) void to_nhwc_kernel(const T *__restrict__ x, T *__restrict__ xt,
+                                                      int C, int HW)
+{
+    __shared__ T tile[kTile][kTile + 1];
+    transpose_tile<T, BLK>(x, xt, C, HW, blockIdx.x, blockIdx.y, blockIdx.z, tile);
+}
+
 // The same transpose with 16-byte global accesses on both sides (pixels
 // along the load, channels along the store); requires C and H*W to be
 // multiples of the vector width (and, for blocks, 8 channels per vector).
 template <typename T, bool BLK>
-__global__ __launch_bounds__(256) void to_nhwc_vec_kernel(const T *__restrict__ x,
-                                                          T *__restrict__ xt, int C, int HW)
+__device__ __forceinline__ void transpose_tile_vec(const T *__restrict__ x, T *__restrict__ xt,
+                                                   int C, int HW, int bx, int by, int bz,
+                                                   T (*tile)[kTile + 1])
 {
     constexpr int V = 16 / sizeof(T);
     constexpr int NV = kTile / V;                      // vectors per tile row
-    __shared__ T tile[kTile][kTile + 1];
-    const int p0 = blockIdx.x * kTile;
-    const int c0 = blockIdx.y * kTile;
-    const size_t img = size_t(blockIdx.z) * size_t(C) * size_t(HW);
+    const int p0 = bx * kTile;
+    const int c0 = by * kTile;
+    const size_t img = size_t(bz) * size_t(C) * size_t(HW);
     const T *src = x + img;
     T *dst = xt + img;
     for (int v = threadIdx.x; v < kTile * NV; v += 256) {
@@ -85,12 +94,18 @@ __global__ __launch_bounds__(256) void to_nhwc_vec_kernel(const T *__restrict__ 
     }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void pack_weight_kernel(const T *__restrict__ w,
-                                                          T *__restrict__ wp, int total, int Kp,
-                                                          int Kg, int Cg, int K)
+template <typename T, bool BLK>
+__global__ __launch_bounds__(256) void to_nhwc_vec_kernel(const T *__restrict__ x,
+                                                          T *__restrict__ xt, int C, int HW)
 {
-    const int t = blockIdx.x * 256 + threadIdx.x;
+    __shared__ T tile[kTile][kTile + 1];
+    transpose_tile_vec<T, BLK>(x, xt, C, HW, blockIdx.x, blockIdx.y, blockIdx.z, tile);
+}
+
+template <typename T>
+__device__ __forceinline__ void pack_weight_elem(const T *__restrict__ w, T *__restrict__ wp,
+                                                 int t, int total, int Kp, int Kg, int Cg, int K)
+{
     if (t >= total)
         return;
     const int kk = t % Kp;
@@ -104,18 +119,23 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const T *__restrict__ 
     wp[t] = v;
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void pack_weight_kernel(const T *__restrict__ w,
+                                                          T *__restrict__ wp, int total, int Kp,
+                                                          int Kg, int Cg, int K)
+{
+    pack_weight_elem(w, wp, int(blockIdx.x * 256 + threadIdx.x), total, Kp, Kg, Cg, K);
+}
+
 // The window path's weight: for each group g, K step st = chunk*K + k
 // (chunk of 16 channels, tap k) and half h, the plane of Mg rows of 8
 // channels: wp[(((g*S + st)*2 + h)*Mg + m)*8 + e] =
 // weight[g*Mg + m][16*chunk + 8*h + e][k], S = (Cg/16)*K.
 template <typename T>
-__global__ __launch_bounds__(256) void pack_weight_steps_kernel(const T *__restrict__ w,
-                                                                T *__restrict__ wp, int total,
-                                                                int Mg, int Cg, int K, int S,
-                                                                uint32_t *__restrict__ flags,
-                                                                int nflags)
+__device__ __forceinline__ void pack_steps_elem(const T *__restrict__ w, T *__restrict__ wp,
+                                                int t, int total, int Mg, int Cg, int K, int S,
+                                                uint32_t *__restrict__ flags, int nflags)
 {
-    const int t = blockIdx.x * 256 + threadIdx.x;
     if (t < nflags)
         flags[t] = 0u;
     if (t >= total)
@@ -131,6 +151,56 @@ __global__ __launch_bounds__(256) void pack_weight_steps_kernel(const T *__restr
     const int chunk = st / K, k = st - chunk * K;
     const int cl = chunk * 16 + h * 8 + e;
     wp[t] = w[(size_t(g * Mg + m) * Cg + cl) * K + k];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void pack_weight_steps_kernel(const T *__restrict__ w,
+                                                                T *__restrict__ wp, int total,
+                                                                int Mg, int Cg, int K, int S,
+                                                                uint32_t *__restrict__ flags,
+                                                                int nflags)
+{
+    pack_steps_elem(w, wp, int(blockIdx.x * 256 + threadIdx.x), total, Mg, Cg, K, S, flags,
+                    nflags);
+}
+
+// Both set-up jobs of a forward in one launch (for small problems the
+// launches cost more than the work): the first `nt` workgroups transpose
+// x (tile b -> (b % gx, b / gx % gy, b / (gx*gy))), the rest repack the
+// weight (PK 1: [G][Mg][Kp] tap-major; PK 2: the window path's step-major
+// planes, and its hand-over flags cleared).
+struct PrepArgs {
+    const void *x;
+    void *xt;
+    const void *w;
+    void *wp;
+    uint32_t *flags;
+    int C, HW, gx, gy, nt;
+    int total, Kp, Kg, Cg, K, Mg, S, nflags;
+};
+
+template <typename T, bool BLK, bool VEC, int PK>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
+{
+    __shared__ T tile[kTile][kTile + 1];
+    const int b = int(blockIdx.x);
+    if (b < a.nt) {
+        const int bx = b % a.gx, by = (b / a.gx) % a.gy, bz = b / (a.gx * a.gy);
+        if constexpr (VEC)
+            transpose_tile_vec<T, BLK>(static_cast<const T *>(a.x), static_cast<T *>(a.xt), a.C,
+                                       a.HW, bx, by, bz, tile);
+        else
+            transpose_tile<T, BLK>(static_cast<const T *>(a.x), static_cast<T *>(a.xt), a.C,
+                                   a.HW, bx, by, bz, tile);
+        return;
+    }
+    const int t = (b - a.nt) * 256 + int(threadIdx.x);
+    if constexpr (PK == 1)
+        pack_weight_elem(static_cast<const T *>(a.w), static_cast<T *>(a.wp), t, a.total, a.Kp,
+                         a.Kg, a.Cg, a.K);
+    else
+        pack_steps_elem(static_cast<const T *>(a.w), static_cast<T *>(a.wp), t, a.total, a.Mg,
+                        a.Cg, a.K, a.S, a.flags, a.nflags);
 }
 
 template <typename T, bool BLK>
@@ -218,6 +288,80 @@ hipError_t launch_pack_weight_steps(const Problem &p, const void *weight, void *
     case MDCN_F32: return pack_weight_steps_t<float>(p, weight, wpack, flags, nflags, stream);
     case MDCN_F16: return pack_weight_steps_t<half_t>(p, weight, wpack, flags, nflags, stream);
     case MDCN_BF16: return pack_weight_steps_t<bf16_t>(p, weight, wpack, flags, nflags, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <typename T, bool BLK, int PK>
+hipError_t prep_t(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
+                  const void *w, void *wp, uint32_t *flags, int nflags, hipStream_t s)
+{
+    const int HW = int(p.H * p.W);
+    PrepArgs a{};
+    a.x = x; a.xt = xt; a.w = w; a.wp = wp; a.flags = flags;
+    a.C = int(p.C); a.HW = HW;
+    a.gx = (HW + kTile - 1) / kTile;
+    a.gy = int((p.C + kTile - 1) / kTile);
+    a.Cg = int(p.Cg); a.K = int(p.K);
+    int64_t npack;
+    if constexpr (PK == 1) {
+        a.total = int(p.Co * plan.Kp);
+        a.Kp = int(plan.Kp);
+        a.Kg = int(p.Kg);
+        npack = a.total;
+    } else {
+        if (p.Cg % 16 != 0)
+            return hipErrorInvalidValue;
+        a.S = int(p.Cg / 16 * p.K);
+        a.total = int(p.G * a.S * 2 * p.Mg * 8);
+        a.Mg = int(p.Mg);
+        a.nflags = flags ? nflags : 0;
+        npack = std::max(a.total, a.nflags);
+    }
+    const int64_t nt = int64_t(a.gx) * a.gy * cnt;
+    const int64_t blocks = nt + (npack + 255) / 256;
+    if (blocks > 0x7fffffffll)
+        return hipErrorInvalidValue;
+    a.nt = int(nt);
+    constexpr int V = 16 / sizeof(T);
+    const bool vec = p.C % V == 0 && HW % V == 0 && (!BLK || V == 8) &&
+                     reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(xt) % 16 == 0;
+    if (vec)
+        hipLaunchKernelGGL((prep_kernel<T, BLK, true, PK>), dim3(unsigned(blocks)), dim3(256), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL((prep_kernel<T, BLK, false, PK>), dim3(unsigned(blocks)), dim3(256), 0,
+                           s, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t prep_dtype(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
+                      const void *w, void *wp, uint32_t *flags, int nflags, hipStream_t s)
+{
+    if (plan.path == Path::Window)
+        return prep_t<T, true, 2>(p, plan, cnt, x, xt, w, wp, flags, nflags, s);
+    return prep_t<T, false, 1>(p, plan, cnt, x, xt, w, wp, flags, nflags, s);
+}
+
+}  // namespace
+
+hipError_t launch_prep(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
+                       const void *weight, void *wpack, uint32_t *flags, int nflags,
+                       hipStream_t stream)
+{
+    if (plan.path == Path::Window && p.C % 8 != 0)
+        return hipErrorInvalidValue;
+    switch (p.dtype) {
+    case MDCN_F32:
+        return prep_dtype<float>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, stream);
+    case MDCN_F16:
+        return prep_dtype<half_t>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, stream);
+    case MDCN_BF16:
+        return prep_dtype<bf16_t>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -206,18 +206,28 @@ def test_off_image_samples_give_bias_exactly(path):
     assert torch.equal(got, inp["bias"][None, :, None, None].expand_as(got))
 
 
-def test_chunked_workspace_matches_default():
-    pr = SMALL["multi_tile_dg2"]
+@pytest.mark.parametrize("name,path", [("multi_tile_dg2", mdcn.MDCN_PATH_AUTO),
+                                       ("fused_multi_tile", mdcn.MDCN_PATH_FUSED),
+                                       ("window_multi_tile", mdcn.MDCN_PATH_WINDOW)])
+def test_chunked_workspace_matches_default(name, path):
+    """The least workspace: one image per chunk; the first chunk's launch
+    also repacks the weight (and clears the window path's flags), the later
+    chunks only move x."""
+    pr = SMALL[name]
     inp = workloads.generate(pr, "f16", seed=5)
-    op = make_op(pr)
+    op = make_op(pr, path)
     dims = [pr.N, pr.C, pr.H, pr.W] + list(inp["offset"].shape) + list(inp["mask"].shape) + \
         list(inp["weight"].shape)
     full, least = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, dims)
     assert least < full
     assert "chunk=1" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, dims, least)
-    a = run_gpu(pr, inp)
-    b = run_gpu(pr, inp, workspace_bytes=least)
+    tr = mdcn.Trace(64)
+    a = run_gpu(pr, inp, path)
+    b = run_gpu(pr, inp, path, workspace_bytes=least, trace=tr)
     assert torch.equal(a, b)
+    names = [n for n, _ in tr.read()]
+    assert names[0].startswith("prep_") and not any(n.startswith("prep_") for n in names[1:])
+    assert len([n for n in names if n.startswith("to_")]) == pr.N - 1
 
 
 def test_traced_forward_matches_and_records():
@@ -228,7 +238,7 @@ def test_traced_forward_matches_and_records():
     b = run_gpu(pr, inp)
     assert torch.equal(a, b)
     names = [n for n, _ in tr.read()]
-    assert names[0] == "pack_weight"
+    assert names[0] == "prep_nhwc"
     assert names.count("gemm_bias") == names.count("deform_gather") >= 1
     assert all(ms >= 0 for _, ms in tr.read())
 
