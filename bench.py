@@ -37,7 +37,7 @@ MEASURED_TRAFFIC = {
     ("window_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
         "bytes": (139748 * 2 + 124594) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'launch.h', 'plan.cpp', 'plan.h'),
-        "sha": "44c655ecd34ddb8f",
+        "sha": "bc579410d1e170c8",
     },
     ("fused_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
         "bytes": (53949 * 2 + 51200) * 1024,

@@ -4,23 +4,33 @@
 //       + sum_{k, c'} A[g][m][k*Cg + c'] * mask * bilinear0(x[n][g*Cg + c'], sample(k, ho, wo))
 // [plugin guide §五 steps 1-3, without a columns buffer between step 1 and 2].
 //
-// A workgroup (4 waves, one per SIMD) computes 256 output channels x one
-// TH x TW tile of output pixels (256 pixels) of one image and group.  The
-// contraction runs chunk-major: for each chunk of 16 input channels, the
-// rectangle of input pixels that the tile's samples can reach -- the anchors
-// of all taps plus a margin of `margin` pixels on every side for the offsets
-// -- is copied into LDS once (the "window", channels-last, two planes of 8
-// channels), and the 9 taps of the chunk are then 9 K-steps that read their
-// bilinear corners from it.  A sample with a corner on the image that falls
-// outside the window is rare with the margin sized for the offsets; its lane
-// reads zeros from the window and its value is computed from global memory
-// instead (the fallback), so the result does not depend on the margin.
+// A tile is 256 output channels of one image and group x 256 output pixels:
+// a TH x TW rectangle, or (TH = 1, narrow images) 256 consecutive pixels in
+// raster order.  The contraction runs chunk-major: for each chunk of 16 input
+// channels, the rectangle of input pixels that the tile's samples can reach
+// -- the anchors of all taps plus a margin of `margin` pixels on every side
+// for the offsets -- is copied into LDS once (the "window", channels-last,
+// two planes of 8 channels), and the 9 taps of the chunk are then 9 K-steps
+// that read their bilinear corners from it.  A sample with a corner on the
+// image that falls outside the window is rare with the margin sized for the
+// offsets; its lane reads zeros from the window and its value is computed
+// from global memory instead (the fallback), so the result does not depend
+// on the margin.
+//
+// The grid is persistent, one workgroup (4 waves, one per SIMD) per CU.  The
+// (tile, chunk) units are cut into contiguous per-workgroup ranges on the
+// host (balanced for chunks plus a per-tile cost); a workgroup walks the
+// tiles of its range from last to first.  A tile split between two
+// workgroups is finished by the one holding its last chunks: the other
+// publishes its accumulators (device-scope stores, then a flag) on the first
+// tile it processes, and the finisher loads them into its accumulators on
+// the last one.
 //
 // Every wave owns 64 pixels (two slabs of 32) and all 256 output channels:
 // it makes the B fragments of its own pixels in registers (lane l of a slab
 // owns pixel l%32 and channels 8*(l/32)..+8 of the chunk, which is exactly
 // the MFMA B-fragment layout), so B never goes through LDS, and reads the A
-// fragments (packed weight rows) from LDS stages filled by DMA three steps
+// fragments (packed weight rows) from LDS stages filled by DMA LEAD steps
 // ahead.  The per-lane sampling geometry of all taps (window address of the
 // top-left corner, four weights with the mask folded in) is computed once per
 // tile and kept in registers.  In each step the MFMAs of step s run beside
