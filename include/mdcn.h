@@ -99,15 +99,20 @@ typedef enum mdcn_path {
                                   column; 64 or 128 columns) that fits in LDS beside the
                                   operand stages                                          */
     MDCN_PATH_WINDOW = 4       /* the gather fused into the MFMA GEMM with each output
-                                  tile's input window staged in LDS: a workgroup computes
-                                  256 output channels x 256 output pixels; per chunk of 16
+                                  tile's input window staged in LDS: a tile is 256 output
+                                  channels x 256 output pixels (16x16, 8x32, 32x8, or 256
+                                  consecutive pixels of a narrow image); per chunk of 16
                                   input channels the input rectangle its samples can reach
                                   (anchors plus an offset margin) is copied to LDS once and
                                   the 9 taps read their bilinear corners from it; a sample
                                   with a corner on the image outside the rectangle is read
-                                  from global memory.  Requires fp16/bf16, a 3x3 kernel,
-                                  C/group a multiple of 16 and each group inside one
-                                  deformable group [plugin guide §五 steps 1-3]           */
+                                  from global memory.  One workgroup per CU walks a range
+                                  of (tile, chunk) units; tiles split between two
+                                  workgroups are summed through the workspace.  Requires
+                                  fp16/bf16, a 3x3 kernel, C/group a multiple of 16 and
+                                  each group inside one deformable group; the automatic
+                                  choice when its tiles are at least 7/8 full
+                                  [plugin guide §五 steps 1-3]                             */
 } mdcn_path;
 
 typedef struct mdcn_op mdcn_op;
