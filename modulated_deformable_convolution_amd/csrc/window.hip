@@ -614,29 +614,37 @@ void window_kernel(WinArgs args)
             const int s = rc * kTaps + k;
             const int chunk = c_lo + rc;
             const bool last_chunk = chunk + 1 >= c_hi;
-            // A of step s+1 (and, with it, every older copy) has landed.  A(s+1)
-            // was issued in step s+1-LEAD; issued after it, and allowed to be in
-            // flight: the A copies of the LEAD-2 steps between, and the window
-            // copy of the next chunk when a step k == 0 lies in [s+1-LEAD, s-1].
-            // In the last chunk no window is issued and the A copies stop at the
-            // last step.  (No LDS wait: every LDS read of an A stage or window
-            // buffer that a copy issued after this barrier overwrites was
-            // consumed -- so waited for -- in an earlier step.)
+            // One barrier every other step (even s): it makes A of steps s+1
+            // and s+2 visible to every wave (the next step, which has none,
+            // reads A(s+2)), so A(s+2) and every older copy must have
+            // landed.  Issued after A(s+2) and allowed to be in flight: the A
+            // copies of the LEAD-3 steps after it, and the window copy of the
+            // next chunk while its first reads (in step k == 7, after the
+            // barrier of step 6 or 7) are still ahead -- k in [1, LEAD-2]
+            // (younger than A(s+2)) and k <= 5.  In the last chunk no window
+            // is issued and the A copies stop at the last step.  (No LDS wait:
+            // every LDS read of an A stage or window buffer that a copy issued
+            // in this or the next step overwrites was consumed -- so waited
+            // for -- before the previous step ended, and every wave has passed
+            // this barrier or the previous one.)
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            constexpr int kNoLgkm = 0x70 | 0xF00;         // expcnt and lgkmcnt: no wait
-            if (last_chunk) {
-                constexpr int NA =
-                    kAInstr * ((LEAD - 2) < (7 - k) ? (LEAD - 2) : (7 - k > 0 ? 7 - k : 0));
-                __builtin_amdgcn_s_waitcnt((NA & 15) | ((NA >> 4) << 14) | kNoLgkm);
-            } else if (k >= 1 && k <= LEAD - 1) {
-                constexpr int N = kAInstr * (LEAD - 2) + kWinInstr;
-                __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
-            } else {
-                constexpr int N = kAInstr * (LEAD - 2);
-                __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+            if (((rc + k) & 1) == 0) {                    // s = 9 rc + k is even
+                constexpr int kNoLgkm = 0x70 | 0xF00;     // expcnt and lgkmcnt: no wait
+                if (last_chunk) {
+                    constexpr int NA = kAInstr * ((LEAD - 3) < (6 - k)
+                                                      ? (LEAD - 3)
+                                                      : (6 - k > 0 ? 6 - k : 0));
+                    __builtin_amdgcn_s_waitcnt((NA & 15) | ((NA >> 4) << 14) | kNoLgkm);
+                } else if (k >= 1 && k <= LEAD - 2 && k <= 5) {
+                    constexpr int N = kAInstr * (LEAD - 3) + kWinInstr;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                } else {
+                    constexpr int N = kAInstr * (LEAD - 3);
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                }
+                __builtin_amdgcn_s_barrier();
             }
-            __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("" ::: "memory");
             if (s + LEAD < steps)
