@@ -113,6 +113,11 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
             # x (NHWC copy), offsets and masks read once, output written once
             return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + pr.Co * Kp * e
                         + bias_bytes, flops=2 * cnt * pr.Co * Kg * P)
+        if name == "direct":
+            # one launch over every image: x, offsets, masks and weight read
+            # once, output written once
+            return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + w_bytes + bias_bytes,
+                        flops=2 * cnt * pr.Co * Kg * P)
         if name == "depthwise_geometry":
             # offsets and masks read once, a 16-byte record per offset group, tap
             # and pixel written once
@@ -140,7 +145,7 @@ def main(argv=None) -> int:
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "gather_gemm", "fused",
-                                                       "window", "depthwise"],
+                                                       "window", "depthwise", "direct"],
                     help="computation path (default: the library's choice)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph that holds one captured forward (the "
@@ -188,7 +193,7 @@ def main(argv=None) -> int:
     g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
     path = {"auto": mdcn.MDCN_PATH_AUTO, "gather_gemm": mdcn.MDCN_PATH_GATHER_GEMM,
             "fused": mdcn.MDCN_PATH_FUSED, "window": mdcn.MDCN_PATH_WINDOW,
-            "depthwise": mdcn.MDCN_PATH_DEPTHWISE}[args.path]
+            "depthwise": mdcn.MDCN_PATH_DEPTHWISE, "direct": mdcn.MDCN_PATH_DIRECT}[args.path]
     op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups,
                           path=path)
     code = mdcn.dtype_code(g["x"].dtype)
@@ -249,7 +254,7 @@ def main(argv=None) -> int:
         avg_ms = total_ms / count
         launches_per_step = count / args.steps
         cnt = (pr.N / max(1, launches_per_step)
-               if name in ("to_nhwc", "to_channel_blocks", "deform_gather", "gemm_bias",
+               if name in ("direct", "to_nhwc", "to_channel_blocks", "deform_gather", "gemm_bias",
                            "fused_gather_gemm", "window_gather_gemm", "depthwise_geometry",
                            "depthwise_direct")
                else 0)

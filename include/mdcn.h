@@ -98,7 +98,7 @@ typedef enum mdcn_path {
                                   geometry table (32 bytes per offset group, tap and output
                                   column; 64 or 128 columns) that fits in LDS beside the
                                   operand stages                                          */
-    MDCN_PATH_WINDOW = 4       /* the gather fused into the MFMA GEMM with each output
+    MDCN_PATH_WINDOW = 4,      /* the gather fused into the MFMA GEMM with each output
                                   tile's input window staged in LDS: a tile is 256 output
                                   channels x 256 output pixels (16x16, 8x32, 32x8, or 256
                                   consecutive pixels of a narrow image); per chunk of 16
@@ -113,6 +113,11 @@ typedef enum mdcn_path {
                                   each group inside one deformable group; the automatic
                                   choice when its tiles are at least 7/8 full
                                   [plugin guide §五 steps 1-3]                             */
+    MDCN_PATH_DIRECT = 5       /* the whole forward in one launch, one thread per output
+                                  element reading x, offsets, masks and weights where they
+                                  are; for problems of at most 2^20 multiply-adds (the
+                                  automatic choice there), any problem when forced; no
+                                  workspace [plugin guide §五 steps 1-3]                   */
 } mdcn_path;
 
 typedef struct mdcn_op mdcn_op;

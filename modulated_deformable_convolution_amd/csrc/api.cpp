@@ -152,6 +152,12 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     const size_t off_img = size_t(2 * p.DG * p.K * p.P) * e;
     const size_t msk_img = size_t(p.DG * p.K * p.P) * e;
     const size_t out_img = size_t(p.Co * p.P) * e;
+    if (plan.path == Path::Direct) {
+        err = rec.run(mdcn::K_DIRECT, [&] {
+            return mdcn::launch_direct(p, x, offset, mask, weight, bias, out, stream);
+        });
+        return err == hipSuccess ? MDCN_OK : MDCN_E_LAUNCH;
+    }
     if (plan.path == Path::Depthwise) {
         for (int64_t n0 = 0; n0 < p.N; n0 += plan.chunk) {
             const int64_t cnt = std::min<int64_t>(plan.chunk, p.N - n0);
@@ -249,7 +255,8 @@ mdcn_status create_impl(const int32_t stride[2], const int32_t padding[2],
     if (st != MDCN_OK)
         return st;
     if (path != MDCN_PATH_AUTO && path != MDCN_PATH_GATHER_GEMM &&
-        path != MDCN_PATH_DEPTHWISE && path != MDCN_PATH_FUSED && path != MDCN_PATH_WINDOW)
+        path != MDCN_PATH_DEPTHWISE && path != MDCN_PATH_FUSED && path != MDCN_PATH_WINDOW &&
+        path != MDCN_PATH_DIRECT)
         return MDCN_E_PATH;
     mdcn_op *op = new (std::nothrow) mdcn_op;
     if (!op)
@@ -449,6 +456,7 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_TO_BLOCKS: return "to_channel_blocks";
     case mdcn::K_PREP_NHWC: return "prep_nhwc";
     case mdcn::K_PREP_BLOCKS: return "prep_blocks";
+    case mdcn::K_DIRECT: return "direct";
     }
     return "?";
 }
@@ -488,7 +496,11 @@ mdcn_status mdcn_describe_plan(const mdcn_op *op, mdcn_dtype dtype, const int64_
         st = mdcn::make_plan(op->attrs, p, workspace_bytes, workspace_bytes == 0, &plan);
         if (st != MDCN_OK)
             return st;
-        if (plan.path == Path::Depthwise)
+        if (plan.path == Path::Direct)
+            std::snprintf(buf, len, "path=direct N=%lld Co=%lld P=%lld Cg=%lld K=%lld ws=0",
+                          (long long)p.N, (long long)p.Co, (long long)p.P, (long long)p.Cg,
+                          (long long)p.K);
+        else if (plan.path == Path::Depthwise)
             std::snprintf(buf, len,
                           "path=depthwise_direct N=%lld C=%lld Co=%lld P=%lld chunk=%lld entry=%d "
                           "ws=%zu (geometry/img=%zu)",

@@ -22,7 +22,8 @@ enum KernelId : int32_t {
     K_TO_BLOCKS = 9,
     K_PREP_NHWC = 10,
     K_PREP_BLOCKS = 11,
-    K_COUNT = 12
+    K_DIRECT = 12,
+    K_COUNT = 13
 };
 
 // weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
@@ -47,6 +48,10 @@ hipError_t launch_to_channel_blocks(const Problem &p, int64_t cnt, const void *x
 hipError_t launch_prep(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
                        const void *weight, void *wpack, uint32_t *flags, int nflags,
                        hipStream_t stream);
+
+// The whole forward of all N images, one thread per output element.
+hipError_t launch_direct(const Problem &p, const void *x, const void *offset, const void *mask,
+                         const void *weight, const void *bias, void *out, hipStream_t stream);
 
 // x [cnt][C][H][W] -> xt [cnt][H][W][C] (channels innermost).
 hipError_t launch_to_nhwc(const Problem &p, int64_t cnt, const void *x, void *xt,

@@ -414,14 +414,29 @@ bool window_preferred(const Problem &p)
     return 8 * p.Ho * p.Wo * p.Mg >= 7 * pad_px * pad_m;
 }
 
+// Small problems: one launch of the direct kernel costs less than the
+// launches of the other paths (a few microseconds each) up to about 2^20
+// multiply-adds.
+bool direct_preferred(const Problem &p)
+{
+    return double(p.N) * double(p.Co) * double(p.P) * double(p.Cg) * double(p.K) <=
+           double(kDirectMaxMacs);
+}
+
 mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
 {
     switch (a.path) {
     case MDCN_PATH_AUTO:
-        *out = (p.Cg == 1)              ? Path::Depthwise
+        *out = direct_preferred(p)      ? Path::Direct
+               : (p.Cg == 1)            ? Path::Depthwise
                : window_preferred(p)   ? Path::Window
                : fused_eligible(p)     ? Path::Fused
                                        : Path::GatherGemm;
+        return MDCN_OK;
+    case MDCN_PATH_DIRECT:
+        if (uint64_t(p.N) * uint64_t(p.Co) * uint64_t(p.P) > kDirectMaxOutputs)
+            return MDCN_E_PATH;
+        *out = Path::Direct;
         return MDCN_OK;
     case MDCN_PATH_WINDOW:
         if (!window_eligible(p))
@@ -452,6 +467,11 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
     mdcn_status st = choose_path(a, p, &plan.path);
     if (st != MDCN_OK)
         return st;
+    if (plan.path == Path::Direct) {
+        plan.chunk = std::max<int64_t>(p.N, 1);    // one launch, no workspace
+        *out = plan;
+        return MDCN_OK;
+    }
     if (plan.path == Path::Depthwise) {
         // The staged kernel reads each (offset group, tap, pixel)'s sampling
         // record (corner entry and weight factors), computed once per image
@@ -590,6 +610,8 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
 size_t min_workspace(const Problem &p, const Plan &plan)
 {
     (void)p;
+    if (plan.path == Path::Direct)
+        return 0;
     if (plan.path == Path::Depthwise)
         return plan.geo_bytes_per_image ? kAlign + plan.geo_bytes_per_image : 0;
     if (plan.path == Path::Window) {

@@ -34,7 +34,7 @@ struct Problem {
     int64_t sh, sw, ph, pw, dh, dw;
 };
 
-enum class Path { GatherGemm, Depthwise, Fused, Window };
+enum class Path { GatherGemm, Depthwise, Fused, Window, Direct };
 
 // Workgroup tile of the GEMM (rows of the packed weight x columns) and its
 // wave grid; every wave owns a block of 32x32 accumulator tiles.
@@ -71,6 +71,8 @@ constexpr int kWindowPixels = 1280;      // input positions one LDS window can h
 constexpr int kWindowZeroBytes = 1024;   // zeroed LDS after each window (>= 16*columns + 32)
 constexpr int64_t kWindowMaxMargin = 8;  // default offset margin around the anchors
 constexpr int kWindowMaxLead = 7;        // weight copies issued this many K steps ahead
+constexpr int64_t kDirectMaxMacs = int64_t(1) << 20;   // automatic direct path, at most
+constexpr uint64_t kDirectMaxOutputs = 0xffffff00ull;  // one 32-bit thread index
 constexpr int64_t kWindowSlots = 256;    // partial-sum slots at most (one per workgroup)
 constexpr size_t kWindowSlotBytes = size_t(256) * 256 * 4;   // fp32 256 x 256 tile
 

@@ -257,7 +257,7 @@ def test_fused_path_plan():
     assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, d128).startswith("path=fused")
     # not eligible: C/group = 36 is not a multiple of 64 -> gather + GEMM
     opg = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_FUSED)
-    d = [1, 36, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 8, 36, 3, 3]
+    d = [1, 36, 64, 64, 1, 18, 64, 64, 1, 9, 64, 64, 8, 36, 3, 3]
     with pytest.raises(mdcn.MdcnError) as e:
         mdcn.mdcn_workspace_bytes(opg, mdcn.MDCN_F16, d)
     assert e.value.status == mdcn.MDCN_E_PATH
@@ -316,10 +316,28 @@ def test_fused_tile_fits_lds():
 
 
 def test_contraction_padding():
-    # Kg = 4*9 = 36 pads to 64
-    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    # Kg = 4*9 = 36 pads to 64 (on the gather + GEMM path)
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_GATHER_GEMM)
     d1 = [1, 4, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 4, 4, 3, 3]
     assert "Kp=64" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F32, d1)
+
+
+def test_direct_path_plan():
+    """Problems of at most 2^20 multiply-adds take the one-launch direct
+    kernel (no workspace); larger ones keep the other paths; it can be forced
+    on any problem whose outputs fit a 32-bit thread index."""
+    auto = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    tiny = [1, 4, 8, 8, 1, 18, 8, 8, 1, 9, 8, 8, 4, 4, 3, 3]          # 9216 MACs
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F32, tiny).startswith("path=direct")
+    assert mdcn.mdcn_workspace_bytes(auto, mdcn.MDCN_F32, tiny) == (0, 0)
+    # 2^20 MACs exactly: direct; one more output channel: not
+    edge = _fused_dims(1, 4, 32, 32, 28, 3, 1, 1)     # 1 * 28 * 1024 * 4 * 9 = 1032192
+    assert mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F32, edge).startswith("path=direct")
+    over = _fused_dims(1, 4, 32, 32, 32, 3, 1, 1)     # 1179648 MACs
+    assert not mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F32, over).startswith("path=direct")
+    opd = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_DIRECT)
+    assert mdcn.mdcn_describe_plan(opd, mdcn.MDCN_F16, DIMS).startswith("path=direct")
+    assert mdcn.mdcn_workspace_bytes(opd, mdcn.MDCN_F16, DIMS) == (0, 0)
 
 
 def test_status_strings():

@@ -135,7 +135,7 @@ def oracle_full(pr, inp):
 
 
 def paths_for(pr, dtype):
-    paths = [mdcn.MDCN_PATH_GATHER_GEMM]
+    paths = [mdcn.MDCN_PATH_GATHER_GEMM, mdcn.MDCN_PATH_DIRECT]
     if pr.C // pr.groups == 1:
         paths.append(mdcn.MDCN_PATH_DEPTHWISE)
     if path_ok(pr, dtype, mdcn.MDCN_PATH_FUSED):
@@ -161,12 +161,21 @@ def test_small_full_tensor(name, dtype, path):
     assert ok, (name, dtype, error_report(got, ref), float((err / bound).max()))
 
 
-def test_auto_path_matches_forced_paths():
-    pr = SMALL["depthwise_mult2"]
+@pytest.mark.parametrize("pr,path,name", [
+    # 146k multiply-adds: the one-launch direct kernel
+    (SMALL["depthwise_mult2"], mdcn.MDCN_PATH_DIRECT, "path=direct"),
+    # 1.8M multiply-adds, C/group = 1: the depthwise kernel
+    (Problem(N=2, C=64, Co=64, H=40, W=40, groups=64, offset_dist=("uniform", 8.0)),
+     mdcn.MDCN_PATH_DEPTHWISE, "path=depthwise_direct"),
+])
+def test_auto_path_matches_forced_paths(pr, path, name):
     inp = workloads.generate(pr, "f32", seed=2)
+    shapes = pr.shapes()
+    dims = [int(v) for k in ("x", "offset", "mask", "weight") for v in shapes[k]]
+    assert mdcn.mdcn_describe_plan(make_op(pr), mdcn.MDCN_F32, dims).startswith(name)
     auto = run_gpu(pr, inp, mdcn.MDCN_PATH_AUTO)
-    dw = run_gpu(pr, inp, mdcn.MDCN_PATH_DEPTHWISE)
-    assert torch.equal(auto, dw)
+    forced = run_gpu(pr, inp, path)
+    assert torch.equal(auto, forced)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
