@@ -535,9 +535,10 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
                 if (v > 0)
                     plan.win_max_ctas = v;
             }
-            // a tile a workgroup touches costs about 3 chunks of main loop
-            // (its prologue and epilogue), in quarter chunks
-            plan.win_seg_cost_x4 = 12;
+            // a tile a workgroup touches costs about 4 chunks of main loop
+            // (its prologue and epilogue), in quarter chunks (measured on the
+            // OCDNet-like stage: 8, 12, 16, 20, 24, 32 -> 16 best)
+            plan.win_seg_cost_x4 = 16;
             if (const char *env = std::getenv("MDCN_WIN_SEG_X4")) {
                 const int v = std::atoi(env);
                 if (v >= 0 && v <= 1024)
