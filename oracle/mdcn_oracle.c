@@ -173,3 +173,164 @@ int mdcn_oracle_points(const double *x, const double *offset, const double *mask
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * FP8 compute mode: the same operator with both contraction operands held
+ * as OCP FP8 E4M3 numbers and the products summed in high precision.
+ *
+ * The pages fix no FP8 arithmetic (the plugin accepts fp32 and fp16 only,
+ * [plugin guide §四]); this mode is this library's extension, and its
+ * definition here is:
+ *   F1 a column value (the modulated bilinear sample, computed exactly) is
+ *      rounded to the nearest E4M3 number, ties to the even code, after
+ *      clamping to [-448, 448] (saturation; NaN stays NaN);
+ *   F2 each output channel's weight row is scaled by 2^e, e the largest
+ *      integer with max|w_row| * 2^e <= 448 (e = 0 for an all-zero row;
+ *      e clamped to [-126, 126]), then rounded as in F1;
+ *   F3 out = 2^-e * sum(q(w) * q(column)) + bias.
+ * E4M3 (OCP 8-bit floating point, E4M3 variant): sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 holds subnormals m * 2^-9; the
+ * all-ones exponent with mantissa 7 is NaN; no infinities; the largest
+ * finite value is 1.75 * 2^8 = 448.
+ * ------------------------------------------------------------------------ */
+
+/* F1: nearest E4M3 value, ties to even, saturating at +-448. */
+double mdcn_oracle_e4m3(double v)
+{
+    if (isnan(v))
+        return v;
+    const double a = fabs(v);
+    if (a >= 448.0)
+        return copysign(448.0, v);
+    /* spacing of E4M3 numbers around a: 2^-9 below the smallest normal
+     * 2^-6, else 2^(floor(log2 a) - 3) (3 mantissa bits) */
+    double step;
+    if (a < 0x1p-6) {
+        step = 0x1p-9;
+    } else {
+        int ex;
+        frexp(a, &ex);                 /* a = f * 2^ex, f in [0.5, 1) */
+        step = ldexp(1.0, ex - 1 - 3);
+    }
+    /* a / step is exact (a power-of-two scaling); nearbyint rounds half to
+     * even in the default rounding mode, and an even multiple of the step is
+     * an even mantissa (also where the rounding carries into the next binade) */
+    return copysign(nearbyint(a / step) * step, v);
+}
+
+/* F2: the exponent e of one weight row of n values. */
+int mdcn_oracle_fp8_row_exponent(const double *row, int64_t n)
+{
+    double mx = 0.0;
+    for (int64_t t = 0; t < n; ++t)
+        if (fabs(row[t]) > mx)
+            mx = fabs(row[t]);
+    if (!(mx > 0.0) || isinf(mx))
+        return 0;
+    /* mx = f * 2^ex with f in [0.5, 1); 448 = 0.875 * 2^9, so
+     * mx * 2^e <= 448 holds for e = 9 - ex when f <= 0.875, else 8 - ex */
+    int ex;
+    const double f = frexp(mx, &ex);
+    int e = (f <= 0.875) ? 9 - ex : 8 - ex;
+    if (e > 126)
+        e = 126;
+    if (e < -126)
+        e = -126;
+    return e;
+}
+
+/* One output element in the FP8 mode (F1-F3).  qw is the quantized weight
+ * q(w * 2^e) of every weight, scale[co] = 2^-e of its row.  *abs_sum gets
+ * 2^-e * sum |q(w) * q(column)| (a scale for the contraction's rounding). */
+static double output_element_fp8(const double *x, const double *offset, const double *mask,
+                                  const double *qw, const double *scale, const double *bias,
+                                  const int64_t *p, int64_t n, int64_t co, int64_t ho,
+                                  int64_t wo, double *abs_sum)
+{
+    const int64_t C = p[P_C], H = p[P_H], W = p[P_W], Co = p[P_CO];
+    const int64_t kh = p[P_KH], kw = p[P_KW], Ho = p[P_HO], Wo = p[P_WO];
+    const int64_t G = p[P_GROUP], DG = p[P_DGROUP];
+    const int64_t K = kh * kw;
+    const int64_t Cg = C / G, Mg = Co / G, Cdg = C / DG;
+    const int64_t g = co / Mg;
+    const int64_t HoWo = Ho * Wo;
+    const int64_t pix = ho * Wo + wo;
+
+    double acc = 0.0, sa = 0.0;
+    for (int64_t cl = 0; cl < Cg; ++cl) {
+        const int64_t c = g * Cg + cl;
+        const int64_t q = c / Cdg;
+        const double *plane = x + (n * C + c) * H * W;
+        for (int64_t i = 0; i < kh; ++i) {
+            for (int64_t j = 0; j < kw; ++j) {
+                const int64_t k = i * kw + j;
+                const int64_t off_h_ch = n * 2 * DG * K + q * 2 * K + 2 * k;
+                const int64_t mask_ch = n * DG * K + q * K + k;
+                const double dh = offset[off_h_ch * HoWo + pix];
+                const double dw = offset[(off_h_ch + 1) * HoWo + pix];
+                const double m = mask[mask_ch * HoWo + pix];
+                const double h = (double)(ho * p[P_SH] - p[P_PH] + i * p[P_DH]) + dh;
+                const double w = (double)(wo * p[P_SW] - p[P_PW] + j * p[P_DW]) + dw;
+                const double col = mdcn_oracle_e4m3(bilinear_zero(plane, H, W, h, w) * m);
+                const double prod = qw[((co * Cg + cl) * kh + i) * kw + j] * col;
+                acc += prod;
+                sa += fabs(prod);
+            }
+        }
+    }
+    if (abs_sum)
+        *abs_sum = sa * scale[co];
+    acc *= scale[co];
+    if (bias)
+        acc += bias[co];
+    return acc;
+}
+
+/* F2 for every row: qw (Co*Cg*K values) and scale (Co values). */
+static void quantize_weight(const double *weight, const int64_t *p, double *qw, double *scale)
+{
+    const int64_t Co = p[P_CO], Cg = p[P_C] / p[P_GROUP], K = p[P_KH] * p[P_KW];
+    for (int64_t co = 0; co < Co; ++co) {
+        const double *row = weight + co * Cg * K;
+        const int e = mdcn_oracle_fp8_row_exponent(row, Cg * K);
+        scale[co] = ldexp(1.0, -e);
+        for (int64_t t = 0; t < Cg * K; ++t)
+            qw[co * Cg * K + t] = mdcn_oracle_e4m3(ldexp(row[t], e));
+    }
+}
+
+/* Selected outputs in the FP8 mode; qw and scale are caller-provided scratch
+ * of Co*Cg*K and Co doubles; abs_sum (may be NULL) gets one value per point. */
+int mdcn_oracle_points_fp8(const double *x, const double *offset, const double *mask,
+                           const double *weight, const double *bias, const int64_t *p,
+                           int64_t npts, const int64_t *idx, double *qw, double *scale,
+                           double *out, double *abs_sum)
+{
+    const int64_t N = p[P_N], Co = p[P_CO], Ho = p[P_HO], Wo = p[P_WO];
+    if (p[P_GROUP] <= 0 || p[P_DGROUP] <= 0 || p[P_C] % p[P_GROUP] || Co % p[P_GROUP] ||
+        p[P_C] % p[P_DGROUP])
+        return -1;
+    const int64_t total = N * Co * Ho * Wo;
+    for (int64_t t = 0; t < npts; ++t)
+        if (idx[t] < 0 || idx[t] >= total)
+            return -1;
+    quantize_weight(weight, p, qw, scale);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t t = 0; t < npts; ++t) {
+        int64_t r = idx[t];
+        const int64_t wo = r % Wo; r /= Wo;
+        const int64_t ho = r % Ho; r /= Ho;
+        const int64_t co = r % Co; r /= Co;
+        const int64_t n = r;
+        out[t] = output_element_fp8(x, offset, mask, qw, scale, bias, p, n, co, ho, wo,
+                                    abs_sum ? abs_sum + t : NULL);
+    }
+    return 0;
+}
+
+/* F1 applied to n values (for the tests of the quantizer itself). */
+void mdcn_oracle_e4m3_array(const double *v, int64_t n, double *out)
+{
+    for (int64_t t = 0; t < n; ++t)
+        out[t] = mdcn_oracle_e4m3(v[t]);
+}

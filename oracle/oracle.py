@@ -45,6 +45,13 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mdcn_oracle_forward.restype = ctypes.c_int
     lib.mdcn_oracle_points.argtypes = [dp, dp, dp, dp, dp, ip, ctypes.c_int64, ip, dp]
     lib.mdcn_oracle_points.restype = ctypes.c_int
+    lib.mdcn_oracle_points_fp8.argtypes = [dp, dp, dp, dp, dp, ip, ctypes.c_int64, ip, dp, dp,
+                                           dp, dp]
+    lib.mdcn_oracle_points_fp8.restype = ctypes.c_int
+    lib.mdcn_oracle_e4m3_array.argtypes = [dp, ctypes.c_int64, dp]
+    lib.mdcn_oracle_e4m3_array.restype = None
+    lib.mdcn_oracle_fp8_row_exponent.argtypes = [dp, ctypes.c_int64]
+    lib.mdcn_oracle_fp8_row_exponent.restype = ctypes.c_int
     lib.mdcn_oracle_max_threads.argtypes = []
     lib.mdcn_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -141,3 +148,59 @@ def forward_points(x, offset, mask, weight, bias, flat_indices, stride=1, paddin
     if rc != 0:
         raise ValueError("oracle: unsupported problem or index out of range")
     return out
+
+
+# --- FP8 compute mode (F1-F3 in mdcn_oracle.c) --------------------------------
+
+def e4m3(values, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """Each value rounded to the nearest OCP E4M3 number (ties to even,
+    saturating at +-448), as float64."""
+    lib = lib or load_library()
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64))
+    out = np.empty_like(v)
+    lib.mdcn_oracle_e4m3_array(_ptr(v.reshape(-1)), v.size, _ptr(out.reshape(-1)))
+    return out
+
+
+def fp8_row_exponent(row, lib: ctypes.CDLL | None = None) -> int:
+    """The exponent e of one weight row: the largest integer with
+    max|row| * 2^e <= 448 (0 for an all-zero row)."""
+    lib = lib or load_library()
+    r = np.ascontiguousarray(np.asarray(row, dtype=np.float64).reshape(-1))
+    return int(lib.mdcn_oracle_fp8_row_exponent(_ptr(r), r.size))
+
+
+def forward_points_fp8(x, offset, mask, weight, bias, flat_indices, stride=1, padding=0,
+                       dilation=1, groups=1, deformable_groups=1,
+                       lib: ctypes.CDLL | None = None):
+    """Selected output elements in the FP8 compute mode, float64, and for each
+    the sum of the absolute scaled products (the contraction's magnitude)."""
+    lib = lib or load_library()
+    x, offset, mask, weight, bias = map(_f64, (x, offset, mask, weight, bias))
+    p = problem(x.shape, offset.shape, weight.shape, stride, padding, dilation,
+                groups, deformable_groups)
+    idx = np.ascontiguousarray(np.asarray(flat_indices, dtype=np.int64))
+    out = np.empty(idx.shape, dtype=np.float64)
+    asum = np.empty(idx.shape, dtype=np.float64)
+    qw = np.empty(weight.size, dtype=np.float64)
+    scale = np.empty(weight.shape[0], dtype=np.float64)
+    rc = lib.mdcn_oracle_points_fp8(_ptr(x), _ptr(offset), _ptr(mask), _ptr(weight),
+                                    _ptr(bias), p.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    idx.size, idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    _ptr(qw), _ptr(scale), _ptr(out), _ptr(asum))
+    if rc != 0:
+        raise ValueError("oracle: unsupported problem or index out of range")
+    return out, asum
+
+
+def forward_fp8(x, offset, mask, weight, bias=None, stride=1, padding=0, dilation=1,
+                groups=1, deformable_groups=1, lib: ctypes.CDLL | None = None):
+    """Every output element in the FP8 compute mode, shape [N, Co, Ho, Wo],
+    and the matching sums of absolute scaled products."""
+    N, Co = x.shape[0], weight.shape[0]
+    Ho, Wo = offset.shape[2], offset.shape[3]
+    idx = np.arange(N * Co * Ho * Wo, dtype=np.int64)
+    out, asum = forward_points_fp8(x, offset, mask, weight, bias, idx, stride, padding,
+                                   dilation, groups, deformable_groups, lib=lib)
+    shape = (N, Co, Ho, Wo)
+    return out.reshape(shape), asum.reshape(shape)
