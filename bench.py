@@ -25,7 +25,7 @@ if ROOT not in sys.path:
 
 METRIC = "modulated deform-conv fwd effective GFLOP/s + HBM GB/s, % roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
 
@@ -89,6 +89,9 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
     w_bytes = pr.Co * Cg * K * e
     bias_bytes = pr.Co * e if pr.bias else 0
     col_img = G * P * Kp * e
+    Kp8 = (Kg + 127) // 128 * 128          # FP8 path: one byte per value, 128-byte K steps
+    col_img8 = G * P * Kp8
+    wq_bytes = pr.Co * Kp8 + 4 * pr.Co     # E4M3 weight and fp32 row scales
 
     def per_launch(name, cnt):
         if name == "pack_weight":
@@ -113,6 +116,13 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
             # x (NHWC copy), offsets and masks read once, output written once
             return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + pr.Co * Kp * e
                         + bias_bytes, flops=2 * cnt * pr.Co * Kg * P)
+        if name == "quantize_weight_fp8":
+            return dict(bytes=w_bytes + wq_bytes, flops=0)
+        if name == "deform_gather_fp8":
+            return dict(bytes=cnt * (x_img + off_img + msk_img + col_img8), flops=0)
+        if name == "gemm_fp8_bias":
+            return dict(bytes=cnt * (col_img8 + out_img) + wq_bytes + bias_bytes,
+                        flops=2 * cnt * pr.Co * Kg * P)
         if name == "direct":
             # one launch over every image: x, offsets, masks and weight read
             # once, output written once
@@ -145,8 +155,10 @@ def main(argv=None) -> int:
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "gather_gemm", "fused",
-                                                       "window", "depthwise", "direct"],
-                    help="computation path (default: the library's choice)")
+                                                       "window", "depthwise", "direct",
+                                                       "gather_gemm_fp8"],
+                    help="computation path (default: the library's choice; gather_gemm_fp8 "
+                         "computes with E4M3 operands, a reduced-precision result)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph that holds one captured forward (the "
                          "launch mode for small problems) instead of eager forwards")
@@ -193,7 +205,9 @@ def main(argv=None) -> int:
     g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
     path = {"auto": mdcn.MDCN_PATH_AUTO, "gather_gemm": mdcn.MDCN_PATH_GATHER_GEMM,
             "fused": mdcn.MDCN_PATH_FUSED, "window": mdcn.MDCN_PATH_WINDOW,
-            "depthwise": mdcn.MDCN_PATH_DEPTHWISE, "direct": mdcn.MDCN_PATH_DIRECT}[args.path]
+            "depthwise": mdcn.MDCN_PATH_DEPTHWISE, "direct": mdcn.MDCN_PATH_DIRECT,
+            "gather_gemm_fp8": mdcn.MDCN_PATH_GATHER_GEMM_FP8}[args.path]
+    fp8 = args.path == "gather_gemm_fp8"
     op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups,
                           path=path)
     code = mdcn.dtype_code(g["x"].dtype)
@@ -256,7 +270,7 @@ def main(argv=None) -> int:
         cnt = (pr.N / max(1, launches_per_step)
                if name in ("direct", "to_nhwc", "to_channel_blocks", "deform_gather", "gemm_bias",
                            "fused_gather_gemm", "window_gather_gemm", "depthwise_geometry",
-                           "depthwise_direct")
+                           "depthwise_direct", "deform_gather_fp8", "gemm_fp8_bias")
                else 0)
         m = model(name, cnt)
         kernels[name] = dict(launches_per_step=launches_per_step, avg_ms=avg_ms,
@@ -267,10 +281,11 @@ def main(argv=None) -> int:
                              tflops=m["flops"] / (avg_ms * 1e-3) / 1e12)
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dominant]
-    peak_tf = MFMA_PEAK_TFLOPS[dtype]
+    peak_tf = MFMA_PEAK_TFLOPS["fp8" if fp8 else dtype]
     t_hbm = dk["algo_bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = dk["algo_flops_per_launch"] / (peak_tf * 1e12)
-    uses_mfma = dominant in ("gemm_bias", "fused_gather_gemm", "window_gather_gemm")
+    uses_mfma = dominant in ("gemm_bias", "fused_gather_gemm", "window_gather_gemm",
+                             "gemm_fp8_bias")
     if uses_mfma and t_mfma > t_hbm:
         roofline = dict(bound="mfma", achieved=round(dk["tflops"], 2), peak=peak_tf,
                         unit="TFLOP/s", frac=round(dk["tflops"] / peak_tf, 4), traffic=None)
@@ -306,13 +321,14 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": "fp8_e4m3" if fp8 else dtype,
         "data": "synthetic (seeded; OCDNet-shaped stand-in, no dataset or weights)",
         "config": {"workload": args.workload, "N": pr.N, "C": pr.C, "Co": pr.Co,
                    "H": pr.H, "W": pr.W, "kernel": [pr.kh, pr.kw], "stride": list(pr.stride),
                    "padding": list(pr.padding), "dilation": list(pr.dilation),
                    "group": pr.groups, "deformable_group": pr.deformable_groups,
                    "bias": pr.bias, "io_dtype": dtype, "accumulate": "f32",
+                   "operands": "e4m3 (reduced precision)" if fp8 else dtype,
                    "parallelism": "single GPU",
                    "launch": "graph replay" if args.graph else "eager"},
         "hbm_gbs_effective": round(min_bytes / (ms_per_step * 1e-3) / 1e9, 1),

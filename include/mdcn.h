@@ -113,11 +113,25 @@ typedef enum mdcn_path {
                                   each group inside one deformable group; the automatic
                                   choice when its tiles are at least 7/8 full
                                   [plugin guide §五 steps 1-3]                             */
-    MDCN_PATH_DIRECT = 5       /* the whole forward in one launch, one thread per output
+    MDCN_PATH_DIRECT = 5,      /* the whole forward in one launch, one thread per output
                                   element reading x, offsets, masks and weights where they
                                   are; for problems of at most 2^20 multiply-adds (the
                                   automatic choice there), any problem when forced; no
                                   workspace [plugin guide §五 steps 1-3]                   */
+    MDCN_PATH_GATHER_GEMM_FP8 = 6 /* REDUCED PRECISION, never chosen automatically: gather +
+                                  GEMM with both contraction operands in OCP FP8 E4M3 and
+                                  fp32 sums on the gfx950 FP8 matrix cores.  Each column
+                                  value (the modulated bilinear sample) is saturated to
+                                  +-448 and rounded to nearest even E4M3 (values below
+                                  2^-9 vanish: inputs are used unscaled); each output
+                                  channel's weight row is scaled by 2^e, e the largest
+                                  integer with max|row| * 2^e <= 448, rounded the same way,
+                                  and its sums are multiplied by 2^-e before the bias is
+                                  added.  Any dtype and problem the gather + GEMM path
+                                  takes; output in the input dtype.  Results differ from the
+                                  other paths by the E4M3 rounding (about 2^-4 relative per
+                                  operand) [plugin guide §五 steps 1-3 with 8-bit operands;
+                                  the FP8 format is not on the pages]                       */
 } mdcn_path;
 
 typedef struct mdcn_op mdcn_op;
@@ -208,7 +222,8 @@ mdcn_status mdcn_trace_read(mdcn_trace *trace, int32_t i, int32_t *kernel_id, fl
  * the first chunk of x to channels-last / 8-channel blocks, in one launch),
  * "to_nhwc" / "to_channel_blocks" (x of a later chunk), "deform_gather",
  * "gemm_bias", "fused_gather_gemm", "window_gather_gemm",
- * "depthwise_geometry", "depthwise_direct"; "pack_weight" and
+ * "depthwise_geometry", "depthwise_direct", "direct"; for the FP8 path
+ * "quantize_weight_fp8", "deform_gather_fp8", "gemm_fp8_bias"; "pack_weight" and
  * "pack_weight_steps" (standalone weight repacking) are not launched by the
  * forward.  "?" if unknown. */
 const char *mdcn_kernel_name(int32_t kernel_id);

@@ -186,6 +186,8 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     void *xt = ws + plan.xt_off;
     void *col = ws + plan.col_off;
     uint32_t *win_flags = reinterpret_cast<uint32_t *>(ws + plan.flag_off);
+    const bool fp8 = plan.path == Path::GatherGemmFp8;
+    float *wscale = fp8 ? reinterpret_cast<float *>(ws + plan.wpack_off + plan.wscale_off) : nullptr;
     // The weight is repacked (and the window path's flags cleared) in the
     // same launch as the first chunk's x layout change.
     for (int64_t n0 = 0; n0 < p.N; n0 += plan.chunk) {
@@ -194,7 +196,15 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         const char *oc = static_cast<const char *>(offset) + size_t(n0) * off_img;
         const char *mc = static_cast<const char *>(mask) + size_t(n0) * msk_img;
         char *outc = static_cast<char *>(out) + size_t(n0) * out_img;
-        if (n0 == 0)
+        if (n0 == 0 && plan.path == Path::GatherGemmFp8) {
+            err = rec.run(mdcn::K_QUANT_WEIGHT, [&] {
+                return mdcn::launch_quantize_weight(p, plan, weight, wpack, wscale, stream);
+            });
+            if (err != hipSuccess)
+                return MDCN_E_LAUNCH;
+            err = rec.run(mdcn::K_TO_NHWC,
+                          [&] { return mdcn::launch_to_nhwc(p, cnt, xc, xt, stream); });
+        } else if (n0 == 0)
             err = rec.run(plan.path == Path::Window ? mdcn::K_PREP_BLOCKS : mdcn::K_PREP_NHWC,
                           [&] {
                               return mdcn::launch_prep(p, plan, cnt, xc, xt, weight, wpack,
@@ -230,13 +240,13 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
                 return MDCN_E_LAUNCH;
             continue;
         }
-        err = rec.run(mdcn::K_GATHER, [&] {
+        err = rec.run(fp8 ? mdcn::K_GATHER_FP8 : mdcn::K_GATHER, [&] {
             return mdcn::launch_gather(p, plan, cnt, xt, oc, mc, col, stream);
         });
         if (err != hipSuccess)
             return MDCN_E_LAUNCH;
-        err = rec.run(mdcn::K_GEMM, [&] {
-            return mdcn::launch_gemm(p, plan, cnt, wpack, col, bias, outc, stream);
+        err = rec.run(fp8 ? mdcn::K_GEMM_FP8 : mdcn::K_GEMM, [&] {
+            return mdcn::launch_gemm(p, plan, cnt, wpack, col, bias, wscale, outc, stream);
         });
         if (err != hipSuccess)
             return MDCN_E_LAUNCH;
@@ -256,7 +266,7 @@ mdcn_status create_impl(const int32_t stride[2], const int32_t padding[2],
         return st;
     if (path != MDCN_PATH_AUTO && path != MDCN_PATH_GATHER_GEMM &&
         path != MDCN_PATH_DEPTHWISE && path != MDCN_PATH_FUSED && path != MDCN_PATH_WINDOW &&
-        path != MDCN_PATH_DIRECT)
+        path != MDCN_PATH_DIRECT && path != MDCN_PATH_GATHER_GEMM_FP8)
         return MDCN_E_PATH;
     mdcn_op *op = new (std::nothrow) mdcn_op;
     if (!op)
@@ -457,6 +467,9 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_PREP_NHWC: return "prep_nhwc";
     case mdcn::K_PREP_BLOCKS: return "prep_blocks";
     case mdcn::K_DIRECT: return "direct";
+    case mdcn::K_QUANT_WEIGHT: return "quantize_weight_fp8";
+    case mdcn::K_GATHER_FP8: return "deform_gather_fp8";
+    case mdcn::K_GEMM_FP8: return "gemm_fp8_bias";
     }
     return "?";
 }
@@ -525,8 +538,9 @@ mdcn_status mdcn_describe_plan(const mdcn_op *op, mdcn_dtype dtype, const int64_
                           plan.wpack_bytes, plan.xt_bytes_per_image);
         else
             std::snprintf(buf, len,
-                          "path=gather_gemm chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld "
+                          "path=%s chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld "
                           "ws=%zu (wpack=%zu xt/img=%zu col/img=%zu)",
+                          plan.path == Path::GatherGemmFp8 ? "gather_gemm_fp8" : "gather_gemm",
                           (long long)plan.chunk, (long long)p.Kg, (long long)plan.Kp,
                           (long long)p.G, (long long)p.Mg, (long long)p.P, plan.ws_bytes,
                           plan.wpack_bytes, plan.xt_bytes_per_image, plan.col_bytes_per_image);

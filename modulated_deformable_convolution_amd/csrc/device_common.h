@@ -25,6 +25,31 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ half_t from_f32<half_t>(float v) { return (half_t)v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return (bf16_t)v; }
 
+// OCP FP8 E4M3 numbers (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// largest finite value 448; S.1111.111 is NaN), one byte each.  gfx950's
+// v_cvt_pk_fp8_f32 writes this format and rounds to nearest even; it turns
+// magnitudes above 464 into NaN, so values are saturated to +-448 first
+// (NaN stays NaN: the comparison is false for it).
+typedef uint8_t e4m3_t;
+
+__device__ __forceinline__ float sat_e4m3(float v)
+{
+    return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+}
+
+// Four values -> four E4M3 bytes (a in the lowest byte).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
+    return uint32_t(w);
+}
+
+__device__ __forceinline__ e4m3_t to_e4m3(float v)
+{
+    return e4m3_t(__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v), 0.0f, 0, false) & 0xff);
+}
+
 // 16 bytes of T: 4 floats or 8 halves / bf16s.
 template <typename T> struct Vec16 {
     static constexpr int N = 16 / sizeof(T);

@@ -4,6 +4,9 @@
 // tap*dilation + learned offset, bilinear interpolation reading 0 off the
 // image, times the mask, into the column buffer].
 //
+// The FP8 path writes the columns as OCP E4M3 bytes (each value saturated to
+// +-448, rounded to nearest even) instead of elements of T.
+//
 // Layout choice (this library's, not the page's): x is read channels-last
 // (NHWC, prepared by to_nhwc) and the columns are written K-contiguous,
 // col[g][n*P + pix][k*Cg + c'], so that
@@ -73,12 +76,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base,
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, int(n), 0x00020000);
 }
 
+// One column element of output type O: T, or E4M3 for the FP8 path.
+template <typename O> __device__ __forceinline__ O col_elem(float v) { return from_f32<O>(v); }
+template <> __device__ __forceinline__ e4m3_t col_elem<e4m3_t>(float v) { return to_e4m3(v); }
+
 // One output vector: VEC channels (c'..c'+VEC-1 of group g) at (pixel p0+pl,
-// tap k0+kl), the four corners read with buffer loads (0 off the image).
-template <typename T, bool VECTOR>
+// tap k0+kl), the four corners read with buffer loads (0 off the image),
+// written as VEC elements of O (T, or E4M3 bytes for the FP8 path).
+template <typename T, typename O, bool VECTOR>
 __device__ __forceinline__ void gather_item(const GatherArgs &a, const Geo *geo,
                                             __amdgpu_buffer_rsrc_t rs, const char *img,
-                                            T *col_g, int g, int q0, int p0, int k0, int pl,
+                                            O *col_g, int g, int q0, int p0, int k0, int pl,
                                             int kl, int cv)
 {
     constexpr int VEC = VECTOR ? 16 / int(sizeof(T)) : 1;
@@ -89,7 +97,7 @@ __device__ __forceinline__ void gather_item(const GatherArgs &a, const Geo *geo,
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
         acc[e] = 0.0f;
-    T *dst = col_g + size_t(p0 + pl) * a.Kp + (k0 + kl) * a.Cg + cv * VEC;
+    O *dst = col_g + size_t(p0 + pl) * a.Kp + (k0 + kl) * a.Cg + cv * VEC;
     if constexpr (VECTOR) {
         uint4 v[4];
 #pragma unroll
@@ -101,26 +109,38 @@ __device__ __forceinline__ void gather_item(const GatherArgs &a, const Geo *geo,
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             vec_fma<T>(acc, v[s], gd.wt[s]);
-        Vec16<T> o;
+        if constexpr (sizeof(O) == 1) {
+            // VEC E4M3 bytes: 8 (fp16/bf16 input) or 4 (fp32)
+            uint32_t w[VEC / 4];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            o.e[e] = from_f32<T>(acc[e]);
-        store16(dst, o);
+            for (int h = 0; h < VEC / 4; ++h)
+                w[h] = pack4_e4m3(acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]);
+            if constexpr (VEC == 8)
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+            else
+                *reinterpret_cast<uint32_t *>(dst) = w[0];
+        } else {
+            Vec16<T> o;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                o.e[e] = from_f32<T>(acc[e]);
+            store16(dst, o);
+        }
     } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             if (gd.off[s] != kOffImage)
                 acc[0] = fmaf(gd.wt[s],
                               to_f32(*reinterpret_cast<const T *>(img + gd.off[s] + cb)), acc[0]);
-        dst[0] = from_f32<T>(acc[0]);
+        dst[0] = col_elem<O>(acc[0]);
     }
 }
 
-template <typename T, bool VECTOR>
+template <typename T, typename O, bool VECTOR>
 __global__ __launch_bounds__(kThreads) void deform_gather_kernel(const T *__restrict__ xt,
                                                                  const T *__restrict__ off,
                                                                  const T *__restrict__ msk,
-                                                                 T *__restrict__ col, GatherArgs a)
+                                                                 O *__restrict__ col, GatherArgs a)
 {
     constexpr int VEC = VECTOR ? 16 / int(sizeof(T)) : 1;
     extern __shared__ __attribute__((aligned(16))) char geo_raw[];
@@ -185,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void deform_gather_kernel(const T *__rest
     const size_t img_bytes = size_t(a.H) * a.W * elem_c;
     const char *img = reinterpret_cast<const char *>(xt) + size_t(nl) * img_bytes;
     const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(img, uint32_t(img_bytes));
-    T *col_g = col + (size_t(g) * a.cnt + nl) * size_t(a.P) * a.Kp;
+    O *col_g = col + (size_t(g) * a.cnt + nl) * size_t(a.P) * a.Kp;
 
     if (CV <= kThreads && kThreads % CV == 0) {
         // Each thread keeps one channel vector and walks (pixel, tap) rows.
@@ -194,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void deform_gather_kernel(const T *__rest
         int r = int(threadIdx.x) / CV;                   // row = pl*nk + kl
         int pl = r / nk, kl = r - (r / nk) * nk;
         while (pl < np) {
-            gather_item<T, VECTOR>(a, geo, rs, img, col_g, g, q0, p0, k0, pl, kl, cv);
+            gather_item<T, O, VECTOR>(a, geo, rs, img, col_g, g, q0, p0, k0, pl, kl, cv);
             kl += stride;
             while (kl >= nk) {
                 kl -= nk;
@@ -206,7 +226,8 @@ __global__ __launch_bounds__(kThreads) void deform_gather_kernel(const T *__rest
         for (int it = int(threadIdx.x); it < items; it += kThreads) {
             const int cv = it % CV;
             const int kl = (it / CV) % nk;
-            gather_item<T, VECTOR>(a, geo, rs, img, col_g, g, q0, p0, k0, it / (CV * nk), kl, cv);
+            gather_item<T, O, VECTOR>(a, geo, rs, img, col_g, g, q0, p0, k0, it / (CV * nk), kl,
+                                      cv);
         }
     }
     // Zero each row's padding [Kg, Kp) (once per row: by the first tap chunk).
@@ -214,12 +235,12 @@ __global__ __launch_bounds__(kThreads) void deform_gather_kernel(const T *__rest
     if (kch == 0) {
         for (int it = int(threadIdx.x); it < np * pad; it += kThreads) {
             const int pl = it / pad;
-            col_g[size_t(p0 + pl) * a.Kp + a.Kg + it % pad] = T(0);
+            col_g[size_t(p0 + pl) * a.Kp + a.Kg + it % pad] = O(0);
         }
     }
 }
 
-template <typename T>
+template <typename T, typename O>
 hipError_t gather_t(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
                     const void *offset, const void *mask, void *col, hipStream_t s)
 {
@@ -253,13 +274,13 @@ hipError_t gather_t(const Problem &p, const Plan &plan, int64_t cnt, const void 
     const size_t lds = size_t(a.nq) * kc * tp * sizeof(Geo);
     const dim3 grid(unsigned(uint64_t(p.G) * cnt * a.kchunks * a.tiles));
     if (vec)
-        hipLaunchKernelGGL((deform_gather_kernel<T, true>), grid, dim3(kThreads), lds, s,
+        hipLaunchKernelGGL((deform_gather_kernel<T, O, true>), grid, dim3(kThreads), lds, s,
                            static_cast<const T *>(xt), static_cast<const T *>(offset),
-                           static_cast<const T *>(mask), static_cast<T *>(col), a);
+                           static_cast<const T *>(mask), static_cast<O *>(col), a);
     else
-        hipLaunchKernelGGL((deform_gather_kernel<T, false>), grid, dim3(kThreads), lds, s,
+        hipLaunchKernelGGL((deform_gather_kernel<T, O, false>), grid, dim3(kThreads), lds, s,
                            static_cast<const T *>(xt), static_cast<const T *>(offset),
-                           static_cast<const T *>(mask), static_cast<T *>(col), a);
+                           static_cast<const T *>(mask), static_cast<O *>(col), a);
     return hipGetLastError();
 }
 
@@ -268,10 +289,19 @@ hipError_t gather_t(const Problem &p, const Plan &plan, int64_t cnt, const void 
 hipError_t launch_gather(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
                          const void *offset, const void *mask, void *col, hipStream_t stream)
 {
+    if (plan.path == Path::GatherGemmFp8) {
+        switch (p.dtype) {
+        case MDCN_F32: return gather_t<float, e4m3_t>(p, plan, cnt, xt, offset, mask, col, stream);
+        case MDCN_F16: return gather_t<half_t, e4m3_t>(p, plan, cnt, xt, offset, mask, col, stream);
+        case MDCN_BF16:
+            return gather_t<bf16_t, e4m3_t>(p, plan, cnt, xt, offset, mask, col, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (p.dtype) {
-    case MDCN_F32: return gather_t<float>(p, plan, cnt, xt, offset, mask, col, stream);
-    case MDCN_F16: return gather_t<half_t>(p, plan, cnt, xt, offset, mask, col, stream);
-    case MDCN_BF16: return gather_t<bf16_t>(p, plan, cnt, xt, offset, mask, col, stream);
+    case MDCN_F32: return gather_t<float, float>(p, plan, cnt, xt, offset, mask, col, stream);
+    case MDCN_F16: return gather_t<half_t, half_t>(p, plan, cnt, xt, offset, mask, col, stream);
+    case MDCN_BF16: return gather_t<bf16_t, bf16_t>(p, plan, cnt, xt, offset, mask, col, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -28,7 +28,11 @@
 // MFMAs instead of delaying the reads.
 //
 //   f16 / bf16: one v_mfma_f32_32x32x16_{f16,bf16} per 16-byte fragment pair;
-//   f32:        four v_mfma_f32_32x32x2_f32 per 16-byte fragment pair.
+//   f32:        four v_mfma_f32_32x32x2_f32 per 16-byte fragment pair;
+//   FP8 path:   E4M3 operands (the quantized weight and columns), one
+//               v_mfma_f32_32x32x64_f8f6f4 per two 16-byte fragment pairs,
+//               and the epilogue multiplies each output channel's sums by its
+//               weight row's scale 2^-e before the bias.
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -65,10 +69,12 @@ __device__ __forceinline__ void issue_step(char *stage_base, __amdgpu_buffer_rsr
     }
 }
 
-template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int STEP>
+// OP: the operand element type, T (or E4M3 bytes for the FP8 path, whose
+// rscale holds each weight row's scale); T: bias and output.
+template <typename T, typename OP, int BM, int BN, int WAVES_M, int WAVES_N, int STEP>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
-    const T *__restrict__ A, const T *__restrict__ B, const T *__restrict__ bias,
-    T *__restrict__ out, GemmArgs a)
+    const OP *__restrict__ A, const OP *__restrict__ B, const T *__restrict__ bias,
+    const float *__restrict__ rscale, T *__restrict__ out, GemmArgs a)
 {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
     // wave index as a scalar: LDS destinations of the loads must be wave-uniform
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
 
-    const uint32_t row_bytes = uint32_t(a.Kp) * uint32_t(sizeof(T));
+    const uint32_t row_bytes = uint32_t(a.Kp) * uint32_t(sizeof(OP));
     const char *Ag = reinterpret_cast<const char *>(A) + size_t(g) * a.Mg * row_bytes;
     const char *Bg = reinterpret_cast<const char *>(B) + size_t(g) * a.Ncols * row_bytes;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ag, uint32_t(a.Mg) * row_bytes);
@@ -127,25 +133,37 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
         const int stage = st & 1;
         __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of step st have landed
         __syncthreads();                 // ... and everyone's; stage^1 is free again
-        StepFrags<FM, FN> f;             // all of step st's fragments, before the DMA
-        load_step_frags<FM, FN>(f, smem + stage * STAGE_BYTES + wm * WTM * STEP,
-                                smem + stage * STAGE_BYTES + (BM + wn * WTN) * STEP, lane);
-        if (st + 1 < steps)
-            issue_step<BM, BN, NW, STEP>(smem + (stage ^ 1) * STAGE_BYTES, ra, rb, voff, wave,
-                                         st + 1);
-        mfma_step_frags<T, FM, FN>(acc, f);
+        // all of step st's fragments, before the DMA
+        const char *sa = smem + stage * STAGE_BYTES + wm * WTM * STEP;
+        const char *sb = smem + stage * STAGE_BYTES + (BM + wn * WTN) * STEP;
+        if constexpr (sizeof(OP) == 1) {
+            StepFragsE4m3<FM, FN> f;
+            load_step_frags_e4m3<FM, FN>(f, sa, sb, lane);
+            if (st + 1 < steps)
+                issue_step<BM, BN, NW, STEP>(smem + (stage ^ 1) * STAGE_BYTES, ra, rb, voff,
+                                             wave, st + 1);
+            mfma_step_frags_e4m3<FM, FN>(acc, f);
+        } else {
+            StepFrags<FM, FN> f;
+            load_step_frags<FM, FN>(f, sa, sb, lane);
+            if (st + 1 < steps)
+                issue_step<BM, BN, NW, STEP>(smem + (stage ^ 1) * STAGE_BYTES, ra, rb, voff,
+                                             wave, st + 1);
+            mfma_step_frags<T, FM, FN>(acc, f);
+        }
     }
 
     // Epilogue through LDS: bias in fp32, one rounding, 16-byte stores.
     static_assert(NW * 32 * (WTN + 4) * 4 <= 2 * STAGE_BYTES, "epilogue slices must fit in LDS");
     __syncthreads();                                   // operand stages no longer needed
-    const EpilogueArgs e{g, m0, n0, a.Mg, a.Ncols, a.P, a.Co, a.has_bias, a.vec_out};
-    epilogue_store<T, WTM, WTN>(acc, smem, bias, out, e, wm, wn, wave, lane);
+    const EpilogueArgs e{g, m0, n0, a.Mg, a.Ncols, a.P, a.Co, a.has_bias, a.vec_out, rscale};
+    epilogue_store<T, WTM, WTN, (sizeof(OP) == 1)>(acc, smem, bias, out, e, wm, wn, wave, lane);
 }
 
-template <typename T, int BM, int BN, int WM, int WN>
+template <typename T, typename OP, int BM, int BN, int WM, int WN>
 hipError_t gemm_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                    const void *col, const void *bias, void *out, hipStream_t s)
+                    const void *col, const void *bias, const float *rscale, void *out,
+                    hipStream_t s)
 {
     constexpr int STEP = 128;
     GemmArgs a;
@@ -159,30 +177,30 @@ hipError_t gemm_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void 
     a.has_bias = bias != nullptr;
     a.vec_out = (p.P % (16 / int(sizeof(T))) == 0) && reinterpret_cast<uintptr_t>(out) % 16 == 0;
     const uint64_t blocks = uint64_t(p.G) * a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((gemm_bias_kernel<T, BM, BN, WM, WN, STEP>), dim3(uint32_t(blocks)),
-                       dim3(WM * WN * 64), 0, s, static_cast<const T *>(wpack),
-                       static_cast<const T *>(col), static_cast<const T *>(bias),
+    hipLaunchKernelGGL((gemm_bias_kernel<T, OP, BM, BN, WM, WN, STEP>), dim3(uint32_t(blocks)),
+                       dim3(WM * WN * 64), 0, s, static_cast<const OP *>(wpack),
+                       static_cast<const OP *>(col), static_cast<const T *>(bias), rscale,
                        static_cast<T *>(out), a);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename OP>
 hipError_t gemm_t(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                  const void *col, const void *bias, void *out, hipStream_t s)
+                  const void *col, const void *bias, const float *rs, void *out, hipStream_t s)
 {
     switch (plan.gemm_tile) {
     case GemmTile::M256_N256_W2x4:
-        return gemm_cfg<T, 256, 256, 2, 4>(p, plan, cnt, wpack, col, bias, out, s);
+        return gemm_cfg<T, OP, 256, 256, 2, 4>(p, plan, cnt, wpack, col, bias, rs, out, s);
     case GemmTile::M256_N128_W4x2:
-        return gemm_cfg<T, 256, 128, 4, 2>(p, plan, cnt, wpack, col, bias, out, s);
+        return gemm_cfg<T, OP, 256, 128, 4, 2>(p, plan, cnt, wpack, col, bias, rs, out, s);
     case GemmTile::M128_N256_W2x4:
-        return gemm_cfg<T, 128, 256, 2, 4>(p, plan, cnt, wpack, col, bias, out, s);
+        return gemm_cfg<T, OP, 128, 256, 2, 4>(p, plan, cnt, wpack, col, bias, rs, out, s);
     case GemmTile::M128_N128_W2x2:
-        return gemm_cfg<T, 128, 128, 2, 2>(p, plan, cnt, wpack, col, bias, out, s);
+        return gemm_cfg<T, OP, 128, 128, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, s);
     case GemmTile::M128_N64_W2x2:
-        return gemm_cfg<T, 128, 64, 2, 2>(p, plan, cnt, wpack, col, bias, out, s);
+        return gemm_cfg<T, OP, 128, 64, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, s);
     case GemmTile::M64_N128_W2x2:
-        return gemm_cfg<T, 64, 128, 2, 2>(p, plan, cnt, wpack, col, bias, out, s);
+        return gemm_cfg<T, OP, 64, 128, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, s);
     }
     return hipErrorInvalidValue;
 }
@@ -190,12 +208,26 @@ hipError_t gemm_t(const Problem &p, const Plan &plan, int64_t cnt, const void *w
 }  // namespace
 
 hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                       const void *col, const void *bias, void *out, hipStream_t stream)
+                       const void *col, const void *bias, const float *wscale, void *out,
+                       hipStream_t stream)
 {
+    if (plan.path == Path::GatherGemmFp8) {
+        switch (p.dtype) {
+        case MDCN_F32:
+            return gemm_t<float, e4m3_t>(p, plan, cnt, wpack, col, bias, wscale, out, stream);
+        case MDCN_F16:
+            return gemm_t<half_t, e4m3_t>(p, plan, cnt, wpack, col, bias, wscale, out, stream);
+        case MDCN_BF16:
+            return gemm_t<bf16_t, e4m3_t>(p, plan, cnt, wpack, col, bias, wscale, out, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (p.dtype) {
-    case MDCN_F32: return gemm_t<float>(p, plan, cnt, wpack, col, bias, out, stream);
-    case MDCN_F16: return gemm_t<half_t>(p, plan, cnt, wpack, col, bias, out, stream);
-    case MDCN_BF16: return gemm_t<bf16_t>(p, plan, cnt, wpack, col, bias, out, stream);
+    case MDCN_F32: return gemm_t<float, float>(p, plan, cnt, wpack, col, bias, nullptr, out, stream);
+    case MDCN_F16:
+        return gemm_t<half_t, half_t>(p, plan, cnt, wpack, col, bias, nullptr, out, stream);
+    case MDCN_BF16:
+        return gemm_t<bf16_t, bf16_t>(p, plan, cnt, wpack, col, bias, nullptr, out, stream);
     }
     return hipErrorInvalidValue;
 }

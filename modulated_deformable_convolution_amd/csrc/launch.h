@@ -23,7 +23,10 @@ enum KernelId : int32_t {
     K_PREP_NHWC = 10,
     K_PREP_BLOCKS = 11,
     K_DIRECT = 12,
-    K_COUNT = 13
+    K_QUANT_WEIGHT = 13,
+    K_GATHER_FP8 = 14,
+    K_GEMM_FP8 = 15,
+    K_COUNT = 16
 };
 
 // weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
@@ -58,13 +61,23 @@ hipError_t launch_to_nhwc(const Problem &p, int64_t cnt, const void *x, void *xt
                           hipStream_t stream);
 
 // Deformable im2col of cnt images: col [G][cnt*P][Kp], row (n, pixel),
-// column kk = k*Cg + c', value bilinear0(x[n][g*Cg + c'], sample) * mask.
+// column kk = k*Cg + c', value bilinear0(x[n][g*Cg + c'], sample) * mask
+// (FP8 path: as an E4M3 byte, saturated to +-448).
 hipError_t launch_gather(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
                          const void *offset, const void *mask, void *col, hipStream_t stream);
 
-// out[n][g*Mg + m][pix] = sum_kk wpack[g][m][kk] * col[g][n*P + pix][kk] (+ bias).
+// out[n][g*Mg + m][pix] = sum_kk wpack[g][m][kk] * col[g][n*P + pix][kk] (+ bias);
+// FP8 path: E4M3 operands and the sums times wscale[g*Mg + m] before the bias
+// (wscale null otherwise).
 hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                       const void *col, const void *bias, void *out, hipStream_t stream);
+                       const void *col, const void *bias, const float *wscale, void *out,
+                       hipStream_t stream);
+
+// FP8 path: weight [Co][Cg][kh][kw] -> wq [Co][Kp] E4M3 bytes, tap-major
+// (kk = k*Cg + c', zero for kk >= Kg), row co scaled by 2^e before rounding
+// (e the largest integer with max|w[co]| * 2^e <= 448), wscale[co] = 2^-e.
+hipError_t launch_quantize_weight(const Problem &p, const Plan &plan, const void *weight,
+                                  void *wq, float *wscale, hipStream_t stream);
 
 // Fused deformable gather + grouped GEMM + bias of cnt images:
 // out[n][g*Mg + m][pix] from the packed weight, NHWC x, offset and mask.

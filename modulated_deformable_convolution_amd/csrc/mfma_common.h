@@ -1,5 +1,6 @@
 // mfma_common.h -- pieces shared by the GEMM and the fused gather-GEMM:
-// the per-dtype MFMA step on 16-byte fragments, the swizzled 128-byte-row
+// the per-dtype MFMA step on 16-byte fragments (and the E4M3 step on pairs
+// of them), the swizzled 128-byte-row
 // LDS tile layout, one pipeline step of MFMAs over such a tile, and the
 // LDS-staged epilogue (bias in fp32, one rounding, 16-byte stores).
 //
@@ -51,6 +52,12 @@ template <> struct Mma<float> {
         return c;
     }
 };
+
+typedef int int8v __attribute__((ext_vector_type(8)));
+
+// (v_mfma_f32_32x32x64_f8f6f4 through the scaled builtin with zero scale
+// operands, which is the unscaled instruction; A and B bytes pair up by
+// (lane, byte), so any lane -> k mapping that A and B share is valid.)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -159,17 +166,70 @@ __device__ __forceinline__ void mfma_step_frags(float16v (&acc)[FM][FN],
                 acc[i][j] = Mma<T>::step(f.a[kg][i], f.b[kg][j], acc[i][j]);
 }
 
+// One 128-byte K step of E4M3 operands: 128 k per row, two MFMAs of 64 k
+// per 32x32 tile.  Lane l of MFMA kp reads 16-byte chunks 4*kp + l/32 and
+// 4*kp + 2 + l/32 of its row (the same chunks for A and B) straight into the
+// two halves of one 8-register operand.
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+template <int FM, int FN>
+struct StepFragsE4m3 {
+    int8v a[2][FM], b[2][FN];
+};
+
+__device__ __forceinline__ int8v load_pair(const char *row, int c0, int c1, int sw)
+{
+    const int4v lo = *reinterpret_cast<const int4v *>(row + (c0 ^ sw) * 16);
+    const int4v hi = *reinterpret_cast<const int4v *>(row + (c1 ^ sw) * 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void load_step_frags_e4m3(StepFragsE4m3<FM, FN> &f, const char *sA,
+                                                     const char *sB, int lane)
+{
+    const char *pa = sA + (lane & 31) * 128;
+    const char *pb = sB + (lane & 31) * 128;
+    const int sw = (lane >> 1) & 7;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            f.a[kp][i] = load_pair(pa + i * 32 * 128, 4 * kp + half, 4 * kp + 2 + half, sw);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            f.b[kp][j] = load_pair(pb + j * 32 * 128, 4 * kp + half, 4 * kp + 2 + half, sw);
+    }
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_step_frags_e4m3(float16v (&acc)[FM][FN],
+                                                     const StepFragsE4m3<FM, FN> &f)
+{
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    f.a[kp][i], f.b[kp][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+}
+
 struct EpilogueArgs {
     int g, m0, n0;            // group, first weight row and first column of the tile
     int Mg, Ncols, P, Co;
     int has_bias, vec_out;    // vec_out: P and `out` allow 16-byte stores
+    const float *rscale;      // SCALED epilogues: factor of each output channel's sums
 };
 
 // Writes the wave's block of accumulators (rows wm*WTM.., columns wn*WTN..
 // of the tile) to out[n][g*Mg + m][pix] for column n*P + pix, adding bias in
-// fp32.  Staged through the wave's own slice of `smem`, which the caller
-// must no longer need (a barrier before the call).
-template <typename T, int WTM, int WTN>
+// fp32 (SCALED: the sums times rscale[g*Mg + m] first).  Staged through the
+// wave's own slice of `smem`, which the caller must no longer need (a
+// barrier before the call).
+template <typename T, int WTM, int WTN, bool SCALED = false>
 __device__ __forceinline__ void epilogue_store(float16v (&acc)[WTM / 32][WTN / 32], char *smem,
                                                const T *__restrict__ bias, T *__restrict__ out,
                                                const EpilogueArgs &e, int wm, int wn, int wave,
@@ -201,13 +261,14 @@ __device__ __forceinline__ void epilogue_store(float16v (&acc)[WTM / 32][WTN / 3
                 const int m = mb + rl, n = nb + cl;
                 if (m < e.Mg && n < e.Ncols) {
                     const float bv = e.has_bias ? to_f32(bias[size_t(e.g) * e.Mg + m]) : 0.0f;
+                    const float rs = SCALED ? e.rscale[size_t(e.g) * e.Mg + m] : 1.0f;
                     const int img = n / e.P;
                     const int pix = n - img * e.P;
                     const float *sp = slice + rl * SROW + cl;
                     Vec16<T> o;
 #pragma unroll
                     for (int t = 0; t < EV; ++t)
-                        o.e[t] = from_f32<T>(sp[t] + bv);
+                        o.e[t] = from_f32<T>(SCALED ? fmaf(sp[t], rs, bv) : sp[t] + bv);
                     store16(out + (size_t(img) * e.Co + size_t(e.g) * e.Mg + m) * e.P + pix, o);
                 }
             }
@@ -217,10 +278,12 @@ __device__ __forceinline__ void epilogue_store(float16v (&acc)[WTM / 32][WTN / 3
                 const int m = mb + rl, n = nb + cl;
                 if (m < e.Mg && n < e.Ncols) {
                     const float bv = e.has_bias ? to_f32(bias[size_t(e.g) * e.Mg + m]) : 0.0f;
+                    const float rs = SCALED ? e.rscale[size_t(e.g) * e.Mg + m] : 1.0f;
                     const int img = n / e.P;
                     const int pix = n - img * e.P;
+                    const float v = slice[rl * SROW + cl];
                     out[(size_t(img) * e.Co + size_t(e.g) * e.Mg + m) * e.P + pix] =
-                        from_f32<T>(slice[rl * SROW + cl] + bv);
+                        from_f32<T>(SCALED ? fmaf(v, rs, bv) : v + bv);
                 }
             }
         }

@@ -451,6 +451,9 @@ mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
     case MDCN_PATH_GATHER_GEMM:
         *out = Path::GatherGemm;
         return MDCN_OK;
+    case MDCN_PATH_GATHER_GEMM_FP8:
+        *out = Path::GatherGemmFp8;
+        return MDCN_OK;
     case MDCN_PATH_DEPTHWISE:
         if (p.Cg != 1)
             return MDCN_E_PATH;
@@ -579,15 +582,25 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
         *out = plan;
         return MDCN_OK;
     }
-    plan.wpack_bytes = align_up(size_t(p.G * p.Mg * plan.Kp) * p.elem, kAlign);
+    // FP8: one-byte operands, so a 128-byte K step is 128 elements; the row
+    // scales follow the weight bytes
+    const bool fp8 = plan.path == Path::GatherGemmFp8;
+    const size_t op_elem = fp8 ? 1 : p.elem;
+    if (fp8)
+        plan.Kp = round_up(p.Kg, 128);
+    plan.wpack_bytes = align_up(size_t(p.G * p.Mg * plan.Kp) * op_elem, kAlign);
+    if (fp8) {
+        plan.wscale_off = plan.wpack_bytes;
+        plan.wpack_bytes += align_up(size_t(p.Co) * sizeof(float), kAlign);
+    }
     plan.xt_bytes_per_image = align_up(size_t(p.H * p.W * p.C) * p.elem, kAlign);
-    plan.col_bytes_per_image = align_up(size_t(p.G * p.P * plan.Kp) * p.elem, kAlign);
+    plan.col_bytes_per_image = align_up(size_t(p.G * p.P * plan.Kp) * op_elem, kAlign);
     // Default chunk: as many images as fit a 256 MiB column buffer, at least
     // one; also keep every launch's element count within 32-bit indexing.
     int64_t by_budget = int64_t(kColumnBudget / std::max<size_t>(plan.col_bytes_per_image, 1));
     // (byte offsets within one launch's columns must fit in 31 bits)
     int64_t by_index = kMaxPerImage /
-                       std::max<int64_t>(p.G * std::max<int64_t>(p.P, 1) * plan.Kp * int64_t(p.elem), 1);
+                       std::max<int64_t>(p.G * std::max<int64_t>(p.P, 1) * plan.Kp * int64_t(op_elem), 1);
     int64_t chunk = std::max<int64_t>(1, std::min<int64_t>({std::max<int64_t>(p.N, 1),
                                                            by_budget, by_index}));
     const size_t per_image = plan.xt_bytes_per_image + plan.col_bytes_per_image;

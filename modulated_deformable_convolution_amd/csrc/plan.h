@@ -34,7 +34,7 @@ struct Problem {
     int64_t sh, sw, ph, pw, dh, dw;
 };
 
-enum class Path { GatherGemm, Depthwise, Fused, Window, Direct };
+enum class Path { GatherGemm, Depthwise, Fused, Window, Direct, GatherGemmFp8 };
 
 // Workgroup tile of the GEMM (rows of the packed weight x columns) and its
 // wave grid; every wave owns a block of 32x32 accumulator tiles.
@@ -78,6 +78,8 @@ constexpr size_t kWindowSlotBytes = size_t(256) * 256 * 4;   // fp32 256 x 256 t
 
 // Workspace layout (all offsets 256-byte aligned):
 //   gather + GEMM: [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
+//   FP8:           [E4M3 weight: Co x Kp bytes] [row scales: Co floats] [x in NHWC: chunk images]
+//                  [E4M3 columns: G x chunk*P x Kp bytes], Kp a multiple of 128
 //   fused:         [packed weight: G x Mg x Kp] [x in NHWC: chunk images]
 //   window:        [packed weight] [x in 8-channel blocks: chunk images]
 //                  [partial sums: slots x 256 KiB] [flags: slots x 4 bytes]
@@ -85,8 +87,9 @@ constexpr size_t kWindowSlotBytes = size_t(256) * 256 * 4;   // fp32 256 x 256 t
 struct Plan {
     Path path;
     int64_t chunk;               // images per pass through gather + GEMM
-    int64_t Kp;                  // contraction length padded to a multiple of 64
-    size_t wpack_off, wpack_bytes;
+    int64_t Kp;                  // contraction length padded to 128 bytes (64 or 32 elements; FP8: 128)
+    size_t wpack_off, wpack_bytes;   // (FP8: the weight bytes and the row scales after them)
+    size_t wscale_off;           // FP8: offset of the Co fp32 row scales
     size_t xt_off, xt_bytes_per_image;
     size_t col_off, col_bytes_per_image;
     size_t geo_bytes_per_image;  // depthwise: sampling geometry of one image (0: none)

@@ -40,6 +40,7 @@ MDCN_PATH_DEPTHWISE = 2
 MDCN_PATH_FUSED = 3
 MDCN_PATH_WINDOW = 4
 MDCN_PATH_DIRECT = 5
+MDCN_PATH_GATHER_GEMM_FP8 = 6
 
 EXPORTED = [
     "mdcn_create", "mdcn_create_with_path", "mdcn_destroy", "mdcn_output_shape",

@@ -115,6 +115,32 @@ def generate(problem: Problem, dtype: str = "f32", seed: int = 0):
     return {k: (v.to(t).contiguous() if v is not None else None) for k, v in out.items()}
 
 
+GRID = (0.0, 0.25, 0.5, 1.0, 1.5, 2.0, 3.0, -0.25, -0.5, -1.0, -1.5, -2.0, -3.0)
+
+
+def generate_grid(problem: Problem, dtype: str = "f32", seed: int = 0):
+    """Inputs on coarse dyadic grids, for checks that need every rounding of
+    the reduced-precision path to be an exact operation: x and the weight
+    (times 2^-5) and bias (times 2^-3) drawn uniformly from GRID, integer
+    offsets in [-2, 2], masks from {0, 0.5, 1}.  Every such value is exact in
+    fp32, fp16, bf16 and the 8-bit E4M3 format."""
+    g = torch.Generator().manual_seed(seed)
+    s = problem.shapes()
+    grid = torch.tensor(GRID)
+
+    def pick(shape, values):
+        return values[torch.randint(0, len(values), shape, generator=g)]
+
+    x = pick(s["x"], grid)
+    offset = torch.randint(-2, 3, s["offset"], generator=g).to(torch.float32)
+    mask = pick(s["mask"], torch.tensor([0.0, 0.5, 1.0]))
+    weight = pick(s["weight"], grid) * 2.0 ** -5
+    bias = pick(s["bias"], grid) * 2.0 ** -3 if problem.bias else None
+    t = DTYPES[dtype]
+    out = {"x": x, "offset": offset, "mask": mask, "weight": weight, "bias": bias}
+    return {k: (v.to(t).contiguous() if v is not None else None) for k, v in out.items()}
+
+
 # The five benchmark workloads (synthetic stand-ins for OCDNet-style stages).
 TINY = Problem(N=1, C=4, Co=4, H=8, W=8, bias=True, offset_dist=("normal", 1.0))
 OCDNET_STAGE = Problem(N=4, C=256, Co=256, H=160, W=160, bias=False,

@@ -432,3 +432,33 @@ def test_window_path_plan():
         assert tile == 1 and margin == 3
     finally:
         del os.environ["MDCN_WIN_MARGIN"], os.environ["MDCN_WIN_TILE"]
+
+
+def test_fp8_path_plan():
+    """The FP8 path: E4M3 weight (Kp = Kg padded to 128 bytes) plus one fp32
+    scale per output channel, x in NHWC of the input dtype, E4M3 columns;
+    all 4 images of the OCDNet-like stage fit the 256 MiB column budget.
+    Never the automatic choice."""
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_GATHER_GEMM_FP8)
+    b, mb = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, DIMS)
+    col_img = 2304 * 25600                        # one byte per column value
+    xt_img = 256 * 160 * 160 * 2
+    wq = 256 * 2304 + 256 * 4                     # weight bytes + row scales (aligned)
+    assert mb == 256 + wq + col_img + xt_img
+    assert b == 256 + wq + 4 * (col_img + xt_img)
+    desc = mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16, DIMS)
+    assert desc.startswith("path=gather_gemm_fp8") and "chunk=4" in desc and "Kp=2304" in desc
+    # a contraction that is not a multiple of 128: padded (Kg = 9 * 20 = 180)
+    d = [1, 20, 16, 16, 1, 18, 16, 16, 1, 9, 16, 16, 8, 20, 3, 3]
+    assert "Kp=256" in mdcn.mdcn_describe_plan(op, mdcn.MDCN_F32, d)
+    assert "Kp=192" in mdcn.mdcn_describe_plan(
+        mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_GATHER_GEMM), mdcn.MDCN_F16, d)
+    # every dtype; the automatic choice never takes it
+    for dt in (mdcn.MDCN_F32, mdcn.MDCN_BF16):
+        assert mdcn.mdcn_describe_plan(op, dt, DIMS).startswith("path=gather_gemm_fp8")
+    auto = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    for dt in (mdcn.MDCN_F32, mdcn.MDCN_F16, mdcn.MDCN_BF16):
+        assert "fp8" not in mdcn.mdcn_describe_plan(auto, dt, DIMS)
+        assert "fp8" not in mdcn.mdcn_describe_plan(auto, dt, d)
+    names = [mdcn.mdcn_kernel_name(i) for i in range(16)]
+    assert {"quantize_weight_fp8", "deform_gather_fp8", "gemm_fp8_bias"} <= set(names)
