@@ -76,10 +76,18 @@ static double bilinear_zero(const double *X, int64_t H, int64_t W, double h, dou
          + fy         * fx         * pixel_or_zero(X, H, W, y0 + 1, x0 + 1);
 }
 
-/* One output element out[n][co][ho][wo], straight from the definition. */
+double mdcn_oracle_e4m3(double v);
+
+/* One output element out[n][co][ho][wo], straight from the definition.
+ * FP8 mode (F1-F3 below) when scale is not NULL: weight then holds the
+ * rounded scaled weights q(w * 2^e), each column value is rounded with
+ * mdcn_oracle_e4m3, and the sum is multiplied by scale[co] = 2^-e before the
+ * bias.  *abs_sum (if not NULL) gets the sum of |weight * column| (times
+ * scale[co] in FP8 mode). */
 static double output_element(const double *x, const double *offset, const double *mask,
                              const double *weight, const double *bias, const int64_t *p,
-                             int64_t n, int64_t co, int64_t ho, int64_t wo)
+                             int64_t n, int64_t co, int64_t ho, int64_t wo,
+                             const double *scale, double *abs_sum)
 {
     const int64_t C = p[P_C], H = p[P_H], W = p[P_W], Co = p[P_CO];
     const int64_t kh = p[P_KH], kw = p[P_KW], Ho = p[P_HO], Wo = p[P_WO];
@@ -92,7 +100,7 @@ static double output_element(const double *x, const double *offset, const double
     const int64_t HoWo = Ho * Wo;
     const int64_t pix = ho * Wo + wo;
 
-    double acc = 0.0;
+    double acc = 0.0, sa = 0.0;
     for (int64_t cl = 0; cl < Cg; ++cl) {
         const int64_t c = g * Cg + cl;
         const int64_t q = c / Cdg;
@@ -109,10 +117,17 @@ static double output_element(const double *x, const double *offset, const double
                 const double h = (double)(ho * p[P_SH] - p[P_PH] + i * p[P_DH]) + dh;  /* R1 */
                 const double w = (double)(wo * p[P_SW] - p[P_PW] + j * p[P_DW]) + dw;
                 const double val = bilinear_zero(plane, H, W, h, w) * m;            /* R7 */
-                acc += weight[((co * Cg + cl) * kh + i) * kw + j] * val;
+                const double col = scale ? mdcn_oracle_e4m3(val) : val;               /* F1 */
+                const double prod = weight[((co * Cg + cl) * kh + i) * kw + j] * col;
+                acc += prod;
+                sa += fabs(prod);
             }
         }
     }
+    if (abs_sum)
+        *abs_sum = scale ? sa * scale[co] : sa;
+    if (scale)
+        acc *= scale[co];                                                         /* F3 */
     if (bias)
         acc += bias[co];
     return acc;
@@ -144,7 +159,8 @@ int mdcn_oracle_forward(const double *x, const double *offset, const double *mas
             for (int64_t ho = 0; ho < Ho; ++ho)
                 for (int64_t wo = 0; wo < Wo; ++wo)
                     out[((n * Co + co) * Ho + ho) * Wo + wo] =
-                        output_element(x, offset, mask, weight, bias, p, n, co, ho, wo);
+                        output_element(x, offset, mask, weight, bias, p, n, co, ho, wo,
+                                       NULL, NULL);
     return 0;
 }
 
@@ -169,7 +185,7 @@ int mdcn_oracle_points(const double *x, const double *offset, const double *mask
         const int64_t ho = r % Ho; r /= Ho;
         const int64_t co = r % Co; r /= Co;
         const int64_t n = r;
-        out[t] = output_element(x, offset, mask, weight, bias, p, n, co, ho, wo);
+        out[t] = output_element(x, offset, mask, weight, bias, p, n, co, ho, wo, NULL, NULL);
     }
     return 0;
 }
@@ -239,53 +255,6 @@ int mdcn_oracle_fp8_row_exponent(const double *row, int64_t n)
     return e;
 }
 
-/* One output element in the FP8 mode (F1-F3).  qw is the quantized weight
- * q(w * 2^e) of every weight, scale[co] = 2^-e of its row.  *abs_sum gets
- * 2^-e * sum |q(w) * q(column)| (a scale for the contraction's rounding). */
-static double output_element_fp8(const double *x, const double *offset, const double *mask,
-                                  const double *qw, const double *scale, const double *bias,
-                                  const int64_t *p, int64_t n, int64_t co, int64_t ho,
-                                  int64_t wo, double *abs_sum)
-{
-    const int64_t C = p[P_C], H = p[P_H], W = p[P_W], Co = p[P_CO];
-    const int64_t kh = p[P_KH], kw = p[P_KW], Ho = p[P_HO], Wo = p[P_WO];
-    const int64_t G = p[P_GROUP], DG = p[P_DGROUP];
-    const int64_t K = kh * kw;
-    const int64_t Cg = C / G, Mg = Co / G, Cdg = C / DG;
-    const int64_t g = co / Mg;
-    const int64_t HoWo = Ho * Wo;
-    const int64_t pix = ho * Wo + wo;
-
-    double acc = 0.0, sa = 0.0;
-    for (int64_t cl = 0; cl < Cg; ++cl) {
-        const int64_t c = g * Cg + cl;
-        const int64_t q = c / Cdg;
-        const double *plane = x + (n * C + c) * H * W;
-        for (int64_t i = 0; i < kh; ++i) {
-            for (int64_t j = 0; j < kw; ++j) {
-                const int64_t k = i * kw + j;
-                const int64_t off_h_ch = n * 2 * DG * K + q * 2 * K + 2 * k;
-                const int64_t mask_ch = n * DG * K + q * K + k;
-                const double dh = offset[off_h_ch * HoWo + pix];
-                const double dw = offset[(off_h_ch + 1) * HoWo + pix];
-                const double m = mask[mask_ch * HoWo + pix];
-                const double h = (double)(ho * p[P_SH] - p[P_PH] + i * p[P_DH]) + dh;
-                const double w = (double)(wo * p[P_SW] - p[P_PW] + j * p[P_DW]) + dw;
-                const double col = mdcn_oracle_e4m3(bilinear_zero(plane, H, W, h, w) * m);
-                const double prod = qw[((co * Cg + cl) * kh + i) * kw + j] * col;
-                acc += prod;
-                sa += fabs(prod);
-            }
-        }
-    }
-    if (abs_sum)
-        *abs_sum = sa * scale[co];
-    acc *= scale[co];
-    if (bias)
-        acc += bias[co];
-    return acc;
-}
-
 /* F2 for every row: qw (Co*Cg*K values) and scale (Co values). */
 static void quantize_weight(const double *weight, const int64_t *p, double *qw, double *scale)
 {
@@ -322,8 +291,8 @@ int mdcn_oracle_points_fp8(const double *x, const double *offset, const double *
         const int64_t ho = r % Ho; r /= Ho;
         const int64_t co = r % Co; r /= Co;
         const int64_t n = r;
-        out[t] = output_element_fp8(x, offset, mask, qw, scale, bias, p, n, co, ho, wo,
-                                    abs_sum ? abs_sum + t : NULL);
+        out[t] = output_element(x, offset, mask, qw, bias, p, n, co, ho, wo, scale,
+                                abs_sum ? abs_sum + t : NULL);
     }
     return 0;
 }

@@ -278,14 +278,15 @@ MUTANTS = {
     "exponent_threshold": ("int e = (f <= 0.875) ? 9 - ex : 8 - ex;",
                            "int e = (f < 0.75) ? 9 - ex : 8 - ex;"),
     "scale_not_undone": ("acc *= scale[co];", "acc *= 1.0;"),
-    "column_not_rounded": ("const double col = mdcn_oracle_e4m3(bilinear_zero(plane, H, W, h, w) * m);",
-                           "const double col = bilinear_zero(plane, H, W, h, w) * m;"),
-    "mask_after_rounding": ("const double col = mdcn_oracle_e4m3(bilinear_zero(plane, H, W, h, w) * m);",
-                            "const double col = mdcn_oracle_e4m3(bilinear_zero(plane, H, W, h, w)) * m;"),
+    "abs_sum_unscaled": ("*abs_sum = scale ? sa * scale[co] : sa;", "*abs_sum = sa;"),
+    "column_not_rounded": ("const double col = scale ? mdcn_oracle_e4m3(val) : val;",
+                           "const double col = val;"),
+    "mask_after_rounding": ("const double col = scale ? mdcn_oracle_e4m3(val) : val;",
+                            "const double col = scale ? mdcn_oracle_e4m3(val / m) * m : val;"),
     "weight_not_rounded": ("qw[co * Cg * K + t] = mdcn_oracle_e4m3(ldexp(row[t], e));",
                            "qw[co * Cg * K + t] = ldexp(row[t], e);"),
-    "fp8_bias_dropped": ("    acc *= scale[co];\n    if (bias)\n        acc += bias[co];",
-                         "    acc *= scale[co];\n    if (bias)\n        acc += 0.0;"),
+    "fp8_bias_dropped": ("    if (bias)\n        acc += bias[co];",
+                         "    if (bias)\n        acc += scale ? 0.0 : bias[co];"),
 }
 
 
