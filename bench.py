@@ -34,6 +34,16 @@ DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
 # profiles/*memory_counters.md), valid only for the kernel sources they were
 # taken on (sha256 of the listed files, first 16 hex digits).
 MEASURED_TRAFFIC = {
+    ("deform_gather_fp8", "ocdnet_n4_c256_160x160", "f16"): {
+        "bytes": (40547 * 2 + 230400) * 1024,
+        "sources": ('gather.hip', 'device_common.h', 'plan.cpp', 'plan.h'),
+        "sha": "830b69d6f3c86deb",
+    },
+    ("gemm_fp8_bias", "ocdnet_n4_c256_160x160", "f16"): {
+        "bytes": (119923 * 2 + 51200) * 1024,
+        "sources": ('gemm.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp'),
+        "sha": "d894354be95dd419",
+    },
     ("window_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
         "bytes": (133655 * 2 + 130189) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'launch.h', 'plan.cpp', 'plan.h'),
