@@ -223,7 +223,8 @@ mdcn_status mdcn_trace_read(mdcn_trace *trace, int32_t i, int32_t *kernel_id, fl
  * "to_nhwc" / "to_channel_blocks" (x of a later chunk), "deform_gather",
  * "gemm_bias", "fused_gather_gemm", "window_gather_gemm",
  * "depthwise_geometry", "depthwise_direct", "direct"; for the FP8 path
- * "quantize_weight_fp8", "deform_gather_fp8", "gemm_fp8_bias"; "pack_weight" and
+ * "prep_nhwc_fp8" (the weight rounded to E4M3 and the first chunk of x to
+ * channels-last), "deform_gather_fp8", "gemm_fp8_bias"; "pack_weight" and
  * "pack_weight_steps" (standalone weight repacking) are not launched by the
  * forward.  "?" if unknown. */
 const char *mdcn_kernel_name(int32_t kernel_id);

@@ -196,19 +196,14 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         const char *oc = static_cast<const char *>(offset) + size_t(n0) * off_img;
         const char *mc = static_cast<const char *>(mask) + size_t(n0) * msk_img;
         char *outc = static_cast<char *>(out) + size_t(n0) * out_img;
-        if (n0 == 0 && plan.path == Path::GatherGemmFp8) {
-            err = rec.run(mdcn::K_QUANT_WEIGHT, [&] {
-                return mdcn::launch_quantize_weight(p, plan, weight, wpack, wscale, stream);
-            });
-            if (err != hipSuccess)
-                return MDCN_E_LAUNCH;
-            err = rec.run(mdcn::K_TO_NHWC,
-                          [&] { return mdcn::launch_to_nhwc(p, cnt, xc, xt, stream); });
-        } else if (n0 == 0)
-            err = rec.run(plan.path == Path::Window ? mdcn::K_PREP_BLOCKS : mdcn::K_PREP_NHWC,
+        if (n0 == 0)
+            err = rec.run(plan.path == Path::Window          ? mdcn::K_PREP_BLOCKS
+                          : plan.path == Path::GatherGemmFp8 ? mdcn::K_PREP_NHWC_FP8
+                                                             : mdcn::K_PREP_NHWC,
                           [&] {
                               return mdcn::launch_prep(p, plan, cnt, xc, xt, weight, wpack,
-                                                       win_flags, int(plan.win_slots), stream);
+                                                       win_flags, int(plan.win_slots), wscale,
+                                                       stream);
                           });
         else if (plan.path == Path::Window)
             err = rec.run(mdcn::K_TO_BLOCKS,
@@ -467,7 +462,7 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_PREP_NHWC: return "prep_nhwc";
     case mdcn::K_PREP_BLOCKS: return "prep_blocks";
     case mdcn::K_DIRECT: return "direct";
-    case mdcn::K_QUANT_WEIGHT: return "quantize_weight_fp8";
+    case mdcn::K_PREP_NHWC_FP8: return "prep_nhwc_fp8";
     case mdcn::K_GATHER_FP8: return "deform_gather_fp8";
     case mdcn::K_GEMM_FP8: return "gemm_fp8_bias";
     }

@@ -23,7 +23,7 @@ enum KernelId : int32_t {
     K_PREP_NHWC = 10,
     K_PREP_BLOCKS = 11,
     K_DIRECT = 12,
-    K_QUANT_WEIGHT = 13,
+    K_PREP_NHWC_FP8 = 13,
     K_GATHER_FP8 = 14,
     K_GEMM_FP8 = 15,
     K_COUNT = 16
@@ -47,10 +47,13 @@ hipError_t launch_to_channel_blocks(const Problem &p, int64_t cnt, const void *x
 
 // The first chunk's set-up in one launch: x of cnt images to channels-last
 // (window path: to 8-channel blocks) and the weight repacked for the plan's
-// path (window path: step-major, with nflags flags cleared).
+// path (window path: step-major, with nflags flags cleared; FP8 path: each
+// output channel's row scaled by 2^e and rounded to E4M3, wpack [Co][Kp]
+// bytes tap-major, e the largest integer with max|w[co]| * 2^e <= 448, and
+// wscale[co] = 2^-e).
 hipError_t launch_prep(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
                        const void *weight, void *wpack, uint32_t *flags, int nflags,
-                       hipStream_t stream);
+                       float *wscale, hipStream_t stream);
 
 // The whole forward of all N images, one thread per output element.
 hipError_t launch_direct(const Problem &p, const void *x, const void *offset, const void *mask,
@@ -73,11 +76,6 @@ hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const vo
                        const void *col, const void *bias, const float *wscale, void *out,
                        hipStream_t stream);
 
-// FP8 path: weight [Co][Cg][kh][kw] -> wq [Co][Kp] E4M3 bytes, tap-major
-// (kk = k*Cg + c', zero for kk >= Kg), row co scaled by 2^e before rounding
-// (e the largest integer with max|w[co]| * 2^e <= 448), wscale[co] = 2^-e.
-hipError_t launch_quantize_weight(const Problem &p, const Plan &plan, const void *weight,
-                                  void *wq, float *wscale, hipStream_t stream);
 
 // Fused deformable gather + grouped GEMM + bias of cnt images:
 // out[n][g*Mg + m][pix] from the packed weight, NHWC x, offset and mask.

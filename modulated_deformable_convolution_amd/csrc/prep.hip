@@ -1,6 +1,7 @@
 // prep.hip -- layout kernels: x to channels-last (NHWC) or to 8-channel
 // blocks ([C/8][H][W][8] per image), and the weight repacked in the order a
-// path's contraction walks it.  All of them only move data.
+// path's contraction walks it (for the FP8 path also scaled and rounded to
+// E4M3).  Apart from that rounding they only move data.
 #include <algorithm>
 
 #include "device_common.h"
@@ -164,17 +165,63 @@ __global__ __launch_bounds__(256) void pack_weight_steps_kernel(const T *__restr
                     nflags);
 }
 
+// The FP8 path's weight, one workgroup (256 threads) per output channel co:
+// the row's exponent e, the largest integer with max|w[co]| * 2^e <= 448
+// (0 for a row with no nonzero finite maximum; clamped to [-126, 126]),
+// wq[co][kk] = E4M3(w * 2^e) in tap-major order (kk = k*Cg + c', zero for
+// kk >= Kg) and wscale[co] = 2^-e, which the GEMM epilogue applies to the
+// row's sums.  Scaling by a power of two is exact, so the only rounding is
+// E4M3's own.  `red` is 4 floats of LDS.
+template <typename T>
+__device__ __forceinline__ void quantize_row(const T *__restrict__ w, e4m3_t *__restrict__ wq,
+                                             float *__restrict__ wscale, int co, int Kg, int Kp,
+                                             int Cg, int K, float *red)
+{
+    const T *row = w + size_t(co) * Kg;              // weight [Co][Cg][kh][kw]: Kg per row
+    float mx = 0.0f;
+    for (int t = int(threadIdx.x); t < Kg; t += 256)  // contiguous reads
+        mx = fmaxf(mx, fabsf(to_f32(row[t])));        // fmaxf skips NaN
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    if (mx > 0.0f && !__builtin_isinf(mx)) {
+        int ex;
+        const float f = frexpf(mx, &ex);              // mx = f * 2^ex, f in [0.5, 1)
+        e = (f <= 0.875f) ? 9 - ex : 8 - ex;          // 448 = 0.875 * 2^9
+        e = min(126, max(-126, e));
+    }
+    e4m3_t *dst = wq + size_t(co) * Kp;
+    for (int kk = int(threadIdx.x); kk < Kp; kk += 256) {   // the row is in L1 by now
+        e4m3_t q = 0;
+        if (kk < Kg) {
+            const int k = kk / Cg;
+            const int cl = kk - k * Cg;
+            q = to_e4m3(ldexpf(to_f32(row[cl * K + k]), e));
+        }
+        dst[kk] = q;
+    }
+    if (threadIdx.x == 0)
+        wscale[co] = ldexpf(1.0f, -e);
+}
+
 // Both set-up jobs of a forward in one launch (for small problems the
 // launches cost more than the work): the first `nt` workgroups transpose
 // x (tile b -> (b % gx, b / gx % gy, b / (gx*gy))), the rest repack the
 // weight (PK 1: [G][Mg][Kp] tap-major; PK 2: the window path's step-major
-// planes, and its hand-over flags cleared).
+// planes, and its hand-over flags cleared; PK 3: the FP8 path's E4M3 rows
+// and scales, one workgroup per row).
 struct PrepArgs {
     const void *x;
     void *xt;
     const void *w;
     void *wp;
     uint32_t *flags;
+    float *wscale;
     int C, HW, gx, gy, nt;
     int total, Kp, Kg, Cg, K, Mg, S, nflags;
 };
@@ -182,7 +229,7 @@ struct PrepArgs {
 template <typename T, bool BLK, bool VEC, int PK>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
 {
-    __shared__ T tile[kTile][kTile + 1];
+    __shared__ __attribute__((aligned(16))) T tile[kTile][kTile + 1];
     const int b = int(blockIdx.x);
     if (b < a.nt) {
         const int bx = b % a.gx, by = (b / a.gx) % a.gy, bz = b / (a.gx * a.gy);
@@ -192,6 +239,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
         else
             transpose_tile<T, BLK>(static_cast<const T *>(a.x), static_cast<T *>(a.xt), a.C,
                                    a.HW, bx, by, bz, tile);
+        return;
+    }
+    if constexpr (PK == 3) {
+        quantize_row(static_cast<const T *>(a.w), static_cast<e4m3_t *>(a.wp), a.wscale,
+                     b - a.nt, a.Kg, a.Kp, a.Cg, a.K, reinterpret_cast<float *>(&tile[0][0]));
         return;
     }
     const int t = (b - a.nt) * 256 + int(threadIdx.x);
@@ -296,17 +348,22 @@ namespace {
 
 template <typename T, bool BLK, int PK>
 hipError_t prep_t(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
-                  const void *w, void *wp, uint32_t *flags, int nflags, hipStream_t s)
+                  const void *w, void *wp, uint32_t *flags, int nflags, float *wscale,
+                  hipStream_t s)
 {
     const int HW = int(p.H * p.W);
     PrepArgs a{};
-    a.x = x; a.xt = xt; a.w = w; a.wp = wp; a.flags = flags;
+    a.x = x; a.xt = xt; a.w = w; a.wp = wp; a.flags = flags; a.wscale = wscale;
     a.C = int(p.C); a.HW = HW;
     a.gx = (HW + kTile - 1) / kTile;
     a.gy = int((p.C + kTile - 1) / kTile);
     a.Cg = int(p.Cg); a.K = int(p.K);
     int64_t npack;
-    if constexpr (PK == 1) {
+    if constexpr (PK == 3) {
+        a.Kp = int(plan.Kp);
+        a.Kg = int(p.Kg);
+        npack = p.Co * 256;                   // one workgroup per row
+    } else if constexpr (PK == 1) {
         a.total = int(p.Co * plan.Kp);
         a.Kp = int(plan.Kp);
         a.Kg = int(p.Kg);
@@ -340,28 +397,36 @@ hipError_t prep_t(const Problem &p, const Plan &plan, int64_t cnt, const void *x
 
 template <typename T>
 hipError_t prep_dtype(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
-                      const void *w, void *wp, uint32_t *flags, int nflags, hipStream_t s)
+                      const void *w, void *wp, uint32_t *flags, int nflags, float *wscale,
+                      hipStream_t s)
 {
     if (plan.path == Path::Window)
-        return prep_t<T, true, 2>(p, plan, cnt, x, xt, w, wp, flags, nflags, s);
-    return prep_t<T, false, 1>(p, plan, cnt, x, xt, w, wp, flags, nflags, s);
+        return prep_t<T, true, 2>(p, plan, cnt, x, xt, w, wp, flags, nflags, nullptr, s);
+    if (plan.path == Path::GatherGemmFp8)
+        return prep_t<T, false, 3>(p, plan, cnt, x, xt, w, wp, nullptr, 0, wscale, s);
+    return prep_t<T, false, 1>(p, plan, cnt, x, xt, w, wp, flags, nflags, nullptr, s);
 }
 
 }  // namespace
 
 hipError_t launch_prep(const Problem &p, const Plan &plan, int64_t cnt, const void *x, void *xt,
                        const void *weight, void *wpack, uint32_t *flags, int nflags,
-                       hipStream_t stream)
+                       float *wscale, hipStream_t stream)
 {
+    if (plan.path == Path::GatherGemmFp8 && !wscale)
+        return hipErrorInvalidValue;
     if (plan.path == Path::Window && p.C % 8 != 0)
         return hipErrorInvalidValue;
     switch (p.dtype) {
     case MDCN_F32:
-        return prep_dtype<float>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, stream);
+        return prep_dtype<float>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, wscale,
+                                stream);
     case MDCN_F16:
-        return prep_dtype<half_t>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, stream);
+        return prep_dtype<half_t>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, wscale,
+                                stream);
     case MDCN_BF16:
-        return prep_dtype<bf16_t>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, stream);
+        return prep_dtype<bf16_t>(p, plan, cnt, x, xt, weight, wpack, flags, nflags, wscale,
+                                stream);
     }
     return hipErrorInvalidValue;
 }

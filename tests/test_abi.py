@@ -461,4 +461,4 @@ def test_fp8_path_plan():
         assert "fp8" not in mdcn.mdcn_describe_plan(auto, dt, DIMS)
         assert "fp8" not in mdcn.mdcn_describe_plan(auto, dt, d)
     names = [mdcn.mdcn_kernel_name(i) for i in range(16)]
-    assert {"quantize_weight_fp8", "deform_gather_fp8", "gemm_fp8_bias"} <= set(names)
+    assert {"prep_nhwc_fp8", "deform_gather_fp8", "gemm_fp8_bias"} <= set(names)

@@ -156,7 +156,7 @@ def test_fp8_differs_from_exact_by_quantization_only():
 
 def test_fp8_chunked_workspace_matches_default():
     """With the least workspace (one image per chunk) the weight is quantized
-    once, by the first chunk, and the result is bit-identical."""
+    once, in the first chunk's set-up launch, and the result is bit-identical."""
     pr = CASES["pointwise"]
     inp = workloads.generate(pr, "f16", seed=5)
     op = make_op(pr)
@@ -170,10 +170,10 @@ def test_fp8_chunked_workspace_matches_default():
     b = run(pr, inp, workspace_bytes=least, trace=tr)
     assert np.array_equal(a, b)
     names = [n for n, _ in tr.read()]
-    assert names[0] == "quantize_weight_fp8"
-    assert names.count("quantize_weight_fp8") == 1
+    assert names[0] == "prep_nhwc_fp8"
+    assert names.count("prep_nhwc_fp8") == 1
     assert names.count("deform_gather_fp8") == names.count("gemm_fp8_bias") == pr.N
-    assert names.count("to_nhwc") == pr.N
+    assert names.count("to_nhwc") == pr.N - 1          # the first chunk's is in prep_nhwc_fp8
 
 
 def test_fp8_zero_mask_gives_bias_exactly():
