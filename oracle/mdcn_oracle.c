@@ -303,3 +303,115 @@ void mdcn_oracle_e4m3_array(const double *v, int64_t n, double *out)
     for (int64_t t = 0; t < n; ++t)
         out[t] = mdcn_oracle_e4m3(v[t]);
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass: the gradients of a scalar loss L with respect to x, offset,
+ * mask, weight and bias, given g = dL/dout ([N][Co][Ho][Wo]).  The pages
+ * describe only the forward; these are the derivatives of its definition
+ * above (R1-R8), read as:
+ *   B1 the bilinear sample is differentiated on the cell that floor()
+ *      selects: with h = y0 + a, w = x0 + b (a, b in [0, 1)),
+ *      d sample/d h = (1-b)(v10 - v00) + b(v11 - v01),
+ *      d sample/d w = (1-a)(v01 - v00) + a(v11 - v10),
+ *      corners off the image counting as 0 (at integer h or w this is the
+ *      derivative from above);
+ *   B2 a sample outside the open window (h <= -1, h >= H, w <= -1, w >= W,
+ *      or not finite) is 0 with zero derivatives;
+ *   B3 the mask, weight and bias enter linearly, so their gradients are the
+ *      sums of g times what multiplies them; x enters through the four
+ *      corner weights times mask times weight.
+ * ------------------------------------------------------------------------ */
+
+/* Bilinear sample of plane X at (h, w) and its two partial derivatives
+ * (B1, B2); dh, dw receive the derivatives. */
+static double bilinear_grad(const double *X, int64_t H, int64_t W, double h, double w,
+                            double *dh, double *dw)
+{
+    *dh = 0.0;
+    *dw = 0.0;
+    if (!(h > -1.0 && h < (double)H && w > -1.0 && w < (double)W))
+        return 0.0;
+    const double hf = floor(h), wf = floor(w);
+    const int64_t y0 = (int64_t)hf, x0 = (int64_t)wf;
+    const double a = h - hf, b = w - wf;
+    const double v00 = pixel_or_zero(X, H, W, y0, x0);
+    const double v01 = pixel_or_zero(X, H, W, y0, x0 + 1);
+    const double v10 = pixel_or_zero(X, H, W, y0 + 1, x0);
+    const double v11 = pixel_or_zero(X, H, W, y0 + 1, x0 + 1);
+    *dh = (1.0 - b) * (v10 - v00) + b * (v11 - v01);
+    *dw = (1.0 - a) * (v01 - v00) + a * (v11 - v10);
+    return (1.0 - a) * (1.0 - b) * v00 + (1.0 - a) * b * v01 + a * (1.0 - b) * v10 + a * b * v11;
+}
+
+/* Adds s times the four corner weights of the sample at (h, w) to the
+ * corners of plane GX that lie on the image (B1, B2, B3). */
+static void scatter_corners(double *GX, int64_t H, int64_t W, double h, double w, double s)
+{
+    if (!(h > -1.0 && h < (double)H && w > -1.0 && w < (double)W))
+        return;
+    const double hf = floor(h), wf = floor(w);
+    const int64_t y0 = (int64_t)hf, x0 = (int64_t)wf;
+    const double a = h - hf, b = w - wf;
+    const double cw[4] = {(1.0 - a) * (1.0 - b), (1.0 - a) * b, a * (1.0 - b), a * b};
+    const int64_t cy[4] = {y0, y0, y0 + 1, y0 + 1}, cx[4] = {x0, x0 + 1, x0, x0 + 1};
+    for (int t = 0; t < 4; ++t)
+        if (cy[t] >= 0 && cy[t] < H && cx[t] >= 0 && cx[t] < W)
+            GX[cy[t] * W + cx[t]] += s * cw[t];
+}
+
+/* All five gradients.  gx, goff, gmask, gw have the shapes of x, offset,
+ * mask, weight; gb has Co values (may be NULL).  Sequential (the scatter
+ * into gx has no fixed owner).  Returns 0, or -1 for an unsupported
+ * description. */
+int mdcn_oracle_backward(const double *x, const double *offset, const double *mask,
+                         const double *weight, const double *grad_out, const int64_t *p,
+                         double *gx, double *goff, double *gmask, double *gw, double *gb)
+{
+    const int64_t N = p[P_N], C = p[P_C], H = p[P_H], W = p[P_W], Co = p[P_CO];
+    const int64_t kh = p[P_KH], kw = p[P_KW], Ho = p[P_HO], Wo = p[P_WO];
+    const int64_t G = p[P_GROUP], DG = p[P_DGROUP];
+    if (G <= 0 || DG <= 0 || C % G || Co % G || C % DG)
+        return -1;
+    const int64_t K = kh * kw, Cg = C / G, Mg = Co / G, Cdg = C / DG, HoWo = Ho * Wo;
+    for (int64_t t = 0; t < N * C * H * W; ++t) gx[t] = 0.0;
+    for (int64_t t = 0; t < N * 2 * DG * K * HoWo; ++t) goff[t] = 0.0;
+    for (int64_t t = 0; t < N * DG * K * HoWo; ++t) gmask[t] = 0.0;
+    for (int64_t t = 0; t < Co * Cg * K; ++t) gw[t] = 0.0;
+    if (gb)
+        for (int64_t t = 0; t < Co; ++t) gb[t] = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t co = 0; co < Co; ++co)
+            for (int64_t ho = 0; ho < Ho; ++ho)
+                for (int64_t wo = 0; wo < Wo; ++wo) {
+                    const int64_t pix = ho * Wo + wo;
+                    const double g = grad_out[(n * Co + co) * HoWo + pix];
+                    if (gb)
+                        gb[co] += g;
+                    const int64_t grp = co / Mg;
+                    for (int64_t cl = 0; cl < Cg; ++cl) {
+                        const int64_t c = grp * Cg + cl;
+                        const int64_t q = c / Cdg;
+                        const double *plane = x + (n * C + c) * H * W;
+                        for (int64_t i = 0; i < kh; ++i)
+                            for (int64_t j = 0; j < kw; ++j) {
+                                const int64_t k = i * kw + j;
+                                const int64_t oh = (n * 2 * DG * K + q * 2 * K + 2 * k) * HoWo + pix;
+                                const int64_t ow = oh + HoWo;
+                                const int64_t mi = (n * DG * K + q * K + k) * HoWo + pix;
+                                const double m = mask[mi];
+                                const double h = (double)(ho * p[P_SH] - p[P_PH] + i * p[P_DH]) + offset[oh];
+                                const double w = (double)(wo * p[P_SW] - p[P_PW] + j * p[P_DW]) + offset[ow];
+                                const int64_t wi = ((co * Cg + cl) * kh + i) * kw + j;
+                                double dh, dw;
+                                const double v = bilinear_grad(plane, H, W, h, w, &dh, &dw);
+                                const double gwt = g * weight[wi];       /* dL/d(modulated sample) */
+                                gw[wi] += g * v * m;
+                                gmask[mi] += gwt * v;
+                                goff[oh] += gwt * m * dh;
+                                goff[ow] += gwt * m * dw;
+                                scatter_corners(gx + (n * C + c) * H * W, H, W, h, w, gwt * m);
+                            }
+                    }
+                }
+    return 0;
+}

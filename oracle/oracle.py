@@ -52,6 +52,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mdcn_oracle_e4m3_array.restype = None
     lib.mdcn_oracle_fp8_row_exponent.argtypes = [dp, ctypes.c_int64]
     lib.mdcn_oracle_fp8_row_exponent.restype = ctypes.c_int
+    lib.mdcn_oracle_backward.argtypes = [dp, dp, dp, dp, dp, ip, dp, dp, dp, dp, dp]
+    lib.mdcn_oracle_backward.restype = ctypes.c_int
     lib.mdcn_oracle_max_threads.argtypes = []
     lib.mdcn_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -204,3 +206,25 @@ def forward_fp8(x, offset, mask, weight, bias=None, stride=1, padding=0, dilatio
                                    dilation, groups, deformable_groups, lib=lib)
     shape = (N, Co, Ho, Wo)
     return out.reshape(shape), asum.reshape(shape)
+
+
+# --- backward (B1-B3 in mdcn_oracle.c) ----------------------------------------
+
+def backward(x, offset, mask, weight, grad_out, with_bias=True, stride=1, padding=0,
+             dilation=1, groups=1, deformable_groups=1, lib: ctypes.CDLL | None = None):
+    """Gradients of sum(grad_out * out) with respect to x, offset, mask,
+    weight and (with_bias) bias, float64, as a dict."""
+    lib = lib or load_library()
+    x, offset, mask, weight, grad_out = map(_f64, (x, offset, mask, weight, grad_out))
+    p = problem(x.shape, offset.shape, weight.shape, stride, padding, dilation,
+                groups, deformable_groups)
+    out = {"x": np.empty_like(x), "offset": np.empty_like(offset), "mask": np.empty_like(mask),
+           "weight": np.empty_like(weight),
+           "bias": np.empty(weight.shape[0]) if with_bias else None}
+    rc = lib.mdcn_oracle_backward(_ptr(x), _ptr(offset), _ptr(mask), _ptr(weight),
+                                  _ptr(grad_out), p.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                  _ptr(out["x"]), _ptr(out["offset"]), _ptr(out["mask"]),
+                                  _ptr(out["weight"]), _ptr(out["bias"]))
+    if rc != 0:
+        raise ValueError("oracle: unsupported problem %s" % (p.tolist(),))
+    return out
