@@ -115,17 +115,24 @@ MUTANTS = {
 }
 
 
+BACKWARD_MARK = " * Backward pass:"
+
+
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, fixture):
     before, after = MUTANTS[name]
     with open(oracle.SOURCE) as f:
         src = f.read()
-    assert src.count(before) == 1, "mutation anchor not found once: %r" % before
+    # these checks exercise the forward: plant the mistake in the forward's
+    # code (the backward section, with similar lines, follows it)
+    cut = src.index(BACKWARD_MARK)
+    head, tail = src[:cut], src[cut:]
+    assert head.count(before) == 1, "mutation anchor not found once: %r" % before
     with tempfile.TemporaryDirectory() as d:
         path = os.path.join(d, "mutant.c")
         with open(path, "w") as f:
-            f.write(src.replace(before, after))
+            f.write(head.replace(before, after) + tail)
         so = oracle.compile_library(path, os.path.join(d, "libmutant.so"))
         lib = oracle.load_library(so)
         try:
