@@ -174,6 +174,8 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph that holds one captured forward (the "
                          "launch mode for small problems) instead of eager forwards")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (mdcn_backward, fp32) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte device buffer --steps times (a plain copy "
                          "of known size, to scale memory-traffic counters) and exit")
@@ -210,6 +212,8 @@ def main(argv=None) -> int:
 
     pr, dtypes = workloads.WORKLOADS[args.workload]
     dtype = args.dtype or ("f16" if "f16" in dtypes else "bf16" if "bf16" in dtypes else dtypes[0])
+    if args.backward:
+        return bench_backward(args, pr)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -349,6 +353,118 @@ def main(argv=None) -> int:
         "kernels": {k: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+def backward_model(pr):
+    """Algorithmic bytes and flops of one launch of each backward kernel
+    (fp32; the per-image kernels cover one image)."""
+    e = 4
+    Ho, Wo = pr.out_hw()
+    P = Ho * Wo
+    K = pr.kh * pr.kw
+    Cg, G, dg = pr.C // pr.groups, pr.groups, pr.deformable_groups
+    Kg = Cg * K
+    Kp = (Kg + 63) // 64 * 64
+    x_img = pr.C * pr.H * pr.W * e
+    om_img = 3 * dg * K * P * e
+    table = {
+        "bwd_zero": dict(bytes=x_img, flops=0),        # per image: the NHWC grad_x buffer
+        "pack_weight": dict(bytes=pr.Co * Kg * e + pr.Co * Kp * e, flops=0),
+        "bwd_to_nchw": dict(bytes=2 * x_img, flops=0),
+        "bwd_bias": dict(bytes=pr.N * pr.Co * P * e + pr.Co * e, flops=0),
+        "to_nhwc": dict(bytes=2 * x_img, flops=0),
+        "deform_gather": dict(bytes=x_img + om_img + G * P * Kp * e, flops=0),
+        "bwd_weight_gemm": dict(bytes=pr.Co * P * e + G * P * Kp * e + pr.Co * Kp * e,
+                                flops=2 * pr.Co * Kg * P),
+        "bwd_col_gemm": dict(bytes=pr.Co * Kp * e + pr.Co * P * e + G * P * Kp * e,
+                             flops=2 * pr.Co * Kg * P),
+        "bwd_sample": dict(bytes=2 * x_img + 2 * om_img + G * P * Kp * e, flops=0),
+        "bwd_weight_out": dict(bytes=2 * pr.Co * Kg * e, flops=0),
+    }
+    return table
+
+
+def bench_backward(args, pr):
+    """The backward pass on the workload's shapes in fp32: gradients of all
+    five inputs from a random grad_out.  One JSON line like the forward's;
+    `value` is 2x the forward's effective flops (the two contractions) per
+    second."""
+    import torch
+    from modulated_deformable_convolution_amd import mdcn, workloads
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workloads.generate(pr, "f32", seed=0)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+    ho, wo = pr.out_hw()
+    go = torch.randn((pr.N, pr.Co, ho, wo), generator=torch.Generator().manual_seed(1)).to(dev)
+    op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups)
+    dims = mdcn.dims_of(g["x"], g["offset"], g["mask"], g["weight"])
+    wsb = mdcn.mdcn_backward_workspace_bytes(op, mdcn.MDCN_F32, dims)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(g["x"]), torch.empty_like(g["offset"]), torch.empty_like(g["mask"]),
+            torch.empty_like(g["weight"]), torch.empty(pr.Co, device=dev)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(trace=None):
+        st = mdcn.mdcn_backward(op, mdcn.MDCN_F32, dims, g["x"].data_ptr(),
+                                g["offset"].data_ptr(), g["mask"].data_ptr(),
+                                g["weight"].data_ptr(), go.data_ptr(),
+                                *[t.data_ptr() for t in outs], pr.Co, ws.data_ptr(), ws.numel(),
+                                stream.cuda_stream, trace)
+        if st != mdcn.MDCN_OK:
+            raise mdcn.MdcnError(st, "mdcn_backward")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    trace = mdcn.Trace(capacity=(8 * pr.N + 8) * args.steps + 64)
+    for _ in range(args.steps):
+        step(trace)
+    torch.cuda.synchronize()
+    per = {}
+    for name, ms in trace.read():
+        d = per.setdefault(name, [0, 0.0])
+        d[0] += 1
+        d[1] += ms
+    model = backward_model(pr)
+    kernels = {}
+    for name, (count, total) in per.items():
+        avg = total / count
+        m = model[name]
+        kernels[name] = dict(launches_per_step=count / args.steps, avg_ms=round(avg, 6),
+                             ms_per_step=round(total / args.steps, 6),
+                             algo_bytes_per_launch=m["bytes"], algo_flops_per_launch=m["flops"],
+                             gbs=round(m["bytes"] / (avg * 1e-3) / 1e9, 1),
+                             tflops=round(m["flops"] / (avg * 1e-3) / 1e12, 3))
+    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dominant]
+    if dk["algo_flops_per_launch"]:
+        # a VALU fp32 contraction: the published fp32 vector peak
+        roofline = dict(bound="alu", achieved=dk["tflops"], peak=157.3, unit="TFLOP/s",
+                        frac=round(dk["tflops"] / 157.3, 4), traffic=None, kernel=dominant)
+    else:
+        roofline = dict(bound="hbm", achieved=dk["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(dk["gbs"] / HBM_PEAK_GBS, 4), traffic=None, kernel=dominant)
+    flops = 2 * pr.flops()
+    line = {
+        "metric": "backward effective GFLOP/s (2 x forward flops per backward)",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; OCDNet-shaped stand-in, no dataset or weights)",
+        "config": {"workload": args.workload, "pass": "backward", "N": pr.N, "C": pr.C,
+                   "Co": pr.Co, "H": pr.H, "W": pr.W, "kernel": [pr.kh, pr.kw],
+                   "group": pr.groups, "deformable_group": pr.deformable_groups},
+        "roofline": roofline, "kernels": kernels, "cpu_baseline": None,
     }
     print(json.dumps(line))
     return 0

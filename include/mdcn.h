@@ -190,6 +190,32 @@ mdcn_status mdcn_forward(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
                          const void *weight, const void *bias, int64_t bias_len, void *out,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- backward ------------------------------------------------------------ */
+
+/* Gradients of a scalar loss L through the forward, given grad_out = dL/dout
+ * ([N][Co][Ho][Wo]): grad_x, grad_offset, grad_mask, grad_weight (the shapes
+ * of x, offset, mask, weight) and, if grad_bias is not NULL, grad_bias
+ * (bias_len == Co values).  The pages define only the forward
+ * [plugin guide §五 steps 1-3]; these are the derivatives of that
+ * definition, with the bilinear sample differentiated on the cell floor()
+ * selects (corners off the image count as 0, so at an integer coordinate
+ * this is the derivative from above) and zero derivatives for a sample
+ * outside the open window (-1, H) x (-1, W) or with a non-finite coordinate.
+ * fp32 only (MDCN_E_DTYPE otherwise).  Accumulations into grad_x and
+ * grad_weight use atomic adds, so their last bits may differ from run to
+ * run.  Buffers: device pointers, the outputs and the workspace (at least
+ * mdcn_backward_workspace_bytes) must overlap no input and no other output
+ * (MDCN_E_ALIAS).  Every output is written (zeros for an empty batch or
+ * output grid).  Errors as mdcn_forward. */
+mdcn_status mdcn_backward_workspace_bytes(const mdcn_op *op, mdcn_dtype dtype,
+                                          const int64_t dims[16], size_t *bytes);
+mdcn_status mdcn_backward(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                          const void *x, const void *offset, const void *mask,
+                          const void *weight, const void *grad_out, void *grad_x,
+                          void *grad_offset, void *grad_mask, void *grad_weight, void *grad_bias,
+                          int64_t bias_len, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
 /* ---- tracing: per-kernel device time, for profiling --------------------- */
 
 typedef struct mdcn_trace mdcn_trace;
@@ -210,6 +236,14 @@ mdcn_status mdcn_forward_traced(const mdcn_op *op, mdcn_dtype dtype, const int64
                                 void *out, void *workspace, size_t workspace_bytes,
                                 void *stream, mdcn_trace *trace);
 
+/* mdcn_backward, recording events around each kernel launch on `stream`. */
+mdcn_status mdcn_backward_traced(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                                 const void *x, const void *offset, const void *mask,
+                                 const void *weight, const void *grad_out, void *grad_x,
+                                 void *grad_offset, void *grad_mask, void *grad_weight,
+                                 void *grad_bias, int64_t bias_len, void *workspace,
+                                 size_t workspace_bytes, void *stream, mdcn_trace *trace);
+
 /* Number of launches recorded so far. */
 mdcn_status mdcn_trace_count(const mdcn_trace *trace, int32_t *count);
 
@@ -224,7 +258,10 @@ mdcn_status mdcn_trace_read(mdcn_trace *trace, int32_t i, int32_t *kernel_id, fl
  * "gemm_bias", "fused_gather_gemm", "window_gather_gemm",
  * "depthwise_geometry", "depthwise_direct", "direct"; for the FP8 path
  * "prep_nhwc_fp8" (the weight rounded to E4M3 and the first chunk of x to
- * channels-last), "deform_gather_fp8", "gemm_fp8_bias"; "pack_weight" and
+ * channels-last), "deform_gather_fp8", "gemm_fp8_bias"; for the backward
+ * "bwd_zero", "bwd_bias", "bwd_weight_gemm", "bwd_col_gemm", "bwd_sample",
+ * "bwd_to_nchw", "bwd_weight_out" (with "pack_weight", "to_nhwc" and
+ * "deform_gather"); "pack_weight" (outside the backward) and
  * "pack_weight_steps" (standalone weight repacking) are not launched by the
  * forward.  "?" if unknown. */
 const char *mdcn_kernel_name(int32_t kernel_id);

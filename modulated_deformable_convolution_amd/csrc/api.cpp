@@ -249,6 +249,143 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     return MDCN_OK;
 }
 
+mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                          const void *x, const void *offset, const void *mask,
+                          const void *weight, const void *grad_out, void *grad_x,
+                          void *grad_offset, void *grad_mask, void *grad_weight, void *grad_bias,
+                          int64_t bias_len, void *workspace, size_t workspace_bytes,
+                          void *stream_ptr, mdcn_trace *trace)
+{
+    if (!op || !dims)
+        return MDCN_E_NULL;
+    Problem p;
+    mdcn_status st = mdcn::derive_problem(op->attrs, dtype, dims, &p);
+    if (st != MDCN_OK)
+        return st;
+    if (dtype != MDCN_F32)
+        return MDCN_E_DTYPE;
+    if (grad_bias && bias_len != p.Co)
+        return MDCN_E_SHAPE;
+    if (!x || !offset || !mask || !weight || !grad_out || !grad_x || !grad_offset ||
+        !grad_mask || !grad_weight)
+        return MDCN_E_NULL;
+    const mdcn::BackwardLayout l = mdcn::backward_layout(p);
+    if (!workspace || workspace_bytes < l.bytes + mdcn::kAlign)
+        return MDCN_E_WORKSPACE;
+    const size_t x_n = size_t(p.C * p.H * p.W), off_n = size_t(2 * p.DG * p.K * p.P);
+    const size_t msk_n = size_t(p.DG * p.K * p.P), out_n = size_t(p.Co * p.P);
+    const size_t w_n = size_t(p.Co * p.Cg * p.K);
+    const Range inputs[] = {
+        range_of(x, size_t(p.N) * x_n * 4), range_of(offset, size_t(p.N) * off_n * 4),
+        range_of(mask, size_t(p.N) * msk_n * 4), range_of(weight, w_n * 4),
+        range_of(grad_out, size_t(p.N) * out_n * 4)};
+    const uintptr_t raw = reinterpret_cast<uintptr_t>(workspace);
+    char *ws = reinterpret_cast<char *>((raw + mdcn::kAlign - 1) / mdcn::kAlign * mdcn::kAlign);
+    const Range outputs[] = {
+        range_of(grad_x, size_t(p.N) * x_n * 4), range_of(grad_offset, size_t(p.N) * off_n * 4),
+        range_of(grad_mask, size_t(p.N) * msk_n * 4), range_of(grad_weight, w_n * 4),
+        range_of(grad_bias, grad_bias ? size_t(p.Co) * 4 : 0), range_of(ws, l.bytes)};
+    for (size_t i = 0; i < sizeof(outputs) / sizeof(outputs[0]); ++i) {
+        for (const Range &in : inputs)
+            if (overlap(outputs[i], in))
+                return MDCN_E_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outputs) / sizeof(outputs[0]); ++j)
+            if (overlap(outputs[i], outputs[j]))
+                return MDCN_E_ALIAS;
+    }
+    st = device_ok();
+    if (st != MDCN_OK)
+        return st;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    Recorder rec{stream, trace};
+    float *gx = static_cast<float *>(grad_x);
+    float *wacc = reinterpret_cast<float *>(ws + l.wacc_off);
+    float *wpack = reinterpret_cast<float *>(ws + l.wpack_off);
+    float *xt = reinterpret_cast<float *>(ws + l.xt_off);
+    float *gxt = reinterpret_cast<float *>(ws + l.gxt_off);
+    float *col = reinterpret_cast<float *>(ws + l.col_off);
+    float *gcol = reinterpret_cast<float *>(ws + l.gcol_off);
+    const bool empty = p.N == 0 || p.P == 0;
+    // the weight accumulator takes atomic adds; an empty batch or output grid
+    // leaves every gradient zero
+    hipError_t err = rec.run(mdcn::K_BWD_ZERO, [&] {
+        hipError_t e = mdcn::launch_bwd_fill_zero(wacc, p.Co * l.Kp, stream);
+        if (e == hipSuccess && empty)
+            e = mdcn::launch_bwd_fill_zero(gx, int64_t(p.N) * int64_t(x_n), stream);
+        return e;
+    });
+    if (err != hipSuccess)
+        return MDCN_E_LAUNCH;
+    if (grad_bias) {
+        err = (p.N == 0 || p.P == 0)
+                  ? mdcn::launch_bwd_fill_zero(static_cast<float *>(grad_bias), p.Co, stream)
+                  : rec.run(mdcn::K_BWD_BIAS, [&] {
+                        return mdcn::launch_bwd_bias(p, static_cast<const float *>(grad_out),
+                                                     static_cast<float *>(grad_bias), stream);
+                    });
+        if (err != hipSuccess)
+            return MDCN_E_LAUNCH;
+    }
+    Plan gp{};
+    gp.path = Path::GatherGemm;     // the forward's im2col and weight packing, fp32
+    gp.Kp = l.Kp;
+    if (!empty) {
+        err = rec.run(mdcn::K_PACK_WEIGHT, [&] {
+            return mdcn::launch_pack_weight(p, gp, weight, wpack, stream);
+        });
+        if (err != hipSuccess)
+            return MDCN_E_LAUNCH;
+    }
+    // grad_x of one image in NHWC -> NCHW: the NHWC transpose with the roles
+    // of channels and positions exchanged ([H*W][C] read as C' = H*W channels
+    // of C positions)
+    Problem pt = p;
+    pt.C = p.H * p.W;
+    pt.H = p.C;
+    pt.W = 1;
+    for (int64_t n = 0; n < p.N && !empty; ++n) {
+        const float *xn = static_cast<const float *>(x) + size_t(n) * x_n;
+        const float *on = static_cast<const float *>(offset) + size_t(n) * off_n;
+        const float *mn = static_cast<const float *>(mask) + size_t(n) * msk_n;
+        const float *gn = static_cast<const float *>(grad_out) + size_t(n) * out_n;
+        err = rec.run(mdcn::K_TO_NHWC, [&] { return mdcn::launch_to_nhwc(p, 1, xn, xt, stream); });
+        if (err == hipSuccess)
+            err = rec.run(mdcn::K_GATHER, [&] {
+                return mdcn::launch_gather(p, gp, 1, xt, on, mn, col, stream);
+            });
+        if (err == hipSuccess)
+            err = rec.run(mdcn::K_BWD_WEIGHT_GEMM, [&] {
+                return mdcn::launch_bwd_weight_gemm(p, l, gn, col, wacc, stream);
+            });
+        if (err == hipSuccess)
+            err = rec.run(mdcn::K_BWD_COL_GEMM, [&] {
+                return mdcn::launch_bwd_col_gemm(p, l, wpack, gn, gcol, stream);
+            });
+        if (err == hipSuccess)
+            err = rec.run(mdcn::K_BWD_ZERO, [&] {
+                return mdcn::launch_bwd_fill_zero(gxt, int64_t(x_n), stream);
+            });
+        if (err == hipSuccess)
+            err = rec.run(mdcn::K_BWD_SAMPLE, [&] {
+                return mdcn::launch_bwd_sample(
+                    p, l, xt, on, mn, gcol, gxt,
+                    static_cast<float *>(grad_offset) + size_t(n) * off_n,
+                    static_cast<float *>(grad_mask) + size_t(n) * msk_n, stream);
+            });
+        if (err == hipSuccess)
+            err = rec.run(mdcn::K_BWD_TO_NCHW, [&] {
+                return mdcn::launch_to_nhwc(pt, 1, gxt, gx + size_t(n) * x_n, stream);
+            });
+        if (err != hipSuccess)
+            return MDCN_E_LAUNCH;
+    }
+    err = rec.run(mdcn::K_BWD_WEIGHT_OUT, [&] {
+        return mdcn::launch_bwd_weight_out(p, l, wacc, static_cast<float *>(grad_weight), stream);
+    });
+    return err == hipSuccess ? MDCN_OK : MDCN_E_LAUNCH;
+}
+
 mdcn_status create_impl(const int32_t stride[2], const int32_t padding[2],
                         const int32_t dilation[2], int32_t group, int32_t dgroup,
                         mdcn_path path, mdcn_op **out)
@@ -372,6 +509,58 @@ mdcn_status mdcn_forward_traced(const mdcn_op *op, mdcn_dtype dtype, const int64
     }
 }
 
+mdcn_status mdcn_backward_workspace_bytes(const mdcn_op *op, mdcn_dtype dtype,
+                                          const int64_t dims[16], size_t *bytes)
+{
+    try {
+        if (!op || !dims || !bytes)
+            return MDCN_E_NULL;
+        Problem p;
+        mdcn_status st = mdcn::derive_problem(op->attrs, dtype, dims, &p);
+        if (st != MDCN_OK)
+            return st;
+        if (dtype != MDCN_F32)
+            return MDCN_E_DTYPE;
+        *bytes = mdcn::backward_layout(p).bytes + mdcn::kAlign;
+        return MDCN_OK;
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+mdcn_status mdcn_backward(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                          const void *x, const void *offset, const void *mask,
+                          const void *weight, const void *grad_out, void *grad_x,
+                          void *grad_offset, void *grad_mask, void *grad_weight, void *grad_bias,
+                          int64_t bias_len, void *workspace, size_t workspace_bytes, void *stream)
+{
+    try {
+        return backward_impl(op, dtype, dims, x, offset, mask, weight, grad_out, grad_x,
+                             grad_offset, grad_mask, grad_weight, grad_bias, bias_len, workspace,
+                             workspace_bytes, stream, nullptr);
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
+mdcn_status mdcn_backward_traced(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                                 const void *x, const void *offset, const void *mask,
+                                 const void *weight, const void *grad_out, void *grad_x,
+                                 void *grad_offset, void *grad_mask, void *grad_weight,
+                                 void *grad_bias, int64_t bias_len, void *workspace,
+                                 size_t workspace_bytes, void *stream, mdcn_trace *trace)
+{
+    try {
+        if (!trace)
+            return MDCN_E_NULL;
+        return backward_impl(op, dtype, dims, x, offset, mask, weight, grad_out, grad_x,
+                             grad_offset, grad_mask, grad_weight, grad_bias, bias_len, workspace,
+                             workspace_bytes, stream, trace);
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
 mdcn_status mdcn_trace_create(int32_t capacity, mdcn_trace **out)
 {
     try {
@@ -465,6 +654,13 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_PREP_NHWC_FP8: return "prep_nhwc_fp8";
     case mdcn::K_GATHER_FP8: return "deform_gather_fp8";
     case mdcn::K_GEMM_FP8: return "gemm_fp8_bias";
+    case mdcn::K_BWD_ZERO: return "bwd_zero";
+    case mdcn::K_BWD_BIAS: return "bwd_bias";
+    case mdcn::K_BWD_WEIGHT_GEMM: return "bwd_weight_gemm";
+    case mdcn::K_BWD_COL_GEMM: return "bwd_col_gemm";
+    case mdcn::K_BWD_SAMPLE: return "bwd_sample";
+    case mdcn::K_BWD_WEIGHT_OUT: return "bwd_weight_out";
+    case mdcn::K_BWD_TO_NCHW: return "bwd_to_nchw";
     }
     return "?";
 }

@@ -26,7 +26,14 @@ enum KernelId : int32_t {
     K_PREP_NHWC_FP8 = 13,
     K_GATHER_FP8 = 14,
     K_GEMM_FP8 = 15,
-    K_COUNT = 16
+    K_BWD_ZERO = 16,
+    K_BWD_BIAS = 17,
+    K_BWD_WEIGHT_GEMM = 18,
+    K_BWD_COL_GEMM = 19,
+    K_BWD_SAMPLE = 20,
+    K_BWD_WEIGHT_OUT = 21,
+    K_BWD_TO_NCHW = 22,
+    K_COUNT = 23
 };
 
 // weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
@@ -115,5 +122,34 @@ hipError_t launch_dw_geometry(const Problem &p, int64_t cnt, const void *offset,
 hipError_t launch_depthwise(const Problem &p, int64_t cnt, const void *x, const void *geo,
                             const void *offset, const void *mask, const void *weight,
                             const void *bias, void *out, hipStream_t stream);
+
+// ---- backward (fp32) ----------------------------------------------------
+// Workspace of the backward, for one image at a time (offsets from the
+// 256-byte aligned start): the packed weight [G][Mg][Kp] (tap-major), x of
+// the image in NHWC, its grad_x accumulator in NHWC (fp32), its columns
+// [G][P][Kp] (tap-major, as the forward's gather writes them), the column
+// gradient in the same layout, and the weight-gradient accumulator [Co][Kp].
+struct BackwardLayout {
+    int64_t Kp;
+    size_t wpack_off, xt_off, gxt_off, col_off, gcol_off, wacc_off, bytes;
+};
+BackwardLayout backward_layout(const Problem &p);
+hipError_t launch_bwd_fill_zero(float *ptr, int64_t n, hipStream_t stream);
+// grad_bias[co] = sum over images and pixels of g[n][co][p].
+hipError_t launch_bwd_bias(const Problem &p, const float *g, float *gb, hipStream_t stream);
+// acc[g][m][kk] += sum_p g_n[g*Mg + m][p] * col[g][p][kk] (atomic adds).
+hipError_t launch_bwd_weight_gemm(const Problem &p, const BackwardLayout &l, const float *g_n,
+                                  const float *col, float *acc, hipStream_t stream);
+// gcol[g][p][kk] = sum_m g_n[g*Mg + m][p] * wpack[g][m][kk] (kk tap-major).
+hipError_t launch_bwd_col_gemm(const Problem &p, const BackwardLayout &l, const float *wpack,
+                               const float *g_n, float *gcol, hipStream_t stream);
+// grad_mask, grad_offset of image n (stored) and its grad_x in NHWC (atomic
+// adds into gxt_n, zeroed by the caller) from gcol and the NHWC x.
+hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const float *xt_n,
+                             const float *off_n, const float *msk_n, const float *gcol,
+                             float *gxt_n, float *goff_n, float *gmask_n, hipStream_t stream);
+// grad_weight[g*Mg + m][c'][k] = acc[g][m][k*Cg + c'].
+hipError_t launch_bwd_weight_out(const Problem &p, const BackwardLayout &l, const float *acc,
+                                 float *gw, hipStream_t stream);
 
 }  // namespace mdcn

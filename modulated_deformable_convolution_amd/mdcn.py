@@ -47,6 +47,7 @@ EXPORTED = [
     "mdcn_workspace_bytes", "mdcn_forward", "mdcn_trace_create", "mdcn_trace_destroy",
     "mdcn_trace_reset", "mdcn_forward_traced", "mdcn_trace_count", "mdcn_trace_read",
     "mdcn_kernel_name", "mdcn_status_string", "mdcn_abi_version", "mdcn_describe_plan",
+    "mdcn_backward_workspace_bytes", "mdcn_backward", "mdcn_backward_traced",
 ]
 
 
@@ -79,6 +80,12 @@ def _bind(lib):
         "mdcn_forward_traced": ([_vp, ctypes.c_int, _i64p, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp, _vp],
                                 ctypes.c_int),
+        "mdcn_backward_workspace_bytes": ([_vp, ctypes.c_int, _i64p, _szp], ctypes.c_int),
+        "mdcn_backward": ([_vp, ctypes.c_int, _i64p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _vp, _vp, ctypes.c_int64, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+        "mdcn_backward_traced": ([_vp, ctypes.c_int, _i64p, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, ctypes.c_int64, _vp, ctypes.c_size_t, _vp, _vp],
+                                 ctypes.c_int),
         "mdcn_trace_create": ([ctypes.c_int32, ctypes.POINTER(_vp)], ctypes.c_int),
         "mdcn_trace_destroy": ([_vp], None),
         "mdcn_trace_reset": ([_vp], ctypes.c_int),
@@ -194,6 +201,31 @@ def mdcn_forward(op: Op, dtype: int, dims, x: int, offset: int, mask: int, weigh
     return lib.mdcn_forward_traced(*args, trace.handle)
 
 
+def mdcn_backward_workspace_bytes(op: Op, dtype: int, dims) -> int:
+    lib = library()
+    d = _arr(ctypes.c_int64, dims)
+    b = ctypes.c_size_t()
+    _check(lib.mdcn_backward_workspace_bytes(op.handle, int(dtype), d, ctypes.byref(b)),
+           "mdcn_backward_workspace_bytes")
+    return b.value
+
+
+def mdcn_backward(op: Op, dtype: int, dims, x: int, offset: int, mask: int, weight: int,
+                  grad_out: int, grad_x: int, grad_offset: int, grad_mask: int,
+                  grad_weight: int, grad_bias: int, bias_len: int, workspace: int,
+                  workspace_bytes: int, stream: int, trace: "Trace | None" = None) -> int:
+    """Raw entry point; returns the status code (does not raise)."""
+    lib = library()
+    d = _arr(ctypes.c_int64, dims)
+    args = (op.handle, int(dtype), d, x or None, offset or None, mask or None, weight or None,
+            grad_out or None, grad_x or None, grad_offset or None, grad_mask or None,
+            grad_weight or None, grad_bias or None, int(bias_len), workspace or None,
+            int(workspace_bytes), stream or None)
+    if trace is None:
+        return lib.mdcn_backward(*args)
+    return lib.mdcn_backward_traced(*args, trace.handle)
+
+
 def mdcn_kernel_name(kernel_id: int) -> str:
     return library().mdcn_kernel_name(int(kernel_id)).decode()
 
@@ -281,3 +313,36 @@ def forward(op: Op, x, offset, mask, weight, bias=None, out=None, workspace=None
                       workspace.data_ptr(), workspace.numel(), int(stream), trace)
     _check(st, "mdcn_forward")
     return out
+
+
+def backward(op: Op, x, offset, mask, weight, grad_out, with_bias=True, workspace=None,
+             stream=None, trace: Trace | None = None):
+    """Run mdcn_backward (fp32) on torch device tensors: returns a dict of
+    gradients x, offset, mask, weight and (with_bias) bias, allocated with
+    torch.  Raises MdcnError on failure."""
+    import torch
+    for t in (x, offset, mask, weight, grad_out):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype:
+            raise MdcnError(MDCN_E_SHAPE if t.is_cuda else MDCN_E_NULL, "backward: tensors "
+                            "must be contiguous device tensors of one dtype")
+    code = dtype_code(x.dtype)
+    dims = dims_of(x, offset, mask, weight)
+    if tuple(grad_out.shape) != mdcn_output_shape(op, dims):
+        raise MdcnError(MDCN_E_SHAPE, "backward: grad_out")
+    if workspace is None:
+        workspace = torch.empty(mdcn_backward_workspace_bytes(op, code, dims),
+                                dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    g = {"x": torch.empty_like(x), "offset": torch.empty_like(offset),
+         "mask": torch.empty_like(mask), "weight": torch.empty_like(weight),
+         "bias": torch.empty(weight.shape[0], dtype=x.dtype, device=x.device) if with_bias
+         else None}
+    st = mdcn_backward(op, code, dims, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
+                       weight.data_ptr(), grad_out.data_ptr(), g["x"].data_ptr(),
+                       g["offset"].data_ptr(), g["mask"].data_ptr(), g["weight"].data_ptr(),
+                       g["bias"].data_ptr() if with_bias else 0,
+                       int(weight.shape[0]) if with_bias else 0, workspace.data_ptr(),
+                       workspace.numel(), int(stream), trace)
+    _check(st, "mdcn_backward")
+    return g

@@ -462,3 +462,31 @@ def test_fp8_path_plan():
         assert "fp8" not in mdcn.mdcn_describe_plan(auto, dt, d)
     names = [mdcn.mdcn_kernel_name(i) for i in range(16)]
     assert {"prep_nhwc_fp8", "deform_gather_fp8", "gemm_fp8_bias"} <= set(names)
+
+
+def test_backward_entry_points():
+    """fp32 only; the workspace holds the packed weight, one image's NHWC x
+    and its gradient, its columns and their gradient, and the weight-gradient
+    accumulator."""
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    b = mdcn.mdcn_backward_workspace_bytes(op, mdcn.MDCN_F32, DIMS)
+    xt = 256 * 160 * 160 * 4          # x and its gradient, NHWC
+    col = 25600 * 2304 * 4            # columns and their gradient
+    wp = 256 * 2304 * 4               # packed weight and the weight-gradient accumulator
+    assert b == 256 + 2 * xt + 2 * col + 2 * wp
+    for dt in (mdcn.MDCN_F16, mdcn.MDCN_BF16):
+        with pytest.raises(mdcn.MdcnError) as e:
+            mdcn.mdcn_backward_workspace_bytes(op, dt, DIMS)
+        assert e.value.status == mdcn.MDCN_E_DTYPE
+        assert mdcn.mdcn_backward(op, dt, DIMS, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0, 1, b, 0) == \
+            mdcn.MDCN_E_DTYPE
+    # missing pointers and a short workspace are refused before any launch
+    assert mdcn.mdcn_backward(op, mdcn.MDCN_F32, DIMS, 0, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0, 1, b,
+                              0) == mdcn.MDCN_E_NULL
+    assert mdcn.mdcn_backward(op, mdcn.MDCN_F32, DIMS, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0, 1,
+                              b - 1, 0) == mdcn.MDCN_E_WORKSPACE
+    assert mdcn.mdcn_backward(op, mdcn.MDCN_F32, DIMS, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 5, 1,
+                              b, 0) == mdcn.MDCN_E_SHAPE         # bias_len != Co
+    names = [mdcn.mdcn_kernel_name(i) for i in range(23)]
+    assert {"bwd_zero", "bwd_bias", "bwd_weight_gemm", "bwd_col_gemm", "bwd_sample",
+            "bwd_to_nchw", "bwd_weight_out"} <= set(names)
