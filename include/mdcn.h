@@ -201,9 +201,10 @@ mdcn_status mdcn_forward(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
  * selects (corners off the image count as 0, so at an integer coordinate
  * this is the derivative from above) and zero derivatives for a sample
  * outside the open window (-1, H) x (-1, W) or with a non-finite coordinate.
- * fp32 only (MDCN_E_DTYPE otherwise).  Accumulations into grad_x and
- * grad_weight use atomic adds, so their last bits may differ from run to
- * run.  Buffers: device pointers, the outputs and the workspace (at least
+ * Inputs and gradients in the dtype (fp32, fp16 or bf16), arithmetic and
+ * accumulation in fp32, one rounding of each gradient.  Accumulations into
+ * grad_x and grad_weight use atomic adds, so their last bits may differ from
+ * run to run.  Buffers: device pointers, the outputs and the workspace (at least
  * mdcn_backward_workspace_bytes) must overlap no input and no other output
  * (MDCN_E_ALIAS).  Every output is written (zeros for an empty batch or
  * output grid).  Errors as mdcn_forward. */

@@ -262,8 +262,6 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
     mdcn_status st = mdcn::derive_problem(op->attrs, dtype, dims, &p);
     if (st != MDCN_OK)
         return st;
-    if (dtype != MDCN_F32)
-        return MDCN_E_DTYPE;
     if (grad_bias && bias_len != p.Co)
         return MDCN_E_SHAPE;
     if (!x || !offset || !mask || !weight || !grad_out || !grad_x || !grad_offset ||
@@ -275,16 +273,17 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
     const size_t x_n = size_t(p.C * p.H * p.W), off_n = size_t(2 * p.DG * p.K * p.P);
     const size_t msk_n = size_t(p.DG * p.K * p.P), out_n = size_t(p.Co * p.P);
     const size_t w_n = size_t(p.Co * p.Cg * p.K);
+    const size_t e = p.elem;
     const Range inputs[] = {
-        range_of(x, size_t(p.N) * x_n * 4), range_of(offset, size_t(p.N) * off_n * 4),
-        range_of(mask, size_t(p.N) * msk_n * 4), range_of(weight, w_n * 4),
-        range_of(grad_out, size_t(p.N) * out_n * 4)};
+        range_of(x, size_t(p.N) * x_n * e), range_of(offset, size_t(p.N) * off_n * e),
+        range_of(mask, size_t(p.N) * msk_n * e), range_of(weight, w_n * e),
+        range_of(grad_out, size_t(p.N) * out_n * e)};
     const uintptr_t raw = reinterpret_cast<uintptr_t>(workspace);
     char *ws = reinterpret_cast<char *>((raw + mdcn::kAlign - 1) / mdcn::kAlign * mdcn::kAlign);
     const Range outputs[] = {
-        range_of(grad_x, size_t(p.N) * x_n * 4), range_of(grad_offset, size_t(p.N) * off_n * 4),
-        range_of(grad_mask, size_t(p.N) * msk_n * 4), range_of(grad_weight, w_n * 4),
-        range_of(grad_bias, grad_bias ? size_t(p.Co) * 4 : 0), range_of(ws, l.bytes)};
+        range_of(grad_x, size_t(p.N) * x_n * e), range_of(grad_offset, size_t(p.N) * off_n * e),
+        range_of(grad_mask, size_t(p.N) * msk_n * e), range_of(grad_weight, w_n * e),
+        range_of(grad_bias, grad_bias ? size_t(p.Co) * e : 0), range_of(ws, l.bytes)};
     for (size_t i = 0; i < sizeof(outputs) / sizeof(outputs[0]); ++i) {
         for (const Range &in : inputs)
             if (overlap(outputs[i], in))
@@ -299,11 +298,12 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
 
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     Recorder rec{stream, trace};
-    float *gx = static_cast<float *>(grad_x);
+    char *gx = static_cast<char *>(grad_x);
     float *wacc = reinterpret_cast<float *>(ws + l.wacc_off);
-    float *wpack = reinterpret_cast<float *>(ws + l.wpack_off);
-    float *xt = reinterpret_cast<float *>(ws + l.xt_off);
+    char *wpack = ws + l.wpack_off;
+    char *xt = ws + l.xt_off;
     float *gxt = reinterpret_cast<float *>(ws + l.gxt_off);
+    float *gxn = reinterpret_cast<float *>(ws + l.gxn_off);
     float *col = reinterpret_cast<float *>(ws + l.col_off);
     float *gcol = reinterpret_cast<float *>(ws + l.gcol_off);
     const bool empty = p.N == 0 || p.P == 0;
@@ -312,17 +312,16 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
     hipError_t err = rec.run(mdcn::K_BWD_ZERO, [&] {
         hipError_t e = mdcn::launch_bwd_fill_zero(wacc, p.Co * l.Kp, stream);
         if (e == hipSuccess && empty)
-            e = mdcn::launch_bwd_fill_zero(gx, int64_t(p.N) * int64_t(x_n), stream);
+            e = mdcn::launch_bwd_fill_zero_dtype(p, gx, int64_t(p.N) * int64_t(x_n), stream);
         return e;
     });
     if (err != hipSuccess)
         return MDCN_E_LAUNCH;
     if (grad_bias) {
         err = (p.N == 0 || p.P == 0)
-                  ? mdcn::launch_bwd_fill_zero(static_cast<float *>(grad_bias), p.Co, stream)
+                  ? mdcn::launch_bwd_fill_zero_dtype(p, grad_bias, p.Co, stream)
                   : rec.run(mdcn::K_BWD_BIAS, [&] {
-                        return mdcn::launch_bwd_bias(p, static_cast<const float *>(grad_out),
-                                                     static_cast<float *>(grad_bias), stream);
+                        return mdcn::launch_bwd_bias(p, grad_out, grad_bias, stream);
                     });
         if (err != hipSuccess)
             return MDCN_E_LAUNCH;
@@ -344,15 +343,17 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
     pt.C = p.H * p.W;
     pt.H = p.C;
     pt.W = 1;
+    pt.dtype = MDCN_F32;               // the accumulator is fp32 whatever the dtype
+    pt.elem = 4;
     for (int64_t n = 0; n < p.N && !empty; ++n) {
-        const float *xn = static_cast<const float *>(x) + size_t(n) * x_n;
-        const float *on = static_cast<const float *>(offset) + size_t(n) * off_n;
-        const float *mn = static_cast<const float *>(mask) + size_t(n) * msk_n;
-        const float *gn = static_cast<const float *>(grad_out) + size_t(n) * out_n;
+        const char *xn = static_cast<const char *>(x) + size_t(n) * x_n * e;
+        const char *on = static_cast<const char *>(offset) + size_t(n) * off_n * e;
+        const char *mn = static_cast<const char *>(mask) + size_t(n) * msk_n * e;
+        const char *gn = static_cast<const char *>(grad_out) + size_t(n) * out_n * e;
         err = rec.run(mdcn::K_TO_NHWC, [&] { return mdcn::launch_to_nhwc(p, 1, xn, xt, stream); });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_GATHER, [&] {
-                return mdcn::launch_gather(p, gp, 1, xt, on, mn, col, stream);
+                return mdcn::launch_gather_f32(p, gp, 1, xt, on, mn, col, stream);
             });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_BWD_WEIGHT_GEMM, [&] {
@@ -370,18 +371,24 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
             err = rec.run(mdcn::K_BWD_SAMPLE, [&] {
                 return mdcn::launch_bwd_sample(
                     p, l, xt, on, mn, gcol, gxt,
-                    static_cast<float *>(grad_offset) + size_t(n) * off_n,
-                    static_cast<float *>(grad_mask) + size_t(n) * msk_n, stream);
+                    static_cast<char *>(grad_offset) + size_t(n) * off_n * e,
+                    static_cast<char *>(grad_mask) + size_t(n) * msk_n * e, stream);
             });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_BWD_TO_NCHW, [&] {
-                return mdcn::launch_to_nhwc(pt, 1, gxt, gx + size_t(n) * x_n, stream);
+                // fp32: straight into grad_x; fp16/bf16: through fp32 NCHW, then rounded
+                if (p.dtype == MDCN_F32)
+                    return mdcn::launch_to_nhwc(pt, 1, gxt, gx + size_t(n) * x_n * e, stream);
+                hipError_t r = mdcn::launch_to_nhwc(pt, 1, gxt, gxn, stream);
+                return r != hipSuccess ? r
+                                       : mdcn::launch_bwd_convert(p, gxn, gx + size_t(n) * x_n * e,
+                                                                  int64_t(x_n), stream);
             });
         if (err != hipSuccess)
             return MDCN_E_LAUNCH;
     }
     err = rec.run(mdcn::K_BWD_WEIGHT_OUT, [&] {
-        return mdcn::launch_bwd_weight_out(p, l, wacc, static_cast<float *>(grad_weight), stream);
+        return mdcn::launch_bwd_weight_out(p, l, wacc, grad_weight, stream);
     });
     return err == hipSuccess ? MDCN_OK : MDCN_E_LAUNCH;
 }
@@ -519,8 +526,6 @@ mdcn_status mdcn_backward_workspace_bytes(const mdcn_op *op, mdcn_dtype dtype,
         mdcn_status st = mdcn::derive_problem(op->attrs, dtype, dims, &p);
         if (st != MDCN_OK)
             return st;
-        if (dtype != MDCN_F32)
-            return MDCN_E_DTYPE;
         *bytes = mdcn::backward_layout(p).bytes + mdcn::kAlign;
         return MDCN_OK;
     } catch (...) {

@@ -33,9 +33,9 @@ constexpr int kBL = 16;     // GEMM contraction slice
 // A[i*ai + l*al], and so on.  Rows i < M, columns j < N, l in
 // [z*lchunk, min(L, (z+1)*lchunk)) for grid z.
 struct GemmDesc {
-    const float *A;
+    const void *A;            // TA elements
     int64_t ai, al;
-    const float *B;
+    const void *B;            // TB elements
     int64_t bl, bj;
     float *C;
     int64_t ci, cj;
@@ -43,8 +43,11 @@ struct GemmDesc {
     int atomic;            // add into C atomically (split contraction) instead of storing
 };
 
+template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void sgemm_kernel(GemmDesc d)
 {
+    const TA *A = static_cast<const TA *>(d.A);
+    const TB *B = static_cast<const TB *>(d.B);
     __shared__ float As[kBL][kBT + 4];
     __shared__ float Bs[kBL][kBT + 4];
     const int i0 = int(blockIdx.y) * kBT, j0 = int(blockIdx.x) * kBT;
@@ -65,11 +68,11 @@ __global__ __launch_bounds__(256) void sgemm_kernel(GemmDesc d)
             const int ii = a_i_fast ? idx % kBT : idx / kBL;
             const int la = a_i_fast ? idx / kBT : idx % kBL;
             const int gi = i0 + ii, gl = l0 + la;
-            As[la][ii] = (gi < d.M && gl < l_end) ? d.A[gi * d.ai + gl * d.al] : 0.0f;
+            As[la][ii] = (gi < d.M && gl < l_end) ? to_f32(A[gi * d.ai + gl * d.al]) : 0.0f;
             const int jj = b_j_fast ? idx % kBT : idx / kBL;
             const int lb = b_j_fast ? idx / kBT : idx % kBL;
             const int gj = j0 + jj, glb = l0 + lb;
-            Bs[lb][jj] = (gj < d.N && glb < l_end) ? d.B[glb * d.bl + gj * d.bj] : 0.0f;
+            Bs[lb][jj] = (gj < d.N && glb < l_end) ? to_f32(B[glb * d.bl + gj * d.bj]) : 0.0f;
         }
         __syncthreads();
 #pragma unroll
@@ -103,6 +106,7 @@ __global__ __launch_bounds__(256) void sgemm_kernel(GemmDesc d)
         }
 }
 
+template <typename TA, typename TB>
 hipError_t run_gemm(const GemmDesc &d, int splits, hipStream_t s)
 {
     if (d.M <= 0 || d.N <= 0 || d.L <= 0)
@@ -111,7 +115,7 @@ hipError_t run_gemm(const GemmDesc &d, int splits, hipStream_t s)
                     unsigned(splits));
     if (grid.y > 65535u || grid.z > 65535u)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(sgemm_kernel, grid, dim3(256), 0, s, d);
+    hipLaunchKernelGGL((sgemm_kernel<TA, TB>), grid, dim3(256), 0, s, d);
     return hipGetLastError();
 }
 
@@ -123,17 +127,17 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, int64_t n)
 }
 
 // grad_bias[co] = sum over images and pixels of g[n][co][p]; one workgroup per co.
-__global__ __launch_bounds__(256) void bias_grad_kernel(const float *__restrict__ g,
-                                                        float *__restrict__ gb, int N, int Co,
-                                                        int P)
+template <typename T>
+__global__ __launch_bounds__(256) void bias_grad_kernel(const T *__restrict__ g,
+                                                        T *__restrict__ gb, int N, int Co, int P)
 {
     __shared__ float part[4];
     const int co = int(blockIdx.x);
     float s = 0.0f;
     for (int n = 0; n < N; ++n) {
-        const float *row = g + (int64_t(n) * Co + co) * P;
+        const T *row = g + (int64_t(n) * Co + co) * P;
         for (int p = int(threadIdx.x); p < P; p += 256)
-            s += row[p];
+            s += to_f32(row[p]);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1)
@@ -142,13 +146,14 @@ __global__ __launch_bounds__(256) void bias_grad_kernel(const float *__restrict_
         part[threadIdx.x >> 6] = s;
     __syncthreads();
     if (threadIdx.x == 0)
-        gb[co] = (part[0] + part[1]) + (part[2] + part[3]);
+        gb[co] = from_f32<T>((part[0] + part[1]) + (part[2] + part[3]));
 }
 
 // grad_weight[g*Mg + m][c'][k] = acc[g][m][k*Cg + c'] (the accumulator is in
 // the columns' tap-major order).
+template <typename T>
 __global__ __launch_bounds__(256) void weight_out_kernel(const float *__restrict__ acc,
-                                                         float *__restrict__ gw, int Co, int Cg,
+                                                         T *__restrict__ gw, int Co, int Cg,
                                                          int K, int Kp)
 {
     const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -158,16 +163,16 @@ __global__ __launch_bounds__(256) void weight_out_kernel(const float *__restrict
     const int k = int(t % K);
     const int cl = int((t / K) % Cg);
     const int64_t co = t / (int64_t(K) * Cg);
-    gw[t] = acc[co * Kp + int64_t(k) * Cg + cl];
+    gw[t] = from_f32<T>(acc[co * Kp + int64_t(k) * Cg + cl]);
 }
 
 struct SampleArgs {
-    const float *xt;        // image n, NHWC (the gather's copy)
-    const float *off;       // image n
-    const float *msk;       // image n
+    const void *xt;         // image n, NHWC (the gather's copy), dtype
+    const void *off;        // image n, dtype
+    const void *msk;        // image n, dtype
     const float *gcol;      // [G][P][Kp], column k*Cg + c' (tap-major)
     float *gxt;             // image n's grad_x, NHWC, fp32 (atomic adds)
-    float *goff, *gmask;    // image n
+    void *goff, *gmask;     // image n, dtype
     int C, H, W, Wo, P, K, kw, Cg, Cdg, DG, Kp;
     int sh, sw, ph, pw, dh, dw;
     int team_shift;         // lanes per (offset group, tap, pixel): 1 << team_shift (<= 64)
@@ -178,8 +183,12 @@ struct SampleArgs {
 // gradients and the atomic adds into grad_x are contiguous across the team
 // (channels-last), and the team reduces its mask and offset gradients with
 // wave shuffles.
+template <typename T>
 __global__ __launch_bounds__(256) void sample_grad_kernel(SampleArgs a)
 {
+    const T *xt = static_cast<const T *>(a.xt);
+    const T *offp = static_cast<const T *>(a.off);
+    const T *mskp = static_cast<const T *>(a.msk);
     const int TS = 1 << a.team_shift;
     const int64_t gt = int64_t(blockIdx.x) * 256 + threadIdx.x;
     const int64_t item = gt >> a.team_shift;
@@ -194,9 +203,9 @@ __global__ __launch_bounds__(256) void sample_grad_kernel(SampleArgs a)
         const int ho = p / a.Wo, wo = p - (p / a.Wo) * a.Wo;
         const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
         ohi = (int64_t(q) * 2 * a.K + 2 * k) * a.P + p;
-        const float oh = a.off[ohi], ow = a.off[ohi + a.P];
+        const float oh = to_f32(offp[ohi]), ow = to_f32(offp[ohi + a.P]);
         mi = (int64_t(q) * a.K + k) * a.P + p;
-        m = a.msk[mi];
+        m = to_f32(mskp[mi]);
         const float lim = 33554432.0f;            // 2^25: certainly off any valid image
         if (fabsf(oh) <= lim && fabsf(ow) <= lim) {
             const float fh = floorf(oh), fw = floorf(ow);
@@ -216,10 +225,10 @@ __global__ __launch_bounds__(256) void sample_grad_kernel(SampleArgs a)
                     const int grp = c / a.Cg, cl = c - grp * a.Cg;
                     const float gc =
                         a.gcol[(int64_t(grp) * a.P + p) * a.Kp + int64_t(k) * a.Cg + cl];
-                    const float v00 = (r0 && c0) ? a.xt[e00 + c] : 0.0f;
-                    const float v01 = (r0 && c1) ? a.xt[e01 + c] : 0.0f;
-                    const float v10 = (r1 && c0) ? a.xt[e10 + c] : 0.0f;
-                    const float v11 = (r1 && c1) ? a.xt[e11 + c] : 0.0f;
+                    const float v00 = (r0 && c0) ? to_f32(xt[e00 + c]) : 0.0f;
+                    const float v01 = (r0 && c1) ? to_f32(xt[e01 + c]) : 0.0f;
+                    const float v10 = (r1 && c0) ? to_f32(xt[e10 + c]) : 0.0f;
+                    const float v11 = (r1 && c1) ? to_f32(xt[e11 + c]) : 0.0f;
                     const float v = w00 * v00 + w01 * v01 + w10 * v10 + w11 * v11;
                     gm = fmaf(gc, v, gm);
                     gh = fmaf(gc, (1.0f - ax) * (v10 - v00) + ax * (v11 - v01), gh);
@@ -240,10 +249,19 @@ __global__ __launch_bounds__(256) void sample_grad_kernel(SampleArgs a)
         gw += __shfl_xor(gw, d, 64);
     }
     if (live && lane == 0) {
-        a.gmask[mi] = gm;
-        a.goff[ohi] = gh * m;
-        a.goff[ohi + a.P] = gw * m;
+        static_cast<T *>(a.gmask)[mi] = from_f32<T>(gm);
+        static_cast<T *>(a.goff)[ohi] = from_f32<T>(gh * m);
+        static_cast<T *>(a.goff)[ohi + a.P] = from_f32<T>(gw * m);
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const float *__restrict__ src,
+                                                      T *__restrict__ dst, int64_t n)
+{
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < n; t += stride)
+        dst[t] = from_f32<T>(src[t]);
 }
 
 }  // namespace
@@ -254,9 +272,10 @@ BackwardLayout backward_layout(const Problem &p)
     auto al = [](size_t b) { return (b + kAlign - 1) / kAlign * kAlign; };
     l.Kp = (p.Kg + 63) / 64 * 64;
     l.wpack_off = 0;
-    l.xt_off = l.wpack_off + al(size_t(p.Co * l.Kp) * 4);
-    l.gxt_off = l.xt_off + al(size_t(p.C * p.H * p.W) * 4);
-    l.col_off = l.gxt_off + al(size_t(p.C * p.H * p.W) * 4);
+    l.xt_off = l.wpack_off + al(size_t(p.Co * l.Kp) * p.elem);
+    l.gxt_off = l.xt_off + al(size_t(p.C * p.H * p.W) * p.elem);
+    l.gxn_off = l.gxt_off + al(size_t(p.C * p.H * p.W) * 4);
+    l.col_off = l.gxn_off + (p.dtype == MDCN_F32 ? 0 : al(size_t(p.C * p.H * p.W) * 4));
     l.gcol_off = l.col_off + al(size_t(p.G * p.P * l.Kp) * 4);
     l.wacc_off = l.gcol_off + al(size_t(p.G * p.P * l.Kp) * 4);
     l.bytes = l.wacc_off + al(size_t(p.Co * l.Kp) * 4);
@@ -272,16 +291,37 @@ hipError_t launch_bwd_fill_zero(float *ptr, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_bias(const Problem &p, const float *g, float *gb, hipStream_t s)
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void fill_zero_t_kernel(T *p, int64_t n)
 {
-    hipLaunchKernelGGL(bias_grad_kernel, dim3(unsigned(p.Co)), dim3(256), 0, s, g, gb, int(p.N),
-                       int(p.Co), int(p.P));
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < n; t += stride)
+        p[t] = T(0);
+}
+
+template <typename T>
+hipError_t fill_zero_t(void *ptr, int64_t n, hipStream_t s)
+{
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+    hipLaunchKernelGGL((fill_zero_t_kernel<T>), dim3(unsigned(blocks)), dim3(256), 0, s,
+                       static_cast<T *>(ptr), n);
     return hipGetLastError();
 }
 
-// acc[g][m][kk] += sum_p g_n[g*Mg + m][p] * col[g][p][kk], all groups.
-hipError_t launch_bwd_weight_gemm(const Problem &p, const BackwardLayout &l, const float *g_n,
-                                  const float *col, float *acc, hipStream_t s)
+template <typename T>
+hipError_t bias_t(const Problem &p, const void *g, void *gb, hipStream_t s)
+{
+    hipLaunchKernelGGL((bias_grad_kernel<T>), dim3(unsigned(p.Co)), dim3(256), 0, s,
+                       static_cast<const T *>(g), static_cast<T *>(gb), int(p.N), int(p.Co),
+                       int(p.P));
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t weight_gemm_t(const Problem &p, const BackwardLayout &l, const void *g_n,
+                         const float *col, float *acc, hipStream_t s)
 {
     // split the pixels so that the launch has about 1024 workgroups
     const int64_t tiles = ((p.Mg + kBT - 1) / kBT) * ((p.Kg + kBT - 1) / kBT);
@@ -291,39 +331,104 @@ hipError_t launch_bwd_weight_gemm(const Problem &p, const BackwardLayout &l, con
     splits = (p.P + lchunk - 1) / lchunk;
     for (int64_t grp = 0; grp < p.G; ++grp) {
         GemmDesc d{};
-        d.A = g_n + grp * p.Mg * p.P;  d.ai = p.P;  d.al = 1;
-        d.B = col + grp * p.P * l.Kp;  d.bl = l.Kp; d.bj = 1;
-        d.C = acc + grp * p.Mg * l.Kp; d.ci = l.Kp; d.cj = 1;
+        d.A = static_cast<const T *>(g_n) + grp * p.Mg * p.P;  d.ai = p.P;  d.al = 1;
+        d.B = col + grp * p.P * l.Kp;                          d.bl = l.Kp; d.bj = 1;
+        d.C = acc + grp * p.Mg * l.Kp;                         d.ci = l.Kp; d.cj = 1;
         d.M = int(p.Mg); d.N = int(p.Kg); d.L = int(p.P); d.lchunk = int(lchunk);
         d.atomic = 1;
-        hipError_t e = run_gemm(d, int(splits), s);
+        hipError_t e = run_gemm<T, float>(d, int(splits), s);
         if (e != hipSuccess)
             return e;
     }
     return hipSuccess;
 }
 
-// gcol[g][p][kk] = sum_m g_n[g*Mg + m][p] * wpack[g][m][kk] (kk tap-major).
-hipError_t launch_bwd_col_gemm(const Problem &p, const BackwardLayout &l, const float *wpack,
-                               const float *g_n, float *gcol, hipStream_t s)
+template <typename T>
+hipError_t col_gemm_t(const Problem &p, const BackwardLayout &l, const void *wpack,
+                      const void *g_n, float *gcol, hipStream_t s)
 {
     for (int64_t grp = 0; grp < p.G; ++grp) {
         GemmDesc d{};
-        d.A = g_n + grp * p.Mg * p.P;        d.ai = 1;    d.al = p.P;
-        d.B = wpack + grp * p.Mg * l.Kp;     d.bl = l.Kp; d.bj = 1;
-        d.C = gcol + grp * p.P * l.Kp;       d.ci = l.Kp; d.cj = 1;
+        d.A = static_cast<const T *>(g_n) + grp * p.Mg * p.P;    d.ai = 1;    d.al = p.P;
+        d.B = static_cast<const T *>(wpack) + grp * p.Mg * l.Kp; d.bl = l.Kp; d.bj = 1;
+        d.C = gcol + grp * p.P * l.Kp;                           d.ci = l.Kp; d.cj = 1;
         d.M = int(p.P); d.N = int(p.Kg); d.L = int(p.Mg); d.lchunk = int(p.Mg);
         d.atomic = 0;
-        hipError_t e = run_gemm(d, 1, s);
+        hipError_t e = run_gemm<T, T>(d, 1, s);
         if (e != hipSuccess)
             return e;
     }
     return hipSuccess;
 }
 
-hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const float *xt_n,
-                             const float *off_n, const float *msk_n, const float *gcol,
-                             float *gxt_n, float *goff_n, float *gmask_n, hipStream_t s)
+template <typename T>
+hipError_t sample_t(const Problem &p, const SampleArgs &a, int64_t threads, hipStream_t s)
+{
+    hipLaunchKernelGGL((sample_grad_kernel<T>), dim3(unsigned((threads + 255) / 256)), dim3(256),
+                       0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t convert_t(const float *src, void *dst, int64_t n, hipStream_t s)
+{
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+    hipLaunchKernelGGL((convert_kernel<T>), dim3(unsigned(blocks)), dim3(256), 0, s, src,
+                       static_cast<T *>(dst), n);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t weight_out_t(const Problem &p, const BackwardLayout &l, const float *acc, void *gw,
+                        hipStream_t s)
+{
+    const int64_t total = p.Co * p.Cg * p.K;
+    hipLaunchKernelGGL((weight_out_kernel<T>), dim3(unsigned((total + 255) / 256)), dim3(256), 0,
+                       s, acc, static_cast<T *>(gw), int(p.Co), int(p.Cg), int(p.K), int(l.Kp));
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bias(const Problem &p, const void *g, void *gb, hipStream_t s)
+{
+    if (p.Co == 0)
+        return hipSuccess;
+    switch (p.dtype) {
+    case MDCN_F32: return bias_t<float>(p, g, gb, s);
+    case MDCN_F16: return bias_t<half_t>(p, g, gb, s);
+    case MDCN_BF16: return bias_t<bf16_t>(p, g, gb, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// acc[g][m][kk] += sum_p g_n[g*Mg + m][p] * col[g][p][kk], all groups.
+hipError_t launch_bwd_weight_gemm(const Problem &p, const BackwardLayout &l, const void *g_n,
+                                  const float *col, float *acc, hipStream_t s)
+{
+    switch (p.dtype) {
+    case MDCN_F32: return weight_gemm_t<float>(p, l, g_n, col, acc, s);
+    case MDCN_F16: return weight_gemm_t<half_t>(p, l, g_n, col, acc, s);
+    case MDCN_BF16: return weight_gemm_t<bf16_t>(p, l, g_n, col, acc, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// gcol[g][p][kk] = sum_m g_n[g*Mg + m][p] * wpack[g][m][kk] (kk tap-major).
+hipError_t launch_bwd_col_gemm(const Problem &p, const BackwardLayout &l, const void *wpack,
+                               const void *g_n, float *gcol, hipStream_t s)
+{
+    switch (p.dtype) {
+    case MDCN_F32: return col_gemm_t<float>(p, l, wpack, g_n, gcol, s);
+    case MDCN_F16: return col_gemm_t<half_t>(p, l, wpack, g_n, gcol, s);
+    case MDCN_BF16: return col_gemm_t<bf16_t>(p, l, wpack, g_n, gcol, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const void *xt_n,
+                             const void *off_n, const void *msk_n, const float *gcol,
+                             float *gxt_n, void *goff_n, void *gmask_n, hipStream_t s)
 {
     SampleArgs a;
     a.xt = xt_n; a.off = off_n; a.msk = msk_n; a.gcol = gcol; a.gxt = gxt_n;
@@ -342,20 +447,50 @@ hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const fl
         return hipSuccess;
     if ((threads + 255) / 256 > 0x7fffffff)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(sample_grad_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
-                       s, a);
-    return hipGetLastError();
+    switch (p.dtype) {
+    case MDCN_F32: return sample_t<float>(p, a, threads, s);
+    case MDCN_F16: return sample_t<half_t>(p, a, threads, s);
+    case MDCN_BF16: return sample_t<bf16_t>(p, a, threads, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_fill_zero_dtype(const Problem &p, void *ptr, int64_t n, hipStream_t s)
+{
+    if (n <= 0)
+        return hipSuccess;
+    switch (p.dtype) {
+    case MDCN_F32: return fill_zero_t<float>(ptr, n, s);
+    case MDCN_F16: return fill_zero_t<half_t>(ptr, n, s);
+    case MDCN_BF16: return fill_zero_t<bf16_t>(ptr, n, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_convert(const Problem &p, const float *src, void *dst, int64_t n,
+                              hipStream_t s)
+{
+    if (n <= 0)
+        return hipSuccess;
+    switch (p.dtype) {
+    case MDCN_F32: return convert_t<float>(src, dst, n, s);
+    case MDCN_F16: return convert_t<half_t>(src, dst, n, s);
+    case MDCN_BF16: return convert_t<bf16_t>(src, dst, n, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_weight_out(const Problem &p, const BackwardLayout &l, const float *acc,
-                                 float *gw, hipStream_t s)
+                                 void *gw, hipStream_t s)
 {
-    const int64_t total = p.Co * p.Cg * p.K;
-    if (total == 0)
+    if (p.Co * p.Cg * p.K == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(weight_out_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s,
-                       acc, gw, int(p.Co), int(p.Cg), int(p.K), int(l.Kp));
-    return hipGetLastError();
+    switch (p.dtype) {
+    case MDCN_F32: return weight_out_t<float>(p, l, acc, gw, s);
+    case MDCN_F16: return weight_out_t<half_t>(p, l, acc, gw, s);
+    case MDCN_BF16: return weight_out_t<bf16_t>(p, l, acc, gw, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mdcn

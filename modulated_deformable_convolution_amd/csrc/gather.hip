@@ -119,6 +119,10 @@ __device__ __forceinline__ void gather_item(const GatherArgs &a, const Geo *geo,
                 *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
             else
                 *reinterpret_cast<uint32_t *>(dst) = w[0];
+        } else if constexpr (sizeof(O) == 4 && sizeof(T) == 2) {
+            // fp32 columns of fp16/bf16 input (the backward's): 8 floats
+            *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
         } else {
             Vec16<T> o;
 #pragma unroll
@@ -285,6 +289,18 @@ hipError_t gather_t(const Problem &p, const Plan &plan, int64_t cnt, const void 
 }
 
 }  // namespace
+
+hipError_t launch_gather_f32(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
+                             const void *offset, const void *mask, float *col,
+                             hipStream_t stream)
+{
+    switch (p.dtype) {
+    case MDCN_F32: return gather_t<float, float>(p, plan, cnt, xt, offset, mask, col, stream);
+    case MDCN_F16: return gather_t<half_t, float>(p, plan, cnt, xt, offset, mask, col, stream);
+    case MDCN_BF16: return gather_t<bf16_t, float>(p, plan, cnt, xt, offset, mask, col, stream);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_gather(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
                          const void *offset, const void *mask, void *col, hipStream_t stream)

@@ -76,6 +76,11 @@ hipError_t launch_to_nhwc(const Problem &p, int64_t cnt, const void *x, void *xt
 hipError_t launch_gather(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
                          const void *offset, const void *mask, void *col, hipStream_t stream);
 
+// The same columns in fp32 whatever the input dtype (the backward's).
+hipError_t launch_gather_f32(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
+                             const void *offset, const void *mask, float *col,
+                             hipStream_t stream);
+
 // out[n][g*Mg + m][pix] = sum_kk wpack[g][m][kk] * col[g][n*P + pix][kk] (+ bias);
 // FP8 path: E4M3 operands and the sums times wscale[g*Mg + m] before the bias
 // (wscale null otherwise).
@@ -123,33 +128,39 @@ hipError_t launch_depthwise(const Problem &p, int64_t cnt, const void *x, const 
                             const void *offset, const void *mask, const void *weight,
                             const void *bias, void *out, hipStream_t stream);
 
-// ---- backward (fp32) ----------------------------------------------------
+// ---- backward (fp32 arithmetic; inputs and gradients in the dtype) ------
 // Workspace of the backward, for one image at a time (offsets from the
-// 256-byte aligned start): the packed weight [G][Mg][Kp] (tap-major), x of
-// the image in NHWC, its grad_x accumulator in NHWC (fp32), its columns
-// [G][P][Kp] (tap-major, as the forward's gather writes them), the column
-// gradient in the same layout, and the weight-gradient accumulator [Co][Kp].
+// 256-byte aligned start): the packed weight [G][Mg][Kp] (tap-major, dtype),
+// x of the image in NHWC (dtype), its grad_x accumulator in NHWC and the
+// same in NCHW (fp32), its columns [G][P][Kp] (tap-major, as the forward's
+// gather writes them, fp32), the column gradient in the same layout, and the
+// weight-gradient accumulator [Co][Kp] (fp32).
 struct BackwardLayout {
     int64_t Kp;
-    size_t wpack_off, xt_off, gxt_off, col_off, gcol_off, wacc_off, bytes;
+    size_t wpack_off, xt_off, gxt_off, gxn_off, col_off, gcol_off, wacc_off, bytes;
 };
 BackwardLayout backward_layout(const Problem &p);
 hipError_t launch_bwd_fill_zero(float *ptr, int64_t n, hipStream_t stream);
+// n zeros of the problem's dtype.
+hipError_t launch_bwd_fill_zero_dtype(const Problem &p, void *ptr, int64_t n, hipStream_t stream);
 // grad_bias[co] = sum over images and pixels of g[n][co][p].
-hipError_t launch_bwd_bias(const Problem &p, const float *g, float *gb, hipStream_t stream);
+hipError_t launch_bwd_bias(const Problem &p, const void *g, void *gb, hipStream_t stream);
 // acc[g][m][kk] += sum_p g_n[g*Mg + m][p] * col[g][p][kk] (atomic adds).
-hipError_t launch_bwd_weight_gemm(const Problem &p, const BackwardLayout &l, const float *g_n,
+hipError_t launch_bwd_weight_gemm(const Problem &p, const BackwardLayout &l, const void *g_n,
                                   const float *col, float *acc, hipStream_t stream);
 // gcol[g][p][kk] = sum_m g_n[g*Mg + m][p] * wpack[g][m][kk] (kk tap-major).
-hipError_t launch_bwd_col_gemm(const Problem &p, const BackwardLayout &l, const float *wpack,
-                               const float *g_n, float *gcol, hipStream_t stream);
+hipError_t launch_bwd_col_gemm(const Problem &p, const BackwardLayout &l, const void *wpack,
+                               const void *g_n, float *gcol, hipStream_t stream);
 // grad_mask, grad_offset of image n (stored) and its grad_x in NHWC (atomic
 // adds into gxt_n, zeroed by the caller) from gcol and the NHWC x.
-hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const float *xt_n,
-                             const float *off_n, const float *msk_n, const float *gcol,
-                             float *gxt_n, float *goff_n, float *gmask_n, hipStream_t stream);
+hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const void *xt_n,
+                             const void *off_n, const void *msk_n, const float *gcol,
+                             float *gxt_n, void *goff_n, void *gmask_n, hipStream_t stream);
+// dst[t] = src[t] rounded to the dtype (n values).
+hipError_t launch_bwd_convert(const Problem &p, const float *src, void *dst, int64_t n,
+                              hipStream_t stream);
 // grad_weight[g*Mg + m][c'][k] = acc[g][m][k*Cg + c'].
 hipError_t launch_bwd_weight_out(const Problem &p, const BackwardLayout &l, const float *acc,
-                                 float *gw, hipStream_t stream);
+                                 void *gw, hipStream_t stream);
 
 }  // namespace mdcn

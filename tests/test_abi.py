@@ -465,21 +465,22 @@ def test_fp8_path_plan():
 
 
 def test_backward_entry_points():
-    """fp32 only; the workspace holds the packed weight, one image's NHWC x
-    and its gradient, its columns and their gradient, and the weight-gradient
-    accumulator."""
+    """Inputs and gradients in the dtype, fp32 arithmetic; the workspace holds
+    the packed weight and one image's NHWC x (dtype), its fp32 gradient
+    accumulator (NHWC, and NCHW for fp16/bf16), its fp32 columns and their
+    gradient, and the weight-gradient accumulator."""
     op = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    hw = 256 * 160 * 160
+    col = 25600 * 2304 * 4            # columns and their gradient (fp32)
+    acc = 256 * 2304 * 4
     b = mdcn.mdcn_backward_workspace_bytes(op, mdcn.MDCN_F32, DIMS)
-    xt = 256 * 160 * 160 * 4          # x and its gradient, NHWC
-    col = 25600 * 2304 * 4            # columns and their gradient
-    wp = 256 * 2304 * 4               # packed weight and the weight-gradient accumulator
-    assert b == 256 + 2 * xt + 2 * col + 2 * wp
+    assert b == 256 + 256 * 2304 * 4 + hw * 4 + hw * 4 + 2 * col + acc
     for dt in (mdcn.MDCN_F16, mdcn.MDCN_BF16):
-        with pytest.raises(mdcn.MdcnError) as e:
-            mdcn.mdcn_backward_workspace_bytes(op, dt, DIMS)
-        assert e.value.status == mdcn.MDCN_E_DTYPE
-        assert mdcn.mdcn_backward(op, dt, DIMS, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0, 1, b, 0) == \
-            mdcn.MDCN_E_DTYPE
+        b16 = mdcn.mdcn_backward_workspace_bytes(op, dt, DIMS)
+        assert b16 == 256 + 256 * 2304 * 2 + hw * 2 + 2 * hw * 4 + 2 * col + acc
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.mdcn_backward_workspace_bytes(op, 7, DIMS)
+    assert e.value.status == mdcn.MDCN_E_DTYPE
     # missing pointers and a short workspace are refused before any launch
     assert mdcn.mdcn_backward(op, mdcn.MDCN_F32, DIMS, 0, 1, 1, 1, 1, 1, 1, 1, 1, 0, 0, 1, b,
                               0) == mdcn.MDCN_E_NULL

@@ -3,9 +3,11 @@ backward (oracle.backward, float64, pinned by adjoint identities and finite
 differences in test_oracle_backward_pins.py).
 
 Tolerance, per gradient tensor: |g - r| <= 1e-4 * max(|r|, RMS(r)), the
-forward's fp32 rule.  Every gradient element is a sum of at most a few
-thousand fp32 products (grad_weight: N*Ho*Wo of them, accumulated by atomic
-adds in any order), so fp32 rounding stays orders of magnitude below it.
+forward's fp32 rule, plus for fp16/bf16 one rounding of the result to the
+dtype (2^-10 or 2^-7 of |r|; the oracle gets the same rounded inputs and
+grad_out).  Every gradient element is a sum of at most a few thousand fp32
+products (grad_weight: N*Ho*Wo of them, accumulated by atomic adds in any
+order), so fp32 rounding stays orders of magnitude below it.
 The GPU splits each sample coordinate into cell and fraction from the fp32
 offset exactly as the oracle does from the same value, so both
 differentiate on the same cell.
@@ -40,31 +42,38 @@ CASES = {
 def grads_gpu(pr, inp, go, trace=None):
     g = {k: (v.to(DEV) if v is not None else None) for k, v in inp.items()}
     op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups)
-    out = mdcn.backward(op, g["x"], g["offset"], g["mask"], g["weight"], go.to(DEV),
-                        with_bias=pr.bias, trace=trace)
+    out = mdcn.backward(op, g["x"], g["offset"], g["mask"], g["weight"],
+                        go.to(g["x"].dtype).to(DEV), with_bias=pr.bias, trace=trace)
     torch.cuda.synchronize()
     return {k: (v.cpu().double().numpy() if v is not None else None) for k, v in out.items()}
 
 
-def check(got, ref, name):
+ROUNDING = {"f32": 0.0, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}
+
+
+def check(got, ref, name, dtype="f32"):
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     err = np.abs(got - ref)
-    bound = 1e-4 * np.maximum(np.abs(ref), rms)
+    bound = 1e-4 * np.maximum(np.abs(ref), rms) + ROUNDING[dtype] * np.abs(ref)
+    if dtype == "f16":
+        bound = bound + 2.0 ** -24                    # fp16 subnormal spacing
     assert (err <= bound).all(), (name, float(err.max()), float((err / np.maximum(bound, 1e-300)).max()))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_backward_matches_oracle(name):
+def test_backward_matches_oracle(name, dtype):
     pr = CASES[name]
-    inp = workloads.generate(pr, "f32", seed=11)
+    inp = workloads.generate(pr, dtype, seed=11)
     ho, wo = pr.out_hw()
     go = torch.randn((pr.N, pr.Co, ho, wo), generator=torch.Generator().manual_seed(12))
-    print("backward", name, flush=True)
+    go = go.to(workloads.DTYPES[dtype])                # the values both sides see
+    print("backward", name, dtype, flush=True)
     ref = oracle.backward(inp["x"], inp["offset"], inp["mask"], inp["weight"], go,
                           with_bias=pr.bias, **pr.attrs())
     got = grads_gpu(pr, inp, go)
     for k in ("x", "offset", "mask", "weight") + (("bias",) if pr.bias else ()):
-        check(got[k], ref[k], (name, k))
+        check(got[k], ref[k], (name, k), dtype)
     if not pr.bias:
         assert got["bias"] is None
 

@@ -39,6 +39,9 @@ CASES = [
     ("depthwise", Problem(N=2, C=24, Co=48, H=13, W=13, groups=24, deformable_groups=3,
                           offset_dist=("uniform", 8.0), mask_dist=("uniform_zeros", 0.1)),
      "f32", mdcn.MDCN_PATH_DEPTHWISE),
+    ("gather_gemm_fp8", Problem(N=2, C=32, Co=48, H=15, W=13, deformable_groups=2,
+                                offset_dist=("normal", 2.0)), "f16",
+     mdcn.MDCN_PATH_GATHER_GEMM_FP8),
 ]
 
 
