@@ -262,6 +262,31 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    # Per-call device time, warm (back to back) and cold (a 1 GiB scrub
+    # buffer written between calls, outside the events, so that the 256 MB
+    # Infinity Cache and the L2 hold none of the inputs): events on the
+    # stream the forward runs on; median, p10, p90.
+    def per_call_ms(scrub):
+        times = []
+        for i in range(args.steps):
+            if scrub is not None:
+                scrub.fill_(i & 255)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        q = np.percentile(np.asarray(times), [50, 10, 90])
+        return {"median_ms": round(float(q[0]), 5), "p10_ms": round(float(q[1]), 5),
+                "p90_ms": round(float(q[2]), 5)}
+    warm_calls = per_call_ms(None)
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold_calls = per_call_ms(scrub)
+    cold_calls["scrub_bytes"] = scrub.numel()
+    del scrub
+
     # Per-kernel device time: HIP events around every launch, on the stream
     # the kernels run on.
     trace = mdcn.Trace(capacity=64 * args.steps + 64)
@@ -348,6 +373,7 @@ def main(argv=None) -> int:
                    "parallelism": "single GPU",
                    "launch": "graph replay" if args.graph else "eager"},
         "hbm_gbs_effective": round(min_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "per_call": {"warm": warm_calls, "cold": cold_calls},
         "plan": plan,
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
