@@ -345,6 +345,27 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
     pt.W = 1;
     pt.dtype = MDCN_F32;               // the accumulator is fp32 whatever the dtype
     pt.elem = 4;
+    // the column gradient on the MFMA GEMM: C(p, kk) = sum_m goT[p][m] * wT[kk][m],
+    // i.e. the GEMM kernel with rows = pixels, columns = kk, contraction = Co
+    float *goT = reinterpret_cast<float *>(ws + l.goT_off);
+    float *wT = reinterpret_cast<float *>(ws + l.wT_off);
+    Problem pq = p;                    // the GEMM's view
+    pq.G = 1; pq.Mg = p.P; pq.Co = p.P; pq.P = l.Kp;
+    Plan qp{};
+    qp.path = Path::GatherGemm;
+    qp.Kp = p.Co;
+    qp.gemm_tile = mdcn::gemm_tile_for(pq, 1);
+    Problem pgo = p;                   // grad_out [Co][P] -> [P][Co]: the NHWC transpose
+    pgo.C = p.Co; pgo.H = p.Ho; pgo.W = p.Wo;
+    Problem pwt = p;                   // packed weight [Co][Kp] -> [Kp][Co]
+    pwt.C = p.Co; pwt.H = l.Kp; pwt.W = 1;
+    if (l.mfma_col && !empty) {
+        err = rec.run(mdcn::K_BWD_TO_NCHW, [&] {
+            return mdcn::launch_to_nhwc(pwt, 1, wpack, wT, stream);
+        });
+        if (err != hipSuccess)
+            return MDCN_E_LAUNCH;
+    }
     for (int64_t n = 0; n < p.N && !empty; ++n) {
         const char *xn = static_cast<const char *>(x) + size_t(n) * x_n * e;
         const char *on = static_cast<const char *>(offset) + size_t(n) * off_n * e;
@@ -361,7 +382,12 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
             });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_BWD_COL_GEMM, [&] {
-                return mdcn::launch_bwd_col_gemm(p, l, wpack, gn, gcol, stream);
+                if (!l.mfma_col)
+                    return mdcn::launch_bwd_col_gemm(p, l, wpack, gn, gcol, stream);
+                hipError_t r = mdcn::launch_to_nhwc(pgo, 1, gn, goT, stream);
+                return r != hipSuccess
+                           ? r
+                           : mdcn::launch_gemm(pq, qp, 1, goT, wT, nullptr, nullptr, gcol, stream);
             });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_BWD_ZERO, [&] {

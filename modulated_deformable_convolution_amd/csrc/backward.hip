@@ -278,7 +278,17 @@ BackwardLayout backward_layout(const Problem &p)
     l.col_off = l.gxn_off + (p.dtype == MDCN_F32 ? 0 : al(size_t(p.C * p.H * p.W) * 4));
     l.gcol_off = l.col_off + al(size_t(p.G * p.P * l.Kp) * 4);
     l.wacc_off = l.gcol_off + al(size_t(p.G * p.P * l.Kp) * 4);
-    l.bytes = l.wacc_off + al(size_t(p.Co * l.Kp) * 4);
+    l.goT_off = l.wacc_off + al(size_t(p.Co * l.Kp) * 4);
+    l.wT_off = l.goT_off;
+    l.bytes = l.goT_off;
+    // the column gradient on the MFMA GEMM (fp32, one group, rows of Co
+    // floats that are whole 128-byte lines): grad_out and the packed weight
+    // transposed so that both operands run along the output channels
+    l.mfma_col = p.dtype == MDCN_F32 && p.G == 1 && p.Co % 32 == 0 && p.P >= 1;
+    if (l.mfma_col) {
+        l.wT_off = l.goT_off + al(size_t(p.P * p.Co) * 4);
+        l.bytes = l.wT_off + al(size_t(l.Kp * p.Co) * 4);
+    }
     return l;
 }
 

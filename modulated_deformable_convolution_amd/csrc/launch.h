@@ -135,9 +135,13 @@ hipError_t launch_depthwise(const Problem &p, int64_t cnt, const void *x, const 
 // same in NCHW (fp32), its columns [G][P][Kp] (tap-major, as the forward's
 // gather writes them, fp32), the column gradient in the same layout, and the
 // weight-gradient accumulator [Co][Kp] (fp32).
+// With mfma_col, also grad_out of the image transposed to [P][Co] and the
+// packed weight transposed to [Kp][Co] (fp32), for the MFMA GEMM.
 struct BackwardLayout {
     int64_t Kp;
     size_t wpack_off, xt_off, gxt_off, gxn_off, col_off, gcol_off, wacc_off, bytes;
+    size_t goT_off, wT_off;
+    bool mfma_col;
 };
 BackwardLayout backward_layout(const Problem &p);
 hipError_t launch_bwd_fill_zero(float *ptr, int64_t n, hipStream_t stream);

@@ -91,6 +91,8 @@ bool choose_fused_tile(const Problem &p, int64_t chunk, FusedTile *out)
 
 }  // namespace
 
+GemmTile gemm_tile_for(const Problem &p, int64_t chunk) { return choose_gemm_tile(p, chunk); }
+
 size_t dtype_size(mdcn_dtype t)
 {
     switch (t) {

@@ -113,6 +113,8 @@ constexpr int64_t kMaxCoord = int64_t(1) << 24;        // spatial extents and an
 constexpr size_t kLdsBytes = size_t(160) << 10;        // LDS of one gfx950 workgroup
 
 size_t dtype_size(mdcn_dtype t);
+// GEMM tile for a gather + GEMM chunk of `chunk` images (MDCN_GEMM_TILE overrides).
+GemmTile gemm_tile_for(const Problem &p, int64_t chunk);
 // Depthwise: the widest LDS entry (bytes of channels per plane position) the
 // staged kernel can use for this problem -- its channels share an offset
 // group and the zero-ringed plane fits in LDS -- or 0 when none can.

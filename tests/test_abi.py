@@ -474,7 +474,10 @@ def test_backward_entry_points():
     col = 25600 * 2304 * 4            # columns and their gradient (fp32)
     acc = 256 * 2304 * 4
     b = mdcn.mdcn_backward_workspace_bytes(op, mdcn.MDCN_F32, DIMS)
-    assert b == 256 + 256 * 2304 * 4 + hw * 4 + hw * 4 + 2 * col + acc
+    # fp32 with one group and Co % 32 == 0: the column gradient on the MFMA
+    # GEMM, with grad_out [P][Co] and the packed weight [Kp][Co] transposed
+    mfma = 25600 * 256 * 4 + 2304 * 256 * 4
+    assert b == 256 + 256 * 2304 * 4 + hw * 4 + hw * 4 + 2 * col + acc + mfma
     for dt in (mdcn.MDCN_F16, mdcn.MDCN_BF16):
         b16 = mdcn.mdcn_backward_workspace_bytes(op, dt, DIMS)
         assert b16 == 256 + 256 * 2304 * 2 + hw * 2 + 2 * hw * 4 + 2 * col + acc
