@@ -357,6 +357,8 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
     qp.gemm_tile = mdcn::gemm_tile_for(pq, 1);
     Problem pgo = p;                   // grad_out [Co][P] -> [P][Co]: the NHWC transpose
     pgo.C = p.Co; pgo.H = p.Ho; pgo.W = p.Wo;
+    Problem pcol = p;                  // columns [P][Kp] -> [Kp][P]
+    pcol.C = p.P; pcol.H = l.Kp; pcol.W = 1;
     Problem pwt = p;                   // packed weight [Co][Kp] -> [Kp][Co]
     pwt.C = p.Co; pwt.H = l.Kp; pwt.W = 1;
     if (l.mfma_col && !empty) {
@@ -378,7 +380,27 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
             });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_BWD_WEIGHT_GEMM, [&] {
-                return mdcn::launch_bwd_weight_gemm(p, l, gn, col, wacc, stream);
+                if (l.wsplit == 0)
+                    return mdcn::launch_bwd_weight_gemm(p, l, gn, col, wacc, stream);
+                // columns [P][Kp] -> [Kp][P] (into the column-gradient buffer),
+                // then per pixel chunk s: part[s][m][kk] = sum over the chunk's
+                // pixels of g[m][p] * colT[kk][p], then summed into wacc
+                const int64_t S = l.wsplit, pc = p.P / S;
+                hipError_t r = mdcn::launch_to_nhwc(pcol, 1, col, gcol, stream);
+                if (r != hipSuccess)
+                    return r;
+                Problem pw = p;
+                pw.G = S; pw.Mg = p.Co; pw.Co = S * p.Co; pw.P = l.Kp;
+                Plan wp{};
+                wp.path = Path::GatherGemm;
+                wp.Kp = pc;
+                wp.gemm_tile = mdcn::gemm_tile_for(pw, 1);
+                const mdcn::GemmStrides st{uint32_t(pc * 4), uint32_t(p.P * 4), uint32_t(p.P * 4),
+                                           uint64_t(pc) * 4, uint64_t(pc) * 4};
+                r = mdcn::launch_gemm_strided(pw, wp, gn, gcol, col, st, stream);
+                return r != hipSuccess ? r
+                                       : mdcn::launch_bwd_reduce_parts(col, wacc, p.Co * l.Kp,
+                                                                       int(S), stream);
             });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_BWD_COL_GEMM, [&] {

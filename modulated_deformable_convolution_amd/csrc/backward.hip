@@ -255,6 +255,21 @@ __global__ __launch_bounds__(256) void sample_grad_kernel(SampleArgs a)
     }
 }
 
+// acc[t] += sum over s < S of part[s * n + t] (the pixel chunks' partial
+// weight gradients).
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float *__restrict__ part,
+                                                           float *__restrict__ acc, int64_t n,
+                                                           int S)
+{
+    const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (t >= n)
+        return;
+    float v = acc[t];
+    for (int s = 0; s < S; ++s)
+        v += part[int64_t(s) * n + t];
+    acc[t] = v;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void convert_kernel(const float *__restrict__ src,
                                                       T *__restrict__ dst, int64_t n)
@@ -285,6 +300,21 @@ BackwardLayout backward_layout(const Problem &p)
     // floats that are whole 128-byte lines): grad_out and the packed weight
     // transposed so that both operands run along the output channels
     l.mfma_col = p.dtype == MDCN_F32 && p.G == 1 && p.Co % 32 == 0 && p.P >= 1;
+    // the weight gradient on the MFMA GEMM as well: the image's pixels split
+    // into S chunks of Pc (a multiple of 32 floats = whole 128-byte K steps,
+    // at most 512) that run as the GEMM's groups; the columns transposed to
+    // [Kp][P] (in the column-gradient buffer, written later) and the S
+    // partial [Co][Kp] results (in the column buffer, consumed by then)
+    l.wsplit = 0;
+    if (l.mfma_col && p.P % 32 == 0) {
+        for (int64_t d = 16; d >= 1; --d) {
+            const int64_t pc = 32 * d;
+            if (p.P % pc == 0 && (p.P / pc) * p.Co <= p.P) {
+                l.wsplit = p.P / pc;
+                break;
+            }
+        }
+    }
     if (l.mfma_col) {
         l.wT_off = l.goT_off + al(size_t(p.P * p.Co) * 4);
         l.bytes = l.wT_off + al(size_t(l.Kp * p.Co) * 4);
@@ -488,6 +518,16 @@ hipError_t launch_bwd_convert(const Problem &p, const float *src, void *dst, int
     case MDCN_BF16: return convert_t<bf16_t>(src, dst, n, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_reduce_parts(const float *part, float *acc, int64_t n, int S,
+                                   hipStream_t s)
+{
+    if (n <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(reduce_parts_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, part,
+                       acc, n, S);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_weight_out(const Problem &p, const BackwardLayout &l, const float *acc,

@@ -45,6 +45,9 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int has_bias;
     int vec_out;        // 16-byte output stores allowed (P and `out` aligned to them)
+    uint32_t kb;        // bytes of K per row (a multiple of STEP)
+    uint32_t sa, sb;    // bytes between consecutive rows of A, of B
+    uint64_t ga, gb;    // bytes between the groups' blocks of A, of B
 };
 
 // One pipeline step's operand loads of one wave: IPW instructions of 8 tile
@@ -98,11 +101,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
     // wave index as a scalar: LDS destinations of the loads must be wave-uniform
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
 
-    const uint32_t row_bytes = uint32_t(a.Kp) * uint32_t(sizeof(OP));
-    const char *Ag = reinterpret_cast<const char *>(A) + size_t(g) * a.Mg * row_bytes;
-    const char *Bg = reinterpret_cast<const char *>(B) + size_t(g) * a.Ncols * row_bytes;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ag, uint32_t(a.Mg) * row_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, uint32_t(a.Ncols) * row_bytes);
+    const char *Ag = reinterpret_cast<const char *>(A) + size_t(g) * a.ga;
+    const char *Bg = reinterpret_cast<const char *>(B) + size_t(g) * a.gb;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ag, uint32_t(a.Mg - 1) * a.sa + a.kb);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, uint32_t(a.Ncols - 1) * a.sb + a.kb);
 
     // Global byte offset of what this lane fetches in each of its wave's load
     // instructions (rows past the edge clamped); the same for every step.
@@ -112,9 +114,9 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
         const int row = (wave * IPW + t) * 8 + (lane >> 3);     // tile row (A rows first)
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
         if (row < BM)
-            voff[t] = uint32_t(min(m0 + row, a.Mg - 1)) * row_bytes + chunk * 16;
+            voff[t] = uint32_t(min(m0 + row, a.Mg - 1)) * a.sa + chunk * 16;
         else
-            voff[t] = uint32_t(min(n0 + row - BM, a.Ncols - 1)) * row_bytes + chunk * 16;
+            voff[t] = uint32_t(min(n0 + row - BM, a.Ncols - 1)) * a.sb + chunk * 16;
     }
 
     const int wm = wave % WAVES_M, wn = wave / WAVES_M;
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    const int steps = int(row_bytes / STEP);
+    const int steps = int(a.kb / STEP);
     issue_step<BM, BN, NW, STEP>(smem, ra, rb, voff, wave, 0);
     for (int st = 0; st < steps; ++st) {
         const int stage = st & 1;
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
 template <typename T, typename OP, int BM, int BN, int WM, int WN>
 hipError_t gemm_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                     const void *col, const void *bias, const float *rscale, void *out,
-                    hipStream_t s)
+                    const GemmStrides *st, hipStream_t s)
 {
     constexpr int STEP = 128;
     GemmArgs a;
@@ -176,6 +178,15 @@ hipError_t gemm_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void 
     a.tiles_n = int((a.Ncols + BN - 1) / BN);
     a.has_bias = bias != nullptr;
     a.vec_out = (p.P % (16 / int(sizeof(T))) == 0) && reinterpret_cast<uintptr_t>(out) % 16 == 0;
+    // rows of Kp elements, one block of rows per group, unless given
+    const uint32_t row_bytes = uint32_t(plan.Kp) * uint32_t(sizeof(OP));
+    a.kb = st ? st->kb : row_bytes;
+    a.sa = st ? st->sa : row_bytes;
+    a.sb = st ? st->sb : row_bytes;
+    a.ga = st ? st->ga : uint64_t(a.Mg) * row_bytes;
+    a.gb = st ? st->gb : uint64_t(a.Ncols) * row_bytes;
+    if (a.kb % STEP != 0 || a.kb == 0)
+        return hipErrorInvalidValue;
     const uint64_t blocks = uint64_t(p.G) * a.tiles_m * a.tiles_n;
     hipLaunchKernelGGL((gemm_bias_kernel<T, OP, BM, BN, WM, WN, STEP>), dim3(uint32_t(blocks)),
                        dim3(WM * WN * 64), 0, s, static_cast<const OP *>(wpack),
@@ -186,26 +197,35 @@ hipError_t gemm_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void 
 
 template <typename T, typename OP>
 hipError_t gemm_t(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                  const void *col, const void *bias, const float *rs, void *out, hipStream_t s)
+                  const void *col, const void *bias, const float *rs, void *out, hipStream_t s,
+                  const GemmStrides *st = nullptr)
 {
     switch (plan.gemm_tile) {
     case GemmTile::M256_N256_W2x4:
-        return gemm_cfg<T, OP, 256, 256, 2, 4>(p, plan, cnt, wpack, col, bias, rs, out, s);
+        return gemm_cfg<T, OP, 256, 256, 2, 4>(p, plan, cnt, wpack, col, bias, rs, out, st, s);
     case GemmTile::M256_N128_W4x2:
-        return gemm_cfg<T, OP, 256, 128, 4, 2>(p, plan, cnt, wpack, col, bias, rs, out, s);
+        return gemm_cfg<T, OP, 256, 128, 4, 2>(p, plan, cnt, wpack, col, bias, rs, out, st, s);
     case GemmTile::M128_N256_W2x4:
-        return gemm_cfg<T, OP, 128, 256, 2, 4>(p, plan, cnt, wpack, col, bias, rs, out, s);
+        return gemm_cfg<T, OP, 128, 256, 2, 4>(p, plan, cnt, wpack, col, bias, rs, out, st, s);
     case GemmTile::M128_N128_W2x2:
-        return gemm_cfg<T, OP, 128, 128, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, s);
+        return gemm_cfg<T, OP, 128, 128, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, st, s);
     case GemmTile::M128_N64_W2x2:
-        return gemm_cfg<T, OP, 128, 64, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, s);
+        return gemm_cfg<T, OP, 128, 64, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, st, s);
     case GemmTile::M64_N128_W2x2:
-        return gemm_cfg<T, OP, 64, 128, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, s);
+        return gemm_cfg<T, OP, 64, 128, 2, 2>(p, plan, cnt, wpack, col, bias, rs, out, st, s);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+hipError_t launch_gemm_strided(const Problem &p, const Plan &plan, const void *a, const void *b,
+                               void *out, const GemmStrides &st, hipStream_t stream)
+{
+    if (p.dtype != MDCN_F32)
+        return hipErrorInvalidValue;
+    return gemm_t<float, float>(p, plan, 1, a, b, nullptr, nullptr, out, stream, &st);
+}
 
 hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                        const void *col, const void *bias, const float *wscale, void *out,

@@ -82,6 +82,17 @@ hipError_t launch_gather_f32(const Problem &p, const Plan &plan, int64_t cnt, co
                              hipStream_t stream);
 
 // out[n][g*Mg + m][pix] = sum_kk wpack[g][m][kk] * col[g][n*P + pix][kk] (+ bias);
+// The same fp32 GEMM (no bias) with explicit operand geometry: each row of A
+// and of B holds kb bytes of K (a multiple of 128), consecutive rows sa / sb
+// bytes apart, group g's blocks at A + g*ga and B + g*gb; out as above with
+// cnt = 1 (rows g*Mg + m, p.P columns; the columns are B's p.P rows).
+struct GemmStrides {
+    uint32_t kb, sa, sb;
+    uint64_t ga, gb;
+};
+hipError_t launch_gemm_strided(const Problem &p, const Plan &plan, const void *a, const void *b,
+                               void *out, const GemmStrides &st, hipStream_t stream);
+
 // FP8 path: E4M3 operands and the sums times wscale[g*Mg + m] before the bias
 // (wscale null otherwise).
 hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
@@ -142,7 +153,11 @@ struct BackwardLayout {
     size_t wpack_off, xt_off, gxt_off, gxn_off, col_off, gcol_off, wacc_off, bytes;
     size_t goT_off, wT_off;
     bool mfma_col;
+    int64_t wsplit;    // > 0: the weight gradient on the MFMA GEMM in wsplit pixel chunks
 };
+// acc[t] += sum over s < S of part[s*n + t].
+hipError_t launch_bwd_reduce_parts(const float *part, float *acc, int64_t n, int S,
+                                   hipStream_t stream);
 BackwardLayout backward_layout(const Problem &p);
 hipError_t launch_bwd_fill_zero(float *ptr, int64_t n, hipStream_t stream);
 // n zeros of the problem's dtype.

@@ -36,6 +36,9 @@ CASES = {
     "depthwise": Problem(N=2, C=8, Co=8, H=9, W=9, groups=8),
     "grid_smaller": Problem(N=1, C=12, Co=8, H=11, W=11, Ho=7, Wo=9),
     "wide_channels": Problem(N=1, C=128, Co=64, H=16, W=16, offset_dist=("normal", 2.0)),
+    # fp32: both contractions on the MFMA GEMM, the weight gradient in two
+    # pixel chunks of 512 (P = 1024)
+    "mfma_split": Problem(N=2, C=32, Co=64, H=32, W=32, offset_dist=("normal", 1.0)),
 }
 
 
