@@ -35,34 +35,34 @@ DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
 # taken on (sha256 of the listed files, first 16 hex digits).
 MEASURED_TRAFFIC = {
     ("deform_gather_fp8", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (40452 * 2 + 230400) * 1024,
+        "bytes": (40485 * 2 + 230400) * 1024,
         "sources": ('gather.hip', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "830b69d6f3c86deb",
+        "sha": "8e5df729feb0ab73",
     },
     ("gemm_fp8_bias", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (119923 * 2 + 51200) * 1024,
+        "bytes": (119933 * 2 + 51200) * 1024,
         "sources": ('gemm.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp'),
-        "sha": "d894354be95dd419",
+        "sha": "9f319b58a68cb257",
     },
     ("window_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (133672 * 2 + 130696) * 1024,
+        "bytes": (133611 * 2 + 131151) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "99bce66d36944154",
+        "sha": "3e2e702a0bc73aaf",
     },
     ("fused_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (53959 * 2 + 51200) * 1024,
+        "bytes": (53919 * 2 + 51200) * 1024,
         "sources": ('fused.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "70e2bc91f997914f",
+        "sha": "2bf816c7db5a8adf",
     },
     ("gemm_bias", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (119917 * 2 + 25600) * 1024,
+        "bytes": (119931 * 2 + 25600) * 1024,
         "sources": ('gemm.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp'),
-        "sha": "d894354be95dd419",
+        "sha": "9f319b58a68cb257",
     },
     ("deform_gather", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (23279 * 2 + 230400) * 1024,
+        "bytes": (23331 * 2 + 230400) * 1024,
         "sources": ('gather.hip', 'device_common.h', 'plan.cpp'),
-        "sha": "3b95bf39cab34874",
+        "sha": "5fd5019368be82e8",
     },
     ("depthwise_direct", "depthwise_n8_c256_96x96", "f32"): {
         "bytes": (47362 * 2 + 73728) * 1024,
