@@ -127,16 +127,17 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, int64_t n)
 }
 
 // grad_bias[co] = sum over images and pixels of g[n][co][p]; one workgroup per co.
+// (1024 threads: one workgroup per output channel sums N*P values)
 template <typename T>
-__global__ __launch_bounds__(256) void bias_grad_kernel(const T *__restrict__ g,
-                                                        T *__restrict__ gb, int N, int Co, int P)
+__global__ __launch_bounds__(1024) void bias_grad_kernel(const T *__restrict__ g,
+                                                         T *__restrict__ gb, int N, int Co, int P)
 {
-    __shared__ float part[4];
+    __shared__ float part[16];
     const int co = int(blockIdx.x);
     float s = 0.0f;
     for (int n = 0; n < N; ++n) {
         const T *row = g + (int64_t(n) * Co + co) * P;
-        for (int p = int(threadIdx.x); p < P; p += 256)
+        for (int p = int(threadIdx.x); p < P; p += 1024)
             s += to_f32(row[p]);
     }
 #pragma unroll
@@ -145,8 +146,12 @@ __global__ __launch_bounds__(256) void bias_grad_kernel(const T *__restrict__ g,
     if ((threadIdx.x & 63) == 0)
         part[threadIdx.x >> 6] = s;
     __syncthreads();
-    if (threadIdx.x == 0)
-        gb[co] = from_f32<T>((part[0] + part[1]) + (part[2] + part[3]));
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int w = 0; w < 16; ++w)
+            t += part[w];
+        gb[co] = from_f32<T>(t);
+    }
 }
 
 // grad_weight[g*Mg + m][c'][k] = acc[g][m][k*Cg + c'] (the accumulator is in
@@ -353,7 +358,7 @@ hipError_t fill_zero_t(void *ptr, int64_t n, hipStream_t s)
 template <typename T>
 hipError_t bias_t(const Problem &p, const void *g, void *gb, hipStream_t s)
 {
-    hipLaunchKernelGGL((bias_grad_kernel<T>), dim3(unsigned(p.Co)), dim3(256), 0, s,
+    hipLaunchKernelGGL((bias_grad_kernel<T>), dim3(unsigned(p.Co)), dim3(1024), 0, s,
                        static_cast<const T *>(g), static_cast<T *>(gb), int(p.N), int(p.Co),
                        int(p.P));
     return hipGetLastError();
