@@ -202,7 +202,11 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
                                                              : mdcn::K_PREP_NHWC,
                           [&] {
                               return mdcn::launch_prep(p, plan, cnt, xc, xt, weight, wpack,
-                                                       win_flags, int(plan.win_slots), wscale,
+                                                       win_flags,
+                                                       plan.path == Path::Window
+                                                           ? int(plan.win_slots) + 1
+                                                           : 0,
+                                                       wscale,
                                                        stream);
                           });
         else if (plan.path == Path::Window)

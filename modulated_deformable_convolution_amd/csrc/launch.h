@@ -112,10 +112,11 @@ hipError_t launch_fused(const Problem &p, const Plan &plan, int64_t cnt, const v
 // (launch_to_channel_blocks).
 // Scratch of the windowed kernel: `slots` partial-sum slots of 256 KiB (one
 // per workgroup; a tile split between two workgroups passes its first
-// chunks' sums through the first one's slot) and one flag per slot, zeroed
-// before the forward (launch_pack_weight_steps); `epoch` (> 0) is the value
-// a launch publishes its flags with, distinct for every launch of one
-// forward.
+// chunks' sums through the first one's slot), one flag per slot and a status
+// word after them (flags[slots]), all zeroed before the forward
+// (launch_pack_weight_steps); `epoch` (> 0) is the value a launch publishes
+// its flags with, distinct for every launch of one forward.  A hand-over
+// wait that gives up sets the status word to kWindowGaveUp.
 struct WindowScratch {
     float *partial;
     uint32_t *flags;

@@ -526,14 +526,10 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
         if (plan.path == Path::Window) {
             if (!choose_window(p, &plan.win_tile, &plan.win_margin))
                 return MDCN_E_PATH;
-            // MDCN_WIN_LEAD=3|5|7 overrides (for tuning); MDCN_WIN_CTAS=<n>
-            // caps the workgroups (more tiles split between two of them)
-            plan.win_lead = kWindowMaxLead;
-            if (const char *env = std::getenv("MDCN_WIN_LEAD")) {
-                const int v = std::atoi(env);
-                if (v == 3 || v == 5 || v == 7)
-                    plan.win_lead = v;
-            }
+            // the weight copies run 5 K steps ahead (the kernel's barrier
+            // schedule needs exactly that); MDCN_WIN_CTAS=<n> caps the
+            // workgroups (more tiles split between two of them)
+            plan.win_lead = kWindowLead;
             plan.win_max_ctas = 0;
             if (const char *env = std::getenv("MDCN_WIN_CTAS")) {
                 const int v = std::atoi(env);
@@ -549,6 +545,17 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
                 if (v >= 0 && v <= 1024)
                     plan.win_seg_cost_x4 = v;
             }
+            // MDCN_WIN_SPIN_LIMIT=<polls> shortens the bounded hand-over wait
+            // (tests force the give-up report with it)
+            plan.win_spin_limit = kWindowSpinLimit;
+            if (const char *env = std::getenv("MDCN_WIN_SPIN_LIMIT")) {
+                const long long v = std::atoll(env);
+                if (v >= 0 && v <= (long long)kWindowSpinLimit)
+                    plan.win_spin_limit = uint32_t(v);
+            }
+            // the chunk's offsets and masks are each one buffer range
+            const int64_t om_img = 2 * p.DG * p.K * p.P * int64_t(p.elem);
+            chunk = std::max<int64_t>(1, std::min<int64_t>(chunk, kMaxPerImage / std::max<int64_t>(om_img, 1)));
             // Partial-sum slots and flags for the chunk's tiles (one slot per
             // workgroup, at most kWindowSlots); with a given workspace, the
             // largest chunk whose layout fits.
@@ -557,7 +564,7 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
                 pl->win_slots = std::min<int64_t>(kWindowSlots, c * pl->win_tiles_per_image);
                 pl->part_off = align_up(pl->xt_off + size_t(c) * pl->xt_bytes_per_image, kAlign);
                 pl->flag_off = pl->part_off + size_t(pl->win_slots) * kWindowSlotBytes;
-                return pl->flag_off + align_up(size_t(pl->win_slots) * 4, kAlign);
+                return pl->flag_off + align_up(size_t(pl->win_slots + 1) * 4, kAlign);
             };
             if (!default_sizing) {
                 if (workspace_bytes < kAlign + layout(1, &plan))
@@ -633,7 +640,7 @@ size_t min_workspace(const Problem &p, const Plan &plan)
     if (plan.path == Path::Window) {
         const int64_t slots = std::min<int64_t>(kWindowSlots, plan.win_tiles_per_image);
         return kAlign + align_up(plan.wpack_bytes + plan.xt_bytes_per_image, kAlign) +
-               size_t(slots) * kWindowSlotBytes + align_up(size_t(slots) * 4, kAlign);
+               size_t(slots) * kWindowSlotBytes + align_up(size_t(slots + 1) * 4, kAlign);
     }
     return kAlign + plan.wpack_bytes + plan.xt_bytes_per_image + plan.col_bytes_per_image;
 }

@@ -70,11 +70,16 @@ constexpr int kWindowTileCount = 4;
 constexpr int kWindowPixels = 1280;      // input positions one LDS window can hold
 constexpr int kWindowZeroBytes = 1024;   // zeroed LDS after each window (>= 16*columns + 32)
 constexpr int64_t kWindowMaxMargin = 8;  // default offset margin around the anchors
-constexpr int kWindowMaxLead = 7;        // weight copies issued this many K steps ahead
+constexpr int kWindowLead = 5;           // weight copies issued this many K steps ahead
 constexpr int64_t kDirectMaxMacs = int64_t(1) << 20;   // automatic direct path, at most
 constexpr uint64_t kDirectMaxOutputs = 0xffffff00ull;  // one 32-bit thread index
 constexpr int64_t kWindowSlots = 256;    // partial-sum slots at most (one per workgroup)
 constexpr size_t kWindowSlotBytes = size_t(256) * 256 * 4;   // fp32 256 x 256 tile
+// Polls of a partial-sum flag before the waiting workgroup gives up (about
+// 4 s at 2 GHz with a 128-cycle sleep between polls): the status word after
+// the flags is then set to kWindowGaveUp and the tile's output to NaN.
+constexpr uint32_t kWindowSpinLimit = 1u << 25;
+constexpr uint32_t kWindowGaveUp = 1u;
 
 // Workspace layout (all offsets 256-byte aligned):
 //   gather + GEMM: [packed weight: G x Mg x Kp] [x in NHWC: chunk images] [columns: G x chunk*P x Kp]
@@ -82,7 +87,7 @@ constexpr size_t kWindowSlotBytes = size_t(256) * 256 * 4;   // fp32 256 x 256 t
 //                  [E4M3 columns: G x chunk*P x Kp bytes], Kp a multiple of 128
 //   fused:         [packed weight: G x Mg x Kp] [x in NHWC: chunk images]
 //   window:        [packed weight] [x in 8-channel blocks: chunk images]
-//                  [partial sums: slots x 256 KiB] [flags: slots x 4 bytes]
+//                  [partial sums: slots x 256 KiB] [flags: slots x 4 bytes] [status: 4 bytes]
 //   depthwise:     [sampling geometry: chunk images x DG x K x 5 x P words]
 struct Plan {
     Path path;
@@ -98,12 +103,14 @@ struct Plan {
     FusedTile fused_tile;
     WindowTile win_tile;
     int64_t win_margin;          // window: pixels of margin around the tile's anchors
-    int win_lead;                // window: K steps the weight copies run ahead (3, 5, 7)
+    int win_lead;                // window: K steps the weight copies run ahead (5)
     int64_t win_tiles_per_image; // window: output tiles (256 x 256) of one image, all groups
     int64_t win_slots;           // window: partial-sum slots
     int64_t win_max_ctas;        // window: cap on the workgroups (0: none; tuning and tests)
     int64_t win_seg_cost_x4;     // window: cost of one tile segment, quarter chunks
+    uint32_t win_spin_limit;     // window: polls of a hand-over flag before giving up
     size_t part_off, flag_off;   // window: offsets of the partial sums and the flags
+                                 // (the status word follows the win_slots flags)
 };
 
 constexpr size_t kColumnBudget = size_t(256) << 20;   // default column-buffer cap

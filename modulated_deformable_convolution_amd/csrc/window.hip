@@ -61,16 +61,23 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kCC = 16;                       // channels per chunk = one MFMA k-group
+constexpr int kWaves = 8;                     // two waves per SIMD, 32 pixels each
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTaps = 9;                      // 3x3 kernels
 constexpr uint32_t kOOB = 0x80000000u;        // a byte offset past every buffer range
 
 // LDS layout (bytes):
+//   A stage s (s = 0..LEAD):    [plane 0: 256 rows x 16][plane 1: 256 rows x 16]
+//                               (eight stages reserved whatever LEAD is, so that every
+//                               A-fragment read is a base register plus an immediate
+//                               offset below 64 KiB)
 //   window buffer b (b = 0, 1): [plane 0: kWinPx x 16][gap][plane 1: kWinPx x 16][zeros]
 //   window copy table:          [instruction t][thread]: source byte offset of the
 //                               thread's 16 bytes of window copy instruction t
 //   parked tile index:          one word per wave (256 bytes reserved)
-//   A stage s (s = 0..LEAD):    [plane 0: 256 rows x 16][plane 1: 256 rows x 16]
-// Plane p of an entry holds channels 8p..8p+7 of the chunk.
+// Plane p of an entry holds channels 8p..8p+7 of the chunk.  At the start of
+// a tile, window buffer 1 (not yet in use) first receives the tile's offsets
+// and masks: [channel of the offset group's 3K][256 tile pixels] elements.
 constexpr int kWinPlane = kWindowPixels * 16;
 // Plane 1 starts this many bytes past the end of plane 0, so that lanes
 // reading the two planes at the same position use different LDS banks.
@@ -80,30 +87,36 @@ constexpr int kWinZeroOff = kPlane1 + kWinPlane;        // start of the zero are
 constexpr int kWinZero = kWindowZeroBytes;
 constexpr int kWinBuf = kWinZeroOff + kWinZero;
 constexpr int kAStage = 256 * 2 * 16;
-constexpr int kWinInstr = 2 * kWindowPixels / 64 / 4;   // window DMA instructions per wave
-constexpr int kWoffOff = 2 * kWinBuf;
-constexpr int kParkOff = kWoffOff + kWinInstr * 256 * 4;  // 4 words: a tile index per wave
-constexpr int kAOff = kParkOff + 256;
+constexpr int kAOff = 0;
+constexpr int kWin0 = 8 * kAStage;                      // window buffer 0
+constexpr int kWinInstr = 2 * kWindowPixels / 64 / kWaves;   // window DMA instructions per wave
+constexpr int kWoffOff = kWin0 + 2 * kWinBuf;
+constexpr int kParkOff = kWoffOff + kWinInstr * kThreads * 4;  // a tile index per wave, a flag
+constexpr int kLdsTotal = kParkOff + 256;
+constexpr int kOmOff = kWin0 + kWinBuf;                 // offsets and masks of a tile
+constexpr int kOmPlanes = 3 * kTaps;                    // 2K offset + K mask channels
+constexpr int kOmInstr = kOmPlanes * 2;                 // 4-byte DMA instructions per tile
+static_assert(kOmPlanes * 256 * 2 <= kWinPlane, "a tile's offsets and masks fit plane 0");
 // A stages: the copy of step s+LEAD is issued in step s, into one of LEAD+1
 // stages.
-constexpr int lds_total(int lead) { return kAOff + (lead + 1) * kAStage; }
-constexpr int kAInstr = kAStage / 1024 / 4;             // A DMA instructions per wave
-constexpr int kEpRow = 256 + 4;                          // epilogue slice row, floats
+constexpr int kAInstr = kAStage / 1024 / kWaves;        // A DMA instructions per wave
 // Cache-policy operand of a buffer access with device scope (the SC1 bit on
 // gfx950): a store is written through to where every XCD sees it and a load
 // is served from there.  The partial sums passed between workgroups use it,
 // so no whole-L2 writeback or invalidate is needed on either side.
 constexpr int kDevScope = 16;
-static_assert(lds_total(kWindowMaxLead) <= int(kLdsBytes), "LDS budget");
-static_assert(32 * kEpRow * 4 <= lds_total(2), "epilogue slice must fit");
-static_assert(kWindowPixels % 128 == 0,
+static_assert(kLdsTotal <= int(kLdsBytes), "LDS budget");
+static_assert(8 * kAStage <= kWin0, "A stages below the window buffers");
+static_assert(kWindowPixels % 64 == 0 && (2 * kWindowPixels / 64) % kWaves == 0,
               "window DMA covers whole wave instructions, none straddling the two planes");
+static_assert(kAStage % (1024 * kWaves) == 0, "A DMA covers whole wave instructions");
 
 struct WinArgs {
     const void *A, *xt, *off, *msk, *bias;   // step-major weight, x blocks, offset, mask, bias|null
     void *out;
     float *partial;                          // partial-sum slots
     uint32_t *flags;                         // one flag per slot
+    uint32_t *status;                        // set to kWindowGaveUp by a hand-over wait that gave up
     int Mg, Kp, Co, P, Ho, Wo;
     int C, H, W, Cg, nch;          // nch: chunks of 16 channels per group
     int sh, sw, ph, pw, dh, dw;
@@ -112,7 +125,10 @@ struct WinArgs {
     int epoch;                     // value that marks partial sums published by this launch
     int offC, mskC, Cdg;           // offset / mask channels per image; C / deformable_group
     int has_bias, vec_out;
+    int om_lds;                    // offsets and masks reach LDS by DMA (4-byte aligned pairs)
+    uint32_t spin_limit;           // polls of a hand-over flag before giving up
     uint32_t img_bytes, chunk_bytes, a_bytes;
+    uint32_t off_bytes, msk_bytes; // offsets / masks of the chunk's images
     // unit range of each workgroup slot (slot j = run * per + index in run)
     uint32_t bounds[kWindowSlots + 1];
 };
@@ -162,6 +178,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void dma16(uint32_t lds, v4i rsrc, uint32_t voff, uint32_t soff)
 {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+
+// 4 bytes per lane from buffer offset voff + soff into LDS at lds + 4*lane
+// (the same contract as dma16).
+__device__ __forceinline__ void dma4(uint32_t lds, v4i rsrc, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  :
                  : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory");
@@ -235,7 +261,8 @@ __device__ __forceinline__ uint4 blend(const uint4 &c0, const uint4 &c1, const u
 }
 
 template <typename T, int TH, int TW, int LEAD>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(2, 2)))
 void window_kernel(WinArgs args)
 {
     (void)args;
@@ -256,8 +283,13 @@ void window_kernel(WinArgs args)
             wo = wo0 + n % TW;
         }
     };
-    static_assert(LEAD >= 2 && LEAD + 1 <= 9, "copies lead by 2..8 steps");
-    constexpr int kAStages = LEAD + 1;
+    // Eight A stages, a barrier every third step (k = 0, 3, 6 of a chunk):
+    // a copy issued in step y overwrites A(y + LEAD - 8), which every wave
+    // consumed before the last barrier (y - 2 or later) when LEAD <= 5, and
+    // A(t), read in step t - 1, was issued in step t - LEAD, at least two
+    // steps before the last barrier, which waited for it when LEAD >= 5.
+    static_assert(LEAD == 5, "a barrier every third step needs a copy lead of 5 steps");
+    constexpr int kAStages = 8;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const uint32_t lds0 = lds_addr(smem);
@@ -265,9 +297,10 @@ void window_kernel(WinArgs args)
 
     // zero areas of both window buffers (read by lanes whose sample is not
     // in the window); no copy ever writes them
-    for (int i = int(threadIdx.x); i < 2 * kWinZero / 8; i += 256) {
+    for (int i = int(threadIdx.x); i < 2 * kWinZero / 8; i += kThreads) {
         const int b = i / (kWinZero / 8), o = i - b * (kWinZero / 8);
-        *reinterpret_cast<uint2 *>(smem + b * kWinBuf + kWinZeroOff + o * 8) = make_uint2(0u, 0u);
+        *reinterpret_cast<uint2 *>(smem + kWin0 + b * kWinBuf + kWinZeroOff + o * 8) =
+            make_uint2(0u, 0u);
     }
 
     // This workgroup's share of the (tile, chunk) units: [u0, u1), split
@@ -329,9 +362,11 @@ void window_kernel(WinArgs args)
             return;
         tile = int((r.u1 - 1) / uint32_t(a->nch));   // the range's last tile comes first
     }
-    // per-wave LDS word that holds the tile index across the main loop
+    // per-wave LDS word that holds the tile index across the main loop, and
+    // the word that says whether this tile's hand-over wait gave up
     int *tile_park = reinterpret_cast<int *>(smem + kParkOff) +
                      __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    int *gave_up_l = reinterpret_cast<int *>(smem + kParkOff) + 32;
 
     for (;;) {
         // Every lane- and argument-derived value is derived afresh per tile
@@ -344,6 +379,8 @@ void window_kernel(WinArgs args)
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int half = lane >> 5;                  // plane: channels 8*half..+8 of a chunk
+        // the wave's 32 pixels (tile pixels 32*wave ..+32; lane: 32*wave + lane%32)
+        const int px_n = wave * 32 + (lane & 31);
         KArgs a = fresh_args(pa);
         const v4i rx = srd(a->xt, a->chunk_bytes);
         const uint32_t hw16 = uint32_t(a->H * a->W) * 16;   // bytes of one 8-channel block plane
@@ -351,7 +388,6 @@ void window_kernel(WinArgs args)
         const uint32_t a_lane = uint32_t(half * (kAStage / 2) + (lane & 31) * 16);
         float zero;
         asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-        const int nch = a->nch;
         const TileInfo ti = tile_info(a, range_of(a), tile);
         const int c_lo = ti.c_lo, c_hi = ti.c_hi;
         const int m0 = ti.m0, ho0 = ti.ho0, wo0 = ti.wo0, img = ti.img;
@@ -362,15 +398,44 @@ void window_kernel(WinArgs args)
         const int q = (g * a->Cg) / a->Cdg;              // the group's offset group
         const v4i ra =
             srd(static_cast<const char *>(a->A) + size_t(g) * a->a_bytes, a->a_bytes);
+        // every wave is done with the previous tile's LDS (window buffers
+        // and copy table): the first of them is about to be overwritten
+        lds_barrier();
         if (lane == 0)
             *tile_park = tile;
+
+        // ---- the tile's offsets and masks, by DMA into window buffer 1
+        // (idle until the main loop's first step), issued before the copies
+        // so that they do not queue behind them: instruction j carries
+        // channel j/2 of the offset group's 2K offset and K mask channels
+        // for tile pixels 128*(j%2) + 2*lane, +1 (an aligned 4-byte pair).
+        const bool om_lds = a->om_lds != 0;
+        if (om_lds) {
+            const v4i ro = srd(a->off, a->off_bytes);
+            const v4i rm = srd(a->msk, a->msk_bytes);
+            for (int j = wave; j < kOmInstr; j += kWaves) {
+                const int plane = j >> 1;
+                const int n = (j & 1) * 128 + 2 * lane;
+                int ho, wo;
+                out_pixel(n, ho0, wo0, a->Wo, ho, wo);
+                const bool ok = ho < a->Ho && wo < a->Wo;
+                const bool is_off = plane < 2 * kTaps;
+                const uint32_t chan =
+                    is_off ? uint32_t(img * a->offC + q * 2 * kTaps + plane)
+                           : uint32_t(img * a->mskC + q * kTaps + plane - 2 * kTaps);
+                const uint32_t voff =
+                    ok ? (chan * uint32_t(a->P) + uint32_t(ho * a->Wo + wo)) * 2u : kOOB;
+                dma4(lds0 + uint32_t(kOmOff + plane * 512 + (j & 1) * 256), is_off ? ro : rm,
+                     voff, 0u);
+            }
+        }
 
         // ---- per-lane DMA source offsets of the window (kept in LDS; each
         // thread reads back only its own entries) and of the A rows
         const float inv_wc = 1.0f / float(a->WC);
 #pragma unroll
         for (int t = 0; t < kWinInstr; ++t) {
-            const int S = (t * 4 + wave) * 64 + lane;          // 16-byte slot of the buffer
+            const int S = (t * kWaves + wave) * 64 + lane;   // 16-byte slot of the buffer
             const int pl = S >= kWindowPixels ? 1 : 0;       // S < 2 * kWindowPixels
             const int px = S - pl * kWindowPixels;
             // px / WC through a float reciprocal: px < 1280 and WC <= 64, so
@@ -380,14 +445,15 @@ void window_kernel(WinArgs args)
             const int gr = r0 + r, gc = c0 + c;
             const bool ok = px < a->WR * a->WC && (unsigned)gr < (unsigned)a->H &&
                             (unsigned)gc < (unsigned)a->W;
-            woff_tab[t * 256 + tid] = ok ? uint32_t(img) * a->img_bytes + uint32_t(pl) * hw16 +
-                                               uint32_t(gr * a->W + gc) * 16
-                                         : kOOB;
+            woff_tab[t * kThreads + tid] = ok ? uint32_t(img) * a->img_bytes +
+                                                    uint32_t(pl) * hw16 +
+                                                    uint32_t(gr * a->W + gc) * 16
+                                              : kOOB;
         }
         uint32_t aoff[kAInstr];
 #pragma unroll
         for (int t = 0; t < kAInstr; ++t) {
-            const int S = (t * 4 + wave) * 64 + lane;
+            const int S = (t * kWaves + wave) * 64 + lane;
             const int pl = S >> 8, row = S & 255;
             aoff[t] = (m0 + row < a->Mg) ? uint32_t(pl * a->Mg + m0 + row) * 16 : kOOB;
         }
@@ -399,11 +465,11 @@ void window_kernel(WinArgs args)
             uint32_t wo[kWinInstr];                 // all table reads first: one LDS wait
 #pragma unroll
             for (int t = 0; t < kWinInstr; ++t)
-                wo[t] = woff_tab[t * 256 + tid];
+                wo[t] = woff_tab[t * kThreads + tid];
 #pragma unroll
             for (int t = 0; t < kWinInstr; ++t)
-                dma16(lds0 + buf * kWinBuf + (t * 4 + wave) * 1024 +
-                          ((t * 4 + wave) * 64 >= kWindowPixels ? kPlaneGap : 0),
+                dma16(lds0 + kWin0 + buf * kWinBuf + (t * kWaves + wave) * 1024 +
+                          ((t * kWaves + wave) * 64 >= kWindowPixels ? kPlaneGap : 0),
                       rx, wo[t], soff);
         };
         // K steps of the segment: step s (relative to its first chunk c_lo)
@@ -419,7 +485,7 @@ void window_kernel(WinArgs args)
             const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(s_base + step) * a_step);
 #pragma unroll
             for (int t = 0; t < kAInstr; ++t)
-                dma16(lds0 + kAOff + (step % kAStages) * kAStage + (t * 4 + wave) * 1024, ra,
+                dma16(lds0 + kAOff + (step % kAStages) * kAStage + (t * kWaves + wave) * 1024, ra,
                       aoff[t], soff);
         };
 
@@ -430,75 +496,96 @@ void window_kernel(WinArgs args)
             if (s < steps)
                 issue_a(s);
 
-        // ---- sampling geometry of the lane's two pixels, all taps
-        uint32_t gaddr[2][kTaps];
-        float gw[2][kTaps][4];
-        uint32_t fbl = 0;                            // lane: (slab, tap) needs the fallback
+        // ---- sampling geometry of the lane's pixel, all taps: the byte
+        // offset of the top-left corner in a window buffer (16 bits, two taps
+        // per register: tap k in half k%2 of gpk[k/2]) and three factors from
+        // which the four corner weights are formed per step (see weights_of)
+        static_assert(kWinBuf <= 65536, "window offsets fit 16 bits");
+        uint32_t gpk[(kTaps + 1) / 2] = {};
+        float gw[kTaps][3];
+        uint32_t fbl = 0;                            // lane: tap k needs the fallback
         {
             const int P = a->P;
+            float oh[kTaps], ow[kTaps], mm[kTaps];
+            if (om_lds) {
+                // this wave's offset and mask copies (issued before the window
+                // and A copies, so older than the last kWinInstr + LEAD*kAInstr
+                // of its copies) have landed, then every wave's
+                constexpr int N = kWinInstr + LEAD * kAInstr;
+                constexpr int kNoLgkm = 0x70 | 0xF00;
+                static_assert(N < 64, "vmcnt range");
+                __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                const char *om = smem + kOmOff + px_n * 2;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int n = (wave * 2 + s) * 32 + (lane & 31);
+                for (int k = 0; k < kTaps; ++k) {
+                    oh[k] = to_f32(*reinterpret_cast<const T *>(om + (2 * k) * 512));
+                    ow[k] = to_f32(*reinterpret_cast<const T *>(om + (2 * k + 1) * 512));
+                    mm[k] = to_f32(*reinterpret_cast<const T *>(om + (2 * kTaps + k) * 512));
+                }
+            } else {
                 int ho, wo;
-                out_pixel(n, ho0, wo0, a->Wo, ho, wo);
+                out_pixel(px_n, ho0, wo0, a->Wo, ho, wo);
                 const bool pv = ho < a->Ho && wo < a->Wo;
                 const int pix = pv ? ho * a->Wo + wo : 0;
                 const size_t ob = (size_t(img) * a->offC + size_t(q) * 2 * kTaps) * P + pix;
                 const size_t mb = (size_t(img) * a->mskC + size_t(q) * kTaps) * P + pix;
                 const T *off = static_cast<const T *>(a->off);
                 const T *msk = static_cast<const T *>(a->msk);
-                float oh[kTaps], ow[kTaps], mm[kTaps];
 #pragma unroll
                 for (int k = 0; k < kTaps; ++k) {
                     oh[k] = to_f32(off[ob + size_t(2 * k) * P]);
                     ow[k] = to_f32(off[ob + size_t(2 * k + 1) * P]);
                     mm[k] = to_f32(msk[mb + size_t(k) * P]);
                 }
+            }
+            int ho, wo;
+            out_pixel(px_n, ho0, wo0, a->Wo, ho, wo);
+            const bool pv = ho < a->Ho && wo < a->Wo;
 #pragma unroll
-                for (int k = 0; k < kTaps; ++k) {
-                    const int i = k / 3, j = k % 3;
-                    const int ah = ho * a->sh - a->ph + i * a->dh;
-                    const int aw = wo * a->sw - a->pw + j * a->dw;
-                    const float lim = 33554432.0f;
-                    const bool fin = fabsf(oh[k]) <= lim && fabsf(ow[k]) <= lim;
-                    const float fh = fin ? floorf(oh[k]) : 0.0f;
-                    const float fw = fin ? floorf(ow[k]) : 0.0f;
-                    const float ly = fin ? oh[k] - fh : 0.0f;
-                    const float lx = fin ? ow[k] - fw : 0.0f;
-                    const int h0 = ah + int(fh), w0 = aw + int(fw);
-                    const bool any = pv && fin && h0 >= -1 && h0 < a->H && w0 >= -1 && w0 < a->W;
-                    const int lr = h0 - r0, lc = w0 - c0;
-                    const bool inw = (unsigned)lr <= unsigned(a->WR - 2) &&
-                                     (unsigned)lc <= unsigned(a->WC - 2);
-                    const bool use = any && inw;
-                    const float hy = 1.0f - ly, hx = 1.0f - lx, m = mm[k];
-                    gw[s][k][0] = use ? hy * hx * m : 0.0f;
-                    gw[s][k][1] = use ? hy * lx * m : 0.0f;
-                    gw[s][k][2] = use ? ly * hx * m : 0.0f;
-                    gw[s][k][3] = use ? ly * lx * m : 0.0f;
-                    gaddr[s][k] = use ? uint32_t(half * kPlane1 + (lr * a->WC + lc) * 16)
-                                      : uint32_t(kWinZeroOff);
-                    fbl |= uint32_t(any && !inw) << (s * kTaps + k);
-                }
+            for (int k = 0; k < kTaps; ++k) {
+                const int i = k / 3, j = k % 3;
+                const int ah = ho * a->sh - a->ph + i * a->dh;
+                const int aw = wo * a->sw - a->pw + j * a->dw;
+                const float lim = 33554432.0f;
+                const bool fin = fabsf(oh[k]) <= lim && fabsf(ow[k]) <= lim;
+                const float fh = fin ? floorf(oh[k]) : 0.0f;
+                const float fw = fin ? floorf(ow[k]) : 0.0f;
+                const float ly = fin ? oh[k] - fh : 0.0f;
+                const float lx = fin ? ow[k] - fw : 0.0f;
+                const int h0 = ah + int(fh), w0 = aw + int(fw);
+                const bool any = pv && fin && h0 >= -1 && h0 < a->H && w0 >= -1 && w0 < a->W;
+                const int lr = h0 - r0, lc = w0 - c0;
+                const bool inw = (unsigned)lr <= unsigned(a->WR - 2) &&
+                                 (unsigned)lc <= unsigned(a->WC - 2);
+                const bool use = any && inw;
+                const float m = use ? mm[k] : 0.0f;
+                gw[k][0] = (1.0f - lx) * m;
+                gw[k][1] = lx * m;
+                gw[k][2] = ly;
+                const uint32_t wa =
+                    use ? uint32_t(half * kPlane1 + (lr * a->WC + lc) * 16) : uint32_t(kWinZeroOff);
+                gpk[k / 2] |= wa << (16 * (k % 2));
+                fbl |= uint32_t(any && !inw) << k;
             }
         }
-        // wave-level: which (slab, tap) has a lane that needs the fallback
+        // wave-level: which tap has a lane that needs the fallback
         uint32_t fbw = 0;
 #pragma unroll
-        for (int b = 0; b < 2 * kTaps; ++b)
+        for (int b = 0; b < kTaps; ++b)
             fbw |= uint32_t(__builtin_amdgcn_ballot_w64(((fbl >> b) & 1u) != 0u) != 0) << b;
         fbw = __builtin_amdgcn_readfirstlane(fbw);
 
-        // Fallback: the lane's 8 channels of sample (slab s, tap k) in chunk
+        // Fallback: the lane's 8 channels of the sample of tap k in chunk
         // `chunk`, from global memory (rare).
-        auto fallback = [&](int s, int k, int chunk, uint4 &bv) {
-            if ((fbl >> (s * kTaps + k)) & 1u) {
+        auto fallback = [&](int k, int chunk, uint4 &bv) {
+            if ((fbl >> k) & 1u) {
                 KArgs a = fresh_args(pa);
                 const T *offp = static_cast<const T *>(a->off);
                 const T *mskp = static_cast<const T *>(a->msk);
-                const int n = (wave * 2 + s) * 32 + (lane & 31);
                 int ho, wo;
-                out_pixel(n, ho0, wo0, a->Wo, ho, wo);
+                out_pixel(px_n, ho0, wo0, a->Wo, ho, wo);
                 const int pix = ho * a->Wo + wo;
                 const size_t ob =
                     (size_t(img) * a->offC + size_t(q) * 2 * kTaps + 2 * k) * a->P + pix;
@@ -528,49 +615,83 @@ void window_kernel(WinArgs args)
 
         // Accumulators: zero, or -- for a tile whose first chunks the
         // previous workgroup of the run computed -- its partial sums, which
-        // that workgroup published first thing (so the wait is short; the
-        // spin is bounded, so that a broken invariant gives a wrong result,
-        // never a stuck GPU).  The slot holds each lane's accumulator
-        // registers as they are: wave w's 64 KB, 16-byte group j of every
-        // lane at w*64K + j*1K + lane*16.
-        float16v acc[8][2];
+        // that workgroup published first thing (so the wait is short).  The
+        // wait is bounded so that a broken invariant can never hang the GPU:
+        // a workgroup that gives up sets the status word and writes NaN for
+        // its tile (a NaN bias in the epilogue), so the failure shows in the
+        // output and is reported to the host (never a silently wrong tensor).
+        // The slot holds each lane's accumulator registers as they are: wave
+        // w's 32 KB, 16-byte group j of every lane at w*32K + j*1K + lane*16.
+        //
+        // Ordering: the publisher's partial-sum stores and both flag accesses
+        // are device-scope (SC1) accesses, which bypass the non-coherent
+        // caches; the publisher waits for its stores to be acknowledged
+        // (vmcnt 0) before its flag store, and the data loads here are issued
+        // after the flag was seen (the barrier follows the poll).  Empty asm
+        // statements with a memory clobber keep the compiler from moving any
+        // of these accesses across the flag.
+        float16v acc[8];
         {
             const bool resume = c_lo > 0;
             const uint32_t prev = range_of(a).prev;
+            if (tid == 0 && !resume)
+                *gave_up_l = 0;
             if (resume && tid == 0) {
-                for (uint32_t it = 0; it < (1u << 26); ++it) {
+                const uint32_t limit = a->spin_limit;
+                uint32_t it = 0;
+                for (; it < limit; ++it) {
                     if (__hip_atomic_load(a->flags + prev, __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT) == uint32_t(a->epoch))
                         break;
                     __builtin_amdgcn_s_sleep(2);
                 }
+                const bool gave = it >= limit;
+                *gave_up_l = gave ? 1 : 0;
+                if (gave)
+                    __hip_atomic_store(a->status, kWindowGaveUp, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
-            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            lds_barrier();
+            asm volatile("" ::: "memory");
+            const bool load = resume && *gave_up_l == 0;
             // (a tile started here reads through an empty buffer: zeros, with
             // no memory access and no branch)
             const __amdgpu_buffer_rsrc_t rs =
-                srd_b(a->partial + (resume ? size_t(prev) * 65536 : 0),
-                      resume ? uint32_t(65536 * 4) : 0u);
-            const uint32_t lo = uint32_t(wave * 65536 + lane * 16);
+                srd_b(a->partial + (load ? size_t(prev) * 65536 : 0),
+                      load ? uint32_t(65536 * 4) : 0u);
+            const uint32_t lo = uint32_t(wave * 32768 + lane * 16);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
+                for (int q = 0; q < 4; ++q) {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                        rs, lo + uint32_t((i * 4 + q) * 1024), 0, kDevScope);
+                    float4v f;
+                    __builtin_memcpy(&f, &v, 16);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-                            rs, lo + uint32_t(((i * 2 + s) * 4 + q) * 1024), 0, kDevScope);
-                        float4v f;
-                        __builtin_memcpy(&f, &v, 16);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[i][s][4 * q + e] = f[e];
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][4 * q + e] = f[e];
+                }
         }
 
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
+        // The four corner weights of tap k with the mask folded in:
+        // (1-ly)(1-lx)m, (1-ly)lx m, ly(1-lx)m, ly lx m from t0 = (1-lx)m,
+        // t1 = lx m and ly (all 0 for a sample that reads nothing).
+        // (The factors pass through an empty asm at every use, so that the
+        // compiler cannot hoist the weights, loop-invariant per tap, out of
+        // the main loop and hold all 36 of them in registers.)
+        auto weights_of = [&](int k, float (&w)[4]) {
+            float t0 = gw[k][0], t1 = gw[k][1], ly = gw[k][2];
+            asm volatile("" : "+v"(t0), "+v"(t1), "+v"(ly));
+            w[0] = fmaf(-ly, t0, t0);
+            w[1] = fmaf(-ly, t1, t1);
+            w[2] = ly * t0;
+            w[3] = ly * t1;
+        };
         // A fragment of block i of step `step` (plane = half, row = 32i + lane%32)
         auto read_a = [&](uint4 (&fa)[8], int step) {
             const uint32_t so = __builtin_amdgcn_readfirstlane(
@@ -580,10 +701,14 @@ void window_kernel(WinArgs args)
             for (int i = 0; i < 8; ++i)
                 fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
         };
-        // corners of (slab s, tap k) from window buffer `buf`
-        auto read_corners = [&](uint4 (&cr)[4], int s, int k, int buf) {
-            const uint32_t bo = __builtin_amdgcn_readfirstlane(uint32_t(buf ? kWinBuf : 0));
-            const char *p = smem + (gaddr[s][k] + bo);
+        // corners of tap k from window buffer `buf`
+        auto read_corners = [&](uint4 (&cr)[4], int k, int buf) {
+            const uint32_t bo =
+                __builtin_amdgcn_readfirstlane(uint32_t(kWin0 + (buf ? kWinBuf : 0)));
+            uint32_t pk = gpk[k / 2];
+            asm volatile("" : "+v"(pk));                 // (not hoisted: see weights_of)
+            const uint32_t wa = (k % 2) ? (pk >> 16) : (pk & 0xffffu);
+            const char *p = smem + (wa + bo);
             const char *p2 = p + wrow;
             cr[0] = *reinterpret_cast<const uint4 *>(p);
             cr[1] = *reinterpret_cast<const uint4 *>(p + 16);
@@ -592,20 +717,19 @@ void window_kernel(WinArgs args)
         };
 
         uint4 fa[8];
-        uint4 cr[2][4];
-        uint4 b[2];
-        // step 0's operands
+        uint4 cr[4];
+        // step 0's A fragments and corners
         read_a(fa, 0);
-        read_corners(cr[0], 0, 0, 0);
-        read_corners(cr[1], 1, 0, 0);
-        b[0] = blend<T>(cr[0][0], cr[0][1], cr[0][2], cr[0][3], gw[0][0], zero);
-        b[1] = blend<T>(cr[1][0], cr[1][1], cr[1][2], cr[1][3], gw[1][0], zero);
-        if (fbw & (1u | (1u << kTaps))) {
-            fallback(0, 0, c_lo, b[0]);
-            fallback(1, 0, c_lo, b[1]);
-        }
-        read_corners(cr[0], 0, 1, 0);
-        read_corners(cr[1], 1, 1, 0);
+        read_corners(cr, 0, 0);
+
+        // Waves w and w + 4 share a SIMD.  Each step is a blend half (this
+        // step's B from the corners read in the previous step, then the next
+        // step's corner reads) and an MFMA half (8 MFMAs and the next step's
+        // A fragment reads).  At a barrier, waves 0-3 wait before their blend
+        // half and waves 4-7 before their MFMA half, so after it the two
+        // waves of a SIMD run opposite halves (the barrier is released once
+        // all eight waves have reached one of the two sites).
+        const bool late = wave >= 4;
 
         // One step: relative step s = rc*9 + k of chunk c_lo + rc.  The tap
         // k is a compile-time index so the geometry stays in registers.
@@ -614,73 +738,87 @@ void window_kernel(WinArgs args)
             const int s = rc * kTaps + k;
             const int chunk = c_lo + rc;
             const bool last_chunk = chunk + 1 >= c_hi;
-            // One barrier every other step (even s): it makes A of steps s+1
-            // and s+2 visible to every wave (the next step, which has none,
-            // reads A(s+2)), so A(s+2) and every older copy must have
-            // landed.  Issued after A(s+2) and allowed to be in flight: the A
-            // copies of the LEAD-3 steps after it, and the window copy of the
-            // next chunk while its first reads (in step k == 7, after the
-            // barrier of step 6 or 7) are still ahead -- k in [1, LEAD-2]
-            // (younger than A(s+2)) and k <= 5.  In the last chunk no window
-            // is issued and the A copies stop at the last step.  (No LDS wait:
-            // every LDS read of an A stage or window buffer that a copy issued
-            // in this or the next step overwrites was consumed -- so waited
-            // for -- before the previous step ended, and every wave has passed
-            // this barrier or the previous one.)
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            if (((rc + k) & 1) == 0) {                    // s = 9 rc + k is even
-                constexpr int kNoLgkm = 0x70 | 0xF00;     // expcnt and lgkmcnt: no wait
-                if (last_chunk) {
-                    constexpr int NA = kAInstr * ((LEAD - 3) < (6 - k)
-                                                      ? (LEAD - 3)
-                                                      : (6 - k > 0 ? 6 - k : 0));
-                    __builtin_amdgcn_s_waitcnt((NA & 15) | ((NA >> 4) << 14) | kNoLgkm);
-                } else if (k >= 1 && k <= LEAD - 2 && k <= 5) {
-                    constexpr int N = kAInstr * (LEAD - 3) + kWinInstr;
+            // One barrier every third step (k = 0, 3, 6): every wave's copies
+            // issued up to two steps before it have landed (each wave waits
+            // for its own, then the barrier), which covers every A stage and
+            // window read until the next barrier.  Still in flight: the A
+            // copy of the previous step, at k == 3 the window copy of the next
+            // chunk (issued in step k == 1 after that step's A copy, waited
+            // for at k == 6, first read in step k == 8), and -- for waves 4-7,
+            // which wait after their blend half -- the copies of this step.
+            // Every copy overwrites data last read at least two steps before
+            // the last barrier (A of step s + LEAD - 8; the window of chunk - 1,
+            // last read in step 9*chunk - 2), which every wave passed.  (No LDS
+            // wait is needed for that: every read was consumed by the step
+            // that used it.)
+            constexpr int kNoLgkm = 0x70 | 0xF00;     // expcnt and lgkmcnt: no wait
+            auto barrier = [&](int own) {
+                // own: copies of this step already issued by this wave
+                const bool a_prev = s >= 1 && s - 1 + LEAD < steps;   // copied in step s-1
+                if (k == 3 && !last_chunk) {
+                    if (own) {
+                        constexpr int N = 2 * kAInstr + kWinInstr;
+                        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    } else {
+                        constexpr int N = kAInstr + kWinInstr;
+                        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    }
+                } else if (a_prev && own) {
+                    constexpr int N = 2 * kAInstr;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                } else if (a_prev || own) {
+                    constexpr int N = kAInstr;
                     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
                 } else {
-                    constexpr int N = kAInstr * (LEAD - 3);
-                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    __builtin_amdgcn_s_waitcnt(kNoLgkm);
                 }
                 __builtin_amdgcn_s_barrier();
-            }
+            };
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (k % 3 == 0 && !late)
+                barrier(0);
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("" ::: "memory");
-            if (s + LEAD < steps)
+            const bool copy_a = s + LEAD < steps;
+            if (copy_a)
                 issue_a(s + LEAD);
-            if (k == 0 && !last_chunk)
+            if (k == 1 && !last_chunk)
                 issue_window(chunk + 1, (rc + 1) & 1);
 
-            // MFMAs of step s, interleaved group by group (the wave issues in
-            // order and is the only one on its SIMD) with the reads of step
-            // s+1's A fragments (block i as soon as its two MFMAs have issued),
-            // the blend of step s+1's B (one element pair per group) and the
-            // corner reads of step s+2 (a slab's, once its blend is done).
-            // Reads past the last step hit valid (stale) LDS and are never used.
-            constexpr int k1 = (k + 1) % kTaps, k2 = (k + 2) % kTaps;
+            // blend half: B of step s (the samples are the MFMA's A operand:
+            // rows are pixels), then the corners of step s+1.  Reads past the
+            // last step hit valid (stale) LDS and are never used.
+            constexpr int k1 = (k + 1) % kTaps;
             const int rc1 = (k + 1 >= kTaps) ? rc + 1 : rc;
-            const int rc2 = (k + 2 >= kTaps) ? rc + 1 : rc;
+            uint4 b;
+            {
+                float w[4];
+                weights_of(k, w);
+                b = blend<T>(cr[0], cr[1], cr[2], cr[3], w, zero);
+            }
+            if (fbw & (1u << k))
+                fallback(k, chunk, b);
+            read_corners(cr, k1, rc1 & 1);
+
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            if (k % 3 == 0 && late)
+                barrier(copy_a ? 1 : 0);
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" ::: "memory");
+
+            // MFMA half: the MFMAs of step s (B: the weights; columns are
+            // output channels), each followed by the read of its A fragment
+            // for step s+1
             const uint32_t so = __builtin_amdgcn_readfirstlane(
                 uint32_t(kAOff + ((s + 1) % kAStages) * kAStage));
             const char *st = smem + (a_lane + so);
-            uint32_t bn[2][4];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                acc[i][0] = Mma<T>::step(fa[i], b[0], acc[i][0]);
-                acc[i][1] = Mma<T>::step(fa[i], b[1], acc[i][1]);
+                acc[i] = Mma<T>::step(b, fa[i], acc[i]);
                 fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
-                const int sl = i >> 2, pr = i & 3;
-                bn[sl][pr] = blend_pair<T>(cr[sl], gw[sl][k1], zero, pr);
-                if (pr == 3)
-                    read_corners(cr[sl], sl, k2, rc2 & 1);
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            b[0] = make_uint4(bn[0][0], bn[0][1], bn[0][2], bn[0][3]);
-            b[1] = make_uint4(bn[1][0], bn[1][1], bn[1][2], bn[1][3]);
-            if (s + 1 < steps && (fbw & ((1u << k1) | (1u << (kTaps + k1))))) {
-                fallback(0, k1, c_lo + rc1, b[0]);
-                fallback(1, k1, c_lo + rc1, b[1]);
             }
         };
 
@@ -713,121 +851,99 @@ void window_kernel(WinArgs args)
             // then the flag once every store is complete
             const __amdgpu_buffer_rsrc_t rs =
                 srd_b(a->partial + size_t(cta) * 65536, uint32_t(65536 * 4));
-            const uint32_t lo = uint32_t((tid >> 6) * 65536 + (tid & 63) * 16);
+            const uint32_t lo = uint32_t((tid >> 6) * 32768 + (tid & 63) * 16);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4v f = {acc[i][s][4 * q], acc[i][s][4 * q + 1],
-                                           acc[i][s][4 * q + 2], acc[i][s][4 * q + 3]};
-                        u32x4 u;
-                        __builtin_memcpy(&u, &f, 16);
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            u, rs, lo + uint32_t(((i * 2 + s) * 4 + q) * 1024), 0, kDevScope);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const float4v f = {acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2],
+                                       acc[i][4 * q + 3]};
+                    u32x4 u;
+                    __builtin_memcpy(&u, &f, 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(u, rs, lo + uint32_t((i * 4 + q) * 1024),
+                                                           0, kDevScope);
+                }
             // device-scope stores are complete (acknowledged where every XCD
             // sees them) once the counter drains; only then the flag
+            asm volatile("" ::: "memory");
             __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
             if (tid == 0)
                 __hip_atomic_store(a->flags + cta, uint32_t(a->epoch), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         } else {
-            // ---- the tile's last chunks: per block of 32 output channels,
-            // through an LDS slice [row][pixel] of fp32 sums, + bias, one
-            // rounding, 16-byte stores of 8 pixels along a tile row.  No load
+            // ---- the tile's last chunks: + bias in fp32, one rounding,
+            // stores straight from the accumulators.  Register r of block i
+            // holds output channel m0 + 32i + lane%32 at tile pixel
+            // 32*wave + 8(r/4) + 4(lane/32) + r%4.  For each half h of the
+            // wave's 32 pixels, one lane swap (v_permlane32_swap: lanes
+            // 32..63 of the first register with lanes 0..31 of the second)
+            // gives lanes < 32 pixels 16h..16h+7 and lanes >= 32 pixels
+            // 16h+8..16h+15 of their channel: one 16-byte store each.  No load
             // is issued between the stores (on this GPU a load's wait also
-            // waits for every older store).
-            float *bias_l = reinterpret_cast<float *>(smem + kWoffOff);   // dead copy table
+            // waits for every older store): the bias comes first.
+            const int Mg = a->Mg, P = a->P, Ho = a->Ho, Wo = a->Wo;
+            const int wv = tid >> 6, ln = tid & 63;
+            float bv[8];
             {
                 const T *bias = static_cast<const T *>(a->bias);
-                const int m = te.m0 + tid;
-                bias_l[tid] =
-                    (bias && m < a->Mg) ? to_f32(bias[size_t(te.g) * a->Mg + m]) : 0.0f;
+                // the hand-over wait of this tile gave up: NaN for all of it
+                const bool poison = te.c_lo > 0 && *gave_up_l != 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int m = te.m0 + 32 * i + (ln & 31);
+                    bv[i] = (bias && m < Mg) ? to_f32(bias[size_t(te.g) * Mg + m]) : 0.0f;
+                    if (poison)
+                        bv[i] = __builtin_nanf("");
+                }
             }
-            __syncthreads();
             // output planes of the tile's image and group, as a buffer (a
-            // lane with nothing to store gets an out-of-range offset, so
-            // every block issues the same stores with no branches)
-            const int Mg = a->Mg, P = a->P, Ho = a->Ho, Wo = a->Wo;
+            // lane with nothing to store gets an out-of-range offset)
             const __amdgpu_buffer_rsrc_t ro =
                 srd_b(static_cast<const T *>(a->out) +
                           (size_t(te.img) * a->Co + size_t(te.g) * a->Mg) * a->P,
                       uint32_t(size_t(Mg) * P * sizeof(T)));
             const bool vec = a->vec_out != 0;
-            float *slice = reinterpret_cast<float *>(smem);
-            // this thread's 4 x 8 sums of a block: row tid/32 + 8*jj, pixels
-            // 8*(tid%32) ..+8
-            const int row0 = tid >> 5, n = (tid & 31) * 8;
-            int ho, wo;
-            out_pixel(n, te.ho0, te.wo0, Wo, ho, wo);
-            const uint32_t pix_off = uint32_t(ho * Wo + wo) * sizeof(T);   // bytes in a plane
-            // (with vec, Wo and wo are multiples of 8: wo < Wo keeps all 8 inside)
-            const bool pix_ok = ho < Ho && wo < Wo;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
+                const int m = te.m0 + 32 * i + (ln & 31);
+                const bool mok = m < Mg;
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        slice[(8 * (r >> 2) + 4 * ((tid >> 5) & 1) + (r & 3)) * kEpRow +
-                              (__builtin_amdgcn_readfirstlane(tid >> 6) * 2 + s) * 32 +
-                              (tid & 31)] = acc[i][s][r];
-                lds_barrier();                       // LDS only: stores stay in flight
-                // per-block bases behind an empty asm, so that the per-(i, jj)
-                // LDS addresses become base + immediate instead of 32 hoisted
-                // (and spilled) registers (integer offsets pass through the
-                // asm: a pointer would lose its LDS address space)
-                uint32_t sl_o = uint32_t(row0 * kEpRow + n), bl_o = uint32_t(i * 32 + row0);
-                asm volatile("" : "+v"(sl_o), "+v"(bl_o));
-                const float *sl_b = slice + sl_o;
-                const float *bl_b = bias_l + bl_o;
-                // all of the block's LDS reads first (16-byte reads: a slice
-                // row is 1040 bytes and n a multiple of 8), then one wait
-                float4v sv[4][2];
-                float bvv[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    sv[jj][0] = *reinterpret_cast<const float4v *>(sl_b + 8 * jj * kEpRow);
-                    sv[jj][1] = *reinterpret_cast<const float4v *>(sl_b + 8 * jj * kEpRow + 4);
-                    bvv[jj] = bl_b[8 * jj];
-                }
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int row = row0 + 8 * jj;
-                    const float sp[8] = {sv[jj][0][0], sv[jj][0][1], sv[jj][0][2], sv[jj][0][3],
-                                         sv[jj][1][0], sv[jj][1][1], sv[jj][1][2], sv[jj][1][3]};
-                    const int m = te.m0 + i * 32 + row;
-                    const bool ok = m < Mg && pix_ok;
-                    const float bv = bvv[jj];
+                for (int h = 0; h < 2; ++h) {
+                    const float16v &c = acc[i];
+                    const float bb = bv[i];
+                    const uint32_t v0 = pack2<T>(c[8 * h + 0] + bb, c[8 * h + 1] + bb);
+                    const uint32_t v1 = pack2<T>(c[8 * h + 2] + bb, c[8 * h + 3] + bb);
+                    const uint32_t v2 = pack2<T>(c[8 * h + 4] + bb, c[8 * h + 5] + bb);
+                    const uint32_t v3 = pack2<T>(c[8 * h + 6] + bb, c[8 * h + 7] + bb);
+                    const auto w0 = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
+                    const auto w1 = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
+                    const u32x4 ov = {uint32_t(w0[0]), uint32_t(w1[0]), uint32_t(w0[1]),
+                                      uint32_t(w1[1])};
+                    const int n = wv * 32 + 16 * h + 8 * (ln >> 5);
+                    int ho, wo;
+                    out_pixel(n, te.ho0, te.wo0, Wo, ho, wo);
+                    const bool ok = mok && ho < Ho && wo < Wo;
                     const uint32_t base =
-                        ok ? uint32_t(m) * uint32_t(P) * sizeof(T) + pix_off : kOOB;
+                        ok ? (uint32_t(m) * uint32_t(P) + uint32_t(ho * Wo + wo)) *
+                                 uint32_t(sizeof(T))
+                           : kOOB;
                     if (vec) {
-                        Vec16<T> o;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            o.e[e] = from_f32<T>(sp[e] + bv);
-                        u32x4 ov;
-                        __builtin_memcpy(&ov, &o.raw, 16);
+                        // (with vec, 8-pixel runs stay inside a row or, for
+                        // flat tiles, inside the plane)
                         __builtin_amdgcn_raw_buffer_store_b128(ov, ro, base, 0, 0);
                     } else {
+                        const uint32_t ow[4] = {ov[0], ov[1], ov[2], ov[3]};
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const T h = from_f32<T>(sp[e] + bv);
-                            uint16_t hb;
-                            __builtin_memcpy(&hb, &h, 2);
+                            const bool in = kFlat ? ho * Wo + wo + e < Ho * Wo : wo + e < Wo;
                             __builtin_amdgcn_raw_buffer_store_b16(
-                                hb, ro,
-                                (kFlat ? ho * Wo + wo + e < Ho * Wo : wo + e < Wo)
-                                    ? base + uint32_t(e) * sizeof(T)
-                                    : kOOB,
-                                0, 0);
+                                uint16_t(ow[e >> 1] >> (16 * (e & 1))), ro,
+                                in ? base + uint32_t(e) * uint32_t(sizeof(T)) : kOOB, 0, 0);
                         }
                     }
                 }
-                lds_barrier();
             }
         }
         if (tile <= int(rg.u0 / uint32_t(a->nch)))
@@ -906,6 +1022,18 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
     a.vec_out = ((flat ? p.P : p.Wo) % 8 == 0) && reinterpret_cast<uintptr_t>(out) % 16 == 0;
     a.img_bytes = uint32_t(size_t(p.H) * p.W * p.C * sizeof(T));
     a.chunk_bytes = uint32_t(size_t(cnt) * a.img_bytes);
+    // offsets and masks reach LDS by 4-byte DMA when every tile pixel pair
+    // (even pixel, same row or, flat, same plane) is a 4-byte aligned pair
+    const uint64_t off_bytes = uint64_t(cnt) * uint64_t(a.offC) * uint64_t(p.P) * sizeof(T);
+    const uint64_t msk_bytes = uint64_t(cnt) * uint64_t(a.mskC) * uint64_t(p.P) * sizeof(T);
+    if (off_bytes >= (uint64_t(1) << 31) || msk_bytes >= (uint64_t(1) << 31))
+        return hipErrorInvalidValue;
+    a.off_bytes = uint32_t(off_bytes);
+    a.msk_bytes = uint32_t(msk_bytes);
+    a.om_lds = p.P % 2 == 0 && (flat || p.Wo % 2 == 0) &&
+               reinterpret_cast<uintptr_t>(offset) % 4 == 0 &&
+               reinterpret_cast<uintptr_t>(mask) % 4 == 0;
+    a.spin_limit = plan.win_spin_limit;
     a.a_bytes = uint32_t(size_t(p.Mg) * p.Kg * sizeof(T));     // one group's weight
     if (a.WR * a.WC > kWindowPixels || a.WC * 16 + 32 > kWinZero)
         return hipErrorInvalidValue;
@@ -929,14 +1057,14 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
                       a.bounds))
         return hipErrorInvalidValue;
     auto kern = window_kernel<T, TH, TW, LEAD>;
-    constexpr int lds = lds_total(LEAD);
+    constexpr int lds = kLdsTotal;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess)
         return attr;
     a.A = wpack; a.xt = xt; a.off = offset; a.msk = mask; a.bias = bias; a.out = out;
-    a.partial = ws.partial; a.flags = ws.flags;
-    hipLaunchKernelGGL(kern, dim3(uint32_t(blocks)), dim3(256), lds, s, a);
+    a.partial = ws.partial; a.flags = ws.flags; a.status = ws.flags + ws.slots;
+    hipLaunchKernelGGL(kern, dim3(uint32_t(blocks)), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -945,18 +1073,9 @@ hipError_t window_lead(const Problem &p, const Plan &plan, int64_t cnt, const vo
                        const void *xt, const void *offset, const void *mask, const void *bias,
                        void *out, const WindowScratch &ws, hipStream_t s)
 {
-    switch (plan.win_lead) {
-    case 3:
-        return window_cfg<T, TH, TW, 3>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws,
-                                          s);
-    case 5:
-        return window_cfg<T, TH, TW, 5>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws,
-                                          s);
-    case 7:
-        return window_cfg<T, TH, TW, 7>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws,
-                                          s);
-    }
-    return hipErrorInvalidValue;
+    if (plan.win_lead != 5)
+        return hipErrorInvalidValue;
+    return window_cfg<T, TH, TW, 5>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
 }
 
 template <typename T>
