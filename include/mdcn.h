@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MDCN_ABI_VERSION 1
+#define MDCN_ABI_VERSION 2
 
 typedef enum mdcn_status {
     MDCN_OK = 0,
@@ -69,7 +69,10 @@ typedef enum mdcn_status {
     MDCN_E_DEVICE = 7,      /* the current device is not a gfx950 GPU                */
     MDCN_E_ALIAS = 8,       /* output or workspace overlaps another buffer           */
     MDCN_E_PATH = 9,        /* the requested path cannot run this problem            */
-    MDCN_E_INTERNAL = 10    /* unexpected host-side failure                          */
+    MDCN_E_INTERNAL = 10,   /* unexpected host-side failure                          */
+    MDCN_E_SYNC = 11        /* a workgroup's bounded wait for another's partial sums
+                               gave up; that tile's outputs are NaN (see
+                               mdcn_forward_check)                                    */
 } mdcn_status;
 
 typedef enum mdcn_dtype {
@@ -189,6 +192,22 @@ mdcn_status mdcn_forward(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
                          const void *x, const void *offset, const void *mask,
                          const void *weight, const void *bias, int64_t bias_len, void *out,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Completion check of the last mdcn_forward that used `workspace`: waits for
+ * `stream` (host synchronisation), then reports MDCN_E_SYNC if a bounded
+ * wait inside that forward gave up, MDCN_OK otherwise.  op, dtype, dims and
+ * workspace_bytes must be those of that forward.  Only the windowed path
+ * waits (a workgroup that finishes an output tile started by another one
+ * polls a flag in the workspace, at most a fixed number of times, so that a
+ * broken invariant can never hang the GPU); a forward whose wait gave up
+ * writes NaN for the affected tile and sets a status word in the workspace,
+ * cleared at the start of every forward.  The other paths always report
+ * MDCN_OK.  The pages ask a plugin to check for errors after enqueueing work
+ * [efficient-plugin page]; this is that check for the one error the kernels
+ * themselves can detect.  Errors: MDCN_E_NULL, the shape/attribute codes of
+ * mdcn_forward, MDCN_E_LAUNCH (a HIP call failed), MDCN_E_SYNC. */
+mdcn_status mdcn_forward_check(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                               const void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- backward ------------------------------------------------------------ */
 

@@ -539,6 +539,44 @@ mdcn_status mdcn_workspace_bytes(const mdcn_op *op, mdcn_dtype dtype, const int6
     }
 }
 
+mdcn_status mdcn_forward_check(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                               const void *workspace, size_t workspace_bytes, void *stream_ptr)
+{
+    try {
+        if (!op || !dims)
+            return MDCN_E_NULL;
+        Problem p;
+        mdcn_status st = mdcn::derive_problem(op->attrs, dtype, dims, &p);
+        if (st != MDCN_OK)
+            return st;
+        Plan plan;
+        st = mdcn::make_plan(op->attrs, p, workspace_bytes, true, &plan);
+        if (st != MDCN_OK)
+            return st;
+        hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+        if (plan.path != Path::Window || p.N == 0 || p.P == 0 || plan.ws_bytes == 0)
+            return hipStreamSynchronize(stream) == hipSuccess ? MDCN_OK : MDCN_E_LAUNCH;
+        if (!workspace)
+            return MDCN_E_NULL;
+        st = mdcn::make_plan(op->attrs, p, workspace_bytes, false, &plan);
+        if (st != MDCN_OK)
+            return st;
+        const uintptr_t raw = reinterpret_cast<uintptr_t>(workspace);
+        const char *ws =
+            reinterpret_cast<const char *>((raw + mdcn::kAlign - 1) / mdcn::kAlign * mdcn::kAlign);
+        const uint32_t *status =
+            reinterpret_cast<const uint32_t *>(ws + plan.flag_off) + plan.win_slots;
+        uint32_t word = 0;
+        if (hipMemcpyAsync(&word, status, sizeof(word), hipMemcpyDeviceToHost, stream) !=
+                hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return MDCN_E_LAUNCH;
+        return word == mdcn::kWindowGaveUp ? MDCN_E_SYNC : MDCN_OK;
+    } catch (...) {
+        return MDCN_E_INTERNAL;
+    }
+}
+
 mdcn_status mdcn_forward(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
                          const void *x, const void *offset, const void *mask,
                          const void *weight, const void *bias, int64_t bias_len, void *out,
@@ -737,6 +775,7 @@ const char *mdcn_status_string(mdcn_status status)
     case MDCN_E_ALIAS: return "output or workspace overlaps another buffer";
     case MDCN_E_PATH: return "the requested computation path cannot run this problem";
     case MDCN_E_INTERNAL: return "internal error";
+    case MDCN_E_SYNC: return "a bounded wait for partial sums gave up; the affected outputs are NaN";
     }
     return "unknown status";
 }

@@ -79,8 +79,12 @@ __global__ __launch_bounds__(256) void direct_kernel(const T *__restrict__ x,
                     for (int k = 0; k < KK; ++k) {
                         float v = 0.0f;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            v = fmaf(tp[k].wt[e], to_f32(plane[tp[k].idx[e]]), v);
+                        for (int e = 0; e < 4; ++e) {
+                            // a corner off the image reads 0 (its safe address
+                            // holds a pixel whose value must not enter)
+                            const float xv = to_f32(plane[tp[k].idx[e]]);
+                            v = fmaf(tp[k].wt[e], tp[k].valid[e] ? xv : 0.0f, v);
+                        }
                         acc = fmaf(on * to_f32(wrow[size_t(c - c_first) * KK + k]), v, acc);
                     }
                 }
@@ -96,8 +100,10 @@ __global__ __launch_bounds__(256) void direct_kernel(const T *__restrict__ x,
                     const T *plane = xn + size_t(c) * HW;
                     float v = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v = fmaf(tp.wt[e], to_f32(plane[tp.idx[e]]), v);
+                    for (int e = 0; e < 4; ++e) {
+                        const float xv = to_f32(plane[tp.idx[e]]);
+                        v = fmaf(tp.wt[e], tp.valid[e] ? xv : 0.0f, v);
+                    }
                     acc = fmaf(to_f32(wrow[size_t(c - c_first) * K + k]), v, acc);
                 }
             }

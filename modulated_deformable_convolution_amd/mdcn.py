@@ -27,6 +27,7 @@ MDCN_E_DEVICE = 7
 MDCN_E_ALIAS = 8
 MDCN_E_PATH = 9
 MDCN_E_INTERNAL = 10
+MDCN_E_SYNC = 11
 
 # mdcn_dtype
 MDCN_F32 = 0
@@ -48,6 +49,7 @@ EXPORTED = [
     "mdcn_trace_reset", "mdcn_forward_traced", "mdcn_trace_count", "mdcn_trace_read",
     "mdcn_kernel_name", "mdcn_status_string", "mdcn_abi_version", "mdcn_describe_plan",
     "mdcn_backward_workspace_bytes", "mdcn_backward", "mdcn_backward_traced",
+    "mdcn_forward_check",
 ]
 
 
@@ -77,6 +79,8 @@ def _bind(lib):
         "mdcn_workspace_bytes": ([_vp, ctypes.c_int, _i64p, _szp, _szp], ctypes.c_int),
         "mdcn_forward": ([_vp, ctypes.c_int, _i64p, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                           _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+        "mdcn_forward_check": ([_vp, ctypes.c_int, _i64p, _vp, ctypes.c_size_t, _vp],
+                               ctypes.c_int),
         "mdcn_forward_traced": ([_vp, ctypes.c_int, _i64p, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp, _vp],
                                 ctypes.c_int),
@@ -201,6 +205,13 @@ def mdcn_forward(op: Op, dtype: int, dims, x: int, offset: int, mask: int, weigh
     return lib.mdcn_forward_traced(*args, trace.handle)
 
 
+def mdcn_forward_check(op: Op, dtype: int, dims, workspace: int, workspace_bytes: int,
+                       stream: int) -> int:
+    """Raw entry point; returns the status code (does not raise)."""
+    return library().mdcn_forward_check(op.handle, int(dtype), _arr(ctypes.c_int64, dims),
+                                        workspace or None, int(workspace_bytes), stream or None)
+
+
 def mdcn_backward_workspace_bytes(op: Op, dtype: int, dims) -> int:
     lib = library()
     d = _arr(ctypes.c_int64, dims)
@@ -285,10 +296,27 @@ def dims_of(x, offset, mask, weight) -> list:
     return dims
 
 
+def _alloc_stream(stream, device):
+    """(handle, context) for a launch on `stream` (an int handle or None =
+    torch's current stream): buffers torch allocates for the call are made
+    inside the context, so the caching allocator ties them to the stream the
+    kernels run on and cannot hand them out while those kernels still use
+    them."""
+    import contextlib
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream, contextlib.nullcontext()
+    if int(stream) == 0:
+        return 0, torch.cuda.stream(torch.cuda.default_stream(device))
+    return int(stream), torch.cuda.stream(torch.cuda.ExternalStream(int(stream), device=device))
+
+
 def forward(op: Op, x, offset, mask, weight, bias=None, out=None, workspace=None,
-            stream=None, trace: Trace | None = None):
+            stream=None, trace: Trace | None = None, check: bool = False):
     """Run mdcn_forward on torch device tensors; allocates `out` (and the
-    workspace) with torch when not given.  Raises MdcnError on failure."""
+    workspace) with torch when not given, on the stream the forward runs on.
+    With check, waits for the forward and raises if a bounded wait inside it
+    gave up (mdcn_forward_check).  Raises MdcnError on failure."""
     import torch
     tensors = [x, offset, mask, weight] + ([bias] if bias is not None else [])
     for t in tensors:
@@ -298,20 +326,23 @@ def forward(op: Op, x, offset, mask, weight, bias=None, out=None, workspace=None
     code = dtype_code(x.dtype)
     dims = dims_of(x, offset, mask, weight)
     shape = mdcn_output_shape(op, dims)
-    if out is None:
-        out = torch.empty(shape, dtype=x.dtype, device=x.device)
-    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous():
-        raise MdcnError(MDCN_E_SHAPE, "forward: out")
-    if workspace is None:
-        nbytes, _ = mdcn_workspace_bytes(op, code, dims)
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = mdcn_forward(op, code, dims, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
-                      weight.data_ptr(), bias.data_ptr() if bias is not None else 0,
-                      int(bias.numel()) if bias is not None else 0, out.data_ptr(),
-                      workspace.data_ptr(), workspace.numel(), int(stream), trace)
-    _check(st, "mdcn_forward")
+    stream, ctx = _alloc_stream(stream, x.device)
+    with ctx:
+        if out is None:
+            out = torch.empty(shape, dtype=x.dtype, device=x.device)
+        elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous():
+            raise MdcnError(MDCN_E_SHAPE, "forward: out")
+        if workspace is None:
+            nbytes, _ = mdcn_workspace_bytes(op, code, dims)
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+        st = mdcn_forward(op, code, dims, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
+                          weight.data_ptr(), bias.data_ptr() if bias is not None else 0,
+                          int(bias.numel()) if bias is not None else 0, out.data_ptr(),
+                          workspace.data_ptr(), workspace.numel(), stream, trace)
+        _check(st, "mdcn_forward")
+        if check:
+            _check(mdcn_forward_check(op, code, dims, workspace.data_ptr(), workspace.numel(),
+                                      stream), "mdcn_forward_check")
     return out
 
 
@@ -329,20 +360,20 @@ def backward(op: Op, x, offset, mask, weight, grad_out, with_bias=True, workspac
     dims = dims_of(x, offset, mask, weight)
     if tuple(grad_out.shape) != mdcn_output_shape(op, dims):
         raise MdcnError(MDCN_E_SHAPE, "backward: grad_out")
-    if workspace is None:
-        workspace = torch.empty(mdcn_backward_workspace_bytes(op, code, dims),
-                                dtype=torch.uint8, device=x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    g = {"x": torch.empty_like(x), "offset": torch.empty_like(offset),
-         "mask": torch.empty_like(mask), "weight": torch.empty_like(weight),
-         "bias": torch.empty(weight.shape[0], dtype=x.dtype, device=x.device) if with_bias
-         else None}
-    st = mdcn_backward(op, code, dims, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
-                       weight.data_ptr(), grad_out.data_ptr(), g["x"].data_ptr(),
-                       g["offset"].data_ptr(), g["mask"].data_ptr(), g["weight"].data_ptr(),
-                       g["bias"].data_ptr() if with_bias else 0,
-                       int(weight.shape[0]) if with_bias else 0, workspace.data_ptr(),
-                       workspace.numel(), int(stream), trace)
-    _check(st, "mdcn_backward")
+    stream, ctx = _alloc_stream(stream, x.device)
+    with ctx:
+        if workspace is None:
+            workspace = torch.empty(mdcn_backward_workspace_bytes(op, code, dims),
+                                    dtype=torch.uint8, device=x.device)
+        g = {"x": torch.empty_like(x), "offset": torch.empty_like(offset),
+             "mask": torch.empty_like(mask), "weight": torch.empty_like(weight),
+             "bias": torch.empty(weight.shape[0], dtype=x.dtype, device=x.device) if with_bias
+             else None}
+        st = mdcn_backward(op, code, dims, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
+                           weight.data_ptr(), grad_out.data_ptr(), g["x"].data_ptr(),
+                           g["offset"].data_ptr(), g["mask"].data_ptr(), g["weight"].data_ptr(),
+                           g["bias"].data_ptr() if with_bias else 0,
+                           int(weight.shape[0]) if with_bias else 0, workspace.data_ptr(),
+                           workspace.numel(), stream, trace)
+        _check(st, "mdcn_backward")
     return g

@@ -25,7 +25,7 @@ def declared_functions():
 
 
 def test_abi_version():
-    assert mdcn.mdcn_abi_version() == 1
+    assert mdcn.mdcn_abi_version() == 2
 
 
 def test_every_declared_symbol_is_exported():
@@ -239,10 +239,10 @@ def test_fused_path_plan():
     assert mb == 256 + 256 * 2304 * 2 + 256 * 160 * 160 * 2
     # the windowed kernel: the same packed weight and x (in 8-channel blocks),
     # plus a 256 KiB partial-sum slot and a flag per workgroup (at most 256;
-    # 100 tiles per image)
+    # 100 tiles per image) and the status word after the flags, 256-byte aligned
     wp, ximg, slot = 256 * 2304 * 2, 256 * 160 * 160 * 2, 256 * 256 * 4
     assert mdcn.mdcn_workspace_bytes(opw, mdcn.MDCN_F16, DIMS) == (
-        256 + wp + 4 * ximg + 256 * slot + 1024, 256 + wp + ximg + 100 * slot + 512)
+        256 + wp + 4 * ximg + 256 * slot + 1280, 256 + wp + ximg + 100 * slot + 512)
     assert mdcn.mdcn_workspace_bytes(auto, mdcn.MDCN_F16, DIMS) == \
         mdcn.mdcn_workspace_bytes(opw, mdcn.MDCN_F16, DIMS)
     # 40x40 in flat tiles: 1600 of 1792 pixels (89%) -> windowed; tiles that

@@ -36,6 +36,11 @@ CASES = [
                             offset_dist=("normal", 2.0)), "f16", mdcn.MDCN_PATH_GATHER_GEMM),
     ("window", Problem(N=2, C=32, Co=288, H=37, W=37, offset_dist=("normal", 3.0)), "f16",
      mdcn.MDCN_PATH_WINDOW),
+    # the same with 7 workgroups (MDCN_WIN_CTAS): 3 of its 24 tiles split
+    # between two of them, partial sums handed over through the workspace on
+    # every replay
+    ("window_split", Problem(N=2, C=32, Co=288, H=37, W=37, offset_dist=("normal", 3.0)), "f16",
+     mdcn.MDCN_PATH_WINDOW),
     ("depthwise", Problem(N=2, C=24, Co=48, H=13, W=13, groups=24, deformable_groups=3,
                           offset_dist=("uniform", 8.0), mask_dist=("uniform_zeros", 0.1)),
      "f32", mdcn.MDCN_PATH_DEPTHWISE),
@@ -50,7 +55,9 @@ def _dev(inp):
 
 
 @pytest.mark.parametrize("name,pr,dtype,path", CASES, ids=[c[0] for c in CASES])
-def test_graph_replays_match_eager(name, pr, dtype, path):
+def test_graph_replays_match_eager(name, pr, dtype, path, monkeypatch):
+    if name == "window_split":
+        monkeypatch.setenv("MDCN_WIN_CTAS", "7")
     op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups,
                           path=path)
     inputs = [workloads.generate(pr, dtype, seed=s) for s in (0, 1, 2)]
@@ -96,6 +103,9 @@ def test_graph_replays_match_eager(name, pr, dtype, path):
         scratch.item()
         torch.cuda.synchronize()
         assert torch.equal(out, eager[k]), f"{name}: replay {rep} differs from the eager forward"
+        stream = torch.cuda.current_stream().cuda_stream
+        assert mdcn.mdcn_forward_check(op, code, dims, ws.data_ptr(), ws.numel(),
+                                       stream) == mdcn.MDCN_OK
 
     if name in ("tiny", "gather_gemm", "depthwise"):
         inp = inputs[2]

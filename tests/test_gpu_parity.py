@@ -73,7 +73,9 @@ SMALL = {
     "fused_5x5": Problem(N=2, C=64, Co=64, H=11, W=10, kh=5, kw=5, padding=(2, 2),
                          offset_dist=("normal", 2.0)),
     # eligible for the windowed kernel (fp16/bf16): Co = 288 (a full and a
-    # partial 256-row tile), 37 x 37 (ragged 16 x 16 tiles), offsets wide
+    # partial 256-row tile), 37 x 37 (1369 pixels: the planner takes six flat
+    # tiles of 256 raster pixels, the last one ragged; MDCN_WIN_TILE forces
+    # the ragged rectangular ones in test_every_window_tile), offsets wide
     # enough that some samples leave the window (the fallback)
     "window_multi_tile": Problem(N=2, C=32, Co=288, H=37, W=37,
                                  offset_dist=("normal", 3.0)),
@@ -91,6 +93,9 @@ SMALL = {
     "window_flat_ragged": Problem(N=2, C=32, Co=64, H=13, W=21, offset_dist=("normal", 2.0)),
     # also eligible for the fused kernel (C/group = 64)
     "window_fused_cmp": Problem(N=2, C=64, Co=128, H=21, W=21, offset_dist=("normal", 2.0)),
+    # 4 output tiles per image of 8 chunks (16 channels) each: with 3 to 13
+    # workgroups the work split cuts tiles (see test_window_split_tiles)
+    "window_split_chunks": Problem(N=2, C=128, Co=64, H=32, W=32, offset_dist=("normal", 2.0)),
 }
 
 
@@ -123,8 +128,10 @@ def run_gpu(pr, inp, path=mdcn.MDCN_PATH_AUTO, workspace_bytes=None, trace=None)
     ws = None
     if workspace_bytes is not None:
         ws = torch.empty(max(workspace_bytes, 1), dtype=torch.uint8, device=DEV)
+    # check: every forward also asks mdcn_forward_check whether a bounded wait
+    # inside it gave up (only the windowed path waits)
     out = mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"],
-                       workspace=ws, trace=trace)
+                       workspace=ws, trace=trace, check=True)
     torch.cuda.synchronize()
     return out.cpu()
 
@@ -332,10 +339,80 @@ def test_workload_sampled(name, dtype):
     ref = oracle.forward_points(inp["x"], inp["offset"], inp["mask"], inp["weight"],
                                 inp["bias"], idx, **pr.attrs())
     g = got.reshape(-1)[torch.from_numpy(idx)].double().numpy()
-    # RMS of the whole output from the GPU result (the fp32 rule's scale floor)
-    rms = float(got.double().pow(2).mean().sqrt())
+    # the fp32 rule's scale floor: RMS of the oracle's values at the sampled
+    # outputs (an estimate of the whole output's, taken from the reference,
+    # never from the result under test)
+    rms = float(np.sqrt(np.mean(np.asarray(ref, dtype=np.float64) ** 2)))
     ok, err, bound = within_tolerance(g, ref, dtype, rms=rms)
     assert ok, (name, dtype, error_report(g, ref), float((err / bound).max()))
+    assert torch.isfinite(got).all()
+
+
+def ulp_of(ref, dtype):
+    """Spacing of the output dtype at |ref| (normal range; the subnormal
+    spacing below it)."""
+    mant, emin = {"f32": (23, -126), "f16": (10, -14), "bf16": (7, -126)}[dtype]
+    a = np.maximum(np.abs(np.asarray(ref, dtype=np.float64)), 2.0 ** emin)
+    return 2.0 ** (np.floor(np.log2(a)) - mant)
+
+
+GRID_CASES = [
+    ("ocdnet_n4_c256_160x160", "f16", mdcn.MDCN_PATH_AUTO, "window"),
+    ("deep_n16_c512_40x40", "f16", mdcn.MDCN_PATH_AUTO, "window"),
+    ("ocdnet_n4_c256_160x160", "f32", mdcn.MDCN_PATH_AUTO, "fused"),
+    ("strided_grouped_n2_c128_co256_128x128", "bf16", mdcn.MDCN_PATH_AUTO, "fused"),
+    ("ocdnet_n4_c256_160x160", "f16", mdcn.MDCN_PATH_GATHER_GEMM, "gather_gemm"),
+    ("ocdnet_n4_c256_160x160", "f32", mdcn.MDCN_PATH_GATHER_GEMM, "gather_gemm"),
+]
+
+
+@pytest.mark.parametrize("name,dtype,path,plan", GRID_CASES,
+                         ids=["%s-%s-%s" % (c[0].split("_")[0], c[1], c[3]) for c in GRID_CASES])
+def test_workload_grid_exact(name, dtype, path, plan):
+    """Full-size workloads on grid inputs (workloads.generate_grid: x and the
+    weight on coarse dyadic grids, integer offsets, masks in {0, 1/2, 1}).
+    Every sample is then a value of the dtype, every product and every fp32
+    partial sum is exact, so the result is the exact value rounded once to
+    the output dtype: each sampled output must be within one unit in the
+    last place of the oracle's value.  A single misplaced tap, channel or
+    pixel moves an output by far more than that."""
+    pr, _ = workloads.WORKLOADS[name]
+    print("grid workload", name, dtype, plan, flush=True)
+    inp = workloads.generate_grid(pr, dtype, seed=3)
+    op = make_op(pr, path)
+    dims = [pr.N, pr.C, pr.H, pr.W] + list(inp["offset"].shape) + list(inp["mask"].shape) + \
+        list(inp["weight"].shape)
+    code = mdcn.dtype_code(workloads.DTYPES[dtype])
+    assert mdcn.mdcn_describe_plan(op, code, dims).startswith("path=%s " % plan)
+    got = run_gpu(pr, inp, path)
+    idx = sample_indices(tuple(got.shape), 8192, seed=13)
+    ref = np.asarray(oracle.forward_points(inp["x"], inp["offset"], inp["mask"], inp["weight"],
+                                           inp["bias"], idx, **pr.attrs()), dtype=np.float64)
+    g = got.reshape(-1)[torch.from_numpy(idx)].double().numpy()
+    err = np.abs(g - ref)
+    ulp = ulp_of(ref, dtype)
+    assert (err <= ulp).all(), (name, dtype, plan, float((err / ulp).max()),
+                                int((err > ulp).sum()))
+    # and the reference itself is not trivial: many distinct, mostly nonzero values
+    assert np.count_nonzero(ref) > 0.9 * ref.size and np.unique(ref).size > 1000
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_gather_gemm_workload_sampled(dtype):
+    """The OCDNet-like stage on the gather + GEMM path (column buffer, chunks
+    of images within the default column budget), random inputs, sampled
+    outputs against the oracle."""
+    pr, _ = workloads.WORKLOADS["ocdnet_n4_c256_160x160"]
+    print("gather_gemm workload", dtype, flush=True)
+    inp = workloads.generate(pr, dtype, seed=0)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_GATHER_GEMM)
+    idx = sample_indices(tuple(got.shape), 4096, seed=14)
+    ref = oracle.forward_points(inp["x"], inp["offset"], inp["mask"], inp["weight"],
+                                inp["bias"], idx, **pr.attrs())
+    g = got.reshape(-1)[torch.from_numpy(idx)].double().numpy()
+    rms = float(np.sqrt(np.mean(np.asarray(ref, dtype=np.float64) ** 2)))
+    ok, err, bound = within_tolerance(g, ref, dtype, rms=rms)
+    assert ok, (dtype, error_report(g, ref), float((err / bound).max()))
     assert torch.isfinite(got).all()
 
 
@@ -496,9 +573,23 @@ def test_window_exact_cases(margin, monkeypatch):
     assert torch.equal(got, bias.expand_as(got))
 
 
-@pytest.mark.parametrize("ctas", [1, 5, 7, 13])
-@pytest.mark.parametrize("name,dtype", [("window_multi_tile", "f16"), ("window_grouped", "bf16"),
-                                        ("window_far_offsets", "f16")])
+def assert_tiles_split(pr, inp, monkeypatch, workspace_bytes=None):
+    """Some output tile really is split between two workgroups in this
+    configuration: with the hand-over wait forced to give up at once
+    (MDCN_WIN_SPIN_LIMIT=0) the forward reports MDCN_E_SYNC.  (The work split
+    keeps tiles whole when it can, so a workgroup count alone proves nothing.)"""
+    monkeypatch.setenv("MDCN_WIN_SPIN_LIMIT", "0")
+    with pytest.raises(mdcn.MdcnError) as e:
+        run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW, workspace_bytes=workspace_bytes)
+    assert e.value.status == mdcn.MDCN_E_SYNC
+    monkeypatch.delenv("MDCN_WIN_SPIN_LIMIT")
+
+
+@pytest.mark.parametrize("ctas,name,dtype", [
+    (3, "window_split_chunks", "f16"), (5, "window_split_chunks", "f16"),
+    (7, "window_split_chunks", "bf16"), (7, "window_split_chunks", "f16"),
+    (7, "window_multi_tile", "f16"), (11, "window_multi_tile", "bf16"),
+    (3, "window_grouped", "bf16")])
 def test_window_split_tiles(ctas, name, dtype, monkeypatch):
     """Fewer workgroups than tiles (MDCN_WIN_CTAS): the (tile, chunk) units
     are split into contiguous ranges, tiles span two workgroups and are
@@ -507,10 +598,109 @@ def test_window_split_tiles(ctas, name, dtype, monkeypatch):
     pr = SMALL[name]
     print("window split", name, dtype, ctas, flush=True)
     inp = workloads.generate(pr, dtype, seed=20)
+    assert_tiles_split(pr, inp, monkeypatch)
     got = run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW).double().numpy()
     ref = oracle_full(pr, inp)
     ok, err, bound = within_tolerance(got, ref, dtype)
     assert ok, (ctas, name, dtype, error_report(got, ref))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_window_split_least_workspace(dtype, monkeypatch):
+    """Split tiles with the least workspace: one image per launch, so the
+    forward makes several launches, each publishing with its own flag value
+    (epoch 1, 2, ...) into the same slots.  (An image has 4 tiles of 8
+    chunks; 3 workgroups cut two of them.)"""
+    monkeypatch.setenv("MDCN_WIN_CTAS", "3")
+    pr = Problem(N=3, C=128, Co=64, H=32, W=32, offset_dist=("normal", 2.0))
+    inp = workloads.generate(pr, dtype, seed=23)
+    op = make_op(pr, mdcn.MDCN_PATH_WINDOW)
+    dims = [pr.N, pr.C, pr.H, pr.W] + list(inp["offset"].shape) + list(inp["mask"].shape) + \
+        list(inp["weight"].shape)
+    code = mdcn.dtype_code(workloads.DTYPES[dtype])
+    _, least = mdcn.mdcn_workspace_bytes(op, code, dims)
+    assert "chunk=1" in mdcn.mdcn_describe_plan(op, code, dims, least)
+    assert_tiles_split(pr, inp, monkeypatch, workspace_bytes=least)
+    tr = mdcn.Trace(64)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_WINDOW, workspace_bytes=least, trace=tr)
+    assert len([n for n, _ in tr.read() if n == "window_gather_gemm"]) == pr.N
+    ok, err, bound = within_tolerance(got.double().numpy(), oracle_full(pr, inp), dtype)
+    assert ok, error_report(got.double().numpy(), oracle_full(pr, inp))
+
+
+def test_window_handover_giveup_is_reported(monkeypatch):
+    """A workgroup that finishes a tile begun by another waits for that one's
+    partial sums for a bounded number of polls.  With the bound forced to
+    zero from the host (MDCN_WIN_SPIN_LIMIT=0) every such wait gives up at
+    once: the kernels still exit normally, the affected tiles come out NaN
+    and mdcn_forward_check reports MDCN_E_SYNC.  The next forward on the same
+    workspace, with the normal bound, is clean again."""
+    # 4 output tiles of 8 chunks each over 3 workgroups: range boundaries
+    # fall inside tiles, so tiles are split
+    pr = Problem(N=1, C=128, Co=64, H=32, W=32, offset_dist=("normal", 2.0))
+    inp = workloads.generate(pr, "f16", seed=24)
+    g = to_dev(inp)
+    op = make_op(pr, mdcn.MDCN_PATH_WINDOW)
+    dims = mdcn.dims_of(g["x"], g["offset"], g["mask"], g["weight"])
+    nbytes, _ = mdcn.mdcn_workspace_bytes(op, mdcn.MDCN_F16, dims)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    monkeypatch.setenv("MDCN_WIN_CTAS", "3")
+    monkeypatch.setenv("MDCN_WIN_SPIN_LIMIT", "0")
+    out = mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"],
+                       workspace=ws)
+    stream = torch.cuda.current_stream().cuda_stream
+    st = mdcn.mdcn_forward_check(op, mdcn.MDCN_F16, dims, ws.data_ptr(), ws.numel(), stream)
+    assert st == mdcn.MDCN_E_SYNC
+    bad = torch.isnan(out).cpu()
+    assert bool(bad.any()) and not bool(bad.all())
+    with pytest.raises(mdcn.MdcnError) as e:
+        mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"],
+                     workspace=ws, check=True)
+    assert e.value.status == mdcn.MDCN_E_SYNC
+    monkeypatch.delenv("MDCN_WIN_SPIN_LIMIT")
+    out = mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"],
+                       workspace=ws, check=True)
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    ok, err, bound = within_tolerance(got, oracle_full(pr, inp), "f16")
+    assert ok, error_report(got, oracle_full(pr, inp))
+
+
+@pytest.mark.parametrize("path,dtype", [(mdcn.MDCN_PATH_DIRECT, "f32"),
+                                        (mdcn.MDCN_PATH_GATHER_GEMM, "f32"),
+                                        (mdcn.MDCN_PATH_FUSED, "f16"),
+                                        (mdcn.MDCN_PATH_WINDOW, "f16")])
+def test_nonfinite_pixel_off_image_corners(path, dtype):
+    """x[n][c][0][0] is NaN (x[n][c][0][1] is +inf) and the samples sit on
+    the top-left border, many with corners off the image.  A corner off the
+    image reads 0 and never that pixel, so an output is non-finite exactly
+    where the definition makes it so: where some tap really reaches one of
+    those pixels (the oracle's non-finite pattern), and finite elsewhere."""
+    pr = Problem(N=2, C=64, Co=32, H=12, W=12, offset_dist=("normal", 1.0))
+    inp = workloads.generate(pr, dtype, seed=26)
+    x = inp["x"].clone()
+    x[:, :, 0, 0] = float("nan")
+    x[:, :, 0, 1] = float("inf")
+    off = inp["offset"].clone()
+    off[:, 0::2] = -0.5 - off[:, 0::2].abs()              # every sample moves up
+    msk = (inp["mask"].float().clamp(0.2, 1.0)).to(inp["mask"].dtype)   # no zero mask
+    inp = dict(inp, x=x, offset=off.to(inp["offset"].dtype), mask=msk)
+    got = run_gpu(pr, inp, path).double().numpy()
+    ref = oracle_full(pr, inp)
+    bad_ref = ~np.isfinite(ref)
+    assert bad_ref.any() and not bad_ref.all()
+    assert np.array_equal(~np.isfinite(got), bad_ref)
+    fin = ~bad_ref
+    ok, err, bound = within_tolerance(got[fin], ref[fin], dtype)
+    assert ok, float((err - bound).max())
+
+
+def test_forward_check_other_paths():
+    """Paths without a hand-over wait always report MDCN_OK."""
+    pr = SMALL["multi_tile_dg2"]
+    inp = workloads.generate(pr, "f32", seed=25)
+    for path in (mdcn.MDCN_PATH_GATHER_GEMM, mdcn.MDCN_PATH_DIRECT):
+        run_gpu(pr, inp, path)
 
 
 def test_window_split_matches_unsplit(monkeypatch):
@@ -536,7 +726,7 @@ def test_window_workload_sampled(name):
     ref = oracle.forward_points(inp["x"], inp["offset"], inp["mask"], inp["weight"],
                                 inp["bias"], idx, **pr.attrs())
     g = got.reshape(-1)[torch.from_numpy(idx)].double().numpy()
-    rms = float(got.double().pow(2).mean().sqrt())
+    rms = float(np.sqrt(np.mean(np.asarray(ref, dtype=np.float64) ** 2)))
     ok, err, bound = within_tolerance(g, ref, "f16", rms=rms)
     assert ok, (name, error_report(g, ref), float((err / bound).max()))
     assert torch.isfinite(got).all()

@@ -9,7 +9,10 @@ routes that do not go through it:
 - the offsets enter nonlinearly: the directional derivative <grad_offset, d>
   must match a central finite difference of <grad_out, forward(offset)>, at
   offsets kept away from integer sample coordinates (where the bilinear
-  sample has a kink) and from the window edges.
+  sample has a kink) and from the window edges;
+- at exact integer sample coordinates (inside the image) reading B1 takes
+  the derivative from above: a one-sided difference along directions that
+  move every coordinate up must match.
 A mutation test plants plausible mistakes in a copy of the backward code
 and requires that one of these checks notices.  No GPU is involved.
 """
@@ -97,6 +100,60 @@ def check_offset_fd(lib):
     return worst
 
 
+def integer_problem(seed):
+    """problem(seed) with every sample coordinate an exact integer inside the
+    image ([0, H-1] x [0, W-1]): the offsets move each anchor to the nearest
+    integer point, clamped onto the image."""
+    x, off, m, w, go = problem(seed)
+    N, _, H, W = x.shape
+    kh, kw = w.shape[2], w.shape[3]
+    K = kh * kw
+    sh, sw = ATTRS["stride"]
+    ph, pw = ATTRS["padding"]
+    dh, dw = ATTRS["dilation"]
+    Ho, Wo = off.shape[2], off.shape[3]
+    ho = np.arange(Ho)[:, None]
+    wo = np.arange(Wo)[None, :]
+    out = np.empty_like(off)
+    for ch in range(off.shape[1]):
+        k = (ch % (2 * K)) // 2
+        i, j = k // kw, k % kw
+        if ch % 2 == 0:
+            anchor = (ho * sh - ph + i * dh) * np.ones((1, Wo))
+            lim = H - 1
+        else:
+            anchor = (wo * sw - pw + j * dw) * np.ones((Ho, 1))
+            lim = W - 1
+        target = np.clip(anchor[None] + np.round(off[:, ch]), 0, lim)
+        out[:, ch] = target - anchor[None]
+    return x, out, m, w, go
+
+
+def check_integer_one_sided(lib):
+    """At exact integer sample coordinates the bilinear sample has a kink;
+    reading B1 differentiates on the cell floor() selects, i.e. from above.
+    A one-sided difference along directions that move every coordinate up
+    must match <grad_offset, d> there."""
+    worst = 0.0
+    for seed in range(3):
+        x, off, m, w, go = integer_problem(seed)
+        g = oracle.backward(x, off, m, w, go, **ATTRS, lib=lib)
+        rng = np.random.default_rng(130 + seed)
+        l0 = dot(go, oracle.forward(x, off, m, w, None, **ATTRS, lib=lib))
+        eps = 1e-7
+        dirs = [rng.uniform(0.1, 1.0, off.shape)]
+        for ch in (0, 1, 4):           # one offset channel at a time: h, w, another tap's h
+            dd = np.zeros_like(off)
+            dd[:, ch] = rng.uniform(0.1, 1.0, dd[:, ch].shape)
+            dirs.append(dd)
+        for d in dirs:
+            lp = dot(go, oracle.forward(x, off + eps * d, m, w, None, **ATTRS, lib=lib))
+            fd = (lp - l0) / eps
+            an = dot(g["offset"], d)
+            worst = max(worst, abs(fd - an) / max(abs(an), 1e-9))
+    return worst
+
+
 def check_off_image(lib):
     """Samples beyond the window give zero gradients for offset and mask."""
     x, off, m, w, go = problem(7)
@@ -108,10 +165,11 @@ def check_off_image(lib):
 
 def all_checks(lib):
     return {"adjoint": check_adjoint(lib), "offset_fd": check_offset_fd(lib),
+            "integer_one_sided": check_integer_one_sided(lib),
             "off_image": check_off_image(lib)}
 
 
-LIMITS = {"adjoint": 1e-10, "offset_fd": 1e-6, "off_image": 0.0}
+LIMITS = {"adjoint": 1e-10, "offset_fd": 1e-6, "integer_one_sided": 1e-5, "off_image": 0.0}
 
 
 def passes(name, v):
@@ -129,6 +187,12 @@ def test_adjoint_identities(lib):
 
 def test_offset_gradient_matches_finite_differences(lib):
     assert passes("offset_fd", check_offset_fd(lib))
+
+
+def test_offset_gradient_at_integer_coordinates_is_from_above(lib):
+    x, off, m, w, go = integer_problem(0)
+    assert np.array_equal(off, np.round(off))   # really on the kinks
+    assert passes("integer_one_sided", check_integer_one_sided(lib))
 
 
 def test_off_image_samples_have_no_gradient(lib):
@@ -158,6 +222,10 @@ MUTANTS = {
     "scatter_weights_transposed": ("(1.0 - a) * b, a * (1.0 - b), a * b};",
                                    "a * (1.0 - b), (1.0 - a) * b, a * b};"),
     "bias_grad_dropped": ("        gb[co] += g;", "        gb[co] += 0.0;"),
+    # at an integer coordinate, the cell below (derivative from below); the
+    # same value and the same derivative everywhere else
+    "derivative_from_below": ("        return 0.0;\n    const double hf = floor(h), wf = floor(w);",
+                              "        return 0.0;\n    const double hf = ceil(h) - 1.0, wf = ceil(w) - 1.0;"),
 }
 
 
