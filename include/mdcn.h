@@ -209,6 +209,34 @@ mdcn_status mdcn_forward(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
 mdcn_status mdcn_forward_check(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
                                const void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- forward without allocation ------------------------------------------ */
+
+/* Bytes of the device array mdcn_forward_noalloc uses as its workspace (per
+ * GPU, held from the library's first use on that GPU until the process
+ * ends). */
+#define MDCN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * forward pass of mdcn_forward, with the same arguments except the
+ * workspace, which is a fixed array of MDCN_NOALLOC_SCRATCH_BYTES in this
+ * library's device memory instead of a caller's buffer.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine) and
+ * enqueues only kernel launches on `stream`.  Images go through in as few
+ * launches as the array allows; a problem whose least workspace
+ * (mdcn_workspace_bytes' min_bytes) exceeds it is rejected with
+ * MDCN_E_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * that GPU's single array and leaves its contents behind (each forward
+ * clears what must start at zero): calls that overlap in time on one GPU
+ * (other streams, other threads) race and corrupt each other's results; the
+ * caller must order them.  mdcn_forward_check does not apply (its workspace
+ * is internal); a bounded wait that gave up still shows as NaN outputs.
+ * Errors as mdcn_forward. */
+mdcn_status mdcn_forward_noalloc(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                                 const void *x, const void *offset, const void *mask,
+                                 const void *weight, const void *bias, int64_t bias_len,
+                                 void *out, void *stream);
+
 /* ---- backward ------------------------------------------------------------ */
 
 /* Gradients of a scalar loss L through the forward, given grad_out = dL/dout

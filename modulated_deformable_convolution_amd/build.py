@@ -21,8 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libmdcn.so")
 
 SOURCES = ["plan.cpp", "api.cpp", "prep.hip", "gather.hip", "gemm.hip", "depthwise.hip",
-           "fused.hip", "window.hip", "direct.hip", "backward.hip"]
-HEADERS = ["plan.h", "launch.h", "device_common.h", "mfma_common.h"]
+           "fused.hip", "window.hip", "direct.hip", "backward.hip", "noalloc.hip"]
+HEADERS = ["plan.h", "launch.h", "device_common.h", "mfma_common.h", "entry.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -10,6 +10,7 @@
 #include <new>
 #include <vector>
 
+#include "entry.h"
 #include "launch.h"
 #include "mdcn.h"
 #include "plan.h"
@@ -469,6 +470,21 @@ mdcn_status create_impl(const int32_t stride[2], const int32_t padding[2],
 }
 
 }  // namespace
+
+namespace mdcn {
+
+mdcn_status forward_with_workspace(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims[16],
+                                   const void *x, const void *offset, const void *mask,
+                                   const void *weight, const void *bias, int64_t bias_len,
+                                   void *out, void *workspace, size_t workspace_bytes,
+                                   void *stream)
+{
+    return forward_impl(op, dtype, dims, x, offset, mask, weight, bias, bias_len, out, workspace,
+                        workspace_bytes, stream, nullptr);
+}
+
+}  // namespace mdcn
+
 
 extern "C" {
 

@@ -49,8 +49,11 @@ EXPORTED = [
     "mdcn_trace_reset", "mdcn_forward_traced", "mdcn_trace_count", "mdcn_trace_read",
     "mdcn_kernel_name", "mdcn_status_string", "mdcn_abi_version", "mdcn_describe_plan",
     "mdcn_backward_workspace_bytes", "mdcn_backward", "mdcn_backward_traced",
-    "mdcn_forward_check",
+    "mdcn_forward_check", "mdcn_forward_noalloc",
 ]
+
+# bytes of the device array mdcn_forward_noalloc works in (include/mdcn.h)
+MDCN_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class MdcnError(RuntimeError):
@@ -81,6 +84,8 @@ def _bind(lib):
                           _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
         "mdcn_forward_check": ([_vp, ctypes.c_int, _i64p, _vp, ctypes.c_size_t, _vp],
                                ctypes.c_int),
+        "mdcn_forward_noalloc": ([_vp, ctypes.c_int, _i64p, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.c_int64, _vp, _vp], ctypes.c_int),
         "mdcn_forward_traced": ([_vp, ctypes.c_int, _i64p, _vp, _vp, _vp, _vp, _vp,
                                  ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp, _vp],
                                 ctypes.c_int),
@@ -210,6 +215,14 @@ def mdcn_forward_check(op: Op, dtype: int, dims, workspace: int, workspace_bytes
     """Raw entry point; returns the status code (does not raise)."""
     return library().mdcn_forward_check(op.handle, int(dtype), _arr(ctypes.c_int64, dims),
                                         workspace or None, int(workspace_bytes), stream or None)
+
+
+def mdcn_forward_noalloc(op: Op, dtype: int, dims, x: int, offset: int, mask: int, weight: int,
+                         bias: int, bias_len: int, out: int, stream: int) -> int:
+    """Raw entry point; returns the status code (does not raise)."""
+    return library().mdcn_forward_noalloc(
+        op.handle, int(dtype), _arr(ctypes.c_int64, dims), x or None, offset or None,
+        mask or None, weight or None, bias or None, int(bias_len), out or None, stream or None)
 
 
 def mdcn_backward_workspace_bytes(op: Op, dtype: int, dims) -> int:
