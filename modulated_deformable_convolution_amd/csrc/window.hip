@@ -725,7 +725,10 @@ void window_kernel(WinArgs args)
         // Waves w and w + 4 share a SIMD.  Each step is a blend half (this
         // step's B from the corners read in the previous step, then the next
         // step's corner reads) and an MFMA half (8 MFMAs and the next step's
-        // A fragment reads).  At a barrier, waves 0-3 wait before their blend
+        // A fragment reads).  (Tried and slower: no workgroup barrier, waves
+        // kept within two steps of each other by arrival counters in LDS --
+        // with 8 A stages and copies 5 steps ahead a copy then has only two
+        // steps to land, and the waves waited on each other 30 % of the time.)  At a barrier, waves 0-3 wait before their blend
         // half and waves 4-7 before their MFMA half, so after it the two
         // waves of a SIMD run opposite halves (the barrier is released once
         // all eight waves have reached one of the two sites).
@@ -814,12 +817,16 @@ void window_kernel(WinArgs args)
             const uint32_t so = __builtin_amdgcn_readfirstlane(
                 uint32_t(kAOff + ((s + 1) % kAStages) * kAStage));
             const char *st = smem + (a_lane + so);
+            // (at a raised wave priority: the SIMD's other wave, in its blend
+            // half, fills the issue slots the MFMAs leave)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 acc[i] = Mma<T>::step(b, fa[i], acc[i]);
                 fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
         };
 
         for (int rc = 0; rc < c_hi - c_lo; ++rc) {
