@@ -309,19 +309,25 @@ def dims_of(x, offset, mask, weight) -> list:
     return dims
 
 
-def _alloc_stream(stream, device):
+def _alloc_stream(stream, device, allocates):
     """(handle, context) for a launch on `stream` (an int handle or None =
     torch's current stream): buffers torch allocates for the call are made
     inside the context, so the caching allocator ties them to the stream the
     kernels run on and cannot hand them out while those kernels still use
-    them."""
+    them.  The context is only built when the call allocates on a stream
+    other than torch's current one (switching streams costs tens of
+    microseconds per call)."""
     import contextlib
     import torch
+    current = torch.cuda.current_stream(device).cuda_stream
     if stream is None:
-        return torch.cuda.current_stream(device).cuda_stream, contextlib.nullcontext()
-    if int(stream) == 0:
+        return current, contextlib.nullcontext()
+    stream = int(stream)
+    if not allocates or stream == current:
+        return stream, contextlib.nullcontext()
+    if stream == 0:
         return 0, torch.cuda.stream(torch.cuda.default_stream(device))
-    return int(stream), torch.cuda.stream(torch.cuda.ExternalStream(int(stream), device=device))
+    return stream, torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device))
 
 
 def forward(op: Op, x, offset, mask, weight, bias=None, out=None, workspace=None,
@@ -339,7 +345,7 @@ def forward(op: Op, x, offset, mask, weight, bias=None, out=None, workspace=None
     code = dtype_code(x.dtype)
     dims = dims_of(x, offset, mask, weight)
     shape = mdcn_output_shape(op, dims)
-    stream, ctx = _alloc_stream(stream, x.device)
+    stream, ctx = _alloc_stream(stream, x.device, out is None or workspace is None)
     with ctx:
         if out is None:
             out = torch.empty(shape, dtype=x.dtype, device=x.device)
@@ -373,7 +379,7 @@ def backward(op: Op, x, offset, mask, weight, grad_out, with_bias=True, workspac
     dims = dims_of(x, offset, mask, weight)
     if tuple(grad_out.shape) != mdcn_output_shape(op, dims):
         raise MdcnError(MDCN_E_SHAPE, "backward: grad_out")
-    stream, ctx = _alloc_stream(stream, x.device)
+    stream, ctx = _alloc_stream(stream, x.device, True)
     with ctx:
         if workspace is None:
             workspace = torch.empty(mdcn_backward_workspace_bytes(op, code, dims),
