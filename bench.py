@@ -26,6 +26,10 @@ if ROOT not in sys.path:
 METRIC = "modulated deform-conv fwd effective GFLOP/s + HBM GB/s, % roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}
+# fp32 FMAs on the vector ALUs without packed math (the kernels are built with
+# packed fp32 off): 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz; the
+# published 157.3 TF/s vector figure counts two-wide packed FMAs
+VALU_FP32_TFLOPS = 78.6
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
 
@@ -350,6 +354,8 @@ def main(argv=None) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(pr, inp, args.cpu_seconds)
+        cpu["cpu_model"] = cpu_model()
+        cpu["other_configs"] = cpu_baseline_other_configs(min(2.0, args.cpu_seconds / 4))
 
     line = {
         "metric": METRIC,
@@ -472,10 +478,21 @@ def bench_backward(args, pr):
                              tflops=round(m["flops"] / (avg * 1e-3) / 1e12, 3))
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dominant]
-    if dk["algo_flops_per_launch"]:
-        # a VALU fp32 contraction: the published fp32 vector peak
-        roofline = dict(bound="alu", achieved=dk["tflops"], peak=157.3, unit="TFLOP/s",
-                        frac=round(dk["tflops"] / 157.3, 4), traffic=None, kernel=dominant)
+    # the two contractions run on the fp32 MFMA GEMM for one group with Co a
+    # multiple of 32 (the weight gradient also needs Ho*Wo a multiple of 32),
+    # else on a VALU kernel (fp32 FMAs, no packed math: half the published
+    # 157.3 TF/s vector peak, which counts packed fp32)
+    ho, wo = pr.out_hw()
+    on_mfma = {"bwd_col_gemm": pr.groups == 1 and pr.Co % 32 == 0,
+               "bwd_weight_gemm": pr.groups == 1 and pr.Co % 32 == 0 and (ho * wo) % 32 == 0}
+    if dk["algo_flops_per_launch"] and on_mfma.get(dominant, False):
+        roofline = dict(bound="mfma", achieved=dk["tflops"], peak=MFMA_PEAK_TFLOPS["f32"],
+                        unit="TFLOP/s", frac=round(dk["tflops"] / MFMA_PEAK_TFLOPS["f32"], 4),
+                        traffic=None, kernel=dominant)
+    elif dk["algo_flops_per_launch"]:
+        roofline = dict(bound="alu", achieved=dk["tflops"], peak=VALU_FP32_TFLOPS,
+                        unit="TFLOP/s", frac=round(dk["tflops"] / VALU_FP32_TFLOPS, 4),
+                        traffic=None, kernel=dominant)
     else:
         roofline = dict(bound="hbm", achieved=dk["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(dk["gbs"] / HBM_PEAK_GBS, 4), traffic=None, kernel=dominant)
@@ -496,11 +513,25 @@ def bench_backward(args, pr):
     return 0
 
 
-def cpu_baseline(pr, inp, target_s):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(pr, inp, target_s, threads=None):
     """The oracle, untouched, on a bounded random sample of the same
-    workload's outputs; scaled to effective GFLOP/s."""
+    workload's outputs; scaled to effective GFLOP/s.  threads: OpenMP threads
+    (None: the runtime's default, every core)."""
     import numpy as np
     from oracle import oracle
+    default_threads = oracle.max_threads()
+    oracle.set_threads(threads or default_threads)
     Ho, Wo = pr.out_hw()
     total = pr.N * pr.Co * Ho * Wo
     Kg = (pr.C // pr.groups) * pr.kh * pr.kw
@@ -522,11 +553,37 @@ def cpu_baseline(pr, inp, target_s):
         if elapsed >= target_s or n >= total:
             break
         n = min(total, int(n * max(2.0, min(16.0, 1.2 * target_s / max(elapsed, 1e-3)))))
+    reps = 1
+    if elapsed < 0.2:
+        # the whole output takes too little time to measure once: repeat it
+        reps = max(1, int(math.ceil(0.2 / max(elapsed, 1e-5))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.forward_points(x, off, msk, w, b, idx, **attrs)
+        elapsed = (time.perf_counter() - t0) / reps
     flops = 2.0 * len(idx) * Kg
+    used = oracle.max_threads()
+    oracle.set_threads(default_threads)
     return {"value": round(flops / elapsed / 1e9, 3), "unit": "GFLOP/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": "%d random output elements of the same workload (seed 0), %.1f s" %
-                      (len(idx), elapsed)}
+            "cores": used, "kind": "oracle",
+            "sample": "%d random output elements of the same workload (seed 0), %.3f s%s" %
+                      (len(idx), elapsed, (" (mean of %d runs)" % reps) if reps > 1 else "")}
+
+
+def cpu_baseline_other_configs(target_s):
+    """The oracle on the tiny, strided/grouped and depthwise configurations,
+    on every core and on one thread (bounded samples, seed 0, each
+    configuration's own dtype)."""
+    from modulated_deformable_convolution_amd import workloads
+    out = {}
+    for name in ("tiny_n1_c4_8x8", "strided_grouped_n2_c128_co256_128x128",
+                 "depthwise_n8_c256_96x96"):
+        pr, dtypes = workloads.WORKLOADS[name]
+        inp = workloads.generate(pr, dtypes[0], seed=0)
+        out[name] = {"dtype": dtypes[0],
+                     "all_cores": cpu_baseline(pr, inp, target_s),
+                     "one_thread": cpu_baseline(pr, inp, target_s, threads=1)}
+    return out
 
 
 if __name__ == "__main__":

@@ -143,6 +143,19 @@ int mdcn_oracle_max_threads(void)
 #endif
 }
 
+/* Sets that thread count (n > 0); for timing the oracle on one thread.  The
+ * results do not depend on it: every output element is one thread's
+ * sequential sum. */
+void mdcn_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Full forward: out is [N][Co][Ho][Wo].  bias may be NULL.
  * Returns 0, or -1 if the description is not one this definition covers. */
 int mdcn_oracle_forward(const double *x, const double *offset, const double *mask,

@@ -56,6 +56,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mdcn_oracle_backward.restype = ctypes.c_int
     lib.mdcn_oracle_max_threads.argtypes = []
     lib.mdcn_oracle_max_threads.restype = ctypes.c_int
+    lib.mdcn_oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.mdcn_oracle_set_threads.restype = None
     return lib
 
 
@@ -78,6 +80,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 
 def max_threads(lib: ctypes.CDLL | None = None) -> int:
     return int((lib or load_library()).mdcn_oracle_max_threads())
+
+
+def set_threads(n: int, lib: ctypes.CDLL | None = None) -> None:
+    """OpenMP threads for the following calls (timing only; results do not
+    depend on it)."""
+    (lib or load_library()).mdcn_oracle_set_threads(int(n))
 
 
 def _f64(a) -> np.ndarray:
