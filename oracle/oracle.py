@@ -28,11 +28,13 @@ _lock = threading.Lock()
 _lib = None
 
 
-def compile_library(source: str = SOURCE, output: str = LIBRARY) -> str:
-    """Build the oracle shared library with gcc (-O2, OpenMP, no fast-math)."""
+def compile_library(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
+    """Build the oracle shared library with gcc (-O2, OpenMP, no fast-math);
+    extra_flags: e.g. sanitizer options for a checking build."""
     tmp = output + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-           "-fno-fast-math", "-ffp-contract=off", source, "-o", tmp, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off"] + list(extra_flags) + [
+           source, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     os.replace(tmp, output)
     return output
@@ -67,6 +69,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     With ``path`` given, that exact file is loaded, which lets a test load a
     deliberately altered build of the oracle."""
     global _lib
+    if path is None:
+        # a checking build (e.g. under sanitizers) in place of the default one
+        path = os.environ.get("MDCN_ORACLE_LIBRARY") or None
     if path is not None:
         return _bind(ctypes.CDLL(path))
     with _lock:
