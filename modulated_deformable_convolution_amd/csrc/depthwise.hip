@@ -54,6 +54,7 @@ struct DwArgs {
     int has_bias;
     int cblocks;             // channel blocks per image (staged kernel)
     int DG;
+    uint32_t w_magic;        // floor(2^32 / W) + 1 for W > 1: pos / W = umulhi(pos, w_magic)
 };
 
 // Sampling geometry: rows r = (img*DG + q)*K + k of P records, one per
@@ -314,33 +315,38 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
                 }
             }
         };
-        // One tap's geometry record (vector offset vo = the pixel's record).
-        auto load_tap = [&](uint4 &g, uint32_t vo) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rgeo, vo, 0, 0);
+        // One tap's geometry record: vector offset vo = the pixel's record in
+        // row 0, scalar offset so = the tap's row.
+        auto load_tap = [&](uint4 &g, uint32_t vo, uint32_t so) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rgeo, vo, int(so), 0);
             g = make_uint4(v[0], v[1], v[2], v[3]);
         };
         if constexpr (KT9) {
-            // 3x3 taps: the geometry of UP pixels is loaded one group ahead
-            // of their taps (two register sets).
-            struct Geo {
-                uint4 g[UP][9];
-            };
-            auto load_geo = [&](Geo &gs, int pbase) {
+            // 3x3 taps, UP pixels per thread at a time.  One register set of
+            // geometry records: as a tap's record is consumed, the same tap's
+            // record of the next group of pixels is loaded into its place, so
+            // each record has about a pixel's worth of taps to arrive.
+            constexpr int STRIDE = UP * kStagedThreads;
+            uint4 g[UP][9];
+            int pb = tid;
 #pragma unroll
-                for (int u = 0; u < UP; ++u) {
-                    // row offsets built up in vector registers: uniform per-row
-                    // offsets would each hold a scalar register for the loop
-                    uint32_t vo = uint32_t(min(pbase + u * kStagedThreads, a.P - 1)) * 16u;
+            for (int u = 0; u < UP; ++u) {
+                const uint32_t vo = uint32_t(min(pb + u * kStagedThreads, a.P - 1)) * 16u;
+                // in tap order (the scheduler would otherwise reverse them,
+                // and the first wait would then be for all of them)
 #pragma unroll
-                    for (int k = 0; k < 9; ++k) {
-                        load_tap(gs.g[u][k], vo);
-                        vo += rowb;
-                    }
+                for (int k = 0; k < 9; ++k) {
+                    load_tap(g[u][k], vo, uint32_t(k) * rowb);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            };
-            auto group = [&](const Geo &gs, int pbase) {
+            }
+            for (; pb < a.P; pb += STRIDE) {
 #pragma unroll
                 for (int u = 0; u < UP; ++u) {
+                    // the next group's records (clamped: past the last pixel
+                    // they are loaded and never used)
+                    const uint32_t vn =
+                        uint32_t(min(pb + STRIDE + u * kStagedThreads, a.P - 1)) * 16u;
                     float acc[CH][kMaxMg];
 #pragma unroll
                     for (int ch = 0; ch < CH; ++ch)
@@ -351,33 +357,22 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
                     // issued before tap k's blend, so the LDS latency overlaps
                     // arithmetic.
                     Smp sp[2];
-                    sample(sp[0], 0, gs.g[u][0]);
+                    sample(sp[0], 0, g[u][0]);
+                    load_tap(g[u][0], vn, 0u);
 #pragma unroll
                     for (int k = 0; k < 9; ++k) {
-                        if (k < 8)
-                            sample(sp[(k + 1) & 1], k + 1, gs.g[u][k + 1]);
+                        if (k < 8) {
+                            sample(sp[(k + 1) & 1], k + 1, g[u][k + 1]);
+                            load_tap(g[u][k + 1], vn, uint32_t(k + 1) * rowb);
+                        }
                         blend(acc, sp[k & 1], k);
                         pin(acc);
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                    if (pbase + u * kStagedThreads < a.P)
-                        store(acc, pbase + u * kStagedThreads);
+                    if (pb + u * kStagedThreads < a.P)
+                        store(acc, pb + u * kStagedThreads);
                 }
-            };
-            constexpr int STRIDE = UP * kStagedThreads;
-            Geo g0, g1;
-            int pb = tid;
-            load_geo(g0, pb);
-            // two groups per trip, so that the register sets keep their names
-            for (; pb + STRIDE < a.P; pb += 2 * STRIDE) {
-                load_geo(g1, pb + STRIDE);
-                group(g0, pb);
-                if (pb + 2 * STRIDE < a.P)
-                    load_geo(g0, pb + 2 * STRIDE);
-                group(g1, pb + STRIDE);
             }
-            if (pb < a.P)
-                group(g0, pb);
         } else {
             for (int pix = tid; pix < a.P; pix += kStagedThreads) {
                 float acc[CH][kMaxMg];
@@ -386,11 +381,12 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
 #pragma unroll
                     for (int mm = 0; mm < kMaxMg; ++mm)
                         acc[ch][mm] = 0.0f;
-                uint32_t vo = uint32_t(pix) * 16u;
+                const uint32_t vo = uint32_t(pix) * 16u;
+                uint32_t so = 0;
                 for (int k = 0; k < a.K; ++k) {
                     uint4 g;
-                    load_tap(g, vo);
-                    vo += rowb;
+                    load_tap(g, vo, so);
+                    so += rowb;
                     Smp sm;
                     sample(sm, k, g);
                     blend(acc, sm, k);
@@ -398,6 +394,320 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
                 }
                 store(acc, pix);
             }
+        }
+    }
+}
+
+// Persistent kernel for the common depthwise case: 3x3 taps and one output
+// per input channel, at most 4 channels per staged entry.  A workgroup takes
+// a run of consecutive channel blocks (of one image, where the run allows)
+// and keeps its LDS plane busy: 8 waves compute one block while 8 loader
+// waves read the next block's plane into their registers (kPersLoadBytes per
+// loader thread), so that after the first block the HBM reads of x overlap
+// the LDS-bound sampling; between blocks the loaders write the plane's
+// interior (the zero ring stays).
+//
+// Compute waves run one pixel per thread at a time and keep two taps of
+// corner reads in flight ahead of the tap being blended (three sample slots;
+// nine taps per pixel keep the slots' rotation aligned across pixels).  The
+// tap weights live in registers, not in LDS: a broadcast LDS read still
+// returns a whole wave's worth of data.  Geometry records roll as in the
+// staged kernel: a tap's record of the pixel 512 further on is loaded as soon
+// as the tap's sample has been issued.
+constexpr int kPersCompute = 512;
+constexpr int kPersLoad = 256;
+constexpr int kPersThreads = kPersCompute + kPersLoad;
+constexpr int kPersLoadBytes = 576;
+
+template <typename T, int ENT>
+__global__ __launch_bounds__(kPersThreads) void depthwise_persistent_kernel(
+    const T *__restrict__ x, const uint4 *__restrict__ geo, const T *__restrict__ w,
+    const T *__restrict__ bias, T *__restrict__ out, DwArgs a)
+{
+    constexpr int CH = ENT / int(sizeof(T));         // channels per entry
+    constexpr int SLOTS = kPersLoadBytes / ENT;      // plane positions per loader thread
+    static_assert(CH <= 4, "tap weights of at most 4 channels stay in registers");
+    using Ent = typename EntryType<ENT>::type;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int PW = a.W + 4, PH = a.H + 4;
+    const int tid = int(threadIdx.x);
+    // pixel-group counter of the compute waves, after the plane
+    uint32_t *ctr = reinterpret_cast<uint32_t *>(lds + size_t(PH) * PW * ENT);
+
+    // this workgroup's channel blocks [b_lo, b_hi) of the (image, block) sequence
+    const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
+    const uint64_t nblk = uint64_t(a.N) * uint64_t(a.cblocks);
+    const int b_lo = __builtin_amdgcn_readfirstlane(int(uint64_t(lid) * nblk / gridDim.x));
+    const int b_hi = __builtin_amdgcn_readfirstlane(int(uint64_t(lid + 1) * nblk / gridDim.x));
+    if (b_lo >= b_hi)
+        return;
+
+    // First block: the whole plane, ring included, by every thread (as in
+    // the staged kernel: SU entries per thread in flight at a time).
+    if (tid == 0)
+        *ctr = 0u;
+    {
+        const int n = b_lo / a.cblocks, c0 = (b_lo % a.cblocks) * CH;
+        const int ncb = min(CH, a.C - c0);
+        constexpr int SU = 8;
+        const int NE = PH * PW;
+        for (int e0 = tid; e0 < NE; e0 += SU * kPersThreads) {
+            T v[SU][CH];
+#pragma unroll
+            for (int su = 0; su < SU; ++su) {
+                const int e = e0 + su * kPersThreads;
+                const int r = e / PW, cc = e - (e / PW) * PW;
+                const int xr = r - 2, xc = cc - 2;
+                const bool in = (e < NE) & (xr >= 0) & (xr < a.H) & (xc >= 0) & (xc < a.W);
+#pragma unroll
+                for (int ch = 0; ch < CH; ++ch)
+                    v[su][ch] = (in && ch < ncb)
+                                    ? x[(size_t(n) * a.C + c0 + ch) * a.HW + size_t(xr) * a.W + xc]
+                                    : from_f32<T>(0.0f);
+            }
+#pragma unroll
+            for (int su = 0; su < SU; ++su) {
+                const int e = e0 + su * kPersThreads;
+                if (e < NE) {
+                    Ent en;
+                    __builtin_memcpy(&en, v[su], ENT);
+                    *reinterpret_cast<Ent *>(lds + size_t(e) * ENT) = en;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const uint32_t rowb = uint32_t(a.P) * 16u;
+    // The two roles run loops of their own (their registers never overlap)
+    // with the same barriers: after each block's sampling, and after the
+    // next block's plane is in LDS.
+    if (__builtin_amdgcn_readfirstlane(tid) >= kPersCompute) {
+        const int lt = tid - kPersCompute;
+        // plane row of a position (exact for pos * W < 2^32)
+        auto row_of = [&](int pos) {
+            return a.W > 1 ? int(__umulhi(uint32_t(pos), a.w_magic)) : pos;
+        };
+        for (int b = b_lo; b + 1 < b_hi; ++b) {
+            // the next block's plane interior into registers; position
+            // j*kPersLoad + lt of the image plane, all CH channels
+            const int n = (b + 1) / a.cblocks, c0 = ((b + 1) % a.cblocks) * CH;
+            const int ncb = min(CH, a.C - c0);
+            // one buffer per channel plane: reads past the plane, and every
+            // read of a channel past the last, return 0
+            __amdgpu_buffer_rsrc_t rx[CH];
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch)
+                rx[ch] = dw_rsrc(x + (size_t(n) * a.C + c0 + min(ch, ncb - 1)) * a.HW,
+                                 ch < ncb ? uint32_t(a.HW) * uint32_t(sizeof(T)) : 0u);
+            if constexpr (sizeof(T) == 4) {
+                Ent R[SLOTS];
+                uint32_t vo = uint32_t(lt) * 4u;
+#pragma unroll
+                for (int j = 0; j < SLOTS; ++j) {
+                    T v[CH];
+#pragma unroll
+                    for (int ch = 0; ch < CH; ++ch)
+                        v[ch] = dw_load<T>(rx[ch], vo, 0);
+                    __builtin_memcpy(&R[j], v, ENT);
+                    // one offset register, stepped (not one per slot)
+                    vo += uint32_t(kPersLoad) * 4u;
+                    asm volatile("" : "+v"(vo));
+                }
+                __syncthreads();                     // block b's sampling is done
+                int pos = lt;
+#pragma unroll
+                for (int j = 0; j < SLOTS; ++j, pos += kPersLoad) {
+                    // addresses one slot at a time (not all hoisted beside R)
+                    asm volatile("" : "+v"(pos));
+                    if (pos < a.HW) {
+                        const int xr = row_of(pos), xc = pos - xr * a.W;
+                        const size_t e = size_t(xr + 2) * PW + xc + 2;
+                        *reinterpret_cast<Ent *>(lds + e * ENT) = R[j];
+                    }
+                }
+            } else {
+                // 16-bit values: one 4-byte read per channel covers the
+                // positions 2p and 2p+1 (the plane has an even size); the
+                // halves are sorted into the two entries when written
+                constexpr int PAIRS = kPersLoadBytes / 4 / CH;
+                uint32_t R[PAIRS][CH];
+                uint32_t vo = uint32_t(lt) * 4u;
+#pragma unroll
+                for (int j = 0; j < PAIRS; ++j) {
+#pragma unroll
+                    for (int ch = 0; ch < CH; ++ch)
+                        R[j][ch] = __builtin_amdgcn_raw_buffer_load_b32(rx[ch], vo, 0, 0);
+                    vo += uint32_t(kPersLoad) * 4u;
+                    asm volatile("" : "+v"(vo));
+                }
+                __syncthreads();                     // block b's sampling is done
+                int pos = 2 * lt;
+#pragma unroll
+                for (int j = 0; j < PAIRS; ++j, pos += 2 * kPersLoad) {
+                    asm volatile("" : "+v"(pos));
+                    if (pos < a.HW) {
+                        uint32_t lo[CH / 2], hi[CH / 2];
+#pragma unroll
+                        for (int c = 0; c < CH / 2; ++c) {
+                            const uint32_t u = R[j][2 * c], v = R[j][2 * c + 1];
+                            lo[c] = __builtin_amdgcn_perm(v, u, 0x05040100u);
+                            hi[c] = __builtin_amdgcn_perm(v, u, 0x07060302u);
+                        }
+                        Ent e0, e1;
+                        __builtin_memcpy(&e0, lo, ENT);
+                        __builtin_memcpy(&e1, hi, ENT);
+                        const int xr = row_of(pos), xc = pos - xr * a.W;
+                        const size_t f0 = size_t(xr + 2) * PW + xc + 2;
+                        *reinterpret_cast<Ent *>(lds + f0 * ENT) = e0;
+                        const int p1 = pos + 1;
+                        const int yr = row_of(p1), yc = p1 - yr * a.W;
+                        const size_t f1 = size_t(yr + 2) * PW + yc + 2;
+                        *reinterpret_cast<Ent *>(lds + f1 * ENT) = e1;
+                    }
+                }
+            }
+            __syncthreads();                         // block b+1's plane is staged
+        }
+        return;
+    }
+    for (int b = b_lo; b < b_hi; ++b) {
+        const int n = b / a.cblocks, c0 = (b % a.cblocks) * CH;
+        const int ncb = min(CH, a.C - c0);
+        const int q = c0 / a.Cdg;
+        const __amdgpu_buffer_rsrc_t rgeo =
+            dw_rsrc(geo + (size_t(n) * a.DG + q) * 9 * size_t(a.P), 9u * rowb);
+        float wk[9][CH];                             // tap weights
+#pragma unroll
+        for (int k = 0; k < 9; ++k)
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch)
+                wk[k][ch] = to_f32(w[size_t(min(c0 + ch, a.C - 1)) * 9 + k]);
+        float bz[CH];                                // bias (scalar loads before the loop)
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch)
+            bz[ch] = a.has_bias ? to_f32(bias[min(c0 + ch, a.C - 1)]) : 0.0f;
+        if constexpr (sizeof(T) == 4) {
+            // the scalar loads land before the sampling loop: a scalar load
+            // still in flight there would make every LDS wait a full drain
+#pragma unroll
+            for (int k = 0; k < 9; ++k)
+#pragma unroll
+                for (int ch = 0; ch < CH; ++ch)
+                    asm volatile("" : "+s"(wk[k][ch]));
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch)
+                asm volatile("" : "+s"(bz[ch]));
+        }
+
+        struct Smp {
+            Ent e00, e01, e10, e11;
+            float w[4];
+        };
+        auto sample = [&](Smp &sm, const uint4 &g) {
+            const float ly = __builtin_bit_cast(float, g.y);
+            const float lxm = __builtin_bit_cast(float, g.z);
+            const float hxm = __builtin_bit_cast(float, g.w);
+            sm.w[0] = fmaf(-ly, hxm, hxm);
+            sm.w[1] = fmaf(-ly, lxm, lxm);
+            sm.w[2] = ly * hxm;
+            sm.w[3] = ly * lxm;
+            // computed here, while the record is live (not sunk to the blend)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                asm volatile("" : "+v"(sm.w[c]));
+            const char *pe = lds + g.x * uint32_t(ENT);
+            sm.e00 = *reinterpret_cast<const Ent *>(pe);
+            sm.e01 = *reinterpret_cast<const Ent *>(pe + ENT);
+            sm.e10 = *reinterpret_cast<const Ent *>(pe + size_t(PW) * ENT);
+            sm.e11 = *reinterpret_cast<const Ent *>(pe + size_t(PW + 1) * ENT);
+        };
+        auto blend = [&](float (&acc)[CH], const Smp &sm, int k) {
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch) {
+                float v = sm.w[0] * entry_at<T, ENT>(sm.e00, ch);
+                v = fmaf(sm.w[1], entry_at<T, ENT>(sm.e01, ch), v);
+                v = fmaf(sm.w[2], entry_at<T, ENT>(sm.e10, ch), v);
+                v = fmaf(sm.w[3], entry_at<T, ENT>(sm.e11, ch), v);
+                acc[ch] = fmaf(wk[k][ch], v, acc[ch]);
+            }
+        };
+        auto load_tap = [&](uint4 &g, int pix, int k) {
+            const uint32_t vo = uint32_t(min(pix, a.P - 1)) * 16u;
+            const auto v =
+                __builtin_amdgcn_raw_buffer_load_b128(rgeo, vo, int(uint32_t(k) * rowb), 0);
+            g = make_uint4(v[0], v[1], v[2], v[3]);
+        };
+        auto store = [&](const float (&acc)[CH], int pix) {
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch)
+                if (ch < ncb)
+                    out[(size_t(n) * a.Co + c0 + ch) * a.P + pix] = from_f32<T>(acc[ch] + bz[ch]);
+        };
+        // Pixels go out in groups of 64 (one per lane of a wave) from a
+        // counter in LDS, so that waves slowed by LDS contention take fewer
+        // groups and all finish together.  A wave knows its next group
+        // while it works on the current one (the next group's geometry
+        // records are loaded tap by tap as the current ones are used) and
+        // draws the one after that at the end of each group, when it has no
+        // LDS reads in flight.
+        const int lane = tid & 63;
+        const uint32_t ngroups = uint32_t(a.P + 63) / 64u;
+        auto draw = [&]() {
+            uint32_t v = 0;
+            if (lane == 0)
+                v = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return __builtin_amdgcn_readfirstlane(v);
+        };
+        uint32_t cur = draw();
+        uint32_t nxt = draw();
+        // g[k]: the record of tap k of the next sample of tap k, in tap order
+        uint4 g[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+            load_tap(g[k], int(cur * 64u) + lane, k);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        while (cur < ngroups) {
+            const int pix = int(cur * 64u) + lane;
+            const int npix = int(nxt * 64u) + lane;
+            float acc[CH];
+#pragma unroll
+            for (int ch = 0; ch < CH; ++ch)
+                acc[ch] = 0.0f;
+            // taps software-pipelined: tap k+1's corner reads go out before
+            // tap k's blend
+            Smp sp[2];
+            sample(sp[0], g[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_tap(g[0], npix, 0);
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                if (k < 8) {
+                    sample(sp[(k + 1) & 1], g[k + 1]);
+                    // the record is consumed before its registers are reloaded
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_tap(g[k + 1], npix, k + 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // the reads go out first
+                blend(acc, sp[k & 1], k);
+#pragma unroll
+                for (int ch = 0; ch < CH; ++ch)
+                    asm volatile("" : "+v"(acc[ch]));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (pix < a.P)
+                store(acc, pix);
+            cur = nxt;
+            nxt = draw();
+        }
+        // the loaders wait here (twice per block but the last) until the
+        // plane is no longer read, then stage the next one
+        if (b + 1 < b_hi) {
+            __syncthreads();                         // the plane is no longer read
+            if (tid == 0)
+                *ctr = 0u;
+            __syncthreads();                         // the next block's plane is staged
         }
     }
 }
@@ -468,6 +778,22 @@ DwKernel<T> staged_fn(int ent, int up, bool kt9, bool mg1)
     return nullptr;
 }
 
+// The persistent kernel instance for an entry width (4 bytes or more, at
+// most 4 channels).
+template <typename T>
+DwKernel<T> pers_fn(int ent)
+{
+    if constexpr (sizeof(T) == 4) {
+        if (ent == 16)
+            return &depthwise_persistent_kernel<T, 16>;
+    }
+    if (ent == 8)
+        return &depthwise_persistent_kernel<T, 8>;
+    if (ent == 4)
+        return &depthwise_persistent_kernel<T, 4>;
+    return nullptr;
+}
+
 template <typename T>
 hipError_t depthwise_t(const Problem &p, int64_t cnt, const void *x, const void *geo,
                        const void *offset, const void *mask, const void *weight, const void *bias,
@@ -483,6 +809,7 @@ hipError_t depthwise_t(const Problem &p, int64_t cnt, const void *x, const void 
     a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
     a.has_bias = bias != nullptr;
     a.DG = int(p.DG);
+    a.w_magic = p.W > 1 ? uint32_t((uint64_t(1) << 32) / uint64_t(p.W) + 1) : 0u;
     // The widest allowed entry, one pixel per thread at a time with the next
     // one's geometry in flight.  MDCN_DW_ENTRY=<bytes> and MDCN_DW_PIXELS=1|2
     // override (for tuning), where allowed.
@@ -497,13 +824,48 @@ hipError_t depthwise_t(const Problem &p, int64_t cnt, const void *x, const void 
         if (v == 1 || v == 2)
             up = v;
     }
+    const bool kt9 = p.kh == 3 && p.kw == 3, mg1 = p.Mg == 1;
+    // 3x3 taps, one output per input channel, entries of 4 bytes or more and
+    // a plane the loader waves can hold: the persistent kernel
+    // (MDCN_DW_PERSISTENT=0 turns it off, for tuning)
+    // (at most 4 channels per entry: 8-byte entries for fp16/bf16).
+    // MDCN_DW_PERSISTENT=0 turns it off, MDCN_DW_PERSISTENT_BLOCKS=<n> sets
+    // the channel blocks per workgroup (for tuning).
+    const int pent = std::min(ent, 4 * int(sizeof(T)));
+    bool pers = kt9 && mg1 && pent >= 4 && geo != nullptr &&
+                p.H * p.W <= int64_t(kPersLoad) * (kPersLoadBytes / pent) &&
+                (sizeof(T) == 4 || (p.H * p.W) % 2 == 0);
+    if (const char *env = std::getenv("MDCN_DW_PERSISTENT"))
+        pers = pers && std::atoi(env) != 0;
+    if (pers) {
+        const int ch = pent / int(sizeof(T));
+        a.cblocks = int((p.C + ch - 1) / ch);
+        const int64_t nblk = cnt * a.cblocks;
+        const int64_t cus = std::max(1, device_cu_count());
+        int64_t per = (nblk + cus - 1) / cus;
+        if (const char *env = std::getenv("MDCN_DW_PERSISTENT_BLOCKS"))
+            per = std::max<int64_t>(1, std::atoi(env));
+        const dim3 grid(unsigned((nblk + per - 1) / per));
+        const size_t lds = size_t(p.H + 4) * size_t(p.W + 4) * size_t(pent) + 16;
+        const DwKernel<T> fn = pers_fn<T>(pent);
+        if (fn != nullptr &&
+            hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess) {
+            hipLaunchKernelGGL(fn, grid, dim3(kPersThreads), lds, s, static_cast<const T *>(x),
+                               static_cast<const uint4 *>(geo),
+                               static_cast<const T *>(weight), static_cast<const T *>(bias),
+                               static_cast<T *>(out), a);
+            return hipGetLastError();
+        }
+        (void)hipGetLastError();           // clear it; use the staged kernel below
+    }
     if (ent > 0 && geo != nullptr) {
         const int ch = ent / int(sizeof(T));
         a.cblocks = int((p.C + ch - 1) / ch);
         const dim3 grid(unsigned(uint64_t(cnt) * a.cblocks));
         const size_t lds = size_t(p.H + 4) * size_t(p.W + 4) * size_t(ent) +
                            9 * size_t(ch) * sizeof(float);
-        const DwKernel<T> fn = staged_fn<T>(ent, up, p.kh == 3 && p.kw == 3, p.Mg == 1);
+        const DwKernel<T> fn = staged_fn<T>(ent, up, kt9, mg1);
         if (fn != nullptr &&
             hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess) {

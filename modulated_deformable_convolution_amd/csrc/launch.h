@@ -36,6 +36,9 @@ enum KernelId : int32_t {
     K_COUNT = 23
 };
 
+// Compute units of the current device (cached per device; 1 if unknown).
+int device_cu_count();
+
 // weight [Co][Cg][kh][kw] -> packed [G][Mg][Kp], contraction index
 // kk = k*Cg + c' (tap-major), zero for kk >= Kg.
 hipError_t launch_pack_weight(const Problem &p, const Plan &plan, const void *weight,

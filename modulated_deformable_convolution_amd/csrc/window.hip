@@ -978,26 +978,6 @@ bool split_cached(int64_t tiles, int64_t nch, int64_t ncta, int64_t seg_x4, uint
     return true;
 }
 
-// Compute units of the current device (cached per device).
-int cu_count()
-{
-    static std::mutex mu;
-    static std::map<int, int> known;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return 1;
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = known.find(dev);
-    if (it == known.end()) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 1;
-        it = known.emplace(dev, n).first;
-    }
-    return it->second;
-}
-
 template <typename T, int TH, int TW, int LEAD>
 hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                       const void *xt, const void *offset, const void *mask, const void *bias,
@@ -1055,7 +1035,7 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
     // every tile then spans at most two workgroups), and no more than the
     // workspace has partial-sum slots for.
     uint64_t blocks = std::min<uint64_t>(
-        {tiles, uint64_t(std::max(1, cu_count())), uint64_t(std::max(1, ws.slots))});
+        {tiles, uint64_t(std::max(1, device_cu_count())), uint64_t(std::max(1, ws.slots))});
     if (plan.win_max_ctas > 0)
         blocks = std::min<uint64_t>(blocks, uint64_t(plan.win_max_ctas));
     if (ws.epoch <= 0 || (blocks < tiles && (!ws.partial || !ws.flags)))
@@ -1118,6 +1098,26 @@ hipError_t launch_window(const Problem &p, const Plan &plan, int64_t cnt, const 
         break;
     }
     return hipErrorInvalidValue;
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count()
+{
+    static std::mutex mu;
+    static std::map<int, int> known;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 1;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = known.find(dev);
+    if (it == known.end()) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        it = known.emplace(dev, n).first;
+    }
+    return it->second;
 }
 
 }  // namespace mdcn

@@ -42,6 +42,17 @@ SMALL = {
     # channel multiplier of 6 (two passes of at most 4 outputs per plane)
     "depthwise_mult6_odd": Problem(N=2, C=9, Co=54, H=11, W=7, groups=9, deformable_groups=3,
                                    offset_dist=("uniform", 5.0), mask_dist=("uniform_zeros", 0.1)),
+    # depthwise 3x3 with one output per input channel (the persistent
+    # kernel): 1517 pixels = two full groups of 512 and a ragged one; an odd
+    # plane size (16-bit types stay on the staged kernel)
+    "depthwise_3x3_ragged": Problem(N=2, C=12, Co=12, H=37, W=41, groups=12,
+                                    deformable_groups=3, offset_dist=("uniform", 16.0),
+                                    mask_dist=("uniform_zeros", 0.1)),
+    # the same with an even plane size and an odd width (16-bit planes are
+    # read two positions at a time, which then straddle rows)
+    "depthwise_3x3_even": Problem(N=2, C=16, Co=16, H=30, W=35, groups=16,
+                                  deformable_groups=2, offset_dist=("uniform", 12.0),
+                                  mask_dist=("uniform_zeros", 0.1)),
     # depthwise with a 5x3 kernel (runtime tap count)
     "depthwise_5x3": Problem(N=2, C=8, Co=8, H=12, W=10, kh=5, kw=3, padding=(2, 1), groups=8,
                              deformable_groups=2, offset_dist=("normal", 2.0)),
@@ -455,6 +466,32 @@ def test_depthwise_variants(entry, pixels, name, dtype, monkeypatch):
     ref = oracle_full(pr, inp)
     ok, err, bound = within_tolerance(got, ref, dtype)
     assert ok, (entry, pixels, name, dtype, error_report(got, ref))
+
+
+@pytest.mark.parametrize("blocks", [0, 1, 2, 5])
+@pytest.mark.parametrize("entry", [16, 8, 4])
+@pytest.mark.parametrize("name,dtype", [("depthwise_3x3_ragged", "f32"),
+                                        ("depthwise_3x3_even", "f32"),
+                                        ("depthwise_3x3_even", "f16"),
+                                        ("depthwise_3x3_even", "bf16"),
+                                        ("depthwise_3x3_ragged", "bf16")])
+def test_depthwise_3x3_persistent(blocks, entry, name, dtype, monkeypatch):
+    """3x3 depthwise with one output per input channel: the persistent
+    kernel with 1, 2 and up to 5 channel blocks per workgroup (a workgroup's
+    run crossing an image boundary; loader waves staging the next block),
+    each LDS entry width the problem allows; blocks = 0 is the staged kernel
+    (MDCN_DW_PERSISTENT=0)."""
+    if blocks == 0:
+        monkeypatch.setenv("MDCN_DW_PERSISTENT", "0")
+    else:
+        monkeypatch.setenv("MDCN_DW_PERSISTENT_BLOCKS", str(blocks))
+    monkeypatch.setenv("MDCN_DW_ENTRY", str(entry))
+    pr = SMALL[name]
+    inp = workloads.generate(pr, dtype, seed=15)
+    got = run_gpu(pr, inp, mdcn.MDCN_PATH_DEPTHWISE).double().numpy()
+    ref = oracle_full(pr, inp)
+    ok, err, bound = within_tolerance(got, ref, dtype)
+    assert ok, (blocks, entry, name, dtype, error_report(got, ref))
 
 
 @pytest.mark.parametrize("name,dtype,path", [
