@@ -71,11 +71,11 @@ struct DwGeoArgs {
 };
 
 constexpr int kGeoThreads = 128;
-constexpr int kGeoTaps = 9;                  // taps whose inputs are loaded at once
+constexpr int kGeoTaps = 3;                  // taps per thread, their inputs loaded at once
 
-// One thread per (image, offset group, pixel), all taps: the loads of up to
-// kGeoTaps taps are issued together (a thread per record would have one load
-// in flight and retire after one round trip).
+// One thread per (image, offset group, pixel, group of kGeoTaps taps): the
+// loads of its taps are issued together, and the grid holds enough waves
+// (one per 64 pixels, image, offset group and tap group) to keep HBM busy.
 template <typename T>
 __global__ __launch_bounds__(kGeoThreads) void dw_geometry_kernel(const T *__restrict__ off,
                                                                   const T *__restrict__ msk,
@@ -87,48 +87,49 @@ __global__ __launch_bounds__(kGeoThreads) void dw_geometry_kernel(const T *__res
         return;
     const int ho = pix / a.Wo, wo = pix - (pix / a.Wo) * a.Wo;
     const int bh = ho * a.sh - a.ph, bw = wo * a.sw - a.pw;
-    // grid y over (image, offset group), strided when there are more
-    for (uint32_t g = blockIdx.y; g < a.groups; g += gridDim.y) {
+    const uint32_t tgroups = uint32_t(a.K + kGeoTaps - 1) / uint32_t(kGeoTaps);
+    // grid y over (image, offset group, tap group), strided when there are more
+    for (uint32_t gy = blockIdx.y; gy < a.groups * tgroups; gy += gridDim.y) {
+        const uint32_t g = gy / tgroups;
+        const int k0 = int(gy - g * tgroups) * kGeoTaps;
         const int q = int(g % uint32_t(a.DG));
         const int img = int(g / uint32_t(a.DG));
         const T *ob = off + (size_t(img) * a.offC + size_t(q) * 2 * a.K) * a.P + pix;
         const T *mb = msk + (size_t(img) * a.mskC + size_t(q) * a.K) * a.P + pix;
         uint4 *gb = geo + size_t(g) * a.K * a.P + pix;
-        for (int k0 = 0; k0 < a.K; k0 += kGeoTaps) {
-            float oh[kGeoTaps], ow[kGeoTaps], m[kGeoTaps];
+        float oh[kGeoTaps], ow[kGeoTaps], m[kGeoTaps];
 #pragma unroll
-            for (int t = 0; t < kGeoTaps; ++t) {
-                const int k = min(k0 + t, a.K - 1);
-                oh[t] = to_f32(ob[size_t(2 * k) * a.P]);
-                ow[t] = to_f32(ob[size_t(2 * k + 1) * a.P]);
-                m[t] = to_f32(mb[size_t(k) * a.P]);
-            }
+        for (int t = 0; t < kGeoTaps; ++t) {
+            const int k = min(k0 + t, a.K - 1);
+            oh[t] = to_f32(ob[size_t(2 * k) * a.P]);
+            ow[t] = to_f32(ob[size_t(2 * k + 1) * a.P]);
+            m[t] = to_f32(mb[size_t(k) * a.P]);
+        }
 #pragma unroll
-            for (int t = 0; t < kGeoTaps; ++t) {
-                const int k = k0 + t;
-                if (k >= a.K)
-                    break;
-                const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
-                const int ah = bh + i * a.dh, aw = bw + j * a.dw;
-                // Offsets clamped to +-2^24 (a NaN becomes -2^24): farther is
-                // off any image, and the integer parts stay exact.  A sample
-                // whose top-left corner (h0, w0) lies outside [-1, H-1] x
-                // [-1, W-1] has no corner on the image; it gets entry 0, whose
-                // 2 x 2 window (ring rows and columns 0 and 1) is all zeros,
-                // so it contributes 0 whatever its weights.
-                const float lim = 16777216.0f;
-                const float vh = fminf(fmaxf(oh[t], -lim), lim);
-                const float vw = fminf(fmaxf(ow[t], -lim), lim);
-                const float fh = floorf(vh), fw = floorf(vw);
-                const float h0 = float(ah) + fh, w0 = float(aw) + fw;
-                const bool on = (h0 >= -1.0f) & (h0 <= float(a.H - 1)) & (w0 >= -1.0f) &
-                                (w0 <= float(a.W - 1));
-                const uint32_t e = on ? uint32_t((int(h0) + 2) * a.PW + (int(w0) + 2)) : 0u;
-                const float ly = vh - fh, lx = vw - fw;
-                gb[size_t(k) * a.P] = make_uint4(e, __builtin_bit_cast(uint32_t, ly),
-                                                 __builtin_bit_cast(uint32_t, lx * m[t]),
-                                                 __builtin_bit_cast(uint32_t, (1.0f - lx) * m[t]));
-            }
+        for (int t = 0; t < kGeoTaps; ++t) {
+            const int k = k0 + t;
+            if (k >= a.K)
+                break;
+            const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+            const int ah = bh + i * a.dh, aw = bw + j * a.dw;
+            // Offsets clamped to +-2^24 (a NaN becomes -2^24): farther is
+            // off any image, and the integer parts stay exact.  A sample
+            // whose top-left corner (h0, w0) lies outside [-1, H-1] x
+            // [-1, W-1] has no corner on the image; it gets entry 0, whose
+            // 2 x 2 window (ring rows and columns 0 and 1) is all zeros,
+            // so it contributes 0 whatever its weights.
+            const float lim = 16777216.0f;
+            const float vh = fminf(fmaxf(oh[t], -lim), lim);
+            const float vw = fminf(fmaxf(ow[t], -lim), lim);
+            const float fh = floorf(vh), fw = floorf(vw);
+            const float h0 = float(ah) + fh, w0 = float(aw) + fw;
+            const bool on = (h0 >= -1.0f) & (h0 <= float(a.H - 1)) & (w0 >= -1.0f) &
+                            (w0 <= float(a.W - 1));
+            const uint32_t e = on ? uint32_t((int(h0) + 2) * a.PW + (int(w0) + 2)) : 0u;
+            const float ly = vh - fh, lx = vw - fw;
+            gb[size_t(k) * a.P] = make_uint4(e, __builtin_bit_cast(uint32_t, ly),
+                                             __builtin_bit_cast(uint32_t, lx * m[t]),
+                                             __builtin_bit_cast(uint32_t, (1.0f - lx) * m[t]));
         }
     }
 }
@@ -896,8 +897,9 @@ hipError_t dw_geometry_t(const Problem &p, int64_t cnt, const void *offset, cons
     a.sh = int(p.sh); a.sw = int(p.sw); a.ph = int(p.ph); a.pw = int(p.pw);
     a.dh = int(p.dh); a.dw = int(p.dw);
     a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
+    const unsigned tgroups = unsigned((p.K + kGeoTaps - 1) / kGeoTaps);
     const dim3 grid(unsigned((p.P + kGeoThreads - 1) / kGeoThreads),
-                    std::min<unsigned>(a.groups, 65535u));
+                    unsigned(std::min<uint64_t>(uint64_t(a.groups) * tgroups, 65535u)));
     hipLaunchKernelGGL(dw_geometry_kernel<T>, grid, dim3(kGeoThreads), 0, s,
                        static_cast<const T *>(offset), static_cast<const T *>(mask),
                        static_cast<uint4 *>(geo), a);
