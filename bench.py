@@ -51,7 +51,7 @@ MEASURED_TRAFFIC = {
     ("window_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
         "bytes": (125786 * 2 + 117135) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "b7a9a76d2f649ec9",
+        "sha": "10df2ec0c4250d9e",
     },
     ("fused_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
         "bytes": (53919 * 2 + 51200) * 1024,

@@ -17,24 +17,29 @@
 // from global memory instead (the fallback), so the result does not depend
 // on the margin.
 //
-// The grid is persistent, one workgroup (4 waves, one per SIMD) per CU.  The
+// The grid is persistent, one workgroup (8 waves, two per SIMD) per CU.  The
 // (tile, chunk) units are cut into contiguous per-workgroup ranges on the
-// host (balanced for chunks plus a per-tile cost); a workgroup walks the
-// tiles of its range from last to first.  A tile split between two
-// workgroups is finished by the one holding its last chunks: the other
-// publishes its accumulators (device-scope stores, then a flag) on the first
-// tile it processes, and the finisher loads them into its accumulators on
-// the last one.
+// host (balanced for chunks plus a per-tile cost, keeping tiles whole where
+// the counts allow); a workgroup walks the tiles of its range from last to
+// first.  A tile split between two workgroups is finished by the one holding
+// its last chunks: the other publishes its accumulators (device-scope
+// stores, then a flag) on the first tile it processes, and the finisher
+// loads them into its accumulators on the last one (a bounded wait: a
+// hand-over that never comes is recorded in a status word, never a hang).
 //
-// Every wave owns 64 pixels (two slabs of 32) and all 256 output channels:
-// it makes the B fragments of its own pixels in registers (lane l of a slab
-// owns pixel l%32 and channels 8*(l/32)..+8 of the chunk, which is exactly
-// the MFMA B-fragment layout), so B never goes through LDS, and reads the A
-// fragments (packed weight rows) from LDS stages filled by DMA LEAD steps
-// ahead.  The per-lane sampling geometry of all taps (window address of the
-// top-left corner, four weights with the mask folded in) is computed once per
-// tile and kept in registers.  In each step the MFMAs of step s run beside
-// the bilinear blend of step s+1 and the LDS reads of step s+2.
+// Every wave owns one slab of 32 pixels and all 256 output channels: it
+// makes the B fragments of its own pixels in registers (lane l owns pixel
+// l%32 and channels 8*(l/32)..+8 of the chunk, which is exactly the MFMA
+// fragment layout), so B never goes through LDS, and reads the A fragments
+// (packed weight rows) from LDS stages filled by DMA LEAD steps ahead.  The
+// per-lane sampling geometry of all taps (window address of the top-left
+// corner as packed 16-bit offsets, the bilinear factors with the mask folded
+// in) is computed once per tile and kept in registers.  A step is a blend
+// half (this step's B from the corners read one step before, then the next
+// step's corner reads) and an MFMA half (8 MFMAs, then the next step's A
+// fragment reads); the two waves of a SIMD run opposite halves, and the
+// MFMA half runs at raised wave priority so that its issue is not starved
+// by the partner's blend.
 //
 // Both operands come in layouts that make every LDS copy contiguous (a copy
 // instruction's cost on the texture path grows with the cache lines it
