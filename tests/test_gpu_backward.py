@@ -36,6 +36,15 @@ CASES = {
     "depthwise": Problem(N=2, C=8, Co=8, H=9, W=9, groups=8),
     "grid_smaller": Problem(N=1, C=12, Co=8, H=11, W=11, Ho=7, Wo=9),
     "wide_channels": Problem(N=1, C=128, Co=64, H=16, W=16, offset_dist=("normal", 2.0)),
+    # 128 channels in two offset groups (64-lane teams), an output grid with
+    # odd sizes, offsets of sigma 3
+    "dg2_ragged": Problem(N=2, C=128, Co=32, H=21, W=19, deformable_groups=2,
+                          offset_dist=("normal", 3.0)),
+    # ... with groups, stride and dilation 2, far offsets and zero masks
+    "grouped_strided_far": Problem(N=1, C=128, Co=64, H=23, W=17, stride=(2, 2),
+                                   padding=(2, 2), dilation=(2, 2), groups=2,
+                                   deformable_groups=2, offset_dist=("uniform", 6.0),
+                                   mask_dist=("uniform_zeros", 0.2)),
     # fp32: both contractions on the MFMA GEMM, the weight gradient in two
     # pixel chunks of 512 (P = 1024)
     "mfma_split": Problem(N=2, C=32, Co=64, H=32, W=32, offset_dist=("normal", 1.0)),
