@@ -44,6 +44,13 @@ CASES = [
     ("depthwise", Problem(N=2, C=24, Co=48, H=13, W=13, groups=24, deformable_groups=3,
                           offset_dist=("uniform", 8.0), mask_dist=("uniform_zeros", 0.1)),
      "f32", mdcn.MDCN_PATH_DEPTHWISE),
+    # 3x3 depthwise, one output per channel: the persistent kernel with two
+    # channel blocks per workgroup (MDCN_DW_PERSISTENT_BLOCKS), its loader
+    # waves staging the second block on every replay
+    ("depthwise_persistent", Problem(N=2, C=16, Co=16, H=30, W=35, groups=16,
+                                     deformable_groups=2, offset_dist=("uniform", 12.0),
+                                     mask_dist=("uniform_zeros", 0.1)),
+     "f32", mdcn.MDCN_PATH_DEPTHWISE),
     ("gather_gemm_fp8", Problem(N=2, C=32, Co=48, H=15, W=13, deformable_groups=2,
                                 offset_dist=("normal", 2.0)), "f16",
      mdcn.MDCN_PATH_GATHER_GEMM_FP8),
@@ -58,6 +65,8 @@ def _dev(inp):
 def test_graph_replays_match_eager(name, pr, dtype, path, monkeypatch):
     if name == "window_split":
         monkeypatch.setenv("MDCN_WIN_CTAS", "7")
+    if name == "depthwise_persistent":
+        monkeypatch.setenv("MDCN_DW_PERSISTENT_BLOCKS", "2")
     op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups,
                           path=path)
     inputs = [workloads.generate(pr, dtype, seed=s) for s in (0, 1, 2)]
@@ -107,7 +116,7 @@ def test_graph_replays_match_eager(name, pr, dtype, path, monkeypatch):
         assert mdcn.mdcn_forward_check(op, code, dims, ws.data_ptr(), ws.numel(),
                                        stream) == mdcn.MDCN_OK
 
-    if name in ("tiny", "gather_gemm", "depthwise"):
+    if name in ("tiny", "gather_gemm", "depthwise", "depthwise_persistent"):
         inp = inputs[2]
         ref = oracle.forward(inp["x"], inp["offset"], inp["mask"], inp["weight"], inp["bias"],
                              **pr.attrs())

@@ -374,6 +374,7 @@ GRID_CASES = [
     ("strided_grouped_n2_c128_co256_128x128", "bf16", mdcn.MDCN_PATH_AUTO, "fused"),
     ("ocdnet_n4_c256_160x160", "f16", mdcn.MDCN_PATH_GATHER_GEMM, "gather_gemm"),
     ("ocdnet_n4_c256_160x160", "f32", mdcn.MDCN_PATH_GATHER_GEMM, "gather_gemm"),
+    ("depthwise_n8_c256_96x96", "f32", mdcn.MDCN_PATH_AUTO, "depthwise_direct"),
 ]
 
 
@@ -404,8 +405,10 @@ def test_workload_grid_exact(name, dtype, path, plan):
     ulp = ulp_of(ref, dtype)
     assert (err <= ulp).all(), (name, dtype, plan, float((err / ulp).max()),
                                 int((err > ulp).sum()))
-    # and the reference itself is not trivial: many distinct, mostly nonzero values
-    assert np.count_nonzero(ref) > 0.9 * ref.size and np.unique(ref).size > 1000
+    # and the reference itself is not trivial: many distinct, mostly nonzero
+    # values (a depthwise output sums only 9 grid products: fewer distinct ones)
+    distinct = 500 if plan == "depthwise_direct" else 1000
+    assert np.count_nonzero(ref) > 0.9 * ref.size and np.unique(ref).size > distinct
 
 
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
