@@ -154,6 +154,9 @@ class Op:
     def __init__(self, handle: int, attrs: dict):
         self.handle = handle
         self.attrs = attrs
+        # forward()'s per-shape set-up: (dtype code, shapes) -> (ctypes dims,
+        # output shape), so that repeated calls skip it
+        self.calls = {}
 
     def __del__(self):
         h, self.handle = getattr(self, "handle", None), None
@@ -291,12 +294,18 @@ class Trace:
 
 # ---------------------------------------------------------------- tensor convenience
 
+_DTYPE_CODES = {}
+
+
 def dtype_code(torch_dtype) -> int:
-    import torch
-    codes = {torch.float32: MDCN_F32, torch.float16: MDCN_F16, torch.bfloat16: MDCN_BF16}
-    if torch_dtype not in codes:
+    if not _DTYPE_CODES:
+        import torch
+        _DTYPE_CODES.update({torch.float32: MDCN_F32, torch.float16: MDCN_F16,
+                             torch.bfloat16: MDCN_BF16})
+    code = _DTYPE_CODES.get(torch_dtype)
+    if code is None:
         raise MdcnError(MDCN_E_DTYPE, "dtype_code")
-    return codes[torch_dtype]
+    return code
 
 
 def dims_of(x, offset, mask, weight) -> list:
@@ -319,11 +328,13 @@ def _alloc_stream(stream, device, allocates):
     microseconds per call)."""
     import contextlib
     import torch
+    if stream is not None and not allocates:
+        return int(stream), contextlib.nullcontext()
     current = torch.cuda.current_stream(device).cuda_stream
     if stream is None:
         return current, contextlib.nullcontext()
     stream = int(stream)
-    if not allocates or stream == current:
+    if stream == current:
         return stream, contextlib.nullcontext()
     if stream == 0:
         return 0, torch.cuda.stream(torch.cuda.default_stream(device))
@@ -343,8 +354,15 @@ def forward(op: Op, x, offset, mask, weight, bias=None, out=None, workspace=None
             raise MdcnError(MDCN_E_SHAPE if t.is_cuda else MDCN_E_NULL, "forward: tensors must "
                             "be contiguous device tensors of one dtype")
     code = dtype_code(x.dtype)
-    dims = dims_of(x, offset, mask, weight)
-    shape = mdcn_output_shape(op, dims)
+    key = (code, x.shape, offset.shape, mask.shape, weight.shape)
+    call = op.calls.get(key)
+    if call is None:
+        dims = dims_of(x, offset, mask, weight)
+        call = (dims, _arr(ctypes.c_int64, dims), mdcn_output_shape(op, dims))
+        if len(op.calls) >= 64:
+            op.calls.clear()
+        op.calls[key] = call
+    dims, dims_c, shape = call
     stream, ctx = _alloc_stream(stream, x.device, out is None or workspace is None)
     with ctx:
         if out is None:
@@ -354,10 +372,13 @@ def forward(op: Op, x, offset, mask, weight, bias=None, out=None, workspace=None
         if workspace is None:
             nbytes, _ = mdcn_workspace_bytes(op, code, dims)
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-        st = mdcn_forward(op, code, dims, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
-                          weight.data_ptr(), bias.data_ptr() if bias is not None else 0,
-                          int(bias.numel()) if bias is not None else 0, out.data_ptr(),
-                          workspace.data_ptr(), workspace.numel(), stream, trace)
+        args = (op.handle, code, dims_c, x.data_ptr(), offset.data_ptr(), mask.data_ptr(),
+                weight.data_ptr(), bias.data_ptr() if bias is not None else None,
+                int(bias.numel()) if bias is not None else 0, out.data_ptr(),
+                workspace.data_ptr() or None, workspace.numel(), stream or None)
+        lib = _lib or library()
+        st = (lib.mdcn_forward(*args) if trace is None
+              else lib.mdcn_forward_traced(*args, trace.handle))
         _check(st, "mdcn_forward")
         if check:
             _check(mdcn_forward_check(op, code, dims, workspace.data_ptr(), workspace.numel(),
