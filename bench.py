@@ -71,7 +71,7 @@ MEASURED_TRAFFIC = {
     ("depthwise_direct", "depthwise_n8_c256_96x96", "f32"): {
         "bytes": (47360 * 2 + 73728) * 1024,
         "sources": ('depthwise.hip', 'device_common.h'),
-        "sha": "8dacda147d54f0c4",
+        "sha": "bc9149a98a87a55d",
     },
 }
 

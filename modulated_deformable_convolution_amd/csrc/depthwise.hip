@@ -402,19 +402,18 @@ __global__ __launch_bounds__(kStagedThreads) void depthwise_staged_kernel(
 // Persistent kernel for the common depthwise case: 3x3 taps and one output
 // per input channel, at most 4 channels per staged entry.  A workgroup takes
 // a run of consecutive channel blocks (of one image, where the run allows)
-// and keeps its LDS plane busy: 8 waves compute one block while 8 loader
+// and keeps its LDS plane busy: 8 waves compute one block while 4 loader
 // waves read the next block's plane into their registers (kPersLoadBytes per
 // loader thread), so that after the first block the HBM reads of x overlap
 // the LDS-bound sampling; between blocks the loaders write the plane's
 // interior (the zero ring stays).
 //
-// Compute waves run one pixel per thread at a time and keep two taps of
-// corner reads in flight ahead of the tap being blended (three sample slots;
-// nine taps per pixel keep the slots' rotation aligned across pixels).  The
-// tap weights live in registers, not in LDS: a broadcast LDS read still
-// returns a whole wave's worth of data.  Geometry records roll as in the
-// staged kernel: a tap's record of the pixel 512 further on is loaded as soon
-// as the tap's sample has been issued.
+// Compute waves take groups of 64 pixels (one per lane) from a counter in
+// LDS, so that waves slowed by LDS contention take fewer; the geometry
+// records of a wave's next group are loaded tap by tap as the current
+// group's records are used, and tap k+1's corner reads go out before tap
+// k's blend.  The tap weights and the bias live in scalar registers, not in
+// LDS: a broadcast LDS read still returns a whole wave's worth of data.
 constexpr int kPersCompute = 512;
 constexpr int kPersLoad = 256;
 constexpr int kPersThreads = kPersCompute + kPersLoad;
