@@ -55,52 +55,185 @@ __global__ __launch_bounds__(256) void to_nhwc_kernel(const T *__restrict__ x, T
     transpose_tile<T, BLK>(x, xt, C, HW, blockIdx.x, blockIdx.y, blockIdx.z, tile);
 }
 
-// The same transpose with 16-byte global accesses on both sides (pixels
-// along the load, channels along the store); requires C and H*W to be
-// multiples of the vector width (and, for blocks, 8 channels per vector).
-template <typename T, bool BLK>
-__device__ __forceinline__ void transpose_tile_vec(const T *__restrict__ x, T *__restrict__ xt,
-                                                   int C, int HW, int bx, int by, int bz,
-                                                   T (*tile)[kTile + 1])
+// The same transpose without LDS, one wave per unit of eight 16-byte
+// chunks a lane.  A chunk holds EV = 16/sizeof(T) elements; the EV lanes
+// whose lane numbers differ only in bits {0, 4, 5} (EV = 8) or {4, 5}
+// (EV = 4) hold the rows of an EV x EV tile (row i = those bits in that
+// order), and exchanging each of those lane bits with one bit of the
+// position inside the chunk (bit 0 with the 16-bit half, by a quad swap and
+// a byte permute; bits 4 and 5 with the dword index, by the row and
+// half-wave swaps) leaves lane j of the group with column j.  Loads read
+// channel rows (x is [C][HW] per image), stores write pixel rows.
+template <int EV>
+__device__ __forceinline__ uint4 transpose_lanes(uint4 v, int lane)
 {
-    constexpr int V = 16 / sizeof(T);
-    constexpr int NV = kTile / V;                      // vectors per tile row
-    const int p0 = bx * kTile;
-    const int c0 = by * kTile;
-    const size_t img = size_t(bz) * size_t(C) * size_t(HW);
-    const T *src = x + img;
-    T *dst = xt + img;
-    for (int v = threadIdx.x; v < kTile * NV; v += 256) {
-        const int r = v / NV, pv = (v % NV) * V;
-        const int c = c0 + r, p = p0 + pv;
-        Vec16<T> val;
-        val.raw = make_uint4(0u, 0u, 0u, 0u);
-        if (c < C && p < HW)
-            val = load16(src + size_t(c) * HW + p);
+    uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (EV == 8) {
+        // lane bit 0 <-> 16-bit half: an even lane keeps its low halves and
+        // takes its partner's low halves as high halves, an odd lane the
+        // reverse
+        const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
 #pragma unroll
-        for (int e = 0; e < V; ++e)
-            tile[r][pv + e] = val.e[e];
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t q = uint32_t(__builtin_amdgcn_update_dpp(
+                0, int(d[k]), 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF, false));
+            d[k] = __builtin_amdgcn_perm(q, d[k], sel);
+        }
+    }
+    // lane bit 4 <-> dword bit 0 (odd rows of 16 lanes of the first operand
+    // swapped with even rows of the second)
+#pragma unroll
+    for (int k = 0; k < 4; k += 2) {
+        const auto r = __builtin_amdgcn_permlane16_swap(d[k], d[k + 1], false, false);
+        d[k] = r[0];
+        d[k + 1] = r[1];
+    }
+    // lane bit 5 <-> dword bit 1 (upper half-wave of the first operand
+    // swapped with the lower half-wave of the second)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const auto r = __builtin_amdgcn_permlane32_swap(d[k], d[k + 2], false, false);
+        d[k] = r[0];
+        d[k + 2] = r[1];
+    }
+    return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// 8-channel blocks (16-bit elements): unit u (one wave) moves one block x
+// 512 pixels.  Chunk t of lane group g holds the block's 8 channel rows at
+// pixels 512*pc + 8*(8*t + g) .. +7, so a load instruction reads 8 whole
+// 128-byte lines of x and, after the transpose, a store instruction writes
+// 1 KiB of contiguous block plane.  Units are ordered (image, block, pixel
+// chunk).  Requires C and HW to be multiples of 8 and 16-byte aligned x
+// and xt.
+template <typename T>
+__device__ __forceinline__ void transpose_blocks_wave(const T *__restrict__ x,
+                                                      T *__restrict__ xt, int C, int HW,
+                                                      uint32_t u)
+{
+    static_assert(sizeof(T) == 2, "8-channel blocks of 16 bytes take 16-bit elements");
+    constexpr int R = 8;                        // chunks per lane
+    const int lane = int(threadIdx.x) & 63;
+    const int i = (lane & 1) | ((lane >> 3) & 6);   // row (load) / column (store) in the group
+    const int g = (lane >> 1) & 7;                  // lane group
+    const uint32_t npc = uint32_t(HW + 511) / 512u, cbs = uint32_t(C) / 8u;
+    const uint32_t pc = u % npc, r = u / npc;
+    const uint32_t cb = r % cbs, n = r / cbs;
+    const T *src = x + (size_t(n) * C + 8 * cb + i) * size_t(HW);
+    T *dst = xt + (size_t(n) * cbs + cb) * size_t(HW) * 8;
+    uint4 v[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int po = int(pc) * 512 + (t * 8 + g) * 8;
+        v[t] = make_uint4(0u, 0u, 0u, 0u);
+        if (po < HW)
+            v[t] = *reinterpret_cast<const uint4 *>(src + po);
+    }
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int po = int(pc) * 512 + (t * 8 + g) * 8;
+        const uint4 w = transpose_lanes<8>(v[t], lane);
+        if (po < HW)
+            *reinterpret_cast<uint4 *>(dst + size_t(po + i) * 8) = w;
+    }
+}
+
+// NHWC: one workgroup (4 waves) per tile of 64 channels x 64 pixels, tiles
+// ordered (image, pixel chunk, channel chunk).  Each wave loads Q/4 chunk
+// rows (EV channels x 64 pixels: EV whole lines of x per instruction),
+// transposes them across lanes, and puts each pixel's 16-byte chunk into
+// LDS (row = pixel, Q = 64/EV chunks of 16 bytes, XOR-swizzled so that
+// neither side conflicts); then each wave stores 64/Q pixels x 64 channels
+// per instruction (contiguous 16*Q bytes per pixel).  lds holds 64*Q
+// chunks.  Requires C and HW to be multiples of EV and 16-byte aligned x
+// and xt.
+template <typename T>
+__device__ __forceinline__ void transpose_nhwc_tile(const T *__restrict__ x, T *__restrict__ xt,
+                                                    int C, int HW, uint32_t tile, uint4 *lds)
+{
+    constexpr int EV = 16 / int(sizeof(T));
+    constexpr int Q = 64 / EV;                  // chunks per pixel row of the tile
+    constexpr int PW = Q / 4;                   // chunk rows per wave
+    const int lane = int(threadIdx.x) & 63;
+    const int wave = int(threadIdx.x) >> 6;
+    const int i = EV == 8 ? ((lane & 1) | ((lane >> 3) & 6)) : ((lane >> 4) & 3);
+    const int g = EV == 8 ? ((lane >> 1) & 7) : (lane & 15);
+    const uint32_t ncc = uint32_t(C + 63) / 64u, npc = uint32_t(HW + 63) / 64u;
+    const uint32_t cc = tile % ncc, r = tile / ncc;
+    const uint32_t pc = r % npc, n = r / npc;
+    const int p0 = int(pc) * 64, c0 = int(cc) * 64;
+    auto swz = [](int pl) { return ((pl / EV) ^ (EV == 8 ? pl : 0)) & (Q - 1); };
+    const int po = p0 + EV * g;                 // first pixel of the lane group
+    uint4 v[PW];
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+        const int c = c0 + EV * (wave * PW + k);
+        v[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (po < HW && c < C)
+            v[k] = *reinterpret_cast<const uint4 *>(x + (size_t(n) * C + c + i) * size_t(HW) + po);
+    }
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+        const int o = wave * PW + k;
+        const int pl = EV * g + i;              // the lane's pixel after the transpose
+        lds[pl * Q + (o ^ swz(pl))] = transpose_lanes<EV>(v[k], lane);
     }
     __syncthreads();
-    for (int v = threadIdx.x; v < kTile * NV; v += 256) {
-        const int r = v / NV, cv = (v % NV) * V;
-        const int p = p0 + r, c = c0 + cv;
-        if (p < HW && c < C) {
-            Vec16<T> val;
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                val.e[e] = tile[cv + e][r];
-            store16(dst + dst_index<BLK>(c, p, C, HW), val);
+    for (int k = 0; k < PW; ++k) {
+        const int pl = (wave * PW + k) * (64 / Q) + lane / Q;
+        const int o = lane % Q;
+        const uint4 w = lds[pl * Q + (o ^ swz(pl))];
+        const int p = p0 + pl, c = c0 + EV * o;
+        if (p < HW && c < C)
+            *reinterpret_cast<uint4 *>(xt + (size_t(n) * HW + p) * size_t(C) + c) = w;
+    }
+}
+
+// Workgroups of the register transposes for cnt images: four block units,
+// or one NHWC tile, a workgroup.
+template <typename T, bool BLK>
+inline int64_t transpose_groups(int64_t C, int64_t HW, int64_t cnt)
+{
+    if constexpr (BLK)
+        return (cnt * (C / 8) * ((HW + 511) / 512) + 3) / 4;
+    return cnt * ((HW + 63) / 64) * ((C + 63) / 64);
+}
+
+// Whether the register transposes apply.
+template <typename T, bool BLK>
+inline bool transpose_regs_ok(int64_t C, int64_t HW, const void *x, const void *xt)
+{
+    constexpr int64_t EV = 16 / int64_t(sizeof(T));
+    return (!BLK || EV == 8) && C % EV == 0 && HW % EV == 0 &&
+           reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(xt) % 16 == 0;
+}
+
+// Workgroup b of the register transpose of images [0, cnt): `units` block
+// units (BLK) or NHWC tiles in all.
+template <typename T, bool BLK>
+__device__ __forceinline__ void transpose_group(const T *__restrict__ x, T *__restrict__ xt,
+                                                int C, int HW, uint32_t b, uint32_t units,
+                                                uint4 *lds)
+{
+    if constexpr (BLK) {
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t u = b * 4u + (threadIdx.x >> 6);
+            if (u < units)
+                transpose_blocks_wave<T>(x, xt, C, HW, u);
         }
+    } else {
+        transpose_nhwc_tile<T>(x, xt, C, HW, b, lds);
     }
 }
 
 template <typename T, bool BLK>
-__global__ __launch_bounds__(256) void to_nhwc_vec_kernel(const T *__restrict__ x,
-                                                          T *__restrict__ xt, int C, int HW)
+__global__ __launch_bounds__(256) void to_nhwc_regs_kernel(const T *__restrict__ x,
+                                                           T *__restrict__ xt, int C, int HW,
+                                                           uint32_t units)
 {
-    __shared__ T tile[kTile][kTile + 1];
-    transpose_tile_vec<T, BLK>(x, xt, C, HW, blockIdx.x, blockIdx.y, blockIdx.z, tile);
+    __shared__ uint4 lds[BLK ? 1 : 64 * 64 * sizeof(T) / 16];
+    transpose_group<T, BLK>(x, xt, C, HW, blockIdx.x, units, lds);
 }
 
 template <typename T>
@@ -211,7 +344,8 @@ __device__ __forceinline__ void quantize_row(const T *__restrict__ w, e4m3_t *__
 
 // Both set-up jobs of a forward in one launch (for small problems the
 // launches cost more than the work): the first `nt` workgroups transpose
-// x (tile b -> (b % gx, b / gx % gy, b / (gx*gy))), the rest repack the
+// x (VEC: register transpose units 4b .. 4b+3, one a wave; otherwise LDS
+// tile b -> (b % gx, b / gx % gy, b / (gx*gy))), the rest repack the
 // weight (PK 1: [G][Mg][Kp] tap-major; PK 2: the window path's step-major
 // planes, and its hand-over flags cleared; PK 3: the FP8 path's E4M3 rows
 // and scales, one workgroup per row).
@@ -223,6 +357,7 @@ struct PrepArgs {
     uint32_t *flags;
     float *wscale;
     int C, HW, gx, gy, nt;
+    uint32_t units;
     int total, Kp, Kg, Cg, K, Mg, S, nflags;
 };
 
@@ -232,13 +367,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
     __shared__ __attribute__((aligned(16))) T tile[kTile][kTile + 1];
     const int b = int(blockIdx.x);
     if (b < a.nt) {
-        const int bx = b % a.gx, by = (b / a.gx) % a.gy, bz = b / (a.gx * a.gy);
-        if constexpr (VEC)
-            transpose_tile_vec<T, BLK>(static_cast<const T *>(a.x), static_cast<T *>(a.xt), a.C,
-                                       a.HW, bx, by, bz, tile);
-        else
+        if constexpr (VEC) {
+            transpose_group<T, BLK>(static_cast<const T *>(a.x), static_cast<T *>(a.xt), a.C,
+                                    a.HW, uint32_t(b), a.units,
+                                    reinterpret_cast<uint4 *>(&tile[0][0]));
+        } else {
+            const int bx = b % a.gx, by = (b / a.gx) % a.gy, bz = b / (a.gx * a.gy);
             transpose_tile<T, BLK>(static_cast<const T *>(a.x), static_cast<T *>(a.xt), a.C,
                                    a.HW, bx, by, bz, tile);
+        }
         return;
     }
     if constexpr (PK == 3) {
@@ -259,21 +396,33 @@ template <typename T, bool BLK>
 hipError_t to_nhwc_t(const Problem &p, int64_t cnt, const void *x, void *xt, hipStream_t s)
 {
     const int HW = int(p.H * p.W);
+    const size_t img = size_t(p.C) * size_t(HW);
+    if (transpose_regs_ok<T, BLK>(p.C, HW, x, xt)) {
+        // images per launch: at most 2^29 workgroups
+        const int64_t per = transpose_groups<T, BLK>(p.C, HW, 1);
+        const int64_t step = std::max<int64_t>(1, (int64_t(1) << 29) / std::max<int64_t>(per, 1));
+        for (int64_t n0 = 0; n0 < cnt; n0 += step) {
+            const int64_t m = std::min(step, cnt - n0);
+            const int64_t units = BLK ? m * (p.C / 8) * ((HW + 511) / 512) : 0;
+            hipLaunchKernelGGL((to_nhwc_regs_kernel<T, BLK>),
+                               dim3(unsigned(transpose_groups<T, BLK>(p.C, HW, m))), dim3(256), 0,
+                               s, static_cast<const T *>(x) + size_t(n0) * img,
+                               static_cast<T *>(xt) + size_t(n0) * img, int(p.C), HW,
+                               uint32_t(units));
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
     dim3 grid((HW + kTile - 1) / kTile, unsigned((p.C + kTile - 1) / kTile), 1);
     // The z dimension is limited to 65535; walk larger batches in slices.
     for (int64_t n0 = 0; n0 < cnt; n0 += 65535) {
         grid.z = unsigned(std::min<int64_t>(65535, cnt - n0));
-        const size_t off = size_t(n0) * size_t(p.C) * size_t(HW);
-        constexpr int V = 16 / sizeof(T);
-        if (p.C % V == 0 && HW % V == 0 && (!BLK || V == 8) &&
-            reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(xt) % 16 == 0)
-            hipLaunchKernelGGL((to_nhwc_vec_kernel<T, BLK>), grid, dim3(256), 0, s,
-                               static_cast<const T *>(x) + off, static_cast<T *>(xt) + off,
-                               int(p.C), HW);
-        else
-            hipLaunchKernelGGL((to_nhwc_kernel<T, BLK>), grid, dim3(256), 0, s,
-                               static_cast<const T *>(x) + off, static_cast<T *>(xt) + off,
-                               int(p.C), HW);
+        const size_t off = size_t(n0) * img;
+        hipLaunchKernelGGL((to_nhwc_kernel<T, BLK>), grid, dim3(256), 0, s,
+                           static_cast<const T *>(x) + off, static_cast<T *>(xt) + off,
+                           int(p.C), HW);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -377,15 +526,14 @@ hipError_t prep_t(const Problem &p, const Plan &plan, int64_t cnt, const void *x
         a.nflags = flags ? nflags : 0;
         npack = std::max(a.total, a.nflags);
     }
-    const int64_t nt = int64_t(a.gx) * a.gy * cnt;
+    const bool vec = transpose_regs_ok<T, BLK>(p.C, HW, x, xt);
+    const int64_t units = vec ? (BLK ? cnt * (p.C / 8) * ((HW + 511) / 512) : 0) : 0;
+    const int64_t nt = vec ? transpose_groups<T, BLK>(p.C, HW, cnt) : int64_t(a.gx) * a.gy * cnt;
     const int64_t blocks = nt + (npack + 255) / 256;
     if (blocks > 0x7fffffffll)
         return hipErrorInvalidValue;
     a.nt = int(nt);
-    constexpr int V = 16 / sizeof(T);
-    const bool vec = p.C % V == 0 && HW % V == 0 && (!BLK || V == 8) &&
-                     reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
-                     reinterpret_cast<uintptr_t>(xt) % 16 == 0;
+    a.units = uint32_t(units);
     if (vec)
         hipLaunchKernelGGL((prep_kernel<T, BLK, true, PK>), dim3(unsigned(blocks)), dim3(256), 0,
                            s, a);
