@@ -126,6 +126,12 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
         if name == "gemm_bias":
             return dict(bytes=cnt * (col_img + out_img) + pr.Co * Kp * e + bias_bytes,
                         flops=2 * cnt * pr.Co * Kg * P)
+        if name == "fused_one_launch":
+            # the whole forward: x (NCHW), offsets, masks and the weight read
+            # once, output written once (the NHWC copy and the packed weight
+            # it makes on the way are not counted)
+            return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + w_bytes + bias_bytes,
+                        flops=2 * cnt * pr.Co * Kg * P)
         if name in ("fused_gather_gemm", "window_gather_gemm"):
             # x (NHWC copy), offsets and masks read once, output written once
             return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + pr.Co * Kp * e
@@ -314,7 +320,8 @@ def main(argv=None) -> int:
         launches_per_step = count / args.steps
         cnt = (pr.N / max(1, launches_per_step)
                if name in ("direct", "to_nhwc", "to_channel_blocks", "deform_gather", "gemm_bias",
-                           "fused_gather_gemm", "window_gather_gemm", "depthwise_geometry",
+                           "fused_gather_gemm", "fused_one_launch", "window_gather_gemm",
+                           "depthwise_geometry",
                            "depthwise_direct", "deform_gather_fp8", "gemm_fp8_bias")
                else 0)
         m = model(name, cnt)
@@ -329,8 +336,8 @@ def main(argv=None) -> int:
     peak_tf = MFMA_PEAK_TFLOPS["fp8" if fp8 else dtype]
     t_hbm = dk["algo_bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = dk["algo_flops_per_launch"] / (peak_tf * 1e12)
-    uses_mfma = dominant in ("gemm_bias", "fused_gather_gemm", "window_gather_gemm",
-                             "gemm_fp8_bias")
+    uses_mfma = dominant in ("gemm_bias", "fused_gather_gemm", "fused_one_launch",
+                             "window_gather_gemm", "gemm_fp8_bias")
     if uses_mfma and t_mfma > t_hbm:
         roofline = dict(bound="mfma", achieved=round(dk["tflops"], 2), peak=peak_tf,
                         unit="TFLOP/s", frac=round(dk["tflops"] / peak_tf, 4), traffic=None)

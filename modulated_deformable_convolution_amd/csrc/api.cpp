@@ -80,6 +80,8 @@ struct Recorder {
                 return e;
         }
         hipError_t e = launch();
+        if (e == hipErrorNotSupported && slot >= 0 && slot == trace->count - 1)
+            trace->count--;                  // nothing was enqueued: no record
         if (e != hipSuccess)
             return e;
         if (slot >= 0)
@@ -191,6 +193,17 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     float *wscale = fp8 ? reinterpret_cast<float *>(ws + plan.wpack_off + plan.wscale_off) : nullptr;
     // The weight is repacked (and the window path's flags cleared) in the
     // same launch as the first chunk's x layout change.
+    if (plan.path == Path::Fused && plan.chunk >= p.N) {
+        // the whole batch in one launch when the grid fits the device
+        err = rec.run(mdcn::K_FUSED_ONE, [&] {
+            return mdcn::launch_fused_one(p, plan, p.N, x, weight, wpack, xt, offset, mask, bias,
+                                          out, stream);
+        });
+        if (err == hipSuccess)
+            return MDCN_OK;
+        if (err != hipErrorNotSupported)
+            return MDCN_E_LAUNCH;
+    }
     for (int64_t n0 = 0; n0 < p.N; n0 += plan.chunk) {
         const int64_t cnt = std::min<int64_t>(plan.chunk, p.N - n0);
         const char *xc = static_cast<const char *>(x) + size_t(n0) * x_img;
@@ -772,6 +785,7 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_BWD_SAMPLE: return "bwd_sample";
     case mdcn::K_BWD_WEIGHT_OUT: return "bwd_weight_out";
     case mdcn::K_BWD_TO_NCHW: return "bwd_to_nchw";
+    case mdcn::K_FUSED_ONE: return "fused_one_launch";
     }
     return "?";
 }

@@ -32,8 +32,14 @@
 // has two steps to land.  One consumer and one producer wave share each SIMD,
 // so MFMA and VALU work overlap; one barrier per step separates the two LDS
 // stages.
+#include <atomic>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+
 #include "launch.h"
 #include "mfma_common.h"
+#include "transpose.h"
 
 namespace mdcn {
 
@@ -54,6 +60,40 @@ struct FusedArgs {
     uint32_t chunk_bytes;        // bytes of the chunk's NHWC images (< 2^31)
     int steps;                   // K steps: Kg / (128 / sizeof(T))
 };
+
+// The one-launch forward: the workgroups first move x to NHWC and repack
+// the weight themselves (each its share), then wait for one another at a
+// bounded grid barrier before the GEMM.  Each workgroup announces that its
+// share is stored by writing this launch's ticket (a value no other launch
+// uses) into its own flag of a slot; it proceeds once every flag of the
+// launch holds the ticket.  A workgroup that gives up waiting (some
+// workgroup of the grid did not get a CU in time) moves all of x and the
+// whole weight itself -- the same values the others store -- so the result
+// never depends on the wait.
+constexpr int kOneSlots = 64;                // flag slots (by workspace address)
+constexpr int kOneMaxBlocks = 512;           // workgroups of a one-launch grid
+constexpr uint32_t kOneSpinLimit = 1u << 15; // polls of the flags before giving up
+__device__ uint64_t g_one_flags[kOneSlots * kOneMaxBlocks];
+
+struct OneArgs {
+    const void *x;               // the chunk's x, [cnt][C][H][W]
+    const void *w;               // weight [Co][Cg][kh][kw]
+    void *xt;                    // NHWC copy the GEMM reads (written here)
+    void *wp;                    // packed weight the GEMM reads (written here)
+    uint64_t *flags;             // the slot's kOneMaxBlocks flags
+    uint64_t ticket;             // this launch's flag value
+    uint32_t spin_limit;         // polls before a workgroup moves everything itself
+    int vec;                     // x moves in 16-byte chunks (C, HW multiples of 16/elem)
+    int HW, cnt;                 // pixels of an image, images of the chunk
+    int total, Kg;               // packed weight elements (Co x Kp), Cg x K
+};
+
+// Cache policy of the set-up's stores and of the flags: device scope (SC1 on
+// gfx950): written through to where every XCD sees them.
+constexpr int kDevScopeAux = 16;
+// LDS of one group of 256 threads in the set-up (the larger of the two tile
+// transposes, 16-byte aligned)
+constexpr int kOneLdsBytes = 64 * 65 * 4 + 64;
 
 // Buffer resource over `bytes` bytes at `base`, built from scalar copies so
 // that it provably lives in scalar registers.
@@ -155,10 +195,188 @@ __device__ __forceinline__ void build_geo_table(char *tab, const FusedArgs &a,
     }
 }
 
-template <typename T, int BM, int BN, int CWM, int CWN, int PW>
+// The one-launch set-up: NHWC tiles of x (256 threads a tile, one LDS
+// buffer of kOneLdsBytes per group of 256 threads at the start of the
+// stages) and packed weight elements ([Co][Kp], tap-major k*Cg + c', zero
+// past Kg), stored with device scope.  A workgroup's share is a contiguous
+// range of each, by its index in the grid.
+struct OneRange {
+    uint32_t lo, hi;             // NHWC tiles
+    uint32_t plo, phi;           // packed weight elements
+};
+
+__device__ __forceinline__ OneRange one_range(const FusedArgs &a, const OneArgs &o, bool all)
+{
+    const uint64_t G = gridDim.x, b = blockIdx.x;
+    const uint32_t TT = nhwc_tiles(a.C, o.HW, o.cnt), tot = uint32_t(o.total);
+    if (all)
+        return {0u, TT, 0u, tot};
+    return {uint32_t(b * TT / G), uint32_t((b + 1) * TT / G), uint32_t(b * tot / G),
+            uint32_t((b + 1) * tot / G)};
+}
+
+template <typename T>
+__device__ __forceinline__ T one_weight(const FusedArgs &a, const OneArgs &o, uint32_t e)
+{
+    const int kk = int(e % uint32_t(a.Kp));
+    const int co = int(e / uint32_t(a.Kp));
+    if (kk >= o.Kg)
+        return T(0);
+    const int k = kk / a.Cg;
+    const int cl = kk - k * a.Cg;
+    return static_cast<const T *>(o.w)[(size_t(co) * a.Cg + cl) * a.K + k];
+}
+
+template <typename T>
+__device__ __forceinline__ void store_dev(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, T v)
+{
+    if constexpr (sizeof(T) == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, byte_off, 0,
+                                              kDevScopeAux);
+    else
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0,
+                                              kDevScopeAux);
+}
+
+// Tiles [from, rg.hi) and weight elements [pfrom, rg.phi) (this thread's
+// share of them), one round of NT/256 tiles at a time.  Every thread of the
+// workgroup calls it (it has barriers).  The barriers order LDS only: the
+// device-scope stores stay in flight until the wait before the grid barrier
+// (a full __syncthreads would wait for each round's stores to be written
+// through, about a microsecond and a half each).
+template <typename T, int NT>
+__device__ __forceinline__ void one_setup_rest(char *smem, const FusedArgs &a, const OneArgs &o,
+                                               int tid, uint32_t from, uint32_t hi,
+                                               uint32_t pfrom, uint32_t phi)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NQ = NT / 256;
+    static_assert(NT % 256 == 0, "whole groups of 256 threads");
+    const int q = tid >> 8, t = tid & 255;
+    uint4 *lds = reinterpret_cast<uint4 *>(smem + q * kOneLdsBytes);
+    const T *x = static_cast<const T *>(o.x);
+    const __amdgpu_buffer_rsrc_t rxt = scalar_rsrc(o.xt, a.chunk_bytes);
+    for (uint32_t base = from; base < hi; base += NQ) {
+        const uint32_t tile = base + uint32_t(q);
+        const bool ok = tile < hi;
+        if (o.vec) {
+            NhwcTile<T> tl;
+            if (ok) {
+                tl.load(x, a.C, o.HW, tile, t);
+                tl.put(lds, t);
+            }
+            lds_barrier();
+            if (ok)
+                tl.take(lds, a.C, o.HW, t, [&](const uint4 &v, size_t off) {
+                    const u32x4 d = {v.x, v.y, v.z, v.w};
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rxt, uint32_t(off * sizeof(T)), 0,
+                                                           kDevScopeAux);
+                });
+        } else {
+            NhwcTileScalar<T> tl;
+            if (ok) {
+                tl.load(x, a.C, o.HW, tile, t);
+                tl.put(reinterpret_cast<T *>(lds), t);
+            }
+            lds_barrier();
+            if (ok)
+                tl.take(reinterpret_cast<const T *>(lds), a.C, o.HW, t,
+                        [&](const T &v, size_t off) {
+                            store_dev(rxt, uint32_t(off * sizeof(T)), v);
+                        });
+        }
+        lds_barrier();
+    }
+    const __amdgpu_buffer_rsrc_t rwp = scalar_rsrc(o.wp, uint32_t(o.total) * uint32_t(sizeof(T)));
+    for (uint32_t e = pfrom + uint32_t(tid); e < phi; e += NT)
+        store_dev(rwp, e * uint32_t(sizeof(T)), one_weight<T>(a, o, e));
+}
+
+// The first loads of the workgroup's share, issued before the geometry table
+// is built so that their latency overlaps it (16-byte tiles only): the
+// first R rounds of tiles and P weight elements a thread.
+template <typename T, int NT>
+struct OnePre {
+    static constexpr int R = 2, P = 2;
+    NhwcTile<T> tl[R];
+    T wv[P];
+};
+
+template <typename T, int NT>
+__device__ __forceinline__ void one_setup_begin(OnePre<T, NT> &pre, const FusedArgs &a,
+                                                const OneArgs &o, int tid)
+{
+    if (!o.vec)
+        return;
+    constexpr int NQ = NT / 256;
+    const OneRange rg = one_range(a, o, false);
+    const int q = tid >> 8, t = tid & 255;
+#pragma unroll
+    for (int r = 0; r < OnePre<T, NT>::R; ++r) {
+        const uint32_t tile = rg.lo + uint32_t(r * NQ + q);
+        if (tile < rg.hi)
+            pre.tl[r].load(static_cast<const T *>(o.x), a.C, o.HW, tile, t);
+    }
+#pragma unroll
+    for (int j = 0; j < OnePre<T, NT>::P; ++j) {
+        const uint32_t e = rg.plo + uint32_t(tid + j * NT);
+        pre.wv[j] = e < rg.phi ? one_weight<T>(a, o, e) : T(0);
+    }
+}
+
+// The rest of the workgroup's share: the preloaded rounds transposed and
+// stored, then whatever they did not cover.
+template <typename T, int NT>
+__device__ __forceinline__ void one_setup_end(const OnePre<T, NT> &pre, char *smem,
+                                              const FusedArgs &a, const OneArgs &o, int tid)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int NQ = NT / 256;
+    const OneRange rg = one_range(a, o, false);
+    if (!o.vec) {
+        one_setup_rest<T, NT>(smem, a, o, tid, rg.lo, rg.hi, rg.plo, rg.phi);
+        return;
+    }
+    const int q = tid >> 8, t = tid & 255;
+    uint4 *lds = reinterpret_cast<uint4 *>(smem + q * kOneLdsBytes);
+    const __amdgpu_buffer_rsrc_t rxt = scalar_rsrc(o.xt, a.chunk_bytes);
+    // The preloaded values landed while the table was built.  Waiting for
+    // them here, explicitly, lets the compiler drop its own waits on them
+    // below, which would otherwise also wait for the stores issued in
+    // between (loads and stores share one counter).
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
+#pragma unroll
+    for (int r = 0; r < OnePre<T, NT>::R; ++r) {
+        const uint32_t base = rg.lo + uint32_t(r * NQ);
+        if (base >= rg.hi)
+            break;
+        const bool ok = base + uint32_t(q) < rg.hi;
+        if (ok)
+            pre.tl[r].put(lds, t);
+        lds_barrier();
+        if (ok)
+            pre.tl[r].take(lds, a.C, o.HW, t, [&](const uint4 &v, size_t off) {
+                const u32x4 d = {v.x, v.y, v.z, v.w};
+                __builtin_amdgcn_raw_buffer_store_b128(d, rxt, uint32_t(off * sizeof(T)), 0,
+                                                       kDevScopeAux);
+            });
+        lds_barrier();
+    }
+    const __amdgpu_buffer_rsrc_t rwp = scalar_rsrc(o.wp, uint32_t(o.total) * uint32_t(sizeof(T)));
+#pragma unroll
+    for (int j = 0; j < OnePre<T, NT>::P; ++j) {
+        const uint32_t e = rg.plo + uint32_t(tid + j * NT);
+        if (e < rg.phi)
+            store_dev(rwp, e * uint32_t(sizeof(T)), pre.wv[j]);
+    }
+    one_setup_rest<T, NT>(smem, a, o, tid, rg.lo + uint32_t(OnePre<T, NT>::R * NQ), rg.hi,
+                          rg.plo + uint32_t(OnePre<T, NT>::P * NT), rg.phi);
+}
+
+template <typename T, int BM, int BN, int CWM, int CWN, int PW, bool ONE>
 __global__ __launch_bounds__((CWM * CWN + PW) * 64) void fused_kernel(
-    const T *__restrict__ A, const T *__restrict__ xt, const T *__restrict__ off,
-    const T *__restrict__ msk, const T *__restrict__ bias, T *__restrict__ out, FusedArgs a)
+    const T *A, const T *xt, const T *__restrict__ off, const T *__restrict__ msk,
+    const T *__restrict__ bias, T *__restrict__ out, FusedArgs a, OneArgs o)
 {
     constexpr int STEP = 128;
     constexpr int NC = CWM * CWN;                // consumer (MFMA) waves
@@ -192,7 +410,52 @@ __global__ __launch_bounds__((CWM * CWN + PW) * 64) void fused_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+    OnePre<T, NT> pre;
+    if constexpr (ONE) {
+        static_assert(NT / 256 * kOneLdsBytes <= 2 * STAGE_BYTES, "set-up buffers in the stages");
+        one_setup_begin<T, NT>(pre, a, o, tid);
+    }
     build_geo_table<T, BN, NT>(tab, a, off, msk, qf, n0, tid);
+    if constexpr (ONE) {
+        one_setup_end<T, NT>(pre, smem, a, o, tid);
+        // grid barrier: every wave's device-scope stores are complete before
+        // the workgroup's flag is written; wave 0 polls the grid's flags
+        __shared__ uint32_t one_late;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave == 0) {
+            const uint32_t G = gridDim.x;
+            if (lane == 0)
+                __hip_atomic_store(o.flags + blockIdx.x, o.ticket, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            bool done = false;
+            for (uint32_t it = 0; it < o.spin_limit && !done; ++it) {
+                bool mine = true;
+                for (uint32_t j = uint32_t(lane); j < G; j += 64)
+                    mine = mine && __hip_atomic_load(o.flags + j, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) == o.ticket;
+                done = __all(mine);
+                if (!done)
+                    __builtin_amdgcn_s_sleep(1);
+            }
+            if (lane == 0)
+                one_late = done ? 0u : 1u;
+        }
+        __syncthreads();
+        if (one_late) {
+            const OneRange all = one_range(a, o, true);
+            one_setup_rest<T, NT>(smem, a, o, tid, all.lo, all.hi, all.plo, all.phi);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        // The NHWC copy and the packed weight are read through the caches
+        // from here on.  No cache can hold a stale line of them: the caches
+        // start the kernel without one, nothing reads them before this
+        // point, and the loads below are issued after every workgroup's
+        // device-scope stores are complete.  (An agent-scope acquire here
+        // would invalidate the whole L2 of the XCD once per workgroup, under
+        // the feet of the workgroups already in their GEMM.)
+    }
     __syncthreads();
 
     if (wave < NC) {
@@ -405,10 +668,10 @@ __global__ __launch_bounds__((CWM * CWN + PW) * 64) void fused_kernel(
     __syncthreads();                     // matches the consumers' barrier before the epilogue
 }
 
-template <typename T, int BM, int BN, int CWM, int CWN, int PW>
+template <typename T, int BM, int BN, int CWM, int CWN, int PW, bool ONE = false>
 hipError_t fused_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                      const void *xt, const void *offset, const void *mask, const void *bias,
-                     void *out, hipStream_t s)
+                     void *out, hipStream_t s, const OneArgs *one = nullptr)
 {
     FusedArgs a;
     a.Mg = int(p.Mg);
@@ -434,10 +697,13 @@ hipError_t fused_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void
     // The geometry table is the dynamic part of the LDS; the plan only picks
     // tiles whose stages and table fit.
     const size_t table = fused_table_bytes(p, BN);
-    const size_t stages = size_t(2) * (BM + BN) * 128;
+    // (the one-launch variant has a few more bytes of static LDS)
+    const size_t stages = size_t(2) * (BM + BN) * 128 + (ONE ? 256 : 0);
     if (stages + table > kLdsBytes)
+        return ONE ? hipErrorNotSupported : hipErrorInvalidValue;
+    if (ONE && (!one || blocks > uint64_t(kOneMaxBlocks)))
         return hipErrorInvalidValue;
-    auto kern = fused_kernel<T, BM, BN, CWM, CWN, PW>;
+    auto kern = fused_kernel<T, BM, BN, CWM, CWN, PW, ONE>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
         int(kLdsBytes - stages));
@@ -447,15 +713,26 @@ hipError_t fused_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void
                        static_cast<const T *>(wpack),
                        static_cast<const T *>(xt), static_cast<const T *>(offset),
                        static_cast<const T *>(mask), static_cast<const T *>(bias),
-                       static_cast<T *>(out), a);
+                       static_cast<T *>(out), a, one ? *one : OneArgs{});
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t fused_t(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                    const void *xt, const void *offset, const void *mask, const void *bias,
-                   void *out, hipStream_t s)
+                   void *out, hipStream_t s, const OneArgs *one = nullptr)
 {
+    if (one) {
+        // the one-launch variant exists for the 64-column tiles (the ones a
+        // grid of at most one workgroup per CU gets)
+        if (plan.fused_tile == FusedTile::M256_N64)
+            return fused_cfg<T, 256, 64, 4, 2, 4, true>(p, plan, cnt, wpack, xt, offset, mask,
+                                                         bias, out, s, one);
+        if (plan.fused_tile == FusedTile::M128_N64)
+            return fused_cfg<T, 128, 64, 2, 2, 4, true>(p, plan, cnt, wpack, xt, offset, mask,
+                                                         bias, out, s, one);
+        return hipErrorNotSupported;
+    }
     switch (plan.fused_tile) {
     // <BM, BN, consumer wave grid CWM x CWN, producer waves>: 16, 16, 12 and
     // 8 waves, i.e. 4, 4, 3 and 2 waves per SIMD (at most 128, 128, 168 and
@@ -472,7 +749,92 @@ hipError_t fused_t(const Problem &p, const Plan &plan, int64_t cnt, const void *
     return hipErrorInvalidValue;
 }
 
+// Device address of g_one_flags on the current device (asked once per device).
+uint64_t *one_flags_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    static std::mutex mu;
+    static std::map<int, uint64_t *> known;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = known.find(dev);
+    if (it == known.end()) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_one_flags)) != hipSuccess || ptr == nullptr)
+            return nullptr;
+        it = known.emplace(dev, static_cast<uint64_t *>(ptr)).first;
+    }
+    return it->second;
+}
+
 }  // namespace
+
+hipError_t launch_fused_one(const Problem &p, const Plan &plan, int64_t cnt, const void *x,
+                            const void *weight, void *wpack, void *xt, const void *offset,
+                            const void *mask, const void *bias, void *out, hipStream_t stream)
+{
+    // opt-in (MDCN_FUSED_ONE=1): measured on the strided/grouped bf16 stage
+    // (N=2, C=128, Co=256, 128x128, 256 workgroups), the two launches take
+    // 20.8 us and the one launch 23.0 us -- the NHWC copy written through to
+    // where every XCD sees it and the flag round trip take about 6 us after
+    // the last store is issued, more than the kernel boundary they replace
+    const char *env = std::getenv("MDCN_FUSED_ONE");
+    if (!env || std::atoi(env) != 1)
+        return hipErrorNotSupported;
+    if (plan.fused_tile != FusedTile::M128_N64 && plan.fused_tile != FusedTile::M256_N64)
+        return hipErrorNotSupported;
+    // a captured launch would replay with the same ticket: two launches there
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return hipErrorNotSupported;
+    // at most one workgroup per CU, so that the whole grid is resident
+    const int64_t bm = plan.fused_tile == FusedTile::M256_N64 ? 256 : 128;
+    const int64_t blocks = p.G * ((p.Mg + bm - 1) / bm) * ((cnt * p.P + 63) / 64);
+    if (blocks > std::min<int64_t>(device_cu_count(), kOneMaxBlocks))
+        return hipErrorNotSupported;
+    const int64_t ev = 16 / int64_t(p.elem);
+    const int64_t HW = p.H * p.W;
+    if (p.Co * plan.Kp * int64_t(p.elem) >= (int64_t(1) << 32))
+        return hipErrorNotSupported;
+    uint64_t *flags = one_flags_address();
+    if (!flags)
+        return hipErrorNotSupported;
+    static std::atomic<uint64_t> tickets{0};
+    // the slot by workspace address: launches that may overlap use different
+    // workspaces; two that share a slot anyway only wait until one gives up
+    const uint64_t h = (uint64_t(reinterpret_cast<uintptr_t>(xt)) >> 8) * 0x9E3779B97F4A7C15ull;
+    OneArgs o{};
+    o.x = x;
+    o.w = weight;
+    o.xt = xt;
+    o.wp = wpack;
+    o.flags = flags + size_t(h >> 58) * kOneMaxBlocks;
+    o.ticket = ++tickets;
+    o.spin_limit = kOneSpinLimit;
+    // MDCN_FUSED_ONE_SPIN=<polls> shortens the wait (tests force the
+    // fallback with 0)
+    if (const char *env = std::getenv("MDCN_FUSED_ONE_SPIN")) {
+        const long long v = std::atoll(env);
+        if (v >= 0 && v <= (long long)kOneSpinLimit)
+            o.spin_limit = uint32_t(v);
+    }
+    o.vec = p.C % ev == 0 && HW % ev == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+            reinterpret_cast<uintptr_t>(xt) % 16 == 0;
+    o.HW = int(HW);
+    o.cnt = int(cnt);
+    o.total = int(p.Co * plan.Kp);
+    o.Kg = int(p.Kg);
+    switch (p.dtype) {
+    case MDCN_F32:
+        return fused_t<float>(p, plan, cnt, wpack, xt, offset, mask, bias, out, stream, &o);
+    case MDCN_F16:
+        return fused_t<half_t>(p, plan, cnt, wpack, xt, offset, mask, bias, out, stream, &o);
+    case MDCN_BF16:
+        return fused_t<bf16_t>(p, plan, cnt, wpack, xt, offset, mask, bias, out, stream, &o);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_fused(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                         const void *xt, const void *offset, const void *mask, const void *bias,

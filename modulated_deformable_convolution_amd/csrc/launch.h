@@ -33,7 +33,8 @@ enum KernelId : int32_t {
     K_BWD_SAMPLE = 20,
     K_BWD_WEIGHT_OUT = 21,
     K_BWD_TO_NCHW = 22,
-    K_COUNT = 23
+    K_FUSED_ONE = 23,
+    K_COUNT = 24
 };
 
 // Compute units of the current device (cached per device; 1 if unknown).
@@ -102,6 +103,16 @@ hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const vo
                        const void *col, const void *bias, const float *wscale, void *out,
                        hipStream_t stream);
 
+// The fused forward of a whole chunk in one launch: the kernel below, whose
+// workgroups first move x (cnt images, NCHW) to the NHWC copy `xt` and repack
+// `weight` into `wpack` themselves, then meet at a bounded grid barrier.
+// Opt-in (MDCN_FUSED_ONE=1; slower than the two launches on gfx950, see
+// fused.hip).  hipErrorNotSupported (nothing enqueued) when it is not asked
+// for or the problem or the stream does not allow it: more workgroups than
+// CUs, a tile without the variant, or a capturing stream.
+hipError_t launch_fused_one(const Problem &p, const Plan &plan, int64_t cnt, const void *x,
+                            const void *weight, void *wpack, void *xt, const void *offset,
+                            const void *mask, const void *bias, void *out, hipStream_t stream);
 
 // Fused deformable gather + grouped GEMM + bias of cnt images:
 // out[n][g*Mg + m][pix] from the packed weight, NHWC x, offset and mask.

@@ -6,6 +6,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "transpose.h"
 
 namespace mdcn {
 
@@ -55,141 +56,6 @@ __global__ __launch_bounds__(256) void to_nhwc_kernel(const T *__restrict__ x, T
     transpose_tile<T, BLK>(x, xt, C, HW, blockIdx.x, blockIdx.y, blockIdx.z, tile);
 }
 
-// The same transpose without LDS, one wave per unit of eight 16-byte
-// chunks a lane.  A chunk holds EV = 16/sizeof(T) elements; the EV lanes
-// whose lane numbers differ only in bits {0, 4, 5} (EV = 8) or {4, 5}
-// (EV = 4) hold the rows of an EV x EV tile (row i = those bits in that
-// order), and exchanging each of those lane bits with one bit of the
-// position inside the chunk (bit 0 with the 16-bit half, by a quad swap and
-// a byte permute; bits 4 and 5 with the dword index, by the row and
-// half-wave swaps) leaves lane j of the group with column j.  Loads read
-// channel rows (x is [C][HW] per image), stores write pixel rows.
-template <int EV>
-__device__ __forceinline__ uint4 transpose_lanes(uint4 v, int lane)
-{
-    uint32_t d[4] = {v.x, v.y, v.z, v.w};
-    if constexpr (EV == 8) {
-        // lane bit 0 <-> 16-bit half: an even lane keeps its low halves and
-        // takes its partner's low halves as high halves, an odd lane the
-        // reverse
-        const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t q = uint32_t(__builtin_amdgcn_update_dpp(
-                0, int(d[k]), 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF, false));
-            d[k] = __builtin_amdgcn_perm(q, d[k], sel);
-        }
-    }
-    // lane bit 4 <-> dword bit 0 (odd rows of 16 lanes of the first operand
-    // swapped with even rows of the second)
-#pragma unroll
-    for (int k = 0; k < 4; k += 2) {
-        const auto r = __builtin_amdgcn_permlane16_swap(d[k], d[k + 1], false, false);
-        d[k] = r[0];
-        d[k + 1] = r[1];
-    }
-    // lane bit 5 <-> dword bit 1 (upper half-wave of the first operand
-    // swapped with the lower half-wave of the second)
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const auto r = __builtin_amdgcn_permlane32_swap(d[k], d[k + 2], false, false);
-        d[k] = r[0];
-        d[k + 2] = r[1];
-    }
-    return make_uint4(d[0], d[1], d[2], d[3]);
-}
-
-// 8-channel blocks (16-bit elements): unit u (one wave) moves one block x
-// 512 pixels.  Chunk t of lane group g holds the block's 8 channel rows at
-// pixels 512*pc + 8*(8*t + g) .. +7, so a load instruction reads 8 whole
-// 128-byte lines of x and, after the transpose, a store instruction writes
-// 1 KiB of contiguous block plane.  Units are ordered (image, block, pixel
-// chunk).  Requires C and HW to be multiples of 8 and 16-byte aligned x
-// and xt.
-template <typename T>
-__device__ __forceinline__ void transpose_blocks_wave(const T *__restrict__ x,
-                                                      T *__restrict__ xt, int C, int HW,
-                                                      uint32_t u)
-{
-    static_assert(sizeof(T) == 2, "8-channel blocks of 16 bytes take 16-bit elements");
-    constexpr int R = 8;                        // chunks per lane
-    const int lane = int(threadIdx.x) & 63;
-    const int i = (lane & 1) | ((lane >> 3) & 6);   // row (load) / column (store) in the group
-    const int g = (lane >> 1) & 7;                  // lane group
-    const uint32_t npc = uint32_t(HW + 511) / 512u, cbs = uint32_t(C) / 8u;
-    const uint32_t pc = u % npc, r = u / npc;
-    const uint32_t cb = r % cbs, n = r / cbs;
-    const T *src = x + (size_t(n) * C + 8 * cb + i) * size_t(HW);
-    T *dst = xt + (size_t(n) * cbs + cb) * size_t(HW) * 8;
-    uint4 v[R];
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-        const int po = int(pc) * 512 + (t * 8 + g) * 8;
-        v[t] = make_uint4(0u, 0u, 0u, 0u);
-        if (po < HW)
-            v[t] = *reinterpret_cast<const uint4 *>(src + po);
-    }
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-        const int po = int(pc) * 512 + (t * 8 + g) * 8;
-        const uint4 w = transpose_lanes<8>(v[t], lane);
-        if (po < HW)
-            *reinterpret_cast<uint4 *>(dst + size_t(po + i) * 8) = w;
-    }
-}
-
-// NHWC: one workgroup (4 waves) per tile of 64 channels x 64 pixels, tiles
-// ordered (image, pixel chunk, channel chunk).  Each wave loads Q/4 chunk
-// rows (EV channels x 64 pixels: EV whole lines of x per instruction),
-// transposes them across lanes, and puts each pixel's 16-byte chunk into
-// LDS (row = pixel, Q = 64/EV chunks of 16 bytes, XOR-swizzled so that
-// neither side conflicts); then each wave stores 64/Q pixels x 64 channels
-// per instruction (contiguous 16*Q bytes per pixel).  lds holds 64*Q
-// chunks.  Requires C and HW to be multiples of EV and 16-byte aligned x
-// and xt.
-template <typename T>
-__device__ __forceinline__ void transpose_nhwc_tile(const T *__restrict__ x, T *__restrict__ xt,
-                                                    int C, int HW, uint32_t tile, uint4 *lds)
-{
-    constexpr int EV = 16 / int(sizeof(T));
-    constexpr int Q = 64 / EV;                  // chunks per pixel row of the tile
-    constexpr int PW = Q / 4;                   // chunk rows per wave
-    const int lane = int(threadIdx.x) & 63;
-    const int wave = int(threadIdx.x) >> 6;
-    const int i = EV == 8 ? ((lane & 1) | ((lane >> 3) & 6)) : ((lane >> 4) & 3);
-    const int g = EV == 8 ? ((lane >> 1) & 7) : (lane & 15);
-    const uint32_t ncc = uint32_t(C + 63) / 64u, npc = uint32_t(HW + 63) / 64u;
-    const uint32_t cc = tile % ncc, r = tile / ncc;
-    const uint32_t pc = r % npc, n = r / npc;
-    const int p0 = int(pc) * 64, c0 = int(cc) * 64;
-    auto swz = [](int pl) { return ((pl / EV) ^ (EV == 8 ? pl : 0)) & (Q - 1); };
-    const int po = p0 + EV * g;                 // first pixel of the lane group
-    uint4 v[PW];
-#pragma unroll
-    for (int k = 0; k < PW; ++k) {
-        const int c = c0 + EV * (wave * PW + k);
-        v[k] = make_uint4(0u, 0u, 0u, 0u);
-        if (po < HW && c < C)
-            v[k] = *reinterpret_cast<const uint4 *>(x + (size_t(n) * C + c + i) * size_t(HW) + po);
-    }
-#pragma unroll
-    for (int k = 0; k < PW; ++k) {
-        const int o = wave * PW + k;
-        const int pl = EV * g + i;              // the lane's pixel after the transpose
-        lds[pl * Q + (o ^ swz(pl))] = transpose_lanes<EV>(v[k], lane);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < PW; ++k) {
-        const int pl = (wave * PW + k) * (64 / Q) + lane / Q;
-        const int o = lane % Q;
-        const uint4 w = lds[pl * Q + (o ^ swz(pl))];
-        const int p = p0 + pl, c = c0 + EV * o;
-        if (p < HW && c < C)
-            *reinterpret_cast<uint4 *>(xt + (size_t(n) * HW + p) * size_t(C) + c) = w;
-    }
-}
-
 // Workgroups of the register transposes for cnt images: four block units,
 // or one NHWC tile, a workgroup.
 template <typename T, bool BLK>
@@ -223,7 +89,13 @@ __device__ __forceinline__ void transpose_group(const T *__restrict__ x, T *__re
                 transpose_blocks_wave<T>(x, xt, C, HW, u);
         }
     } else {
-        transpose_nhwc_tile<T>(x, xt, C, HW, b, lds);
+        NhwcTile<T> tl;
+        tl.load(x, C, HW, b, int(threadIdx.x));
+        tl.put(lds, int(threadIdx.x));
+        __syncthreads();
+        tl.take(lds, C, HW, int(threadIdx.x), [&](const uint4 &v, size_t off) {
+            *reinterpret_cast<uint4 *>(xt + off) = v;
+        });
     }
 }
 
