@@ -170,6 +170,51 @@ __global__ __launch_bounds__(256) void pack_weight_steps_kernel(const T *__restr
                     nflags);
 }
 
+// Eight consecutive elements of a packed weight (PK 1: [Co][Kp]; PK 2: the
+// window path's step-major planes), elements 8*t8 .. 8*t8+7, one thread:
+// eight loads and one (16-bit) or two (fp32) 16-byte stores.  Kp and the
+// planes' 8-element rows keep every group of eight inside one row.
+template <typename T, int PK>
+__device__ __forceinline__ void pack8(const T *__restrict__ w, T *__restrict__ wp, int t8,
+                                      int total, int Kp, int Kg, int Cg, int K, int Mg, int S)
+{
+    const int t = t8 * 8;
+    if (t >= total)
+        return;
+    union {
+        T e[8];
+        uint4 q[8 * sizeof(T) / 16];
+    } v;
+    if constexpr (PK == 1) {
+        const int kk0 = t % Kp;
+        const int co = t / Kp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int kk = kk0 + e;
+            const int k = kk / Cg;
+            const int cl = kk - k * Cg;
+            v.e[e] = kk < Kg ? w[(size_t(co) * Cg + cl) * K + k] : T(0);
+        }
+    } else {
+        int r = t8;
+        const int m = r % Mg;
+        r /= Mg;
+        const int h = r & 1;
+        r >>= 1;
+        const int st = r % S;
+        const int g = r / S;
+        const int chunk = st / K, k = st - chunk * K;
+        const T *src = w + (size_t(g * Mg + m) * Cg + chunk * 16 + h * 8) * K + k;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v.e[e] = src[size_t(e) * K];
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(wp + t);
+#pragma unroll
+    for (int j = 0; j < int(8 * sizeof(T) / 16); ++j)
+        dst[j] = v.q[j];
+}
+
 // The FP8 path's weight, one workgroup (256 threads) per output channel co:
 // the row's exponent e, the largest integer with max|w[co]| * 2^e <= 448
 // (0 for a row with no nonzero finite maximum; clamped to [-126, 126]),
@@ -255,13 +300,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
                      b - a.nt, a.Kg, a.Kp, a.Cg, a.K, reinterpret_cast<float *>(&tile[0][0]));
         return;
     }
-    const int t = (b - a.nt) * 256 + int(threadIdx.x);
-    if constexpr (PK == 1)
-        pack_weight_elem(static_cast<const T *>(a.w), static_cast<T *>(a.wp), t, a.total, a.Kp,
-                         a.Kg, a.Cg, a.K);
-    else
-        pack_steps_elem(static_cast<const T *>(a.w), static_cast<T *>(a.wp), t, a.total, a.Mg,
-                        a.Cg, a.K, a.S, a.flags, a.nflags);
+    // eight weight elements a thread (and, window path, one flag)
+    const int t8 = (b - a.nt) * 256 + int(threadIdx.x);
+    if (PK == 2 && t8 < a.nflags)
+        a.flags[t8] = 0u;
+    pack8<T, PK>(static_cast<const T *>(a.w), static_cast<T *>(a.wp), t8, a.total, a.Kp, a.Kg,
+                 a.Cg, a.K, a.Mg, a.S);
 }
 
 template <typename T, bool BLK>
@@ -388,15 +432,17 @@ hipError_t prep_t(const Problem &p, const Plan &plan, int64_t cnt, const void *x
         a.total = int(p.Co * plan.Kp);
         a.Kp = int(plan.Kp);
         a.Kg = int(p.Kg);
-        npack = a.total;
+        if (a.Kp % 8 != 0 || reinterpret_cast<uintptr_t>(wp) % 32 != 0)
+            return hipErrorInvalidValue;
+        npack = a.total / 8;                  // threads: eight elements each
     } else {
-        if (p.Cg % 16 != 0)
+        if (p.Cg % 16 != 0 || reinterpret_cast<uintptr_t>(wp) % 32 != 0)
             return hipErrorInvalidValue;
         a.S = int(p.Cg / 16 * p.K);
         a.total = int(p.G * a.S * 2 * p.Mg * 8);
         a.Mg = int(p.Mg);
         a.nflags = flags ? nflags : 0;
-        npack = std::max(a.total, a.nflags);
+        npack = std::max<int64_t>(a.total / 8, a.nflags);
     }
     const bool vec = transpose_regs_ok<T, BLK>(p.C, HW, x, xt);
     const int64_t units = vec ? (BLK ? cnt * (p.C / 8) * ((HW + 511) / 512) : 0) : 0;
