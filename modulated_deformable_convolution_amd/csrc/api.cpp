@@ -327,10 +327,15 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
     const bool empty = p.N == 0 || p.P == 0;
     // the weight accumulator takes atomic adds; an empty batch or output grid
     // leaves every gradient zero
+    char *bins = ws + l.bins_off;
     hipError_t err = rec.run(mdcn::K_BWD_ZERO, [&] {
         hipError_t e = mdcn::launch_bwd_fill_zero(wacc, p.Co * l.Kp, stream);
         if (e == hipSuccess && empty)
             e = mdcn::launch_bwd_fill_zero_dtype(p, gx, int64_t(p.N) * int64_t(x_n), stream);
+        // the bucket counts (each image's fill pass leaves them zero again)
+        if (e == hipSuccess && l.binned && !empty)
+            e = mdcn::launch_bwd_fill_zero(reinterpret_cast<float *>(bins + l.cnt_off),
+                                           p.DG * p.H * p.W, stream);
         return e;
     });
     if (err != hipSuccess)
@@ -429,7 +434,7 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
                            ? r
                            : mdcn::launch_gemm(pq, qp, 1, goT, wT, nullptr, nullptr, gcol, stream);
             });
-        if (err == hipSuccess)
+        if (err == hipSuccess && !l.binned)
             err = rec.run(mdcn::K_BWD_ZERO, [&] {
                 return mdcn::launch_bwd_fill_zero(gxt, int64_t(x_n), stream);
             });
@@ -438,7 +443,7 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
                 return mdcn::launch_bwd_sample(
                     p, l, xt, on, mn, gcol, gxt,
                     static_cast<char *>(grad_offset) + size_t(n) * off_n * e,
-                    static_cast<char *>(grad_mask) + size_t(n) * msk_n * e, stream);
+                    static_cast<char *>(grad_mask) + size_t(n) * msk_n * e, bins, stream);
             });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_BWD_TO_NCHW, [&] {

@@ -183,12 +183,48 @@ struct SampleArgs {
     int team_shift;         // lanes per (offset group, tap, pixel): 1 << team_shift (<= 64)
 };
 
+// Sampling geometry of (offset group q, tap k, output pixel p) for the
+// backward: the cell floor() selects, its fractions, which corners lie on
+// the image, and whether the sample has derivatives at all (inside the open
+// window (-1, H) x (-1, W), finite coordinate).
+struct BwdTaps {
+    bool live;
+    bool r0, r1, c0, c1;
+    int y0, x0;
+    float ay, ax;
+};
+
+__device__ __forceinline__ BwdTaps bwd_taps(float oh, float ow, int ho, int wo, int i, int j,
+                                            int H, int W, int sh, int sw, int ph, int pw, int dh,
+                                            int dw)
+{
+    BwdTaps t{};
+    const float lim = 33554432.0f;                // 2^25: certainly off any valid image
+    if (!(fabsf(oh) <= lim && fabsf(ow) <= lim))
+        return t;
+    const float fh = floorf(oh), fw = floorf(ow);
+    t.ay = oh - fh;                               // fractions (the anchor is an integer)
+    t.ax = ow - fw;
+    t.y0 = ho * sh - ph + i * dh + int(fh);
+    t.x0 = wo * sw - pw + j * dw + int(fw);
+    // inside the open window (-1, H) x (-1, W): h > -1 is y0 >= 0, or
+    // y0 == -1 with a nonzero fraction; h < H is y0 <= H-1 (same for w)
+    t.live = (t.y0 >= 0 || (t.y0 == -1 && t.ay > 0.0f)) && t.y0 < H &&
+             (t.x0 >= 0 || (t.x0 == -1 && t.ax > 0.0f)) && t.x0 < W;
+    t.r0 = t.y0 >= 0;
+    t.r1 = t.y0 + 1 < H;
+    t.c0 = t.x0 >= 0;
+    t.c1 = t.x0 + 1 < W;
+    return t;
+}
+
 // A team of lanes per (offset group q, tap k, pixel p) of one image, its
 // lanes spread over q's channels: the corner reads of x, the column
-// gradients and the atomic adds into grad_x are contiguous across the team
-// (channels-last), and the team reduces its mask and offset gradients with
-// wave shuffles.
-template <typename T>
+// gradients and (ATOMIC_X) the atomic adds into grad_x are contiguous across
+// the team (channels-last), and the team reduces its mask and offset
+// gradients with wave shuffles.  Without ATOMIC_X, grad_x is left to the
+// binned gather (bin_corners_kernel, gather_gx_kernel).
+template <typename T, bool ATOMIC_X>
 __global__ __launch_bounds__(256) void sample_grad_kernel(SampleArgs a)
 {
     const T *xt = static_cast<const T *>(a.xt);
@@ -238,11 +274,13 @@ __global__ __launch_bounds__(256) void sample_grad_kernel(SampleArgs a)
                     gm = fmaf(gc, v, gm);
                     gh = fmaf(gc, (1.0f - ax) * (v10 - v00) + ax * (v11 - v01), gh);
                     gw = fmaf(gc, (1.0f - ay) * (v01 - v00) + ay * (v11 - v10), gw);
-                    const float s = gc * m;
-                    if (r0 && c0) atomicAdd(a.gxt + e00 + c, s * w00);
-                    if (r0 && c1) atomicAdd(a.gxt + e01 + c, s * w01);
-                    if (r1 && c0) atomicAdd(a.gxt + e10 + c, s * w10);
-                    if (r1 && c1) atomicAdd(a.gxt + e11 + c, s * w11);
+                    if constexpr (ATOMIC_X) {
+                        const float s = gc * m;
+                        if (r0 && c0) atomicAdd(a.gxt + e00 + c, s * w00);
+                        if (r0 && c1) atomicAdd(a.gxt + e01 + c, s * w01);
+                        if (r1 && c0) atomicAdd(a.gxt + e10 + c, s * w10);
+                        if (r1 && c1) atomicAdd(a.gxt + e11 + c, s * w11);
+                    }
                 }
             }
         }
@@ -257,6 +295,305 @@ __global__ __launch_bounds__(256) void sample_grad_kernel(SampleArgs a)
         static_cast<T *>(a.gmask)[mi] = from_f32<T>(gm);
         static_cast<T *>(a.goff)[ohi] = from_f32<T>(gh * m);
         static_cast<T *>(a.goff)[ohi + a.P] = from_f32<T>(gw * m);
+    }
+}
+
+// Four consecutive channels of element type T at p (aligned to four
+// elements) as floats.
+template <typename T>
+__device__ __forceinline__ float4 load4f(const T *p)
+{
+    if constexpr (sizeof(T) == 4) {
+        return *reinterpret_cast<const float4 *>(p);
+    } else {
+        const uint2 r = *reinterpret_cast<const uint2 *>(p);
+        T e[4];
+        __builtin_memcpy(e, &r, 8);
+        return make_float4(to_f32(e[0]), to_f32(e[1]), to_f32(e[2]), to_f32(e[3]));
+    }
+}
+
+// The mask and offset gradients alone (grad_x by the binned gather), four
+// channels a lane: one 16-byte column-gradient load and four corner loads
+// of four channels per step.  Requires C/group and C/deformable_group to be
+// multiples of 4.
+template <typename T>
+__global__ __launch_bounds__(256) void sample_grad_vec_kernel(SampleArgs a)
+{
+    const T *xt = static_cast<const T *>(a.xt);
+    const T *offp = static_cast<const T *>(a.off);
+    const T *mskp = static_cast<const T *>(a.msk);
+    const int TS = 1 << a.team_shift;
+    const int64_t gt = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t item = gt >> a.team_shift;
+    const int lane = int(gt & (TS - 1));
+    const bool live = item < int64_t(a.DG) * a.K * a.P;
+    float gm = 0.0f, gh = 0.0f, gw = 0.0f, m = 0.0f;
+    int64_t ohi = 0, mi = 0;
+    if (live) {
+        const int p = int(item % a.P);
+        const int k = int((item / a.P) % a.K);
+        const int q = int(item / (int64_t(a.P) * a.K));
+        const int ho = p / a.Wo, wo = p - (p / a.Wo) * a.Wo;
+        const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+        ohi = (int64_t(q) * 2 * a.K + 2 * k) * a.P + p;
+        mi = (int64_t(q) * a.K + k) * a.P + p;
+        m = to_f32(mskp[mi]);
+        const BwdTaps t = bwd_taps(to_f32(offp[ohi]), to_f32(offp[ohi + a.P]), ho, wo, i, j, a.H,
+                                   a.W, a.sh, a.sw, a.ph, a.pw, a.dh, a.dw);
+        if (t.live) {
+            const float ay = t.ay, ax = t.ax;
+            const float w00 = (1.0f - ay) * (1.0f - ax), w01 = (1.0f - ay) * ax;
+            const float w10 = ay * (1.0f - ax), w11 = ay * ax;
+            const int64_t e00 = (int64_t(t.y0) * a.W + t.x0) * a.C;   // NHWC entry of (y0, x0)
+            const int64_t e01 = e00 + a.C, e10 = e00 + int64_t(a.W) * a.C, e11 = e10 + a.C;
+            const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            for (int c = q * a.Cdg + lane * 4; c < (q + 1) * a.Cdg; c += TS * 4) {
+                const int grp = c / a.Cg, cl = c - grp * a.Cg;
+                const float4 g4 = *reinterpret_cast<const float4 *>(
+                    a.gcol + (int64_t(grp) * a.P + p) * a.Kp + int64_t(k) * a.Cg + cl);
+                const float4 a00 = (t.r0 && t.c0) ? load4f(xt + e00 + c) : z;
+                const float4 a01 = (t.r0 && t.c1) ? load4f(xt + e01 + c) : z;
+                const float4 a10 = (t.r1 && t.c0) ? load4f(xt + e10 + c) : z;
+                const float4 a11 = (t.r1 && t.c1) ? load4f(xt + e11 + c) : z;
+                const float gcv[4] = {g4.x, g4.y, g4.z, g4.w};
+                const float v00[4] = {a00.x, a00.y, a00.z, a00.w};
+                const float v01[4] = {a01.x, a01.y, a01.z, a01.w};
+                const float v10[4] = {a10.x, a10.y, a10.z, a10.w};
+                const float v11[4] = {a11.x, a11.y, a11.z, a11.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float v = w00 * v00[u] + w01 * v01[u] + w10 * v10[u] + w11 * v11[u];
+                    gm = fmaf(gcv[u], v, gm);
+                    gh = fmaf(gcv[u], (1.0f - ax) * (v10[u] - v00[u]) + ax * (v11[u] - v01[u]),
+                              gh);
+                    gw = fmaf(gcv[u], (1.0f - ay) * (v01[u] - v00[u]) + ay * (v11[u] - v10[u]),
+                              gw);
+                }
+            }
+        }
+    }
+    for (int d = TS >> 1; d >= 1; d >>= 1) {
+        gm += __shfl_xor(gm, d, 64);
+        gh += __shfl_xor(gh, d, 64);
+        gw += __shfl_xor(gw, d, 64);
+    }
+    if (live && lane == 0) {
+        static_cast<T *>(a.gmask)[mi] = from_f32<T>(gm);
+        static_cast<T *>(a.goff)[ohi] = from_f32<T>(gh * m);
+        static_cast<T *>(a.goff)[ohi + a.P] = from_f32<T>(gw * m);
+    }
+}
+
+// grad_x without atomics: every on-image corner of every live sample is an
+// entry (source column k*P + p, weight mask * corner weight) in the bucket of
+// its (offset group, input pixel) cell.  A counting pass (FILL = false)
+// counts the entries of each cell, a scan turns the counts into bucket
+// starts, and a fill pass (FILL = true) places each entry at
+// start + (count after a decrement), which also leaves every count at zero
+// for the next image.  Then one thread per (cell, channel) sums its bucket:
+//   grad_x[c][cell] = sum over entries (k, p, w) of w * gcol(c, k, p).
+struct BinArgs {
+    const void *off;        // image n, dtype
+    const void *msk;        // image n, dtype
+    uint32_t *cnt;          // [DG][H*W]: zero before the counting pass and after the fill
+    const uint32_t *start;  // [DG][H*W] + 1: bucket starts
+    uint2 *entries;         // {k*P + p, weight bits}
+    int H, W, Wo, P, K, kw, DG;
+    int sh, sw, ph, pw, dh, dw;
+};
+
+template <typename T, bool FILL>
+__global__ __launch_bounds__(256) void bin_corners_kernel(BinArgs a)
+{
+    const int64_t item = int64_t(blockIdx.x) * 256 + threadIdx.x;   // (q, k, p)
+    if (item >= int64_t(a.DG) * a.K * a.P)
+        return;
+    const int p = int(item % a.P);
+    const int k = int((item / a.P) % a.K);
+    const int q = int(item / (int64_t(a.P) * a.K));
+    const int ho = p / a.Wo, wo = p - (p / a.Wo) * a.Wo;
+    const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+    const T *offp = static_cast<const T *>(a.off);
+    const int64_t ohi = (int64_t(q) * 2 * a.K + 2 * k) * a.P + p;
+    const BwdTaps t = bwd_taps(to_f32(offp[ohi]), to_f32(offp[ohi + a.P]), ho, wo, i, j, a.H,
+                               a.W, a.sh, a.sw, a.ph, a.pw, a.dh, a.dw);
+    if (!t.live)
+        return;
+    const float m = to_f32(static_cast<const T *>(a.msk)[(int64_t(q) * a.K + k) * a.P + p]);
+    const float wt[4] = {(1.0f - t.ay) * (1.0f - t.ax), (1.0f - t.ay) * t.ax,
+                         t.ay * (1.0f - t.ax), t.ay * t.ax};
+    const bool on[4] = {t.r0 && t.c0, t.r0 && t.c1, t.r1 && t.c0, t.r1 && t.c1};
+    const int64_t base = int64_t(q) * a.H * a.W;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if (!on[s])
+            continue;
+        const int64_t cell = base + int64_t(t.y0 + (s >> 1)) * a.W + t.x0 + (s & 1);
+        if constexpr (!FILL) {
+            atomicAdd(a.cnt + cell, 1u);
+        } else {
+            const uint32_t slot = atomicSub(a.cnt + cell, 1u) - 1u;
+            a.entries[a.start[cell] + slot] =
+                make_uint2(uint32_t(k * a.P + p), __float_as_uint(m * wt[s]));
+        }
+    }
+}
+
+// Exclusive scan of n counts into start[0..n] (start[n] = total), in three
+// launches: per 4096-element block (1024 threads, 4 elements each) the local
+// scan and the block's total; the scan of the block totals (one workgroup,
+// at most 4096 blocks); the block offsets added.
+constexpr int kScanBlock = 4096;
+
+__device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t *sh, uint32_t *total)
+{
+    // inclusive scan within the wave, then across the 16 waves
+    const int lane = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t u = __shfl_up(v, d, 64);
+        if (lane >= d)
+            v += u;
+    }
+    if (lane == 63)
+        sh[wave] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t run = 0;
+        for (int w = 0; w < 16; ++w) {
+            const uint32_t x = sh[w];
+            sh[w] = run;
+            run += x;
+        }
+        sh[16] = run;
+    }
+    __syncthreads();
+    const uint32_t r = v + sh[wave];
+    *total = sh[16];
+    __syncthreads();
+    return r;                                    // inclusive
+}
+
+__global__ __launch_bounds__(1024) void scan_blocks_kernel(const uint32_t *__restrict__ cnt,
+                                                           uint32_t *__restrict__ start,
+                                                           uint32_t *__restrict__ bsum,
+                                                           int64_t n)
+{
+    __shared__ uint32_t sh[17];
+    const int64_t i0 = int64_t(blockIdx.x) * kScanBlock + int64_t(threadIdx.x) * 4;
+    uint32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        v[e] = i0 + e < n ? cnt[i0 + e] : 0u;
+    const uint32_t mine = v[0] + v[1] + v[2] + v[3];
+    uint32_t total;
+    const uint32_t incl = block_scan_1024(mine, sh, &total);
+    uint32_t run = incl - mine;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (i0 + e < n)
+            start[i0 + e] = run;
+        run += v[e];
+    }
+    if (threadIdx.x == 0)
+        bsum[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(1024) void scan_sums_kernel(uint32_t *__restrict__ bsum, int nb,
+                                                         uint32_t *__restrict__ last)
+{
+    __shared__ uint32_t sh[17];
+    uint32_t v[4];
+    const int i0 = int(threadIdx.x) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        v[e] = i0 + e < nb ? bsum[i0 + e] : 0u;
+    const uint32_t mine = v[0] + v[1] + v[2] + v[3];
+    uint32_t total;
+    const uint32_t incl = block_scan_1024(mine, sh, &total);
+    uint32_t run = incl - mine;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (i0 + e < nb)
+            bsum[i0 + e] = run;
+        run += v[e];
+    }
+    if (threadIdx.x == 0)
+        *last = total;
+}
+
+__global__ __launch_bounds__(256) void scan_add_kernel(uint32_t *__restrict__ start,
+                                                       const uint32_t *__restrict__ bsum,
+                                                       int64_t n)
+{
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n)
+        start[i] += bsum[i / kScanBlock];
+}
+
+struct GatherGxArgs {
+    const uint32_t *start;  // [DG][H*W] + 1
+    const uint2 *entries;
+    const float *gcol;      // [G][P][Kp], column k*Cg + c'
+    float *gxt;             // image n's grad_x, NHWC, fp32 (every element written)
+    int C, HW, P, Cg, Cdg, Kp, DG;
+};
+
+// One wave per (offset group q, input cell): its lanes run over q's
+// channels, V consecutive channels a lane (one 16-byte column-gradient load
+// when V = 4), in slices of 64*V.  The bucket's entries are read 64 at a
+// time, one per lane, and handed to the whole wave one by one (readlane), so
+// that the column-gradient loads of several entries are in flight together.
+template <int V>
+__global__ __launch_bounds__(256) void gather_gx_kernel(GatherGxArgs a)
+{
+    const int64_t wv = (int64_t(blockIdx.x) * 256 + threadIdx.x) >> 6;   // (q, cell)
+    const int lane = int(threadIdx.x) & 63;
+    if (wv >= int64_t(a.DG) * a.HW)
+        return;
+    const int q = int(wv / a.HW);
+    const int64_t cell = wv - int64_t(q) * a.HW;
+    const uint32_t e0 = a.start[wv], e1 = a.start[wv + 1];
+    for (int cs = 0; cs < a.Cdg; cs += 64 * V) {
+        const int cq = cs + lane * V;               // the lane's first channel within q
+        const bool on = cq < a.Cdg;
+        const int c = q * a.Cdg + (on ? cq : 0);
+        const int grp = c / a.Cg, cl = c - grp * a.Cg;
+        const float *gc = a.gcol + int64_t(grp) * a.P * a.Kp + cl;
+        float acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            acc[v] = 0.0f;
+        for (uint32_t eb = e0; eb < e1; eb += 64) {
+            const int n = int(min(64u, e1 - eb));
+            const uint2 my = lane < n ? a.entries[eb + lane] : make_uint2(0u, 0u);
+#pragma unroll 4
+            for (int j = 0; j < n; ++j) {
+                const int kp = __builtin_amdgcn_readlane(int(my.x), j);
+                const float w = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(my.y), j)));
+                const int k = kp / a.P, p = kp - k * a.P;
+                const float *src = gc + int64_t(p) * a.Kp + int64_t(k) * a.Cg;
+                if (on) {
+                    if constexpr (V == 4) {
+                        const float4 g4 = *reinterpret_cast<const float4 *>(src);
+                        acc[0] = fmaf(w, g4.x, acc[0]);
+                        acc[1] = fmaf(w, g4.y, acc[1]);
+                        acc[2] = fmaf(w, g4.z, acc[2]);
+                        acc[3] = fmaf(w, g4.w, acc[3]);
+                    } else {
+                        acc[0] = fmaf(w, *src, acc[0]);
+                    }
+                }
+            }
+        }
+        if (on) {
+            float *dst = a.gxt + cell * a.C + c;
+            if constexpr (V == 4)
+                *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            else
+                *dst = acc[0];
+        }
     }
 }
 
@@ -323,6 +660,21 @@ BackwardLayout backward_layout(const Problem &p)
     if (l.mfma_col) {
         l.wT_off = l.goT_off + al(size_t(p.P * p.Co) * 4);
         l.bytes = l.wT_off + al(size_t(l.Kp * p.Co) * 4);
+    }
+    // grad_x binned by input cell (no atomics on grad_x): counts, bucket
+    // starts, scan block totals and up to four entries per sample, after
+    // everything else (counts zeroed once per call, left zero by each image)
+    const int64_t cells = p.DG * p.H * p.W;
+    const int64_t entries = 4 * p.DG * p.K * p.P;
+    l.binned = cells > 0 && cells <= int64_t(kScanBlock) * kScanBlock &&
+               entries < (int64_t(1) << 32) && p.K * p.P < (int64_t(1) << 32);
+    if (l.binned) {
+        l.bins_off = l.bytes;
+        l.cnt_off = 0;
+        l.start_off = l.cnt_off + al(size_t(cells) * 4);
+        l.bsum_off = l.start_off + al(size_t(cells + 1) * 4);
+        l.entries_off = l.bsum_off + al(size_t(kScanBlock + 1) * 4);
+        l.bytes = l.bins_off + l.entries_off + al(size_t(entries) * 8);
     }
     return l;
 }
@@ -407,10 +759,39 @@ hipError_t col_gemm_t(const Problem &p, const BackwardLayout &l, const void *wpa
 }
 
 template <typename T>
-hipError_t sample_t(const Problem &p, const SampleArgs &a, int64_t threads, hipStream_t s)
+hipError_t sample_t(const Problem &p, const SampleArgs &a, int64_t threads, bool atomic_x,
+                    hipStream_t s)
 {
-    hipLaunchKernelGGL((sample_grad_kernel<T>), dim3(unsigned((threads + 255) / 256)), dim3(256),
-                       0, s, a);
+    if (!atomic_x && p.Cg % 4 == 0 && p.Cdg % 4 == 0) {
+        // four channels a lane: a team of at most 64 lanes covers Cdg/4 slots
+        SampleArgs v = a;
+        int shift = 0;
+        while ((1 << shift) * 4 < p.Cdg && shift < 6)
+            ++shift;
+        v.team_shift = shift;
+        const int64_t n = (p.DG * p.K * p.P) << shift;
+        hipLaunchKernelGGL((sample_grad_vec_kernel<T>), dim3(unsigned((n + 255) / 256)),
+                           dim3(256), 0, s, v);
+        return hipGetLastError();
+    }
+    if (atomic_x)
+        hipLaunchKernelGGL((sample_grad_kernel<T, true>), dim3(unsigned((threads + 255) / 256)),
+                           dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((sample_grad_kernel<T, false>), dim3(unsigned((threads + 255) / 256)),
+                           dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t bin_t(const BinArgs &b, int64_t items, bool fill, hipStream_t s)
+{
+    if (fill)
+        hipLaunchKernelGGL((bin_corners_kernel<T, true>), dim3(unsigned((items + 255) / 256)),
+                           dim3(256), 0, s, b);
+    else
+        hipLaunchKernelGGL((bin_corners_kernel<T, false>), dim3(unsigned((items + 255) / 256)),
+                           dim3(256), 0, s, b);
     return hipGetLastError();
 }
 
@@ -473,7 +854,8 @@ hipError_t launch_bwd_col_gemm(const Problem &p, const BackwardLayout &l, const 
 
 hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const void *xt_n,
                              const void *off_n, const void *msk_n, const float *gcol,
-                             float *gxt_n, void *goff_n, void *gmask_n, hipStream_t s)
+                             float *gxt_n, void *goff_n, void *gmask_n, char *bins,
+                             hipStream_t s)
 {
     SampleArgs a;
     a.xt = xt_n; a.off = off_n; a.msk = msk_n; a.gcol = gcol; a.gxt = gxt_n;
@@ -487,15 +869,65 @@ hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const vo
     while ((1 << shift) < p.Cdg && shift < 6)
         ++shift;
     a.team_shift = shift;
-    const int64_t threads = (p.DG * p.K * p.P) << shift;
+    const int64_t items = p.DG * p.K * p.P;
+    const int64_t threads = items << shift;
     if (threads == 0)
         return hipSuccess;
     if ((threads + 255) / 256 > 0x7fffffff)
         return hipErrorInvalidValue;
+    hipError_t e = hipSuccess;
+    if (l.binned) {
+        const int64_t cells = p.DG * p.H * p.W;
+        BinArgs b;
+        b.off = off_n; b.msk = msk_n;
+        b.cnt = reinterpret_cast<uint32_t *>(bins + l.cnt_off);
+        b.start = reinterpret_cast<const uint32_t *>(bins + l.start_off);
+        b.entries = reinterpret_cast<uint2 *>(bins + l.entries_off);
+        b.H = int(p.H); b.W = int(p.W); b.Wo = int(p.Wo); b.P = int(p.P); b.K = int(p.K);
+        b.kw = int(p.kw); b.DG = int(p.DG);
+        b.sh = int(p.sh); b.sw = int(p.sw); b.ph = int(p.ph); b.pw = int(p.pw);
+        b.dh = int(p.dh); b.dw = int(p.dw);
+        uint32_t *start = reinterpret_cast<uint32_t *>(bins + l.start_off);
+        uint32_t *bsum = reinterpret_cast<uint32_t *>(bins + l.bsum_off);
+        const int nb = int((cells + kScanBlock - 1) / kScanBlock);
+        auto bin = [&](bool fill) {
+            switch (p.dtype) {
+            case MDCN_F32: return bin_t<float>(b, items, fill, s);
+            case MDCN_F16: return bin_t<half_t>(b, items, fill, s);
+            case MDCN_BF16: return bin_t<bf16_t>(b, items, fill, s);
+            }
+            return hipErrorInvalidValue;
+        };
+        e = bin(false);
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(scan_blocks_kernel, dim3(unsigned(nb)), dim3(1024), 0, s, b.cnt,
+                               start, bsum, cells);
+            hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(1024), 0, s, bsum, nb,
+                               start + cells);
+            hipLaunchKernelGGL(scan_add_kernel, dim3(unsigned((cells + 255) / 256)), dim3(256),
+                               0, s, start, bsum, cells);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess)
+            e = bin(true);
+        if (e == hipSuccess) {
+            GatherGxArgs g{start, b.entries, gcol, gxt_n, int(p.C), int(p.H * p.W), int(p.P),
+                           int(p.Cg), int(p.Cdg), int(l.Kp), int(p.DG)};
+            const int64_t waves = cells;           // one per (offset group, cell)
+            const dim3 grid(unsigned((waves + 3) / 4));
+            if (p.Cg % 4 == 0 && p.Cdg % 4 == 0 && l.Kp % 4 == 0)
+                hipLaunchKernelGGL(gather_gx_kernel<4>, grid, dim3(256), 0, s, g);
+            else
+                hipLaunchKernelGGL(gather_gx_kernel<1>, grid, dim3(256), 0, s, g);
+            e = hipGetLastError();
+        }
+        if (e != hipSuccess)
+            return e;
+    }
     switch (p.dtype) {
-    case MDCN_F32: return sample_t<float>(p, a, threads, s);
-    case MDCN_F16: return sample_t<half_t>(p, a, threads, s);
-    case MDCN_BF16: return sample_t<bf16_t>(p, a, threads, s);
+    case MDCN_F32: return sample_t<float>(p, a, threads, !l.binned, s);
+    case MDCN_F16: return sample_t<half_t>(p, a, threads, !l.binned, s);
+    case MDCN_BF16: return sample_t<bf16_t>(p, a, threads, !l.binned, s);
     }
     return hipErrorInvalidValue;
 }

@@ -169,6 +169,9 @@ struct BackwardLayout {
     size_t goT_off, wT_off;
     bool mfma_col;
     int64_t wsplit;    // > 0: the weight gradient on the MFMA GEMM in wsplit pixel chunks
+    bool binned;       // grad_x gathered from per-cell buckets (else atomic adds)
+    size_t bins_off;   // the buckets' area; inside it:
+    size_t cnt_off, start_off, bsum_off, entries_off;
 };
 // acc[t] += sum over s < S of part[s*n + t].
 hipError_t launch_bwd_reduce_parts(const float *part, float *acc, int64_t n, int S,
@@ -185,11 +188,15 @@ hipError_t launch_bwd_weight_gemm(const Problem &p, const BackwardLayout &l, con
 // gcol[g][p][kk] = sum_m g_n[g*Mg + m][p] * wpack[g][m][kk] (kk tap-major).
 hipError_t launch_bwd_col_gemm(const Problem &p, const BackwardLayout &l, const void *wpack,
                                const void *g_n, float *gcol, hipStream_t stream);
-// grad_mask, grad_offset of image n (stored) and its grad_x in NHWC (atomic
-// adds into gxt_n, zeroed by the caller) from gcol and the NHWC x.
+// grad_mask, grad_offset of image n (stored) and its grad_x in NHWC from
+// gcol and the NHWC x.  l.binned: grad_x summed per input cell from buckets
+// built at `bins` (the layout's bins area, whose counts must be zero; they
+// are zero again afterwards), every element of gxt_n written; otherwise
+// atomic adds into gxt_n, which the caller zeroes.
 hipError_t launch_bwd_sample(const Problem &p, const BackwardLayout &l, const void *xt_n,
                              const void *off_n, const void *msk_n, const float *gcol,
-                             float *gxt_n, void *goff_n, void *gmask_n, hipStream_t stream);
+                             float *gxt_n, void *goff_n, void *gmask_n, char *bins,
+                             hipStream_t stream);
 // dst[t] = src[t] rounded to the dtype (n values).
 hipError_t launch_bwd_convert(const Problem &p, const float *src, void *dst, int64_t n,
                               hipStream_t stream);

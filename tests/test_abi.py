@@ -468,7 +468,9 @@ def test_backward_entry_points():
     """Inputs and gradients in the dtype, fp32 arithmetic; the workspace holds
     the packed weight and one image's NHWC x (dtype), its fp32 gradient
     accumulator (NHWC, and NCHW for fp16/bf16), its fp32 columns and their
-    gradient, and the weight-gradient accumulator."""
+    gradient, the weight-gradient accumulator, and the buckets of grad_x's
+    gather (counts, starts, scan block totals, up to four 8-byte entries per
+    sample)."""
     op = mdcn.mdcn_create(1, 1, 1, 1, 1)
     hw = 256 * 160 * 160
     col = 25600 * 2304 * 4            # columns and their gradient (fp32)
@@ -477,10 +479,15 @@ def test_backward_entry_points():
     # fp32 with one group and Co % 32 == 0: the column gradient on the MFMA
     # GEMM, with grad_out [P][Co] and the packed weight [Kp][Co] transposed
     mfma = 25600 * 256 * 4 + 2304 * 256 * 4
-    assert b == 256 + 256 * 2304 * 4 + hw * 4 + hw * 4 + 2 * col + acc + mfma
+
+    def al(v):
+        return (v + 255) // 256 * 256
+    cells = 160 * 160
+    bins = al(cells * 4) + al((cells + 1) * 4) + al(4097 * 4) + al(4 * 9 * 25600 * 8)
+    assert b == 256 + 256 * 2304 * 4 + hw * 4 + hw * 4 + 2 * col + acc + mfma + bins
     for dt in (mdcn.MDCN_F16, mdcn.MDCN_BF16):
         b16 = mdcn.mdcn_backward_workspace_bytes(op, dt, DIMS)
-        assert b16 == 256 + 256 * 2304 * 2 + hw * 2 + 2 * hw * 4 + 2 * col + acc
+        assert b16 == 256 + 256 * 2304 * 2 + hw * 2 + 2 * hw * 4 + 2 * col + acc + bins
     with pytest.raises(mdcn.MdcnError) as e:
         mdcn.mdcn_backward_workspace_bytes(op, 7, DIMS)
     assert e.value.status == mdcn.MDCN_E_DTYPE
