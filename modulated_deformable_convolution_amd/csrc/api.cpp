@@ -380,8 +380,6 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
     qp.gemm_tile = mdcn::gemm_tile_for(pq, 1);
     Problem pgo = p;                   // grad_out [Co][P] -> [P][Co]: the NHWC transpose
     pgo.C = p.Co; pgo.H = p.Ho; pgo.W = p.Wo;
-    Problem pcol = p;                  // columns [P][Kp] -> [Kp][P]
-    pcol.C = p.P; pcol.H = l.Kp; pcol.W = 1;
     Problem pwt = p;                   // packed weight [Co][Kp] -> [Kp][Co]
     pwt.C = p.Co; pwt.H = l.Kp; pwt.W = 1;
     if (l.mfma_col && !empty) {
@@ -397,21 +395,23 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
         const char *mn = static_cast<const char *>(mask) + size_t(n) * msk_n * e;
         const char *gn = static_cast<const char *>(grad_out) + size_t(n) * out_n * e;
         err = rec.run(mdcn::K_TO_NHWC, [&] { return mdcn::launch_to_nhwc(p, 1, xn, xt, stream); });
+        // the columns: [P][Kp], or (weight gradient in pixel chunks) straight
+        // into the column-gradient buffer transposed, [Kp][P]
         if (err == hipSuccess)
             err = rec.run(mdcn::K_GATHER, [&] {
-                return mdcn::launch_gather_f32(p, gp, 1, xt, on, mn, col, stream);
+                return l.wsplit == 0
+                           ? mdcn::launch_gather_f32(p, gp, 1, xt, on, mn, col, stream)
+                           : mdcn::launch_gather_f32_t(p, gp, xt, on, mn, gcol, stream);
             });
         if (err == hipSuccess)
             err = rec.run(mdcn::K_BWD_WEIGHT_GEMM, [&] {
                 if (l.wsplit == 0)
                     return mdcn::launch_bwd_weight_gemm(p, l, gn, col, wacc, stream);
-                // columns [P][Kp] -> [Kp][P] (into the column-gradient buffer),
-                // then per pixel chunk s: part[s][m][kk] = sum over the chunk's
-                // pixels of g[m][p] * colT[kk][p], then summed into wacc
+                // per pixel chunk s of the transposed columns [Kp][P] (in the
+                // column-gradient buffer): part[s][m][kk] = sum over the
+                // chunk's pixels of g[m][p] * colT[kk][p], then summed into wacc
                 const int64_t S = l.wsplit, pc = p.P / S;
-                hipError_t r = mdcn::launch_to_nhwc(pcol, 1, col, gcol, stream);
-                if (r != hipSuccess)
-                    return r;
+                hipError_t r = hipSuccess;
                 Problem pw = p;
                 pw.G = S; pw.Mg = p.Co; pw.Co = S * p.Co; pw.P = l.Kp;
                 Plan wp{};

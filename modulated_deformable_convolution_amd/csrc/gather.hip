@@ -244,6 +244,146 @@ __global__ __launch_bounds__(kThreads) void deform_gather_kernel(const T *__rest
     }
 }
 
+// The backward's columns of one image, transposed: colT[g][k*Cg + c'][pix]
+// (fp32, pixels contiguous), the layout the weight gradient's GEMM reads
+// (contraction over pixels).  A workgroup owns 64 consecutive pixels, one
+// tap and a slice of up to 64 channels of one group: phase 1 as above (the
+// geometry of its pixels), phase 2 samples them channel vector by channel
+// vector as the gather does (corner reads of whole 16-byte vectors) into an
+// LDS tile [pixel][channel] (row pitch CS + 4 floats), phase 3 writes the
+// tile out row by row (a wave stores 64 pixels of one channel row).  Rows
+// kk in [Kg, Kp) are zeroed by the tap-0 workgroups.
+constexpr int kTPX = 64;         // pixels per workgroup of the transposed gather
+constexpr int kTCS = 64;         // channels per slice
+
+template <typename T, bool VECTOR>
+__global__ __launch_bounds__(kThreads) void deform_gather_t_kernel(const T *__restrict__ xt,
+                                                                   const T *__restrict__ off,
+                                                                   const T *__restrict__ msk,
+                                                                   float *__restrict__ colT,
+                                                                   GatherArgs a, int slices)
+{
+    constexpr int VEC = VECTOR ? 16 / int(sizeof(T)) : 1;
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    Geo *geo = reinterpret_cast<Geo *>(lds_raw);                    // nq * kTPX entries
+    float *tile = reinterpret_cast<float *>(lds_raw + size_t(a.nq) * kTPX * sizeof(Geo));
+
+    uint32_t b = xcd_swizzle(blockIdx.x, gridDim.x);
+    const int ptile = __builtin_amdgcn_readfirstlane(int(b % uint32_t(a.tiles)));
+    b /= uint32_t(a.tiles);
+    const int sl = __builtin_amdgcn_readfirstlane(int(b % uint32_t(slices)));
+    b /= uint32_t(slices);
+    const int k = __builtin_amdgcn_readfirstlane(int(b % uint32_t(a.K)));
+    const int g = __builtin_amdgcn_readfirstlane(int(b / uint32_t(a.K)));
+    const int p0 = ptile * kTPX;
+    const int np = min(kTPX, a.P - p0);
+    const int c_lo = sl * kTCS;                          // channel slice within the group
+    const int cs = min(kTCS, a.Cg - c_lo);
+    const int pitch = kTCS + 4;
+    const int q0 = (g * a.Cg) / a.Cdg;
+
+    // Phase 1: geometry of (offset group q0+qq, tap k, pixel p0+pl)
+    const uint32_t elem_c = uint32_t(a.C) * uint32_t(sizeof(T));
+    for (int e = int(threadIdx.x); e < a.nq * kTPX; e += kThreads) {
+        const int pl = e % kTPX;
+        const int q = q0 + e / kTPX;
+        Geo gd;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            gd.off[s] = kOffImage;
+            gd.wt[s] = 0.0f;
+        }
+        if (pl < np && q < a.offC / (2 * a.K)) {
+            const int pix = p0 + pl;
+            const int ho = pix / a.Wo, wo = pix - (pix / a.Wo) * a.Wo;
+            const int i = k / a.kw, j = k - (k / a.kw) * a.kw;
+            const size_t ob = (size_t(q) * 2 * a.K + 2 * k) * a.P + pix;
+            const float oh = to_f32(off[ob]);
+            const float ow = to_f32(off[ob + a.P]);
+            const float m = to_f32(msk[(size_t(q) * a.K + k) * a.P + pix]);
+            const Taps tp = make_taps(ho * a.sh - a.ph + i * a.dh, wo * a.sw - a.pw + j * a.dw,
+                                      oh, ow, m, a.H, a.W);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                gd.off[s] = tp.valid[s] ? uint32_t(tp.idx[s]) * elem_c : kOffImage;
+                gd.wt[s] = tp.wt[s];
+            }
+        }
+        geo[e] = gd;
+    }
+    __syncthreads();
+
+    // Phase 2: (pixel, channel vector) items, channel vector fastest
+    const size_t img_bytes = size_t(a.H) * a.W * elem_c;
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(xt, uint32_t(img_bytes));
+    const int CV = cs / VEC;
+    for (int it = int(threadIdx.x); it < np * CV; it += kThreads) {
+        const int pl = it / CV, cv = it - (it / CV) * CV;
+        const int c = g * a.Cg + c_lo + cv * VEC;        // input channel
+        const Geo gd = geo[(c / a.Cdg - q0) * kTPX + pl];
+        const uint32_t cb = uint32_t(c) * uint32_t(sizeof(T));
+        float acc[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            acc[e] = 0.0f;
+        if constexpr (VECTOR) {
+            uint4 v[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t o = gd.off[s] == kOffImage ? kOffImage : gd.off[s] + cb;
+                const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
+                __builtin_memcpy(&v[s], &r, 16);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                vec_fma<T>(acc, v[s], gd.wt[s]);
+        } else {
+            const char *img = reinterpret_cast<const char *>(xt);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (gd.off[s] != kOffImage)
+                    acc[0] = fmaf(gd.wt[s],
+                                  to_f32(*reinterpret_cast<const T *>(img + gd.off[s] + cb)),
+                                  acc[0]);
+        }
+        float *row = tile + pl * pitch + cv * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            if constexpr (VEC >= 4)
+                *reinterpret_cast<float4 *>(row + e) =
+                    make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+        }
+        if constexpr (VEC < 4)
+            row[0] = acc[0];
+    }
+    __syncthreads();
+
+    // Phase 3: channel rows out, 64 pixels a wave; a lane reads four
+    // channels of its pixel at once (16 lanes of a 16-byte read hit 16
+    // distinct bank groups: the row pitch is 4 floats past a multiple of 64)
+    const int lane = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6;
+    float *dst = colT + size_t(g) * a.Kp * a.P + size_t(k * a.Cg + c_lo) * a.P + p0;
+    if (cs % 4 == 0) {
+        for (int c = wave * 4; c < cs; c += kThreads / 16) {
+            const float4 v = *reinterpret_cast<const float4 *>(tile + lane * pitch + c);
+            if (lane < np) {
+                dst[size_t(c) * a.P + lane] = v.x;
+                dst[size_t(c + 1) * a.P + lane] = v.y;
+                dst[size_t(c + 2) * a.P + lane] = v.z;
+                dst[size_t(c + 3) * a.P + lane] = v.w;
+            }
+        }
+    } else {
+        for (int c = wave; c < cs; c += kThreads / 64)
+            if (lane < np)
+                dst[size_t(c) * a.P + lane] = tile[lane * pitch + c];
+    }
+    if (k == 0 && sl == 0)
+        for (int r = a.Kg + wave; r < a.Kp; r += kThreads / 64)
+            if (lane < np)
+                colT[size_t(g) * a.Kp * a.P + size_t(r) * a.P + p0 + lane] = 0.0f;
+}
+
 template <typename T, typename O>
 hipError_t gather_t(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
                     const void *offset, const void *mask, void *col, hipStream_t s)
@@ -298,6 +438,60 @@ hipError_t launch_gather_f32(const Problem &p, const Plan &plan, int64_t cnt, co
     case MDCN_F32: return gather_t<float, float>(p, plan, cnt, xt, offset, mask, col, stream);
     case MDCN_F16: return gather_t<half_t, float>(p, plan, cnt, xt, offset, mask, col, stream);
     case MDCN_BF16: return gather_t<bf16_t, float>(p, plan, cnt, xt, offset, mask, col, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_f32_t(const Problem &p, const Plan &plan, const void *xt,
+                               const void *offset, const void *mask, float *colT,
+                               hipStream_t stream)
+{
+    GatherArgs a{};
+    a.Cg = int(p.Cg); a.Cdg = int(p.Cdg); a.C = int(p.C);
+    a.H = int(p.H); a.W = int(p.W); a.Wo = int(p.Wo); a.kw = int(p.kw); a.K = int(p.K);
+    a.P = int(p.P);
+    a.sh = int(p.sh); a.sw = int(p.sw); a.ph = int(p.ph); a.pw = int(p.pw);
+    a.dh = int(p.dh); a.dw = int(p.dw);
+    a.offC = int(2 * p.DG * p.K); a.mskC = int(p.DG * p.K);
+    a.Kg = int(p.Kg); a.Kp = int(plan.Kp); a.cnt = 1;
+    a.nq = int(std::min<int64_t>(p.DG, (p.Cg + p.Cdg - 1) / p.Cdg + 1));
+    a.tiles = int((p.P + kTPX - 1) / kTPX);
+    const int slices = int((p.Cg + kTCS - 1) / kTCS);
+    const size_t lds = size_t(a.nq) * kTPX * sizeof(Geo) + size_t(kTPX) * (kTCS + 4) * 4;
+    if (lds > size_t(160) * 1024)
+        return hipErrorInvalidValue;
+    const uint64_t blocks = uint64_t(p.G) * p.K * slices * a.tiles;
+    if (blocks > 0x7fffffffull)
+        return hipErrorInvalidValue;
+    const dim3 grid{unsigned(blocks), 1u, 1u};
+    auto run = [&](auto tag) -> hipError_t {
+        using T = decltype(tag);
+        constexpr int V = 16 / sizeof(T);
+        auto kv = deform_gather_t_kernel<T, true>;
+        auto ks = deform_gather_t_kernel<T, false>;
+        const bool vec = (p.Cg % V == 0) && (p.Cdg % V == 0) && (p.Cg >= kTCS || p.Cg % V == 0);
+        static const hipError_t av = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(kv), hipFuncAttributeMaxDynamicSharedMemorySize,
+            160 * 1024);
+        static const hipError_t as = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(ks), hipFuncAttributeMaxDynamicSharedMemorySize,
+            160 * 1024);
+        if (av != hipSuccess || as != hipSuccess)
+            return av != hipSuccess ? av : as;
+        if (vec)
+            hipLaunchKernelGGL(kv, grid, dim3(kThreads), lds, stream, static_cast<const T *>(xt),
+                               static_cast<const T *>(offset), static_cast<const T *>(mask),
+                               colT, a, slices);
+        else
+            hipLaunchKernelGGL(ks, grid, dim3(kThreads), lds, stream, static_cast<const T *>(xt),
+                               static_cast<const T *>(offset), static_cast<const T *>(mask),
+                               colT, a, slices);
+        return hipGetLastError();
+    };
+    switch (p.dtype) {
+    case MDCN_F32: return run(float{});
+    case MDCN_F16: return run(half_t{});
+    case MDCN_BF16: return run(bf16_t{});
     }
     return hipErrorInvalidValue;
 }

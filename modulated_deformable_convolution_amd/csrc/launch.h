@@ -84,6 +84,11 @@ hipError_t launch_gather(const Problem &p, const Plan &plan, int64_t cnt, const 
 hipError_t launch_gather_f32(const Problem &p, const Plan &plan, int64_t cnt, const void *xt,
                              const void *offset, const void *mask, float *col,
                              hipStream_t stream);
+// The same fp32 columns of one image, transposed: colT[g][kk][pix] (rows kk
+// in [Kg, Kp) zero).
+hipError_t launch_gather_f32_t(const Problem &p, const Plan &plan, const void *xt,
+                               const void *offset, const void *mask, float *colT,
+                               hipStream_t stream);
 
 // out[n][g*Mg + m][pix] = sum_kk wpack[g][m][kk] * col[g][n*P + pix][kk] (+ bias);
 // The same fp32 GEMM (no bias) with explicit operand geometry: each row of A
