@@ -18,6 +18,7 @@
 // NHWC buffer, transposed to NCHW per image), and small fill, reduce and
 // permute kernels.  The images are processed one at a time.
 #include <algorithm>
+#include <cstdlib>
 
 #include "device_common.h"
 #include "launch.h"
@@ -644,12 +645,20 @@ BackwardLayout backward_layout(const Problem &p)
     l.mfma_col = p.dtype == MDCN_F32 && p.G == 1 && p.Co % 32 == 0 && p.P >= 1;
     // the weight gradient on the MFMA GEMM as well: the image's pixels split
     // into S chunks of Pc (a multiple of 32 floats = whole 128-byte K steps,
-    // at most 512) that run as the GEMM's groups; the columns transposed to
-    // [Kp][P] (in the column-gradient buffer, written later) and the S
-    // partial [Co][Kp] results (in the column buffer, consumed by then)
+    // at most 1024; MDCN_BWD_PC_MAX=<floats> lowers the cap) that run as the
+    // GEMM's groups; the columns gathered transposed, [Kp][P] (into the
+    // column-gradient buffer, written later), and the S partial [Co][Kp]
+    // results (in the column buffer).  (OCDNet-like stage, P = 25600:
+    // Pc = 1024 takes 270 us, 512 307 us, 640-1600 331-411 us.)
     l.wsplit = 0;
     if (l.mfma_col && p.P % 32 == 0) {
-        for (int64_t d = 16; d >= 1; --d) {
+        int64_t dmax = 32;
+        if (const char *env = std::getenv("MDCN_BWD_PC_MAX")) {
+            const int64_t v = std::atoll(env) / 32;
+            if (v >= 1 && v <= 256)
+                dmax = v;
+        }
+        for (int64_t d = dmax; d >= 1; --d) {
             const int64_t pc = 32 * d;
             if (p.P % pc == 0 && (p.P / pc) * p.Co <= p.P) {
                 l.wsplit = p.P / pc;

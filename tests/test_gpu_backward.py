@@ -46,8 +46,8 @@ CASES = {
                                    deformable_groups=2, offset_dist=("uniform", 6.0),
                                    mask_dist=("uniform_zeros", 0.2)),
     # fp32: both contractions on the MFMA GEMM, the weight gradient in two
-    # pixel chunks of 512 (P = 1024)
-    "mfma_split": Problem(N=2, C=32, Co=64, H=32, W=32, offset_dist=("normal", 1.0)),
+    # pixel chunks of 1024 (P = 2048)
+    "mfma_split": Problem(N=2, C=32, Co=64, H=32, W=64, offset_dist=("normal", 1.0)),
 }
 
 
