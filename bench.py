@@ -106,6 +106,7 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
     Kp8 = (Kg + 127) // 128 * 128          # FP8 path: one byte per value, 128-byte K steps
     col_img8 = G * P * Kp8
     wq_bytes = pr.Co * Kp8 + 4 * pr.Co     # E4M3 weight and fp32 row scales
+    wqw_bytes = pr.Co * (Cg // 16) * 144 + 4 * pr.Co   # windowed FP8: E4M3 chunk blocks, scales
 
     def per_launch(name, cnt):
         if name == "pack_weight":
@@ -135,6 +136,15 @@ def kernel_model(pr, dtype, plan_chunk, plan_geo=False):
         if name in ("fused_gather_gemm", "window_gather_gemm"):
             # x (NHWC copy), offsets and masks read once, output written once
             return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + pr.Co * Kp * e
+                        + bias_bytes, flops=2 * cnt * pr.Co * Kg * P)
+        if name == "prep_blocks_fp8":
+            # the weight rounded to E4M3 chunk blocks and the first chunk's x
+            # moved to 8-channel blocks, in one launch
+            first = min(plan_chunk, pr.N)
+            return dict(bytes=w_bytes + wqw_bytes + 2 * first * x_img, flops=0)
+        if name == "window_gather_gemm_fp8":
+            # as window_gather_gemm, with the E4M3 weight
+            return dict(bytes=cnt * (x_img + off_img + msk_img + out_img) + wqw_bytes
                         + bias_bytes, flops=2 * cnt * pr.Co * Kg * P)
         if name == "prep_nhwc_fp8":
             # the weight rounded to E4M3 and the first chunk's x moved, in one launch
@@ -178,9 +188,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "gather_gemm", "fused",
                                                        "window", "depthwise", "direct",
-                                                       "gather_gemm_fp8"],
+                                                       "gather_gemm_fp8", "window_fp8"],
                     help="computation path (default: the library's choice; gather_gemm_fp8 "
-                         "computes with E4M3 operands, a reduced-precision result)")
+                         "and window_fp8 compute with E4M3 operands, a reduced-precision "
+                         "result)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph that holds one captured forward (the "
                          "launch mode for small problems) instead of eager forwards")
@@ -232,8 +243,9 @@ def main(argv=None) -> int:
     path = {"auto": mdcn.MDCN_PATH_AUTO, "gather_gemm": mdcn.MDCN_PATH_GATHER_GEMM,
             "fused": mdcn.MDCN_PATH_FUSED, "window": mdcn.MDCN_PATH_WINDOW,
             "depthwise": mdcn.MDCN_PATH_DEPTHWISE, "direct": mdcn.MDCN_PATH_DIRECT,
-            "gather_gemm_fp8": mdcn.MDCN_PATH_GATHER_GEMM_FP8}[args.path]
-    fp8 = args.path == "gather_gemm_fp8"
+            "gather_gemm_fp8": mdcn.MDCN_PATH_GATHER_GEMM_FP8,
+            "window_fp8": mdcn.MDCN_PATH_WINDOW_FP8}[args.path]
+    fp8 = args.path in ("gather_gemm_fp8", "window_fp8")
     op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups, pr.deformable_groups,
                           path=path)
     code = mdcn.dtype_code(g["x"].dtype)
@@ -321,7 +333,7 @@ def main(argv=None) -> int:
         cnt = (pr.N / max(1, launches_per_step)
                if name in ("direct", "to_nhwc", "to_channel_blocks", "deform_gather", "gemm_bias",
                            "fused_gather_gemm", "fused_one_launch", "window_gather_gemm",
-                           "depthwise_geometry",
+                           "window_gather_gemm_fp8", "depthwise_geometry",
                            "depthwise_direct", "deform_gather_fp8", "gemm_fp8_bias")
                else 0)
         m = model(name, cnt)
@@ -337,7 +349,7 @@ def main(argv=None) -> int:
     t_hbm = dk["algo_bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = dk["algo_flops_per_launch"] / (peak_tf * 1e12)
     uses_mfma = dominant in ("gemm_bias", "fused_gather_gemm", "fused_one_launch",
-                             "window_gather_gemm", "gemm_fp8_bias")
+                             "window_gather_gemm", "window_gather_gemm_fp8", "gemm_fp8_bias")
     if uses_mfma and t_mfma > t_hbm:
         roofline = dict(bound="mfma", achieved=round(dk["tflops"], 2), peak=peak_tf,
                         unit="TFLOP/s", frac=round(dk["tflops"] / peak_tf, 4), traffic=None)

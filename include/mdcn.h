@@ -121,7 +121,7 @@ typedef enum mdcn_path {
                                   are; for problems of at most 2^20 multiply-adds (the
                                   automatic choice there), any problem when forced; no
                                   workspace [plugin guide §五 steps 1-3]                   */
-    MDCN_PATH_GATHER_GEMM_FP8 = 6 /* REDUCED PRECISION, never chosen automatically: gather +
+    MDCN_PATH_GATHER_GEMM_FP8 = 6, /* REDUCED PRECISION, never chosen automatically: gather +
                                   GEMM with both contraction operands in OCP FP8 E4M3 and
                                   fp32 sums on the gfx950 FP8 matrix cores.  Each column
                                   value (the modulated bilinear sample) is saturated to
@@ -135,6 +135,21 @@ typedef enum mdcn_path {
                                   other paths by the E4M3 rounding (about 2^-4 relative per
                                   operand) [plugin guide §五 steps 1-3 with 8-bit operands;
                                   the FP8 format is not on the pages]                       */
+    MDCN_PATH_WINDOW_FP8 = 7   /* REDUCED PRECISION, never chosen automatically: the
+                                  windowed kernel (MDCN_PATH_WINDOW, same tiles, window
+                                  and eligibility) with the E4M3 rounding of
+                                  MDCN_PATH_GATHER_GEMM_FP8: each modulated bilinear
+                                  sample is computed in fp32 from the LDS window,
+                                  saturated to +-448 and rounded to E4M3; the weight rows
+                                  are scaled by 2^e and rounded likewise; the products are
+                                  summed in fp32 on the FP8 matrix cores (four taps of 16
+                                  channels per 64-deep instruction, the ninth tap of a
+                                  16-channel chunk on the 16-deep one) and each output is
+                                  2^-e * sum + bias, rounded once to the input dtype.  No
+                                  column buffer.  Results agree with
+                                  MDCN_PATH_GATHER_GEMM_FP8 up to the order of the fp32
+                                  sums [plugin guide §五 steps 1-3 with 8-bit operands; the
+                                  FP8 format is not on the pages]                          */
 } mdcn_path;
 
 typedef struct mdcn_op mdcn_op;
@@ -306,7 +321,10 @@ mdcn_status mdcn_trace_read(mdcn_trace *trace, int32_t i, int32_t *kernel_id, fl
  * "gemm_bias", "fused_gather_gemm", "window_gather_gemm",
  * "depthwise_geometry", "depthwise_direct", "direct"; for the FP8 path
  * "prep_nhwc_fp8" (the weight rounded to E4M3 and the first chunk of x to
- * channels-last), "deform_gather_fp8", "gemm_fp8_bias"; for the backward
+ * channels-last), "deform_gather_fp8", "gemm_fp8_bias"; for the windowed
+ * FP8 path "prep_blocks_fp8" (the weight rounded to E4M3 in the windowed
+ * kernel's chunk layout and the first chunk of x to 8-channel blocks) and
+ * "window_gather_gemm_fp8"; for the backward
  * "bwd_zero", "bwd_bias", "bwd_weight_gemm", "bwd_col_gemm", "bwd_sample",
  * "bwd_to_nchw", "bwd_weight_out" (with "pack_weight", "to_nhwc" and
  * "deform_gather"); "pack_weight" (outside the backward) and

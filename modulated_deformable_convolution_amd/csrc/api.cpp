@@ -190,7 +190,10 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
     void *col = ws + plan.col_off;
     uint32_t *win_flags = reinterpret_cast<uint32_t *>(ws + plan.flag_off);
     const bool fp8 = plan.path == Path::GatherGemmFp8;
-    float *wscale = fp8 ? reinterpret_cast<float *>(ws + plan.wpack_off + plan.wscale_off) : nullptr;
+    const bool windowed = plan.path == Path::Window || plan.path == Path::WindowFp8;
+    float *wscale = (fp8 || plan.path == Path::WindowFp8)
+                        ? reinterpret_cast<float *>(ws + plan.wpack_off + plan.wscale_off)
+                        : nullptr;
     // The weight is repacked (and the window path's flags cleared) in the
     // same launch as the first chunk's x layout change.
     if (plan.path == Path::Fused && plan.chunk >= p.N) {
@@ -212,18 +215,16 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
         char *outc = static_cast<char *>(out) + size_t(n0) * out_img;
         if (n0 == 0)
             err = rec.run(plan.path == Path::Window          ? mdcn::K_PREP_BLOCKS
+                          : plan.path == Path::WindowFp8     ? mdcn::K_PREP_BLOCKS_FP8
                           : plan.path == Path::GatherGemmFp8 ? mdcn::K_PREP_NHWC_FP8
                                                              : mdcn::K_PREP_NHWC,
                           [&] {
                               return mdcn::launch_prep(p, plan, cnt, xc, xt, weight, wpack,
                                                        win_flags,
-                                                       plan.path == Path::Window
-                                                           ? int(plan.win_slots) + 1
-                                                           : 0,
-                                                       wscale,
-                                                       stream);
+                                                       windowed ? int(plan.win_slots) + 1 : 0,
+                                                       wscale, stream);
                           });
-        else if (plan.path == Path::Window)
+        else if (windowed)
             err = rec.run(mdcn::K_TO_BLOCKS,
                           [&] { return mdcn::launch_to_channel_blocks(p, cnt, xc, xt, stream); });
         else
@@ -239,16 +240,17 @@ mdcn_status forward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dims
                 return MDCN_E_LAUNCH;
             continue;
         }
-        if (plan.path == Path::Window) {
+        if (windowed) {
             // every launch of this forward publishes partial sums with its own
             // flag value (the flags were zeroed with the weight packing)
             const mdcn::WindowScratch scratch{reinterpret_cast<float *>(ws + plan.part_off),
                                               win_flags, int(plan.win_slots),
                                               int(n0 / plan.chunk) + 1};
-            err = rec.run(mdcn::K_WINDOW, [&] {
-                return mdcn::launch_window(p, plan, cnt, wpack, xt, oc, mc, bias, outc, scratch,
-                                           stream);
-            });
+            err = rec.run(plan.path == Path::WindowFp8 ? mdcn::K_WINDOW_FP8 : mdcn::K_WINDOW,
+                          [&] {
+                              return mdcn::launch_window(p, plan, cnt, wpack, wscale, xt, oc, mc,
+                                                         bias, outc, scratch, stream);
+                          });
             if (err != hipSuccess)
                 return MDCN_E_LAUNCH;
             continue;
@@ -476,7 +478,8 @@ mdcn_status create_impl(const int32_t stride[2], const int32_t padding[2],
         return st;
     if (path != MDCN_PATH_AUTO && path != MDCN_PATH_GATHER_GEMM &&
         path != MDCN_PATH_DEPTHWISE && path != MDCN_PATH_FUSED && path != MDCN_PATH_WINDOW &&
-        path != MDCN_PATH_DIRECT && path != MDCN_PATH_GATHER_GEMM_FP8)
+        path != MDCN_PATH_DIRECT && path != MDCN_PATH_GATHER_GEMM_FP8 &&
+        path != MDCN_PATH_WINDOW_FP8)
         return MDCN_E_PATH;
     mdcn_op *op = new (std::nothrow) mdcn_op;
     if (!op)
@@ -588,7 +591,8 @@ mdcn_status mdcn_forward_check(const mdcn_op *op, mdcn_dtype dtype, const int64_
         if (st != MDCN_OK)
             return st;
         hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-        if (plan.path != Path::Window || p.N == 0 || p.P == 0 || plan.ws_bytes == 0)
+        if ((plan.path != Path::Window && plan.path != Path::WindowFp8) || p.N == 0 ||
+            p.P == 0 || plan.ws_bytes == 0)
             return hipStreamSynchronize(stream) == hipSuccess ? MDCN_OK : MDCN_E_LAUNCH;
         if (!workspace)
             return MDCN_E_NULL;
@@ -791,6 +795,8 @@ const char *mdcn_kernel_name(int32_t kernel_id)
     case mdcn::K_BWD_WEIGHT_OUT: return "bwd_weight_out";
     case mdcn::K_BWD_TO_NCHW: return "bwd_to_nchw";
     case mdcn::K_FUSED_ONE: return "fused_one_launch";
+    case mdcn::K_PREP_BLOCKS_FP8: return "prep_blocks_fp8";
+    case mdcn::K_WINDOW_FP8: return "window_gather_gemm_fp8";
     }
     return "?";
 }
@@ -850,10 +856,11 @@ mdcn_status mdcn_describe_plan(const mdcn_op *op, mdcn_dtype dtype, const int64_
                           (long long)p.G, (long long)p.Mg, (long long)p.P,
                           int(plan.fused_tile), plan.ws_bytes, plan.wpack_bytes,
                           plan.xt_bytes_per_image);
-        else if (plan.path == Path::Window)
+        else if (plan.path == Path::Window || plan.path == Path::WindowFp8)
             std::snprintf(buf, len,
-                          "path=window chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld tile=%d "
+                          "path=%s chunk=%lld Kg=%lld Kp=%lld G=%lld Mg=%lld P=%lld tile=%d "
                           "margin=%lld slots=%lld ws=%zu (wpack=%zu xt/img=%zu)",
+                          plan.path == Path::WindowFp8 ? "window_fp8" : "window",
                           (long long)plan.chunk, (long long)p.Kg, (long long)plan.Kp,
                           (long long)p.G, (long long)p.Mg, (long long)p.P, int(plan.win_tile),
                           (long long)plan.win_margin, (long long)plan.win_slots, plan.ws_bytes,

@@ -45,6 +45,14 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
     return uint32_t(w);
 }
 
+// The same without the saturation, for values already within +-448 (or NaN).
+__device__ __forceinline__ uint32_t pack4_e4m3_unsat(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return uint32_t(w);
+}
+
 __device__ __forceinline__ e4m3_t to_e4m3(float v)
 {
     return e4m3_t(__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v), 0.0f, 0, false) & 0xff);

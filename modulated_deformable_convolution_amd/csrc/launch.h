@@ -34,7 +34,9 @@ enum KernelId : int32_t {
     K_BWD_WEIGHT_OUT = 21,
     K_BWD_TO_NCHW = 22,
     K_FUSED_ONE = 23,
-    K_COUNT = 24
+    K_PREP_BLOCKS_FP8 = 24,
+    K_WINDOW_FP8 = 25,
+    K_COUNT = 26
 };
 
 // Compute units of the current device (cached per device; 1 if unknown).
@@ -142,9 +144,13 @@ struct WindowScratch {
     int slots;
     int epoch;
 };
+// plan.path == Path::WindowFp8: the E4M3 variant, from the E4M3 chunk blocks
+// and the row scales `wscale` (launch_prep with that plan); otherwise wscale
+// is unused.
 hipError_t launch_window(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                         const void *xt, const void *offset, const void *mask, const void *bias,
-                         void *out, const WindowScratch &ws, hipStream_t stream);
+                         const float *wscale, const void *xt, const void *offset,
+                         const void *mask, const void *bias, void *out, const WindowScratch &ws,
+                         hipStream_t stream);
 
 // Depthwise sampling geometry of cnt images: for each (image, offset group,
 // tap, pixel) a 16-byte record geo[((img*DG + q)*K + k)*P + pix] = {staged

@@ -445,6 +445,11 @@ mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
             return MDCN_E_PATH;
         *out = Path::Window;
         return MDCN_OK;
+    case MDCN_PATH_WINDOW_FP8:
+        if (!window_eligible(p))
+            return MDCN_E_PATH;
+        *out = Path::WindowFp8;
+        return MDCN_OK;
     case MDCN_PATH_FUSED:
         if (!fused_eligible(p))
             return MDCN_E_PATH;
@@ -504,10 +509,18 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
     }
     plan.Kp = round_up(p.Kg, 64);
     plan.wpack_off = 0;
-    if (plan.path == Path::Fused || plan.path == Path::Window) {
+    const bool windowed = plan.path == Path::Window || plan.path == Path::WindowFp8;
+    if (plan.path == Path::Fused || windowed) {
         // Workspace: packed weight + the chunk's images in NHWC.  A chunk's
         // NHWC bytes stay below 2^31 (one buffer range) and within 512 MiB.
         plan.wpack_bytes = align_up(size_t(p.G * p.Mg * plan.Kp) * p.elem, kAlign);
+        if (plan.path == Path::WindowFp8) {
+            // E4M3 chunk layout, then the row scales
+            plan.wscale_off = align_up(size_t(p.G * (p.Cg / 16) * p.Mg) *
+                                           size_t(kWindowFp8ChunkBytesPerRow),
+                                       kAlign);
+            plan.wpack_bytes = plan.wscale_off + align_up(size_t(p.Co) * sizeof(float), kAlign);
+        }
         plan.xt_bytes_per_image = align_up(size_t(p.H * p.W * p.C) * p.elem, kAlign);
         plan.col_bytes_per_image = 0;
         const int64_t img = int64_t(plan.xt_bytes_per_image);
@@ -523,7 +536,7 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
         if (plan.path == Path::Fused && !choose_fused_tile(p, chunk, &plan.fused_tile))
             return MDCN_E_PATH;                 // fused_eligible said some tile fits
         plan.xt_off = plan.wpack_bytes;
-        if (plan.path == Path::Window) {
+        if (windowed) {
             if (!choose_window(p, &plan.win_tile, &plan.win_margin))
                 return MDCN_E_PATH;
             // the weight copies run 5 K steps ahead (the kernel's barrier
@@ -637,7 +650,7 @@ size_t min_workspace(const Problem &p, const Plan &plan)
         return 0;
     if (plan.path == Path::Depthwise)
         return plan.geo_bytes_per_image ? kAlign + plan.geo_bytes_per_image : 0;
-    if (plan.path == Path::Window) {
+    if (plan.path == Path::Window || plan.path == Path::WindowFp8) {
         const int64_t slots = std::min<int64_t>(kWindowSlots, plan.win_tiles_per_image);
         return kAlign + align_up(plan.wpack_bytes + plan.xt_bytes_per_image, kAlign) +
                size_t(slots) * kWindowSlotBytes + align_up(size_t(slots + 1) * 4, kAlign);

@@ -34,7 +34,14 @@ struct Problem {
     int64_t sh, sw, ph, pw, dh, dw;
 };
 
-enum class Path { GatherGemm, Depthwise, Fused, Window, Direct, GatherGemmFp8 };
+enum class Path { GatherGemm, Depthwise, Fused, Window, Direct, GatherGemmFp8, WindowFp8 };
+
+// The windowed kernel's E4M3 weight: per group and 16-channel chunk, 144 bytes
+// per output channel in three regions -- taps 0-3 [2 halves][2 parts][Mg][16
+// bytes] (part 0: taps 0 and 1, part 1: taps 2 and 3), taps 4-7 likewise,
+// tap 8 [2 halves][Mg][8 bytes] -- each 8-byte piece the E4M3 values of
+// channels 8h..8h+7 of the chunk at one tap.
+constexpr int64_t kWindowFp8ChunkBytesPerRow = 144;
 
 // Workgroup tile of the GEMM (rows of the packed weight x columns) and its
 // wave grid; every wave owns a block of 32x32 accumulator tiles.
@@ -88,13 +95,15 @@ constexpr uint32_t kWindowGaveUp = 1u;
 //   fused:         [packed weight: G x Mg x Kp] [x in NHWC: chunk images]
 //   window:        [packed weight] [x in 8-channel blocks: chunk images]
 //                  [partial sums: slots x 256 KiB] [flags: slots x 4 bytes] [status: 4 bytes]
+//   window FP8:    as window, with the packed weight replaced by the E4M3 chunk
+//                  layout (G x Cg/16 x 144 x Mg bytes) and the Co fp32 row scales
 //   depthwise:     [sampling geometry: chunk images x DG x K x 5 x P words]
 struct Plan {
     Path path;
     int64_t chunk;               // images per pass through gather + GEMM
     int64_t Kp;                  // contraction length padded to 128 bytes (64 or 32 elements; FP8: 128)
     size_t wpack_off, wpack_bytes;   // (FP8: the weight bytes and the row scales after them)
-    size_t wscale_off;           // FP8: offset of the Co fp32 row scales
+    size_t wscale_off;           // FP8 paths: offset of the Co fp32 row scales in the weight area
     size_t xt_off, xt_bytes_per_image;
     size_t col_off, col_bytes_per_image;
     size_t geo_bytes_per_image;  // depthwise: sampling geometry of one image (0: none)

@@ -215,21 +215,15 @@ __device__ __forceinline__ void pack8(const T *__restrict__ w, T *__restrict__ w
         dst[j] = v.q[j];
 }
 
-// The FP8 path's weight, one workgroup (256 threads) per output channel co:
-// the row's exponent e, the largest integer with max|w[co]| * 2^e <= 448
-// (0 for a row with no nonzero finite maximum; clamped to [-126, 126]),
-// wq[co][kk] = E4M3(w * 2^e) in tap-major order (kk = k*Cg + c', zero for
-// kk >= Kg) and wscale[co] = 2^-e, which the GEMM epilogue applies to the
-// row's sums.  Scaling by a power of two is exact, so the only rounding is
-// E4M3's own.  `red` is 4 floats of LDS.
+// The exponent e of an FP8 weight row: the largest integer with
+// max|row| * 2^e <= 448 (0 for a row with no nonzero finite maximum; clamped
+// to [-126, 126]).  One workgroup (256 threads) per row, contiguous reads;
+// `red` is 4 floats of LDS.
 template <typename T>
-__device__ __forceinline__ void quantize_row(const T *__restrict__ w, e4m3_t *__restrict__ wq,
-                                             float *__restrict__ wscale, int co, int Kg, int Kp,
-                                             int Cg, int K, float *red)
+__device__ __forceinline__ int row_exponent(const T *__restrict__ row, int Kg, float *red)
 {
-    const T *row = w + size_t(co) * Kg;              // weight [Co][Cg][kh][kw]: Kg per row
     float mx = 0.0f;
-    for (int t = int(threadIdx.x); t < Kg; t += 256)  // contiguous reads
+    for (int t = int(threadIdx.x); t < Kg; t += 256)
         mx = fmaxf(mx, fabsf(to_f32(row[t])));        // fmaxf skips NaN
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1)
@@ -245,6 +239,21 @@ __device__ __forceinline__ void quantize_row(const T *__restrict__ w, e4m3_t *__
         e = (f <= 0.875f) ? 9 - ex : 8 - ex;          // 448 = 0.875 * 2^9
         e = min(126, max(-126, e));
     }
+    return e;
+}
+
+// The FP8 path's weight, one workgroup (256 threads) per output channel co:
+// the row's exponent e (row_exponent), wq[co][kk] = E4M3(w * 2^e) in
+// tap-major order (kk = k*Cg + c', zero for kk >= Kg) and wscale[co] = 2^-e,
+// which the GEMM epilogue applies to the row's sums.  Scaling by a power of
+// two is exact, so the only rounding is E4M3's own.
+template <typename T>
+__device__ __forceinline__ void quantize_row(const T *__restrict__ w, e4m3_t *__restrict__ wq,
+                                             float *__restrict__ wscale, int co, int Kg, int Kp,
+                                             int Cg, int K, float *red)
+{
+    const T *row = w + size_t(co) * Kg;              // weight [Co][Cg][kh][kw]: Kg per row
+    const int e = row_exponent(row, Kg, red);
     e4m3_t *dst = wq + size_t(co) * Kp;
     for (int kk = int(threadIdx.x); kk < Kp; kk += 256) {   // the row is in L1 by now
         e4m3_t q = 0;
@@ -259,13 +268,55 @@ __device__ __forceinline__ void quantize_row(const T *__restrict__ w, e4m3_t *__
         wscale[co] = ldexpf(1.0f, -e);
 }
 
+// The windowed FP8 kernel's weight, one workgroup per output channel
+// co = g*Mg + m (3x3 taps): the same exponent and rounding as quantize_row,
+// written per 16-channel chunk c as 144 bytes of the chunk's block
+// [G][Cg/16][region]: an 8-byte piece (channels 16c + 8h .. +7 at tap k) goes
+// to region k / 4 for k < 8, laid out [h][part][Mg][16 bytes] with part
+// (k % 4) / 2 and the piece at byte 8 * (k % 2) of the 16, and to region 2,
+// [h][Mg][8 bytes], for tap 8.  One thread per piece: eight loads and one
+// 8-byte store.
+template <typename T>
+__device__ __forceinline__ void quantize_row_window(const T *__restrict__ w,
+                                                    e4m3_t *__restrict__ wq,
+                                                    float *__restrict__ wscale, int co, int Kg,
+                                                    int Cg, int Mg, float *red)
+{
+    constexpr int K = 9;
+    const T *row = w + size_t(co) * Kg;
+    const int e = row_exponent(row, Kg, red);
+    const int g = co / Mg, m = co - g * Mg;
+    const int nch = Cg / 16;
+    for (int t = int(threadIdx.x); t < nch * 2 * K; t += 256) {
+        const int k = t % K;
+        const int ch = t / K;                         // 8-channel piece of the row
+        const int c = ch >> 1, h = ch & 1;
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = ldexpf(to_f32(row[(ch * 8 + i) * K + k]), e);
+        const uint2 q = make_uint2(pack4_e4m3(v[0], v[1], v[2], v[3]),
+                                   pack4_e4m3(v[4], v[5], v[6], v[7]));
+        const size_t blk = (size_t(g) * nch + c) * size_t(Mg) * 144;
+        const size_t o = k < 8 ? blk + size_t(k / 4) * 64 * Mg +
+                                     (size_t(h * 2 + (k % 4) / 2) * Mg + m) * 16 +
+                                     size_t(k % 2) * 8
+                               : blk + size_t(128) * Mg + (size_t(h) * Mg + m) * 8;
+        *reinterpret_cast<uint2 *>(wq + o) = q;
+    }
+    if (threadIdx.x == 0)
+        wscale[co] = ldexpf(1.0f, -e);
+}
+
 // Both set-up jobs of a forward in one launch (for small problems the
 // launches cost more than the work): the first `nt` workgroups transpose
 // x (VEC: register transpose units 4b .. 4b+3, one a wave; otherwise LDS
 // tile b -> (b % gx, b / gx % gy, b / (gx*gy))), the rest repack the
 // weight (PK 1: [G][Mg][Kp] tap-major; PK 2: the window path's step-major
 // planes, and its hand-over flags cleared; PK 3: the FP8 path's E4M3 rows
-// and scales, one workgroup per row).
+// and scales, one workgroup per row; PK 4: the windowed FP8 kernel's E4M3
+// chunk blocks and scales, one workgroup per row, and its hand-over flags
+// cleared).
 struct PrepArgs {
     const void *x;
     void *xt;
@@ -298,6 +349,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a)
     if constexpr (PK == 3) {
         quantize_row(static_cast<const T *>(a.w), static_cast<e4m3_t *>(a.wp), a.wscale,
                      b - a.nt, a.Kg, a.Kp, a.Cg, a.K, reinterpret_cast<float *>(&tile[0][0]));
+        return;
+    }
+    if constexpr (PK == 4) {
+        // one row a workgroup; workgroups past the last row only clear flags
+        const int r = b - a.nt;
+        const int t = r * 256 + int(threadIdx.x);
+        if (t < a.nflags)
+            a.flags[t] = 0u;
+        if (r < a.total)
+            quantize_row_window(static_cast<const T *>(a.w), static_cast<e4m3_t *>(a.wp),
+                                a.wscale, r, a.Kg, a.Cg, a.Mg,
+                                reinterpret_cast<float *>(&tile[0][0]));
         return;
     }
     // eight weight elements a thread (and, window path, one flag)
@@ -428,6 +491,14 @@ hipError_t prep_t(const Problem &p, const Plan &plan, int64_t cnt, const void *x
         a.Kp = int(plan.Kp);
         a.Kg = int(p.Kg);
         npack = p.Co * 256;                   // one workgroup per row
+    } else if constexpr (PK == 4) {
+        if (p.Cg % 16 != 0 || p.K != 9 || reinterpret_cast<uintptr_t>(wp) % 8 != 0)
+            return hipErrorInvalidValue;
+        a.total = int(p.Co);                  // rows
+        a.Kg = int(p.Kg);
+        a.Mg = int(p.Mg);
+        a.nflags = flags ? nflags : 0;
+        npack = std::max<int64_t>(p.Co * 256, a.nflags);   // one workgroup per row
     } else if constexpr (PK == 1) {
         a.total = int(p.Co * plan.Kp);
         a.Kp = int(plan.Kp);
@@ -468,6 +539,8 @@ hipError_t prep_dtype(const Problem &p, const Plan &plan, int64_t cnt, const voi
 {
     if (plan.path == Path::Window)
         return prep_t<T, true, 2>(p, plan, cnt, x, xt, w, wp, flags, nflags, nullptr, s);
+    if (plan.path == Path::WindowFp8)
+        return prep_t<T, true, 4>(p, plan, cnt, x, xt, w, wp, flags, nflags, wscale, s);
     if (plan.path == Path::GatherGemmFp8)
         return prep_t<T, false, 3>(p, plan, cnt, x, xt, w, wp, nullptr, 0, wscale, s);
     return prep_t<T, false, 1>(p, plan, cnt, x, xt, w, wp, flags, nflags, nullptr, s);
@@ -479,9 +552,9 @@ hipError_t launch_prep(const Problem &p, const Plan &plan, int64_t cnt, const vo
                        const void *weight, void *wpack, uint32_t *flags, int nflags,
                        float *wscale, hipStream_t stream)
 {
-    if (plan.path == Path::GatherGemmFp8 && !wscale)
+    if ((plan.path == Path::GatherGemmFp8 || plan.path == Path::WindowFp8) && !wscale)
         return hipErrorInvalidValue;
-    if (plan.path == Path::Window && p.C % 8 != 0)
+    if ((plan.path == Path::Window || plan.path == Path::WindowFp8) && p.C % 8 != 0)
         return hipErrorInvalidValue;
     switch (p.dtype) {
     case MDCN_F32:

@@ -116,6 +116,29 @@ static_assert(kWindowPixels % 64 == 0 && (2 * kWindowPixels / 64) % kWaves == 0,
               "window DMA covers whole wave instructions, none straddling the two planes");
 static_assert(kAStage % (1024 * kWaves) == 0, "A DMA covers whole wave instructions");
 
+// The E4M3 variant (F8) keeps one chunk's weight in LDS, in three slots that
+// the chunk's three MFMA groups read in turn: taps 0-3 and taps 4-7, each
+// [half h][16-byte part][256 rows][16 bytes] (part 0: taps 0 and 1 of the
+// row's 32 bytes, part 1: taps 2 and 3), and tap 8, [half h][256 rows][8 bytes].
+// Every part is the 8 channels 8h..8h+7 of one tap as E4M3 bytes.  The window
+// buffers, copy table and parked words follow the slots.
+constexpr int kF8Quad = 2 * 256 * 32;              // 16 KiB: four taps
+constexpr int kF8Single = 2 * 256 * 8;             // 4 KiB: the ninth tap
+constexpr int kF8Slots = 2 * kF8Quad + kF8Single;  // 36 KiB
+static_assert(kF8Quad % (1024 * kWaves) == 0 && kF8Single % (256 * kWaves) == 0,
+              "E4M3 weight DMA covers whole wave instructions");
+
+template <bool F8> struct WinLds {
+    static constexpr int win0 = F8 ? kF8Slots : kWin0;             // window buffer 0
+    static constexpr int woff = win0 + 2 * kWinBuf;                // window copy table
+    static constexpr int park = woff + kWinInstr * kThreads * 4;  // tile index per wave, flag
+    static constexpr int total = park + 256;
+    static constexpr int om = win0 + kWinBuf;                      // offsets and masks of a tile
+    static_assert(total <= int(kLdsBytes), "LDS budget");
+    static_assert(win0 % 1024 == 0, "window buffers start on a 1 KiB boundary");
+};
+static_assert(WinLds<false>::total == kLdsTotal && WinLds<false>::om == kOmOff, "layout");
+
 struct WinArgs {
     const void *A, *xt, *off, *msk, *bias;   // step-major weight, x blocks, offset, mask, bias|null
     void *out;
@@ -136,6 +159,7 @@ struct WinArgs {
     uint32_t off_bytes, msk_bytes; // offsets / masks of the chunk's images
     // unit range of each workgroup slot (slot j = run * per + index in run)
     uint32_t bounds[kWindowSlots + 1];
+    const float *wscale;           // F8: 2^-e of each output channel's weight row
 };
 static_assert(sizeof(WinArgs) <= 4096, "kernel arguments are at most 4 KiB");
 
@@ -265,7 +289,37 @@ __device__ __forceinline__ uint4 blend(const uint4 &c0, const uint4 &c1, const u
                       pack2<T>(acc[4], acc[5]), pack2<T>(acc[6], acc[7]));
 }
 
-template <typename T, int TH, int TW, int LEAD>
+// The same sample as `blend`, as 8 E4M3 bytes (channel 0 in the lowest
+// byte): the fp32 values saturated to +-448 -- only where some lane of the
+// wave holds a value beyond that (or an infinity; a NaN stays NaN) -- and
+// rounded to nearest even by the converter.
+template <typename T>
+__device__ __forceinline__ uint2 blend_e4m3(const uint4 (&c)[4], const float (&w)[4], float zero)
+{
+    Vec16<T> v0, v1, v2, v3;
+    v0.raw = c[0]; v1.raw = c[1]; v2.raw = c[2]; v3.raw = c[3];
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        acc[e] = fmaf(to_f32(v0.e[e]), w[0], zero);
+        acc[e] = fmaf(to_f32(v1.e[e]), w[1], acc[e]);
+        acc[e] = fmaf(to_f32(v2.e[e]), w[2], acc[e]);
+        acc[e] = fmaf(to_f32(v3.e[e]), w[3], acc[e]);
+    }
+    const float m = fmaxf(fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])),
+                                fmaxf(fabsf(acc[2]), fabsf(acc[3]))),
+                          fmaxf(fmaxf(fabsf(acc[4]), fabsf(acc[5])),
+                                fmaxf(fabsf(acc[6]), fabsf(acc[7]))));
+    if (__builtin_amdgcn_ballot_w64(m > 448.0f) != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] = sat_e4m3(acc[e]);
+    }
+    return make_uint2(pack4_e4m3_unsat(acc[0], acc[1], acc[2], acc[3]),
+                      pack4_e4m3_unsat(acc[4], acc[5], acc[6], acc[7]));
+}
+
+template <typename T, int TH, int TW, int LEAD, bool F8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void window_kernel(WinArgs args)
@@ -296,15 +350,16 @@ void window_kernel(WinArgs args)
     static_assert(LEAD == 5, "a barrier every third step needs a copy lead of 5 steps");
     constexpr int kAStages = 8;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
+    using L = WinLds<F8>;
 
     const uint32_t lds0 = lds_addr(smem);
-    uint32_t *woff_tab = reinterpret_cast<uint32_t *>(smem + kWoffOff);
+    uint32_t *woff_tab = reinterpret_cast<uint32_t *>(smem + L::woff);
 
     // zero areas of both window buffers (read by lanes whose sample is not
     // in the window); no copy ever writes them
     for (int i = int(threadIdx.x); i < 2 * kWinZero / 8; i += kThreads) {
         const int b = i / (kWinZero / 8), o = i - b * (kWinZero / 8);
-        *reinterpret_cast<uint2 *>(smem + kWin0 + b * kWinBuf + kWinZeroOff + o * 8) =
+        *reinterpret_cast<uint2 *>(smem + L::win0 + b * kWinBuf + kWinZeroOff + o * 8) =
             make_uint2(0u, 0u);
     }
 
@@ -369,9 +424,9 @@ void window_kernel(WinArgs args)
     }
     // per-wave LDS word that holds the tile index across the main loop, and
     // the word that says whether this tile's hand-over wait gave up
-    int *tile_park = reinterpret_cast<int *>(smem + kParkOff) +
+    int *tile_park = reinterpret_cast<int *>(smem + L::park) +
                      __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-    int *gave_up_l = reinterpret_cast<int *>(smem + kParkOff) + 32;
+    int *gave_up_l = reinterpret_cast<int *>(smem + L::park) + 32;
 
     for (;;) {
         // Every lane- and argument-derived value is derived afresh per tile
@@ -430,7 +485,7 @@ void window_kernel(WinArgs args)
                            : uint32_t(img * a->mskC + q * kTaps + plane - 2 * kTaps);
                 const uint32_t voff =
                     ok ? (chan * uint32_t(a->P) + uint32_t(ho * a->Wo + wo)) * 2u : kOOB;
-                dma4(lds0 + uint32_t(kOmOff + plane * 512 + (j & 1) * 256), is_off ? ro : rm,
+                dma4(lds0 + uint32_t(L::om + plane * 512 + (j & 1) * 256), is_off ? ro : rm,
                      voff, 0u);
             }
         }
@@ -455,12 +510,28 @@ void window_kernel(WinArgs args)
                                                     uint32_t(gr * a->W + gc) * 16
                                               : kOOB;
         }
-        uint32_t aoff[kAInstr];
+        // (F8: entries 0, 1 for the four-tap slots, 16-byte slot S = half S/512,
+        // part S/256 % 2, row S % 256; entries 2, 3 for the tap-8 slot, 4-byte
+        // slot S = half S/512, row S/2 % 256, word S % 2)
+        uint32_t aoff[F8 ? 4 : kAInstr];
+        if constexpr (F8) {
 #pragma unroll
-        for (int t = 0; t < kAInstr; ++t) {
-            const int S = (t * kWaves + wave) * 64 + lane;
-            const int pl = S >> 8, row = S & 255;
-            aoff[t] = (m0 + row < a->Mg) ? uint32_t(pl * a->Mg + m0 + row) * 16 : kOOB;
+            for (int t = 0; t < 2; ++t) {
+                const int S = (t * kWaves + wave) * 64 + lane;
+                const int pq = S >> 8, row = S & 255;
+                aoff[t] = (m0 + row < a->Mg) ? uint32_t(pq * a->Mg + m0 + row) * 16 : kOOB;
+                const int h = S >> 9, r2 = (S >> 1) & 255;
+                aoff[2 + t] = (m0 + r2 < a->Mg)
+                                  ? uint32_t(h * a->Mg + m0 + r2) * 8 + uint32_t(S & 1) * 4
+                                  : kOOB;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < kAInstr; ++t) {
+                const int S = (t * kWaves + wave) * 64 + lane;
+                const int pl = S >> 8, row = S & 255;
+                aoff[t] = (m0 + row < a->Mg) ? uint32_t(pl * a->Mg + m0 + row) * 16 : kOOB;
+            }
         }
         // the group's first 8-channel block plane, bytes
         const uint32_t ch_base = uint32_t(g * a->Cg / 8) * hw16;
@@ -473,7 +544,7 @@ void window_kernel(WinArgs args)
                 wo[t] = woff_tab[t * kThreads + tid];
 #pragma unroll
             for (int t = 0; t < kWinInstr; ++t)
-                dma16(lds0 + kWin0 + buf * kWinBuf + (t * kWaves + wave) * 1024 +
+                dma16(lds0 + L::win0 + buf * kWinBuf + (t * kWaves + wave) * 1024 +
                           ((t * kWaves + wave) * 64 >= kWindowPixels ? kPlaneGap : 0),
                       rx, wo[t], soff);
         };
@@ -493,13 +564,41 @@ void window_kernel(WinArgs args)
                 dma16(lds0 + kAOff + (step % kAStages) * kAStage + (t * kWaves + wave) * 1024, ra,
                       aoff[t], soff);
         };
+        // F8: the weight of MFMA group j (0: taps 0-3, 1: taps 4-7, 2: tap 8)
+        // of relative chunk rc into slot j; a chunk's block is 144*Mg bytes,
+        // its regions 64*Mg bytes apart
+        uint32_t a_chunk = 0, a_region = 0;
+        if constexpr (F8) {
+            a_chunk = uint32_t(a->Mg) * 144;
+            a_region = uint32_t(a->Mg) * 64;
+            asm volatile("" : "+s"(a_chunk), "+s"(a_region));
+        }
+        auto issue_a8 = [&](int rc, auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const uint32_t soff = __builtin_amdgcn_readfirstlane(uint32_t(c_lo + rc) * a_chunk +
+                                                                 uint32_t(j) * a_region);
+            if constexpr (j < 2) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    dma16(lds0 + j * kF8Quad + (t * kWaves + wave) * 1024, ra, aoff[t], soff);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    dma4(lds0 + 2 * kF8Quad + (t * kWaves + wave) * 256, ra, aoff[2 + t], soff);
+            }
+        };
 
         // ---- prologue copies: window of the first chunk, A of steps 0 .. LEAD-1
+        // (F8: of the first chunk's first group)
         issue_window(c_lo, 0);
+        if constexpr (F8) {
+            issue_a8(0, std::integral_constant<int, 0>{});
+        } else {
 #pragma unroll
-        for (int s = 0; s < LEAD; ++s)
-            if (s < steps)
-                issue_a(s);
+            for (int s = 0; s < LEAD; ++s)
+                if (s < steps)
+                    issue_a(s);
+        }
 
         // ---- sampling geometry of the lane's pixel, all taps: the byte
         // offset of the top-left corner in a window buffer (16 bits, two taps
@@ -516,13 +615,13 @@ void window_kernel(WinArgs args)
                 // this wave's offset and mask copies (issued before the window
                 // and A copies, so older than the last kWinInstr + LEAD*kAInstr
                 // of its copies) have landed, then every wave's
-                constexpr int N = kWinInstr + LEAD * kAInstr;
+                constexpr int N = kWinInstr + (F8 ? 2 : LEAD * kAInstr);
                 constexpr int kNoLgkm = 0x70 | 0xF00;
                 static_assert(N < 64, "vmcnt range");
                 __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
-                const char *om = smem + kOmOff + px_n * 2;
+                const char *om = smem + L::om + px_n * 2;
 #pragma unroll
                 for (int k = 0; k < kTaps; ++k) {
                     oh[k] = to_f32(*reinterpret_cast<const T *>(om + (2 * k) * 512));
@@ -584,7 +683,7 @@ void window_kernel(WinArgs args)
 
         // Fallback: the lane's 8 channels of the sample of tap k in chunk
         // `chunk`, from global memory (rare).
-        auto fallback = [&](int k, int chunk, uint4 &bv) {
+        auto fallback = [&](int k, int chunk, auto &bv) {
             if ((fbl >> k) & 1u) {
                 KArgs a = fresh_args(pa);
                 const T *offp = static_cast<const T *>(a->off);
@@ -614,7 +713,10 @@ void window_kernel(WinArgs args)
                     __builtin_memcpy(&cv[t], &r, 16);
                 }
                 const float w4[4] = {tp.wt[0], tp.wt[1], tp.wt[2], tp.wt[3]};
-                bv = blend<T>(cv[0], cv[1], cv[2], cv[3], w4, 0.0f);
+                if constexpr (F8)
+                    bv = blend_e4m3<T>(cv, w4, 0.0f);
+                else
+                    bv = blend<T>(cv[0], cv[1], cv[2], cv[3], w4, 0.0f);
             }
         };
 
@@ -709,7 +811,7 @@ void window_kernel(WinArgs args)
         // corners of tap k from window buffer `buf`
         auto read_corners = [&](uint4 (&cr)[4], int k, int buf) {
             const uint32_t bo =
-                __builtin_amdgcn_readfirstlane(uint32_t(kWin0 + (buf ? kWinBuf : 0)));
+                __builtin_amdgcn_readfirstlane(uint32_t(L::win0 + (buf ? kWinBuf : 0)));
             uint32_t pk = gpk[k / 2];
             asm volatile("" : "+v"(pk));                 // (not hoisted: see weights_of)
             const uint32_t wa = (k % 2) ? (pk >> 16) : (pk & 0xffffu);
@@ -721,129 +823,275 @@ void window_kernel(WinArgs args)
             cr[3] = *reinterpret_cast<const uint4 *>(p2 + 16);
         };
 
-        uint4 fa[8];
-        uint4 cr[4];
-        // step 0's A fragments and corners
-        read_a(fa, 0);
-        read_corners(cr, 0, 0);
+        if constexpr (!F8) {
+            uint4 fa[8];
+            uint4 cr[4];
+            // step 0's A fragments and corners
+            read_a(fa, 0);
+            read_corners(cr, 0, 0);
 
-        // Waves w and w + 4 share a SIMD.  Each step is a blend half (this
-        // step's B from the corners read in the previous step, then the next
-        // step's corner reads) and an MFMA half (8 MFMAs and the next step's
-        // A fragment reads).  (Tried and slower: no workgroup barrier, waves
-        // kept within two steps of each other by arrival counters in LDS --
-        // with 8 A stages and copies 5 steps ahead a copy then has only two
-        // steps to land, and the waves waited on each other 30 % of the time.)  At a barrier, waves 0-3 wait before their blend
-        // half and waves 4-7 before their MFMA half, so after it the two
-        // waves of a SIMD run opposite halves (the barrier is released once
-        // all eight waves have reached one of the two sites).
-        const bool late = wave >= 4;
+            // Waves w and w + 4 share a SIMD.  Each step is a blend half (this
+            // step's B from the corners read in the previous step, then the next
+            // step's corner reads) and an MFMA half (8 MFMAs and the next step's
+            // A fragment reads).  (Tried and slower: no workgroup barrier, waves
+            // kept within two steps of each other by arrival counters in LDS --
+            // with 8 A stages and copies 5 steps ahead a copy then has only two
+            // steps to land, and the waves waited on each other 30 % of the time.)  At a barrier, waves 0-3 wait before their blend
+            // half and waves 4-7 before their MFMA half, so after it the two
+            // waves of a SIMD run opposite halves (the barrier is released once
+            // all eight waves have reached one of the two sites).
+            const bool late = wave >= 4;
 
-        // One step: relative step s = rc*9 + k of chunk c_lo + rc.  The tap
-        // k is a compile-time index so the geometry stays in registers.
-        auto step_body = [&](int rc, auto kc) {
-            constexpr int k = decltype(kc)::value;
-            const int s = rc * kTaps + k;
-            const int chunk = c_lo + rc;
-            const bool last_chunk = chunk + 1 >= c_hi;
-            // One barrier every third step (k = 0, 3, 6): every wave's copies
-            // issued up to two steps before it have landed (each wave waits
-            // for its own, then the barrier), which covers every A stage and
-            // window read until the next barrier.  Still in flight: the A
-            // copy of the previous step, at k == 3 the window copy of the next
-            // chunk (issued in step k == 1 after that step's A copy, waited
-            // for at k == 6, first read in step k == 8), and -- for waves 4-7,
-            // which wait after their blend half -- the copies of this step.
-            // Every copy overwrites data last read at least two steps before
-            // the last barrier (A of step s + LEAD - 8; the window of chunk - 1,
-            // last read in step 9*chunk - 2), which every wave passed.  (No LDS
-            // wait is needed for that: every read was consumed by the step
-            // that used it.)
-            constexpr int kNoLgkm = 0x70 | 0xF00;     // expcnt and lgkmcnt: no wait
-            auto barrier = [&](int own) {
-                // own: copies of this step already issued by this wave
-                const bool a_prev = s >= 1 && s - 1 + LEAD < steps;   // copied in step s-1
-                if (k == 3 && !last_chunk) {
-                    if (own) {
-                        constexpr int N = 2 * kAInstr + kWinInstr;
+            // One step: relative step s = rc*9 + k of chunk c_lo + rc.  The tap
+            // k is a compile-time index so the geometry stays in registers.
+            auto step_body = [&](int rc, auto kc) {
+                constexpr int k = decltype(kc)::value;
+                const int s = rc * kTaps + k;
+                const int chunk = c_lo + rc;
+                const bool last_chunk = chunk + 1 >= c_hi;
+                // One barrier every third step (k = 0, 3, 6): every wave's copies
+                // issued up to two steps before it have landed (each wave waits
+                // for its own, then the barrier), which covers every A stage and
+                // window read until the next barrier.  Still in flight: the A
+                // copy of the previous step, at k == 3 the window copy of the next
+                // chunk (issued in step k == 1 after that step's A copy, waited
+                // for at k == 6, first read in step k == 8), and -- for waves 4-7,
+                // which wait after their blend half -- the copies of this step.
+                // Every copy overwrites data last read at least two steps before
+                // the last barrier (A of step s + LEAD - 8; the window of chunk - 1,
+                // last read in step 9*chunk - 2), which every wave passed.  (No LDS
+                // wait is needed for that: every read was consumed by the step
+                // that used it.)
+                constexpr int kNoLgkm = 0x70 | 0xF00;     // expcnt and lgkmcnt: no wait
+                auto barrier = [&](int own) {
+                    // own: copies of this step already issued by this wave
+                    const bool a_prev = s >= 1 && s - 1 + LEAD < steps;   // copied in step s-1
+                    if (k == 3 && !last_chunk) {
+                        if (own) {
+                            constexpr int N = 2 * kAInstr + kWinInstr;
+                            __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                        } else {
+                            constexpr int N = kAInstr + kWinInstr;
+                            __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                        }
+                    } else if (a_prev && own) {
+                        constexpr int N = 2 * kAInstr;
+                        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    } else if (a_prev || own) {
+                        constexpr int N = kAInstr;
                         __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
                     } else {
-                        constexpr int N = kAInstr + kWinInstr;
-                        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                        __builtin_amdgcn_s_waitcnt(kNoLgkm);
                     }
-                } else if (a_prev && own) {
-                    constexpr int N = 2 * kAInstr;
-                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
-                } else if (a_prev || own) {
-                    constexpr int N = kAInstr;
-                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
-                } else {
-                    __builtin_amdgcn_s_waitcnt(kNoLgkm);
-                }
-                __builtin_amdgcn_s_barrier();
-            };
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            if (k % 3 == 0 && !late)
-                barrier(0);
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("" ::: "memory");
-            const bool copy_a = s + LEAD < steps;
-            if (copy_a)
-                issue_a(s + LEAD);
-            if (k == 1 && !last_chunk)
-                issue_window(chunk + 1, (rc + 1) & 1);
-
-            // blend half: B of step s (the samples are the MFMA's A operand:
-            // rows are pixels), then the corners of step s+1.  Reads past the
-            // last step hit valid (stale) LDS and are never used.
-            constexpr int k1 = (k + 1) % kTaps;
-            const int rc1 = (k + 1 >= kTaps) ? rc + 1 : rc;
-            uint4 b;
-            {
-                float w[4];
-                weights_of(k, w);
-                b = blend<T>(cr[0], cr[1], cr[2], cr[3], w, zero);
-            }
-            if (fbw & (1u << k))
-                fallback(k, chunk, b);
-            read_corners(cr, k1, rc1 & 1);
-
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            if (k % 3 == 0 && late)
-                barrier(copy_a ? 1 : 0);
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("" ::: "memory");
-
-            // MFMA half: the MFMAs of step s (B: the weights; columns are
-            // output channels), each followed by the read of its A fragment
-            // for step s+1
-            const uint32_t so = __builtin_amdgcn_readfirstlane(
-                uint32_t(kAOff + ((s + 1) % kAStages) * kAStage));
-            const char *st = smem + (a_lane + so);
-            // (at a raised wave priority: the SIMD's other wave, in its blend
-            // half, fills the issue slots the MFMAs leave)
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                acc[i] = Mma<T>::step(b, fa[i], acc[i]);
-                fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
+                    __builtin_amdgcn_s_barrier();
+                };
+                asm volatile("" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            __builtin_amdgcn_s_setprio(0);
-        };
+                if (k % 3 == 0 && !late)
+                    barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("" ::: "memory");
+                const bool copy_a = s + LEAD < steps;
+                if (copy_a)
+                    issue_a(s + LEAD);
+                if (k == 1 && !last_chunk)
+                    issue_window(chunk + 1, (rc + 1) & 1);
 
-        for (int rc = 0; rc < c_hi - c_lo; ++rc) {
-            step_body(rc, std::integral_constant<int, 0>{});
-            step_body(rc, std::integral_constant<int, 1>{});
-            step_body(rc, std::integral_constant<int, 2>{});
-            step_body(rc, std::integral_constant<int, 3>{});
-            step_body(rc, std::integral_constant<int, 4>{});
-            step_body(rc, std::integral_constant<int, 5>{});
-            step_body(rc, std::integral_constant<int, 6>{});
-            step_body(rc, std::integral_constant<int, 7>{});
-            step_body(rc, std::integral_constant<int, 8>{});
+                // blend half: B of step s (the samples are the MFMA's A operand:
+                // rows are pixels), then the corners of step s+1.  Reads past the
+                // last step hit valid (stale) LDS and are never used.
+                constexpr int k1 = (k + 1) % kTaps;
+                const int rc1 = (k + 1 >= kTaps) ? rc + 1 : rc;
+                uint4 b;
+                {
+                    float w[4];
+                    weights_of(k, w);
+                    b = blend<T>(cr[0], cr[1], cr[2], cr[3], w, zero);
+                }
+                if (fbw & (1u << k))
+                    fallback(k, chunk, b);
+                read_corners(cr, k1, rc1 & 1);
+
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                if (k % 3 == 0 && late)
+                    barrier(copy_a ? 1 : 0);
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("" ::: "memory");
+
+                // MFMA half: the MFMAs of step s (B: the weights; columns are
+                // output channels), each followed by the read of its A fragment
+                // for step s+1
+                const uint32_t so = __builtin_amdgcn_readfirstlane(
+                    uint32_t(kAOff + ((s + 1) % kAStages) * kAStage));
+                const char *st = smem + (a_lane + so);
+                // (at a raised wave priority: the SIMD's other wave, in its blend
+                // half, fills the issue slots the MFMAs leave)
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    acc[i] = Mma<T>::step(b, fa[i], acc[i]);
+                    fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                __builtin_amdgcn_s_setprio(0);
+            };
+
+            for (int rc = 0; rc < c_hi - c_lo; ++rc) {
+                step_body(rc, std::integral_constant<int, 0>{});
+                step_body(rc, std::integral_constant<int, 1>{});
+                step_body(rc, std::integral_constant<int, 2>{});
+                step_body(rc, std::integral_constant<int, 3>{});
+                step_body(rc, std::integral_constant<int, 4>{});
+                step_body(rc, std::integral_constant<int, 5>{});
+                step_body(rc, std::integral_constant<int, 6>{});
+                step_body(rc, std::integral_constant<int, 7>{});
+                step_body(rc, std::integral_constant<int, 8>{});
+            }
+        } else {
+            // ---- E4M3 main loop.  A chunk's 9 taps are three MFMA groups
+            // (macro-steps j = 0, 1, 2): taps 0-3 and 4-7 each one 64-deep FP8
+            // instruction per 32x32 block (the lane's 8 channels of four taps,
+            // 32 bytes), tap 8 one 16-deep instruction (8 bytes).  Macro-step
+            // q = 3*rc + j reads weight slot j, which holds group j of relative
+            // chunk rc.  At barrier B_q (one per macro-step; waves 0-3 take it
+            // before their blend half, waves 4-7 before their MFMA half, as in
+            // the 16-bit loop) every wave's copy of A(q) has landed and every
+            // wave has finished MFMA(q-1); right after it each wave issues its
+            // share of A(q+2) into slot (q+2) % 3, the slot of A(q-1), and, at
+            // j == 2, the window of chunk rc+2 into the buffer of chunk rc,
+            // whose last corners were read in blend(q-1).  That window is
+            // waited for at B_{q+2} (j == 1 of chunk rc+1), before any wave
+            // reads the next chunk's corners (in blend(3rc+5), which waves 4-7
+            // run between B_{q+2} and B_{q+3}).  In flight at B_q besides
+            // A(q): A(q+1) and, at j == 0, the window issued with it.
+            const int nseg = c_hi - c_lo;
+            const int nq = 3 * nseg;
+            const bool late = wave >= 4;
+            const int hh = lane >> 5;
+            // the lane's A fragment of block i: four-tap slot part p at
+            // q8_lane + p*4096 + i*512; tap-8 slot at s8_lane + i*256
+            const uint32_t q8_lane = uint32_t(hh * 8192 + (lane & 31) * 16);
+            const uint32_t s8_lane = uint32_t(2 * kF8Quad + hh * 2048 + (lane & 31) * 8);
+
+            uint4 cr[4];
+            read_corners(cr, 0, 0);
+            // after the prologue's wait and barrier (B_-1): A(1), window(1)
+            issue_a8(0, std::integral_constant<int, 1>{});
+            if (nseg > 1)
+                issue_window(c_lo + 1, 1);
+
+            auto macro_body = [&](int rc, auto jc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr int k0 = 4 * j;                 // first tap
+                constexpr int nt = j < 2 ? 4 : 1;         // taps
+                const int q = 3 * rc + j;
+                const int chunk = c_lo + rc;
+                constexpr int kNoLgkm = 0x70 | 0xF00;
+                auto barrier_issue = [&]() {
+                    const bool a_next = q + 1 < nq;
+                    const bool win = j == 0 && rc + 1 < nseg;   // implies a_next
+                    if (win) {
+                        constexpr int N = 2 + kWinInstr;
+                        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    } else if (a_next) {
+                        constexpr int N = 2;
+                        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    } else {
+                        __builtin_amdgcn_s_waitcnt(kNoLgkm);
+                    }
+                    __builtin_amdgcn_s_barrier();
+                    constexpr int j2 = (j + 2) % 3;
+                    if (q + 2 < nq)
+                        issue_a8(rc + (j + 2) / 3, std::integral_constant<int, j2>{});
+                    if (j == 2 && rc + 2 < nseg)
+                        issue_window(chunk + 2, rc & 1);
+                };
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                if (!late)
+                    barrier_issue();
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("" ::: "memory");
+
+                // blend half: B of the group's taps (2 registers a tap), each
+                // tap's corners read one tap ahead (the last tap reads the
+                // next group's first)
+                uint32_t bq[2 * nt];
+#pragma unroll
+                for (int tt = 0; tt < nt; ++tt) {
+                    const int k = k0 + tt;
+                    const int k1 = (k + 1) % kTaps;
+                    const int buf1 = (k + 1 >= kTaps) ? ((rc + 1) & 1) : (rc & 1);
+                    uint4 cn[4];
+                    read_corners(cn, k1, buf1);
+                    float w[4];
+                    weights_of(k, w);
+                    uint2 b8 = blend_e4m3<T>(cr, w, zero);
+                    if (fbw & (1u << k))
+                        fallback(k, chunk, b8);
+                    bq[2 * tt] = b8.x;
+                    bq[2 * tt + 1] = b8.y;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        cr[c] = cn[c];
+                }
+
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                if (late)
+                    barrier_issue();
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("" ::: "memory");
+
+                // MFMA half: block by block, each fragment read two blocks ahead
+                __builtin_amdgcn_s_setprio(1);
+                if constexpr (j < 2) {
+                    const char *st = smem + (uint32_t(j * kF8Quad) + q8_lane);
+                    const int8v bop = {int(bq[0]), int(bq[1]), int(bq[2]), int(bq[3]),
+                                         int(bq[4]), int(bq[5]), int(bq[6]), int(bq[7])};
+                    auto frag = [&](int i) {
+                        const int4v lo = *reinterpret_cast<const int4v *>(st + i * 512);
+                        const int4v hi = *reinterpret_cast<const int4v *>(st + 4096 + i * 512);
+                        return int8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    };
+                    int8v f0 = frag(0), f1 = frag(1);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        int8v f2;
+                        if (i + 2 < 8)
+                            f2 = frag(i + 2);
+                        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            bop, f0, acc[i], 0, 0, 0, 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        f0 = f1;
+                        f1 = f2;
+                    }
+                } else {
+                    const char *st = smem + s8_lane;
+                    const long bop = long(uint64_t(bq[0]) | (uint64_t(bq[1]) << 32));
+                    auto frag = [&](int i) { return *reinterpret_cast<const long *>(st + i * 256); };
+                    long f0 = frag(0), f1 = frag(1);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        long f2 = 0;
+                        if (i + 2 < 8)
+                            f2 = frag(i + 2);
+                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(bop, f0, acc[i], 0, 0,
+                                                                            0);
+                        __builtin_amdgcn_sched_barrier(0);
+                        f0 = f1;
+                        f1 = f2;
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+            };
+
+            for (int rc = 0; rc < nseg; ++rc) {
+                macro_body(rc, std::integral_constant<int, 0>{});
+                macro_body(rc, std::integral_constant<int, 1>{});
+                macro_body(rc, std::integral_constant<int, 2>{});
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);
 
@@ -898,6 +1146,7 @@ void window_kernel(WinArgs args)
             const int Mg = a->Mg, P = a->P, Ho = a->Ho, Wo = a->Wo;
             const int wv = tid >> 6, ln = tid & 63;
             float bv[8];
+            float sv[8];                             // F8: the rows' 2^-e
             {
                 const T *bias = static_cast<const T *>(a->bias);
                 // the hand-over wait of this tile gave up: NaN for all of it
@@ -908,6 +1157,8 @@ void window_kernel(WinArgs args)
                     bv[i] = (bias && m < Mg) ? to_f32(bias[size_t(te.g) * Mg + m]) : 0.0f;
                     if (poison)
                         bv[i] = __builtin_nanf("");
+                    if constexpr (F8)
+                        sv[i] = m < Mg ? a->wscale[size_t(te.g) * Mg + m] : 0.0f;
                 }
             }
             // output planes of the tile's image and group, as a buffer (a
@@ -925,10 +1176,17 @@ void window_kernel(WinArgs args)
                 for (int h = 0; h < 2; ++h) {
                     const float16v &c = acc[i];
                     const float bb = bv[i];
-                    const uint32_t v0 = pack2<T>(c[8 * h + 0] + bb, c[8 * h + 1] + bb);
-                    const uint32_t v1 = pack2<T>(c[8 * h + 2] + bb, c[8 * h + 3] + bb);
-                    const uint32_t v2 = pack2<T>(c[8 * h + 4] + bb, c[8 * h + 5] + bb);
-                    const uint32_t v3 = pack2<T>(c[8 * h + 6] + bb, c[8 * h + 7] + bb);
+                    // (F8: 2^-e * sum + bias, one rounding: the product is exact)
+                    auto o = [&](int r) {
+                        if constexpr (F8)
+                            return fmaf(c[8 * h + r], sv[i], bb);
+                        else
+                            return c[8 * h + r] + bb;
+                    };
+                    const uint32_t v0 = pack2<T>(o(0), o(1));
+                    const uint32_t v1 = pack2<T>(o(2), o(3));
+                    const uint32_t v2 = pack2<T>(o(4), o(5));
+                    const uint32_t v3 = pack2<T>(o(6), o(7));
                     const auto w0 = __builtin_amdgcn_permlane32_swap(v0, v2, false, false);
                     const auto w1 = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
                     const u32x4 ov = {uint32_t(w0[0]), uint32_t(w1[0]), uint32_t(w0[1]),
@@ -983,10 +1241,10 @@ bool split_cached(int64_t tiles, int64_t nch, int64_t ncta, int64_t seg_x4, uint
     return true;
 }
 
-template <typename T, int TH, int TW, int LEAD>
+template <typename T, int TH, int TW, int LEAD, bool F8>
 hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                      const void *xt, const void *offset, const void *mask, const void *bias,
-                      void *out, const WindowScratch &ws, hipStream_t s)
+                      const float *wscale, const void *xt, const void *offset, const void *mask,
+                      const void *bias, void *out, const WindowScratch &ws, hipStream_t s)
 {
     WinArgs a;
     a.Mg = int(p.Mg); a.Kp = int(plan.Kp); a.Co = int(p.Co); a.P = int(p.P);
@@ -1026,7 +1284,11 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
                reinterpret_cast<uintptr_t>(offset) % 4 == 0 &&
                reinterpret_cast<uintptr_t>(mask) % 4 == 0;
     a.spin_limit = plan.win_spin_limit;
-    a.a_bytes = uint32_t(size_t(p.Mg) * p.Kg * sizeof(T));     // one group's weight
+    // one group's weight (F8: its E4M3 chunk blocks)
+    a.a_bytes = F8 ? uint32_t(size_t(p.Cg / kCC) * size_t(p.Mg) * kWindowFp8ChunkBytesPerRow)
+                   : uint32_t(size_t(p.Mg) * p.Kg * sizeof(T));
+    if (F8 && !wscale)
+        return hipErrorInvalidValue;
     if (a.WR * a.WC > kWindowPixels || a.WC * 16 + 32 > kWinZero)
         return hipErrorInvalidValue;
     const uint64_t tiles = uint64_t(p.G) * cnt * a.tiles_y * a.tiles_x * a.tiles_m;
@@ -1048,13 +1310,14 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
     if (!split_cached(int64_t(tiles), int64_t(a.nch), int64_t(blocks), plan.win_seg_cost_x4,
                       a.bounds))
         return hipErrorInvalidValue;
-    auto kern = window_kernel<T, TH, TW, LEAD>;
-    constexpr int lds = kLdsTotal;
+    auto kern = window_kernel<T, TH, TW, LEAD, F8>;
+    constexpr int lds = WinLds<F8>::total;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess)
         return attr;
     a.A = wpack; a.xt = xt; a.off = offset; a.msk = mask; a.bias = bias; a.out = out;
+    a.wscale = wscale;
     a.partial = ws.partial; a.flags = ws.flags; a.status = ws.flags + ws.slots;
     hipLaunchKernelGGL(kern, dim3(uint32_t(blocks)), dim3(kThreads), lds, s, a);
     return hipGetLastError();
@@ -1062,28 +1325,36 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
 
 template <typename T, int TH, int TW>
 hipError_t window_lead(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                       const void *xt, const void *offset, const void *mask, const void *bias,
-                       void *out, const WindowScratch &ws, hipStream_t s)
+                       const float *wscale, const void *xt, const void *offset, const void *mask,
+                       const void *bias, void *out, const WindowScratch &ws, hipStream_t s)
 {
     if (plan.win_lead != 5)
         return hipErrorInvalidValue;
-    return window_cfg<T, TH, TW, 5>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
+    if (plan.path == Path::WindowFp8)
+        return window_cfg<T, TH, TW, 5, true>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias,
+                                              out, ws, s);
+    return window_cfg<T, TH, TW, 5, false>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias,
+                                           out, ws, s);
 }
 
 template <typename T>
 hipError_t window_t(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                    const void *xt, const void *offset, const void *mask, const void *bias,
-                    void *out, const WindowScratch &ws, hipStream_t s)
+                    const float *wscale, const void *xt, const void *offset, const void *mask,
+                    const void *bias, void *out, const WindowScratch &ws, hipStream_t s)
 {
     switch (plan.win_tile) {
     case WindowTile::H16_W16:
-        return window_lead<T, 16, 16>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
+        return window_lead<T, 16, 16>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out,
+                                      ws, s);
     case WindowTile::H8_W32:
-        return window_lead<T, 8, 32>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
+        return window_lead<T, 8, 32>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out,
+                                     ws, s);
     case WindowTile::H32_W8:
-        return window_lead<T, 32, 8>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
+        return window_lead<T, 32, 8>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out,
+                                     ws, s);
     case WindowTile::FLAT:
-        return window_lead<T, 1, 256>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, s);
+        return window_lead<T, 1, 256>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out,
+                                      ws, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1091,14 +1362,17 @@ hipError_t window_t(const Problem &p, const Plan &plan, int64_t cnt, const void 
 }  // namespace
 
 hipError_t launch_window(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
-                         const void *xt, const void *offset, const void *mask, const void *bias,
-                         void *out, const WindowScratch &ws, hipStream_t stream)
+                         const float *wscale, const void *xt, const void *offset,
+                         const void *mask, const void *bias, void *out, const WindowScratch &ws,
+                         hipStream_t stream)
 {
     switch (p.dtype) {
     case MDCN_F16:
-        return window_t<half_t>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, stream);
+        return window_t<half_t>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out, ws,
+                                stream);
     case MDCN_BF16:
-        return window_t<bf16_t>(p, plan, cnt, wpack, xt, offset, mask, bias, out, ws, stream);
+        return window_t<bf16_t>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out, ws,
+                                stream);
     case MDCN_F32:
         break;
     }

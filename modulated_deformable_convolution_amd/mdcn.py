@@ -42,6 +42,7 @@ MDCN_PATH_FUSED = 3
 MDCN_PATH_WINDOW = 4
 MDCN_PATH_DIRECT = 5
 MDCN_PATH_GATHER_GEMM_FP8 = 6
+MDCN_PATH_WINDOW_FP8 = 7
 
 EXPORTED = [
     "mdcn_create", "mdcn_create_with_path", "mdcn_destroy", "mdcn_output_shape",

@@ -464,6 +464,39 @@ def test_fp8_path_plan():
     assert {"prep_nhwc_fp8", "deform_gather_fp8", "gemm_fp8_bias"} <= set(names)
 
 
+def test_window_fp8_path_plan():
+    """The windowed FP8 path: the window path's tiles, margin, chunking and
+    partial-sum slots, with the 16-bit step-major weight replaced by the E4M3
+    chunk blocks (144 bytes per output channel and 16-channel chunk) and one
+    fp32 scale per output channel.  Eligible where the window path is; never
+    the automatic choice."""
+    op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_WINDOW_FP8)
+    win = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_WINDOW)
+    for dt in (mdcn.MDCN_F16, mdcn.MDCN_BF16):
+        b, mb = mdcn.mdcn_workspace_bytes(op, dt, DIMS)
+        bw, mbw = mdcn.mdcn_workspace_bytes(win, dt, DIMS)
+        w16 = 256 * 2304 * 2
+        w8 = 16 * 256 * 144 + 256 * 4             # chunk blocks + row scales (aligned)
+        assert b == bw - w16 + w8 and mb == mbw - w16 + w8
+        d, tile, margin = _win_desc(op, dt, DIMS)
+        assert d.startswith("path=window_fp8") and tile == 0 and margin == 8
+    d40 = [16, 512, 40, 40, 16, 18, 40, 40, 16, 9, 40, 40, 512, 512, 3, 3]
+    d, tile, margin = _win_desc(op, mdcn.MDCN_F16, d40)
+    assert d.startswith("path=window_fp8") and tile == 3 and margin == 6
+    # the window path's limits: fp32 and a 5x5 kernel are refused
+    for dtype, dims in [(mdcn.MDCN_F32, DIMS),
+                        (mdcn.MDCN_F16, _fused_dims(1, 32, 12, 12, 32, 5, 1, 1))]:
+        with pytest.raises(mdcn.MdcnError) as e:
+            mdcn.mdcn_workspace_bytes(op, dtype, dims)
+        assert e.value.status == mdcn.MDCN_E_PATH
+    auto = mdcn.mdcn_create(1, 1, 1, 1, 1)
+    for dims in (DIMS, d40):
+        assert "fp8" not in mdcn.mdcn_describe_plan(auto, mdcn.MDCN_F16, dims)
+    assert mdcn.mdcn_kernel_name(24) == "prep_blocks_fp8"
+    assert mdcn.mdcn_kernel_name(25) == "window_gather_gemm_fp8"
+    assert mdcn.mdcn_kernel_name(26) == "?"
+
+
 def test_backward_entry_points():
     """Inputs and gradients in the dtype, fp32 arithmetic; the workspace holds
     the packed weight and one image's NHWC x (dtype), its fp32 gradient
