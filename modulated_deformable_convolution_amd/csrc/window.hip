@@ -51,6 +51,17 @@
 // The LDS copies are issued as inline-assembly DMA (buffer_load ... lds): the
 // waits for them are explicit (s_waitcnt vmcnt + barrier), so the compiler,
 // which does not see them, cannot make LDS reads wait for unrelated copies.
+//
+// The E4M3 variant (F8) keeps the tiles, window, geometry, work split and
+// hand-overs, and changes the contraction: each sample is blended in fp32,
+// saturated to +-448 and rounded to E4M3, and a 16-channel chunk's 9 taps run
+// as three MFMA groups on the FP8 matrix cores -- taps 0-3 and 4-7 as one
+// 64-deep v_mfma_f32_32x32x64_f8f6f4 each (the lane's 8 channels of four taps,
+// 32 bytes, per 32x32 block), tap 8 as one 16-deep v_mfma_f32_32x32x16_fp8_fp8
+// -- with the weight rows scaled by 2^e (e per output channel) and rounded to
+// E4M3 by the set-up kernel, and 2^-e applied in the epilogue.  Its main loop
+// is software-pipelined: every wave blends group q while the MFMAs of group
+// q-1 run, with one barrier per group and one chunk's weight (36 KiB) in LDS.
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -294,11 +305,11 @@ __device__ __forceinline__ uint4 blend(const uint4 &c0, const uint4 &c1, const u
 // wave holds a value beyond that (or an infinity; a NaN stays NaN) -- and
 // rounded to nearest even by the converter.
 template <typename T>
-__device__ __forceinline__ uint2 blend_e4m3(const uint4 (&c)[4], const float (&w)[4], float zero)
+__device__ __forceinline__ void blend_f32(const uint4 (&c)[4], const float (&w)[4], float zero,
+                                          float (&acc)[8])
 {
     Vec16<T> v0, v1, v2, v3;
     v0.raw = c[0]; v1.raw = c[1]; v2.raw = c[2]; v3.raw = c[3];
-    float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         acc[e] = fmaf(to_f32(v0.e[e]), w[0], zero);
@@ -306,6 +317,10 @@ __device__ __forceinline__ uint2 blend_e4m3(const uint4 (&c)[4], const float (&w
         acc[e] = fmaf(to_f32(v2.e[e]), w[2], acc[e]);
         acc[e] = fmaf(to_f32(v3.e[e]), w[3], acc[e]);
     }
+}
+
+__device__ __forceinline__ uint2 e4m3_of(float (&acc)[8])
+{
     const float m = fmaxf(fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])),
                                 fmaxf(fabsf(acc[2]), fabsf(acc[3]))),
                           fmaxf(fmaxf(fabsf(acc[4]), fabsf(acc[5])),
@@ -317,6 +332,14 @@ __device__ __forceinline__ uint2 blend_e4m3(const uint4 (&c)[4], const float (&w
     }
     return make_uint2(pack4_e4m3_unsat(acc[0], acc[1], acc[2], acc[3]),
                       pack4_e4m3_unsat(acc[4], acc[5], acc[6], acc[7]));
+}
+
+template <typename T>
+__device__ __forceinline__ uint2 blend_e4m3(const uint4 (&c)[4], const float (&w)[4], float zero)
+{
+    float acc[8];
+    blend_f32<T>(c, w, zero, acc);
+    return e4m3_of(acc);
 }
 
 template <typename T, int TH, int TW, int LEAD, bool F8>
@@ -950,74 +973,130 @@ void window_kernel(WinArgs args)
             }
         } else {
             // ---- E4M3 main loop.  A chunk's 9 taps are three MFMA groups
-            // (macro-steps j = 0, 1, 2): taps 0-3 and 4-7 each one 64-deep FP8
-            // instruction per 32x32 block (the lane's 8 channels of four taps,
-            // 32 bytes), tap 8 one 16-deep instruction (8 bytes).  Macro-step
-            // q = 3*rc + j reads weight slot j, which holds group j of relative
-            // chunk rc.  At barrier B_q (one per macro-step; waves 0-3 take it
-            // before their blend half, waves 4-7 before their MFMA half, as in
-            // the 16-bit loop) every wave's copy of A(q) has landed and every
-            // wave has finished MFMA(q-1); right after it each wave issues its
-            // share of A(q+2) into slot (q+2) % 3, the slot of A(q-1), and, at
-            // j == 2, the window of chunk rc+2 into the buffer of chunk rc,
-            // whose last corners were read in blend(q-1).  That window is
-            // waited for at B_{q+2} (j == 1 of chunk rc+1), before any wave
-            // reads the next chunk's corners (in blend(3rc+5), which waves 4-7
-            // run between B_{q+2} and B_{q+3}).  In flight at B_q besides
-            // A(q): A(q+1) and, at j == 0, the window issued with it.
+            // (j = 0: taps 0-3 and j = 1: taps 4-7, each one 64-deep FP8
+            // instruction per 32x32 block on the lane's 8 channels of four
+            // taps, 32 bytes; j = 2: tap 8, one 16-deep instruction on 8
+            // bytes).  Group q = 3*rc + j of the segment reads weight slot j.
+            // The loop is software-pipelined: phase p blends group p (its B
+            // operand built tap by tap, each tap's corners read one tap ahead)
+            // and, interleaved with the blend, runs the MFMAs of group p-1, so
+            // that the matrix cores work while the VALU blends.  Barrier X_p
+            // ends phase p: every wave's copy of A(p) has landed (each wave
+            // waits for its own copies, then the barrier) and, for p = 3c+1,
+            // the window of chunk c+1, whose first corners phase p+1 reads.
+            // After X_p each wave issues its share of A(p+2) into slot
+            // (p+2) % 3, the slot of A(p-1), whose MFMAs ran in phase p, and,
+            // for p = 3c+1, the window of chunk c+2 into the buffer of chunk
+            // c, last read in phase p.  In flight at X_p besides what it waits
+            // for: A(p+1) and the windows issued after X_{p-1} (p = 3c+2) or
+            // after X_{p-2} with A(p) (p = 3c+3).
             const int nseg = c_hi - c_lo;
             const int nq = 3 * nseg;
-            const bool late = wave >= 4;
             const int hh = lane >> 5;
-            // the lane's A fragment of block i: four-tap slot part p at
-            // q8_lane + p*4096 + i*512; tap-8 slot at s8_lane + i*256
+            // the lane's A fragment of block i: four-tap slot j part p at
+            // j*kF8Quad + q8_lane + p*4096 + i*512; tap-8 slot at s8_lane + i*256
             const uint32_t q8_lane = uint32_t(hh * 8192 + (lane & 31) * 16);
             const uint32_t s8_lane = uint32_t(2 * kF8Quad + hh * 2048 + (lane & 31) * 8);
+            constexpr int kNoLgkm = 0x70 | 0xF00;
 
             uint4 cr[4];
             read_corners(cr, 0, 0);
-            // after the prologue's wait and barrier (B_-1): A(1), window(1)
+            // after the prologue's wait and barrier: A(1), window(1)
             issue_a8(0, std::integral_constant<int, 1>{});
             if (nseg > 1)
                 issue_window(c_lo + 1, 1);
 
-            auto macro_body = [&](int rc, auto jc) {
-                constexpr int j = decltype(jc)::value;
-                constexpr int k0 = 4 * j;                 // first tap
-                constexpr int nt = j < 2 ? 4 : 1;         // taps
-                const int q = 3 * rc + j;
-                const int chunk = c_lo + rc;
-                constexpr int kNoLgkm = 0x70 | 0xF00;
-                auto barrier_issue = [&]() {
-                    const bool a_next = q + 1 < nq;
-                    const bool win = j == 0 && rc + 1 < nseg;   // implies a_next
-                    if (win) {
-                        constexpr int N = 2 + kWinInstr;
-                        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
-                    } else if (a_next) {
-                        constexpr int N = 2;
-                        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
-                    } else {
-                        __builtin_amdgcn_s_waitcnt(kNoLgkm);
-                    }
-                    __builtin_amdgcn_s_barrier();
-                    constexpr int j2 = (j + 2) % 3;
-                    if (q + 2 < nq)
-                        issue_a8(rc + (j + 2) / 3, std::integral_constant<int, j2>{});
-                    if (j == 2 && rc + 2 < nseg)
-                        issue_window(chunk + 2, rc & 1);
-                };
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
-                if (!late)
-                    barrier_issue();
-                __builtin_amdgcn_sched_barrier(0);
-                asm volatile("" ::: "memory");
+            // B operands: of the group being blended and of the one whose
+            // MFMAs run meanwhile
+            uint32_t bcur[8] = {}, bprev[8] = {};
 
-                // blend half: B of the group's taps (2 registers a tap), each
-                // tap's corners read one tap ahead (the last tap reads the
-                // next group's first)
-                uint32_t bq[2 * nt];
+            // A fragment of block i of group jm (compile time) from its slot
+            auto frag64 = [&](int jm, int i) {
+                const char *st = smem + (uint32_t(jm * kF8Quad) + q8_lane);
+                const int4v lo = *reinterpret_cast<const int4v *>(st + i * 512);
+                const int4v hi = *reinterpret_cast<const int4v *>(st + 4096 + i * 512);
+                return int8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            auto frag16 = [&](int i) {
+                return *reinterpret_cast<const long *>(smem + s8_lane + i * 256);
+            };
+
+            // barrier X_p and the copies issued after it (p = 3*rc + j)
+            auto barrier_issue = [&](int rc, auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const int p = 3 * rc + j;
+                const bool a_next = p + 1 < nq;
+                // window issued after X_{p-1} (p = 3c+2: chunk c+1 < nseg-1)
+                // or after X_{p-2}, with A(p) (p = 3c+3, c = rc-1: chunk rc+1)
+                const bool w_younger = (j == 2 && rc + 2 < nseg) || (j == 0 && rc >= 1 &&
+                                                                     rc + 1 < nseg);
+                if (p == 0) {
+                    // A(0) landed before the loop; A(1), window(1) may fly
+                    __builtin_amdgcn_s_waitcnt(
+                        ((2 + kWinInstr) & 15) | (((2 + kWinInstr) >> 4) << 14) | kNoLgkm);
+                } else if (a_next && w_younger) {
+                    constexpr int N = 2 + kWinInstr;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                } else if (a_next) {
+                    constexpr int N = 2;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                } else if (w_younger) {
+                    constexpr int N = kWinInstr;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                } else {
+                    __builtin_amdgcn_s_waitcnt(kNoLgkm);
+                }
+                __builtin_amdgcn_s_barrier();
+                constexpr int j2 = (j + 2) % 3;
+                if (p + 2 < nq)
+                    issue_a8(rc + (j + 2) / 3, std::integral_constant<int, j2>{});
+                if (j == 1 && rc + 2 < nseg)
+                    issue_window(c_lo + rc + 2, rc & 1);
+            };
+
+            // Phase p = 3*rc + j: blend group (rc, j) into bcur while the
+            // MFMAs of group p-1 (type jm, operand bprev) run, if any.
+            auto phase = [&](int rc, auto jc, auto mfc) {
+                constexpr int j = decltype(jc)::value;
+                constexpr bool mfma = decltype(mfc)::value;
+                constexpr int jm = (j + 2) % 3;            // the previous group's type
+                constexpr int k0 = 4 * j;                  // first tap
+                constexpr int nt = j < 2 ? 4 : 1;          // taps
+                constexpr int per = 8 / nt;                // MFMAs per tap
+                const int chunk = c_lo + rc;
+                // phase 0 of the segment has no previous group: its MFMAs
+                // multiply zero fragments (whatever the slot holds)
+                const bool live = j != 0 || rc > 0;
+                const int8v bop64 = {int(bprev[0]), int(bprev[1]), int(bprev[2]), int(bprev[3]),
+                                     int(bprev[4]), int(bprev[5]), int(bprev[6]), int(bprev[7])};
+                const long bop16 = long(uint64_t(bprev[0]) | (uint64_t(bprev[1]) << 32));
+                // fragments of MFMAs i and i+1 in flight (read two ahead)
+                int8v f64[2];
+                long f16[2];
+                if constexpr (mfma) {
+                    if constexpr (jm < 2) {
+                        f64[0] = frag64(jm, 0);
+                        f64[1] = frag64(jm, 1);
+                    } else {
+                        f16[0] = frag16(0);
+                        f16[1] = frag16(1);
+                    }
+                }
+                auto mma = [&](int i) {
+                    if constexpr (jm < 2) {
+                        const int8v f = f64[i & 1];
+                        if (i + 2 < 8)
+                            f64[i & 1] = frag64(jm, i + 2);
+                        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            bop64, f, acc[i], 0, 0, 0, 0, 0, 0);
+                    } else {
+                        const long f = live ? f16[i & 1] : 0;
+                        if (i + 2 < 8)
+                            f16[i & 1] = frag16(i + 2);
+                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(bop16, f, acc[i], 0,
+                                                                            0, 0);
+                    }
+                };
 #pragma unroll
                 for (int tt = 0; tt < nt; ++tt) {
                     const int k = k0 + tt;
@@ -1027,71 +1106,64 @@ void window_kernel(WinArgs args)
                     read_corners(cn, k1, buf1);
                     float w[4];
                     weights_of(k, w);
-                    uint2 b8 = blend_e4m3<T>(cr, w, zero);
+                    // the tap's share of the previous group's MFMAs, spread
+                    // through its blend FMAs (one basic block: the scheduler
+                    // interleaves them as the group barriers ask)
+                    if constexpr (mfma) {
+#pragma unroll
+                        for (int u = 0; u < per; ++u)
+                            mma(tt * per + u);
+                    }
+                    float bf[8];
+                    blend_f32<T>(cr, w, zero, bf);
+                    if constexpr (mfma) {
+#pragma unroll
+                        for (int u = 0; u < per; ++u) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x002, 32 / per, 0);   // VALU
+                        }
+                    }
+                    uint2 b8 = e4m3_of(bf);
                     if (fbw & (1u << k))
                         fallback(k, chunk, b8);
-                    bq[2 * tt] = b8.x;
-                    bq[2 * tt + 1] = b8.y;
+                    bcur[2 * tt] = b8.x;
+                    bcur[2 * tt + 1] = b8.y;
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         cr[c] = cn[c];
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
-                if (late)
-                    barrier_issue();
-                __builtin_amdgcn_sched_barrier(0);
-                asm volatile("" ::: "memory");
-
-                // MFMA half: block by block, each fragment read two blocks ahead
-                __builtin_amdgcn_s_setprio(1);
-                if constexpr (j < 2) {
-                    const char *st = smem + (uint32_t(j * kF8Quad) + q8_lane);
-                    const int8v bop = {int(bq[0]), int(bq[1]), int(bq[2]), int(bq[3]),
-                                         int(bq[4]), int(bq[5]), int(bq[6]), int(bq[7])};
-                    auto frag = [&](int i) {
-                        const int4v lo = *reinterpret_cast<const int4v *>(st + i * 512);
-                        const int4v hi = *reinterpret_cast<const int4v *>(st + 4096 + i * 512);
-                        return int8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    };
-                    int8v f0 = frag(0), f1 = frag(1);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        int8v f2;
-                        if (i + 2 < 8)
-                            f2 = frag(i + 2);
-                        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            bop, f0, acc[i], 0, 0, 0, 0, 0, 0);
-                        __builtin_amdgcn_sched_barrier(0);
-                        f0 = f1;
-                        f1 = f2;
-                    }
-                } else {
-                    const char *st = smem + s8_lane;
-                    const long bop = long(uint64_t(bq[0]) | (uint64_t(bq[1]) << 32));
-                    auto frag = [&](int i) { return *reinterpret_cast<const long *>(st + i * 256); };
-                    long f0 = frag(0), f1 = frag(1);
+                for (int e = 0; e < 8; ++e)
+                    bprev[e] = bcur[e];
+            };
+            // the last group's MFMAs (type 2), after the last phase's barrier
+            auto tail = [&]() {
+                const long bop16 = long(uint64_t(bprev[0]) | (uint64_t(bprev[1]) << 32));
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        long f2 = 0;
-                        if (i + 2 < 8)
-                            f2 = frag(i + 2);
-                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(bop, f0, acc[i], 0, 0,
-                                                                            0);
-                        __builtin_amdgcn_sched_barrier(0);
-                        f0 = f1;
-                        f1 = f2;
-                    }
-                }
-                __builtin_amdgcn_s_setprio(0);
+                for (int i = 0; i < 8; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(bop16, frag16(i), acc[i],
+                                                                        0, 0, 0);
             };
 
-            for (int rc = 0; rc < nseg; ++rc) {
-                macro_body(rc, std::integral_constant<int, 0>{});
-                macro_body(rc, std::integral_constant<int, 1>{});
-                macro_body(rc, std::integral_constant<int, 2>{});
-            }
+            using yes = std::true_type;
+            auto chunk_body = [&](int rc) {
+                phase(rc, std::integral_constant<int, 0>{}, yes{});
+                asm volatile("" ::: "memory");
+                barrier_issue(rc, std::integral_constant<int, 0>{});
+                asm volatile("" ::: "memory");
+                phase(rc, std::integral_constant<int, 1>{}, yes{});
+                asm volatile("" ::: "memory");
+                barrier_issue(rc, std::integral_constant<int, 1>{});
+                asm volatile("" ::: "memory");
+                phase(rc, std::integral_constant<int, 2>{}, yes{});
+                asm volatile("" ::: "memory");
+                barrier_issue(rc, std::integral_constant<int, 2>{});
+                asm volatile("" ::: "memory");
+            };
+            for (int rc = 0; rc < nseg; ++rc)
+                chunk_body(rc);
+            tail();
         }
         __builtin_amdgcn_s_waitcnt(0);
 
