@@ -53,6 +53,11 @@ MEASURED_TRAFFIC = {
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
         "sha": "10df2ec0c4250d9e",
     },
+    ("window_gather_gemm_fp8", "ocdnet_n4_c256_160x160", "f16"): {
+        "bytes": (116159 * 2 + 116533) * 1024,
+        "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
+        "sha": "6069f918806c3dbd",
+    },
     ("fused_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
         "bytes": (53919 * 2 + 51200) * 1024,
         "sources": ('fused.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
