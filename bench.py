@@ -49,9 +49,9 @@ MEASURED_TRAFFIC = {
         "sha": "9f319b58a68cb257",
     },
     ("window_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (125851 * 2 + 117350) * 1024,
+        "bytes": (125884 * 2 + 117225) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "10df2ec0c4250d9e",
+        "sha": "6069f918806c3dbd",
     },
     ("window_gather_gemm_fp8", "ocdnet_n4_c256_160x160", "f16"): {
         "bytes": (116159 * 2 + 116533) * 1024,
