@@ -54,6 +54,11 @@ CASES = [
     ("gather_gemm_fp8", Problem(N=2, C=32, Co=48, H=15, W=13, deformable_groups=2,
                                 offset_dist=("normal", 2.0)), "f16",
      mdcn.MDCN_PATH_GATHER_GEMM_FP8),
+    # the windowed FP8 kernel, whole tiles and (MDCN_WIN_CTAS=7) split ones
+    ("window_fp8", Problem(N=2, C=32, Co=288, H=37, W=37, offset_dist=("normal", 3.0)), "bf16",
+     mdcn.MDCN_PATH_WINDOW_FP8),
+    ("window_fp8_split", Problem(N=2, C=32, Co=288, H=37, W=37, offset_dist=("normal", 3.0)),
+     "f16", mdcn.MDCN_PATH_WINDOW_FP8),
 ]
 
 
@@ -63,7 +68,7 @@ def _dev(inp):
 
 @pytest.mark.parametrize("name,pr,dtype,path", CASES, ids=[c[0] for c in CASES])
 def test_graph_replays_match_eager(name, pr, dtype, path, monkeypatch):
-    if name == "window_split":
+    if name in ("window_split", "window_fp8_split"):
         monkeypatch.setenv("MDCN_WIN_CTAS", "7")
     if name == "depthwise_persistent":
         monkeypatch.setenv("MDCN_DW_PERSISTENT_BLOCKS", "2")

@@ -20,9 +20,9 @@ Covered: several tiles with ragged edges, partial output-channel tiles,
 groups, strides and dilations, samples through the global-memory fallback,
 every tile shape, tiles split between workgroups (hand-overs through the
 workspace), the least workspace (one image per launch), saturation, a zero
-mask, and the two benchmark workloads at full size (grid inputs exactly,
-random inputs within tolerance, in the launch configuration the benchmark
-times).
+mask, 30 seeded random problems the windowed kernel takes, and the two
+benchmark workloads at full size (grid inputs exactly, random inputs within
+tolerance, in the launch configuration the benchmark times).
 """
 import numpy as np
 import pytest
@@ -253,3 +253,50 @@ def test_window_fp8_workload_full_size(wl):
                                           idx, **pr.attrs())
     rms = float(np.sqrt(np.mean(ref ** 2)))
     assert_random_close(got[idx], ref, asum, "f16", wl, rms=rms)
+
+
+def _random_cases(seed, count):
+    """Problems the windowed kernel takes: 3x3, C/group a multiple of 16,
+    offset groups that hold whole groups; strides, paddings, dilations,
+    output channels, image sizes and offset spreads drawn at random (draws
+    whose window does not fit are dropped by asking the planner)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        groups = int(rng.choice([1, 1, 2]))
+        cg = int(rng.choice([16, 32, 48]))
+        dg = int(rng.choice([d for d in (1, 2) if groups % d == 0]))
+        pr = Problem(N=int(rng.integers(1, 3)), C=groups * cg,
+                     Co=groups * int(rng.choice([8, 40, 96, 272])),
+                     H=int(rng.integers(6, 40)), W=int(rng.integers(6, 40)),
+                     stride=(int(rng.choice([1, 1, 2])), int(rng.choice([1, 2]))),
+                     padding=(int(rng.integers(0, 3)), int(rng.integers(0, 3))),
+                     dilation=(int(rng.choice([1, 1, 2])), int(rng.choice([1, 2]))),
+                     groups=groups, deformable_groups=dg, bias=bool(rng.random() < 0.7),
+                     offset_dist=(("normal", float(rng.choice([0.5, 2.0, 4.0])))
+                                  if rng.random() < 0.8 else ("uniform", 12.0)),
+                     mask_dist=(("uniform_zeros", 0.1) if rng.random() < 0.3
+                                else ("sigmoid_normal",)))
+        ho, wo = pr.out_hw()
+        if ho < 1 or wo < 1:
+            continue
+        shapes = pr.shapes()
+        dims = [int(v) for k in ("x", "offset", "mask", "weight") for v in shapes[k]]
+        try:
+            mdcn.mdcn_workspace_bytes(make_op(pr), mdcn.MDCN_F16, dims)
+        except mdcn.MdcnError:
+            continue                                  # no window fits this problem
+        dtype = str(rng.choice(["f16", "bf16"]))
+        out.append(pytest.param(pr, dtype, id=f"r{len(out)}-{dtype}"))
+    return out
+
+
+@pytest.mark.parametrize("pr,dtype", _random_cases(5151, 30))
+def test_window_fp8_random_problems(pr, dtype):
+    print("window fp8 random problem", pr, dtype, flush=True)
+    g = workloads.generate_grid(pr, dtype, seed=12)
+    ref, _ = fp8_ref(pr, g)
+    assert_grid_exact(run(pr, g), ref, dtype, "grid")
+    r = workloads.generate(pr, dtype, seed=13)
+    ref, asum = fp8_ref(pr, r)
+    assert_random_close(run(pr, r), ref, asum, dtype, "random")
