@@ -496,18 +496,23 @@ void window_kernel(WinArgs args)
         if (om_lds) {
             const v4i ro = srd(a->off, a->off_bytes);
             const v4i rm = srd(a->msk, a->msk_bytes);
+            // the fields the loop needs, read once: the DMA's memory clobber
+            // would make the compiler reload each of them (a dependent
+            // scalar load and wait) per instruction
+            const int Wo = a->Wo, Ho = a->Ho;
+            const uint32_t P = uint32_t(a->P);
+            const uint32_t ob = uint32_t(img * a->offC + q * 2 * kTaps);
+            const uint32_t mb = uint32_t(img * a->mskC + q * kTaps);
             for (int j = wave; j < kOmInstr; j += kWaves) {
                 const int plane = j >> 1;
                 const int n = (j & 1) * 128 + 2 * lane;
                 int ho, wo;
-                out_pixel(n, ho0, wo0, a->Wo, ho, wo);
-                const bool ok = ho < a->Ho && wo < a->Wo;
+                out_pixel(n, ho0, wo0, Wo, ho, wo);
+                const bool ok = ho < Ho && wo < Wo;
                 const bool is_off = plane < 2 * kTaps;
-                const uint32_t chan =
-                    is_off ? uint32_t(img * a->offC + q * 2 * kTaps + plane)
-                           : uint32_t(img * a->mskC + q * kTaps + plane - 2 * kTaps);
-                const uint32_t voff =
-                    ok ? (chan * uint32_t(a->P) + uint32_t(ho * a->Wo + wo)) * 2u : kOOB;
+                const uint32_t chan = is_off ? ob + uint32_t(plane)
+                                             : mb + uint32_t(plane - 2 * kTaps);
+                const uint32_t voff = ok ? (chan * P + uint32_t(ho * Wo + wo)) * 2u : kOOB;
                 dma4(lds0 + uint32_t(L::om + plane * 512 + (j & 1) * 256), is_off ? ro : rm,
                      voff, 0u);
             }
@@ -515,23 +520,25 @@ void window_kernel(WinArgs args)
 
         // ---- per-lane DMA source offsets of the window (kept in LDS; each
         // thread reads back only its own entries) and of the A rows
-        const float inv_wc = 1.0f / float(a->WC);
+        {
+            // (the fields read once, before the table stores)
+            const int WC = a->WC, WRC = a->WR * a->WC, H = a->H, W = a->W;
+            const uint32_t img_base = uint32_t(img) * a->img_bytes;
+            const float inv_wc = 1.0f / float(WC);
 #pragma unroll
-        for (int t = 0; t < kWinInstr; ++t) {
-            const int S = (t * kWaves + wave) * 64 + lane;   // 16-byte slot of the buffer
-            const int pl = S >= kWindowPixels ? 1 : 0;       // S < 2 * kWindowPixels
-            const int px = S - pl * kWindowPixels;
-            // px / WC through a float reciprocal: px < 1280 and WC <= 64, so
-            // px/WC is at least 1/128 away from the next integer, far above
-            // the float error (the plane of slot S is S / 1280 likewise)
-            const int r = int((float(px) + 0.5f) * inv_wc), c = px - r * a->WC;
-            const int gr = r0 + r, gc = c0 + c;
-            const bool ok = px < a->WR * a->WC && (unsigned)gr < (unsigned)a->H &&
-                            (unsigned)gc < (unsigned)a->W;
-            woff_tab[t * kThreads + tid] = ok ? uint32_t(img) * a->img_bytes +
-                                                    uint32_t(pl) * hw16 +
-                                                    uint32_t(gr * a->W + gc) * 16
-                                              : kOOB;
+            for (int t = 0; t < kWinInstr; ++t) {
+                const int S = (t * kWaves + wave) * 64 + lane;   // 16-byte slot of the buffer
+                const int pl = S >= kWindowPixels ? 1 : 0;       // S < 2 * kWindowPixels
+                const int px = S - pl * kWindowPixels;
+                // px / WC through a float reciprocal: px < 1280 and WC <= 64, so
+                // px/WC is at least 1/128 away from the next integer, far above
+                // the float error (the plane of slot S is S / 1280 likewise)
+                const int r = int((float(px) + 0.5f) * inv_wc), c = px - r * WC;
+                const int gr = r0 + r, gc = c0 + c;
+                const bool ok = px < WRC && (unsigned)gr < (unsigned)H && (unsigned)gc < (unsigned)W;
+                woff_tab[t * kThreads + tid] =
+                    ok ? img_base + uint32_t(pl) * hw16 + uint32_t(gr * W + gc) * 16 : kOOB;
+            }
         }
         // (F8: entries 0, 1 for the four-tap slots, 16-byte slot S = half S/512,
         // part S/256 % 2, row S % 256; entries 2, 3 for the tap-8 slot, 4-byte
