@@ -38,45 +38,45 @@ DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
 # profiles/*memory_counters.md), valid only for the kernel sources they were
 # taken on (sha256 of the listed files, first 16 hex digits).
 MEASURED_TRAFFIC = {
-    ("deform_gather_fp8", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (40485 * 2 + 230400) * 1024,
+    ('deform_gather_fp8', 'ocdnet_n4_c256_160x160', 'f16'): {
+        "bytes": (40449 * 2 + 230400) * 1024,
         "sources": ('gather.hip', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "8e5df729feb0ab73",
+        "sha": "8627bef73018e322",
     },
-    ("gemm_fp8_bias", "ocdnet_n4_c256_160x160", "f16"): {
+    ('gemm_fp8_bias', 'ocdnet_n4_c256_160x160', 'f16'): {
         "bytes": (119933 * 2 + 51200) * 1024,
         "sources": ('gemm.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp'),
-        "sha": "9f319b58a68cb257",
+        "sha": "aa6405c00fe4b3ae",
     },
-    ("window_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (125884 * 2 + 117225) * 1024,
+    ('window_gather_gemm', 'ocdnet_n4_c256_160x160', 'f16'): {
+        "bytes": (125313 * 2 + 116149) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "6069f918806c3dbd",
+        "sha": "aa68d208ec7e6372",
     },
-    ("window_gather_gemm_fp8", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (116159 * 2 + 116533) * 1024,
+    ('window_gather_gemm_fp8', 'ocdnet_n4_c256_160x160', 'f16'): {
+        "bytes": (115362 * 2 + 116202) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "6069f918806c3dbd",
+        "sha": "aa68d208ec7e6372",
     },
-    ("fused_gather_gemm", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (53919 * 2 + 51200) * 1024,
+    ('fused_gather_gemm', 'ocdnet_n4_c256_160x160', 'f16'): {
+        "bytes": (53970 * 2 + 51200) * 1024,
         "sources": ('fused.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "2bf816c7db5a8adf",
+        "sha": "07d4064a99ad3a60",
     },
-    ("gemm_bias", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (119931 * 2 + 25600) * 1024,
+    ('gemm_bias', 'ocdnet_n4_c256_160x160', 'f16'): {
+        "bytes": (119948 * 2 + 25600) * 1024,
         "sources": ('gemm.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp'),
-        "sha": "9f319b58a68cb257",
+        "sha": "aa6405c00fe4b3ae",
     },
-    ("deform_gather", "ocdnet_n4_c256_160x160", "f16"): {
-        "bytes": (23331 * 2 + 230400) * 1024,
+    ('deform_gather', 'ocdnet_n4_c256_160x160', 'f16'): {
+        "bytes": (23282 * 2 + 230400) * 1024,
         "sources": ('gather.hip', 'device_common.h', 'plan.cpp'),
-        "sha": "5fd5019368be82e8",
+        "sha": "f84b4baa3a2e48e6",
     },
-    ("depthwise_direct", "depthwise_n8_c256_96x96", "f32"): {
-        "bytes": (47360 * 2 + 73728) * 1024,
+    ('depthwise_direct', 'depthwise_n8_c256_96x96', 'f32'): {
+        "bytes": (47349 * 2 + 73728) * 1024,
         "sources": ('depthwise.hip', 'device_common.h'),
-        "sha": "bc9149a98a87a55d",
+        "sha": "6edca1bd9b79c9cc",
     },
 }
 
