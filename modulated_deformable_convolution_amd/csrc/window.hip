@@ -439,6 +439,10 @@ void window_kernel(WinArgs args)
         return ti;
     };
     int tile;
+    // A partial-sum slot this workgroup published whose flag is still to be
+    // set (see the publish below): wave-uniform, set by the tile that
+    // published and cleared once the flag is out.
+    bool flag_pending = false;
     {
         const Range r = range_of(a);
         if (r.u0 >= r.u1)
@@ -674,6 +678,24 @@ void window_kernel(WinArgs args)
                     mm[k] = to_f32(msk[mb + size_t(k) * P]);
                 }
             }
+            if (flag_pending) {
+                // the previous tile's published partial sums: everything
+                // but this prologue's window and weight copies (the youngest
+                // vector memory operations) is complete after this wait,
+                // those stores included; then the flag
+                constexpr int N = kWinInstr + (F8 ? 2 : LEAD * kAInstr);
+                constexpr int kNoLgkmF = 0x70 | 0xF00;
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkmF);
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (tid == 0) {
+                    KArgs af = fresh_args(pa);
+                    __hip_atomic_store(af->flags + cta, uint32_t(af->epoch), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                flag_pending = false;
+            }
             int ho, wo;
             out_pixel(px_n, ho0, wo0, a->Wo, ho, wo);
             const bool pv = ho < a->Ho && wo < a->Wo;
@@ -762,11 +784,12 @@ void window_kernel(WinArgs args)
         //
         // Ordering: the publisher's partial-sum stores and both flag accesses
         // are device-scope (SC1) accesses, which bypass the non-coherent
-        // caches; the publisher waits for its stores to be acknowledged
-        // (vmcnt 0) before its flag store, and the data loads here are issued
-        // after the flag was seen (the barrier follows the poll).  Empty asm
-        // statements with a memory clobber keep the compiler from moving any
-        // of these accesses across the flag.
+        // caches; every wave of the publisher waits for its stores to be
+        // acknowledged (a vmcnt wait that leaves only younger operations in
+        // flight, then a barrier) before the flag store, and the data loads
+        // here are issued after the flag was seen (the barrier follows the
+        // poll).  Empty asm statements with a memory clobber keep the
+        // compiler from moving any of these accesses across the flag.
         float16v acc[8];
         {
             const bool resume = c_lo > 0;
@@ -1202,15 +1225,16 @@ void window_kernel(WinArgs args)
                     __builtin_amdgcn_raw_buffer_store_b128(u, rs, lo + uint32_t((i * 4 + q) * 1024),
                                                            0, kDevScope);
                 }
-            // device-scope stores are complete (acknowledged where every XCD
-            // sees them) once the counter drains; only then the flag
+            // The flag goes out once these device-scope stores are complete
+            // (acknowledged where every XCD sees them).  Rather than draining
+            // the counter here, the next tile's prologue sets it after its
+            // own copies are issued: its counter wait then covers these
+            // older stores.  The workgroup that finishes the tile reads the
+            // flag only at the end of its range, so the later flag costs
+            // nothing, and it still precedes any hand-over wait of this
+            // workgroup (no chain of waits between neighbours).
             asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if (tid == 0)
-                __hip_atomic_store(a->flags + cta, uint32_t(a->epoch), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            flag_pending = true;
         } else {
             // ---- the tile's last chunks: + bias in fp32, one rounding,
             // stores straight from the accumulators.  Register r of block i
@@ -1298,6 +1322,18 @@ void window_kernel(WinArgs args)
         if (tile <= int(rg.u0 / uint32_t(a->nch)))
             break;                                   // that was the range's first tile
         --tile;
+    }
+    if (flag_pending) {
+        // the range held only the published tile: drain, then the flag
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (threadIdx.x == 0) {
+            KArgs af = fresh_args(pa);
+            __hip_atomic_store(af->flags + cta, uint32_t(af->epoch), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
