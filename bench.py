@@ -49,14 +49,14 @@ MEASURED_TRAFFIC = {
         "sha": "aa6405c00fe4b3ae",
     },
     ('window_gather_gemm', 'ocdnet_n4_c256_160x160', 'f16'): {
-        "bytes": (125313 * 2 + 116149) * 1024,
+        "bytes": (124119 * 2 + 116401) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "aa68d208ec7e6372",
+        "sha": "560201c54f2ef031",
     },
     ('window_gather_gemm_fp8', 'ocdnet_n4_c256_160x160', 'f16'): {
-        "bytes": (115362 * 2 + 116202) * 1024,
+        "bytes": (114334 * 2 + 116435) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "aa68d208ec7e6372",
+        "sha": "560201c54f2ef031",
     },
     ('fused_gather_gemm', 'ocdnet_n4_c256_160x160', 'f16'): {
         "bytes": (53970 * 2 + 51200) * 1024,
