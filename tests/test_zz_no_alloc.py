@@ -2,7 +2,8 @@
 device array (for callers that cannot allocate), against mdcn_forward.
 
 Two calls in a row through the C ABI, the second on a smaller input, each
-compared with mdcn_forward on the same inputs and with the oracle.  Both calls
+compared with mdcn_forward on the same inputs and with the oracle (on the
+windowed path and, separately, on the windowed FP8 path).  Both calls
 split output tiles between workgroups (MDCN_WIN_CTAS), so the first leaves
 published partial sums and set flags in the shared array: the second is only
 right if the forward clears what must start at zero.  A problem that needs
@@ -70,6 +71,32 @@ def test_noalloc_matches_forward_twice(monkeypatch):
                              **pr.attrs())
         ok, err, bound = within_tolerance(a, ref, dtype)
         assert ok, float((err - bound).max())
+
+
+def test_noalloc_window_fp8_twice(monkeypatch):
+    """The same two calls on the windowed FP8 path (E4M3 weight and row
+    scales in the array, split tiles): bit-identical to mdcn_forward, and
+    within the FP8 tolerance of the oracle's FP8 mode."""
+    monkeypatch.setenv("MDCN_WIN_CTAS", "3")
+    cases = [(Problem(N=2, C=128, Co=64, H=32, W=32, offset_dist=("normal", 2.0)), "f16", 33),
+             (Problem(N=1, C=128, Co=64, H=32, W=32, bias=True, offset_dist=("normal", 2.0)),
+              "bf16", 34)]
+    for pr, dtype, seed in cases:
+        print("noalloc fp8", pr, dtype, flush=True)
+        op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups,
+                              pr.deformable_groups, path=mdcn.MDCN_PATH_WINDOW_FP8)
+        inp = workloads.generate(pr, dtype, seed=seed)
+        g = _dev(inp)
+        st, got = _noalloc(op, g, dtype)
+        assert st == mdcn.MDCN_OK, mdcn.status_string(st)
+        ref_fwd = mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"],
+                               check=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref_fwd)
+        ref, asum = oracle.forward_fp8(inp["x"], inp["offset"], inp["mask"], inp["weight"],
+                                       inp["bias"], **pr.attrs())
+        _, err, bound = within_tolerance(got.cpu().double().numpy(), ref, dtype)
+        assert (err <= bound + 2.0 ** -11 * asum).all()
 
 
 def test_noalloc_rejects_problems_beyond_the_array():
