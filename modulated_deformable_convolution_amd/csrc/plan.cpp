@@ -231,9 +231,14 @@ int64_t window_extent(int64_t tile, int64_t stride, int64_t k, int64_t dil, int6
     return (tile - 1) * stride + (k - 1) * dil + 2 + 2 * margin;
 }
 
-int64_t window_flat_rows(int64_t Wo)
+int64_t window_flat_rows(int64_t Wo, int64_t n)
 {
-    return (Wo - 1 + 255) / Wo + 1;
+    return (Wo - 1 + n - 1) / Wo + 1;
+}
+
+bool window_tile_wide(WindowTile t)
+{
+    return int(t) >= kWindowWideFirst;
 }
 
 namespace {
@@ -245,18 +250,36 @@ void window_tile_dims(WindowTile t, int64_t *th, int64_t *tw)
     case WindowTile::H8_W32: *th = 8; *tw = 32; return;
     case WindowTile::H32_W8: *th = 32; *tw = 8; return;
     case WindowTile::FLAT: *th = 1; *tw = 256; return;
+    case WindowTile::H8_W16: *th = 8; *tw = 16; return;
+    case WindowTile::H16_W8: *th = 16; *tw = 8; return;
+    case WindowTile::FLAT128: *th = 1; *tw = 128; return;
     }
     *th = 16;
     *tw = 16;
 }
 
+bool window_tile_flat(WindowTile t)
+{
+    return t == WindowTile::FLAT || t == WindowTile::FLAT128;
+}
+
+// pixels and output channels of one tile
+int64_t window_tile_pixels(WindowTile t)
+{
+    return window_tile_wide(t) ? 128 : 256;
+}
+int64_t window_tile_channels(WindowTile t)
+{
+    return window_tile_wide(t) ? 512 : 256;
+}
+
 // Output rows and columns a tile's window must cover: the rectangle, or for
-// a flat tile every column and the rows that 256 consecutive pixels starting
+// a flat tile every column and the rows that its consecutive pixels starting
 // anywhere in a row can reach.
 void window_cover(const Problem &p, WindowTile t, int64_t *rows, int64_t *cols)
 {
-    if (t == WindowTile::FLAT) {
-        *rows = window_flat_rows(p.Wo);
+    if (window_tile_flat(t)) {
+        *rows = window_flat_rows(p.Wo, window_tile_pixels(t));
         *cols = p.Wo;
         return;
     }
@@ -266,8 +289,10 @@ void window_cover(const Problem &p, WindowTile t, int64_t *rows, int64_t *cols)
 // Output pixels the tiles of one image and group cover (ragged edges).
 int64_t window_padded_pixels(const Problem &p, WindowTile t)
 {
-    if (t == WindowTile::FLAT)
-        return (p.P + 255) / 256 * 256;
+    if (window_tile_flat(t)) {
+        const int64_t n = window_tile_pixels(t);
+        return (p.P + n - 1) / n * n;
+    }
     int64_t th, tw;
     window_tile_dims(t, &th, &tw);
     return ((p.Ho + th - 1) / th) * th * ((p.Wo + tw - 1) / tw) * tw;
@@ -278,10 +303,11 @@ int64_t window_margin_fit(const Problem &p, WindowTile t, int64_t cap)
 {
     int64_t th, tw;
     window_cover(p, t, &th, &tw);
+    const int64_t cap_px = window_tile_wide(t) ? kWindowPixelsWide : kWindowPixels;
     for (int64_t m = cap; m >= 0; --m) {
         const int64_t wr = window_extent(th, p.sh, p.kh, p.dh, m);
         const int64_t wc = window_extent(tw, p.sw, p.kw, p.dw, m);
-        if (wr * wc <= kWindowPixels && wc * 16 + 32 <= kWindowZeroBytes)
+        if (wr * wc <= cap_px && wc * 16 + 32 <= kWindowZeroBytes)
             return m;
     }
     return -1;
@@ -290,10 +316,12 @@ int64_t window_margin_fit(const Problem &p, WindowTile t, int64_t cap)
 }  // namespace
 
 // Tile: the fewest padded output pixels (ragged edges), then the widest
-// margin, among tiles whose window fits with a margin >= 2.
-// MDCN_WIN_TILE=<0..2> and MDCN_WIN_MARGIN=<m> override (for tuning).
-bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin)
+// margin, among tiles of the asked kind whose window fits with a margin >= 2.
+// MDCN_WIN_TILE=<tile> and MDCN_WIN_MARGIN=<m> override (for tuning).
+bool choose_window(const Problem &p, bool wide, WindowTile *tile, int64_t *margin)
 {
+    const int first = wide ? kWindowWideFirst : 0;
+    const int count = wide ? kWindowWideCount : kWindowTileCount;
     int64_t cap = kWindowMaxMargin;
     if (const char *env = std::getenv("MDCN_WIN_MARGIN")) {
         const int v = std::atoi(env);
@@ -303,7 +331,7 @@ bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin)
     const int64_t min_margin = std::min<int64_t>(2, cap);
     if (const char *env = std::getenv("MDCN_WIN_TILE")) {
         const int v = std::atoi(env);
-        if (v >= 0 && v < kWindowTileCount) {
+        if (v >= first && v < first + count) {
             const int64_t m = window_margin_fit(p, static_cast<WindowTile>(v), cap);
             if (m >= min_margin) {
                 *tile = static_cast<WindowTile>(v);
@@ -314,7 +342,7 @@ bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin)
     }
     bool found = false;
     int64_t best_pad = 0, best_m = 0;
-    for (int i = 0; i < kWindowTileCount; ++i) {
+    for (int i = first; i < first + count; ++i) {
         const WindowTile t = static_cast<WindowTile>(i);
         const int64_t m = window_margin_fit(p, t, cap);
         if (m < min_margin)
@@ -333,7 +361,8 @@ bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin)
 
 int64_t window_tiles_per_image(const Problem &p, WindowTile t)
 {
-    return p.G * (window_padded_pixels(p, t) / 256) * ((p.Mg + 255) / 256);
+    const int64_t m = window_tile_channels(t);
+    return p.G * (window_padded_pixels(p, t) / window_tile_pixels(t)) * ((p.Mg + m - 1) / m);
 }
 
 namespace {
@@ -390,13 +419,13 @@ bool window_split(int64_t tiles, int64_t nch, int64_t ncta, int64_t seg_cost_x4,
     return true;
 }
 
-bool window_eligible(const Problem &p)
+bool window_eligible(const Problem &p, bool wide)
 {
     const int64_t img_bytes = p.C * p.H * p.W * int64_t(p.elem);
     WindowTile t;
     int64_t m;
     return p.elem == 2 && p.kh == 3 && p.kw == 3 && p.Cg % 16 == 0 && p.Cdg % p.Cg == 0 &&
-           img_bytes <= kMaxPerImage && choose_window(p, &t, &m);
+           img_bytes <= kMaxPerImage && (!wide || p.Mg > 256) && choose_window(p, wide, &t, &m);
 }
 
 // The windowed kernel is the faster of the two MFMA paths when its tiles are
@@ -410,7 +439,7 @@ bool window_preferred(const Problem &p)
         return false;
     WindowTile t;
     int64_t m;
-    choose_window(p, &t, &m);
+    choose_window(p, false, &t, &m);
     const int64_t pad_px = window_padded_pixels(p, t);
     const int64_t pad_m = ((p.Mg + 255) / 256) * 256;
     return 8 * p.Ho * p.Wo * p.Mg >= 7 * pad_px * pad_m;
@@ -446,7 +475,7 @@ mdcn_status choose_path(const Attrs &a, const Problem &p, Path *out)
         *out = Path::Window;
         return MDCN_OK;
     case MDCN_PATH_WINDOW_FP8:
-        if (!window_eligible(p))
+        if (!window_eligible(p) && !window_eligible(p, true))
             return MDCN_E_PATH;
         *out = Path::WindowFp8;
         return MDCN_OK;
@@ -537,7 +566,17 @@ mdcn_status make_plan(const Attrs &a, const Problem &p, size_t workspace_bytes,
             return MDCN_E_PATH;                 // fused_eligible said some tile fits
         plan.xt_off = plan.wpack_bytes;
         if (windowed) {
-            if (!choose_window(p, &plan.win_tile, &plan.win_margin))
+            // E4M3 on groups of more than 256 output channels: the wide
+            // tiles (128 pixels x 512 channels; each sample is blended once
+            // for all of them rather than once per 256), unless
+            // MDCN_WIN_WIDE=0 or none fits
+            plan.win_wide = false;
+            if (plan.path == Path::WindowFp8 && p.Mg > 256) {
+                const char *env = std::getenv("MDCN_WIN_WIDE");
+                if (!(env && std::atoi(env) == 0))
+                    plan.win_wide = choose_window(p, true, &plan.win_tile, &plan.win_margin);
+            }
+            if (!plan.win_wide && !choose_window(p, false, &plan.win_tile, &plan.win_margin))
                 return MDCN_E_PATH;
             // the weight copies run 5 K steps ahead (the kernel's barrier
             // schedule needs exactly that); MDCN_WIN_CTAS=<n> caps the

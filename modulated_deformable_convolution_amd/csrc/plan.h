@@ -65,16 +65,23 @@ enum class FusedTile : int {
 };
 constexpr int kFusedTileCount = 4;
 
-// Output-pixel tile (rows x columns, 256 pixels) of the windowed fused
-// kernel.
+// Output-pixel tile (rows x columns) of the windowed fused kernel: 256
+// pixels x 256 output channels, or -- the wide tiles of the E4M3 variant on
+// groups of more than 256 output channels -- 128 pixels x 512 channels.
 enum class WindowTile : int {
     H16_W16 = 0,
     H8_W32 = 1,
     H32_W8 = 2,
     FLAT = 3,        // 256 consecutive output pixels in raster order (narrow images)
+    H8_W16 = 4,      // wide tiles
+    H16_W8 = 5,
+    FLAT128 = 6,     // 128 consecutive output pixels in raster order
 };
-constexpr int kWindowTileCount = 4;
+constexpr int kWindowTileCount = 4;      // tiles 0..3: 256 pixels
+constexpr int kWindowWideFirst = 4;      // tiles 4..6: 128 pixels x 512 channels
+constexpr int kWindowWideCount = 3;
 constexpr int kWindowPixels = 1280;      // input positions one LDS window can hold
+constexpr int kWindowPixelsWide = 1024;  // (wide tiles: their weight slots take the rest)
 constexpr int kWindowZeroBytes = 1024;   // zeroed LDS after each window (>= 16*columns + 32)
 constexpr int64_t kWindowMaxMargin = 8;  // default offset margin around the anchors
 constexpr int kWindowLead = 5;           // weight copies issued this many K steps ahead
@@ -112,6 +119,7 @@ struct Plan {
     FusedTile fused_tile;
     WindowTile win_tile;
     int64_t win_margin;          // window: pixels of margin around the tile's anchors
+    bool win_wide;               // window FP8: 128-pixel x 512-channel tiles
     int win_lead;                // window: K steps the weight copies run ahead (5)
     int64_t win_tiles_per_image; // window: output tiles (256 x 256) of one image, all groups
     int64_t win_slots;           // window: partial-sum slots
@@ -155,14 +163,18 @@ size_t fused_lds_bytes(const Problem &p, FusedTile t);
 int64_t window_extent(int64_t tile, int64_t stride, int64_t k, int64_t dil, int64_t margin);
 // Whether the windowed fused kernel can run this problem: fp16/bf16, 3x3
 // kernels, C/group a multiple of 16 inside one offset group, and some tile
-// whose window (with a margin of at least 2) fits in LDS.
-bool window_eligible(const Problem &p);
-// Tile and margin for the windowed kernel (false when none fits).
-bool choose_window(const Problem &p, WindowTile *tile, int64_t *margin);
+// (wide: some wide tile, on groups of more than 256 output channels) whose
+// window (with a margin of at least 2) fits in LDS.
+bool window_eligible(const Problem &p, bool wide = false);
+// Tile and margin for the windowed kernel among the 256-pixel tiles, or
+// (wide) the 128-pixel ones (false when none fits).
+bool choose_window(const Problem &p, bool wide, WindowTile *tile, int64_t *margin);
+// Whether a tile is one of the wide (128-pixel x 512-channel) tiles.
+bool window_tile_wide(WindowTile t);
 // Output tiles of one image (all groups) for a window tile shape.
 int64_t window_tiles_per_image(const Problem &p, WindowTile t);
-// Output rows a flat tile (256 consecutive pixels of rows Wo wide) can span.
-int64_t window_flat_rows(int64_t Wo);
+// Output rows a flat tile of n consecutive pixels (of rows Wo wide) can span.
+int64_t window_flat_rows(int64_t Wo, int64_t n);
 
 // Split the windowed kernel's (tile, chunk) units over `ncta` workgroups
 // (ncta <= kWindowSlots): bounds[j]..bounds[j+1] is the range of workgroup

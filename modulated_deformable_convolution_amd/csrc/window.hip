@@ -111,7 +111,6 @@ constexpr int kParkOff = kWoffOff + kWinInstr * kThreads * 4;  // a tile index p
 constexpr int kLdsTotal = kParkOff + 256;
 constexpr int kOmOff = kWin0 + kWinBuf;                 // offsets and masks of a tile
 constexpr int kOmPlanes = 3 * kTaps;                    // 2K offset + K mask channels
-constexpr int kOmInstr = kOmPlanes * 2;                 // 4-byte DMA instructions per tile
 static_assert(kOmPlanes * 256 * 2 <= kWinPlane, "a tile's offsets and masks fit plane 0");
 // A stages: the copy of step s+LEAD is issued in step s, into one of LEAD+1
 // stages.
@@ -129,26 +128,48 @@ static_assert(kAStage % (1024 * kWaves) == 0, "A DMA covers whole wave instructi
 
 // The E4M3 variant (F8) keeps one chunk's weight in LDS, in three slots that
 // the chunk's three MFMA groups read in turn: taps 0-3 and taps 4-7, each
-// [half h][16-byte part][256 rows][16 bytes] (part 0: taps 0 and 1 of the
-// row's 32 bytes, part 1: taps 2 and 3), and tap 8, [half h][256 rows][8 bytes].
-// Every part is the 8 channels 8h..8h+7 of one tap as E4M3 bytes.  The window
-// buffers, copy table and parked words follow the slots.
-constexpr int kF8Quad = 2 * 256 * 32;              // 16 KiB: four taps
-constexpr int kF8Single = 2 * 256 * 8;             // 4 KiB: the ninth tap
-constexpr int kF8Slots = 2 * kF8Quad + kF8Single;  // 36 KiB
-static_assert(kF8Quad % (1024 * kWaves) == 0 && kF8Single % (256 * kWaves) == 0,
-              "E4M3 weight DMA covers whole wave instructions");
-
-template <bool F8> struct WinLds {
-    static constexpr int win0 = F8 ? kF8Slots : kWin0;             // window buffer 0
-    static constexpr int woff = win0 + 2 * kWinBuf;                // window copy table
-    static constexpr int park = woff + kWinInstr * kThreads * 4;  // tile index per wave, flag
+// [half h][16-byte part][rows][16 bytes] (part 0: taps 0 and 1 of the row's
+// 32 bytes, part 1: taps 2 and 3), and tap 8, [half h][rows][8 bytes], for
+// the tile's 256 (wide tiles: 512) output channels.  Every part is the 8
+// channels 8h..8h+7 of one tap as E4M3 bytes.  The window buffers, copy
+// table and parked words follow the slots.
+//
+// The wide tiles (128 pixels x 512 output channels, E4M3 only) need 72 KiB of
+// weight slots, so their window buffers hold kWindowPixelsWide positions, the
+// window copy offsets stay in registers instead of the table, and in its
+// place is the exchange area through which the two waves of a SIMD pass each
+// other their halves of a group's E4M3 operand: [parity 2][wave pair 4]
+// [half 2][64 lanes][16 bytes].
+template <bool F8, bool WIDE> struct WinLds {
+    static constexpr int px = WIDE ? kWindowPixelsWide : kWindowPixels;  // window positions
+    static constexpr int plane = px * 16;                      // bytes of one window plane
+    static constexpr int plane1 = plane + kPlaneGap;           // start of plane 1
+    static constexpr int zero = plane1 + plane;                // start of the zero area
+    static constexpr int buf = zero + kWinZero;                // one window buffer
+    static constexpr int instr = 2 * px / 64 / kWaves;         // window DMA instructions per wave
+    static constexpr int rows = WIDE ? 512 : 256;              // output channels of a tile
+    static constexpr int quad = 2 * rows * 32;                 // E4M3 slot of four taps
+    static constexpr int single = 2 * rows * 8;                // E4M3 slot of the ninth tap
+    static constexpr int a8 = quad / 1024 / kWaves;            // E4M3 DMA instructions per wave and slot
+    static constexpr int win0 = F8 ? 2 * quad + single : kWin0;   // window buffer 0
+    static constexpr int woff = win0 + 2 * buf;                // window copy table (not WIDE)
+    static constexpr int xch = woff + (WIDE ? 0 : instr * kThreads * 4);   // exchange (WIDE)
+    static constexpr int park = xch + (WIDE ? 2 * 8192 : 0);   // tile index per wave, flag
     static constexpr int total = park + 256;
-    static constexpr int om = win0 + kWinBuf;                      // offsets and masks of a tile
+    static constexpr int om = win0 + buf;                      // offsets and masks of a tile
+    static_assert(!WIDE || F8, "wide tiles are E4M3 only");
     static_assert(total <= int(kLdsBytes), "LDS budget");
     static_assert(win0 % 1024 == 0, "window buffers start on a 1 KiB boundary");
+    static_assert(buf <= 65536, "window offsets fit 16 bits");
+    static_assert(px % 64 == 0 && (2 * px / 64) % kWaves == 0,
+                  "window DMA covers whole wave instructions, none straddling the two planes");
+    static_assert(quad % (1024 * kWaves) == 0 && single / 256 / kWaves == a8,
+                  "E4M3 weight DMA covers whole wave instructions");
+    static_assert(kOmPlanes * (WIDE ? 128 : 256) * 2 <= plane, "a tile's offsets and masks fit plane 0");
 };
-static_assert(WinLds<false>::total == kLdsTotal && WinLds<false>::om == kOmOff, "layout");
+static_assert(WinLds<false, false>::total == kLdsTotal && WinLds<false, false>::om == kOmOff &&
+                  WinLds<false, false>::buf == kWinBuf && WinLds<false, false>::instr == kWinInstr,
+              "layout");
 
 struct WinArgs {
     const void *A, *xt, *off, *msk, *bias;   // step-major weight, x blocks, offset, mask, bias|null
@@ -319,6 +340,34 @@ __device__ __forceinline__ void blend_f32(const uint4 (&c)[4], const float (&w)[
     }
 }
 
+// Four channels (elements 0..3 of each corner chunk) of a sample in fp32.
+template <typename T>
+__device__ __forceinline__ void blend_f32_4(const uint4 (&c)[4], const float (&w)[4], float zero,
+                                            float (&acc)[4])
+{
+    Vec16<T> v0, v1, v2, v3;
+    v0.raw = c[0]; v1.raw = c[1]; v2.raw = c[2]; v3.raw = c[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(to_f32(v0.e[e]), w[0], zero);
+        acc[e] = fmaf(to_f32(v1.e[e]), w[1], acc[e]);
+        acc[e] = fmaf(to_f32(v2.e[e]), w[2], acc[e]);
+        acc[e] = fmaf(to_f32(v3.e[e]), w[3], acc[e]);
+    }
+}
+
+// Four fp32 values as E4M3 bytes, saturated as in e4m3_of.
+__device__ __forceinline__ uint32_t e4m3_of4(float (&acc)[4])
+{
+    const float m = fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3])));
+    if (__builtin_amdgcn_ballot_w64(m > 448.0f) != 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[e] = sat_e4m3(acc[e]);
+    }
+    return pack4_e4m3_unsat(acc[0], acc[1], acc[2], acc[3]);
+}
+
 __device__ __forceinline__ uint2 e4m3_of(float (&acc)[8])
 {
     const float m = fmaxf(fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])),
@@ -342,7 +391,7 @@ __device__ __forceinline__ uint2 blend_e4m3(const uint4 (&c)[4], const float (&w
     return e4m3_of(acc);
 }
 
-template <typename T, int TH, int TW, int LEAD, bool F8>
+template <typename T, int TH, int TW, int LEAD, bool F8, bool WIDE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void window_kernel(WinArgs args)
@@ -350,8 +399,11 @@ void window_kernel(WinArgs args)
     (void)args;
     const KArgs pa = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
     KArgs a = fresh_args(pa);
-    static_assert(TH * TW == 256 && TW % 8 == 0, "a tile is 256 pixels, rows of 8-pixel vectors");
-    // TH = 1: a flat tile, 256 consecutive output pixels in raster order
+    // pixels and output channels of a tile
+    constexpr int kTilePx = WIDE ? 128 : 256;
+    constexpr int kTileM = WIDE ? 512 : 256;
+    static_assert(TH * TW == kTilePx && TW % 8 == 0, "a tile's pixels, rows of 8-pixel vectors");
+    // TH = 1: a flat tile, kTilePx consecutive output pixels in raster order
     // (ho0 holds its first pixel's index, wo0 is 0)
     constexpr bool kFlat = TH == 1;
     // output pixel (ho, wo) of the tile's pixel n
@@ -373,7 +425,11 @@ void window_kernel(WinArgs args)
     static_assert(LEAD == 5, "a barrier every third step needs a copy lead of 5 steps");
     constexpr int kAStages = 8;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    using L = WinLds<F8>;
+    using L = WinLds<F8, WIDE>;
+    // Sampling taps a wave blends: all 9, or on wide tiles 5 -- taps
+    // 2s, 2s+1, 4+2s, 5+2s and (channels 4s..4s+3 of each 8) tap 8, for s =
+    // wave / 4 -- as local taps 0..kLT-1.
+    constexpr int kLT = WIDE ? 5 : kTaps;
 
     const uint32_t lds0 = lds_addr(smem);
     uint32_t *woff_tab = reinterpret_cast<uint32_t *>(smem + L::woff);
@@ -382,7 +438,7 @@ void window_kernel(WinArgs args)
     // in the window); no copy ever writes them
     for (int i = int(threadIdx.x); i < 2 * kWinZero / 8; i += kThreads) {
         const int b = i / (kWinZero / 8), o = i - b * (kWinZero / 8);
-        *reinterpret_cast<uint2 *>(smem + L::win0 + b * kWinBuf + kWinZeroOff + o * 8) =
+        *reinterpret_cast<uint2 *>(smem + L::win0 + b * L::buf + L::zero + o * 8) =
             make_uint2(0u, 0u);
     }
 
@@ -428,11 +484,11 @@ void window_kernel(WinArgs args)
         ti.c_lo = int(max(r.u0, uint32_t(tile) * nch) - uint32_t(tile) * nch);
         ti.c_hi = int(min(r.u1, uint32_t(tile + 1) * nch) - uint32_t(tile) * nch);
         uint32_t bid = uint32_t(tile);
-        ti.m0 = int(bid % uint32_t(a->tiles_m)) * 256;
+        ti.m0 = int(bid % uint32_t(a->tiles_m)) * kTileM;
         bid /= uint32_t(a->tiles_m);
         ti.wo0 = int(bid % uint32_t(a->tiles_x)) * TW;
         bid /= uint32_t(a->tiles_x);
-        ti.ho0 = int(bid % uint32_t(a->tiles_y)) * (kFlat ? 256 : TH);
+        ti.ho0 = int(bid % uint32_t(a->tiles_y)) * (kFlat ? kTilePx : TH);
         bid /= uint32_t(a->tiles_y);
         ti.img = int(bid % uint32_t(a->cnt));
         ti.g = int(bid / uint32_t(a->cnt));
@@ -466,8 +522,19 @@ void window_kernel(WinArgs args)
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int half = lane >> 5;                  // plane: channels 8*half..+8 of a chunk
-        // the wave's 32 pixels (tile pixels 32*wave ..+32; lane: 32*wave + lane%32)
-        const int px_n = wave * 32 + (lane & 31);
+        // wide tiles: waves w and w + 4 (one SIMD) share 32 pixels, and take
+        // output channels 256*sub..+256 of the tile
+        const int pair = WIDE ? (wave & 3) : wave;
+        const int sub = WIDE ? (wave >> 2) : 0;
+        // the wave's 32 pixels (tile pixels 32*pair ..+32; lane: 32*pair + lane%32)
+        const int px_n = pair * 32 + (lane & 31);
+        // global tap of local tap lt
+        auto tap_of = [&](int lt) {
+            if constexpr (WIDE)
+                return lt < 4 ? (lt >> 1) * 4 + 2 * sub + (lt & 1) : 8;
+            else
+                return lt;
+        };
         KArgs a = fresh_args(pa);
         const v4i rx = srd(a->xt, a->chunk_bytes);
         const uint32_t hw16 = uint32_t(a->H * a->W) * 16;   // bytes of one 8-channel block plane
@@ -494,8 +561,9 @@ void window_kernel(WinArgs args)
         // ---- the tile's offsets and masks, by DMA into window buffer 1
         // (idle until the main loop's first step), issued before the copies
         // so that they do not queue behind them: instruction j carries
-        // channel j/2 of the offset group's 2K offset and K mask channels
-        // for tile pixels 128*(j%2) + 2*lane, +1 (an aligned 4-byte pair).
+        // channel j/kOmPer of the offset group's 2K offset and K mask channels
+        // for tile pixels 128*(j%kOmPer) + 2*lane, +1 (an aligned 4-byte pair).
+        constexpr int kOmPer = kTilePx / 128;
         const bool om_lds = a->om_lds != 0;
         if (om_lds) {
             const v4i ro = srd(a->off, a->off_bytes);
@@ -507,9 +575,10 @@ void window_kernel(WinArgs args)
             const uint32_t P = uint32_t(a->P);
             const uint32_t ob = uint32_t(img * a->offC + q * 2 * kTaps);
             const uint32_t mb = uint32_t(img * a->mskC + q * kTaps);
-            for (int j = wave; j < kOmInstr; j += kWaves) {
-                const int plane = j >> 1;
-                const int n = (j & 1) * 128 + 2 * lane;
+            for (int j = wave; j < kOmPlanes * kOmPer; j += kWaves) {
+                const int plane = int(unsigned(j) / kOmPer);
+                const int part = int(unsigned(j) % kOmPer);
+                const int n = part * 128 + 2 * lane;
                 int ho, wo;
                 out_pixel(n, ho0, wo0, Wo, ho, wo);
                 const bool ok = ho < Ho && wo < Wo;
@@ -517,47 +586,53 @@ void window_kernel(WinArgs args)
                 const uint32_t chan = is_off ? ob + uint32_t(plane)
                                              : mb + uint32_t(plane - 2 * kTaps);
                 const uint32_t voff = ok ? (chan * P + uint32_t(ho * Wo + wo)) * 2u : kOOB;
-                dma4(lds0 + uint32_t(L::om + plane * 512 + (j & 1) * 256), is_off ? ro : rm,
-                     voff, 0u);
+                dma4(lds0 + uint32_t(L::om + plane * (2 * kTilePx) + part * 256),
+                     is_off ? ro : rm, voff, 0u);
             }
         }
 
-        // ---- per-lane DMA source offsets of the window (kept in LDS; each
-        // thread reads back only its own entries) and of the A rows
+        // ---- per-lane DMA source offsets of the window (kept in LDS, each
+        // thread reading back only its own entries; wide tiles: in registers)
+        // and of the A rows
+        uint32_t wsrc[WIDE ? L::instr : 1];
         {
             // (the fields read once, before the table stores)
             const int WC = a->WC, WRC = a->WR * a->WC, H = a->H, W = a->W;
             const uint32_t img_base = uint32_t(img) * a->img_bytes;
             const float inv_wc = 1.0f / float(WC);
 #pragma unroll
-            for (int t = 0; t < kWinInstr; ++t) {
+            for (int t = 0; t < L::instr; ++t) {
                 const int S = (t * kWaves + wave) * 64 + lane;   // 16-byte slot of the buffer
-                const int pl = S >= kWindowPixels ? 1 : 0;       // S < 2 * kWindowPixels
-                const int px = S - pl * kWindowPixels;
+                const int pl = S >= L::px ? 1 : 0;               // S < 2 * L::px
+                const int px = S - pl * L::px;
                 // px / WC through a float reciprocal: px < 1280 and WC <= 64, so
                 // px/WC is at least 1/128 away from the next integer, far above
-                // the float error (the plane of slot S is S / 1280 likewise)
+                // the float error
                 const int r = int((float(px) + 0.5f) * inv_wc), c = px - r * WC;
                 const int gr = r0 + r, gc = c0 + c;
                 const bool ok = px < WRC && (unsigned)gr < (unsigned)H && (unsigned)gc < (unsigned)W;
-                woff_tab[t * kThreads + tid] =
+                const uint32_t v =
                     ok ? img_base + uint32_t(pl) * hw16 + uint32_t(gr * W + gc) * 16 : kOOB;
+                if constexpr (WIDE)
+                    wsrc[t] = v;
+                else
+                    woff_tab[t * kThreads + tid] = v;
             }
         }
-        // (F8: entries 0, 1 for the four-tap slots, 16-byte slot S = half S/512,
-        // part S/256 % 2, row S % 256; entries 2, 3 for the tap-8 slot, 4-byte
-        // slot S = half S/512, row S/2 % 256, word S % 2)
-        uint32_t aoff[F8 ? 4 : kAInstr];
+        // (F8, R = L::rows: entries 0..a8-1 for the four-tap slots, 16-byte
+        // slot S = half S/2R, part S/R % 2, row S % R; entries a8..2a8-1 for
+        // the tap-8 slot, 4-byte slot S = half S/2R, row S/2 % R, word S % 2)
+        uint32_t aoff[F8 ? 2 * L::a8 : kAInstr];
         if constexpr (F8) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < L::a8; ++t) {
                 const int S = (t * kWaves + wave) * 64 + lane;
-                const int pq = S >> 8, row = S & 255;
+                const int pq = S / L::rows, row = S % L::rows;
                 aoff[t] = (m0 + row < a->Mg) ? uint32_t(pq * a->Mg + m0 + row) * 16 : kOOB;
-                const int h = S >> 9, r2 = (S >> 1) & 255;
-                aoff[2 + t] = (m0 + r2 < a->Mg)
-                                  ? uint32_t(h * a->Mg + m0 + r2) * 8 + uint32_t(S & 1) * 4
-                                  : kOOB;
+                const int h = S / (2 * L::rows), r2 = (S >> 1) % L::rows;
+                aoff[L::a8 + t] = (m0 + r2 < a->Mg)
+                                      ? uint32_t(h * a->Mg + m0 + r2) * 8 + uint32_t(S & 1) * 4
+                                      : kOOB;
             }
         } else {
 #pragma unroll
@@ -572,14 +647,18 @@ void window_kernel(WinArgs args)
         auto issue_window = [&](int chunk, int buf) {
             const uint32_t soff =
                 __builtin_amdgcn_readfirstlane(ch_base + uint32_t(chunk * 2) * hw16);
-            uint32_t wo[kWinInstr];                 // all table reads first: one LDS wait
+            uint32_t wo[L::instr];                  // all table reads first: one LDS wait
 #pragma unroll
-            for (int t = 0; t < kWinInstr; ++t)
-                wo[t] = woff_tab[t * kThreads + tid];
+            for (int t = 0; t < L::instr; ++t) {
+                if constexpr (WIDE)
+                    wo[t] = wsrc[t];
+                else
+                    wo[t] = woff_tab[t * kThreads + tid];
+            }
 #pragma unroll
-            for (int t = 0; t < kWinInstr; ++t)
-                dma16(lds0 + L::win0 + buf * kWinBuf + (t * kWaves + wave) * 1024 +
-                          ((t * kWaves + wave) * 64 >= kWindowPixels ? kPlaneGap : 0),
+            for (int t = 0; t < L::instr; ++t)
+                dma16(lds0 + L::win0 + buf * L::buf + (t * kWaves + wave) * 1024 +
+                          ((t * kWaves + wave) * 64 >= L::px ? kPlaneGap : 0),
                       rx, wo[t], soff);
         };
         // K steps of the segment: step s (relative to its first chunk c_lo)
@@ -613,12 +692,13 @@ void window_kernel(WinArgs args)
                                                                  uint32_t(j) * a_region);
             if constexpr (j < 2) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    dma16(lds0 + j * kF8Quad + (t * kWaves + wave) * 1024, ra, aoff[t], soff);
+                for (int t = 0; t < L::a8; ++t)
+                    dma16(lds0 + j * L::quad + (t * kWaves + wave) * 1024, ra, aoff[t], soff);
             } else {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    dma4(lds0 + 2 * kF8Quad + (t * kWaves + wave) * 256, ra, aoff[2 + t], soff);
+                for (int t = 0; t < L::a8; ++t)
+                    dma4(lds0 + 2 * L::quad + (t * kWaves + wave) * 256, ra, aoff[L::a8 + t],
+                         soff);
             }
         };
 
@@ -634,33 +714,35 @@ void window_kernel(WinArgs args)
                     issue_a(s);
         }
 
-        // ---- sampling geometry of the lane's pixel, all taps: the byte
-        // offset of the top-left corner in a window buffer (16 bits, two taps
-        // per register: tap k in half k%2 of gpk[k/2]) and three factors from
-        // which the four corner weights are formed per step (see weights_of)
-        static_assert(kWinBuf <= 65536, "window offsets fit 16 bits");
-        uint32_t gpk[(kTaps + 1) / 2] = {};
-        float gw[kTaps][3];
-        uint32_t fbl = 0;                            // lane: tap k needs the fallback
+        // ---- sampling geometry of the lane's pixel, all (local) taps: the
+        // byte offset of the top-left corner in a window buffer (16 bits, two
+        // taps per register: local tap t in half t%2 of gpk[t/2]) and three
+        // factors from which the four corner weights are formed per step (see
+        // weights_of)
+        uint32_t gpk[(kLT + 1) / 2] = {};
+        float gw[kLT][3];
+        uint32_t fbl = 0;                            // lane: local tap t needs the fallback
         {
             const int P = a->P;
-            float oh[kTaps], ow[kTaps], mm[kTaps];
+            float oh[kLT], ow[kLT], mm[kLT];
             if (om_lds) {
                 // this wave's offset and mask copies (issued before the window
-                // and A copies, so older than the last kWinInstr + LEAD*kAInstr
+                // and A copies, so older than the last L::instr + LEAD*kAInstr
                 // of its copies) have landed, then every wave's
-                constexpr int N = kWinInstr + (F8 ? 2 : LEAD * kAInstr);
+                constexpr int N = L::instr + (F8 ? L::a8 : LEAD * kAInstr);
                 constexpr int kNoLgkm = 0x70 | 0xF00;
                 static_assert(N < 64, "vmcnt range");
                 __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
                 __builtin_amdgcn_s_barrier();
                 asm volatile("" ::: "memory");
                 const char *om = smem + L::om + px_n * 2;
+                constexpr int kOmPlane = 2 * kTilePx;
 #pragma unroll
-                for (int k = 0; k < kTaps; ++k) {
-                    oh[k] = to_f32(*reinterpret_cast<const T *>(om + (2 * k) * 512));
-                    ow[k] = to_f32(*reinterpret_cast<const T *>(om + (2 * k + 1) * 512));
-                    mm[k] = to_f32(*reinterpret_cast<const T *>(om + (2 * kTaps + k) * 512));
+                for (int lt = 0; lt < kLT; ++lt) {
+                    const int k = tap_of(lt);
+                    oh[lt] = to_f32(*reinterpret_cast<const T *>(om + (2 * k) * kOmPlane));
+                    ow[lt] = to_f32(*reinterpret_cast<const T *>(om + (2 * k + 1) * kOmPlane));
+                    mm[lt] = to_f32(*reinterpret_cast<const T *>(om + (2 * kTaps + k) * kOmPlane));
                 }
             } else {
                 int ho, wo;
@@ -672,10 +754,11 @@ void window_kernel(WinArgs args)
                 const T *off = static_cast<const T *>(a->off);
                 const T *msk = static_cast<const T *>(a->msk);
 #pragma unroll
-                for (int k = 0; k < kTaps; ++k) {
-                    oh[k] = to_f32(off[ob + size_t(2 * k) * P]);
-                    ow[k] = to_f32(off[ob + size_t(2 * k + 1) * P]);
-                    mm[k] = to_f32(msk[mb + size_t(k) * P]);
+                for (int lt = 0; lt < kLT; ++lt) {
+                    const int k = tap_of(lt);
+                    oh[lt] = to_f32(off[ob + size_t(2 * k) * P]);
+                    ow[lt] = to_f32(off[ob + size_t(2 * k + 1) * P]);
+                    mm[lt] = to_f32(msk[mb + size_t(k) * P]);
                 }
             }
             if (flag_pending) {
@@ -683,7 +766,7 @@ void window_kernel(WinArgs args)
                 // but this prologue's window and weight copies (the youngest
                 // vector memory operations) is complete after this wait,
                 // those stores included; then the flag
-                constexpr int N = kWinInstr + (F8 ? 2 : LEAD * kAInstr);
+                constexpr int N = L::instr + (F8 ? L::a8 : LEAD * kAInstr);
                 constexpr int kNoLgkmF = 0x70 | 0xF00;
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkmF);
@@ -700,43 +783,49 @@ void window_kernel(WinArgs args)
             out_pixel(px_n, ho0, wo0, a->Wo, ho, wo);
             const bool pv = ho < a->Ho && wo < a->Wo;
 #pragma unroll
-            for (int k = 0; k < kTaps; ++k) {
+            for (int lt = 0; lt < kLT; ++lt) {
+                const int k = tap_of(lt);
                 const int i = k / 3, j = k % 3;
                 const int ah = ho * a->sh - a->ph + i * a->dh;
                 const int aw = wo * a->sw - a->pw + j * a->dw;
                 const float lim = 33554432.0f;
-                const bool fin = fabsf(oh[k]) <= lim && fabsf(ow[k]) <= lim;
-                const float fh = fin ? floorf(oh[k]) : 0.0f;
-                const float fw = fin ? floorf(ow[k]) : 0.0f;
-                const float ly = fin ? oh[k] - fh : 0.0f;
-                const float lx = fin ? ow[k] - fw : 0.0f;
+                const bool fin = fabsf(oh[lt]) <= lim && fabsf(ow[lt]) <= lim;
+                const float fh = fin ? floorf(oh[lt]) : 0.0f;
+                const float fw = fin ? floorf(ow[lt]) : 0.0f;
+                const float ly = fin ? oh[lt] - fh : 0.0f;
+                const float lx = fin ? ow[lt] - fw : 0.0f;
                 const int h0 = ah + int(fh), w0 = aw + int(fw);
                 const bool any = pv && fin && h0 >= -1 && h0 < a->H && w0 >= -1 && w0 < a->W;
                 const int lr = h0 - r0, lc = w0 - c0;
                 const bool inw = (unsigned)lr <= unsigned(a->WR - 2) &&
                                  (unsigned)lc <= unsigned(a->WC - 2);
                 const bool use = any && inw;
-                const float m = use ? mm[k] : 0.0f;
-                gw[k][0] = (1.0f - lx) * m;
-                gw[k][1] = lx * m;
-                gw[k][2] = ly;
+                const float m = use ? mm[lt] : 0.0f;
+                gw[lt][0] = (1.0f - lx) * m;
+                gw[lt][1] = lx * m;
+                gw[lt][2] = ly;
+                // (wide tiles, tap 8: the wave's 4 channels are bytes 8s..8s+7
+                // of the 16-byte entry)
+                const uint32_t sub8 = (WIDE && lt == 4) ? uint32_t(sub * 8) : 0u;
                 const uint32_t wa =
-                    use ? uint32_t(half * kPlane1 + (lr * a->WC + lc) * 16) : uint32_t(kWinZeroOff);
-                gpk[k / 2] |= wa << (16 * (k % 2));
-                fbl |= uint32_t(any && !inw) << k;
+                    use ? uint32_t(half * L::plane1 + (lr * a->WC + lc) * 16) + sub8
+                        : uint32_t(L::zero);
+                gpk[lt / 2] |= wa << (16 * (lt % 2));
+                fbl |= uint32_t(any && !inw) << lt;
             }
         }
-        // wave-level: which tap has a lane that needs the fallback
+        // wave-level: which local tap has a lane that needs the fallback
         uint32_t fbw = 0;
 #pragma unroll
-        for (int b = 0; b < kTaps; ++b)
+        for (int b = 0; b < kLT; ++b)
             fbw |= uint32_t(__builtin_amdgcn_ballot_w64(((fbl >> b) & 1u) != 0u) != 0) << b;
         fbw = __builtin_amdgcn_readfirstlane(fbw);
 
-        // Fallback: the lane's 8 channels of the sample of tap k in chunk
-        // `chunk`, from global memory (rare).
-        auto fallback = [&](int k, int chunk, auto &bv) {
-            if ((fbl >> k) & 1u) {
+        // Fallback: the lane's 8 channels of the sample of local tap lt in
+        // chunk `chunk`, from global memory (rare).
+        auto fallback = [&](int lt, int chunk, auto &bv) {
+            if ((fbl >> lt) & 1u) {
+                const int k = tap_of(lt);
                 KArgs a = fresh_args(pa);
                 const T *offp = static_cast<const T *>(a->off);
                 const T *mskp = static_cast<const T *>(a->msk);
@@ -861,19 +950,31 @@ void window_kernel(WinArgs args)
             for (int i = 0; i < 8; ++i)
                 fa[i] = *reinterpret_cast<const uint4 *>(st + i * 32 * 16);
         };
-        // corners of tap k from window buffer `buf`
+        // corners of local tap k from window buffer `buf` (wide tiles, tap 8:
+        // the wave's 8 bytes of each, into .x and .y)
         auto read_corners = [&](uint4 (&cr)[4], int k, int buf) {
             const uint32_t bo =
-                __builtin_amdgcn_readfirstlane(uint32_t(L::win0 + (buf ? kWinBuf : 0)));
+                __builtin_amdgcn_readfirstlane(uint32_t(L::win0 + (buf ? L::buf : 0)));
             uint32_t pk = gpk[k / 2];
             asm volatile("" : "+v"(pk));                 // (not hoisted: see weights_of)
             const uint32_t wa = (k % 2) ? (pk >> 16) : (pk & 0xffffu);
             const char *p = smem + (wa + bo);
             const char *p2 = p + wrow;
-            cr[0] = *reinterpret_cast<const uint4 *>(p);
-            cr[1] = *reinterpret_cast<const uint4 *>(p + 16);
-            cr[2] = *reinterpret_cast<const uint4 *>(p2);
-            cr[3] = *reinterpret_cast<const uint4 *>(p2 + 16);
+            if (WIDE && k == 4) {
+                const uint2 v0 = *reinterpret_cast<const uint2 *>(p);
+                const uint2 v1 = *reinterpret_cast<const uint2 *>(p + 16);
+                const uint2 v2 = *reinterpret_cast<const uint2 *>(p2);
+                const uint2 v3 = *reinterpret_cast<const uint2 *>(p2 + 16);
+                cr[0].x = v0.x; cr[0].y = v0.y;
+                cr[1].x = v1.x; cr[1].y = v1.y;
+                cr[2].x = v2.x; cr[2].y = v2.y;
+                cr[3].x = v3.x; cr[3].y = v3.y;
+            } else {
+                cr[0] = *reinterpret_cast<const uint4 *>(p);
+                cr[1] = *reinterpret_cast<const uint4 *>(p + 16);
+                cr[2] = *reinterpret_cast<const uint4 *>(p2);
+                cr[3] = *reinterpret_cast<const uint4 *>(p2 + 16);
+            }
         };
 
         if constexpr (!F8) {
@@ -921,10 +1022,10 @@ void window_kernel(WinArgs args)
                     const bool a_prev = s >= 1 && s - 1 + LEAD < steps;   // copied in step s-1
                     if (k == 3 && !last_chunk) {
                         if (own) {
-                            constexpr int N = 2 * kAInstr + kWinInstr;
+                            constexpr int N = 2 * kAInstr + L::instr;
                             __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
                         } else {
-                            constexpr int N = kAInstr + kWinInstr;
+                            constexpr int N = kAInstr + L::instr;
                             __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
                         }
                     } else if (a_prev && own) {
@@ -1014,25 +1115,33 @@ void window_kernel(WinArgs args)
             // ends phase p: every wave's copy of A(p) has landed (each wave
             // waits for its own copies, then the barrier) and, for p = 3c+1,
             // the window of chunk c+1, whose first corners phase p+1 reads.
-            // After X_p each wave issues its share of A(p+2) into slot
+            // During phase p+1 each wave issues its share of A(p+2) into slot
             // (p+2) % 3, the slot of A(p-1), whose MFMAs ran in phase p, and,
-            // for p = 3c+1, the window of chunk c+2 into the buffer of chunk
-            // c, last read in phase p.  In flight at X_p besides what it waits
-            // for: A(p+1) and the windows issued after X_{p-1} (p = 3c+2) or
-            // after X_{p-2} with A(p) (p = 3c+3).
+            // for p = 3c+1, then the window of chunk c+2 into the buffer of
+            // chunk c, last read in phase p -- spread through the phase, one
+            // copy instruction after every 8/D of its MFMAs (D: the phase's
+            // copy instructions), so that the texture unit works through
+            // them while the waves compute instead of stalling every wave's
+            // issue right after the barrier.  In flight at X_p besides what
+            // it waits for: A(p+1) and the windows issued in phase p (p =
+            // 3c+2) or in phase p-1 with A(p) (p = 3c+3).
             const int nseg = c_hi - c_lo;
             const int nq = 3 * nseg;
             const int hh = lane >> 5;
-            // the lane's A fragment of block i: four-tap slot j part p at
-            // j*kF8Quad + q8_lane + p*4096 + i*512; tap-8 slot at s8_lane + i*256
-            const uint32_t q8_lane = uint32_t(hh * 8192 + (lane & 31) * 16);
-            const uint32_t s8_lane = uint32_t(2 * kF8Quad + hh * 2048 + (lane & 31) * 8);
+            // the lane's A fragment of block i (slot row 256*sub + 32i + lane%32,
+            // R = L::rows): four-tap slot j part p at j*L::quad + q8_lane +
+            // p*16R + i*512; tap-8 slot at s8_lane + i*256
+            const int arow = sub * 256 + (lane & 31);
+            const uint32_t q8_lane = uint32_t(hh * (32 * L::rows) + arow * 16);
+            const uint32_t s8_lane = uint32_t(2 * L::quad + hh * (8 * L::rows) + arow * 8);
             constexpr int kNoLgkm = 0x70 | 0xF00;
+            // (wide tiles: a barrier also waits for the wave's exchange store)
+            constexpr int kBarLgkm = WIDE ? 0x70 : kNoLgkm;
 
             uint4 cr[4];
             read_corners(cr, 0, 0);
-            // after the prologue's wait and barrier: A(1), window(1)
-            issue_a8(0, std::integral_constant<int, 1>{});
+            // after the prologue's wait and barrier: window(1) (A(1) goes out
+            // in phase 0)
             if (nseg > 1)
                 issue_window(c_lo + 1, 1);
 
@@ -1042,9 +1151,9 @@ void window_kernel(WinArgs args)
 
             // A fragment of block i of group jm (compile time) from its slot
             auto frag64 = [&](int jm, int i) {
-                const char *st = smem + (uint32_t(jm * kF8Quad) + q8_lane);
+                const char *st = smem + (uint32_t(jm * L::quad) + q8_lane);
                 const int4v lo = *reinterpret_cast<const int4v *>(st + i * 512);
-                const int4v hi = *reinterpret_cast<const int4v *>(st + 4096 + i * 512);
+                const int4v hi = *reinterpret_cast<const int4v *>(st + 16 * L::rows + i * 512);
                 return int8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             };
             auto frag16 = [&](int i) {
@@ -1061,45 +1170,122 @@ void window_kernel(WinArgs args)
                 const bool w_younger = (j == 2 && rc + 2 < nseg) || (j == 0 && rc >= 1 &&
                                                                      rc + 1 < nseg);
                 if (p == 0) {
-                    // A(0) landed before the loop; A(1), window(1) may fly
-                    __builtin_amdgcn_s_waitcnt(
-                        ((2 + kWinInstr) & 15) | (((2 + kWinInstr) >> 4) << 14) | kNoLgkm);
+                    // A(0) landed before the loop; window(1), A(1) may fly
+                    constexpr int N = L::a8 + L::instr;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kBarLgkm);
                 } else if (a_next && w_younger) {
-                    constexpr int N = 2 + kWinInstr;
-                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    constexpr int N = L::a8 + L::instr;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kBarLgkm);
                 } else if (a_next) {
-                    constexpr int N = 2;
-                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    constexpr int N = L::a8;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kBarLgkm);
                 } else if (w_younger) {
-                    constexpr int N = kWinInstr;
-                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kNoLgkm);
+                    constexpr int N = L::instr;
+                    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | kBarLgkm);
                 } else {
-                    __builtin_amdgcn_s_waitcnt(kNoLgkm);
+                    __builtin_amdgcn_s_waitcnt(kBarLgkm);
                 }
                 __builtin_amdgcn_s_barrier();
-                constexpr int j2 = (j + 2) % 3;
-                if (p + 2 < nq)
-                    issue_a8(rc + (j + 2) / 3, std::integral_constant<int, j2>{});
-                if (j == 1 && rc + 2 < nseg)
-                    issue_window(c_lo + rc + 2, rc & 1);
             };
 
             // Phase p = 3*rc + j: blend group (rc, j) into bcur while the
-            // MFMAs of group p-1 (type jm, operand bprev) run, if any.
+            // MFMAs of group p-1 (type jm, operand bprev) run, if any.  Wide
+            // tiles: each wave of a SIMD blends half of the group (local taps
+            // 2j, 2j+1 -- its two of the four -- or its 4 channels of tap 8)
+            // and stores its E4M3 bytes into the pair's exchange entry of
+            // parity p % 2: [half s][lane][16 bytes] (tap 8: [half s][lane][4
+            // bytes]); the MFMAs of group p, in phase p+1, read both halves
+            // back -- the bytes of half s are exactly the operand's bytes
+            // 16s..16s+15 (tap 8: 4s..4s+3) -- after barrier X_p, which waits
+            // for the stores.  The entry is written again in phase p+2, after
+            // barrier X_{p+1}, by when both reads have returned.
             auto phase = [&](int rc, auto jc, auto mfc) {
                 constexpr int j = decltype(jc)::value;
                 constexpr bool mfma = decltype(mfc)::value;
                 constexpr int jm = (j + 2) % 3;            // the previous group's type
-                constexpr int k0 = 4 * j;                  // first tap
-                constexpr int nt = j < 2 ? 4 : 1;          // taps
+                constexpr int nt = j < 2 ? (WIDE ? 2 : 4) : 1;   // (local) taps
+                constexpr int k0 = (WIDE ? 2 : 4) * j;     // first local tap
                 constexpr int per = 8 / nt;                // MFMAs per tap
                 const int chunk = c_lo + rc;
+                const int p = 3 * rc + j;
                 // phase 0 of the segment has no previous group: its MFMAs
                 // multiply zero fragments (whatever the slot holds)
                 const bool live = j != 0 || rc > 0;
-                const int8v bop64 = {int(bprev[0]), int(bprev[1]), int(bprev[2]), int(bprev[3]),
-                                     int(bprev[4]), int(bprev[5]), int(bprev[6]), int(bprev[7])};
-                const long bop16 = long(uint64_t(bprev[0]) | (uint64_t(bprev[1]) << 32));
+                int8v bop64 = {};
+                long bop16 = 0;
+                if constexpr (WIDE) {
+                    const char *xr =
+                        smem + (uint32_t(L::xch + ((p + 1) & 1) * 8192) + uint32_t(pair * 2048));
+                    if constexpr (jm < 2) {
+                        const int4v lo = *reinterpret_cast<const int4v *>(xr + lane * 16);
+                        const int4v hi = *reinterpret_cast<const int4v *>(xr + 1024 + lane * 16);
+                        bop64 = int8v(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    } else {
+                        const uint32_t d0 = *reinterpret_cast<const uint32_t *>(xr + lane * 4);
+                        const uint32_t d1 =
+                            *reinterpret_cast<const uint32_t *>(xr + 256 + lane * 4);
+                        bop16 = live ? long(uint64_t(d0) | (uint64_t(d1) << 32)) : 0;
+                    }
+                } else {
+                    bop64 = int8v{int(bprev[0]), int(bprev[1]), int(bprev[2]), int(bprev[3]),
+                                  int(bprev[4]), int(bprev[5]), int(bprev[6]), int(bprev[7])};
+                    bop16 = long(uint64_t(bprev[0]) | (uint64_t(bprev[1]) << 32));
+                }
+                // This phase's copies: A(p+1) (type ja of relative chunk rca)
+                // and, for j = 2, then the window of chunk rc+2, as kD
+                // instructions, instruction d after MFMA d*kStride.  A copy
+                // past the segment's end is not skipped by a branch, which
+                // would split the tap's block: its scalar offset is 2^31
+                // instead, which takes a lane's offset past the buffer's
+                // range (zeros) or, for a lane already at kOOB, wraps around
+                // to an in-range read -- either way it fills a slot or
+                // buffer that no wave reads again in this segment (and the
+                // next tile's copies are issued after the main loop's final
+                // full wait).
+                constexpr int ja = (j + 1) % 3;
+                const int rca = rc + (j + 1) / 3;
+                constexpr int kD = L::a8 + (j == 2 ? L::instr : 0);
+                constexpr int kStride = kD >= 8 ? 1 : 8 / kD;
+                static_assert(kD <= 8, "one copy instruction per MFMA at most");
+                const bool dma_a = p + 1 < nq;
+                const bool dma_w = j == 2 && rc + 2 < nseg;
+                const uint32_t soff_a = __builtin_amdgcn_readfirstlane(
+                    dma_a ? uint32_t(c_lo + rca) * a_chunk + uint32_t(ja) * a_region : kOOB);
+                const uint32_t soff_w = __builtin_amdgcn_readfirstlane(
+                    dma_w ? ch_base + uint32_t((c_lo + rc + 2) * 2) * hw16 : kOOB);
+                // window copy source offsets, each read one copy ahead (the
+                // 256-channel kernels keep them in the LDS table: registers
+                // for all of them would spill)
+                auto woff_entry = [&](int t) {
+                    if constexpr (WIDE)
+                        return wsrc[t];
+                    else
+                        return woff_tab[t * kThreads + tid];
+                };
+                uint32_t wcur = 0;
+                if constexpr (j == 2)
+                    wcur = woff_entry(0);
+                auto copy_after = [&](int i) {
+                    if (i % kStride != 0 || i / kStride >= kD)
+                        return;
+                    const int d = i / kStride;
+                    if (d < L::a8) {
+                        if constexpr (ja < 2)
+                            dma16(lds0 + ja * L::quad + (d * kWaves + wave) * 1024, ra, aoff[d],
+                                  soff_a);
+                        else
+                            dma4(lds0 + 2 * L::quad + (d * kWaves + wave) * 256, ra,
+                                 aoff[L::a8 + d], soff_a);
+                    } else if constexpr (j == 2) {
+                        const int t = d - L::a8;
+                        const uint32_t wo = wcur;
+                        if (t + 1 < L::instr)
+                            wcur = woff_entry(t + 1);
+                        dma16(lds0 + L::win0 + uint32_t(rc & 1) * L::buf + (t * kWaves + wave) * 1024 +
+                                  ((t * kWaves + wave) * 64 >= L::px ? kPlaneGap : 0),
+                              rx, wo, soff_w);
+                    }
+                };
                 // fragments of MFMAs i and i+1 in flight (read two ahead)
                 int8v f64[2];
                 long f16[2];
@@ -1127,11 +1313,12 @@ void window_kernel(WinArgs args)
                                                                             0, 0);
                     }
                 };
+                uint32_t own[4] = {};                      // wide: the wave's half
 #pragma unroll
                 for (int tt = 0; tt < nt; ++tt) {
                     const int k = k0 + tt;
-                    const int k1 = (k + 1) % kTaps;
-                    const int buf1 = (k + 1 >= kTaps) ? ((rc + 1) & 1) : (rc & 1);
+                    const int k1 = (k + 1) % kLT;
+                    const int buf1 = (k + 1 >= kLT) ? ((rc + 1) & 1) : (rc & 1);
                     uint4 cn[4];
                     read_corners(cn, k1, buf1);
                     float w[4];
@@ -1139,37 +1326,79 @@ void window_kernel(WinArgs args)
                     // the tap's share of the previous group's MFMAs, spread
                     // through its blend FMAs (one basic block: the scheduler
                     // interleaves them as the group barriers ask)
-                    if constexpr (mfma) {
 #pragma unroll
-                        for (int u = 0; u < per; ++u)
+                    for (int u = 0; u < per; ++u) {
+                        if constexpr (mfma)
                             mma(tt * per + u);
+                        copy_after(tt * per + u);
                     }
-                    float bf[8];
-                    blend_f32<T>(cr, w, zero, bf);
-                    if constexpr (mfma) {
+                    if (WIDE && k == 4) {
+                        // wide tiles, tap 8: the wave's 4 channels
+                        float bf[4];
+                        blend_f32_4<T>(cr, w, zero, bf);
+                        if constexpr (mfma) {
 #pragma unroll
-                        for (int u = 0; u < per; ++u) {
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-                            __builtin_amdgcn_sched_group_barrier(0x002, 32 / per, 0);   // VALU
+                            for (int u = 0; u < per; ++u) {
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                                __builtin_amdgcn_sched_group_barrier(0x002, 16 / per, 0);
+                            }
+                        }
+                        const uint32_t b4 = e4m3_of4(bf);
+                        uint2 b8 = make_uint2(b4, b4);
+                        if (fbw & (1u << k))
+                            fallback(k, chunk, b8);
+                        own[0] = sub ? b8.y : b8.x;
+                    } else {
+                        float bf[8];
+                        blend_f32<T>(cr, w, zero, bf);
+                        if constexpr (mfma) {
+#pragma unroll
+                            for (int u = 0; u < per; ++u) {
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+                                __builtin_amdgcn_sched_group_barrier(0x002, 32 / per, 0);   // VALU
+                            }
+                        }
+                        uint2 b8 = e4m3_of(bf);
+                        if (fbw & (1u << k))
+                            fallback(k, chunk, b8);
+                        if constexpr (WIDE) {
+                            own[2 * tt] = b8.x;
+                            own[2 * tt + 1] = b8.y;
+                        } else {
+                            bcur[2 * tt] = b8.x;
+                            bcur[2 * tt + 1] = b8.y;
                         }
                     }
-                    uint2 b8 = e4m3_of(bf);
-                    if (fbw & (1u << k))
-                        fallback(k, chunk, b8);
-                    bcur[2 * tt] = b8.x;
-                    bcur[2 * tt + 1] = b8.y;
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         cr[c] = cn[c];
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                if constexpr (WIDE) {
+                    char *xw = smem + (uint32_t(L::xch + (p & 1) * 8192) + uint32_t(pair * 2048));
+                    if constexpr (j < 2)
+                        *reinterpret_cast<uint4 *>(xw + sub * 1024 + lane * 16) =
+                            make_uint4(own[0], own[1], own[2], own[3]);
+                    else
+                        *reinterpret_cast<uint32_t *>(xw + sub * 256 + lane * 4) = own[0];
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    bprev[e] = bcur[e];
+                    for (int e = 0; e < 8; ++e)
+                        bprev[e] = bcur[e];
+                }
             };
             // the last group's MFMAs (type 2), after the last phase's barrier
             auto tail = [&]() {
-                const long bop16 = long(uint64_t(bprev[0]) | (uint64_t(bprev[1]) << 32));
+                long bop16;
+                if constexpr (WIDE) {
+                    const char *xr = smem + (uint32_t(L::xch + ((nq - 1) & 1) * 8192) +
+                                             uint32_t(pair * 2048));
+                    const uint32_t d0 = *reinterpret_cast<const uint32_t *>(xr + lane * 4);
+                    const uint32_t d1 = *reinterpret_cast<const uint32_t *>(xr + 256 + lane * 4);
+                    bop16 = long(uint64_t(d0) | (uint64_t(d1) << 32));
+                } else {
+                    bop16 = long(uint64_t(bprev[0]) | (uint64_t(bprev[1]) << 32));
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(bop16, frag16(i), acc[i],
@@ -1239,7 +1468,8 @@ void window_kernel(WinArgs args)
             // ---- the tile's last chunks: + bias in fp32, one rounding,
             // stores straight from the accumulators.  Register r of block i
             // holds output channel m0 + 32i + lane%32 at tile pixel
-            // 32*wave + 8(r/4) + 4(lane/32) + r%4.  For each half h of the
+            // 32*wave + 8(r/4) + 4(lane/32) + r%4 (wide tiles: channel
+            // m0 + 256*(wave/4) + 32i + lane%32 at pixel 32*(wave%4) + ...).  For each half h of the
             // wave's 32 pixels, one lane swap (v_permlane32_swap: lanes
             // 32..63 of the first register with lanes 0..31 of the second)
             // gives lanes < 32 pixels 16h..16h+7 and lanes >= 32 pixels
@@ -1248,6 +1478,7 @@ void window_kernel(WinArgs args)
             // waits for every older store): the bias comes first.
             const int Mg = a->Mg, P = a->P, Ho = a->Ho, Wo = a->Wo;
             const int wv = tid >> 6, ln = tid & 63;
+            const int wsub = WIDE ? (wv >> 2) : 0, wpair = WIDE ? (wv & 3) : wv;
             float bv[8];
             float sv[8];                             // F8: the rows' 2^-e
             {
@@ -1256,7 +1487,7 @@ void window_kernel(WinArgs args)
                 const bool poison = te.c_lo > 0 && *gave_up_l != 0;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const int m = te.m0 + 32 * i + (ln & 31);
+                    const int m = te.m0 + 256 * wsub + 32 * i + (ln & 31);
                     bv[i] = (bias && m < Mg) ? to_f32(bias[size_t(te.g) * Mg + m]) : 0.0f;
                     if (poison)
                         bv[i] = __builtin_nanf("");
@@ -1273,7 +1504,7 @@ void window_kernel(WinArgs args)
             const bool vec = a->vec_out != 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int m = te.m0 + 32 * i + (ln & 31);
+                const int m = te.m0 + 256 * wsub + 32 * i + (ln & 31);
                 const bool mok = m < Mg;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -1294,7 +1525,7 @@ void window_kernel(WinArgs args)
                     const auto w1 = __builtin_amdgcn_permlane32_swap(v1, v3, false, false);
                     const u32x4 ov = {uint32_t(w0[0]), uint32_t(w1[0]), uint32_t(w0[1]),
                                       uint32_t(w1[1])};
-                    const int n = wv * 32 + 16 * h + 8 * (ln >> 5);
+                    const int n = wpair * 32 + 16 * h + 8 * (ln >> 5);
                     int ho, wo;
                     out_pixel(n, te.ho0, te.wo0, Wo, ho, wo);
                     const bool ok = mok && ho < Ho && wo < Wo;
@@ -1356,7 +1587,7 @@ bool split_cached(int64_t tiles, int64_t nch, int64_t ncta, int64_t seg_x4, uint
     return true;
 }
 
-template <typename T, int TH, int TW, int LEAD, bool F8>
+template <typename T, int TH, int TW, int LEAD, bool F8, bool WIDE>
 hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,
                       const float *wscale, const void *xt, const void *offset, const void *mask,
                       const void *bias, void *out, const WindowScratch &ws, hipStream_t s)
@@ -1370,12 +1601,13 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
     a.dh = int(p.dh); a.dw = int(p.dw);
     a.margin = int(plan.win_margin);
     constexpr bool flat = TH == 1;
-    a.WR = int(window_extent(flat ? window_flat_rows(p.Wo) : TH, p.sh, p.kh, p.dh,
+    constexpr int tile_px = TH * TW, tile_m = WIDE ? 512 : 256;
+    a.WR = int(window_extent(flat ? window_flat_rows(p.Wo, tile_px) : TH, p.sh, p.kh, p.dh,
                              plan.win_margin));
     a.WC = int(window_extent(flat ? p.Wo : TW, p.sw, p.kw, p.dw, plan.win_margin));
-    a.tiles_y = int(flat ? (p.P + 255) / 256 : (p.Ho + TH - 1) / TH);
+    a.tiles_y = int(flat ? (p.P + tile_px - 1) / tile_px : (p.Ho + TH - 1) / TH);
     a.tiles_x = int(flat ? 1 : (p.Wo + TW - 1) / TW);
-    a.tiles_m = int((p.Mg + 255) / 256);
+    a.tiles_m = int((p.Mg + tile_m - 1) / tile_m);
     a.cnt = int(cnt);
     a.offC = int(2 * p.DG * p.K);
     a.mskC = int(p.DG * p.K);
@@ -1404,7 +1636,7 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
                    : uint32_t(size_t(p.Mg) * p.Kg * sizeof(T));
     if (F8 && !wscale)
         return hipErrorInvalidValue;
-    if (a.WR * a.WC > kWindowPixels || a.WC * 16 + 32 > kWinZero)
+    if (a.WR * a.WC > WinLds<F8, WIDE>::px || a.WC * 16 + 32 > kWinZero)
         return hipErrorInvalidValue;
     const uint64_t tiles = uint64_t(p.G) * cnt * a.tiles_y * a.tiles_x * a.tiles_m;
     if (tiles == 0)
@@ -1425,8 +1657,8 @@ hipError_t window_cfg(const Problem &p, const Plan &plan, int64_t cnt, const voi
     if (!split_cached(int64_t(tiles), int64_t(a.nch), int64_t(blocks), plan.win_seg_cost_x4,
                       a.bounds))
         return hipErrorInvalidValue;
-    auto kern = window_kernel<T, TH, TW, LEAD, F8>;
-    constexpr int lds = WinLds<F8>::total;
+    auto kern = window_kernel<T, TH, TW, LEAD, F8, WIDE>;
+    constexpr int lds = WinLds<F8, WIDE>::total;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess)
@@ -1445,11 +1677,20 @@ hipError_t window_lead(const Problem &p, const Plan &plan, int64_t cnt, const vo
 {
     if (plan.win_lead != 5)
         return hipErrorInvalidValue;
-    if (plan.path == Path::WindowFp8)
-        return window_cfg<T, TH, TW, 5, true>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias,
-                                              out, ws, s);
-    return window_cfg<T, TH, TW, 5, false>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias,
-                                           out, ws, s);
+    if constexpr (TH * TW == 128) {
+        if (plan.path != Path::WindowFp8 || !plan.win_wide)
+            return hipErrorInvalidValue;
+        return window_cfg<T, TH, TW, 5, true, true>(p, plan, cnt, wpack, wscale, xt, offset, mask,
+                                                    bias, out, ws, s);
+    } else {
+        if (plan.win_wide)
+            return hipErrorInvalidValue;
+        if (plan.path == Path::WindowFp8)
+            return window_cfg<T, TH, TW, 5, true, false>(p, plan, cnt, wpack, wscale, xt, offset,
+                                                         mask, bias, out, ws, s);
+        return window_cfg<T, TH, TW, 5, false, false>(p, plan, cnt, wpack, wscale, xt, offset,
+                                                      mask, bias, out, ws, s);
+    }
 }
 
 template <typename T>
@@ -1469,6 +1710,15 @@ hipError_t window_t(const Problem &p, const Plan &plan, int64_t cnt, const void 
                                      ws, s);
     case WindowTile::FLAT:
         return window_lead<T, 1, 256>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out,
+                                      ws, s);
+    case WindowTile::H8_W16:
+        return window_lead<T, 8, 16>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out,
+                                     ws, s);
+    case WindowTile::H16_W8:
+        return window_lead<T, 16, 8>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out,
+                                     ws, s);
+    case WindowTile::FLAT128:
+        return window_lead<T, 1, 128>(p, plan, cnt, wpack, wscale, xt, offset, mask, bias, out,
                                       ws, s);
     }
     return hipErrorInvalidValue;

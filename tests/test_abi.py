@@ -464,12 +464,14 @@ def test_fp8_path_plan():
     assert {"prep_nhwc_fp8", "deform_gather_fp8", "gemm_fp8_bias"} <= set(names)
 
 
-def test_window_fp8_path_plan():
+def test_window_fp8_path_plan(monkeypatch):
     """The windowed FP8 path: the window path's tiles, margin, chunking and
     partial-sum slots, with the 16-bit step-major weight replaced by the E4M3
     chunk blocks (144 bytes per output channel and 16-channel chunk) and one
-    fp32 scale per output channel.  Eligible where the window path is; never
-    the automatic choice."""
+    fp32 scale per output channel; on groups of more than 256 output channels
+    the wide tiles (128 pixels x 512 channels, windows of at most 1024
+    positions).  Eligible where the window path is; never the automatic
+    choice."""
     op = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_WINDOW_FP8)
     win = mdcn.mdcn_create(1, 1, 1, 1, 1, path=mdcn.MDCN_PATH_WINDOW)
     for dt in (mdcn.MDCN_F16, mdcn.MDCN_BF16):
@@ -481,8 +483,39 @@ def test_window_fp8_path_plan():
         d, tile, margin = _win_desc(op, dt, DIMS)
         assert d.startswith("path=window_fp8") and tile == 0 and margin == 8
     d40 = [16, 512, 40, 40, 16, 18, 40, 40, 16, 9, 40, 40, 512, 512, 3, 3]
+    # 40x40, Mg = 512: flat 128-pixel tiles, 5 rows of 40 output pixels ->
+    # a window of (4 + 2 + 2 + 2m) x (39 + 2 + 2 + 2m) <= 1024 positions:
+    # m = 5 (18 x 53); 13 tiles of one image, 16 images -> 208 slots
     d, tile, margin = _win_desc(op, mdcn.MDCN_F16, d40)
-    assert d.startswith("path=window_fp8") and tile == 3 and margin == 6
+    assert d.startswith("path=window_fp8") and tile == 6 and margin == 5
+    assert "slots=208" in d
+    # MDCN_WIN_WIDE=0: the 256-pixel tiles (flat, 8 rows: m = 6), each image
+    # 7 tiles x 2 channel halves -> 224 slots
+    monkeypatch.setenv("MDCN_WIN_WIDE", "0")
+    d, tile, margin = _win_desc(op, mdcn.MDCN_F16, d40)
+    assert tile == 3 and margin == 6 and "slots=224" in d
+    monkeypatch.delenv("MDCN_WIN_WIDE")
+    # a forced wide tile: 8 x 16 (window (7+4+2m) x (15+4+2m): m = 8, 27 x 35)
+    monkeypatch.setenv("MDCN_WIN_TILE", "4")
+    d, tile, margin = _win_desc(op, mdcn.MDCN_F16, d40)
+    assert tile == 4 and margin == 8
+    # a narrow tile asked for a wide problem is not one of the wide tiles:
+    # the planner's own choice
+    monkeypatch.setenv("MDCN_WIN_TILE", "0")
+    d, tile, margin = _win_desc(op, mdcn.MDCN_F16, d40)
+    assert tile == 6 and margin == 5
+    monkeypatch.delenv("MDCN_WIN_TILE")
+    # more than 256 but not 512 output channels per group: wide as well
+    # (one 512-row tile, rows past Mg unused); 256: the narrow tiles
+    d384 = [2, 64, 24, 24, 2, 18, 24, 24, 2, 9, 24, 24, 384, 64, 3, 3]
+    d, tile, margin = _win_desc(op, mdcn.MDCN_BF16, d384)
+    assert tile in (4, 5, 6)
+    d256 = [2, 64, 24, 24, 2, 18, 24, 24, 2, 9, 24, 24, 256, 64, 3, 3]
+    d, tile, margin = _win_desc(op, mdcn.MDCN_BF16, d256)
+    assert tile in (0, 1, 2, 3)
+    # the 16-bit window path never takes them
+    d, tile, margin = _win_desc(win, mdcn.MDCN_F16, d40)
+    assert tile in (0, 1, 2, 3)
     # the window path's limits: fp32 and a 5x5 kernel are refused
     for dtype, dims in [(mdcn.MDCN_F32, DIMS),
                         (mdcn.MDCN_F16, _fused_dims(1, 32, 12, 12, 32, 5, 1, 1))]:

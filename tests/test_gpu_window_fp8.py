@@ -130,8 +130,10 @@ def test_window_fp8_random_inputs(name, dtype):
 @pytest.mark.parametrize("tile,margin", [(0, 8), (1, 2), (2, 8), (3, 3)])
 @pytest.mark.parametrize("name", ["multi_tile", "far_offsets", "three_chunks"])
 def test_window_fp8_every_tile(tile, margin, name, monkeypatch):
-    """Each tile shape (MDCN_WIN_TILE) with a narrow margin (many samples
-    through the fallback) or the default one (MDCN_WIN_MARGIN)."""
+    """Each 256-pixel tile shape (MDCN_WIN_TILE; MDCN_WIN_WIDE=0 keeps the
+    groups of more than 256 channels on them) with a narrow margin (many
+    samples through the fallback) or the default one (MDCN_WIN_MARGIN)."""
+    monkeypatch.setenv("MDCN_WIN_WIDE", "0")
     monkeypatch.setenv("MDCN_WIN_TILE", str(tile))
     monkeypatch.setenv("MDCN_WIN_MARGIN", str(margin))
     pr = CASES[name]
@@ -148,7 +150,9 @@ def test_window_fp8_every_tile(tile, margin, name, monkeypatch):
 def test_window_fp8_split_tiles(ctas, name, dtype, monkeypatch):
     """Fewer workgroups than tiles (MDCN_WIN_CTAS): tiles split between two
     workgroups pass their first chunks' sums through the workspace; a forced
-    give-up (MDCN_WIN_SPIN_LIMIT=0) shows that some tile really is split."""
+    give-up (MDCN_WIN_SPIN_LIMIT=0) shows that some tile really is split.
+    (256-pixel tiles: MDCN_WIN_WIDE=0; the wide ones are split below.)"""
+    monkeypatch.setenv("MDCN_WIN_WIDE", "0")
     monkeypatch.setenv("MDCN_WIN_CTAS", str(ctas))
     pr = CASES[name]
     print("window fp8 split", name, dtype, ctas, flush=True)
@@ -300,3 +304,117 @@ def test_window_fp8_random_problems(pr, dtype):
     r = workloads.generate(pr, dtype, seed=13)
     ref, asum = fp8_ref(pr, r)
     assert_random_close(run(pr, r), ref, asum, dtype, "random")
+
+
+# ---- wide tiles: groups of more than 256 output channels run 128-pixel x
+# 512-channel tiles, the two waves of a SIMD sharing 32 pixels (each blends
+# two of a group's four taps, or four of tap 8's eight channels, and passes
+# its E4M3 bytes to the other through LDS).  The same tolerances apply: the
+# samples, weights and sums are the same as on the 256-pixel tiles.
+WIDE_CASES = {
+    # Mg = 288: one 512-row tile with rows past Mg unused; 37 x 37 pixels
+    "multi_tile": CASES["multi_tile"],
+    # Mg = 512 exactly, 2 chunks, 21 x 19 pixels
+    "full_rows": Problem(N=2, C=32, Co=512, H=21, W=19, offset_dist=("normal", 2.0)),
+    # Mg = 640: a full and a partial channel tile, 3 chunks
+    "two_row_tiles": Problem(N=1, C=48, Co=640, H=17, W=23, offset_dist=("normal", 3.0)),
+    # 2 groups (Mg = 320) in 2 offset groups, stride (2, 1), dilation (1, 2)
+    "grouped": Problem(N=2, C=64, Co=640, H=23, W=19, stride=(2, 1), padding=(1, 2),
+                       dilation=(1, 2), groups=2, deformable_groups=2,
+                       offset_dist=("normal", 2.0)),
+    # offsets up to 20 px: the global-memory fallback on every local tap of
+    # both waves of a pair (tap 8: each wave's half of the channels)
+    "far_offsets": Problem(N=1, C=16, Co=320, H=24, W=26, offset_dist=("uniform", 20.0),
+                           mask_dist=("uniform_zeros", 0.1)),
+}
+
+
+def _tile_of(pr, dtype):
+    shapes = pr.shapes()
+    dims = [int(v) for k in ("x", "offset", "mask", "weight") for v in shapes[k]]
+    d = mdcn.mdcn_describe_plan(make_op(pr), mdcn.MDCN_F16 if dtype == "f16" else mdcn.MDCN_BF16,
+                                dims)
+    return int(d.split("tile=")[1].split()[0])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("name", sorted(WIDE_CASES))
+def test_window_fp8_wide_grid_exact(name, dtype):
+    pr = WIDE_CASES[name]
+    print("window fp8 wide grid", name, dtype, flush=True)
+    assert _tile_of(pr, dtype) in (4, 5, 6)
+    inp = workloads.generate_grid(pr, dtype, seed=21)
+    ref, _ = fp8_ref(pr, inp)
+    tr = mdcn.Trace(16)
+    got = run(pr, inp, trace=tr)
+    assert [n for n, _ in tr.read()] == ["prep_blocks_fp8", "window_gather_gemm_fp8"]
+    assert_grid_exact(got, ref, dtype, name)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("name", sorted(WIDE_CASES))
+def test_window_fp8_wide_random(name, dtype):
+    pr = WIDE_CASES[name]
+    print("window fp8 wide random", name, dtype, flush=True)
+    inp = workloads.generate(pr, dtype, seed=22)
+    ref, asum = fp8_ref(pr, inp)
+    assert_random_close(run(pr, inp), ref, asum, dtype, name)
+
+
+@pytest.mark.parametrize("tile,margin", [(4, 8), (5, 2), (6, 8), (6, 2)])
+@pytest.mark.parametrize("name", ["multi_tile", "two_row_tiles", "far_offsets"])
+def test_window_fp8_wide_every_tile(tile, margin, name, monkeypatch):
+    """Each wide tile shape with the widest margin that fits (at most the
+    one asked) or a narrow one (many samples through the fallback)."""
+    monkeypatch.setenv("MDCN_WIN_TILE", str(tile))
+    monkeypatch.setenv("MDCN_WIN_MARGIN", str(margin))
+    pr = WIDE_CASES[name]
+    print("window fp8 wide tile", name, tile, margin, flush=True)
+    assert _tile_of(pr, "f16") == tile
+    inp = workloads.generate_grid(pr, "f16", seed=23)
+    ref, _ = fp8_ref(pr, inp)
+    assert_grid_exact(run(pr, inp), ref, "f16", (name, tile, margin))
+    rnd = workloads.generate(pr, "bf16", seed=24)
+    ref, asum = fp8_ref(pr, rnd)
+    assert_random_close(run(pr, rnd), ref, asum, "bf16", (name, tile, margin))
+
+
+@pytest.mark.parametrize("ctas,name,dtype", [(7, "full_rows", "f16"),
+                                             (7, "two_row_tiles", "bf16"),
+                                             (6, "grouped", "f16")])
+def test_window_fp8_wide_split_tiles(ctas, name, dtype, monkeypatch):
+    """Wide tiles split between workgroups (MDCN_WIN_CTAS; MDCN_WIN_SEG_X4=0
+    balances chunks alone, so these few whole tiles do not stay whole); a
+    forced give-up shows that some tile really is split."""
+    monkeypatch.setenv("MDCN_WIN_CTAS", str(ctas))
+    monkeypatch.setenv("MDCN_WIN_SEG_X4", "0")
+    pr = WIDE_CASES[name]
+    print("window fp8 wide split", name, dtype, ctas, flush=True)
+    inp = workloads.generate_grid(pr, dtype, seed=25)
+    monkeypatch.setenv("MDCN_WIN_SPIN_LIMIT", "0")
+    with pytest.raises(mdcn.MdcnError) as e:
+        run(pr, inp)
+    assert e.value.status == mdcn.MDCN_E_SYNC
+    monkeypatch.delenv("MDCN_WIN_SPIN_LIMIT")
+    ref, _ = fp8_ref(pr, inp)
+    assert_grid_exact(run(pr, inp), ref, dtype, (name, ctas))
+    rnd = workloads.generate(pr, dtype, seed=26)
+    ref, asum = fp8_ref(pr, rnd)
+    assert_random_close(run(pr, rnd), ref, asum, dtype, (name, ctas))
+
+
+@pytest.mark.parametrize("name", ["multi_tile", "two_row_tiles", "grouped"])
+def test_window_fp8_narrow_tiles_on_wide_groups(name, monkeypatch):
+    """MDCN_WIN_WIDE=0: the same groups on the 256-pixel tiles (each tile
+    run once per 256-channel half).  On grid inputs both tilings sum exactly,
+    so they agree bit for bit as well as with the oracle."""
+    pr = WIDE_CASES[name]
+    print("window fp8 narrow on wide groups", name, flush=True)
+    inp = workloads.generate_grid(pr, "f16", seed=27)
+    wide = run(pr, inp)
+    monkeypatch.setenv("MDCN_WIN_WIDE", "0")
+    assert _tile_of(pr, "f16") in (0, 1, 2, 3)
+    narrow = run(pr, inp)
+    ref, _ = fp8_ref(pr, inp)
+    assert_grid_exact(narrow, ref, "f16", name)
+    assert np.array_equal(wide, narrow)
