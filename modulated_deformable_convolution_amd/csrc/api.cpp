@@ -434,7 +434,7 @@ mdcn_status backward_impl(const mdcn_op *op, mdcn_dtype dtype, const int64_t dim
                 hipError_t r = mdcn::launch_to_nhwc(pgo, 1, gn, goT, stream);
                 return r != hipSuccess
                            ? r
-                           : mdcn::launch_gemm(pq, qp, 1, goT, wT, nullptr, nullptr, gcol, stream);
+                           : mdcn::launch_gemm_f32_split(pq, qp, goT, wT, gcol, stream);
             });
         if (err == hipSuccess && !l.binned)
             err = rec.run(mdcn::K_BWD_ZERO, [&] {

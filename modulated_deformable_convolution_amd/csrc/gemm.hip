@@ -29,10 +29,15 @@
 //
 //   f16 / bf16: one v_mfma_f32_32x32x16_{f16,bf16} per 16-byte fragment pair;
 //   f32:        four v_mfma_f32_32x32x2_f32 per 16-byte fragment pair;
+//   f32, split (the backward's GEMMs): each fp32 operand as three bf16
+//               parts, three v_mfma_f32_32x32x16_bf16 per fragment pair
+//               (f32x3_t in mfma_common.h);
 //   FP8 path:   E4M3 operands (the quantized weight and columns), one
 //               v_mfma_f32_32x32x64_f8f6f4 per two 16-byte fragment pairs,
 //               and the epilogue multiplies each output channel's sums by its
 //               weight row's scale 2^-e before the bias.
+#include <type_traits>
+
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -151,7 +156,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bias_kernel(
             if (st + 1 < steps)
                 issue_step<BM, BN, NW, STEP>(smem + (stage ^ 1) * STAGE_BYTES, ra, rb, voff,
                                              wave, st + 1);
-            mfma_step_frags<T, FM, FN>(acc, f);
+            if constexpr (std::is_same<OP, f32x3_t>::value)
+                mfma_step_frags_x3<FM, FN>(acc, f);
+            else
+                mfma_step_frags<T, FM, FN>(acc, f);
         }
     }
 
@@ -224,7 +232,15 @@ hipError_t launch_gemm_strided(const Problem &p, const Plan &plan, const void *a
 {
     if (p.dtype != MDCN_F32)
         return hipErrorInvalidValue;
-    return gemm_t<float, float>(p, plan, 1, a, b, nullptr, nullptr, out, stream, &st);
+    return gemm_t<float, f32x3_t>(p, plan, 1, a, b, nullptr, nullptr, out, stream, &st);
+}
+
+hipError_t launch_gemm_f32_split(const Problem &p, const Plan &plan, const void *a,
+                                 const void *b, void *out, hipStream_t stream)
+{
+    if (p.dtype != MDCN_F32)
+        return hipErrorInvalidValue;
+    return gemm_t<float, f32x3_t>(p, plan, 1, a, b, nullptr, nullptr, out, stream);
 }
 
 hipError_t launch_gemm(const Problem &p, const Plan &plan, int64_t cnt, const void *wpack,

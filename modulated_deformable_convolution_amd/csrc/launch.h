@@ -103,6 +103,12 @@ struct GemmStrides {
 };
 hipError_t launch_gemm_strided(const Problem &p, const Plan &plan, const void *a, const void *b,
                                void *out, const GemmStrides &st, hipStream_t stream);
+// The two fp32 GEMMs of the backward (launch_gemm_strided above, and this
+// one: launch_gemm's fp32 GEMM with cnt = 1 and no bias) run on the bf16
+// matrix cores with every operand split into three bf16 parts (six product
+// terms; about 2^-22 relative error per product, fp32 sums).
+hipError_t launch_gemm_f32_split(const Problem &p, const Plan &plan, const void *a,
+                                 const void *b, void *out, hipStream_t stream);
 
 // FP8 path: E4M3 operands and the sums times wscale[g*Mg + m] before the bias
 // (wscale null otherwise).

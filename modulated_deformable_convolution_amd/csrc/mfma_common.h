@@ -166,6 +166,93 @@ __device__ __forceinline__ void mfma_step_frags(float16v (&acc)[FM][FN],
                 acc[i][j] = Mma<T>::step(f.a[kg][i], f.b[kg][j], acc[i][j]);
 }
 
+// fp32 operands on the bf16 matrix cores (the "split" GEMM of the backward):
+// each fp32 value a is hi + mid + lo up to 2^-25 |a|, three bf16 values
+// (hi = bf16(a), mid = bf16(a - hi), lo = bf16(a - hi - mid), each rounded to
+// nearest even; the differences are exact in fp32), and a product a*b is
+// taken as the six terms hi*hi + mid*hi + hi*mid + mid*mid + hi*lo + lo*hi
+// (the dropped mid*lo + lo*mid + lo*lo are below 2^-23 |ab|).  A 16-byte
+// fragment pair (4 fp32 k per lane) is three v_mfma_f32_32x32x16_bf16 on
+// 8-bf16 operands whose two halves pair up by (lane, position):
+// [hi | mid] x [hi | hi], [hi | mid] x [mid | mid], [hi | lo] x [lo | hi].
+// The products of bf16 values are exact and the sums are fp32.  (A value
+// beyond the largest bf16, about 3.39e38, or an infinity gives a NaN.)
+struct f32x3_t {
+    float v;
+};
+
+struct Split3 {
+    uint2 hi, mid, lo;                    // 4 bf16 each, k order
+};
+
+__device__ __forceinline__ uint32_t bf16_pair_rne(float a, float b)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 r = __builtin_convertvector((f2){a, b}, b2);
+    uint32_t o;
+    __builtin_memcpy(&o, &r, 4);
+    return o;
+}
+
+__device__ __forceinline__ Split3 split3(const uint4 &a)
+{
+    const float v[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                        __uint_as_float(a.w)};
+    uint32_t h[2], m[2], l[2];
+    float r[4], t[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        h[q] = bf16_pair_rne(v[2 * q], v[2 * q + 1]);
+        r[2 * q] = v[2 * q] - __uint_as_float(h[q] << 16);
+        r[2 * q + 1] = v[2 * q + 1] - __uint_as_float(h[q] & 0xffff0000u);
+        m[q] = bf16_pair_rne(r[2 * q], r[2 * q + 1]);
+        t[2 * q] = r[2 * q] - __uint_as_float(m[q] << 16);
+        t[2 * q + 1] = r[2 * q + 1] - __uint_as_float(m[q] & 0xffff0000u);
+        l[q] = bf16_pair_rne(t[2 * q], t[2 * q + 1]);
+    }
+    Split3 o;
+    o.hi = make_uint2(h[0], h[1]);
+    o.mid = make_uint2(m[0], m[1]);
+    o.lo = make_uint2(l[0], l[1]);
+    return o;
+}
+
+__device__ __forceinline__ float16v mfma_bf16_halves(const uint2 &a0, const uint2 &a1,
+                                                     const uint2 &b0, const uint2 &b1,
+                                                     float16v c)
+{
+    const uint4 av = make_uint4(a0.x, a0.y, a1.x, a1.y);
+    const uint4 bv = make_uint4(b0.x, b0.y, b1.x, b1.y);
+    return Mma<bf16_t>::step(av, bv, c);
+}
+
+// The MFMAs of one 128-byte fp32 K step on the bf16 matrix cores (see
+// f32x3_t), one k-group at a time: B's parts first, then each A fragment's
+// parts right before its MFMAs, so that few split registers are live.
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_step_frags_x3(float16v (&acc)[FM][FN],
+                                                   const StepFrags<FM, FN> &f)
+{
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+        Split3 sb[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            sb[j] = split3(f.b[kg][j]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const Split3 sa = split3(f.a[kg][i]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                acc[i][j] = mfma_bf16_halves(sa.hi, sa.mid, sb[j].hi, sb[j].hi, acc[i][j]);
+                acc[i][j] = mfma_bf16_halves(sa.hi, sa.mid, sb[j].mid, sb[j].mid, acc[i][j]);
+                acc[i][j] = mfma_bf16_halves(sa.hi, sa.lo, sb[j].lo, sb[j].hi, acc[i][j]);
+            }
+        }
+    }
+}
+
 // One 128-byte K step of E4M3 operands: 128 k per row, two MFMAs of 64 k
 // per 32x32 tile.  Lane l of MFMA kp reads 16-byte chunks 4*kp + l/32 and
 // 4*kp + 2 + l/32 of its row (the same chunks for A and B) straight into the
