@@ -39,39 +39,49 @@ DEFAULT_WORKLOAD = "ocdnet_n4_c256_160x160"
 # taken on (sha256 of the listed files, first 16 hex digits).
 MEASURED_TRAFFIC = {
     ('deform_gather_fp8', 'ocdnet_n4_c256_160x160', 'f16'): {
-        "bytes": (40449 * 2 + 230400) * 1024,
+        "bytes": (40450 * 2 + 230400) * 1024,
         "sources": ('gather.hip', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "8627bef73018e322",
+        "sha": "116efe5da826d87e",
     },
     ('gemm_fp8_bias', 'ocdnet_n4_c256_160x160', 'f16'): {
         "bytes": (119933 * 2 + 51200) * 1024,
         "sources": ('gemm.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp'),
-        "sha": "aa6405c00fe4b3ae",
+        "sha": "4acbc1ebd6152ab1",
     },
     ('window_gather_gemm', 'ocdnet_n4_c256_160x160', 'f16'): {
-        "bytes": (124119 * 2 + 116401) * 1024,
+        "bytes": (124405 * 2 + 116836) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "560201c54f2ef031",
+        "sha": "6bc0a308ced7d4de",
+    },
+    ('window_gather_gemm', 'deep_n16_c512_40x40', 'f16'): {
+        "bytes": (32163 * 2 + 25709) * 1024,
+        "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
+        "sha": "6bc0a308ced7d4de",
     },
     ('window_gather_gemm_fp8', 'ocdnet_n4_c256_160x160', 'f16'): {
-        "bytes": (114334 * 2 + 116435) * 1024,
+        "bytes": (114914 * 2 + 116890) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "560201c54f2ef031",
+        "sha": "6bc0a308ced7d4de",
+    },
+    ('window_gather_gemm_fp8', 'deep_n16_c512_40x40', 'f16'): {
+        "bytes": (22923 * 2 + 25602) * 1024,
+        "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
+        "sha": "6bc0a308ced7d4de",
     },
     ('fused_gather_gemm', 'ocdnet_n4_c256_160x160', 'f16'): {
-        "bytes": (53970 * 2 + 51200) * 1024,
+        "bytes": (53920 * 2 + 51200) * 1024,
         "sources": ('fused.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "07d4064a99ad3a60",
+        "sha": "53dfca86e4afcaff",
     },
     ('gemm_bias', 'ocdnet_n4_c256_160x160', 'f16'): {
-        "bytes": (119948 * 2 + 25600) * 1024,
+        "bytes": (119950 * 2 + 25600) * 1024,
         "sources": ('gemm.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp'),
-        "sha": "aa6405c00fe4b3ae",
+        "sha": "4acbc1ebd6152ab1",
     },
     ('deform_gather', 'ocdnet_n4_c256_160x160', 'f16'): {
-        "bytes": (23282 * 2 + 230400) * 1024,
+        "bytes": (23283 * 2 + 230400) * 1024,
         "sources": ('gather.hip', 'device_common.h', 'plan.cpp'),
-        "sha": "f84b4baa3a2e48e6",
+        "sha": "a7330ce3959e9adb",
     },
     ('depthwise_direct', 'depthwise_n8_c256_96x96', 'f32'): {
         "bytes": (47349 * 2 + 73728) * 1024,
