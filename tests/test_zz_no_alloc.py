@@ -99,6 +99,38 @@ def test_noalloc_window_fp8_twice(monkeypatch):
         assert (err <= bound + 2.0 ** -11 * asum).all()
 
 
+def test_noalloc_window_fp8_wide_twice(monkeypatch):
+    """Two calls on the windowed FP8 path's wide tiles (groups of more than
+    256 output channels: 128-pixel x 512-channel tiles, split between
+    workgroups), the second smaller: bit-identical to mdcn_forward and within
+    the FP8 tolerance of the oracle's FP8 mode."""
+    monkeypatch.setenv("MDCN_WIN_CTAS", "5")
+    cases = [(Problem(N=2, C=32, Co=288, H=37, W=37, offset_dist=("normal", 3.0)), "f16", 35),
+             (Problem(N=1, C=32, Co=320, H=21, W=19, bias=True, offset_dist=("normal", 2.0)),
+              "bf16", 36)]
+    for pr, dtype, seed in cases:
+        print("noalloc fp8 wide", pr, dtype, flush=True)
+        op = mdcn.mdcn_create(pr.stride, pr.padding, pr.dilation, pr.groups,
+                              pr.deformable_groups, path=mdcn.MDCN_PATH_WINDOW_FP8)
+        s = pr.shapes()
+        dims = [int(v) for k in ("x", "offset", "mask", "weight") for v in s[k]]
+        desc = mdcn.mdcn_describe_plan(op, mdcn.MDCN_F16 if dtype == "f16" else mdcn.MDCN_BF16,
+                                       dims)
+        assert int(desc.split("tile=")[1].split()[0]) in (4, 5, 6), desc
+        inp = workloads.generate(pr, dtype, seed=seed)
+        g = _dev(inp)
+        st, got = _noalloc(op, g, dtype)
+        assert st == mdcn.MDCN_OK, mdcn.status_string(st)
+        ref_fwd = mdcn.forward(op, g["x"], g["offset"], g["mask"], g["weight"], g["bias"],
+                               check=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref_fwd)
+        ref, asum = oracle.forward_fp8(inp["x"], inp["offset"], inp["mask"], inp["weight"],
+                                       inp["bias"], **pr.attrs())
+        _, err, bound = within_tolerance(got.cpu().double().numpy(), ref, dtype)
+        assert (err <= bound + 2.0 ** -11 * asum).all()
+
+
 def test_noalloc_rejects_problems_beyond_the_array():
     # the OCDNet-like stage on the gather + GEMM path in fp32: one image's
     # column buffer alone (236 MB) exceeds the array
