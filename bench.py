@@ -51,22 +51,22 @@ MEASURED_TRAFFIC = {
     ('window_gather_gemm', 'ocdnet_n4_c256_160x160', 'f16'): {
         "bytes": (124405 * 2 + 116836) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "6bc0a308ced7d4de",
+        "sha": "93a731dbcdfce33a",
     },
     ('window_gather_gemm', 'deep_n16_c512_40x40', 'f16'): {
         "bytes": (32163 * 2 + 25709) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "6bc0a308ced7d4de",
+        "sha": "93a731dbcdfce33a",
     },
     ('window_gather_gemm_fp8', 'ocdnet_n4_c256_160x160', 'f16'): {
         "bytes": (114914 * 2 + 116890) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "6bc0a308ced7d4de",
+        "sha": "93a731dbcdfce33a",
     },
     ('window_gather_gemm_fp8', 'deep_n16_c512_40x40', 'f16'): {
         "bytes": (22923 * 2 + 25602) * 1024,
         "sources": ('window.hip', 'mfma_common.h', 'device_common.h', 'plan.cpp', 'plan.h'),
-        "sha": "6bc0a308ced7d4de",
+        "sha": "93a731dbcdfce33a",
     },
     ('fused_gather_gemm', 'ocdnet_n4_c256_160x160', 'f16'): {
         "bytes": (53920 * 2 + 51200) * 1024,

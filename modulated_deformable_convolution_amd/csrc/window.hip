@@ -52,7 +52,7 @@
 // waits for them are explicit (s_waitcnt vmcnt + barrier), so the compiler,
 // which does not see them, cannot make LDS reads wait for unrelated copies.
 //
-// The E4M3 variant (F8) keeps the tiles, window, geometry, work split and
+// The E4M3 variant (F8) keeps the window, geometry, work split and
 // hand-overs, and changes the contraction: each sample is blended in fp32,
 // saturated to +-448 and rounded to E4M3, and a 16-channel chunk's 9 taps run
 // as three MFMA groups on the FP8 matrix cores -- taps 0-3 and 4-7 as one
@@ -62,6 +62,12 @@
 // E4M3 by the set-up kernel, and 2^-e applied in the epilogue.  Its main loop
 // is software-pipelined: every wave blends group q while the MFMAs of group
 // q-1 run, with one barrier per group and one chunk's weight (36 KiB) in LDS.
+// On groups of more than 256 output channels it runs wide tiles, 128 pixels
+// x 512 output channels (72 KiB of weight, windows of kWindowPixelsWide
+// positions): waves w and w+4 share 32 pixels and take one 256-channel half
+// each, and each blends half of every group's samples and passes its E4M3
+// bytes to the other through LDS, so that every sample is blended once for
+// all 512 channels.
 #include <algorithm>
 #include <map>
 #include <mutex>
